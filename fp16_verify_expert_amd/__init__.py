@@ -1,0 +1,234 @@
+"""Python binding of libsmoe.so (the routed-expert MoE FFN path for gfx950).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch provides device memory and the stream; outputs not passed in are
+allocated with torch.  Functions carry the C entry points' names.  There is no
+CPU fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsmoe.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "smoe.h")
+ABI_VERSION = 1
+
+SMOE_DERR_BAD_ID = 1
+SMOE_DERR_NULL_EXPERT = 2
+
+_STATUS = {0: "SMOE_OK", 1: "SMOE_ERR_NULL", 2: "SMOE_ERR_SHAPE", 3: "SMOE_ERR_UNSUPPORTED",
+           4: "SMOE_ERR_HIP", 5: "SMOE_ERR_NOT_PINNED", 6: "SMOE_ERR_WORKSPACE"}
+
+
+class SmoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+_SIGS = {
+    "smoe_abi_version": (_i, []),
+    "smoe_last_error": (ctypes.c_char_p, []),
+    "smoe_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "moe_route_topk": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
+    "elb_count": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "moe_gather": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "w4a16_grouped_ffn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp,
+                               _sz, _vp, _vp]),
+    "verify_grouped_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp,
+                                 _vp, _sz, _vp, _vp]),
+    "moe_combine": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
+    "expert_stage_async": (_i, [_vp, _vp, _sz, _vp, _vp]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing; build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        v = L.smoe_abi_version()
+        if v != ABI_VERSION:
+            raise ImportError(f"libsmoe ABI {v} != binding ABI {ABI_VERSION}")
+        _lib = L
+    return _lib
+
+
+def header_functions() -> Sequence[str]:
+    """Names of the functions declared in include/smoe.h."""
+    txt = open(HEADER_PATH).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    names = re.findall(r"^\s*(?:smoe_status|int|const char\*|size_t)\s+(\w+)\s*\(", txt, re.M)
+    return names
+
+
+def _call(name: str, *args) -> None:
+    st = getattr(lib(), name)(*args)
+    if st != 0:
+        raise SmoeError(name, st, lib().smoe_last_error().decode())
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else _vp(t.data_ptr())
+
+
+def _s(stream) -> _vp:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return _vp(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
+    if not (t.is_cuda and t.dtype == dtype and t.is_contiguous()):
+        raise ValueError(f"{name}: expected a contiguous {dtype} CUDA tensor, got "
+                         f"{t.dtype} on {t.device} (contiguous={t.is_contiguous()})")
+
+
+def workspace_bytes(which: int, T: int, k: int, H: int, I: int, E: int) -> int:
+    return int(lib().smoe_workspace_bytes(which, T, k, H, I, E))
+
+
+def new_workspace(which: int, T: int, k: int, H: int, I: int, E: int,
+                  device="cuda") -> torch.Tensor:
+    """Zero-filled workspace (the w4a16 counters must start at zero)."""
+    n = max(256, workspace_bytes(which, T, k, H, I, E))
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- calls ----
+
+def moe_route_topk(x, w_router, k: int, renormalize: bool = False, w_shared_gate=None, *,
+                   topk_ids=None, topk_w=None, shared_gate=None, stream=None):
+    _check(x, torch.float16, "x")
+    _check(w_router, torch.float16, "w_router")
+    T, H = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if w_shared_gate is not None:
+        _check(w_shared_gate, torch.float16, "w_shared_gate")
+        if shared_gate is None:
+            shared_gate = torch.empty((T,), dtype=torch.float32, device=dev)
+    _call("moe_route_topk", _p(x), _p(w_router), _p(w_shared_gate), T, H, E, k,
+          1 if renormalize else 0, _p(topk_ids), _p(topk_w),
+          _p(shared_gate) if w_shared_gate is not None else None, _s(stream))
+    return topk_ids, topk_w, shared_gate
+
+
+def elb_count(topk_ids, E: int, layer: int, counters, err_word=None, stream=None):
+    _check(topk_ids, torch.int32, "topk_ids")
+    _check(counters, torch.int32, "counters")
+    T, k = topk_ids.shape
+    L = counters.shape[0]
+    _call("elb_count", _p(topk_ids), T, k, E, layer, L, _p(counters), _p(err_word), _s(stream))
+    return counters
+
+
+def moe_gather(topk_ids, E: int, err_word=None, *, out=None, stream=None):
+    """Returns dict(offsets, sorted_token, sorted_pair, pair_pos, active, n_active)."""
+    _check(topk_ids, torch.int32, "topk_ids")
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    n = T * k
+    if out is None:
+        out = dict(offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                   sorted_token=torch.empty(max(n, 1), dtype=torch.int32, device=dev),
+                   sorted_pair=torch.empty(max(n, 1), dtype=torch.int32, device=dev),
+                   pair_pos=torch.empty(max(n, 1), dtype=torch.int32, device=dev),
+                   active=torch.empty(E, dtype=torch.int32, device=dev),
+                   n_active=torch.empty(1, dtype=torch.int32, device=dev))
+    _call("moe_gather", _p(topk_ids), T, k, E, _p(out["offsets"]), _p(out["sorted_token"]),
+          _p(out["sorted_pair"]), _p(out["pair_pos"]), _p(out["active"]), _p(out["n_active"]),
+          _p(err_word), _s(stream))
+    return out
+
+
+def w4_expert_table(experts: Sequence, device="cuda") -> torch.Tensor:
+    """Device array of smoe_w4_expert from per-expert dicts
+    {w13: (qweight, scales, qzeros), w2: (...)} of CUDA tensors (None = absent)."""
+    rows = []
+    for ex in experts:
+        if ex is None:
+            rows.append([0] * 6)
+            continue
+        r = []
+        for key in ("w13", "w2"):
+            for t in ex[key]:
+                r.append(0 if t is None else t.data_ptr())
+        rows.append(r)
+    return torch.tensor(rows, dtype=torch.int64).to(device)
+
+
+def f16_expert_table(experts: Sequence, device="cuda") -> torch.Tensor:
+    """Device array of smoe_f16_expert from (w13, w2) CUDA tensor pairs."""
+    rows = [[0, 0] if ex is None else [0 if t is None else t.data_ptr() for t in ex]
+            for ex in experts]
+    return torch.tensor(rows, dtype=torch.int64).to(device)
+
+
+def w4a16_grouped_ffn(x, maps, table, T: int, k: int, H: int, I: int, E: int, workspace,
+                      *, y_sorted=None, err_word=None, stream=None):
+    _check(x, torch.float16, "x")
+    if y_sorted is None:
+        y_sorted = torch.empty((max(T * k, 1), H), dtype=torch.float16, device=x.device)
+    _call("w4a16_grouped_ffn", _p(x), _p(maps["sorted_token"]), _p(maps["offsets"]),
+          _p(maps["active"]), _p(maps["n_active"]), _p(table), T, k, H, I, E, 128,
+          _p(y_sorted), _p(workspace), workspace.numel() * workspace.element_size(),
+          _p(err_word), _s(stream))
+    return y_sorted
+
+
+def verify_grouped_gemm(x, sorted_token, offsets, table, T: int, rows: int, H: int, I: int,
+                        E: int, workspace, *, active=None, n_active=None, expert_mask=None,
+                        y_sorted=None, err_word=None, stream=None):
+    _check(x, torch.float16, "x")
+    if y_sorted is None:
+        y_sorted = torch.empty((max(rows, 1), H), dtype=torch.float16, device=x.device)
+    _call("verify_grouped_gemm", _p(x), _p(sorted_token), _p(offsets), _p(active),
+          _p(n_active), _p(table), _p(expert_mask), T, rows, H, I, E, _p(y_sorted),
+          _p(workspace), workspace.numel() * workspace.element_size(), _p(err_word), _s(stream))
+    return y_sorted
+
+
+def moe_combine(y_sorted, pair_pos, topk_w, shared_out=None, shared_scale=None, residual=None,
+                *, out=None, stream=None):
+    T, k = topk_w.shape
+    H = y_sorted.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float16, device=y_sorted.device)
+    _call("moe_combine", _p(y_sorted), _p(pair_pos), _p(topk_w), _p(shared_out),
+          _p(shared_scale), _p(residual), T, k, H, _p(out), _s(stream))
+    return out
+
+
+def expert_stage_async(dst: torch.Tensor, src_pinned: torch.Tensor, side_stream=None,
+                       done_event=None) -> None:
+    nbytes = src_pinned.numel() * src_pinned.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("expert_stage_async: destination smaller than source")
+    ev = None
+    if done_event is not None:
+        if not done_event.cuda_event:      # torch creates the event lazily
+            done_event.record(side_stream if side_stream is not None else None)
+        ev = _vp(done_event.cuda_event)
+    _call("expert_stage_async", _p(dst), _vp(src_pinned.data_ptr()), nbytes, _s(side_stream), ev)

@@ -1,0 +1,259 @@
+// C ABI of libsmoe.so: host-side argument checks, device check, dispatch.
+// Every check runs before anything is enqueued; no call allocates memory.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+smoe_status fail(smoe_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+smoe_status ok() {
+    g_err.clear();
+    return SMOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+smoe_status hip_result(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(SMOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// gfx950 check, once per device.
+smoe_status check_device() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SMOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    static std::mutex mu;
+    static int state[256];  // 0 unknown, 1 gfx950, 2 other
+    static char names[256][64];
+    if (dev < 0 || dev >= 256) return fail(SMOE_ERR_UNSUPPORTED, "device index %d", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (state[dev] == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess)
+            return fail(SMOE_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+        snprintf(names[dev], sizeof(names[dev]), "%s", prop.gcnArchName);
+        state[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    }
+    if (state[dev] != 1)
+        return fail(SMOE_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950", dev,
+                    names[dev]);
+    return SMOE_OK;
+}
+
+#define REQUIRE(cond, st, ...)                     \
+    do {                                           \
+        if (!(cond)) return fail(st, __VA_ARGS__); \
+    } while (0)
+
+#define CHECK_DEVICE()                         \
+    do {                                       \
+        smoe_status _s = check_device();       \
+        if (_s != SMOE_OK) return _s;          \
+    } while (0)
+
+smoe_status check_hek(int H, int E, int k) {
+    REQUIRE(H > 0 && H % 128 == 0, SMOE_ERR_SHAPE, "H=%d must be a positive multiple of 128", H);
+    REQUIRE(E >= 1 && E <= 256, SMOE_ERR_SHAPE, "E=%d must be in [1, 256]", E);
+    REQUIRE(k >= 1 && k <= E, SMOE_ERR_SHAPE, "k=%d must be in [1, E=%d]", k, E);
+    return SMOE_OK;
+}
+
+constexpr long long kMaxPairs = 1 << 20;
+
+}  // namespace
+
+extern "C" {
+
+int smoe_abi_version(void) { return SMOE_ABI_VERSION; }
+
+const char* smoe_last_error(void) { return g_err.c_str(); }
+
+size_t smoe_workspace_bytes(int which, int T, int k, int H, int I, int E) {
+    if (T < 0 || k < 1 || E < 1 || E > 256 || H <= 0 || I <= 0 || H % 128 || I % 128) return 0;
+    if ((long long)T * k > kMaxPairs) return 0;
+    if (which == 0) return smoe::w4a16_workspace_bytes(T, k, H, I, E);
+    if (which == 1) return smoe::verify_workspace_bytes(T, T * k, H, I, E);
+    return 0;
+}
+
+smoe_status moe_route_topk(const uint16_t* x, const uint16_t* w_router,
+                           const uint16_t* w_shared_gate, int T, int H, int E, int k,
+                           int renormalize, int32_t* topk_ids, float* topk_w,
+                           float* shared_gate, void* stream) {
+    REQUIRE(x && w_router && topk_ids && topk_w, SMOE_ERR_NULL,
+            "moe_route_topk: x, w_router, topk_ids and topk_w are required");
+    REQUIRE(!w_shared_gate || shared_gate, SMOE_ERR_NULL,
+            "moe_route_topk: shared_gate output is required with w_shared_gate");
+    REQUIRE(T >= 0, SMOE_ERR_SHAPE, "moe_route_topk: T=%d < 0", T);
+    smoe_status st = check_hek(H, E, k);
+    if (st != SMOE_OK) return st;
+    REQUIRE(aligned(x, 16) && aligned(w_router, 16) && aligned(w_shared_gate, 16),
+            SMOE_ERR_SHAPE, "moe_route_topk: x, w_router, w_shared_gate must be 16-byte aligned");
+    if (T == 0) return ok();
+    CHECK_DEVICE();
+    return hip_result(smoe::launch_route_topk(x, w_router, w_shared_gate, T, H, E, k,
+                                              renormalize ? 1 : 0, topk_ids, topk_w, shared_gate,
+                                              static_cast<hipStream_t>(stream)),
+                      "moe_route_topk launch");
+}
+
+smoe_status elb_count(const int32_t* topk_ids, int T, int k, int E, int layer, int L,
+                      int32_t* counters, int32_t* err_word, void* stream) {
+    REQUIRE(topk_ids && counters, SMOE_ERR_NULL, "elb_count: topk_ids and counters are required");
+    REQUIRE(T >= 0, SMOE_ERR_SHAPE, "elb_count: T=%d < 0", T);
+    REQUIRE(E >= 1 && E <= 256 && k >= 1 && k <= E, SMOE_ERR_SHAPE,
+            "elb_count: need 1 <= k=%d <= E=%d <= 256", k, E);
+    REQUIRE(L >= 1 && layer >= 0 && layer < L, SMOE_ERR_SHAPE,
+            "elb_count: layer=%d must be in [0, L=%d)", layer, L);
+    REQUIRE((long long)T * k <= kMaxPairs, SMOE_ERR_SHAPE, "elb_count: T*k exceeds 2^20");
+    if (T == 0) return ok();
+    CHECK_DEVICE();
+    return hip_result(smoe::launch_elb_count(topk_ids, T * k, E, layer, counters, err_word,
+                                             static_cast<hipStream_t>(stream)),
+                      "elb_count launch");
+}
+
+smoe_status moe_gather(const int32_t* topk_ids, int T, int k, int E, int32_t* expert_offsets,
+                       int32_t* sorted_token, int32_t* sorted_pair, int32_t* pair_pos,
+                       int32_t* active, int32_t* n_active, int32_t* err_word, void* stream) {
+    REQUIRE(expert_offsets && active && n_active, SMOE_ERR_NULL,
+            "moe_gather: expert_offsets, active and n_active are required");
+    REQUIRE(T == 0 || (topk_ids && sorted_token && sorted_pair && pair_pos), SMOE_ERR_NULL,
+            "moe_gather: topk_ids, sorted_token, sorted_pair and pair_pos are required");
+    REQUIRE(T >= 0, SMOE_ERR_SHAPE, "moe_gather: T=%d < 0", T);
+    REQUIRE(E >= 1 && E <= 256 && k >= 1 && k <= E, SMOE_ERR_SHAPE,
+            "moe_gather: need 1 <= k=%d <= E=%d <= 256", k, E);
+    REQUIRE((long long)T * k <= kMaxPairs, SMOE_ERR_SHAPE, "moe_gather: T*k exceeds 2^20");
+    CHECK_DEVICE();
+    // T == 0 still writes empty maps (zero offsets, no active experts).
+    return hip_result(smoe::launch_gather(topk_ids, T * k, k, E, expert_offsets, sorted_token,
+                                          sorted_pair, pair_pos, active, n_active, err_word,
+                                          static_cast<hipStream_t>(stream)),
+                      "moe_gather launch");
+}
+
+smoe_status w4a16_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
+                              const int32_t* expert_offsets, const int32_t* active,
+                              const int32_t* n_active, const smoe_w4_expert* experts, int T,
+                              int k, int H, int I, int E, int group_size, uint16_t* y_sorted,
+                              void* workspace, size_t workspace_bytes, int32_t* err_word,
+                              void* stream) {
+    REQUIRE(x && sorted_token && expert_offsets && active && n_active && experts && y_sorted,
+            SMOE_ERR_NULL, "w4a16_grouped_ffn: a required pointer is NULL");
+    REQUIRE(T >= 0, SMOE_ERR_SHAPE, "w4a16_grouped_ffn: T=%d < 0", T);
+    smoe_status st = check_hek(H, E, k);
+    if (st != SMOE_OK) return st;
+    REQUIRE(I > 0 && I % 128 == 0, SMOE_ERR_SHAPE,
+            "w4a16_grouped_ffn: I=%d must be a positive multiple of 128", I);
+    REQUIRE(group_size == 128, SMOE_ERR_UNSUPPORTED,
+            "w4a16_grouped_ffn: group_size=%d (only 128 is supported)", group_size);
+    REQUIRE((long long)T * k <= kMaxPairs, SMOE_ERR_SHAPE, "w4a16_grouped_ffn: T*k exceeds 2^20");
+    REQUIRE(aligned(x, 16), SMOE_ERR_SHAPE, "w4a16_grouped_ffn: x must be 16-byte aligned");
+    if (T == 0) return ok();
+    const size_t need = smoe::w4a16_workspace_bytes(T, k, H, I, E);
+    REQUIRE(workspace && workspace_bytes >= need && aligned(workspace, 256), SMOE_ERR_WORKSPACE,
+            "w4a16_grouped_ffn: workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+            workspace_bytes);
+    CHECK_DEVICE();
+    return hip_result(smoe::launch_w4a16_ffn(x, sorted_token, expert_offsets, active, n_active,
+                                             experts, T, k, H, I, E, y_sorted, workspace,
+                                             err_word, static_cast<hipStream_t>(stream)),
+                      "w4a16_grouped_ffn launch");
+}
+
+smoe_status verify_grouped_gemm(const uint16_t* x, const int32_t* sorted_token,
+                                const int32_t* expert_offsets, const int32_t* active,
+                                const int32_t* n_active, const smoe_f16_expert* experts,
+                                const uint8_t* expert_mask, int T, int rows, int H, int I, int E,
+                                uint16_t* y_sorted, void* workspace, size_t workspace_bytes,
+                                int32_t* err_word, void* stream) {
+    REQUIRE(x && sorted_token && expert_offsets && experts && y_sorted, SMOE_ERR_NULL,
+            "verify_grouped_gemm: a required pointer is NULL");
+    REQUIRE((active == nullptr) == (n_active == nullptr), SMOE_ERR_NULL,
+            "verify_grouped_gemm: pass both active and n_active, or neither");
+    REQUIRE(T >= 0 && rows >= 0, SMOE_ERR_SHAPE, "verify_grouped_gemm: T=%d, rows=%d", T, rows);
+    REQUIRE(H > 0 && H % 128 == 0 && I > 0 && I % 128 == 0, SMOE_ERR_SHAPE,
+            "verify_grouped_gemm: H=%d and I=%d must be positive multiples of 128", H, I);
+    REQUIRE(E >= 1 && E <= 256, SMOE_ERR_SHAPE, "verify_grouped_gemm: E=%d must be in [1, 256]",
+            E);
+    REQUIRE(rows <= kMaxPairs, SMOE_ERR_SHAPE, "verify_grouped_gemm: rows exceeds 2^20");
+    REQUIRE(aligned(x, 16), SMOE_ERR_SHAPE, "verify_grouped_gemm: x must be 16-byte aligned");
+    if (rows == 0 || T == 0) return ok();
+    const size_t need = smoe::verify_workspace_bytes(T, rows, H, I, E);
+    REQUIRE(workspace && workspace_bytes >= need && aligned(workspace, 256), SMOE_ERR_WORKSPACE,
+            "verify_grouped_gemm: workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+            workspace_bytes);
+    CHECK_DEVICE();
+    return hip_result(smoe::launch_verify_ffn(x, sorted_token, expert_offsets, active, n_active,
+                                              experts, expert_mask, T, rows, H, I, E, y_sorted,
+                                              workspace, err_word,
+                                              static_cast<hipStream_t>(stream)),
+                      "verify_grouped_gemm launch");
+}
+
+smoe_status moe_combine(const uint16_t* y_sorted, const int32_t* pair_pos, const float* topk_w,
+                        const uint16_t* shared_out, const float* shared_scale,
+                        const uint16_t* residual, int T, int k, int H, uint16_t* out,
+                        void* stream) {
+    REQUIRE(y_sorted && pair_pos && topk_w && out, SMOE_ERR_NULL,
+            "moe_combine: y_sorted, pair_pos, topk_w and out are required");
+    REQUIRE(T >= 0 && T <= 65535, SMOE_ERR_SHAPE, "moe_combine: T=%d must be in [0, 65535]", T);
+    REQUIRE(k >= 1 && k <= 256, SMOE_ERR_SHAPE, "moe_combine: k=%d must be in [1, 256]", k);
+    REQUIRE(H > 0 && H % 128 == 0, SMOE_ERR_SHAPE, "moe_combine: H=%d must be a multiple of 128",
+            H);
+    REQUIRE(aligned(y_sorted, 16) && aligned(shared_out, 16) && aligned(residual, 16) &&
+                aligned(out, 16),
+            SMOE_ERR_SHAPE, "moe_combine: fp16 tensors must be 16-byte aligned");
+    if (T == 0) return ok();
+    CHECK_DEVICE();
+    return hip_result(smoe::launch_combine(y_sorted, pair_pos, topk_w, shared_out, shared_scale,
+                                           residual, T, k, H, out,
+                                           static_cast<hipStream_t>(stream)),
+                      "moe_combine launch");
+}
+
+smoe_status expert_stage_async(void* dst_device, const void* src_pinned_host, size_t bytes,
+                               void* side_stream, void* done_event) {
+    REQUIRE(dst_device && src_pinned_host, SMOE_ERR_NULL,
+            "expert_stage_async: dst_device and src_pinned_host are required");
+    if (bytes == 0) return ok();
+    CHECK_DEVICE();
+    hipPointerAttribute_t attr;
+    memset(&attr, 0, sizeof(attr));
+    hipError_t e = hipPointerGetAttributes(&attr, src_pinned_host);
+    if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+        (void)hipGetLastError();  // clear the query's error state
+        return fail(SMOE_ERR_NOT_PINNED,
+                    "expert_stage_async: source %p is not page-locked host memory",
+                    src_pinned_host);
+    }
+    hipStream_t s = static_cast<hipStream_t>(side_stream);
+    e = hipMemcpyAsync(dst_device, src_pinned_host, bytes, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_result(e, "expert_stage_async: hipMemcpyAsync");
+    if (done_event) {
+        e = hipEventRecord(static_cast<hipEvent_t>(done_event), s);
+        if (e != hipSuccess) return hip_result(e, "expert_stage_async: hipEventRecord");
+    }
+    return ok();
+}
+
+}  // extern "C"

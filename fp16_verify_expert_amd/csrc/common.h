@@ -1,0 +1,52 @@
+// Internal helpers shared by the gfx950 kernels of libsmoe.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "smoe.h"
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+#define SMOE_DEV __device__ __forceinline__
+
+SMOE_DEV float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+SMOE_DEV uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }  // RNE
+
+SMOE_DEV void flag_error(int32_t* err, int32_t bit) {
+    if (err) atomicOr(err, bit);
+}
+
+// Number of sorted rows in [0, rows) that belong to expert slot bounds.
+struct RowRange {
+    int r0, r1;
+};
+
+// Launchers (one per kernel family), defined next to their kernels.
+namespace smoe {
+hipError_t launch_route_topk(const uint16_t* x, const uint16_t* wr, const uint16_t* wsg, int T,
+                             int H, int E, int k, int renorm, int32_t* ids, float* w, float* gate,
+                             hipStream_t s);
+hipError_t launch_elb_count(const int32_t* ids, int n, int E, int layer, int32_t* counters,
+                            int32_t* err, hipStream_t s);
+hipError_t launch_gather(const int32_t* ids, int n, int k, int E, int32_t* off, int32_t* st,
+                         int32_t* sp, int32_t* pp, int32_t* active, int32_t* n_active,
+                         int32_t* err, hipStream_t s);
+hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, const int32_t* off,
+                            const int32_t* active, const int32_t* n_active,
+                            const smoe_w4_expert* experts, int T, int k, int H, int I, int E,
+                            uint16_t* y, void* ws, int32_t* err, hipStream_t s);
+size_t w4a16_workspace_bytes(int T, int k, int H, int I, int E);
+hipError_t launch_verify_ffn(const uint16_t* x, const int32_t* sorted_token, const int32_t* off,
+                             const int32_t* active, const int32_t* n_active,
+                             const smoe_f16_expert* experts, const uint8_t* mask, int T, int rows,
+                             int H, int I, int E, uint16_t* y, void* ws, int32_t* err,
+                             hipStream_t s);
+size_t verify_workspace_bytes(int T, int rows, int H, int I, int E);
+hipError_t launch_combine(const uint16_t* y, const int32_t* pp, const float* w,
+                          const uint16_t* shared, const float* sscale, const uint16_t* resid,
+                          int T, int k, int H, uint16_t* out, hipStream_t s);
+}  // namespace smoe

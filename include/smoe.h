@@ -1,0 +1,268 @@
+/*
+ * smoe.h -- C ABI of libsmoe.so: the routed-expert MoE FFN path of a
+ * speculative MoE decoder (INT4 self-draft, FP16 verification), hand-written
+ * HIP for gfx950 (MI355X).
+ *
+ * Sources, cited by page title and section:
+ *   [S1] "Specter: Fast MoE Inference via Quantization-Enabled Multi-Step
+ *        Speculative Offloading" (AI summary), Key Contributions 1-4 and
+ *        Methodology in Plain English.
+ *   [S2] "Specter previews expert routing with an INT4 copy of the model
+ *        itself", What shipped.
+ *
+ * Conventions shared by every entry point
+ *   - fp16 tensors are passed as raw IEEE binary16 bit patterns (uint16_t).
+ *   - All tensors are row-major and dense (no strides).
+ *   - Every pointer is device memory unless a parameter says "host".  The
+ *     caller owns every buffer; the library never allocates or frees.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work; results are valid once the stream reaches that point.
+ *   - Shapes: H % 128 == 0, I % 128 == 0, 1 <= k <= E <= 256, T >= 0.
+ *     T == 0 (or rows == 0) is a no-op that returns SMOE_OK.
+ *   - Arguments are checked on the host before anything is enqueued; a bad
+ *     argument returns a nonzero status and sets smoe_last_error() (thread
+ *     local, valid until the next call on that thread).  The library never
+ *     aborts.  Launch failures return SMOE_ERR_HIP with HIP's message.
+ *   - Data errors only visible on the device (an expert id outside [0, E),
+ *     a null weight pointer for a touched expert) are reported by OR-ing a
+ *     SMOE_DERR_* bit into the optional `err_word` (int32 device memory);
+ *     the offending work is skipped, nothing is read or written out of
+ *     bounds.  The caller reads err_word after synchronising.
+ *   - The first call on a device checks that it is a gfx950 GPU and returns
+ *     SMOE_ERR_UNSUPPORTED otherwise.
+ */
+#ifndef SMOE_H
+#define SMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SMOE_ABI_VERSION 1
+
+typedef enum {
+    SMOE_OK = 0,
+    SMOE_ERR_NULL = 1,         /* a required pointer is NULL                 */
+    SMOE_ERR_SHAPE = 2,        /* a size or shape constraint is violated     */
+    SMOE_ERR_UNSUPPORTED = 3,  /* device is not gfx950, or option not built  */
+    SMOE_ERR_HIP = 4,          /* a HIP runtime call or launch failed        */
+    SMOE_ERR_NOT_PINNED = 5,   /* host source of a stage is not page-locked  */
+    SMOE_ERR_WORKSPACE = 6     /* workspace NULL or smaller than required    */
+} smoe_status;
+
+/* device-side data error bits (OR-ed into err_word) */
+#define SMOE_DERR_BAD_ID      1   /* an expert id outside [0, E)            */
+#define SMOE_DERR_NULL_EXPERT 2   /* a touched expert has a NULL weight     */
+
+/* Version of this header's ABI; the binding refuses a mismatched library. */
+int smoe_abi_version(void);
+
+/* Message of the last failed call on this thread ("" after a success). */
+const char* smoe_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Expert weight descriptors (device arrays of E entries, uploaded by the
+ * caller; entries may point anywhere in device memory, e.g. at resident or
+ * staging slots).
+ *
+ * smoe_w4_mat: one GPTQ INT4 matrix W[K, N] with group size 128, in the usual
+ * GPTQ checkpoint layout ([S2] the draft's routed experts are GPTQ INT4,
+ * group 128):
+ *   qweight int32 [K/8, N]    nibble i (bits 4i..4i+3) of word [r, n] is the
+ *                             4-bit code of row 8r+i, column n;
+ *   scales  fp16  [K/128, N]  scale of (group, column);
+ *   qzeros  int32 [K/128, N/8] nibble i of word [g, c] is the 4-bit zero of
+ *                             column 8c+i in group g (no offset).
+ *   W[kk, n] = (q[kk, n] - z[kk/128, n]) * s[kk/128, n].
+ * A draft expert holds w13 (K = H, N = 2I; columns 0..I-1 are the gate
+ * projection, I..2I-1 the up projection) and w2 (K = I, N = H).
+ *
+ * smoe_f16_expert: the FP16 target expert in nn.Linear layout (y = x W^T):
+ *   w13 fp16 [2I, H] (rows 0..I-1 gate, I..2I-1 up), w2 fp16 [H, I].
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    const int32_t* qweight;
+    const uint16_t* scales;
+    const int32_t* qzeros;
+} smoe_w4_mat;
+
+typedef struct {
+    smoe_w4_mat w13;
+    smoe_w4_mat w2;
+} smoe_w4_expert;
+
+typedef struct {
+    const uint16_t* w13;
+    const uint16_t* w2;
+} smoe_f16_expert;
+
+/* ------------------------------------------------------------------------
+ * moe_route_topk -- top-k routing by the FP16 router ([S1] Key Contributions
+ * 3: the target router's decisions are authoritative; [S2] the draft reuses
+ * the target's router and shared-expert tensors).
+ *
+ *   x             fp16 [T, H]   token activations
+ *   w_router      fp16 [E, H]   router weight
+ *   w_shared_gate fp16 [H]      optional (NULL = none) shared-expert gate
+ *   renormalize   0: weights are the softmax over all E at the chosen ids;
+ *                 1: those weights divided by their sum
+ *   topk_ids      int32 [T, k]  out: experts by decreasing logit, equal
+ *                               logits lower index first
+ *   topk_w        fp32  [T, k]  out: routing weights
+ *   shared_gate   fp32  [T]     out (required iff w_shared_gate is given):
+ *                               sigmoid(x . w_shared_gate)
+ * Logits are fp32 sums of exact fp16 products taken in one fixed order, so
+ * the chosen ids are reproducible bit for bit: hidden chunks of 8 elements,
+ * chunk c owned by lane c mod 64, each lane adding its products in
+ * increasing index; then six pairwise rounds s_p += s_(p xor d), d = 32..1.
+ * ---------------------------------------------------------------------- */
+smoe_status moe_route_topk(const uint16_t* x, const uint16_t* w_router,
+                           const uint16_t* w_shared_gate, int T, int H, int E, int k,
+                           int renormalize, int32_t* topk_ids, float* topk_w,
+                           float* shared_gate, void* stream);
+
+/* ------------------------------------------------------------------------
+ * elb_count -- Expert Lookahead Buffer update ([S1] Key Contributions 3 and
+ * Methodology: GPU-resident, layer-indexed counters tallying how often each
+ * expert is chosen while drafting; snapshots of them drive prefetch).
+ *
+ *   topk_ids  int32 [T, k]
+ *   counters  int32 [L, E]  in/out: counters[layer, e] += number of (t, j)
+ *                           with topk_ids[t, j] == e.  Accumulates across
+ *                           calls; the caller clears or snapshots it at
+ *                           chunk boundaries (plain copies / memsets).
+ *   err_word  optional; ids outside [0, E) are skipped and flagged.
+ * Integer atomics: the result does not depend on execution order.
+ * ---------------------------------------------------------------------- */
+smoe_status elb_count(const int32_t* topk_ids, int T, int k, int E, int layer, int L,
+                      int32_t* counters, int32_t* err_word, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_gather -- group the T*k (token, slot) pairs by expert ([S1] Key
+ * Contributions 4: the draft kernel gathers tokens by expert; Methodology:
+ * verification packs the tokens of one expert together).  Pair p = t*k + j.
+ * Stable: inside one expert, rows follow increasing p.
+ *
+ *   expert_offsets int32 [E+1]  out: rows of expert e are [off[e], off[e+1])
+ *   sorted_pair    int32 [T*k]  out: pair held by each sorted row (-1 past
+ *                               the last valid row)
+ *   sorted_token   int32 [T*k]  out: sorted_pair / k (-1 past the end)
+ *   pair_pos       int32 [T*k]  out: sorted row of pair p (-1 if dropped)
+ *   active         int32 [E]    out: touched experts in increasing id, then -1
+ *   n_active       int32 [1]    out: number of touched experts
+ *   err_word       optional; ids outside [0, E) are dropped and flagged.
+ * T*k must not exceed 1<<20.
+ * ---------------------------------------------------------------------- */
+smoe_status moe_gather(const int32_t* topk_ids, int T, int k, int E, int32_t* expert_offsets,
+                       int32_t* sorted_token, int32_t* sorted_pair, int32_t* pair_pos,
+                       int32_t* active, int32_t* n_active, int32_t* err_word, void* stream);
+
+/* ------------------------------------------------------------------------
+ * w4a16_grouped_ffn -- draft routed-expert SwiGLU FFN over GPTQ INT4 weights
+ * for every touched expert, one launch per projection across all experts
+ * ([S1] Key Contributions 4: fused multi-expert INT4 draft kernel, one GPU
+ * launch; [S2] W4A16: INT4 tiles dequantised while the products are formed
+ * in higher precision).
+ *
+ * For every sorted row r of expert e (rows from moe_gather):
+ *   h = silu(x[sorted_token[r]] . Wg_e) * (x[sorted_token[r]] . Wu_e)   (fp16)
+ *   y_sorted[r] = h . Wd_e                                              (fp16)
+ * with W dequantised per group; products accumulate in fp32.
+ *
+ *   x              fp16 [T, H]
+ *   sorted_token, expert_offsets, active, n_active: from moe_gather
+ *   experts        device array of E smoe_w4_expert
+ *   k              top-k (rows = T*k bounds the sorted rows)
+ *   group_size     must be 128
+ *   y_sorted       fp16 [T*k, H] out (rows past off[E] untouched)
+ *   workspace      device, >= smoe_workspace_bytes(0, T, k, H, I, E) bytes,
+ *                  256-byte aligned.  Its first 4096 bytes are completion
+ *                  counters that must be zero before the first call with this
+ *                  workspace; every call that completes leaves them zero.
+ *                  Calls sharing one workspace must be stream-ordered.
+ * ---------------------------------------------------------------------- */
+smoe_status w4a16_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
+                              const int32_t* expert_offsets, const int32_t* active,
+                              const int32_t* n_active, const smoe_w4_expert* experts, int T,
+                              int k, int H, int I, int E, int group_size, uint16_t* y_sorted,
+                              void* workspace, size_t workspace_bytes, int32_t* err_word,
+                              void* stream);
+
+/* ------------------------------------------------------------------------
+ * verify_grouped_gemm -- FP16 SwiGLU FFN of the target experts over the
+ * rows grouped by expert: expert-wise verification regrouping ([S1] Key
+ * Contributions 4 and Methodology: the tokens routed to one expert are packed
+ * so per-token matrix-vector products become one matrix-matrix product per
+ * expert; results equal the per-token ordering).  Runs on MFMA with fp32
+ * accumulation; h is rounded to fp16 between the projections.
+ *
+ *   x              fp16 [T, H]
+ *   sorted_token   int32 [rows]  token of each sorted row
+ *   expert_offsets int32 [E+1]
+ *   active/n_active  optional pair (both NULL = scan all E experts)
+ *   experts        device array of E smoe_f16_expert (may point at resident
+ *                  or staging slots)
+ *   expert_mask    optional uint8 [E]; experts with mask 0 are skipped, so
+ *                  cache hits can run before misses arrive ([S1] Key
+ *                  Contributions 3 and Methodology: experts already resident
+ *                  are computed first while the missing ones load)
+ *   rows           number of sorted rows (T*k for routed experts; T for a
+ *                  shared expert run as one group with offsets {0, T})
+ *   y_sorted       fp16 [rows, H] out
+ *   workspace      >= smoe_workspace_bytes(1, T, k, H, I, E) with k = rows/T
+ *                  (rounded up); no zeroing needed.
+ * ---------------------------------------------------------------------- */
+smoe_status verify_grouped_gemm(const uint16_t* x, const int32_t* sorted_token,
+                                const int32_t* expert_offsets, const int32_t* active,
+                                const int32_t* n_active, const smoe_f16_expert* experts,
+                                const uint8_t* expert_mask, int T, int rows, int H, int I,
+                                int E, uint16_t* y_sorted, void* workspace,
+                                size_t workspace_bytes, int32_t* err_word, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_combine -- weighted sum of the chosen experts' outputs plus the shared
+ * expert (the pages leave this step implicit; it is the usual routed-MoE
+ * combine):
+ *   out[t] = fp16( sum_j topk_w[t,j] * y_sorted[pair_pos[t*k+j]]
+ *                  + c_t * shared_out[t] + residual[t] )
+ * summed in fp32 in that order (j increasing), one rounding to fp16.
+ *   shared_out   fp16 [T, H] optional (NULL = no shared term)
+ *   shared_scale fp32 [T]    optional (NULL = 1), c_t
+ *   residual     fp16 [T, H] optional (NULL = none)
+ *   pairs with pair_pos == -1 contribute nothing.
+ *   out          fp16 [T, H]; may alias residual.
+ * ---------------------------------------------------------------------- */
+smoe_status moe_combine(const uint16_t* y_sorted, const int32_t* pair_pos, const float* topk_w,
+                        const uint16_t* shared_out, const float* shared_scale,
+                        const uint16_t* residual, int T, int k, int H, uint16_t* out,
+                        void* stream);
+
+/* ------------------------------------------------------------------------
+ * expert_stage_async -- copy one non-resident expert from page-locked host
+ * memory into a device slot on a side stream and record an event after it
+ * ([S1] Key Contributions 3-4: cache-miss expert loads overlap the compute of
+ * cache hits, using dedicated streams, events and pinned non-blocking copies).
+ *
+ *   dst_device       device destination (bytes long)
+ *   src_pinned_host  host source; must be page-locked (hipHostMalloc or
+ *                    torch pin_memory), else SMOE_ERR_NOT_PINNED
+ *   side_stream      hipStream_t the copy is queued on
+ *   done_event       hipEvent_t recorded on side_stream after the copy
+ *                    (NULL = none); the compute stream waits on it before
+ *                    touching dst.
+ * ---------------------------------------------------------------------- */
+smoe_status expert_stage_async(void* dst_device, const void* src_pinned_host, size_t bytes,
+                               void* side_stream, void* done_event);
+
+/* Workspace size in bytes for which = 0 (w4a16_grouped_ffn) or
+ * 1 (verify_grouped_gemm); 0 for an invalid request. */
+size_t smoe_workspace_bytes(int which, int T, int k, int H, int I, int E);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMOE_H */

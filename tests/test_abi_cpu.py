@@ -1,0 +1,118 @@
+"""The C ABI library loads, exports every entry point declared in
+include/smoe.h, and rejects bad arguments on the host (no GPU needed: these
+calls return before anything touches a device)."""
+import ctypes
+import os
+
+import pytest
+
+import fp16_verify_expert_amd as fve
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fve.LIB_PATH),
+                                reason="libsmoe.so not built")
+
+V = ctypes.c_void_p
+FAKE = V(0x1000)  # never dereferenced: the checks below fail before any use
+
+
+def test_exports_every_header_function():
+    names = fve.header_functions()
+    expected = {"smoe_abi_version", "smoe_last_error", "moe_route_topk", "elb_count",
+                "moe_gather", "w4a16_grouped_ffn", "verify_grouped_gemm", "moe_combine",
+                "expert_stage_async", "smoe_workspace_bytes"}
+    assert set(names) == expected
+    L = ctypes.CDLL(fve.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version():
+    assert fve.lib().smoe_abi_version() == fve.ABI_VERSION
+
+
+def _err():
+    return fve.lib().smoe_last_error().decode()
+
+
+def test_route_validation():
+    L = fve.lib()
+    assert L.moe_route_topk(None, FAKE, None, 1, 256, 8, 2, 0, FAKE, FAKE, None, None) == 1
+    assert "required" in _err()
+    assert L.moe_route_topk(FAKE, FAKE, None, 1, 200, 8, 2, 0, FAKE, FAKE, None, None) == 2
+    assert "H=200" in _err()
+    assert L.moe_route_topk(FAKE, FAKE, None, 1, 256, 8, 9, 0, FAKE, FAKE, None, None) == 2
+    assert L.moe_route_topk(FAKE, FAKE, None, 1, 256, 300, 2, 0, FAKE, FAKE, None, None) == 2
+    assert L.moe_route_topk(FAKE, FAKE, FAKE, 1, 256, 8, 2, 0, FAKE, FAKE, None, None) == 1
+    assert L.moe_route_topk(V(0x1002), FAKE, None, 1, 256, 8, 2, 0, FAKE, FAKE, None, None) == 2
+    assert "aligned" in _err()
+    # T == 0 is a no-op and succeeds without a device
+    assert L.moe_route_topk(FAKE, FAKE, None, 0, 256, 8, 2, 0, FAKE, FAKE, None, None) == 0
+    assert _err() == ""
+
+
+def test_elb_validation():
+    L = fve.lib()
+    assert L.elb_count(None, 1, 2, 8, 0, 1, FAKE, None, None) == 1
+    assert L.elb_count(FAKE, 1, 2, 8, 1, 1, FAKE, None, None) == 2      # layer >= L
+    assert L.elb_count(FAKE, 1, 9, 8, 0, 1, FAKE, None, None) == 2      # k > E
+    assert L.elb_count(FAKE, 0, 2, 8, 0, 1, FAKE, None, None) == 0
+
+
+def test_gather_validation():
+    L = fve.lib()
+    assert L.moe_gather(FAKE, 1, 2, 8, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 1
+    assert L.moe_gather(FAKE, 1 << 20, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 2
+    assert L.moe_gather(FAKE, 1, 3, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 2
+
+
+def test_w4a16_validation():
+    L = fve.lib()
+    args = [FAKE] * 6
+    assert L.w4a16_grouped_ffn(*args, 1, 2, 256, 512, 8, 64, FAKE, FAKE, 1 << 20, None, None) == 3
+    assert "group_size" in _err()
+    assert L.w4a16_grouped_ffn(*args, 1, 2, 256, 500, 8, 128, FAKE, FAKE, 1 << 20, None, None) == 2
+    need = L.smoe_workspace_bytes(0, 4, 2, 256, 512, 8)
+    assert need > 0
+    assert L.w4a16_grouped_ffn(*args, 4, 2, 256, 512, 8, 128, FAKE, FAKE, need - 1, None,
+                               None) == 6
+    assert L.w4a16_grouped_ffn(*args, 4, 2, 256, 512, 8, 128, FAKE, None, need, None, None) == 6
+    assert L.w4a16_grouped_ffn(*args[:5], None, 4, 2, 256, 512, 8, 128, FAKE, FAKE, need, None,
+                               None) == 1
+    assert L.w4a16_grouped_ffn(*args, 0, 2, 256, 512, 8, 128, FAKE, None, 0, None, None) == 0
+
+
+def test_verify_validation():
+    L = fve.lib()
+    a = [FAKE, FAKE, FAKE]
+    assert L.verify_grouped_gemm(*a, FAKE, None, FAKE, None, 9, 36, 2048, 1408, 60, FAKE, FAKE,
+                                 1 << 30, None, None) == 1
+    assert L.verify_grouped_gemm(*a, None, None, FAKE, None, 9, 36, 2048, 1400, 60, FAKE, FAKE,
+                                 1 << 30, None, None) == 2
+    need = L.smoe_workspace_bytes(1, 9, 4, 2048, 1408, 60)
+    assert need >= 36 * 1408 * 2
+    assert L.verify_grouped_gemm(*a, None, None, FAKE, None, 9, 36, 2048, 1408, 60, FAKE, FAKE,
+                                 need - 1, None, None) == 6
+    assert L.verify_grouped_gemm(*a, None, None, FAKE, None, 9, 0, 2048, 1408, 60, FAKE, None, 0,
+                                 None, None) == 0
+
+
+def test_combine_validation():
+    L = fve.lib()
+    assert L.moe_combine(FAKE, FAKE, None, None, None, None, 1, 2, 256, FAKE, None) == 1
+    assert L.moe_combine(FAKE, FAKE, FAKE, None, None, None, 70000, 2, 256, FAKE, None) == 2
+    assert L.moe_combine(FAKE, FAKE, FAKE, V(0x1008), None, None, 1, 2, 256, FAKE, None) == 2
+    assert L.moe_combine(FAKE, FAKE, FAKE, None, None, None, 0, 2, 256, FAKE, None) == 0
+
+
+def test_stage_validation():
+    L = fve.lib()
+    assert L.expert_stage_async(None, FAKE, 16, None, None) == 1
+    assert L.expert_stage_async(FAKE, FAKE, 0, None, None) == 0
+
+
+def test_workspace_sizes():
+    L = fve.lib()
+    assert L.smoe_workspace_bytes(0, 1, 6, 2048, 1408, 64) > 0
+    assert L.smoe_workspace_bytes(0, 1, 6, 2000, 1408, 64) == 0
+    assert L.smoe_workspace_bytes(2, 1, 6, 2048, 1408, 64) == 0
+    assert L.smoe_workspace_bytes(1, 17, 2, 4096, 6400, 16) >= 34 * 6400 * 2

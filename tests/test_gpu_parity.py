@@ -1,0 +1,344 @@
+"""GPU parity: every entry point of libsmoe.so against the CPU oracle on the
+same seeded inputs.  Integer outputs (ids, counters, maps) must match exactly;
+FP16 outputs within normalised L2 5e-3 and max |err| 2e-2; routing weights
+within 1e-5 relative."""
+import numpy as np
+import pytest
+import torch
+
+import fp16_verify_expert_amd as fve
+import oracle
+import synth
+from gpu_util import (W_RTOL, Layer, assert_fp16_close, dev, host, run_layer, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    fve.lib()
+    torch.cuda.init()
+
+
+def _err():
+    return torch.zeros(1, dtype=torch.int32, device="cuda")
+
+
+# ---------------------------------------------------------------- S1 ----
+
+ROUTE_CASES = [(synth.TINY, 4), (synth.TINY, 1), (synth.DS, 1), (synth.DS, 16), (synth.QWEN, 9),
+               (synth.QWEN, 17), (synth.PHI, 1), (synth.PHI, 17), (synth.DS, 257)]
+
+
+@pytest.mark.parametrize("shape,T", ROUTE_CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_route_topk(shape, T):
+    say(f"route {shape.name} T={T}")
+    wr = synth.router(shape)
+    x = synth.tokens(shape, T, step=3)
+    sh = synth.shared_expert(shape)
+    gvec = None if sh is None else sh.get("gate")
+    ref = oracle.route_topk(x, wr, shape.k, shape.renormalize, gvec)
+    ids, w, gate = fve.moe_route_topk(dev(x), dev(wr), shape.k, shape.renormalize,
+                                      None if gvec is None else dev(gvec))
+    assert np.array_equal(host(ids), ref["ids"])
+    assert np.allclose(host(w), ref["weights"], rtol=W_RTOL, atol=1e-7)
+    if gvec is not None:
+        assert np.allclose(host(gate), ref["gate"], rtol=W_RTOL, atol=1e-7)
+
+
+def test_route_renormalize_and_ties():
+    s = synth.TINY
+    wr = synth.router(s)
+    x = np.zeros((3, s.H), np.float16)
+    ids, w, _ = fve.moe_route_topk(dev(x), dev(wr), 3)
+    assert host(ids).tolist() == [[0, 1, 2]] * 3
+    assert np.allclose(host(w), 1.0 / s.E, rtol=1e-6)
+    x = synth.tokens(s, 5)
+    ref = oracle.route_topk(x, wr, 3, renormalize=True)
+    ids, w, _ = fve.moe_route_topk(dev(x), dev(wr), 3, True)
+    assert np.array_equal(host(ids), ref["ids"])
+    assert np.allclose(host(w), ref["weights"], rtol=W_RTOL)
+    # k == E: the full ranking
+    ref = oracle.route_topk(x, wr, s.E)
+    ids, w, _ = fve.moe_route_topk(dev(x), dev(wr), s.E)
+    assert np.array_equal(host(ids), ref["ids"])
+
+
+def test_route_pinned_order_cases():
+    # the hand cases of the oracle pins, through the kernel: 2^24 + ones
+    for H, ones, want in ((512, range(1, 8), 2.0 ** 24), (1024, (512, 513), 2.0 ** 24),
+                          (512, (8, 24), 2.0 ** 24 + 2)):
+        x = np.zeros((1, H), np.float16)
+        w = np.zeros((2, H), np.float16)
+        x[0, 0] = w[0, 0] = 4096.0
+        for h in ones:
+            x[0, h] = w[0, h] = 1.0
+        w[1, 0] = 4096.0            # expert 1 logit: exactly 2^24
+        ids, wt, _ = fve.moe_route_topk(dev(x), dev(w), 2)
+        # expert 0 wins iff its logit rounds above 2^24; equal -> lower id
+        assert host(ids)[0].tolist() == [0, 1]
+        p0 = host(wt)[0, 0]
+        expect = 1.0 / (1.0 + np.exp(2.0 ** 24 - want))
+        assert abs(p0 - expect) < 1e-6
+
+
+# ---------------------------------------------------------------- S2 ----
+
+def test_elb_count_accumulates():
+    s = synth.QWEN_CHUNK
+    wr = synth.router(s)
+    L = 24
+    counters = torch.zeros((L, s.E), dtype=torch.int32, device="cuda")
+    ref = np.zeros((L, s.E), np.int32)
+    err = _err()
+    for step in range(16):
+        for layer in (0, 5, 23):
+            x = synth.tokens(s, 1, step=step, layer=layer)
+            r = oracle.route_topk(x, wr, s.k)
+            ids, _, _ = fve.moe_route_topk(dev(x), dev(wr), s.k)
+            fve.elb_count(ids, s.E, layer, counters, err)
+            ref = oracle.elb_update(ref, r["ids"], layer)
+    c = host(counters)
+    assert np.array_equal(c, ref)
+    assert c[0].sum() == 16 * s.k and c[1].sum() == 0
+    assert int(host(err)[0]) == 0
+
+
+def test_elb_count_bad_ids_flagged():
+    ids = dev(np.array([[0, 7], [8, -1], [3, 3]], np.int32))
+    counters = torch.zeros((2, 8), dtype=torch.int32, device="cuda")
+    err = _err()
+    fve.elb_count(ids, 8, 1, counters, err)
+    assert host(counters)[1].tolist() == [1, 0, 0, 2, 0, 0, 0, 1]
+    assert int(host(err)[0]) & fve.SMOE_DERR_BAD_ID
+
+
+# ---------------------------------------------------------------- S3 ----
+
+GATHER_CASES = [(4, 2, 8), (1, 6, 64), (16, 6, 64), (17, 4, 60), (9, 4, 60), (17, 2, 16),
+                (300, 8, 64), (2000, 2, 16), (1, 1, 1), (5, 256, 256)]
+
+
+@pytest.mark.parametrize("T,k,E", GATHER_CASES)
+def test_gather_maps(T, k, E):
+    rng = np.random.default_rng(T * 1000 + k * 10 + E)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    if T == 2000:  # heavily skewed: most pairs on two experts
+        ids[:, 0] = rng.integers(0, 2, size=T)
+        ids[:, 1] = np.where(ids[:, 0] == 0, 1, 0)
+    ref = oracle.gather_maps(ids, E)
+    m = fve.moe_gather(dev(ids), E, _err())
+    n = T * k
+    for key in ("offsets", "active"):
+        assert np.array_equal(host(m[key]), ref[key]), key
+    for key in ("sorted_token", "sorted_pair", "pair_pos"):
+        assert np.array_equal(host(m[key])[:n], ref[key]), key
+    assert int(host(m["n_active"])[0]) == int(ref["n_active"])
+
+
+def test_gather_bad_ids_and_empty():
+    ids = np.array([[1, 9], [0, -3], [1, 2]], np.int32)
+    err = _err()
+    m = fve.moe_gather(dev(ids), 4, err)
+    ref = oracle.gather_maps(ids, 4)
+    assert host(m["offsets"]).tolist() == ref["offsets"].tolist()
+    assert host(m["pair_pos"]).tolist() == ref["pair_pos"].tolist()
+    assert host(m["sorted_pair"]).tolist() == ref["sorted_pair"].tolist()
+    assert int(host(err)[0]) & fve.SMOE_DERR_BAD_ID
+    m = fve.moe_gather(torch.zeros((0, 2), dtype=torch.int32, device="cuda"), 4)
+    assert host(m["offsets"]).tolist() == [0] * 5
+    assert int(host(m["n_active"])[0]) == 0
+    assert host(m["active"]).tolist() == [-1] * 4
+
+
+# ------------------------------------------------------------- S4 / S6 ----
+
+_layers = {}
+
+
+def _layer(shape, Ts, steps=(0,), int4=True, f16=True):
+    key = (shape.name, Ts, steps, int4, f16)
+    if key not in _layers:
+        xs = [synth.tokens(shape, T, step=st) for T in Ts for st in steps]
+        _layers[key] = Layer(shape, xs, int4=int4, f16=f16)
+    return _layers[key]
+
+
+W4_CASES = [(synth.TINY, 4), (synth.TINY, 40), (synth.DS, 1), (synth.DS, 4), (synth.DS, 16),
+            (synth.PHI, 1), (synth.QWEN, 1)]
+
+
+@pytest.mark.parametrize("shape,T", W4_CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_w4a16_grouped_ffn(shape, T):
+    say(f"w4a16 {shape.name} T={T}")
+    L = _layer(shape, (T,), f16=False)
+    x = synth.tokens(shape, T, step=0)
+    r = oracle.route_topk(x, L.router, shape.k)
+    maps = oracle.gather_maps(r["ids"], shape.E)
+    ref = oracle.grouped_ffn(x, maps, L.int4, "int4")
+    err = _err()
+    dx = dev(x)
+    ids, _, _ = fve.moe_route_topk(dx, L.d_router, shape.k)
+    gm = fve.moe_gather(ids, shape.E, err)
+    ws = fve.new_workspace(0, T, shape.k, shape.H, shape.I, shape.E)
+    y = fve.w4a16_grouped_ffn(dx, gm, L.t4, T, shape.k, shape.H, shape.I, shape.E, ws,
+                              err_word=err)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) == 0
+    rows = T * shape.k
+    st = assert_fp16_close(host(y)[:rows], ref, f"w4a16 {shape.name} T={T}")
+    say(f"  l2={st['l2']:.2e} maxabs={st['maxabs']:.2e}")
+    # deterministic: a second call gives the same bits; counters reset
+    y2 = fve.w4a16_grouped_ffn(dx, gm, L.t4, T, shape.k, shape.H, shape.I, shape.E, ws,
+                               err_word=err)
+    assert torch.equal(y[:rows], y2[:rows])
+
+
+VERIFY_CASES = [(synth.TINY, 17), (synth.TINY, 40), (synth.QWEN, 9), (synth.PHI, 17),
+                (synth.DS, 16)]
+
+
+@pytest.mark.parametrize("shape,T", VERIFY_CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_verify_grouped_gemm(shape, T):
+    say(f"verify {shape.name} T={T}")
+    L = _layer(shape, (T,), int4=False)
+    x = synth.tokens(shape, T, step=0)
+    r = oracle.route_topk(x, L.router, shape.k)
+    maps = oracle.gather_maps(r["ids"], shape.E)
+    ref = oracle.grouped_ffn(x, maps, L.f16, "f16")
+    err = _err()
+    dx = dev(x)
+    ids, _, _ = fve.moe_route_topk(dx, L.d_router, shape.k)
+    gm = fve.moe_gather(ids, shape.E, err)
+    ws = fve.new_workspace(1, T, shape.k, shape.H, shape.I, shape.E)
+    rows = T * shape.k
+    y = fve.verify_grouped_gemm(dx, gm["sorted_token"], gm["offsets"], L.t16, T, rows, shape.H,
+                                shape.I, shape.E, ws, active=gm["active"],
+                                n_active=gm["n_active"], err_word=err)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) == 0
+    st = assert_fp16_close(host(y)[:rows], ref, f"verify {shape.name} T={T}")
+    say(f"  l2={st['l2']:.2e} maxabs={st['maxabs']:.2e}")
+    # the regrouped result equals the per-token GEMV ordering
+    if shape.name in ("qwen15_moe", "tiny"):
+        pt = oracle.per_token_ffn(x, r["ids"], L.f16, "f16")
+        yy = host(y).astype(np.float64)
+        per = np.stack([yy[maps["pair_pos"][t * shape.k:(t + 1) * shape.k]] for t in range(T)])
+        assert_fp16_close(per, pt, "verify vs per-token ordering")
+    # without the active list (scan all E) the result is bit-identical
+    y2 = fve.verify_grouped_gemm(dx, gm["sorted_token"], gm["offsets"], L.t16, T, rows, shape.H,
+                                 shape.I, shape.E, ws, err_word=err)
+    assert torch.equal(y[:rows], y2[:rows])
+
+
+def test_verify_expert_mask_hits_then_misses():
+    s, T = synth.QWEN, 9
+    L = _layer(s, (T,), int4=False)
+    x = dev(synth.tokens(s, T, step=0))
+    ids, _, _ = fve.moe_route_topk(x, L.d_router, s.k)
+    gm = fve.moe_gather(ids, s.E)
+    ws = fve.new_workspace(1, T, s.k, s.H, s.I, s.E)
+    rows = T * s.k
+    full = fve.verify_grouped_gemm(x, gm["sorted_token"], gm["offsets"], L.t16, T, rows, s.H,
+                                   s.I, s.E, ws, active=gm["active"], n_active=gm["n_active"])
+    hit = torch.zeros(s.E, dtype=torch.uint8, device="cuda")
+    hit[torch.tensor(L.touched[::2])] = 1
+    miss = 1 - hit
+    y = torch.full_like(full, float("nan"))
+    fve.verify_grouped_gemm(x, gm["sorted_token"], gm["offsets"], L.t16, T, rows, s.H, s.I, s.E,
+                            ws, active=gm["active"], n_active=gm["n_active"], expert_mask=hit,
+                            y_sorted=y)
+    fve.verify_grouped_gemm(x, gm["sorted_token"], gm["offsets"], L.t16, T, rows, s.H, s.I, s.E,
+                            ws, active=gm["active"], n_active=gm["n_active"], expert_mask=miss,
+                            y_sorted=y)
+    assert torch.equal(y[:rows], full[:rows])
+
+
+def test_null_expert_flagged():
+    s, T = synth.TINY, 4
+    L = _layer(s, (T,))
+    x = dev(synth.tokens(s, T, step=0))
+    ids, _, _ = fve.moe_route_topk(x, L.d_router, s.k)
+    gm = fve.moe_gather(ids, s.E)
+    e0 = L.touched[0]
+    t4 = L.t4.clone()
+    t4[e0] = 0
+    t16 = L.t16.clone()
+    t16[e0] = 0
+    for kind in ("int4", "f16"):
+        err = _err()
+        if kind == "int4":
+            ws = fve.new_workspace(0, T, s.k, s.H, s.I, s.E)
+            fve.w4a16_grouped_ffn(x, gm, t4, T, s.k, s.H, s.I, s.E, ws, err_word=err)
+        else:
+            ws = fve.new_workspace(1, T, s.k, s.H, s.I, s.E)
+            fve.verify_grouped_gemm(x, gm["sorted_token"], gm["offsets"], t16, T, T * s.k, s.H,
+                                    s.I, s.E, ws, active=gm["active"], n_active=gm["n_active"],
+                                    err_word=err)
+        assert int(host(err)[0]) & fve.SMOE_DERR_NULL_EXPERT
+
+
+# ---------------------------------------------------------------- S5 ----
+
+@pytest.mark.parametrize("shape,T", [(synth.DS, 1), (synth.DS, 16), (synth.QWEN, 9),
+                                     (synth.QWEN, 17)], ids=lambda v: getattr(v, "name", str(v)))
+def test_shared_expert(shape, T):
+    sh = synth.shared_expert(shape)
+    x = synth.tokens(shape, T, step=1)
+    ref = oracle.expert_ffn_f16(x, sh["w13"], sh["w2"])
+    from gpu_util import upload_f16
+    tab, keep = upload_f16([(sh["w13"], sh["w2"])])
+    dx = dev(x)
+    iota = torch.arange(T, dtype=torch.int32, device="cuda")
+    offs = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    ws = fve.new_workspace(1, T, 1, shape.H, shape.shared_I, 1)
+    y = fve.verify_grouped_gemm(dx, iota, offs, tab, T, T, shape.H, shape.shared_I, 1, ws)
+    assert_fp16_close(host(y)[:T], ref, f"shared {shape.name} T={T}")
+
+
+# ---------------------------------------------------------------- S7 ----
+
+def test_combine():
+    rng = np.random.default_rng(0)
+    T, k, H = 9, 4, 2048
+    y = rng.standard_normal((T * k, H)).astype(np.float16)
+    pp = rng.permutation(T * k).astype(np.int32)
+    pp[5] = -1
+    w = rng.random((T, k)).astype(np.float32)
+    sh = rng.standard_normal((T, H)).astype(np.float16)
+    c = rng.random(T).astype(np.float32)
+    res = rng.standard_normal((T, H)).astype(np.float16)
+    ref = oracle.combine(y, pp, w.astype(np.float64), sh, c, res)
+    out = fve.moe_combine(dev(y), dev(pp), dev(w), dev(sh), dev(c), dev(res))
+    assert_fp16_close(host(out), ref, "combine", l2=1e-3, maxabs=4e-3)
+    ref1 = oracle.combine(y, pp, w.astype(np.float64))
+    out1 = fve.moe_combine(dev(y), dev(pp), dev(w))
+    assert_fp16_close(host(out1), ref1, "combine plain", l2=1e-3, maxabs=4e-3)
+    # k = 1, weight 1: a permutation copy, exact
+    pp1 = rng.permutation(T).astype(np.int32)
+    out2 = fve.moe_combine(dev(y[:T]), dev(pp1), dev(np.ones((T, 1), np.float32)))
+    assert np.array_equal(host(out2), y[:T][pp1])
+
+
+# ----------------------------------------------------------- whole layer ----
+
+LAYER_CASES = [(synth.TINY, 4, "int4"), (synth.DS, 1, "int4"), (synth.DS, 16, "int4"),
+               (synth.QWEN, 9, "f16"), (synth.PHI, 1, "int4"), (synth.PHI, 17, "f16")]
+
+
+@pytest.mark.parametrize("shape,T,kind", LAYER_CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_layer_end_to_end(shape, T, kind):
+    say(f"layer {shape.name} T={T} {kind}")
+    L = _layer(shape, (T,), int4=(kind == "int4"), f16=(kind == "f16"))
+    x = synth.tokens(shape, T, step=0)
+    experts = L.int4 if kind == "int4" else L.f16
+    shared = None if L.shared is None else dict(w13=L.shared["w13"], w2=L.shared["w2"],
+                                                 gate=L.shared.get("gate"))
+    ref = oracle.moe_layer(x, L.router, shape.k, experts, kind, shared)
+    err = _err()
+    got = run_layer(L, dev(x), kind, err)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) == 0
+    assert np.array_equal(host(got["ids"]), ref["route"]["ids"])
+    st = assert_fp16_close(host(got["out"]), ref["out"], f"layer {shape.name} T={T} {kind}")
+    say(f"  l2={st['l2']:.2e} maxabs={st['maxabs']:.2e}")
