@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Throughput of the routed-expert MoE FFN path on one MI355X.
+
+Default workload: the Phi-3.5-MoE-shaped layer (hidden 4096, 16 experts,
+top-2, SwiGLU intermediate 6400, no shared expert).  One step is one INT4
+draft decode step (T = 1: route, ELB count, gather, W4A16 FFN, combine)
+followed by one FP16 verification of K+1 = 17 tokens (route, gather,
+regrouped verify FFN, combine), every step through the C ABI of libsmoe.so
+on seeded synthetic inputs already resident in HBM.  Steps cycle over a pool
+of 8 seeded token batches.
+
+Printed JSON line (rank 0):
+  value       draft INT4 weight GB/s: INT4 bytes (packed codes + fp16 scales
+              + packed zeros) of the experts each draft step touches, over
+              the wall time of the draft half of the step (HIP events around
+              all of its calls)
+  verify      the verify half: TFLOP/s (2 x rows x 3 H I), % of FP16 MFMA
+              peak, and its FP16 weight GB/s
+  roofline    the dominant kernel of the step (verify_grouped_gemm, HBM
+              bound): touched FP16 weight bytes per call / average call time
+  roofline_draft  the same for w4a16_grouped_ffn (INT4 bytes)
+  cpu_baseline    the CPU oracle on a bounded sample of draft steps
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFS = 2516.6   # dense FP16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+POOL = 8                     # distinct seeded batches
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-sample", type=int, default=6,
+                    help="draft steps of the oracle timed for cpu_baseline (0 = skip)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the path is single-GPU and no multi-GPU figure is produced.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp16_verify_expert_amd as fve
+    import synth
+
+    fve.lib()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda")
+    s = synth.PHI
+    T_D, T_V = 1, 17
+    H, I, E, k = s.H, s.I, s.E, s.k
+
+    # ---- weights: all experts resident (INT4 draft + FP16 target) ----
+    t0 = time.perf_counter()
+    layer = synth.make_layer(s)
+    gen_s = time.perf_counter() - t0
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    w4 = [{key: tuple(up(t) for t in ex[key]) for key in ("w13", "w2")} for ex in layer["int4"]]
+    w16 = [(up(a), up(b)) for a, b in layer["f16"]]
+    t4 = fve.w4_expert_table(w4)
+    t16 = fve.f16_expert_table(w16)
+    router = up(layer["router"])
+    xs_d = [up(synth.tokens(s, T_D, step=i)) for i in range(POOL)]
+    xs_v = [up(synth.tokens(s, T_V, step=100 + i)) for i in range(POOL)]
+
+    # ---- preallocated buffers (no allocation inside the timed loop) ----
+    def bufs(T):
+        n = T * k
+        return dict(ids=torch.empty((T, k), dtype=torch.int32, device=dev),
+                    w=torch.empty((T, k), dtype=torch.float32, device=dev),
+                    maps=dict(offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                              sorted_token=torch.empty(n, dtype=torch.int32, device=dev),
+                              sorted_pair=torch.empty(n, dtype=torch.int32, device=dev),
+                              pair_pos=torch.empty(n, dtype=torch.int32, device=dev),
+                              active=torch.empty(E, dtype=torch.int32, device=dev),
+                              n_active=torch.empty(1, dtype=torch.int32, device=dev)),
+                    y=torch.empty((n, H), dtype=torch.float16, device=dev),
+                    out=torch.empty((T, H), dtype=torch.float16, device=dev))
+    bd, bv = bufs(T_D), bufs(T_V)
+    ws_d = fve.new_workspace(0, T_D, k, H, I, E)
+    ws_v = fve.new_workspace(1, T_V, k, H, I, E)
+    counters = torch.zeros((1, E), dtype=torch.int32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def draft(i, ev=None):
+        x = xs_d[i % POOL]
+        fve.moe_route_topk(x, router, k, topk_ids=bd["ids"], topk_w=bd["w"])
+        fve.elb_count(bd["ids"], E, 0, counters, err)
+        fve.moe_gather(bd["ids"], E, err, out=bd["maps"])
+        if ev: ev[0].record()
+        fve.w4a16_grouped_ffn(x, bd["maps"], t4, T_D, k, H, I, E, ws_d, y_sorted=bd["y"],
+                              err_word=err)
+        if ev: ev[1].record()
+        fve.moe_combine(bd["y"], bd["maps"]["pair_pos"], bd["w"], out=bd["out"])
+
+    def verify(i, ev=None):
+        x = xs_v[i % POOL]
+        fve.moe_route_topk(x, router, k, topk_ids=bv["ids"], topk_w=bv["w"])
+        fve.moe_gather(bv["ids"], E, err, out=bv["maps"])
+        if ev: ev[0].record()
+        fve.verify_grouped_gemm(x, bv["maps"]["sorted_token"], bv["maps"]["offsets"], t16, T_V,
+                                T_V * k, H, I, E, ws_v, active=bv["maps"]["active"],
+                                n_active=bv["maps"]["n_active"], y_sorted=bv["y"], err_word=err)
+        if ev: ev[1].record()
+        fve.moe_combine(bv["y"], bv["maps"]["pair_pos"], bv["w"], out=bv["out"])
+
+    # ---- per-batch algorithmic work (routing is deterministic) ----
+    touched_d, touched_v = [], []
+    for i in range(POOL):
+        draft(i)
+        verify(i)
+        torch.cuda.synchronize()
+        touched_d.append(int(bd["maps"]["n_active"].item()))
+        touched_v.append(int(bv["maps"]["n_active"].item()))
+    assert int(err.item()) == 0, "device error word set"
+    b4 = s.int4_bytes_per_expert
+    b16 = s.f16_bytes_per_expert
+    flop_v = lambda i: 2.0 * T_V * k * 3 * H * I
+
+    for i in range(args.warmup):
+        draft(i)
+        verify(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region ----
+    K = args.steps
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    ph = [(mk(), mk(), mk()) for _ in range(K)]            # draft start / verify start / end
+    kd = [(mk(), mk()) for _ in range(K)]                  # w4a16 call
+    kv = [(mk(), mk()) for _ in range(K)]                  # verify call
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for st in range(K):
+        i = args.warmup + st
+        ph[st][0].record()
+        draft(i, kd[st])
+        ph[st][1].record()
+        verify(i, kv[st])
+        ph[st][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    assert int(err.item()) == 0, "device error word set"
+
+    idx = [(args.warmup + st) % POOL for st in range(K)]
+    draft_ms = sum(ph[st][0].elapsed_time(ph[st][1]) for st in range(K))
+    verify_ms = sum(ph[st][1].elapsed_time(ph[st][2]) for st in range(K))
+    w4_ms = [kd[st][0].elapsed_time(kd[st][1]) for st in range(K)]
+    vg_ms = [kv[st][0].elapsed_time(kv[st][1]) for st in range(K)]
+    bytes_d = sum(touched_d[i] * b4 for i in idx)
+    bytes_v = sum(touched_v[i] * b16 for i in idx)
+    flops_v = sum(flop_v(i) for i in idx)
+    step_ms = (draft_ms + verify_ms) / K
+
+    value = bytes_d / (draft_ms * 1e-3) / 1e9
+    v_tfs = flops_v / (verify_ms * 1e-3) / 1e12
+    v_gbs = bytes_v / (verify_ms * 1e-3) / 1e9
+    rv_ach = bytes_v / (sum(vg_ms) * 1e-3) / 1e9
+    rd_ach = bytes_d / (sum(w4_ms) * 1e-3) / 1e9
+    prof_dir = os.path.join(ROOT, "profiles")
+
+    def pmc_traffic(name):
+        """HBM bytes per call from the committed rocprofv3 --pmc summary, when
+        it was taken on the current kernels (else None)."""
+        p = os.path.join(prof_dir, "pmc_traffic.json")
+        if not os.path.exists(p):
+            return None
+        try:
+            with open(p) as f:
+                d = json.load(f)
+            return d.get(name)
+        except Exception:
+            return None
+
+    res = {
+        "metric": "MoE-layer INT4 draft weight GB/s (% HBM peak); verify TFLOP/s (% MFMA)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4-w/fp16-a (draft), fp16 (verify); fp32 accumulate",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) tokens; RTN GPTQ INT4 g128 draft)",
+        "config": {"workload": "phi35_moe_layer: H=4096 E=16 top-2 I=6400; draft T=1 INT4 + "
+                               "verify K+1=17 FP16; all experts HBM-resident",
+                   "draft_tokens": T_D, "verify_tokens": T_V, "batch_pool": POOL},
+        "draft": {"ms": round(draft_ms / K, 4), "gbps": round(value, 2),
+                  "frac_hbm": round(value / HBM_PEAK_GBS, 4),
+                  "touched_experts_avg": round(sum(touched_d[i] for i in idx) / K, 3),
+                  "int4_bytes_avg": round(bytes_d / K)},
+        "verify": {"ms": round(verify_ms / K, 4), "tflops": round(v_tfs, 3),
+                   "frac_mfma": round(v_tfs / MFMA_F16_PEAK_TFS, 5), "gbps": round(v_gbs, 2),
+                   "frac_hbm": round(v_gbs / HBM_PEAK_GBS, 4),
+                   "touched_experts_avg": round(sum(touched_v[i] for i in idx) / K, 3),
+                   "f16_bytes_avg": round(bytes_v / K)},
+        "roofline": {"kernel": "verify_grouped_gemm (gate/up + down launches)", "bound": "hbm",
+                     "achieved": round(rv_ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(rv_ach / HBM_PEAK_GBS, 4),
+                     "avg_us": round(1e3 * sum(vg_ms) / K, 3),
+                     "traffic": pmc_traffic("verify_grouped_gemm")},
+        "roofline_draft": {"kernel": "w4a16_grouped_ffn (gate/up + down launches)",
+                           "bound": "hbm", "achieved": round(rd_ach, 2), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(rd_ach / HBM_PEAK_GBS, 4),
+                           "avg_us": round(1e3 * sum(w4_ms) / K, 3),
+                           "traffic": pmc_traffic("w4a16_grouped_ffn")},
+        "host_wall_s": round(wall, 4),
+        "gen_s": round(gen_s, 2),
+    }
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    if args.cpu_sample > 0:
+        res["cpu_baseline"] = cpu_baseline(layer, s, args.cpu_sample)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(layer, s, n):
+    """The oracle (as it stands) on n draft steps of the same workload."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    nbytes = 0
+    t0 = time.perf_counter()
+    for i in range(n):
+        x = synth.tokens(s, 1, step=i)
+        r = oracle.route_topk(x, layer["router"], s.k)
+        m = oracle.gather_maps(r["ids"], s.E)
+        y = oracle.grouped_ffn(x, m, layer["int4"], "int4")
+        oracle.combine(y, m["pair_pos"], r["weights"])
+        nbytes += int(m["n_active"]) * s.int4_bytes_per_expert
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{n} INT4 draft steps (T=1, route+gather+dequant+fp64 FFN+combine) of the "
+                      f"phi35 layer in {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

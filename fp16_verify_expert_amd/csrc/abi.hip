@@ -167,6 +167,8 @@ smoe_status w4a16_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
     REQUIRE(group_size == 128, SMOE_ERR_UNSUPPORTED,
             "w4a16_grouped_ffn: group_size=%d (only 128 is supported)", group_size);
     REQUIRE((long long)T * k <= kMaxPairs, SMOE_ERR_SHAPE, "w4a16_grouped_ffn: T*k exceeds 2^20");
+    REQUIRE(smoe::w4a16_shape_supported(H, I), SMOE_ERR_SHAPE,
+            "w4a16_grouped_ffn: H=%d, I=%d (each must be <= 16384)", H, I);
     REQUIRE(aligned(x, 16), SMOE_ERR_SHAPE, "w4a16_grouped_ffn: x must be 16-byte aligned");
     if (T == 0) return ok();
     const size_t need = smoe::w4a16_workspace_bytes(T, k, H, I, E);

@@ -16,6 +16,15 @@ typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 SMOE_DEV float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 SMOE_DEV uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }  // RNE
 
+// Pointers read from descriptor tables are generic; casting them to the
+// global address space lets the compiler use global (not flat) loads.
+template <typename T>
+using gptr = const __attribute__((address_space(1))) T*;
+template <typename T>
+SMOE_DEV gptr<T> as_global(const T* p) {
+    return (gptr<T>)p;
+}
+
 SMOE_DEV void flag_error(int32_t* err, int32_t bit) {
     if (err) atomicOr(err, bit);
 }
@@ -40,6 +49,7 @@ hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, cons
                             const smoe_w4_expert* experts, int T, int k, int H, int I, int E,
                             uint16_t* y, void* ws, int32_t* err, hipStream_t s);
 size_t w4a16_workspace_bytes(int T, int k, int H, int I, int E);
+bool w4a16_shape_supported(int H, int I);
 hipError_t launch_verify_ffn(const uint16_t* x, const int32_t* sorted_token, const int32_t* off,
                              const int32_t* active, const int32_t* n_active,
                              const smoe_f16_expert* experts, const uint8_t* mask, int T, int rows,

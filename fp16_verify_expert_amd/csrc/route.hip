@@ -18,7 +18,7 @@
 
 namespace {
 
-constexpr int kRouteThreads = 512;  // 8 waves; wave w takes experts w, w+8, ...
+constexpr int kRouteThreads = 1024;  // 16 waves; wave w takes experts w, w+16, ...
 
 __device__ __forceinline__ float acc_chunk(float s, uint4 xv, uint4 wv) {
     const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
@@ -38,11 +38,27 @@ __device__ __forceinline__ float acc_chunk(float s, uint4 xv, uint4 wv) {
 }
 
 // Pinned-order dot product of one fp16 row of x with one fp16 row of w,
-// evaluated by a whole wave; every lane returns the same value.
+// evaluated by a whole wave; every lane returns the same value.  Each lane
+// first requests up to 8 of its chunks, then adds them in increasing order.
 __device__ __forceinline__ float pinned_dot(const uint4* __restrict__ xr,
                                             const uint4* __restrict__ wrow, int nch, int lane) {
     float s = 0.0f;
-    for (int c = lane; c < nch; c += 64) s = acc_chunk(s, xr[c], wrow[c]);
+    for (int c0 = 0; c0 < nch; c0 += 64 * 8) {
+        uint4 xv[8], wv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int c = c0 + lane + 64 * u;
+            if (c < nch) {
+                xv[u] = xr[c];
+                wv[u] = wrow[c];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int c = c0 + lane + 64 * u;
+            if (c < nch) s = acc_chunk(s, xv[u], wv[u]);
+        }
+    }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) s = s + __shfl_xor(s, d);
     return s;

@@ -12,40 +12,45 @@
 // GEMV: every packed byte is read from HBM once, so the design is about bytes
 // in flight and VALU cost per weight, not matrix cores.
 //
-// Work decomposition.  A workgroup (4 waves) owns one (touched expert, block
-// of 256 weight columns, range of 4 K-groups).  Lane l of a wave reads 16
-// bytes = 4 adjacent columns of one packed row, so a wave load is 1 KB of
-// contiguous qweight (two 512-byte runs in the gate/up projection, whose block
-// is 128 gate columns next to the matching 128 up columns).  Each wave streams
-// whole 128-row groups (16 packed rows, 16 loads in flight per lane).
+// Work decomposition.  A workgroup owns one (touched expert, block of NB
+// weight columns) over the whole reduction, so no workgroup ever waits for
+// another.  Inside a wave, LPR lanes share one packed row: lane q of the
+// group reads 16 bytes = 4 adjacent columns, so a wave load is RPL = 64/LPR
+// rows of 4*LPR columns (64- or 128-byte runs per row).  The RPL lane groups
+// of every wave ("slots") each take whole 128-K quantisation groups, round
+// robin, streaming a group's 16 packed rows with 16 loads in flight per lane;
+// latency is hidden by the other waves resident on the SIMD.
+// In the gate/up projection a block is NB/2 gate columns next to the matching
+// NB/2 up columns, so SwiGLU is applied inside the workgroup.
 //
 // Dequantisation.  For a packed word w, (w & 0x000F000F) | 0x64006400 is the
 // fp16 pair (1024 + q_i, 1024 + q_(i+4)) and (w & 0x00F000F0) | 0x64006400 is
 // (1024 + 16 q_(i+1), 1024 + 16 q_(i+5)); a shift by 8 gives the other four
 // codes.  These pairs go straight into v_dot2_f32_f16 against the matching
-// activation pairs (fp32 accumulate).  Per group and column the constant
-// parts are removed once:
-//   sum_k (q_k - z) x_k = A_even + A_odd / 16 - (1024 + z) S_even - (64 + z) S_odd
-// where S_even / S_odd are the group's sums of x over even / odd k; the group
-// result is then multiplied by the fp16 scale.  Cost: 5 integer ops per packed
-// word plus 4 dot2 per word per row.
+// activation pairs (fp32 accumulation; every product is exact).  The constant
+// parts and the zero point are removed once per group and column with the
+// group's activation sums over even and odd k, then the group sum is scaled by
+// the fp16 scale.  Cost per packed word: 5 VALU ops (one shift, four
+// and-or) plus 4 dot2 per activation row.  Activations are staged once per
+// workgroup in LDS, already permuted into the pairs the dot2 needs, together
+// with their per-group sums.
 //
-// Split-K.  Partial sums of the K ranges of one (expert, column block) are
-// written to the workspace; the last workgroup to finish (an atomic counter)
-// adds them in a fixed order and applies the epilogue (SwiGLU -> fp16 h for
-// the gate/up projection; fp16 y for the down projection), then resets the
-// counter.  No floating-point atomics: the output is deterministic.
+// The slots' partial sums are added in a fixed order through LDS: the output
+// is deterministic and no floating-point atomics are used.
 #include "common.h"
 
 namespace {
 
-constexpr int kW4Threads = 256;
-constexpr int kW4Waves = 4;
-constexpr int kGroupsPerWave = 1;
-constexpr int kGroupsPerBlock = kW4Waves * kGroupsPerWave;
-constexpr int kRowsPerGroup = 16;  // packed rows (8 K each) per 128-K group
 constexpr uint32_t kMagic = 0x64006400u;
-constexpr int kMaxM = 8;
+constexpr int kRowsPerGroup = 16;     // packed rows (8 K each) per 128-K group
+#ifndef SMOE_W4_MAX_WAVES
+#define SMOE_W4_MAX_WAVES 8
+#endif
+#ifndef SMOE_W4_MIN_WG
+#define SMOE_W4_MIN_WG 256
+#endif
+constexpr int kMaxWaves = SMOE_W4_MAX_WAVES;  // waves per workgroup (upper bound)
+constexpr int kLdsBytes = 32 * 1024;  // activation staging budget per workgroup
 
 struct W4Args {
     const uint16_t* xin;          // phase 1: x [T, H]; phase 2: h [rows, I]
@@ -54,28 +59,47 @@ struct W4Args {
     const int32_t* active;
     const int32_t* n_active;
     const smoe_w4_expert* experts;
-    int K;       // reduction length: H (phase 1) or I (phase 2)
-    int N;       // weight columns: 2I or H
+    int K;      // reduction length: H (phase 1) or I (phase 2)
+    int N;      // weight columns: 2I or H
     int I;
-    int nCB;     // column blocks of 256 logical columns
-    int KS;      // K splits (workgroups per column block)
-    float* part;     // [KS][rows_total][N] fp32
-    int32_t* cnt;    // [slots][nCB] completion counters
-    uint16_t* out;   // phase 1: h [rows_total, I]; phase 2: y [rows_total, H]
+    int nCB;    // column blocks
+    int MCH;    // rows per chunk (<= the kernel's row capacity)
+    int XR;     // activation rows held in LDS
+    int direct; // 1: all T token rows of x staged up front (gate/up projection)
+    int T;      // token rows of x
+    uint16_t* out;  // phase 1: h [rows, I]; phase 2: y [rows, H]
     int32_t* err;
-    int rows_total;  // rows of the partial buffer (T*k)
 };
 
 __device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
-
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
-// One 128-K group for M rows: accumulate the four dot2 streams of every row
-// and column, then fold the constants, zero and scale into tot.
-template <int M>
-__device__ __forceinline__ void group_dot(const u4_t (&wv)[kRowsPerGroup], const uint4* xs_g,
-                                          int xs_stride, const float2* sg, uint2 sv, uint32_t zw,
-                                          float (&tot)[kMaxM][4]) {
+// Masks held in VGPRs: with a VGPR mask and the magic constant in an SGPR the
+// compiler emits one v_and_or_b32 per code pair (a VOP3 op cannot take two
+// scalar/literal operands on this target).
+__device__ __forceinline__ uint32_t vgpr_const_lo() {
+    uint32_t v;
+    asm("v_mov_b32 %0, 0xf000f" : "=v"(v));
+    return v;
+}
+__device__ __forceinline__ uint32_t vgpr_const_hi() {
+    uint32_t v;
+    asm("v_mov_b32 %0, 0xf000f0" : "=v"(v));
+    return v;
+}
+
+// One 128-K group of M activation rows against this lane's 4 columns.
+//   A_even = sum over even k of (1024 + q_k) x_k,
+//   A_odd  = sum over odd  k of (1024 + 16 q_k) x_k,
+//   sum_k (q_k - z) x_k = A_even + A_odd/16 - (1024 + z) S_even - (64 + z) S_odd
+// with S_even, S_odd the group's activation sums (precomputed in LDS).
+template <int M, int MAXM>
+__device__ __forceinline__ void group_dot(const u4_t (&wv)[kRowsPerGroup],
+                                          const uint4* __restrict__ xs,
+                                          const float2* __restrict__ sums,
+                                          const int (&xoff)[MAXM], const int (&soff)[MAXM],
+                                          uint2 sv, uint32_t zw, uint32_t mlo, uint32_t mhi,
+                                          float (&acc)[MAXM][4]) {
     float ae[M][4], ao[M][4];
 #pragma unroll
     for (int m = 0; m < M; ++m)
@@ -85,15 +109,15 @@ __device__ __forceinline__ void group_dot(const u4_t (&wv)[kRowsPerGroup], const
     for (int i = 0; i < kRowsPerGroup; ++i) {
         uint4 xp[M];
 #pragma unroll
-        for (int m = 0; m < M; ++m) xp[m] = xs_g[m * xs_stride + i];
+        for (int m = 0; m < M; ++m) xp[m] = xs[xoff[m] + i];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const uint32_t w = wv[i][c];
             const uint32_t b = w >> 8;
-            const h2_t e0 = as_h2((w & 0x000F000Fu) | kMagic);
-            const h2_t o0 = as_h2((w & 0x00F000F0u) | kMagic);
-            const h2_t e1 = as_h2((b & 0x000F000Fu) | kMagic);
-            const h2_t o1 = as_h2((b & 0x00F000F0u) | kMagic);
+            const h2_t e0 = as_h2((w & mlo) | kMagic);  // 1024+q0, 1024+q4
+            const h2_t o0 = as_h2((w & mhi) | kMagic);  // 1024+16q1, 1024+16q5
+            const h2_t e1 = as_h2((b & mlo) | kMagic);  // 1024+q2, 1024+q6
+            const h2_t o1 = as_h2((b & mhi) | kMagic);  // 1024+16q3, 1024+16q7
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 ae[m][c] = __builtin_amdgcn_fdot2(e0, as_h2(xp[m].x), ae[m][c], false);
@@ -103,6 +127,9 @@ __device__ __forceinline__ void group_dot(const u4_t (&wv)[kRowsPerGroup], const
             }
         }
     }
+    float2 se[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) se[m] = sums[soff[m]];
     const uint32_t sw[2] = {sv.x, sv.y};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -113,253 +140,285 @@ __device__ __forceinline__ void group_dot(const u4_t (&wv)[kRowsPerGroup], const
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             float t = ae[m][c] + 0.0625f * ao[m][c];
-            t -= ce * sg[m].x;
-            t -= co * sg[m].y;
-            tot[m][c] += s * t;
+            t -= ce * se[m].x;
+            t -= co * se[m].y;
+            acc[m][c] += s * t;
         }
     }
 }
 
-template <int PHASE>
-__global__ __launch_bounds__(kW4Threads) void w4_kernel(W4Args a) {
-    __shared__ uint4 xs[kMaxM][kGroupsPerBlock * kRowsPerGroup];  // permuted x pairs
-    __shared__ float2 sums[kMaxM][kGroupsPerBlock];               // (S_even, S_odd)
-    __shared__ float red[kW4Waves][kMaxM][256];
-    __shared__ int s_last;
+struct GroupLoad {
+    u4_t w[kRowsPerGroup];
+    uint2 s;
+    uint32_t z;
+};
+
+__device__ __forceinline__ void load_group(GroupLoad& L, const smoe_w4_mat& wm, int g, int N,
+                                           int col, bool colok) {
+    gptr<u4_t> qp =
+        as_global(reinterpret_cast<const u4_t*>(wm.qweight + (size_t)(g * kRowsPerGroup) * N + col));
+    const int N4 = N >> 2;
+#pragma unroll
+    for (int i = 0; i < kRowsPerGroup; ++i)
+        L.w[i] = colok ? __builtin_nontemporal_load(qp + (size_t)i * N4) : u4_t{0, 0, 0, 0};
+    if (colok) {
+        const uint64_t sv = *as_global(reinterpret_cast<const uint64_t*>(wm.scales + (size_t)g * N + col));
+        L.s = make_uint2((uint32_t)sv, (uint32_t)(sv >> 32));
+        L.z = (uint32_t)*as_global(wm.qzeros + (size_t)g * (N >> 3) + (col >> 3)) >> (4 * (col & 7));
+    } else {
+        L.s = make_uint2(0, 0);
+        L.z = 0;
+    }
+}
+
+template <int MAXM>
+__device__ __forceinline__ void group_step(const GroupLoad& L, const uint4* xs, const float2* sums,
+                                           const int (&xrow)[MAXM], int g, int K8, int G, int M,
+                                           uint32_t mlo, uint32_t mhi, float (&acc)[MAXM][4]) {
+    int xoff[MAXM], soff[MAXM];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+        xoff[m] = xrow[m] * K8 + g * kRowsPerGroup;
+        soff[m] = xrow[m] * G + g;
+    }
+    if (MAXM == 1) {
+        group_dot<1, MAXM>(L.w, xs, sums, xoff, soff, L.s, L.z, mlo, mhi, acc);
+    } else {
+        switch (M) {
+            case 1: group_dot<1, MAXM>(L.w, xs, sums, xoff, soff, L.s, L.z, mlo, mhi, acc); break;
+            case 2: group_dot<(MAXM >= 2 ? 2 : 1), MAXM>(L.w, xs, sums, xoff, soff, L.s, L.z, mlo, mhi, acc); break;
+            case 3: group_dot<(MAXM >= 3 ? 3 : 1), MAXM>(L.w, xs, sums, xoff, soff, L.s, L.z, mlo, mhi, acc); break;
+            default: group_dot<MAXM, MAXM>(L.w, xs, sums, xoff, soff, L.s, L.z, mlo, mhi, acc); break;
+        }
+    }
+}
+
+// Stage activation rows src_row(j), j < nrows, into LDS rows 0..nrows-1 as
+// dot2 pairs, then their per-group sums over even and odd k.
+template <typename RowPtr>
+__device__ __forceinline__ void stage_rows(uint4* xs, float2* sums, int nrows, int K8, int G,
+                                           RowPtr src_row) {
+#pragma unroll 1
+    for (int idx = threadIdx.x; idx < nrows * K8; idx += blockDim.x) {
+        const int j = idx / K8;
+        const int rr = idx - j * K8;
+        const uint4 d = src_row(j)[rr];
+        uint4 p;
+        p.x = (d.x & 0xFFFFu) | (d.z << 16);      // (x0, x4)
+        p.y = (d.x >> 16) | (d.z & 0xFFFF0000u);  // (x1, x5)
+        p.z = (d.y & 0xFFFFu) | (d.w << 16);      // (x2, x6)
+        p.w = (d.y >> 16) | (d.w & 0xFFFF0000u);  // (x3, x7)
+        xs[j * K8 + rr] = p;
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int idx = threadIdx.x; idx < nrows * G; idx += blockDim.x) {
+        const int j = idx / G;
+        const int gg = idx - j * G;
+        const uint4* xr = xs + j * K8 + gg * kRowsPerGroup;
+        float se = 0.0f, so = 0.0f;
+#pragma unroll 4
+        for (int i = 0; i < kRowsPerGroup; ++i) {
+            const uint4 p = xr[i];
+            const h2_t x04 = as_h2(p.x), x15 = as_h2(p.y), x26 = as_h2(p.z), x37 = as_h2(p.w);
+            se += ((float)x04.x + (float)x04.y) + ((float)x26.x + (float)x26.y);
+            so += ((float)x15.x + (float)x15.y) + ((float)x37.x + (float)x37.y);
+        }
+        sums[j * G + gg] = make_float2(se, so);
+    }
+    __syncthreads();
+}
+
+template <int PHASE, int LPR, int MAXM>
+__global__ __launch_bounds__(64 * (MAXM == 1 ? kMaxWaves : 4)) void w4_kernel(W4Args a) {
+    constexpr int RPL = 64 / LPR;  // lane groups (slots) per wave
+    constexpr int NB = 4 * LPR;    // columns per block
+    extern __shared__ uint4 smem[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int ks = blockIdx.x % a.KS;
-    const int rest = blockIdx.x / a.KS;
-    const int cb = rest % a.nCB;
-    const int slot = rest / a.nCB;
-    if (slot >= *a.n_active) return;
-    const int e = a.active[slot];
-    const int r0 = a.off[e];
-    const int r1 = a.off[e + 1];
-    const smoe_w4_mat wm = (PHASE == 1) ? a.experts[e].w13 : a.experts[e].w2;
-    if (!wm.qweight || !wm.scales || !wm.qzeros) {
-        if (tid == 0 && ks == 0 && cb == 0) flag_error(a.err, SMOE_DERR_NULL_EXPERT);
-        return;
-    }
+    const int nwaves = blockDim.x >> 6;
+    const int rho = lane / LPR;
+    const int q = lane % LPR;
+    const int cb = blockIdx.x % a.nCB;
+    const int slot = blockIdx.x / a.nCB;
     const int K = a.K, N = a.N;
     const int G = K >> 7;
-    const int g0 = ks * kGroupsPerBlock;
-    const int g1 = min(G, g0 + kGroupsPerBlock);
-    const int nrow_local = (g1 - g0) * kRowsPerGroup;
+    const int K8 = K >> 3;
+    uint4* xs = smem;                                                       // [XR][K8]
+    float2* sums = reinterpret_cast<float2*>(smem + (size_t)a.XR * K8);     // [XR][G]
+    float* red = reinterpret_cast<float*>(sums + (size_t)a.XR * G);  // [nslots][MAXM][NB]
 
-    // this lane's 4 adjacent weight columns
+    // The gate/up projection with every token fitting in LDS stages all T
+    // activation rows first: that work does not wait for the routing maps.
+    const bool direct = (PHASE == 1) && a.direct;
+    const int e = a.active[slot];  // -1 past the touched experts
+    if (e < 0) return;
+    if (direct)
+        stage_rows(xs, sums, a.T, K8, G, [&](int j) {
+            return reinterpret_cast<const uint4*>(a.xin + (size_t)j * K);
+        });
+    const smoe_w4_mat wm = (PHASE == 1) ? a.experts[e].w13 : a.experts[e].w2;
+    const int r0 = a.off[e];
+    const int r1 = a.off[e + 1];
+    if (!wm.qweight || !wm.scales || !wm.qzeros) {
+        if (tid == 0 && cb == 0) flag_error(a.err, SMOE_DERR_NULL_EXPERT);
+        return;
+    }
+    const int nslots = nwaves * RPL;
+    const int myslot = wave * RPL + rho;
+
     int col;
     bool colok;
     if (PHASE == 1) {
-        col = (lane < 32) ? cb * 128 + 4 * lane : a.I + cb * 128 + 4 * (lane - 32);
+        col = (q < LPR / 2) ? cb * (NB / 2) + 4 * q : a.I + cb * (NB / 2) + 4 * (q - LPR / 2);
         colok = true;
     } else {
-        col = cb * 256 + 4 * lane;
+        col = cb * NB + 4 * q;
         colok = col < N;
     }
-    const int N4 = N >> 2;
+    const uint32_t mlo = vgpr_const_lo();
+    const uint32_t mhi = vgpr_const_hi();
 
-    for (int mc = r0; mc < r1; mc += kMaxM) {
-        const int M = min(kMaxM, r1 - mc);
-        __syncthreads();  // xs / sums / red reuse across row chunks
-        // ---- stage x (permuted into dot2 pairs) for rows mc .. mc+M-1 ----
-        for (int idx = tid; idx < M * nrow_local; idx += kW4Threads) {
-            const int m = idx / nrow_local;
-            const int rr = idx - m * nrow_local;
-            const uint16_t* src;
+    for (int mc = r0; mc < r1; mc += a.MCH) {
+        const int M = min(a.MCH, r1 - mc);
+        // the first group's weights are requested before anything waits
+        GroupLoad cur;
+        int g = myslot;
+        if (g < G) load_group(cur, wm, g, N, col, colok);
+        int xrow[MAXM];
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m)
+            xrow[m] = direct ? a.sorted_token[mc + (m < M ? m : 0)] : m;
+        if (!direct) {
+            __syncthreads();  // LDS reuse across row chunks
             if (PHASE == 1)
-                src = a.xin + (size_t)a.sorted_token[mc + m] * K;
+                stage_rows(xs, sums, M, K8, G, [&](int j) {
+                    return reinterpret_cast<const uint4*>(a.xin + (size_t)a.sorted_token[mc + j] * K);
+                });
             else
-                src = a.xin + (size_t)(mc + m) * K;
-            const uint4 d = reinterpret_cast<const uint4*>(src)[(g0 * kRowsPerGroup + rr)];
-            uint4 p;
-            p.x = (d.x & 0xFFFFu) | (d.z << 16);          // (x0, x4)
-            p.y = (d.x >> 16) | (d.z & 0xFFFF0000u);      // (x1, x5)
-            p.z = (d.y & 0xFFFFu) | (d.w << 16);          // (x2, x6)
-            p.w = (d.y >> 16) | (d.w & 0xFFFF0000u);      // (x3, x7)
-            xs[m][rr] = p;
+                stage_rows(xs, sums, M, K8, G, [&](int j) {
+                    return reinterpret_cast<const uint4*>(a.xin + (size_t)(mc + j) * K);
+                });
         }
-        __syncthreads();
-        if (tid < M * (g1 - g0)) {
-            const int m = tid / (g1 - g0);
-            const int gl = tid - m * (g1 - g0);
-            float se = 0.0f, so = 0.0f;
-            for (int i = 0; i < kRowsPerGroup; ++i) {
-                const uint4 p = xs[m][gl * kRowsPerGroup + i];
-                const h2_t x04 = as_h2(p.x), x15 = as_h2(p.y), x26 = as_h2(p.z),
-                           x37 = as_h2(p.w);
-                se += (float)x04.x + (float)x04.y + (float)x26.x + (float)x26.y;
-                so += (float)x15.x + (float)x15.y + (float)x37.x + (float)x37.y;
-            }
-            sums[m][gl] = make_float2(se, so);
-        }
-        __syncthreads();
 
-        // ---- stream this wave's groups ----
-        float tot[kMaxM][4];
+        float acc[MAXM][4];
 #pragma unroll
-        for (int m = 0; m < kMaxM; ++m)
+        for (int m = 0; m < MAXM; ++m)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) tot[m][c] = 0.0f;
+            for (int c = 0; c < 4; ++c) acc[m][c] = 0.0f;
 
-        for (int g = g0 + wave; g < g1; g += kW4Waves) {
-            const int gl = g - g0;
-            u4_t wv[kRowsPerGroup];
-            const u4_t* qp =
-                reinterpret_cast<const u4_t*>(wm.qweight + (size_t)(g * kRowsPerGroup) * N + col);
-#pragma unroll
-            for (int i = 0; i < kRowsPerGroup; ++i)
-                wv[i] = colok ? __builtin_nontemporal_load(qp + (size_t)i * N4) : u4_t{0, 0, 0, 0};
-            uint2 sv = make_uint2(0, 0);
-            uint32_t zw = 0;
-            if (colok) {
-                sv = *reinterpret_cast<const uint2*>(wm.scales + (size_t)g * N + col);
-                zw = (uint32_t)wm.qzeros[(size_t)g * (N >> 3) + (col >> 3)] >> (4 * (col & 7));
-            }
-            const uint4* xg = &xs[0][gl * kRowsPerGroup];
-            const float2* sg = &sums[0][gl];
-            constexpr int xstr = kGroupsPerBlock * kRowsPerGroup;
-            switch (M) {
-                case 1: group_dot<1>(wv, xg, xstr, sg, sv, zw, tot); break;
-                case 2: {
-                    const float2 s2[2] = {sums[0][gl], sums[1][gl]};
-                    group_dot<2>(wv, xg, xstr, s2, sv, zw, tot);
-                } break;
-                default: {
-                    float2 s8[kMaxM];
-#pragma unroll
-                    for (int m = 0; m < kMaxM; ++m) s8[m] = sums[m][gl];
-                    if (M <= 4)
-                        group_dot<4>(wv, xg, xstr, s8, sv, zw, tot);
-                    else
-                        group_dot<8>(wv, xg, xstr, s8, sv, zw, tot);
-                }
-            }
+        if (g < G) group_step<MAXM>(cur, xs, sums, xrow, g, K8, G, M, mlo, mhi, acc);
+        // later groups: load, then consume (other waves hide the latency)
+        for (g += nslots; g < G; g += nslots) {
+            GroupLoad nxt;
+            load_group(nxt, wm, g, N, col, colok);
+            group_step<MAXM>(nxt, xs, sums, xrow, g, K8, G, M, mlo, mhi, acc);
         }
-        // ---- reduce the 4 waves (fixed order) ----
+
+        // ---- add the slots' partials in a fixed order ----
+        __syncthreads();  // all slots done reading xs
 #pragma unroll
-        for (int m = 0; m < kMaxM; ++m)
+        for (int m = 0; m < MAXM; ++m)
             if (m < M)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) red[wave][m][4 * lane + c] = tot[m][c];
+                for (int c = 0; c < 4; ++c) red[(myslot * MAXM + m) * NB + 4 * q + c] = acc[m][c];
         __syncthreads();
-        for (int m = 0; m < M; ++m) {
-            const float v = ((red[0][m][tid] + red[1][m][tid]) + red[2][m][tid]) + red[3][m][tid];
-            red[0][m][tid] = v;
-        }
-        __syncthreads();
-
-        if (a.KS == 1) {
-            // ---- epilogue straight from LDS ----
-            if (PHASE == 1) {
-                for (int idx = tid; idx < M * 128; idx += kW4Threads) {
-                    const int m = idx >> 7, j = idx & 127;
-                    const float gv = red[0][m][j], uv = red[0][m][128 + j];
-                    a.out[(size_t)(mc + m) * a.I + cb * 128 + j] = f2h(silu_f(gv) * uv);
+        if (PHASE == 1) {
+            for (int idx = tid; idx < M * (NB / 2); idx += blockDim.x) {
+                const int m = idx / (NB / 2);
+                const int j = idx - m * (NB / 2);
+                float gv = 0.0f, uv = 0.0f;
+                for (int s = 0; s < nslots; ++s) {
+                    gv += red[(s * MAXM + m) * NB + j];
+                    uv += red[(s * MAXM + m) * NB + NB / 2 + j];
                 }
-            } else if (cb * 256 + tid < N) {
-                for (int m = 0; m < M; ++m)
-                    a.out[(size_t)(mc + m) * N + cb * 256 + tid] = f2h(red[0][m][tid]);
+                a.out[(size_t)(mc + m) * a.I + cb * (NB / 2) + j] = f2h(silu_f(gv) * uv);
             }
         } else {
-            // ---- write this K range's partial ----
-            int pcol;
-            bool pok;
-            if (PHASE == 1) {
-                pcol = (tid < 128) ? cb * 128 + tid : a.I + cb * 128 + (tid - 128);
-                pok = true;
-            } else {
-                pcol = cb * 256 + tid;
-                pok = pcol < N;
+            for (int idx = tid; idx < M * NB; idx += blockDim.x) {
+                const int m = idx / NB;
+                const int j = idx - m * NB;
+                if (cb * NB + j < N) {
+                    float v = 0.0f;
+                    for (int s = 0; s < nslots; ++s) v += red[(s * MAXM + m) * NB + j];
+                    a.out[(size_t)(mc + m) * N + cb * NB + j] = f2h(v);
+                }
             }
-            if (pok)
-                for (int m = 0; m < M; ++m)
-                    a.part[((size_t)ks * a.rows_total + (mc + m)) * N + pcol] = red[0][m][tid];
         }
+        __syncthreads();  // red is rewritten by the next row chunk
     }
-    if (a.KS == 1) return;
-
-    // ---- last workgroup of this (expert, column block) finishes ----
-    __threadfence();
-    __syncthreads();
-    int32_t* ctr = a.cnt + (size_t)slot * a.nCB + cb;
-    if (tid == 0) s_last = (atomicAdd(ctr, 1) == a.KS - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const size_t kstride = (size_t)a.rows_total * N;
-    if (PHASE == 1) {
-        for (int idx = tid; idx < (r1 - r0) * 128; idx += kW4Threads) {
-            const int r = r0 + (idx >> 7), j = idx & 127;
-            const float* pg = a.part + (size_t)r * N + cb * 128 + j;
-            const float* pu = a.part + (size_t)r * N + a.I + cb * 128 + j;
-            float gv = 0.0f, uv = 0.0f;
-            for (int s = 0; s < a.KS; ++s) {
-                gv += __builtin_nontemporal_load(pg + s * kstride);
-                uv += __builtin_nontemporal_load(pu + s * kstride);
-            }
-            a.out[(size_t)r * a.I + cb * 128 + j] = f2h(silu_f(gv) * uv);
-        }
-    } else {
-        const int n = cb * 256 + tid;
-        if (n < N)
-            for (int r = r0; r < r1; ++r) {
-                const float* pp = a.part + (size_t)r * N + n;
-                float v = 0.0f;
-                for (int s = 0; s < a.KS; ++s) v += __builtin_nontemporal_load(pp + s * kstride);
-                a.out[(size_t)r * N + n] = f2h(v);
-            }
-    }
-    if (tid == 0) atomicExch(ctr, 0);
 }
 
-struct W4Plan {
-    int slots, rows, G1, G2, nCB1, nCB2, KS1, KS2;
-    size_t off_cnt2, off_h, off_p1, off_p2, total;
+// ---------------------------------------------------------------- launch ----
+
+struct PhasePlan {
+    int lpr, nCB, waves, mch, xr, direct;
+    size_t lds;
 };
 
-__host__ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
-
-W4Plan plan_w4(int T, int k, int H, int I, int E) {
-    W4Plan p{};
-    p.rows = T * k;
-    p.slots = E < p.rows ? E : p.rows;
-    p.G1 = H / 128;
-    p.G2 = I / 128;
-    p.nCB1 = I / 128;
-    p.nCB2 = (H + 255) / 256;
-    p.KS1 = (p.G1 + kGroupsPerBlock - 1) / kGroupsPerBlock;
-    p.KS2 = (p.G2 + kGroupsPerBlock - 1) / kGroupsPerBlock;
-    size_t o = 0;
-    o += align256((size_t)p.slots * p.nCB1 * 4);
-    p.off_cnt2 = o;
-    o += align256((size_t)p.slots * p.nCB2 * 4);
-    p.off_h = o;
-    o += align256((size_t)p.rows * I * 2);
-    p.off_p1 = o;
-    o += align256((size_t)(p.KS1 > 1 ? p.KS1 : 0) * p.rows * (2 * (size_t)I) * 4);
-    p.off_p2 = o;
-    o += align256((size_t)(p.KS2 > 1 ? p.KS2 : 0) * p.rows * (size_t)H * 4);
-    p.total = o;
+PhasePlan plan_phase(int phase, int slots, int T, int K, int N, int I, int maxm) {
+    // LPR 16 (64-column blocks, 256-byte row runs) when that already gives
+    // enough workgroups to cover the chip, else LPR 8 (32 columns)
+    PhasePlan p{};
+    const int cols16 = (phase == 1) ? I / 32 : (N + 63) / 64;
+    p.lpr = ((long long)slots * cols16 >= SMOE_W4_MIN_WG) ? 16 : 8;
+    const int NB = 4 * p.lpr;
+    p.nCB = (phase == 1) ? I / (NB / 2) : (N + NB - 1) / NB;
+    const int rpl = 64 / p.lpr;
+    const int G = K / 128;
+    p.waves = (G + rpl - 1) / rpl;
+    const int wmax = (maxm == 1) ? kMaxWaves : 4;  // register budget of the multi-row kernels
+    if (p.waves > wmax) p.waves = wmax;
+    if (p.waves < 1) p.waves = 1;
+    const size_t row_bytes = (size_t)K * 2 + (size_t)G * 8;  // pairs + group sums
+    int cap = (int)(kLdsBytes / row_bytes);
+    if (cap < 1) cap = 1;
+    p.mch = cap < maxm ? cap : maxm;
+    p.direct = (phase == 1 && T <= cap) ? 1 : 0;
+    p.xr = p.direct ? T : p.mch;
+    const size_t red_bytes = (size_t)p.waves * rpl * maxm * NB * 4;
+    p.lds = (size_t)p.xr * row_bytes + red_bytes;
     return p;
+}
+
+template <int PHASE, int MAXM>
+hipError_t launch_phase(const W4Args& a, int slots, const PhasePlan& p, hipStream_t s) {
+    const dim3 grid(slots * p.nCB), block(64 * p.waves);
+    if (p.lpr == 16)
+        hipLaunchKernelGGL((w4_kernel<PHASE, 16, MAXM>), grid, block, p.lds, s, a);
+    else
+        hipLaunchKernelGGL((w4_kernel<PHASE, 8, MAXM>), grid, block, p.lds, s, a);
+    return hipGetLastError();
+}
+
+template <int PHASE>
+hipError_t launch_any(const W4Args& a, int slots, const PhasePlan& p, int maxm, hipStream_t s) {
+    return (maxm == 1) ? launch_phase<PHASE, 1>(a, slots, p, s)
+                       : launch_phase<PHASE, 4>(a, slots, p, s);
 }
 
 }  // namespace
 
 namespace smoe {
-size_t w4a16_workspace_bytes(int T, int k, int H, int I, int E) {
-    return plan_w4(T, k, H, I, E).total;
+size_t w4a16_workspace_bytes(int T, int k, int /*H*/, int I, int /*E*/) {
+    return ((size_t)T * k * I * 2 + 255) & ~(size_t)255;  // h [T*k, I] fp16
+}
+
+bool w4a16_shape_supported(int H, int I) {
+    return (size_t)H * 2 <= (size_t)kLdsBytes && (size_t)I * 2 <= (size_t)kLdsBytes;
 }
 
 hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, const int32_t* off,
                             const int32_t* active, const int32_t* n_active,
                             const smoe_w4_expert* experts, int T, int k, int H, int I, int E,
                             uint16_t* y, void* ws, int32_t* err, hipStream_t s) {
-    const W4Plan p = plan_w4(T, k, H, I, E);
-    char* base = static_cast<char*>(ws);
-    uint16_t* h = reinterpret_cast<uint16_t*>(base + p.off_h);
+    const int rows = T * k;
+    const int slots = E < rows ? E : rows;
+    const int maxm = (T == 1) ? 1 : 4;  // an expert holds at most T rows
+    uint16_t* h = static_cast<uint16_t*>(ws);
+    const PhasePlan p1 = plan_phase(1, slots, T, H, 2 * I, I, maxm);
     W4Args a1{};
     a1.xin = x;
     a1.sorted_token = sorted_token;
@@ -370,29 +429,26 @@ hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, cons
     a1.K = H;
     a1.N = 2 * I;
     a1.I = I;
-    a1.nCB = p.nCB1;
-    a1.KS = p.KS1;
-    a1.part = reinterpret_cast<float*>(base + p.off_p1);
-    a1.cnt = reinterpret_cast<int32_t*>(base);
+    a1.nCB = p1.nCB;
+    a1.MCH = p1.mch;
+    a1.XR = p1.xr;
+    a1.direct = p1.direct;
+    a1.T = T;
     a1.out = h;
     a1.err = err;
-    a1.rows_total = p.rows;
-    hipLaunchKernelGGL(w4_kernel<1>, dim3(p.slots * p.nCB1 * p.KS1, 1, 1), dim3(kW4Threads), 0,
-                       s, a1);
-    hipError_t st = hipGetLastError();
+    hipError_t st = launch_any<1>(a1, slots, p1, maxm, s);
     if (st != hipSuccess) return st;
+    const PhasePlan p2 = plan_phase(2, slots, T, I, H, I, maxm);
     W4Args a2 = a1;
     a2.xin = h;
     a2.sorted_token = nullptr;
     a2.K = I;
     a2.N = H;
-    a2.nCB = p.nCB2;
-    a2.KS = p.KS2;
-    a2.part = reinterpret_cast<float*>(base + p.off_p2);
-    a2.cnt = reinterpret_cast<int32_t*>(base + p.off_cnt2);
+    a2.nCB = p2.nCB;
+    a2.MCH = p2.mch;
+    a2.XR = p2.xr;
+    a2.direct = 0;
     a2.out = y;
-    hipLaunchKernelGGL(w4_kernel<2>, dim3(p.slots * p.nCB2 * p.KS2, 1, 1), dim3(kW4Threads), 0,
-                       s, a2);
-    return hipGetLastError();
+    return launch_any<2>(a2, slots, p2, maxm, s);
 }
 }  // namespace smoe

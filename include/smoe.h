@@ -179,10 +179,9 @@ smoe_status moe_gather(const int32_t* topk_ids, int T, int k, int E, int32_t* ex
  *   group_size     must be 128
  *   y_sorted       fp16 [T*k, H] out (rows past off[E] untouched)
  *   workspace      device, >= smoe_workspace_bytes(0, T, k, H, I, E) bytes,
- *                  256-byte aligned.  Its first 4096 bytes are completion
- *                  counters that must be zero before the first call with this
- *                  workspace; every call that completes leaves them zero.
- *                  Calls sharing one workspace must be stream-ordered.
+ *                  256-byte aligned: holds h (fp16 [T*k, I]) between the two
+ *                  projections; no initialisation needed.
+ *   H, I           at most 16384 each (activations are staged in LDS).
  * ---------------------------------------------------------------------- */
 smoe_status w4a16_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
                               const int32_t* expert_offsets, const int32_t* active,
