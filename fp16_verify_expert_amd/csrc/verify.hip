@@ -8,13 +8,13 @@
 // experts already resident are computed first while missing ones load, hence
 // the optional expert mask.
 //
-// Each wave owns 16 output columns of one touched expert and streams the
-// weight rows of those columns over the whole reduction, feeding
+// A workgroup owns 16 output columns of one touched expert; its waves split
+// the reduction and stream the weight rows of those columns, feeding
 // v_mfma_f32_16x16x32_f16 directly from registers: lane l loads 16 bytes of
 // weight row (n0 + l%16) at K offset 8*(l/16) -- exactly the B-operand layout
 // -- and the matching activation row (l%16) of the expert's packed rows as the
-// A operand.  Rows beyond the expert's count are zero, so the MFMA is only as
-// wide as the data; at K+1 <= 33 tokens the kernel is bound by the HBM stream
+// A operand.  Small work units keep the tail of the launch short.  Rows
+// beyond the expert's count are zero, so the MFMA is only as wide as the data; at K+1 <= 33 tokens the kernel is bound by the HBM stream
 // of the touched experts' weights.  Up to RB row blocks of 16 share one weight
 // stream.  The gate/up projection applies SwiGLU in registers and writes h as
 // fp16; the down projection writes y_sorted.
@@ -22,9 +22,8 @@
 
 namespace {
 
-constexpr int kF16Threads = 256;  // 4 waves, 16 columns each
-constexpr int kF16Waves = 4;
-constexpr int kUnroll = 4;        // 4 x 32 K per step
+constexpr int kTileBytes = 4096; // one 16-row x 128-K fp16 tile
+constexpr int kKStep = 128;      // K per pipeline step
 
 struct F16Args {
     const uint16_t* xin;          // phase 1: x [T, H]; phase 2: h [rows, I]
@@ -38,23 +37,49 @@ struct F16Args {
     int Ncol;   // output columns: I (phase 1) or H (phase 2)
     int I;
     int H;
-    int nWB;    // workgroup column blocks (64 columns each)
+    int nCB;    // 16-column blocks
     uint16_t* out;  // phase 1: h [rows, I]; phase 2: y [rows, H]
     int32_t* err;
 };
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() {
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
+}
+
+// ---------------------------------------------------------------------------
+// Register-pipelined variant (short reductions).  Same work unit: one
+// workgroup per (expert, 16-column block), 4 waves splitting the reduction;
+// weights and activations of step st+1 are loaded into registers straight in
+// the MFMA operand layout (lane l: row l%16, 16 bytes at K offset 8*(l/16))
+// while step st is multiplied.  No LDS ring, so several workgroups share a
+// CU and their start-up latencies overlap; for long reductions the wide-run
+// LDS variant below streams HBM better.
+constexpr int kRegWaves = 4;
+
 template <int PHASE, int RB>
-__global__ __launch_bounds__(kF16Threads) void f16_kernel(F16Args a) {
+__global__ __launch_bounds__(64 * kRegWaves) void f16_reg_kernel(F16Args a) {
+    constexpr int NACC = (PHASE == 1) ? 2 : 1;
+    constexpr int kUnroll = (PHASE == 1) ? 4 : 8;  // 32-K chunks per step
+    __shared__ f4_t part[kRegWaves][NACC][RB][64];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int wb = blockIdx.x % a.nWB;
-    const int slot = blockIdx.x / a.nWB;
+    const int cb = blockIdx.x % a.nCB;
+    const int slot = blockIdx.x / a.nCB;
     int e;
     if (a.active) {
-        if (slot >= *a.n_active) return;
-        e = a.active[slot];
+        e = a.active[slot];  // -1 past the touched experts
+        if (e < 0) return;
     } else {
         e = slot;
     }
@@ -64,23 +89,25 @@ __global__ __launch_bounds__(kF16Threads) void f16_kernel(F16Args a) {
     if (r1 <= r0) return;
     const uint16_t* W = (PHASE == 1) ? a.experts[e].w13 : a.experts[e].w2;
     if (!W) {
-        if (threadIdx.x == 0 && wb == 0) flag_error(a.err, SMOE_DERR_NULL_EXPERT);
+        if (threadIdx.x == 0 && cb == 0) flag_error(a.err, SMOE_DERR_NULL_EXPERT);
         return;
     }
     const int K = a.K;
-    const int n = (wb * kF16Waves + wave) * 16 + (lane & 15);
-    if ((wb * kF16Waves + wave) * 16 >= a.Ncol) return;  // whole wave past the end
-    const bool colok = n < a.Ncol;
+    const int n = cb * 16 + (lane & 15);
     const int kq = 8 * (lane >> 4);
     const h8_t zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    // this wave's steps (32*kUnroll K each; the matrix's last step may be partial)
+    const int nchunks = K / 32;
+    const int nsteps = (nchunks + kUnroll - 1) / kUnroll;
+    const int s0 = (nsteps * wave) / kRegWaves;
+    const int s1 = (nsteps * (wave + 1)) / kRegWaves;
 
-    const h8_t* wg = reinterpret_cast<const h8_t*>(W + (size_t)(colok ? n : 0) * K + kq);
-    const h8_t* wu = (PHASE == 1)
-                         ? reinterpret_cast<const h8_t*>(W + (size_t)(a.I + (colok ? n : 0)) * K + kq)
-                         : wg;
+    gptr<h8_t> wg = as_global(reinterpret_cast<const h8_t*>(W + (size_t)n * K + kq));
+    gptr<h8_t> wu = as_global(reinterpret_cast<const h8_t*>(
+        W + (size_t)((PHASE == 1) ? a.I + n : n) * K + kq));
 
     for (int mb = r0; mb < r1; mb += 16 * RB) {
-        const h8_t* arow[RB];
+        gptr<h8_t> arow[RB];
         bool aok[RB];
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
@@ -91,7 +118,7 @@ __global__ __launch_bounds__(kF16Threads) void f16_kernel(F16Args a) {
                 src = a.xin + (size_t)(aok[b] ? a.sorted_token[r] : 0) * K;
             else
                 src = a.xin + (size_t)(aok[b] ? r : 0) * K;
-            arow[b] = reinterpret_cast<const h8_t*>(src + kq);
+            arow[b] = as_global(reinterpret_cast<const h8_t*>(src + kq));
         }
         f4_t accg[RB], accu[RB];
 #pragma unroll
@@ -99,71 +126,290 @@ __global__ __launch_bounds__(kF16Threads) void f16_kernel(F16Args a) {
             accg[b] = f4_t{0.f, 0.f, 0.f, 0.f};
             accu[b] = f4_t{0.f, 0.f, 0.f, 0.f};
         }
-        // software pipeline: weights for step s+1 are in flight while step s
-        // is multiplied
-        h8_t bg[kUnroll], bu[kUnroll], nbg[kUnroll], nbu[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            bg[u] = colok ? __builtin_nontemporal_load(wg + 4 * u) : zero8;
-            if (PHASE == 1) bu[u] = colok ? __builtin_nontemporal_load(wu + 4 * u) : zero8;
-        }
-        for (int k0 = 0; k0 < K; k0 += 32 * kUnroll) {
-            const int kn = k0 + 32 * kUnroll;
-            const bool more = kn < K;
+        h8_t bg[kUnroll], bu[kUnroll], av[RB][kUnroll];
+        if (s0 < s1) {
+            const size_t o = (size_t)s0 * 4 * kUnroll;  // in h8 units
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                const size_t o = (size_t)(kn >> 3) + 4 * u;  // in h8 units
-                nbg[u] = (more && colok) ? __builtin_nontemporal_load(wg + o) : zero8;
-                if (PHASE == 1) nbu[u] = (more && colok) ? __builtin_nontemporal_load(wu + o) : zero8;
+                const bool in = s0 * kUnroll + u < nchunks;
+                bg[u] = in ? __builtin_nontemporal_load(wg + o + 4 * u) : zero8;
+                if (PHASE == 1) bu[u] = in ? __builtin_nontemporal_load(wu + o + 4 * u) : zero8;
+#pragma unroll
+                for (int b = 0; b < RB; ++b) av[b][u] = (in && aok[b]) ? arow[b][o + 4 * u] : zero8;
             }
-            h8_t av[RB][kUnroll];
+        }
+        for (int st = s0; st < s1; ++st) {
+            const size_t o = (size_t)(st + 1) * 4 * kUnroll;
+            h8_t nbg[kUnroll], nbu[kUnroll], nav[RB][kUnroll];
 #pragma unroll
-            for (int b = 0; b < RB; ++b)
+            for (int u = 0; u < kUnroll; ++u) {
+                const bool in = st + 1 < s1 && (st + 1) * kUnroll + u < nchunks;
+                nbg[u] = in ? __builtin_nontemporal_load(wg + o + 4 * u) : zero8;
+                if (PHASE == 1) nbu[u] = in ? __builtin_nontemporal_load(wu + o + 4 * u) : zero8;
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u)
-                    av[b][u] = aok[b] ? arow[b][(k0 >> 3) + 4 * u] : zero8;
+                for (int b = 0; b < RB; ++b) nav[b][u] = (in && aok[b]) ? arow[b][o + 4 * u] : zero8;
+            }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
                 for (int b = 0; b < RB; ++b) {
                     accg[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[b][u], bg[u], accg[b], 0, 0, 0);
                     if (PHASE == 1)
-                        accu[b] =
-                            __builtin_amdgcn_mfma_f32_16x16x32_f16(av[b][u], bu[u], accu[b], 0, 0, 0);
+                        accu[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[b][u], bu[u], accu[b], 0, 0, 0);
                 }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 bg[u] = nbg[u];
                 if (PHASE == 1) bu[u] = nbu[u];
+#pragma unroll
+                for (int b = 0; b < RB; ++b) av[b][u] = nav[b][u];
             }
         }
-        // D[row = 4*(lane/16) + i][col = lane%16]
-        if (colok) {
+        // ---- add the waves' partial tiles (fixed order) ----
 #pragma unroll
-            for (int b = 0; b < RB; ++b)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = mb + 16 * b + 4 * (lane >> 4) + i;
-                    if (r < r1) {
-                        float v;
-                        if (PHASE == 1)
-                            v = silu_f(accg[b][i]) * accu[b][i];
-                        else
-                            v = accg[b][i];
-                        a.out[(size_t)r * a.Ncol + n] = f2h(v);
-                    }
-                }
+        for (int b = 0; b < RB; ++b) {
+            part[wave][0][b][lane] = accg[b];
+            if (PHASE == 1) part[wave][NACC - 1][b][lane] = accu[b];
         }
+        __syncthreads();
+        for (int b = wave; b < RB; b += kRegWaves) {
+            f4_t g = part[0][0][b][lane];
+            f4_t u = part[0][NACC - 1][b][lane];
+            for (int w = 1; w < kRegWaves; ++w) {
+                g += part[w][0][b][lane];
+                if (PHASE == 1) u += part[w][NACC - 1][b][lane];
+            }
+            // D[row = 4*(lane/16) + i][col = lane%16]
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = mb + 16 * b + 4 * (lane >> 4) + i;
+                if (r < r1) {
+                    const float v = (PHASE == 1) ? silu_f(g[i]) * u[i] : g[i];
+                    a.out[(size_t)r * a.Ncol + n] = f2h(v);
+                }
+            }
+        }
+        __syncthreads();  // part is reused by the next row block
     }
 }
 
+// ---------------------------------------------------------------------------
+// LDS-ring variant (long reductions).
+// NT 16-byte LDS reads at byte addresses addr + t*4096, completed before the
+// block ends.  Written as one asm block so the compiler's counter analysis
+// (which cannot tell the ring stages apart and would otherwise drain every
+// outstanding global->LDS load before any LDS read) leaves the explicit
+// vmcnt waits of the pipeline in charge.
+template <int NT>
+__device__ __forceinline__ void lds_read_tiles(uint32_t addr, h8_t (&v)[NT]) {
+    static_assert(NT >= 2 && NT <= 4, "tiles per step");
+    if constexpr (NT == 2) {
+        asm volatile(
+            "ds_read_b128 %0, %2\n\t"
+            "ds_read_b128 %1, %2 offset:4096\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(v[0]), "=&v"(v[1])
+            : "v"(addr)
+            : "memory");
+    } else if constexpr (NT == 3) {
+        asm volatile(
+            "ds_read_b128 %0, %3\n\t"
+            "ds_read_b128 %1, %3 offset:4096\n\t"
+            "ds_read_b128 %2, %3 offset:8192\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2])
+            : "v"(addr)
+            : "memory");
+    } else {
+        asm volatile(
+            "ds_read_b128 %0, %4\n\t"
+            "ds_read_b128 %1, %4 offset:4096\n\t"
+            "ds_read_b128 %2, %4 offset:8192\n\t"
+            "ds_read_b128 %3, %4 offset:12288\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+            : "v"(addr)
+            : "memory");
+    }
+}
+
+// One workgroup = one (expert, 16-column block); its waves split the
+// reduction into contiguous step ranges.  Each wave streams its tiles through
+// a private NSTAGE-deep LDS ring with direct global->LDS loads: a load
+// instruction covers 4 rows x 256 contiguous bytes (lane l: row 4j + l/16,
+// 16-byte chunk (l%16) xor row), which is what keeps HBM streaming near its
+// peak; the xor swizzle makes the MFMA-layout reads (row l%16, chunk
+// 4u + l/16) hit 16 different bank groups.  The activation rows of the step
+// come through the same ring, so one counter wait covers a whole step.
+template <int PHASE, int RB, int NSTAGE, int kVWaves>
+__global__ __launch_bounds__(64 * kVWaves) void f16_kernel(F16Args a) {
+    constexpr int NM = (PHASE == 1) ? 2 : 1;            // weight matrices per step
+    constexpr int NT = NM + RB;                          // tiles per step
+    constexpr int STAGE = NT * kTileBytes;
+    constexpr int LOADS = 4 * NT;                        // load instructions per step
+    constexpr int D = NSTAGE - 1;                        // steps in flight ahead
+    __shared__ __attribute__((aligned(16))) char ring[kVWaves][NSTAGE][STAGE];
+    __shared__ f4_t part[kVWaves][NM][RB][64];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int cb = blockIdx.x % a.nCB;
+    const int slot = blockIdx.x / a.nCB;
+    int e;
+    if (a.active) {
+        e = a.active[slot];  // -1 past the touched experts
+        if (e < 0) return;
+    } else {
+        e = slot;
+    }
+    if (a.mask && !a.mask[e]) return;
+    const int r0 = a.off[e];
+    const int r1 = a.off[e + 1];
+    if (r1 <= r0) return;
+    const uint16_t* W = (PHASE == 1) ? a.experts[e].w13 : a.experts[e].w2;
+    if (!W) {
+        if (threadIdx.x == 0 && cb == 0) flag_error(a.err, SMOE_DERR_NULL_EXPERT);
+        return;
+    }
+    const int K = a.K;
+    const int nsteps = K / kKStep;
+    const int s0 = (nsteps * wave) / kVWaves;
+    const int s1 = (nsteps * (wave + 1)) / kVWaves;
+    const int n0 = cb * 16;
+
+    // loader geometry: instruction j covers tile rows 4j + lane/16
+    const int lrow = lane >> 4;          // + 4j
+    const int lslot = lane & 15;
+    // reader geometry: row lane%16, chunk 4u + lane/16 at slot chunk ^ row
+    const int rrow = lane & 15;
+    const int rq = lane >> 4;
+
+    // global source row pointers of this lane (4 tile rows per matrix)
+    const uint16_t* wrow[NM][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 4 * j + lrow;
+        wrow[0][j] = W + (size_t)(n0 + r) * K;
+        if (PHASE == 1) wrow[NM - 1][j] = W + (size_t)(a.I + n0 + r) * K;
+    }
+
+    for (int mb = r0; mb < r1; mb += 16 * RB) {
+        // activation rows of this lane's loads (rows past the group repeat a
+        // valid row; they only feed output rows that are not stored)
+        const uint16_t* arow[RB][4];
+#pragma unroll
+        for (int b = 0; b < RB; ++b)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                int r = mb + 16 * b + 4 * j + lrow;
+                if (r >= r1) r = r0;
+                arow[b][j] = (PHASE == 1) ? a.xin + (size_t)a.sorted_token[r] * K
+                                          : a.xin + (size_t)r * K;
+            }
+        auto issue = [&](int st) {
+            char* stage = &ring[wave][st % NSTAGE][0];
+            const int k0 = st * kKStep;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = lslot ^ (4 * j + lrow);  // swizzled 16-byte chunk
+                const int koff = k0 + 8 * c;
+#pragma unroll
+                for (int m = 0; m < NM; ++m)
+                    __builtin_amdgcn_global_load_lds(
+                        (const void*)(wrow[m][j] + koff),
+                        (lds_ptr_t)(stage + m * kTileBytes + j * 1024), 16, 0, 0);
+#pragma unroll
+                for (int b = 0; b < RB; ++b)
+                    __builtin_amdgcn_global_load_lds(
+                        (const void*)(arow[b][j] + koff),
+                        (lds_ptr_t)(stage + (NM + b) * kTileBytes + j * 1024), 16, 0, 0);
+            }
+        };
+
+        f4_t accg[RB], accu[RB];
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            accg[b] = f4_t{0.f, 0.f, 0.f, 0.f};
+            accu[b] = f4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        wait_lgkm0();  // the ring of the previous row block has been read
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            if (s0 + d < s1) issue(s0 + d);
+        for (int st = s0; st < s1; ++st) {
+            wait_lgkm0();  // reads of the stage about to be refilled are done
+            if (st + D < s1) issue(st + D);
+            // loads issued after step st's: min(D, s1-1-st) steps
+            const int ahead = min(D, s1 - 1 - st);
+            if (ahead >= D) wait_vmcnt<D * LOADS>();
+            else if (D >= 2 && ahead == 1) wait_vmcnt<LOADS>();
+            else if (D >= 3 && ahead == 2) wait_vmcnt<(D >= 3 ? 2 * LOADS : 0)>();
+            else wait_vmcnt<0>();
+            const uint32_t stage_addr =
+                (uint32_t)(uintptr_t)(lds_ptr_t)&ring[wave][st % NSTAGE][0];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t off = rrow * 256 + (((4 * u + rq) ^ rrow) << 4);
+                h8_t t[NT];  // weight tile(s), then RB activation tiles
+                lds_read_tiles<NT>(stage_addr + off, t);
+#pragma unroll
+                for (int b = 0; b < RB; ++b) {
+                    accg[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(t[NM + b], t[0], accg[b], 0, 0, 0);
+                    if (PHASE == 1)
+                        accu[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(t[NM + b], t[1], accu[b], 0, 0, 0);
+                }
+            }
+        }
+        // ---- add the waves' partial tiles (fixed order) ----
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            part[wave][0][b][lane] = accg[b];
+            if (PHASE == 1) part[wave][NM - 1][b][lane] = accu[b];
+        }
+        __syncthreads();
+        for (int b = wave; b < RB; b += kVWaves) {
+            f4_t g = part[0][0][b][lane];
+            f4_t u = part[0][NM - 1][b][lane];
+            for (int w = 1; w < kVWaves; ++w) {
+                g += part[w][0][b][lane];
+                if (PHASE == 1) u += part[w][NM - 1][b][lane];
+            }
+            // D[row = 4*(lane/16) + i][col = lane%16]
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = mb + 16 * b + 4 * (lane >> 4) + i;
+                if (r < r1) {
+                    const float v = (PHASE == 1) ? silu_f(g[i]) * u[i] : g[i];
+                    a.out[(size_t)r * a.Ncol + n0 + (lane & 15)] = f2h(v);
+                }
+            }
+        }
+        __syncthreads();  // part is reused by the next row block
+    }
+}
+
+#ifndef SMOE_VF_LONG
+#define SMOE_VF_LONG 8
+#endif
+
 template <int PHASE>
 hipError_t launch_phase(const F16Args& a, int slots, int RB, hipStream_t s) {
-    const dim3 grid(slots * a.nWB), block(kF16Threads);
-    switch (RB) {
-        case 1: hipLaunchKernelGGL((f16_kernel<PHASE, 1>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((f16_kernel<PHASE, 2>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((f16_kernel<PHASE, 4>), grid, block, 0, s, a); break;
+    // Reductions with at least SMOE_VF_LONG 128-K steps per wave take the
+    // LDS-ring kernel (4 waves; LDS per workgroup: 4 x NSTAGE x (NM + RB) x
+    // 4 KB <= 160 KB), shorter ones the register-pipelined kernel.
+    const int nsteps = a.K / kKStep;
+    const bool ring = nsteps / 4 >= SMOE_VF_LONG;
+    const dim3 grid(slots * a.nCB), block(256);
+    if (ring) {
+        if (RB == 1)
+            hipLaunchKernelGGL((f16_kernel<PHASE, 1, 3, 4>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((f16_kernel<PHASE, 2, 2, 4>), grid, block, 0, s, a);
+    } else {
+        if (RB == 1)
+            hipLaunchKernelGGL((f16_reg_kernel<PHASE, 1>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((f16_reg_kernel<PHASE, 2>), grid, block, 0, s, a);
     }
     return hipGetLastError();
 }
@@ -180,9 +426,13 @@ hipError_t launch_verify_ffn(const uint16_t* x, const int32_t* sorted_token, con
                              const smoe_f16_expert* experts, const uint8_t* mask, int T, int rows,
                              int H, int I, int E, uint16_t* y, void* ws, int32_t* err,
                              hipStream_t s) {
-    // row blocks held per weight stream: enough for the largest possible
-    // expert group (<= T rows) up to 64
-    const int RB = (T <= 16) ? 1 : (T <= 32) ? 2 : 4;
+    // row blocks of 16 held per weight stream, sized for the largest group
+    // expected: all rows when there is one expert (a shared expert), else
+    // about twice the mean plus slack (bigger groups take extra passes)
+    const int mean = (rows + E - 1) / E;
+    int est = (E == 1) ? rows : 2 * mean + 8;
+    if (est > T) est = T;
+    const int RB = (est <= 16) ? 1 : 2;
     const int slots = active ? (E < rows ? E : rows) : E;
     uint16_t* h = static_cast<uint16_t*>(ws);
     F16Args a1{};
@@ -197,7 +447,7 @@ hipError_t launch_verify_ffn(const uint16_t* x, const int32_t* sorted_token, con
     a1.Ncol = I;
     a1.I = I;
     a1.H = H;
-    a1.nWB = (I + 63) / 64;
+    a1.nCB = I / 16;
     a1.out = h;
     a1.err = err;
     hipError_t st = launch_phase<1>(a1, slots, RB, s);
@@ -207,7 +457,7 @@ hipError_t launch_verify_ffn(const uint16_t* x, const int32_t* sorted_token, con
     a2.sorted_token = nullptr;
     a2.K = I;
     a2.Ncol = H;
-    a2.nWB = (H + 63) / 64;
+    a2.nCB = H / 16;
     a2.out = y;
     return launch_phase<2>(a2, slots, RB, s);
 }

@@ -342,3 +342,22 @@ def test_layer_end_to_end(shape, T, kind):
     assert np.array_equal(host(got["ids"]), ref["route"]["ids"])
     st = assert_fp16_close(host(got["out"]), ref["out"], f"layer {shape.name} T={T} {kind}")
     say(f"  l2={st['l2']:.2e} maxabs={st['maxabs']:.2e}")
+
+
+@pytest.mark.parametrize("shape,T", [(synth.PHI, 20), (synth.PHI, 40), (synth.TINY, 100),
+                                     (synth.QWEN, 33)], ids=lambda v: getattr(v, "name", str(v)))
+def test_verify_one_expert_many_rows(shape, T):
+    # one expert holding all T rows: 16/32-row blocks and several passes over
+    # the weights, in both the short-reduction and the long-reduction kernels
+    say(f"verify one expert {shape.name} T={T}")
+    w13, w2 = synth.expert_f16(shape, 0, 0)
+    x = synth.tokens(shape, T, step=7)
+    ref = oracle.expert_ffn_f16(x, w13, w2)
+    from gpu_util import upload_f16
+    tab, keep = upload_f16([(w13, w2)])
+    iota = torch.arange(T, dtype=torch.int32, device="cuda")
+    offs = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    ws = fve.new_workspace(1, T, 1, shape.H, shape.I, 1)
+    y = fve.verify_grouped_gemm(dev(x), iota, offs, tab, T, T, shape.H, shape.I, 1, ws)
+    st = assert_fp16_close(host(y)[:T], ref, f"verify one expert {shape.name} T={T}")
+    say(f"  l2={st['l2']:.2e} maxabs={st['maxabs']:.2e}")
