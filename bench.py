@@ -178,17 +178,22 @@ def main():
     prof_dir = os.path.join(ROOT, "profiles")
 
     def pmc_traffic(name):
-        """HBM bytes per call from the committed rocprofv3 --pmc summary, when
-        it was taken on the current kernels (else None)."""
+        """HBM bytes per call from the committed rocprofv3 --pmc summary
+        (FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy), or None when the
+        kernel sources changed since the counters were taken."""
+        import hashlib
         p = os.path.join(prof_dir, "pmc_traffic.json")
         if not os.path.exists(p):
             return None
-        try:
-            with open(p) as f:
-                d = json.load(f)
-            return d.get(name)
-        except Exception:
-            return None
+        with open(p) as f:
+            d = json.load(f)
+        for src, h in d.get("sources_sha256", {}).items():
+            path = os.path.join(ROOT, "fp16_verify_expert_amd", "csrc", src)
+            with open(path, "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest()[:16] != h:
+                    return None
+        v = d.get(name)
+        return None if v is None else round(float(v))
 
     res = {
         "metric": "MoE-layer INT4 draft weight GB/s (% HBM peak); verify TFLOP/s (% MFMA)",
