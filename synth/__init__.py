@@ -239,3 +239,79 @@ def make_layer(shape: LayerShape, layer: int = 0, seed: int = BASE_SEED,
             q_list[e] = q
     return dict(shape=shape, layer=layer, router=router(shape, layer, seed),
                 shared=shared_expert(shape, layer, seed), f16=f16_list, int4=q_list)
+
+
+# ---------------------------------------------------------------------------
+# Device-side generation for the large multi-layer workload (24 layers x 60
+# experts = 12.5 G parameters would take tens of minutes in NumPy).  Same
+# recipe -- N(0, 0.02) fp32 draws rounded to fp16, RTN into the GPTQ layout
+# -- from torch's Philox generator seeded per tensor; the values differ from
+# the NumPy streams above, so a comparison always hands the same generated
+# tensors to the oracle and to the kernels.
+# ---------------------------------------------------------------------------
+
+def _torch_seed(*key: int) -> int:
+    ss = np.random.SeedSequence([int(v) for v in key])
+    return int(ss.generate_state(1, dtype=np.uint64)[0] & ((1 << 63) - 1))
+
+
+def torch_normal_f16(key, shape, std, device):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(_torch_seed(*key))
+    a = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        a.mul_(std)
+    return a.to(torch.float16)
+
+
+def torch_gptq_from_linear(w_nk):
+    """GPTQ INT4 (qweight int32 [K/8, N], scales fp16 [K/128, N], qzeros int32
+    [K/128, N/8]) of an fp16 nn.Linear weight [N, K] on its device; same RTN
+    rule as `rtn_quantize`."""
+    import torch
+    w = w_nk.t().float()
+    K, N = w.shape
+    wg = w.reshape(K // GROUP, GROUP, N)
+    lo = torch.clamp(wg.amin(dim=1), max=0.0)
+    hi = torch.clamp(wg.amax(dim=1), min=0.0)
+    s16 = ((hi - lo) / 15.0).to(torch.float16)
+    one = torch.ones_like(s16)
+    s16 = torch.where(hi == lo, one, s16)
+    s16 = torch.where(s16 == 0, one, s16)
+    s = s16.float()
+    z = torch.clamp(torch.round(-lo / s), 0, 15)
+    q = torch.clamp(torch.round(wg / s[:, None, :]) + z[:, None, :], 0, 15).to(torch.int32)
+    q = q.reshape(K // 8, 8, N)
+    qweight = torch.zeros((K // 8, N), dtype=torch.int32, device=w.device)
+    for i in range(8):
+        qweight |= q[:, i, :] << (4 * i)
+    zi = z.to(torch.int32).reshape(K // GROUP, N // 8, 8)
+    qzeros = torch.zeros((K // GROUP, N // 8), dtype=torch.int32, device=w.device)
+    for i in range(8):
+        qzeros |= zi[:, :, i] << (4 * i)
+    return qweight.contiguous(), s16.contiguous(), qzeros.contiguous()
+
+
+def torch_layer(shape: LayerShape, layer: int, device, seed: int = BASE_SEED, int4: bool = True):
+    """One layer generated on `device`: router, shared expert (+gate), and per
+    expert the FP16 target weights (w13 [2I, H], w2 [H, I]) and, optionally,
+    their GPTQ INT4 draft copies."""
+    c = shape.config_id
+    out = dict(router=torch_normal_f16((seed, c, layer, 0, T_ROUTER, 0), (shape.E, shape.H), 0.02,
+                                       device), f16=[], int4=[])
+    for e in range(shape.E):
+        w13 = torch_normal_f16((seed, c, layer, e, T_W13, 0), (2 * shape.I, shape.H), 0.02, device)
+        w2 = torch_normal_f16((seed, c, layer, e, T_W2, 0), (shape.H, shape.I), 0.02, device)
+        out["f16"].append((w13, w2))
+        if int4:
+            out["int4"].append(dict(w13=torch_gptq_from_linear(w13), w2=torch_gptq_from_linear(w2)))
+    out["shared"] = None
+    if shape.shared_I:
+        Is = shape.shared_I
+        out["shared"] = dict(
+            w13=torch_normal_f16((seed, c, layer, 1000, T_SH_W13, 0), (2 * Is, shape.H), 0.02, device),
+            w2=torch_normal_f16((seed, c, layer, 1000, T_SH_W2, 0), (shape.H, Is), 0.02, device),
+            gate=(torch_normal_f16((seed, c, layer, 1000, T_SH_GATE, 0), (shape.H,), 0.02, device)
+                  if shape.shared_gate else None))
+    return out

@@ -286,3 +286,14 @@ def test_generator_deterministic():
     assert h(synth.tokens(synth.TINY, 4, step=1)) != h(synth.tokens(synth.TINY, 4, step=2))
     w = a["f16"][0][0].astype(np.float64)
     assert abs(w.std() - 0.02) < 0.002 and abs(w.mean()) < 0.002
+
+
+def test_torch_rtn_matches_numpy_rtn():
+    # the device-side generator's quantiser is the same RTN rule (run on CPU)
+    import torch
+    rng = np.random.default_rng(11)
+    w = (rng.standard_normal((256, 384)) * 0.02).astype(np.float16)
+    a = synth.gptq_from_linear(w)
+    b = synth.torch_gptq_from_linear(torch.from_numpy(w))
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y.numpy())
