@@ -46,6 +46,11 @@ def parse():
                     help="draft steps of the oracle timed for cpu_baseline (0 = skip)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--workload", default="phi_layer", choices=["phi_layer", "qwen_chunk"],
+                    help="phi_layer (default): one draft + verify step of the Phi-3.5-MoE-shaped "
+                         "layer; qwen_chunk: 24 Qwen-shaped layers, 16 draft steps, ELB snapshot, "
+                         "top-16 residency, 17-token verify with staged misses")
+    ap.add_argument("--layers", type=int, default=24, help="qwen_chunk: number of layers")
     return ap.parse_args()
 
 
@@ -55,6 +60,8 @@ def main():
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
               "the path is single-GPU and no multi-GPU figure is produced.", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "qwen_chunk":
+        return bench_qwen_chunk(args)
 
     import numpy as np
     import torch
@@ -245,6 +252,117 @@ def main():
     if args.cpu_sample > 0:
         res["cpu_baseline"] = cpu_baseline(layer, s, args.cpu_sample)
     print(json.dumps(res), flush=True)
+
+
+def bench_qwen_chunk(args):
+    """Draft chunk + verify over L Qwen-shaped layers with 16 of 60 FP16
+    experts resident per layer.  One step = 16 INT4 draft decode steps through
+    all layers (ELB table [L, 60]), the chunk-boundary snapshot and placement of
+    the top-16 experts per layer, then the 17-token FP16 verify where misses
+    are staged from pinned host memory on a side stream behind the hit GEMMs.
+    The same verify with every expert in HBM gives the PCIe-free figure."""
+    import numpy as np
+    import torch
+
+    import fp16_verify_expert_amd as fve
+    import synth
+    from fp16_verify_expert_amd.chunk import ChunkEngine, ChunkLayer
+
+    fve.lib()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda")
+    s = synth.QWEN_CHUNK
+    L, STEPS, TV, NRES = args.layers, 16, 17, 16
+    t0 = time.perf_counter()
+    layers, full = [], torch.empty((L, s.E, 3 * s.H * s.I), dtype=torch.float16, device=dev)
+    for l in range(L):
+        g = synth.torch_layer(s, l, dev)
+        for e, (w13, w2) in enumerate(g["f16"]):
+            full[l, e, :2 * s.I * s.H].copy_(w13.reshape(-1))
+            full[l, e, 2 * s.I * s.H:].copy_(w2.reshape(-1))
+        del g["f16"]
+        host_f16 = torch.empty((s.E, 3 * s.H * s.I), dtype=torch.float16, pin_memory=True)
+        host_f16.copy_(full[l])
+        layers.append(ChunkLayer(router=g["router"], int4=g["int4"], host_f16=host_f16,
+                                 shared=(g["shared"]["w13"], g["shared"]["w2"]),
+                                 shared_gate=g["shared"]["gate"]))
+        print(f"generated layer {l}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t0
+    eng = ChunkEngine(layers, s.H, s.E, s.k, s.I, s.shared_I, NRES, TV, device=dev)
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+
+    def chunk(c, timed):
+        xs = [torch.from_numpy(synth.tokens(s, 1, step=1000 * c + st)).to(dev)
+              for st in range(STEPS)]
+        xv = torch.cat(xs + [torch.from_numpy(synth.tokens(s, 1, step=1000 * c + STEPS)).to(dev)])
+        ev = [mk() for _ in range(5)]
+        eng.clear_counters()
+        before = dict(eng.stats)
+        ev[0].record()
+        rec = []
+        for st in range(STEPS):
+            eng.draft_step(xs[st], rec)
+        ev[1].record()
+        counts = eng.snapshot()
+        eng.place_residents(counts)
+        ev[2].record()
+        eng.verify(xv)
+        ev[3].record()
+        eng.verify(xv, all_resident=full)
+        ev[4].record()
+        torch.cuda.synchronize()
+        # T = 1: each layer-step reads exactly k distinct INT4 experts
+        assert all(int(r["ids"].unique().numel()) == s.k for r in rec)
+        d = {k2: eng.stats[k2] - before[k2] for k2 in eng.stats}
+        return dict(draft_ms=ev[0].elapsed_time(ev[1]), place_ms=ev[1].elapsed_time(ev[2]),
+                    verify_ms=ev[2].elapsed_time(ev[3]), verify_res_ms=ev[3].elapsed_time(ev[4]),
+                    int4_bytes=STEPS * L * s.k * s.int4_bytes_per_expert,
+                    shared_bytes=STEPS * L * s.shared_f16_bytes, stats=d,
+                    place_bytes=L * NRES * s.f16_bytes_per_expert)
+
+    for c in range(args.warmup and 1):
+        chunk(c, False)
+    res_list = [chunk(100 + c, True) for c in range(max(1, min(args.steps, 3)))]
+    n = len(res_list)
+    avg = lambda key: sum(r[key] for r in res_list) / n
+    draft_ms, verify_ms, verify_res_ms, place_ms = (avg("draft_ms"), avg("verify_ms"),
+                                                    avg("verify_res_ms"), avg("place_ms"))
+    int4_b, sh_b = avg("int4_bytes"), avg("shared_bytes")
+    staged = sum(r["stats"]["staged_bytes"] for r in res_list) / n
+    hits = sum(r["stats"]["hit_experts"] for r in res_list) / n
+    misses = sum(r["stats"]["miss_experts"] for r in res_list) / n
+    flops_v = 2.0 * TV * s.k * 3 * s.H * s.I * L + 2.0 * TV * 3 * s.H * s.shared_I * L
+    touched_v = (hits + misses)
+    vbytes = touched_v * s.f16_bytes_per_expert + L * s.shared_f16_bytes
+    value = int4_b / (draft_ms * 1e-3) / 1e9
+    out = {
+        "metric": "MoE-layer INT4 draft weight GB/s (% HBM peak); verify TFLOP/s (% MFMA)",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": n, "warmup": 1,
+        "ms_per_step": round(draft_ms + place_ms + verify_ms, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4-w/fp16-a (draft), fp16 (verify); fp32 accumulate",
+        "data": "synthetic (seeded N(0,0.02) weights from torch Philox, N(0,1) tokens)",
+        "config": {"workload": f"qwen15_moe_chunk: {L} layers H=2048 E=60 top-4 I=1408 + shared "
+                               f"5632 gated; 16 draft steps (T=1), ELB [{L},60], 16/60 resident, "
+                               f"verify K+1=17 with staged misses"},
+        "draft": {"ms": round(draft_ms, 3), "int4_gbps": round(value, 2),
+                  "int4_plus_shared_gbps": round((int4_b + sh_b) / (draft_ms * 1e-3) / 1e9, 2),
+                  "int4_bytes": round(int4_b), "shared_f16_bytes": round(sh_b),
+                  "us_per_layer_step": round(1e3 * draft_ms / (STEPS * L), 2)},
+        "placement": {"ms": round(place_ms, 3), "bytes": res_list[0]["place_bytes"],
+                      "h2d_gbps": round(res_list[0]["place_bytes"] / (place_ms * 1e-3) / 1e9, 2)},
+        "verify_staged": {"ms": round(verify_ms, 3), "hits": hits, "misses": misses,
+                          "staged_bytes": round(staged),
+                          "staged_gbps_over_verify": round(staged / (verify_ms * 1e-3) / 1e9, 2)},
+        "verify_all_resident": {"ms": round(verify_res_ms, 3),
+                                "tflops": round(flops_v / (verify_res_ms * 1e-3) / 1e12, 3),
+                                "frac_mfma": round(flops_v / (verify_res_ms * 1e-3) / 1e12
+                                                   / MFMA_F16_PEAK_TFS, 5),
+                                "weight_gbps": round(vbytes / (verify_res_ms * 1e-3) / 1e9, 2)},
+        "gen_s": round(gen_s, 1),
+    }
+    print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(layer, s, n):

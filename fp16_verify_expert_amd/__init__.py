@@ -48,7 +48,8 @@ _SIGS = {
                                _sz, _vp, _vp]),
     "verify_grouped_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp,
                                  _vp, _sz, _vp, _vp]),
-    "moe_combine": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
+    "moe_combine": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, ctypes.c_float,
+                         _vp]),
     "expert_stage_async": (_i, [_vp, _vp, _sz, _vp, _vp]),
 }
 
@@ -211,14 +212,20 @@ def verify_grouped_gemm(x, sorted_token, offsets, table, T: int, rows: int, H: i
 
 
 def moe_combine(y_sorted, pair_pos, topk_w, shared_out=None, shared_scale=None, residual=None,
-                *, out=None, stream=None):
+                *, out=None, norm_out=None, norm_eps: float = 1e-6, stream=None):
+    """Returns out, or (out, norm_out) when norm_out is given (a tensor, or
+    True to allocate one)."""
     T, k = topk_w.shape
     H = y_sorted.shape[1]
     if out is None:
         out = torch.empty((T, H), dtype=torch.float16, device=y_sorted.device)
+    want_norm = norm_out is not None and norm_out is not False
+    if norm_out is True:
+        norm_out = torch.empty((T, H), dtype=torch.float16, device=y_sorted.device)
     _call("moe_combine", _p(y_sorted), _p(pair_pos), _p(topk_w), _p(shared_out),
-          _p(shared_scale), _p(residual), T, k, H, _p(out), _s(stream))
-    return out
+          _p(shared_scale), _p(residual), T, k, H, _p(out),
+          _p(norm_out) if want_norm else None, float(norm_eps), _s(stream))
+    return (out, norm_out) if want_norm else out
 
 
 def expert_stage_async(dst: torch.Tensor, src_pinned: torch.Tensor, side_stream=None,

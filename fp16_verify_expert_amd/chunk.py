@@ -13,8 +13,10 @@ memory.
 This module only sequences calls of the C ABI (routing, ELB counters, gather,
 W4A16 draft FFN, FP16 verify FFN with an expert mask, combine, expert staging)
 and does the host-side bookkeeping the copies need (which experts are resident,
-which are missing, where each expert's weights live).  Layers are chained by a
-residual: x <- x + MoE(x).
+which are missing, where each expert's weights live).  Layers are pre-norm
+residual blocks: x <- x + MoE(rms(x)), the normalised input of the next layer
+being written by the combine epilogue; the first layer takes the incoming
+token rows (unit RMS in expectation) as its normalised input.
 """
 from __future__ import annotations
 
@@ -95,17 +97,18 @@ class ChunkEngine:
     def draft_step(self, x: torch.Tensor, record: Optional[list] = None) -> torch.Tensor:
         """One INT4 draft decode step (T = 1) through all layers, counting each
         layer's expert choices in the ELB table."""
+        xn = x
         for l, ly in enumerate(self.layers):
-            ids, w, gate = moe_route_topk(x, ly.router, self.k, False, ly.shared_gate)
+            ids, w, gate = moe_route_topk(xn, ly.router, self.k, False, ly.shared_gate)
             elb_count(ids, self.E, l, self.counters, self.err)
             maps = moe_gather(ids, self.E, self.err)
-            y = w4a16_grouped_ffn(x, maps, self.t4[l], 1, self.k, self.H, self.I, self.E,
+            y = w4a16_grouped_ffn(xn, maps, self.t4[l], 1, self.k, self.H, self.I, self.E,
                                   self.ws_d, err_word=self.err)
-            sh = self._shared(l, x)
-            out = moe_combine(y, maps["pair_pos"], w, sh, gate, x)
+            sh = self._shared(l, xn)
+            out, xn_next = moe_combine(y, maps["pair_pos"], w, sh, gate, x, norm_out=True)
             if record is not None:
-                record.append(dict(layer=l, x=x, ids=ids, out=out))
-            x = out
+                record.append(dict(layer=l, x=x, xn=xn, ids=ids, out=out, xn_next=xn_next))
+            x, xn = out, xn_next
         return x
 
     def snapshot(self) -> np.ndarray:
@@ -134,8 +137,9 @@ class ChunkEngine:
         from there instead (the reference for residency invariance)."""
         main = torch.cuda.current_stream()
         T = x.shape[0]
+        xn = x
         for l, ly in enumerate(self.layers):
-            ids, w, gate = moe_route_topk(x, ly.router, self.k, False, ly.shared_gate)
+            ids, w, gate = moe_route_topk(xn, ly.router, self.k, False, ly.shared_gate)
             maps = moe_gather(ids, self.E, self.err)
             rows = T * self.k
             y = torch.empty((rows, self.H), dtype=torch.float16, device=self.dev)
@@ -146,17 +150,17 @@ class ChunkEngine:
                     tab[e, 0] = base[e].data_ptr()
                     tab[e, 1] = base[e].data_ptr() + self.w13_bytes
                 self.d_table[l].copy_(tab, non_blocking=True)
-                verify_grouped_gemm(x, maps["sorted_token"], maps["offsets"], self.d_table[l], T,
-                                    rows, self.H, self.I, self.E, self.ws_v,
+                verify_grouped_gemm(xn, maps["sorted_token"], maps["offsets"], self.d_table[l],
+                                    T, rows, self.H, self.I, self.E, self.ws_v,
                                     active=maps["active"], n_active=maps["n_active"],
                                     y_sorted=y, err_word=self.err)
             else:
-                self._verify_staged(l, x, maps, y, main)
-            sh = self._shared(l, x)
-            out = moe_combine(y, maps["pair_pos"], w, sh, gate, x)
+                self._verify_staged(l, xn, maps, y, main)
+            sh = self._shared(l, xn)
+            out, xn_next = moe_combine(y, maps["pair_pos"], w, sh, gate, x, norm_out=True)
             if record is not None:
-                record.append(dict(layer=l, x=x, ids=ids, out=out))
-            x = out
+                record.append(dict(layer=l, x=x, xn=xn, ids=ids, out=out, xn_next=xn_next))
+            x, xn = out, xn_next
         return x
 
     def _verify_staged(self, l, x, maps, y, main) -> None:

@@ -215,7 +215,7 @@ smoe_status verify_grouped_gemm(const uint16_t* x, const int32_t* sorted_token,
 smoe_status moe_combine(const uint16_t* y_sorted, const int32_t* pair_pos, const float* topk_w,
                         const uint16_t* shared_out, const float* shared_scale,
                         const uint16_t* residual, int T, int k, int H, uint16_t* out,
-                        void* stream) {
+                        uint16_t* norm_out, float norm_eps, void* stream) {
     REQUIRE(y_sorted && pair_pos && topk_w && out, SMOE_ERR_NULL,
             "moe_combine: y_sorted, pair_pos, topk_w and out are required");
     REQUIRE(T >= 0 && T <= 65535, SMOE_ERR_SHAPE, "moe_combine: T=%d must be in [0, 65535]", T);
@@ -223,12 +223,14 @@ smoe_status moe_combine(const uint16_t* y_sorted, const int32_t* pair_pos, const
     REQUIRE(H > 0 && H % 128 == 0, SMOE_ERR_SHAPE, "moe_combine: H=%d must be a multiple of 128",
             H);
     REQUIRE(aligned(y_sorted, 16) && aligned(shared_out, 16) && aligned(residual, 16) &&
-                aligned(out, 16),
+                aligned(out, 16) && aligned(norm_out, 16),
             SMOE_ERR_SHAPE, "moe_combine: fp16 tensors must be 16-byte aligned");
+    REQUIRE(!norm_out || (norm_eps >= 0.0f && norm_out != out), SMOE_ERR_SHAPE,
+            "moe_combine: norm_out needs norm_eps >= 0 and must not alias out");
     if (T == 0) return ok();
     CHECK_DEVICE();
     return hip_result(smoe::launch_combine(y_sorted, pair_pos, topk_w, shared_out, shared_scale,
-                                           residual, T, k, H, out,
+                                           residual, T, k, H, out, norm_out, norm_eps,
                                            static_cast<hipStream_t>(stream)),
                       "moe_combine launch");
 }

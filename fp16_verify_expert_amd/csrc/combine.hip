@@ -1,8 +1,10 @@
 // Weighted combine of the routed experts' outputs (plus shared expert and an
 // optional residual).  The pages leave this step implicit; it is the usual
-// routed-MoE weighted sum.  One thread owns 8 adjacent hidden elements of one
-// token (16-byte loads and stores); sums are fp32 in a fixed order (slots in
-// increasing j, then the shared term, then the residual), rounded once.
+// routed-MoE weighted sum.  One workgroup per token; a thread owns 8 adjacent
+// hidden elements at a time (16-byte loads and stores); sums are fp32 in a
+// fixed order (slots in increasing j, then the shared term, then the
+// residual), rounded once.  Optionally the epilogue also writes the row
+// RMS-normalised (the next pre-norm layer's input), from the rounded values.
 #include "common.h"
 
 namespace {
@@ -21,28 +23,61 @@ __device__ __forceinline__ void add8(float (&acc)[8], uint4 v, float w) {
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     const uint16_t* __restrict__ y, const int32_t* __restrict__ pp, const float* __restrict__ w,
     const uint16_t* __restrict__ shared, const float* __restrict__ sscale,
-    const uint16_t* resid, int k, int H, uint16_t* out) {
-    const int t = blockIdx.y;
-    const int c8 = blockIdx.x * kCombThreads + threadIdx.x;  // 8-element chunk
-    if (c8 * 8 >= H) return;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-        const int r = pp[(size_t)t * k + j];
-        if (r < 0) continue;
-        const uint4 v = reinterpret_cast<const uint4*>(y + (size_t)r * H)[c8];
-        add8(acc, v, w[(size_t)t * k + j]);
+    const uint16_t* resid, int k, int H, uint16_t* out, uint16_t* __restrict__ norm_out,
+    float eps) {
+    __shared__ float red[kCombThreads / 64];
+    const int t = blockIdx.x;
+    const int nch = H / 8;
+    float sq = 0.0f;  // sum of squares of the rounded outputs (norm_out only)
+    for (int c8 = threadIdx.x; c8 < nch; c8 += kCombThreads) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < k; ++j) {
+            const int r = pp[(size_t)t * k + j];
+            if (r < 0) continue;
+            const uint4 v = reinterpret_cast<const uint4*>(y + (size_t)r * H)[c8];
+            add8(acc, v, w[(size_t)t * k + j]);
+        }
+        if (shared) {
+            const float c = sscale ? sscale[t] : 1.0f;
+            add8(acc, reinterpret_cast<const uint4*>(shared + (size_t)t * H)[c8], c);
+        }
+        if (resid) add8(acc, reinterpret_cast<const uint4*>(resid + (size_t)t * H)[c8], 1.0f);
+        uint16_t o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            o[i] = f2h(acc[i]);
+            const float r = h2f(o[i]);
+            sq += r * r;
+        }
+        uint4 ov;
+        ov.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+        ov.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+        ov.z = (uint32_t)o[4] | ((uint32_t)o[5] << 16);
+        ov.w = (uint32_t)o[6] | ((uint32_t)o[7] << 16);
+        reinterpret_cast<uint4*>(out + (size_t)t * H)[c8] = ov;
     }
-    if (shared) {
-        const float c = sscale ? sscale[t] : 1.0f;
-        add8(acc, reinterpret_cast<const uint4*>(shared + (size_t)t * H)[c8], c);
+    if (!norm_out) return;
+    // row mean of squares (fixed-order tree over the block)
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) sq += __shfl_xor(sq, d);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = sq;
+    __syncthreads();
+    float tot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kCombThreads / 64; ++i) tot += red[i];
+    const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+    for (int c8 = threadIdx.x; c8 < nch; c8 += kCombThreads) {
+        const uint4 v = reinterpret_cast<const uint4*>(out + (size_t)t * H)[c8];
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+        uint32_t q[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint16_t lo = f2h(h2f((uint16_t)(u[i] & 0xFFFFu)) * inv);
+            const uint16_t hi = f2h(h2f((uint16_t)(u[i] >> 16)) * inv);
+            q[i] = (uint32_t)lo | ((uint32_t)hi << 16);
+        }
+        reinterpret_cast<uint4*>(norm_out + (size_t)t * H)[c8] = make_uint4(q[0], q[1], q[2], q[3]);
     }
-    if (resid) add8(acc, reinterpret_cast<const uint4*>(resid + (size_t)t * H)[c8], 1.0f);
-    uint4 o;
-    o.x = (uint32_t)f2h(acc[0]) | ((uint32_t)f2h(acc[1]) << 16);
-    o.y = (uint32_t)f2h(acc[2]) | ((uint32_t)f2h(acc[3]) << 16);
-    o.z = (uint32_t)f2h(acc[4]) | ((uint32_t)f2h(acc[5]) << 16);
-    o.w = (uint32_t)f2h(acc[6]) | ((uint32_t)f2h(acc[7]) << 16);
-    reinterpret_cast<uint4*>(out + (size_t)t * H)[c8] = o;
 }
 
 }  // namespace
@@ -50,10 +85,10 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
 namespace smoe {
 hipError_t launch_combine(const uint16_t* y, const int32_t* pp, const float* w,
                           const uint16_t* shared, const float* sscale, const uint16_t* resid,
-                          int T, int k, int H, uint16_t* out, hipStream_t s) {
-    const int chunks = H / 8;
-    const dim3 grid((chunks + kCombThreads - 1) / kCombThreads, T);
-    combine_kernel<<<grid, dim3(kCombThreads), 0, s>>>(y, pp, w, shared, sscale, resid, k, H, out);
+                          int T, int k, int H, uint16_t* out, uint16_t* norm_out, float eps,
+                          hipStream_t s) {
+    combine_kernel<<<dim3(T), dim3(kCombThreads), 0, s>>>(y, pp, w, shared, sscale, resid, k, H,
+                                                           out, norm_out, eps);
     return hipGetLastError();
 }
 }  // namespace smoe

@@ -58,5 +58,6 @@ hipError_t launch_verify_ffn(const uint16_t* x, const int32_t* sorted_token, con
 size_t verify_workspace_bytes(int T, int rows, int H, int I, int E);
 hipError_t launch_combine(const uint16_t* y, const int32_t* pp, const float* w,
                           const uint16_t* shared, const float* sscale, const uint16_t* resid,
-                          int T, int k, int H, uint16_t* out, hipStream_t s);
+                          int T, int k, int H, uint16_t* out, uint16_t* norm_out, float eps,
+                          hipStream_t s);
 }  // namespace smoe

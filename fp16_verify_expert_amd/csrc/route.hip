@@ -64,6 +64,15 @@ __device__ __forceinline__ float pinned_dot(const uint4* __restrict__ xr,
     return s;
 }
 
+// Ranking of (logit, expert id) pairs: larger logit first, NaN below every
+// number, equal logits (or two NaNs) lower id first.
+__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
+    const bool na = va != va, nb = vb != vb;
+    if (na != nb) return nb;
+    if (!na && va != vb) return va > vb;
+    return ia < ib;
+}
+
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const uint16_t* __restrict__ wsg, int H, int E, int k, int renorm,
@@ -101,7 +110,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = lane + 64 * i;
-            if (live[i] && (bi == 0x7fffffff || v[i] > bv || (v[i] == bv && e < bi))) {
+            if (live[i] && (bi == 0x7fffffff || ranks_before(v[i], e, bv, bi))) {
                 bv = v[i];
                 bi = e;
             }
@@ -110,8 +119,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
         for (int d = 32; d >= 1; d >>= 1) {
             const float ov = __shfl_xor(bv, d);
             const int oi = __shfl_xor(bi, d);
-            if (oi != 0x7fffffff &&
-                (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
+            if (oi != 0x7fffffff && (bi == 0x7fffffff || ranks_before(ov, oi, bv, bi))) {
                 bv = ov;
                 bi = oi;
             }

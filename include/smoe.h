@@ -233,11 +233,16 @@ smoe_status verify_grouped_gemm(const uint16_t* x, const int32_t* sorted_token,
  *   residual     fp16 [T, H] optional (NULL = none)
  *   pairs with pair_pos == -1 contribute nothing.
  *   out          fp16 [T, H]; may alias residual.
+ *   norm_out     fp16 [T, H] optional (NULL = none): the next pre-norm
+ *                layer's input, out[t] / sqrt(mean(out[t]^2) + norm_eps)
+ *                computed from the rounded out (the pages say draft and
+ *                target share the normalisation without defining it; this
+ *                is a unit-weight RMS norm).  Must not alias out.
  * ---------------------------------------------------------------------- */
 smoe_status moe_combine(const uint16_t* y_sorted, const int32_t* pair_pos, const float* topk_w,
                         const uint16_t* shared_out, const float* shared_scale,
                         const uint16_t* residual, int T, int k, int H, uint16_t* out,
-                        void* stream);
+                        uint16_t* norm_out, float norm_eps, void* stream);
 
 /* ------------------------------------------------------------------------
  * expert_stage_async -- copy one non-resident expert from page-locked host

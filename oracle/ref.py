@@ -30,6 +30,7 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
   per_token_ffn .................... pinned (equals grouped_ffn, the pages'
                                      "mathematically identical" claim)
   combine .......................... pinned (k=1 identity, hand sums)
+  rms_norm ......................... pinned (constant rows, scale invariance)
 """
 from __future__ import annotations
 
@@ -45,7 +46,7 @@ __all__ = [
     "logits_pinned_f32", "logits_f64", "route_topk", "elb_update", "gather_maps",
     "unpack_gptq", "dequant_gptq", "silu", "swiglu_ffn", "expert_ffn_f16",
     "expert_ffn_int4", "grouped_ffn", "per_token_ffn", "combine", "moe_layer",
-    "to_f16",
+    "to_f16", "rms_norm",
 ]
 
 
@@ -391,16 +392,29 @@ def combine(y_sorted: np.ndarray, pair_pos: np.ndarray, weights: np.ndarray,
     return out
 
 
+def rms_norm(x: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) per row, fp64, unit weight.
+
+    R17: the pages say draft and target share the non-expert parts, the
+    normalisation included ([S1] Methodology), without defining them.  Layers
+    of a multi-layer chunk are pre-norm residual blocks x <- x + MoE(rms(x)),
+    the plainest reading that keeps a synthetic chain finite.
+    """
+    a = np.asarray(x).astype(np.float64)
+    return a / np.sqrt(np.mean(a * a, axis=-1, keepdims=True) + eps)
+
+
 # ---------------------------------------------------------------------------
 # whole layer (the plain definition)
 # ---------------------------------------------------------------------------
 
 def moe_layer(x: np.ndarray, w_router: np.ndarray, k: int, experts: Sequence, kind: str,
               shared: Optional[Dict] = None, renormalize: bool = False,
-              residual: bool = False, dtype=np.float64) -> Dict[str, np.ndarray]:
+              residual=None, dtype=np.float64) -> Dict[str, np.ndarray]:
     """One routed-expert MoE layer: route, group, per-expert FFN, combine.
 
-    out_t = sum_j w_tj FFN_(ids_tj)(x_t) + c_t FFN_shared(x_t)  (+ x_t).
+    out_t = sum_j w_tj FFN_(ids_tj)(x_t) + c_t FFN_shared(x_t)  (+ r_t),
+    with r the `residual` array (or x itself when `residual` is True).
     [S1 Key Contributions 2] routers and shared experts are FP16 in both the
     draft and the target; only routed experts are INT4 in the draft.
     """
@@ -412,6 +426,9 @@ def moe_layer(x: np.ndarray, w_router: np.ndarray, k: int, experts: Sequence, ki
     sh = None
     if shared is not None:
         sh = expert_ffn_f16(x, shared["w13"], shared["w2"], dtype)
-    out = combine(y, maps["pair_pos"], r["weights"], sh, r["gate"],
-                  x if residual else None, dtype)
+    if residual is True:
+        residual = x
+    elif residual is False:
+        residual = None
+    out = combine(y, maps["pair_pos"], r["weights"], sh, r["gate"], residual, dtype)
     return dict(route=r, maps=maps, y_sorted=y, shared_out=sh, out=out)

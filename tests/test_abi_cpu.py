@@ -98,10 +98,16 @@ def test_verify_validation():
 
 def test_combine_validation():
     L = fve.lib()
-    assert L.moe_combine(FAKE, FAKE, None, None, None, None, 1, 2, 256, FAKE, None) == 1
-    assert L.moe_combine(FAKE, FAKE, FAKE, None, None, None, 70000, 2, 256, FAKE, None) == 2
-    assert L.moe_combine(FAKE, FAKE, FAKE, V(0x1008), None, None, 1, 2, 256, FAKE, None) == 2
-    assert L.moe_combine(FAKE, FAKE, FAKE, None, None, None, 0, 2, 256, FAKE, None) == 0
+    assert L.moe_combine(FAKE, FAKE, None, None, None, None, 1, 2, 256, FAKE, None, 0.0, None) == 1
+    assert L.moe_combine(FAKE, FAKE, FAKE, None, None, None, 70000, 2, 256, FAKE, None, 0.0,
+                         None) == 2
+    assert L.moe_combine(FAKE, FAKE, FAKE, V(0x1008), None, None, 1, 2, 256, FAKE, None, 0.0,
+                         None) == 2
+    assert L.moe_combine(FAKE, FAKE, FAKE, None, None, None, 1, 2, 256, FAKE, FAKE, 1e-6,
+                         None) == 2                                   # norm_out aliases out
+    assert L.moe_combine(FAKE, FAKE, FAKE, None, None, None, 1, 2, 256, FAKE, V(0x2000), -1.0,
+                         None) == 2
+    assert L.moe_combine(FAKE, FAKE, FAKE, None, None, None, 0, 2, 256, FAKE, None, 0.0, None) == 0
 
 
 def test_stage_validation():

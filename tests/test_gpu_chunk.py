@@ -3,8 +3,10 @@
 with a sigmoid gate; 16 resident experts per layer, the rest staged from
 pinned host memory).
 
-Parity is teacher-forced per layer: the oracle recomputes layer l from the
-GPU's own layer-l input.  The ELB table must equal the oracle's counts of the
+Layers are pre-norm residual blocks x <- x + MoE(rms(x)).  Parity is
+teacher-forced per layer: the oracle recomputes layer l from the GPU's own
+layer-l input (normalised input and residual), and the fused normalisation
+of each layer's output against the oracle's rms_norm.  The ELB table must equal the oracle's counts of the
 same inputs exactly; the verify output must be bit-identical to a run with
 every expert resident (staging changes where weights come from, never what is
 computed)."""
@@ -79,6 +81,8 @@ def _shared_np(g):
 
 def test_chunk_error_word_clear(chunk):
     assert int(host(chunk["eng"].err)[0]) == 0
+    for r in chunk["rec_d"] + chunk["rec_v"]:
+        assert torch.isfinite(r["out"]).all()
 
 
 def test_chunk_elb_counters_exact(chunk):
@@ -86,7 +90,7 @@ def test_chunk_elb_counters_exact(chunk):
     ref = np.zeros((LAYERS, s.E), np.int32)
     for r in chunk["rec_d"]:
         g = chunk["gen"][r["layer"]]
-        x = host(r["x"])
+        x = host(r["xn"])
         ro = oracle.route_topk(x, host(g["router"]), s.k, False, host(g["shared"]["gate"]))
         assert np.array_equal(host(r["ids"]), ro["ids"])
         ref = oracle.elb_update(ref, ro["ids"], r["layer"])
@@ -100,13 +104,15 @@ def test_chunk_draft_layers_teacher_forced(chunk, step):
     for l in range(LAYERS):
         r = chunk["rec_d"][step * LAYERS + l]
         g = chunk["gen"][l]
-        x = host(r["x"])
+        xn = host(r["xn"])
         ids = host(r["ids"])
         experts = _np_layer(g, sorted(set(ids.ravel().tolist())), "int4")
-        ref = oracle.moe_layer(x, host(g["router"]), s.k, experts, "int4", _shared_np(g),
-                               residual=True)
+        ref = oracle.moe_layer(xn, host(g["router"]), s.k, experts, "int4", _shared_np(g),
+                               residual=host(r["x"]))
         assert np.array_equal(ids, ref["route"]["ids"])
         assert_fp16_close(host(r["out"]), ref["out"], f"draft step {step} layer {l}")
+        assert_fp16_close(host(r["xn_next"]), oracle.rms_norm(host(r["out"])),
+                          f"draft step {step} layer {l} norm")
 
 
 def test_chunk_residency_from_snapshot(chunk):
@@ -124,13 +130,15 @@ def test_chunk_verify_teacher_forced(chunk):
     for r in chunk["rec_v"]:
         l = r["layer"]
         g = chunk["gen"][l]
-        x = host(r["x"])
+        xn = host(r["xn"])
         ids = host(r["ids"])
         experts = _np_layer(g, sorted(set(ids.ravel().tolist())), "f16")
-        ref = oracle.moe_layer(x, host(g["router"]), s.k, experts, "f16", _shared_np(g),
-                               residual=True)
+        ref = oracle.moe_layer(xn, host(g["router"]), s.k, experts, "f16", _shared_np(g),
+                               residual=host(r["x"]))
         assert np.array_equal(ids, ref["route"]["ids"])
         st = assert_fp16_close(host(r["out"]), ref["out"], f"verify layer {l}")
+        assert_fp16_close(host(r["xn_next"]), oracle.rms_norm(host(r["out"])),
+                          f"verify layer {l} norm")
         say(f"verify layer {l}: l2={st['l2']:.2e}")
     assert chunk["eng"].stats["staged_experts"] > 0
 

@@ -46,6 +46,21 @@ def test_route_topk(shape, T):
         assert np.allclose(host(gate), ref["gate"], rtol=W_RTOL, atol=1e-7)
 
 
+def test_route_nan_logits_rank_last():
+    # NaN logits rank below every number (the oracle's sort puts them last);
+    # the ids stay valid and distinct
+    s = synth.TINY
+    x = synth.tokens(s, 2)
+    w = synth.router(s).copy()
+    w[3, 0] = np.float16(np.inf)       # inf * 0-crossing products give NaN for x[0]=... below
+    x[:, 0] = 0.0                      # 0 * inf = NaN in expert 3's logit
+    ids, _, _ = fve.moe_route_topk(dev(x), dev(w), s.E)
+    ref = oracle.route_topk(x, w, s.E)
+    assert np.isnan(ref["logits32"][:, 3]).all()
+    assert np.array_equal(host(ids), ref["ids"])
+    assert host(ids)[:, -1].tolist() == [3, 3]
+
+
 def test_route_renormalize_and_ties():
     s = synth.TINY
     wr = synth.router(s)
@@ -314,6 +329,10 @@ def test_combine():
     ref1 = oracle.combine(y, pp, w.astype(np.float64))
     out1 = fve.moe_combine(dev(y), dev(pp), dev(w))
     assert_fp16_close(host(out1), ref1, "combine plain", l2=1e-3, maxabs=4e-3)
+    # fused RMS normalisation of the rounded output
+    o, nrm = fve.moe_combine(dev(y), dev(pp), dev(w), dev(sh), dev(c), dev(res), norm_out=True)
+    assert_fp16_close(host(nrm), oracle.rms_norm(host(o)), "combine norm", l2=1e-3, maxabs=4e-3)
+    assert np.array_equal(host(o), host(out))
     # k = 1, weight 1: a permutation copy, exact
     pp1 = rng.permutation(T).astype(np.int32)
     out2 = fve.moe_combine(dev(y[:T]), dev(pp1), dev(np.ones((T, 1), np.float32)))

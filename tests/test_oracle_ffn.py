@@ -297,3 +297,15 @@ def test_torch_rtn_matches_numpy_rtn():
     b = synth.torch_gptq_from_linear(torch.from_numpy(w))
     for x, y in zip(a, b):
         assert np.array_equal(x, y.numpy())
+
+
+def test_rms_norm_closed_forms():
+    x = np.array([[3.0] * 8, [-2.0] * 8, [1.0, -1.0] * 4])
+    y = oracle.rms_norm(x, eps=0.0)
+    assert np.allclose(y, np.sign(x), rtol=0, atol=1e-15)
+    z = oracle.rms_norm(np.zeros((1, 4)), eps=1e-6)
+    assert np.all(z == 0)
+    rng = np.random.default_rng(2)
+    a = rng.standard_normal((5, 256))
+    assert np.allclose(oracle.rms_norm(a * 7.0, eps=0.0), oracle.rms_norm(a, eps=0.0))
+    assert np.allclose(np.mean(oracle.rms_norm(a, eps=0.0) ** 2, axis=1), 1.0)
