@@ -44,6 +44,8 @@ _SIGS = {
     "moe_route_topk": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "elb_count": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
     "moe_gather": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_route_plan": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
+                            _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "w4a16_grouped_ffn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp,
                                _sz, _vp, _vp]),
     "verify_grouped_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp,
@@ -149,19 +151,55 @@ def moe_gather(topk_ids, E: int, err_word=None, *, out=None, stream=None):
     """Returns dict(offsets, sorted_token, sorted_pair, pair_pos, active, n_active)."""
     _check(topk_ids, torch.int32, "topk_ids")
     T, k = topk_ids.shape
-    dev = topk_ids.device
-    n = T * k
     if out is None:
-        out = dict(offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
-                   sorted_token=torch.empty(max(n, 1), dtype=torch.int32, device=dev),
-                   sorted_pair=torch.empty(max(n, 1), dtype=torch.int32, device=dev),
-                   pair_pos=torch.empty(max(n, 1), dtype=torch.int32, device=dev),
-                   active=torch.empty(E, dtype=torch.int32, device=dev),
-                   n_active=torch.empty(1, dtype=torch.int32, device=dev))
+        out = _new_maps(T, k, E, topk_ids.device)
     _call("moe_gather", _p(topk_ids), T, k, E, _p(out["offsets"]), _p(out["sorted_token"]),
           _p(out["sorted_pair"]), _p(out["pair_pos"]), _p(out["active"]), _p(out["n_active"]),
           _p(err_word), _s(stream))
     return out
+
+
+def _new_maps(T: int, k: int, E: int, dev) -> dict:
+    n = max(T * k, 1)
+    return dict(offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                sorted_token=torch.empty(n, dtype=torch.int32, device=dev),
+                sorted_pair=torch.empty(n, dtype=torch.int32, device=dev),
+                pair_pos=torch.empty(n, dtype=torch.int32, device=dev),
+                active=torch.empty(E, dtype=torch.int32, device=dev),
+                n_active=torch.empty(1, dtype=torch.int32, device=dev))
+
+
+def moe_route_plan(x, w_router, k: int, renormalize: bool = False, w_shared_gate=None, *,
+                   counters=None, layer: int = 0, err_word=None, topk_ids=None, topk_w=None,
+                   shared_gate=None, maps=None, stream=None):
+    """Routing, ELB update (when counters is given) and gather maps in one
+    launch.  Returns (topk_ids, topk_w, shared_gate, maps) with maps as from
+    moe_gather."""
+    _check(x, torch.float16, "x")
+    _check(w_router, torch.float16, "w_router")
+    T, H = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if w_shared_gate is not None:
+        _check(w_shared_gate, torch.float16, "w_shared_gate")
+        if shared_gate is None:
+            shared_gate = torch.empty((T,), dtype=torch.float32, device=dev)
+    L = 0
+    if counters is not None:
+        _check(counters, torch.int32, "counters")
+        L = counters.shape[0]
+    if maps is None:
+        maps = _new_maps(T, k, E, dev)
+    _call("moe_route_plan", _p(x), _p(w_router), _p(w_shared_gate), T, H, E, k,
+          1 if renormalize else 0, layer, L, _p(counters), _p(topk_ids), _p(topk_w),
+          _p(shared_gate) if w_shared_gate is not None else None, _p(maps["offsets"]),
+          _p(maps["sorted_token"]), _p(maps["sorted_pair"]), _p(maps["pair_pos"]),
+          _p(maps["active"]), _p(maps["n_active"]), _p(err_word), _s(stream))
+    return topk_ids, topk_w, shared_gate, maps
 
 
 def w4_expert_table(experts: Sequence, device="cuda") -> torch.Tensor:

@@ -11,7 +11,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsmoe.so")
 OBJ = os.path.join(PKG, "_build")
-SOURCES = ["abi.hip", "route.hip", "maps.hip", "w4a16.hip", "verify.hip", "combine.hip"]
+SOURCES = ["abi.hip", "route.hip", "maps.hip", "plan.hip", "w4a16.hip", "verify.hip",
+           "combine.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -26,7 +26,7 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (elb_count, expert_stage_async, f16_expert_table, moe_combine, moe_gather,
+from . import (expert_stage_async, f16_expert_table, moe_combine, moe_gather, moe_route_plan,
                moe_route_topk, new_workspace, verify_grouped_gemm, w4_expert_table,
                w4a16_grouped_ffn)
 
@@ -99,9 +99,10 @@ class ChunkEngine:
         layer's expert choices in the ELB table."""
         xn = x
         for l, ly in enumerate(self.layers):
-            ids, w, gate = moe_route_topk(xn, ly.router, self.k, False, ly.shared_gate)
-            elb_count(ids, self.E, l, self.counters, self.err)
-            maps = moe_gather(ids, self.E, self.err)
+            # routing, ELB update and gather maps in one launch
+            ids, w, gate, maps = moe_route_plan(xn, ly.router, self.k, False, ly.shared_gate,
+                                                counters=self.counters, layer=l,
+                                                err_word=self.err)
             y = w4a16_grouped_ffn(xn, maps, self.t4[l], 1, self.k, self.H, self.I, self.E,
                                   self.ws_d, err_word=self.err)
             sh = self._shared(l, xn)
@@ -110,6 +111,36 @@ class ChunkEngine:
                 record.append(dict(layer=l, x=x, xn=xn, ids=ids, out=out, xn_next=xn_next))
             x, xn = out, xn_next
         return x
+
+    # ------------------------------------------------------ draft graph ----
+    def capture_draft(self) -> None:
+        """Record one draft step (all layers, T = 1) as a HIP graph reading a
+        fixed input row; draft_step_graph then costs one launch per step.
+        Every buffer the step touches is allocated here, before capture, or
+        from the graph's private pool during it; the library's kernels write
+        no memsets."""
+        self.x_static = torch.zeros((1, self.H), dtype=torch.float16, device=self.dev)
+        side = torch.cuda.Stream(device=self.dev)
+        side.wait_stream(torch.cuda.current_stream())
+        # a first eager pass on the capture stream (one-time library set-up),
+        # then the counters are restored
+        saved = self.counters.clone()
+        with torch.cuda.stream(side):
+            self.draft_step(self.x_static)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.counters.copy_(saved)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.out_static = self.draft_step(self.x_static)
+        torch.cuda.synchronize()
+
+    def draft_step_graph(self, x: torch.Tensor) -> torch.Tensor:
+        """draft_step(x) through the captured graph; returns the graph's
+        output buffer (overwritten by the next replay)."""
+        self.x_static.copy_(x)
+        self.graph.replay()
+        return self.out_static
 
     def snapshot(self) -> np.ndarray:
         """Copy of the ELB table (synchronises)."""

@@ -151,6 +151,44 @@ smoe_status moe_gather(const int32_t* topk_ids, int T, int k, int E, int32_t* ex
                       "moe_gather launch");
 }
 
+smoe_status moe_route_plan(const uint16_t* x, const uint16_t* w_router,
+                           const uint16_t* w_shared_gate, int T, int H, int E, int k,
+                           int renormalize, int layer, int L, int32_t* counters,
+                           int32_t* topk_ids, float* topk_w, float* shared_gate,
+                           int32_t* expert_offsets, int32_t* sorted_token, int32_t* sorted_pair,
+                           int32_t* pair_pos, int32_t* active, int32_t* n_active,
+                           int32_t* err_word, void* stream) {
+    REQUIRE(expert_offsets && active && n_active, SMOE_ERR_NULL,
+            "moe_route_plan: expert_offsets, active and n_active are required");
+    REQUIRE(T == 0 || (x && w_router && topk_ids && topk_w && sorted_token && sorted_pair &&
+                       pair_pos),
+            SMOE_ERR_NULL,
+            "moe_route_plan: x, w_router, topk_ids, topk_w and the sorted maps are required");
+    REQUIRE(!w_shared_gate || shared_gate, SMOE_ERR_NULL,
+            "moe_route_plan: shared_gate output is required with w_shared_gate");
+    REQUIRE(T >= 0, SMOE_ERR_SHAPE, "moe_route_plan: T=%d < 0", T);
+    smoe_status st = check_hek(H, E, k);
+    if (st != SMOE_OK) return st;
+    REQUIRE((long long)T * k <= smoe::kPlanMaxPairs, SMOE_ERR_SHAPE,
+            "moe_route_plan: T*k=%lld exceeds %d (use the separate calls)", (long long)T * k,
+            smoe::kPlanMaxPairs);
+    REQUIRE((long long)T * (E + 1) <= smoe::kPlanMaxLogits, SMOE_ERR_SHAPE,
+            "moe_route_plan: T*(E+1)=%lld exceeds %d (use the separate calls)",
+            (long long)T * (E + 1), smoe::kPlanMaxLogits);
+    REQUIRE(!counters || (L >= 1 && layer >= 0 && layer < L), SMOE_ERR_SHAPE,
+            "moe_route_plan: layer=%d must be in [0, L=%d)", layer, L);
+    REQUIRE(aligned(x, 16) && aligned(w_router, 16) && aligned(w_shared_gate, 16),
+            SMOE_ERR_SHAPE, "moe_route_plan: x, w_router, w_shared_gate must be 16-byte aligned");
+    CHECK_DEVICE();
+    // T == 0 still writes empty maps (zero offsets, no active experts).
+    return hip_result(smoe::launch_route_plan(x, w_router, w_shared_gate, T, H, E, k,
+                                              renormalize ? 1 : 0, layer, counters, topk_ids,
+                                              topk_w, shared_gate, expert_offsets, sorted_token,
+                                              sorted_pair, pair_pos, active, n_active, err_word,
+                                              static_cast<hipStream_t>(stream)),
+                      "moe_route_plan launch");
+}
+
 smoe_status w4a16_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
                               const int32_t* expert_offsets, const int32_t* active,
                               const int32_t* n_active, const smoe_w4_expert* experts, int T,

@@ -39,6 +39,15 @@ namespace smoe {
 hipError_t launch_route_topk(const uint16_t* x, const uint16_t* wr, const uint16_t* wsg, int T,
                              int H, int E, int k, int renorm, int32_t* ids, float* w, float* gate,
                              hipStream_t s);
+// Fused route + ELB + gather (one workgroup): limits on T*k and on the
+// logits held in LDS.
+constexpr int kPlanMaxPairs = 1024;
+constexpr int kPlanMaxLogits = 4096;
+hipError_t launch_route_plan(const uint16_t* x, const uint16_t* wr, const uint16_t* wsg, int T,
+                             int H, int E, int k, int renorm, int layer, int32_t* counters,
+                             int32_t* ids, float* w, float* gate, int32_t* off, int32_t* st,
+                             int32_t* sp, int32_t* pp, int32_t* active, int32_t* n_active,
+                             int32_t* err, hipStream_t s);
 hipError_t launch_elb_count(const int32_t* ids, int n, int E, int layer, int32_t* counters,
                             int32_t* err, hipStream_t s);
 hipError_t launch_gather(const int32_t* ids, int n, int k, int E, int32_t* off, int32_t* st,

@@ -6,165 +6,25 @@
 // Key Contributions 4: the fused draft kernel gathers tokens by expert;
 // verification packs the tokens of one expert together.
 //
-// Both kernels aggregate equal expert ids inside a wave with ballots (one
-// atomic or one LDS update per distinct id per wave), so the integer results
-// are independent of scheduling.
-#include "common.h"
+// The device routines live in maps_core.h.
+#include "maps_core.h"
 
 namespace {
 
-__device__ __forceinline__ uint64_t lanemask_lt(int lane) {
-    return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-}
-
-// ------------------------------------------------------------------ ELB ----
 __global__ __launch_bounds__(256) void elb_count_kernel(const int32_t* __restrict__ ids, int n,
                                                         int E, int32_t* __restrict__ row,
                                                         int32_t* __restrict__ err) {
-    const int lane = threadIdx.x & 63;
-    for (int base = blockIdx.x * blockDim.x; base < n; base += gridDim.x * blockDim.x) {
-        const int p = base + (int)threadIdx.x;
-        const int e = (p < n) ? ids[p] : -1;
-        const bool valid = (p < n) && e >= 0 && e < E;
-        if (p < n && !valid) flag_error(err, SMOE_DERR_BAD_ID);
-        uint64_t todo = __ballot(valid);
-        while (todo) {
-            const int leader = __ffsll((unsigned long long)todo) - 1;
-            const int v = __shfl(e, leader);
-            const uint64_t same = __ballot(valid && e == v);
-            if (lane == leader) atomicAdd(row + v, (int32_t)__popcll(same));
-            todo &= ~same;
-        }
-    }
+    smoe_maps::elb_accumulate(ids, n, blockIdx.x * blockDim.x + threadIdx.x,
+                              gridDim.x * blockDim.x, E, row, err);
 }
 
-// --------------------------------------------------------------- gather ----
-constexpr int kGatherThreads = 1024;  // 16 waves
-constexpr int kGatherWaves = kGatherThreads / 64;
-
-__global__ __launch_bounds__(kGatherThreads) void gather_kernel(
+__global__ __launch_bounds__(smoe_maps::kGatherThreads) void gather_kernel(
     const int32_t* __restrict__ ids, int n, int k, int E, int32_t* __restrict__ off,
     int32_t* __restrict__ sorted_token, int32_t* __restrict__ sorted_pair,
     int32_t* __restrict__ pair_pos, int32_t* __restrict__ active, int32_t* __restrict__ n_active,
     int32_t* __restrict__ err) {
-    __shared__ int cnt[256];
-    __shared__ int base[256];
-    __shared__ int wcnt[kGatherWaves][256];
-    __shared__ int nvalid;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-
-    for (int e = tid; e < 256; e += kGatherThreads) cnt[e] = 0;
-    for (int i = tid; i < kGatherWaves * 256; i += kGatherThreads) (&wcnt[0][0])[i] = 0;
-    __syncthreads();
-
-    // 1. per-expert counts (ballot-aggregated LDS adds; order-free)
-    for (int c0 = 0; c0 < n; c0 += kGatherThreads) {
-        const int p = c0 + tid;
-        const int e = (p < n) ? ids[p] : -1;
-        const bool valid = (p < n) && e >= 0 && e < E;
-        if (p < n && !valid) flag_error(err, SMOE_DERR_BAD_ID);
-        uint64_t todo = __ballot(valid);
-        while (todo) {
-            const int leader = __ffsll((unsigned long long)todo) - 1;
-            const int v = __shfl(e, leader);
-            const uint64_t same = __ballot(valid && e == v);
-            if (lane == leader) atomicAdd(&cnt[v], (int)__popcll(same));
-            todo &= ~same;
-        }
-    }
-    __syncthreads();
-
-    // 2. exclusive scan of the counts and the active list (wave 0; E <= 256,
-    //    4 consecutive experts per lane)
-    if (wave == 0) {
-        int c[4], a[4];
-        int s = 0, na = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = 4 * lane + i;
-            c[i] = (e < E) ? cnt[e] : 0;
-            a[i] = (c[i] > 0) ? 1 : 0;
-            s += c[i];
-            na += a[i];
-        }
-        int incl = s, inca = na;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int o = __shfl_up(incl, d);
-            const int oa = __shfl_up(inca, d);
-            if (lane >= d) {
-                incl += o;
-                inca += oa;
-            }
-        }
-        int run = incl - s, runa = inca - na;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = 4 * lane + i;
-            if (e < E) {
-                base[e] = run;
-                off[e] = run;
-                if (a[i]) active[runa] = e;
-            }
-            run += c[i];
-            runa += a[i];
-        }
-        const int total = __shfl(incl, 63);
-        const int total_a = __shfl(inca, 63);
-        if (lane == 0) {
-            off[E] = total;
-            *n_active = total_a;
-            nvalid = total;
-        }
-        for (int e = total_a + lane; e < E; e += 64) active[e] = -1;
-    }
-    __syncthreads();
-
-    // 3. stable placement, one chunk of kGatherThreads pairs at a time:
-    //    position = base[e] + (same-expert pairs in earlier waves of the
-    //    chunk) + (same-expert lanes below this one in the wave)
-    for (int c0 = 0; c0 < n; c0 += kGatherThreads) {
-        const int p = c0 + tid;
-        const int e = (p < n) ? ids[p] : -1;
-        const bool valid = (p < n) && e >= 0 && e < E;
-        int rank = 0;
-        uint64_t todo = __ballot(valid);
-        while (todo) {
-            const int leader = __ffsll((unsigned long long)todo) - 1;
-            const int v = __shfl(e, leader);
-            const uint64_t same = __ballot(valid && e == v);
-            if (valid && e == v) rank = (int)__popcll(same & lanemask_lt(lane));
-            if (lane == leader) wcnt[wave][v] = (int)__popcll(same);
-            todo &= ~same;
-        }
-        __syncthreads();
-        if (valid) {
-            int pos = base[e] + rank;
-            for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
-            sorted_pair[pos] = p;
-            sorted_token[pos] = p / k;
-            pair_pos[p] = pos;
-        } else if (p < n) {
-            pair_pos[p] = -1;
-        }
-        __syncthreads();
-        for (int ee = tid; ee < E; ee += kGatherThreads) {
-            int add = 0;
-            for (int w = 0; w < kGatherWaves; ++w) {
-                add += wcnt[w][ee];
-                wcnt[w][ee] = 0;
-            }
-            base[ee] += add;
-        }
-        __syncthreads();
-    }
-    // rows past the last valid one (dropped pairs) carry -1
-    for (int r = nvalid + tid; r < n; r += kGatherThreads) {
-        sorted_pair[r] = -1;
-        sorted_token[r] = -1;
-    }
+    smoe_maps::gather_block(ids, n, k, E, off, sorted_token, sorted_pair, pair_pos, active,
+                            n_active, err);
 }
 
 }  // namespace
@@ -182,8 +42,8 @@ hipError_t launch_elb_count(const int32_t* ids, int n, int E, int layer, int32_t
 hipError_t launch_gather(const int32_t* ids, int n, int k, int E, int32_t* off, int32_t* st,
                          int32_t* sp, int32_t* pp, int32_t* active, int32_t* n_active,
                          int32_t* err, hipStream_t s) {
-    gather_kernel<<<dim3(1), dim3(kGatherThreads), 0, s>>>(ids, n, k, E, off, st, sp, pp, active,
-                                                            n_active, err);
+    gather_kernel<<<dim3(1), dim3(smoe_maps::kGatherThreads), 0, s>>>(ids, n, k, E, off, st, sp,
+                                                                       pp, active, n_active, err);
     return hipGetLastError();
 }
 }  // namespace smoe

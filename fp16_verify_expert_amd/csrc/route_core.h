@@ -1,0 +1,149 @@
+// Device routines of the top-k router, shared by the routing kernel and the
+// fused route + ELB + gather kernel (both must choose the same ids bit for
+// bit, so they run the very same code).
+//
+// The logit sum is taken in one pinned fp32 order: 8-element hidden chunks,
+// chunk c owned by lane c mod 64 of the wave, each lane adding its exact
+// fp16*fp16 products in increasing hidden index, then six xor-butterfly
+// rounds (distance 32 .. 1).  Contraction is switched off for every file that
+// includes this header: a fused multiply-add would give the same value (the
+// products are exact), but the compiler must not fold two products into one
+// dot instruction with a different rounding sequence.
+#pragma once
+
+#include "common.h"
+
+#pragma clang fp contract(off)
+
+namespace smoe_route {
+
+SMOE_DEV float acc_chunk(float s, uint4 xv, uint4 wv) {
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float x0 = h2f((uint16_t)(xw[i] & 0xFFFFu));
+        const float w0 = h2f((uint16_t)(ww[i] & 0xFFFFu));
+        const float x1 = h2f((uint16_t)(xw[i] >> 16));
+        const float w1 = h2f((uint16_t)(ww[i] >> 16));
+        const float p0 = x0 * w0;  // exact: 11-bit x 11-bit significands
+        s = s + p0;
+        const float p1 = x1 * w1;
+        s = s + p1;
+    }
+    return s;
+}
+
+// Pinned-order dot product of one fp16 row of x with one fp16 row of w,
+// evaluated by a whole wave; every lane returns the same value.  Each lane
+// first requests up to 8 of its chunks, then adds them in increasing order.
+SMOE_DEV float pinned_dot(const uint4* __restrict__ xr, const uint4* __restrict__ wrow, int nch,
+                          int lane) {
+    float s = 0.0f;
+    for (int c0 = 0; c0 < nch; c0 += 64 * 8) {
+        uint4 xv[8], wv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int c = c0 + lane + 64 * u;
+            if (c < nch) {
+                xv[u] = xr[c];
+                wv[u] = wrow[c];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int c = c0 + lane + 64 * u;
+            if (c < nch) s = acc_chunk(s, xv[u], wv[u]);
+        }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) s = s + __shfl_xor(s, d);
+    return s;
+}
+
+// Ranking of (logit, expert id) pairs: larger logit first, NaN below every
+// number, equal logits (or two NaNs) lower id first.
+SMOE_DEV bool ranks_before(float va, int ia, float vb, int ib) {
+    const bool na = va != va, nb = vb != vb;
+    if (na != nb) return nb;
+    if (!na && va != vb) return va > vb;
+    return ia < ib;
+}
+
+// One wave selects the top k of a token's E logits (lg, in LDS; lg[E] is the
+// shared-gate logit when has_gate) and writes ids, weights (softmax over all
+// E at the chosen ids, optionally renormalised over the k) and the gate.
+// ids_copy (nullable) receives the ids as well.
+SMOE_DEV void topk_softmax_wave(const float* lg, int E, int k, int renorm, bool has_gate,
+                                int lane, int32_t* ids, float* wout, float* gate,
+                                int32_t* ids_copy) {
+    float v[4];
+    bool live[4];
+    float mysel[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // lane j%64 keeps winner j
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        live[i] = e < E;
+        v[i] = live[i] ? lg[e] : 0.0f;
+    }
+    float m = 0.0f;  // largest logit (the first winner)
+    for (int j = 0; j < k; ++j) {
+        float bv = 0.0f;
+        int bi = 0x7fffffff;  // no candidate
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane + 64 * i;
+            if (live[i] && (bi == 0x7fffffff || ranks_before(v[i], e, bv, bi))) {
+                bv = v[i];
+                bi = e;
+            }
+        }
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) {
+            const float ov = __shfl_xor(bv, d);
+            const int oi = __shfl_xor(bi, d);
+            if (oi != 0x7fffffff && (bi == 0x7fffffff || ranks_before(ov, oi, bv, bi))) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        // every lane now holds the same winner
+        if (j == 0) m = bv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if ((bi & 63) == lane && (bi >> 6) == i) live[i] = false;
+            if ((j & 63) == lane && (j >> 6) == i) mysel[i] = bv;
+        }
+        if (lane == 0) {
+            ids[j] = bi;
+            if (ids_copy) ids_copy[j] = bi;
+        }
+    }
+
+    // softmax over all E at the chosen ids
+    float ssum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (lane + 64 * i < E) ssum += expf(v[i] - m);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) ssum = ssum + __shfl_xor(ssum, d);
+    float p[4];
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        p[i] = (lane + 64 * i < k) ? expf(mysel[i] - m) / ssum : 0.0f;
+        part += p[i];
+    }
+    if (renorm) {
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) part = part + __shfl_xor(part, d);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = lane + 64 * i;
+        if (j < k) wout[j] = renorm ? p[i] / part : p[i];
+    }
+    if (has_gate && lane == 0) *gate = 1.0f / (1.0f + expf(-lg[E]));
+}
+
+}  // namespace smoe_route

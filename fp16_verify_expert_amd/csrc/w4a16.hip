@@ -18,8 +18,11 @@
 // group reads 16 bytes = 4 adjacent columns, so a wave load is RPL = 64/LPR
 // rows of 4*LPR columns (64- or 128-byte runs per row).  The RPL lane groups
 // of every wave ("slots") each take whole 128-K quantisation groups, round
-// robin, streaming a group's 16 packed rows with 16 loads in flight per lane;
-// latency is hidden by the other waves resident on the SIMD.
+// robin, streaming a group's 16 packed rows with 16 loads in flight per lane
+// (and, for one-row experts, the next group's rows requested before the
+// current group is consumed); latency is hidden by the other waves resident on
+// the SIMD.  With one activation row per expert (a one-token step) the row and
+// the first weights are requested together before the row is staged.
 // In the gate/up projection a block is NB/2 gate columns next to the matching
 // NB/2 up columns, so SwiGLU is applied inside the workgroup.
 //
@@ -44,10 +47,19 @@ namespace {
 constexpr uint32_t kMagic = 0x64006400u;
 constexpr int kRowsPerGroup = 16;     // packed rows (8 K each) per 128-K group
 #ifndef SMOE_W4_MAX_WAVES
-#define SMOE_W4_MAX_WAVES 8
+#define SMOE_W4_MAX_WAVES 4
 #endif
 #ifndef SMOE_W4_MIN_WG
-#define SMOE_W4_MIN_WG 256
+#define SMOE_W4_MIN_WG 128
+#endif
+#ifndef SMOE_W4_MAX_GROUPS_PER_SLOT
+#define SMOE_W4_MAX_GROUPS_PER_SLOT 2
+#endif
+#ifndef SMOE_W4_ROWFENCE
+#define SMOE_W4_ROWFENCE 1
+#endif
+#ifndef SMOE_W4_PREFETCH
+#define SMOE_W4_PREFETCH 1
 #endif
 constexpr int kMaxWaves = SMOE_W4_MAX_WAVES;  // waves per workgroup (upper bound)
 constexpr int kLdsBytes = 32 * 1024;  // activation staging budget per workgroup
@@ -107,6 +119,9 @@ __device__ __forceinline__ void group_dot(const u4_t (&wv)[kRowsPerGroup],
         for (int c = 0; c < 4; ++c) ae[m][c] = ao[m][c] = 0.0f;
 #pragma unroll
     for (int i = 0; i < kRowsPerGroup; ++i) {
+        // one packed row at a time: keeps the activation reads from being
+        // hoisted ahead of the whole group (register pressure)
+        if (SMOE_W4_ROWFENCE) __builtin_amdgcn_sched_barrier(0);
         uint4 xp[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) xp[m] = xs[xoff[m] + i];
@@ -153,18 +168,40 @@ struct GroupLoad {
     uint32_t z;
 };
 
-__device__ __forceinline__ void load_group(GroupLoad& L, const smoe_w4_mat& wm, int g, int N,
-                                           int col, bool colok) {
-    gptr<u4_t> qp =
-        as_global(reinterpret_cast<const u4_t*>(wm.qweight + (size_t)(g * kRowsPerGroup) * N + col));
-    const int N4 = N >> 2;
+// Packed weights are read through a buffer resource: the lane's byte offset
+// (column and group) is one VGPR and the packed-row stride a scalar offset,
+// so a group's 16 row addresses cost no vector registers.
+struct W4Src {
+    __amdgpu_buffer_rsrc_t q;  // qweight [K/8, N] int32
+    smoe_w4_mat m;
+    int N;
+};
+
+constexpr int kBufWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 family
+constexpr int kAuxNT = 2;              // non-temporal (streamed once)
+
+__device__ __forceinline__ W4Src make_src(const smoe_w4_mat& m, int K, int N) {
+    W4Src s;
+    s.q = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(m.qweight), (short)0,
+                                            (K >> 3) * N * 4, kBufWord3);
+    s.m = m;
+    s.N = N;
+    return s;
+}
+
+__device__ __forceinline__ void load_group(GroupLoad& L, const W4Src& src, int g, int col,
+                                           bool colok) {
+    const int N = src.N;
+    const int voff = ((g * kRowsPerGroup) * N + col) * 4;
 #pragma unroll
     for (int i = 0; i < kRowsPerGroup; ++i)
-        L.w[i] = colok ? __builtin_nontemporal_load(qp + (size_t)i * N4) : u4_t{0, 0, 0, 0};
+        L.w[i] = colok ? __builtin_amdgcn_raw_buffer_load_b128(src.q, voff, i * N * 4, kAuxNT)
+                       : u4_t{0, 0, 0, 0};
     if (colok) {
-        const uint64_t sv = *as_global(reinterpret_cast<const uint64_t*>(wm.scales + (size_t)g * N + col));
+        const uint64_t sv =
+            *as_global(reinterpret_cast<const uint64_t*>(src.m.scales + (size_t)g * N + col));
         L.s = make_uint2((uint32_t)sv, (uint32_t)(sv >> 32));
-        L.z = (uint32_t)*as_global(wm.qzeros + (size_t)g * (N >> 3) + (col >> 3)) >> (4 * (col & 7));
+        L.z = (uint32_t)*as_global(src.m.qzeros + (size_t)g * (N >> 3) + (col >> 3)) >> (4 * (col & 7));
     } else {
         L.s = make_uint2(0, 0);
         L.z = 0;
@@ -193,6 +230,17 @@ __device__ __forceinline__ void group_step(const GroupLoad& L, const uint4* xs, 
     }
 }
 
+// Activations as the dot2 pairs the dequantised codes meet: (x0,x4), (x1,x5),
+// (x2,x6), (x3,x7) of each 8-element chunk.
+__device__ __forceinline__ uint4 pair_permute(uint4 d) {
+    uint4 p;
+    p.x = (d.x & 0xFFFFu) | (d.z << 16);      // (x0, x4)
+    p.y = (d.x >> 16) | (d.z & 0xFFFF0000u);  // (x1, x5)
+    p.z = (d.y & 0xFFFFu) | (d.w << 16);      // (x2, x6)
+    p.w = (d.y >> 16) | (d.w & 0xFFFF0000u);  // (x3, x7)
+    return p;
+}
+
 // Stage activation rows src_row(j), j < nrows, into LDS rows 0..nrows-1 as
 // dot2 pairs, then their per-group sums over even and odd k.
 template <typename RowPtr>
@@ -202,13 +250,7 @@ __device__ __forceinline__ void stage_rows(uint4* xs, float2* sums, int nrows, i
     for (int idx = threadIdx.x; idx < nrows * K8; idx += blockDim.x) {
         const int j = idx / K8;
         const int rr = idx - j * K8;
-        const uint4 d = src_row(j)[rr];
-        uint4 p;
-        p.x = (d.x & 0xFFFFu) | (d.z << 16);      // (x0, x4)
-        p.y = (d.x >> 16) | (d.z & 0xFFFF0000u);  // (x1, x5)
-        p.z = (d.y & 0xFFFFu) | (d.w << 16);      // (x2, x6)
-        p.w = (d.y >> 16) | (d.w & 0xFFFF0000u);  // (x3, x7)
-        xs[j * K8 + rr] = p;
+        xs[j * K8 + rr] = pair_permute(src_row(j)[rr]);
     }
     __syncthreads();
 #pragma unroll 1
@@ -229,8 +271,70 @@ __device__ __forceinline__ void stage_rows(uint4* xs, float2* sums, int nrows, i
     __syncthreads();
 }
 
+// Add the slots' partial sums of rows [mc, mc+M) in a fixed order and write
+// the epilogue: SwiGLU into h (gate/up projection) or y (down projection).
+template <int PHASE, int MAXM, int NB>
+__device__ __forceinline__ void reduce_store(const W4Args& a, float* red, const float (&acc)[MAXM][4],
+                                             int myslot, int nslots, int q, int cb, int mc, int M) {
+    const int tid = threadIdx.x;
+    __syncthreads();  // every slot is done with the activations in LDS
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m)
+        if (m < M)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) red[(myslot * MAXM + m) * NB + 4 * q + c] = acc[m][c];
+    __syncthreads();
+    if (PHASE == 1) {
+        for (int idx = tid; idx < M * (NB / 2); idx += blockDim.x) {
+            const int m = idx / (NB / 2);
+            const int j = idx - m * (NB / 2);
+            float gv = 0.0f, uv = 0.0f;
+            for (int s = 0; s < nslots; ++s) {
+                gv += red[(s * MAXM + m) * NB + j];
+                uv += red[(s * MAXM + m) * NB + NB / 2 + j];
+            }
+            a.out[(size_t)(mc + m) * a.I + cb * (NB / 2) + j] = f2h(silu_f(gv) * uv);
+        }
+    } else {
+        const int N = a.N;
+        for (int idx = tid; idx < M * NB; idx += blockDim.x) {
+            const int m = idx / NB;
+            const int j = idx - m * NB;
+            if (cb * NB + j < N) {
+                float v = 0.0f;
+                for (int s = 0; s < nslots; ++s) v += red[(s * MAXM + m) * NB + j];
+                a.out[(size_t)(mc + m) * N + cb * NB + j] = f2h(v);
+            }
+        }
+    }
+    __syncthreads();  // red is rewritten by the next row chunk
+}
+
+// A slot's groups g, g + nslots, ... of the reduction.  With kPrefetch the
+// next group's weights are requested before the current group is consumed.
+template <bool kPrefetch, int MAXM>
+__device__ __forceinline__ void run_groups(GroupLoad& cur, int g, int nslots, int G,
+                                           const W4Src& src, int col, bool colok,
+                                           const uint4* xs, const float2* sums,
+                                           const int (&xrow)[MAXM], int K8, int M, uint32_t mlo,
+                                           uint32_t mhi, float (&acc)[MAXM][4]) {
+    if (g >= G) return;
+    for (;;) {
+        const int gn = g + nslots;
+        GroupLoad nxt;
+        if (kPrefetch && gn < G) load_group(nxt, src, gn, col, colok);
+        group_step<MAXM>(cur, xs, sums, xrow, g, K8, G, M, mlo, mhi, acc);
+        if (gn >= G) break;
+        if (!kPrefetch) load_group(nxt, src, gn, col, colok);
+        cur = nxt;
+        g = gn;
+    }
+}
+
+constexpr int kRowChunksPerThread = 8;  // K/8 <= 2048 chunks over >= 256 threads
+
 template <int PHASE, int LPR, int MAXM>
-__global__ __launch_bounds__(64 * (MAXM == 1 ? kMaxWaves : 4)) void w4_kernel(W4Args a) {
+__global__ __launch_bounds__(64 * kMaxWaves) void w4_kernel(W4Args a) {
     constexpr int RPL = 64 / LPR;  // lane groups (slots) per wave
     constexpr int NB = 4 * LPR;    // columns per block
     extern __shared__ uint4 smem[];
@@ -250,15 +354,8 @@ __global__ __launch_bounds__(64 * (MAXM == 1 ? kMaxWaves : 4)) void w4_kernel(W4
     float2* sums = reinterpret_cast<float2*>(smem + (size_t)a.XR * K8);     // [XR][G]
     float* red = reinterpret_cast<float*>(sums + (size_t)a.XR * G);  // [nslots][MAXM][NB]
 
-    // The gate/up projection with every token fitting in LDS stages all T
-    // activation rows first: that work does not wait for the routing maps.
-    const bool direct = (PHASE == 1) && a.direct;
     const int e = a.active[slot];  // -1 past the touched experts
     if (e < 0) return;
-    if (direct)
-        stage_rows(xs, sums, a.T, K8, G, [&](int j) {
-            return reinterpret_cast<const uint4*>(a.xin + (size_t)j * K);
-        });
     const smoe_w4_mat wm = (PHASE == 1) ? a.experts[e].w13 : a.experts[e].w2;
     const int r0 = a.off[e];
     const int r1 = a.off[e + 1];
@@ -280,74 +377,86 @@ __global__ __launch_bounds__(64 * (MAXM == 1 ? kMaxWaves : 4)) void w4_kernel(W4
     }
     const uint32_t mlo = vgpr_const_lo();
     const uint32_t mhi = vgpr_const_hi();
+    const W4Src src = make_src(wm, K, N);
 
-    for (int mc = r0; mc < r1; mc += a.MCH) {
-        const int M = min(a.MCH, r1 - mc);
-        // the first group's weights are requested before anything waits
+    if constexpr (MAXM == 1) {
+        // One activation row per expert (a one-token step): the row and the
+        // first group's weights are requested together, then the row is
+        // permuted into LDS while the weights are in flight.
+        const uint16_t* row = (PHASE == 1) ? a.xin + (size_t)a.sorted_token[r0] * K
+                                           : a.xin + (size_t)r0 * K;
+        const uint4* row4 = reinterpret_cast<const uint4*>(row);
+        uint4 xv[kRowChunksPerThread];
+#pragma unroll
+        for (int u = 0; u < kRowChunksPerThread; ++u) {
+            const int idx = tid + u * (int)blockDim.x;
+            if (idx < K8) xv[u] = row4[idx];
+        }
         GroupLoad cur;
-        int g = myslot;
-        if (g < G) load_group(cur, wm, g, N, col, colok);
-        int xrow[MAXM];
+        const int g = myslot;
+        if (g < G) load_group(cur, src, g, col, colok);
 #pragma unroll
-        for (int m = 0; m < MAXM; ++m)
-            xrow[m] = direct ? a.sorted_token[mc + (m < M ? m : 0)] : m;
-        if (!direct) {
-            __syncthreads();  // LDS reuse across row chunks
-            if (PHASE == 1)
-                stage_rows(xs, sums, M, K8, G, [&](int j) {
-                    return reinterpret_cast<const uint4*>(a.xin + (size_t)a.sorted_token[mc + j] * K);
-                });
-            else
-                stage_rows(xs, sums, M, K8, G, [&](int j) {
-                    return reinterpret_cast<const uint4*>(a.xin + (size_t)(mc + j) * K);
-                });
+        for (int u = 0; u < kRowChunksPerThread; ++u) {
+            const int idx = tid + u * (int)blockDim.x;
+            if (idx < K8) xs[idx] = pair_permute(xv[u]);
         }
-
-        float acc[MAXM][4];
-#pragma unroll
-        for (int m = 0; m < MAXM; ++m)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[m][c] = 0.0f;
-
-        if (g < G) group_step<MAXM>(cur, xs, sums, xrow, g, K8, G, M, mlo, mhi, acc);
-        // later groups: load, then consume (other waves hide the latency)
-        for (g += nslots; g < G; g += nslots) {
-            GroupLoad nxt;
-            load_group(nxt, wm, g, N, col, colok);
-            group_step<MAXM>(nxt, xs, sums, xrow, g, K8, G, M, mlo, mhi, acc);
-        }
-
-        // ---- add the slots' partials in a fixed order ----
-        __syncthreads();  // all slots done reading xs
-#pragma unroll
-        for (int m = 0; m < MAXM; ++m)
-            if (m < M)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) red[(myslot * MAXM + m) * NB + 4 * q + c] = acc[m][c];
         __syncthreads();
-        if (PHASE == 1) {
-            for (int idx = tid; idx < M * (NB / 2); idx += blockDim.x) {
-                const int m = idx / (NB / 2);
-                const int j = idx - m * (NB / 2);
-                float gv = 0.0f, uv = 0.0f;
-                for (int s = 0; s < nslots; ++s) {
-                    gv += red[(s * MAXM + m) * NB + j];
-                    uv += red[(s * MAXM + m) * NB + NB / 2 + j];
-                }
-                a.out[(size_t)(mc + m) * a.I + cb * (NB / 2) + j] = f2h(silu_f(gv) * uv);
+        for (int gg = tid; gg < G; gg += blockDim.x) {
+            const uint4* xr = xs + gg * kRowsPerGroup;
+            float se = 0.0f, so = 0.0f;
+#pragma unroll 4
+            for (int i = 0; i < kRowsPerGroup; ++i) {
+                const uint4 p = xr[i];
+                const h2_t x04 = as_h2(p.x), x15 = as_h2(p.y), x26 = as_h2(p.z), x37 = as_h2(p.w);
+                se += ((float)x04.x + (float)x04.y) + ((float)x26.x + (float)x26.y);
+                so += ((float)x15.x + (float)x15.y) + ((float)x37.x + (float)x37.y);
             }
-        } else {
-            for (int idx = tid; idx < M * NB; idx += blockDim.x) {
-                const int m = idx / NB;
-                const int j = idx - m * NB;
-                if (cb * NB + j < N) {
-                    float v = 0.0f;
-                    for (int s = 0; s < nslots; ++s) v += red[(s * MAXM + m) * NB + j];
-                    a.out[(size_t)(mc + m) * N + cb * NB + j] = f2h(v);
-                }
-            }
+            sums[gg] = make_float2(se, so);
         }
-        __syncthreads();  // red is rewritten by the next row chunk
+        __syncthreads();
+        float acc[1][4] = {{0.0f, 0.0f, 0.0f, 0.0f}};
+        const int xrow[1] = {0};
+        run_groups<SMOE_W4_PREFETCH != 0, 1>(cur, g, nslots, G, src, col, colok, xs, sums, xrow,
+                                             K8, 1, mlo, mhi, acc);
+        reduce_store<PHASE, 1, NB>(a, red, acc, myslot, nslots, q, cb, r0, 1);
+        return;
+    } else {
+        // The gate/up projection with every token fitting in LDS stages all
+        // T activation rows once.
+        const bool direct = (PHASE == 1) && a.direct;
+        if (direct)
+            stage_rows(xs, sums, a.T, K8, G, [&](int j) {
+                return reinterpret_cast<const uint4*>(a.xin + (size_t)j * K);
+            });
+        for (int mc = r0; mc < r1; mc += a.MCH) {
+            const int M = min(a.MCH, r1 - mc);
+            int xrow[MAXM];
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m)
+                xrow[m] = direct ? a.sorted_token[mc + (m < M ? m : 0)] : m;
+            if (!direct) {
+                if (PHASE == 1)
+                    stage_rows(xs, sums, M, K8, G, [&](int j) {
+                        return reinterpret_cast<const uint4*>(a.xin +
+                                                              (size_t)a.sorted_token[mc + j] * K);
+                    });
+                else
+                    stage_rows(xs, sums, M, K8, G, [&](int j) {
+                        return reinterpret_cast<const uint4*>(a.xin + (size_t)(mc + j) * K);
+                    });
+            }
+            GroupLoad cur;
+            const int g = myslot;
+            if (g < G) load_group(cur, src, g, col, colok);
+            float acc[MAXM][4];
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[m][c] = 0.0f;
+            run_groups<false, MAXM>(cur, g, nslots, G, src, col, colok, xs, sums, xrow, K8, M, mlo,
+                                    mhi, acc);
+            reduce_store<PHASE, MAXM, NB>(a, red, acc, myslot, nslots, q, cb, mc, M);
+        }
     }
 }
 
@@ -359,11 +468,17 @@ struct PhasePlan {
 };
 
 PhasePlan plan_phase(int phase, int slots, int T, int K, int N, int I, int maxm) {
-    // LPR 16 (64-column blocks, 256-byte row runs) when that already gives
-    // enough workgroups to cover the chip, else LPR 8 (32 columns)
+    // LPR 16 (64-column blocks, 256-byte row runs) when that still gives
+    // SMOE_W4_MIN_WG workgroups and no slot walks more than
+    // SMOE_W4_MAX_GROUPS_PER_SLOT groups in sequence; else LPR 8 (32 columns,
+    // twice the workgroups and slots).  Measured on the decode shapes (H 2048
+    // and 4096, I 1408 and 6400, one to sixteen rows per expert).
     PhasePlan p{};
     const int cols16 = (phase == 1) ? I / 32 : (N + 63) / 64;
-    p.lpr = ((long long)slots * cols16 >= SMOE_W4_MIN_WG) ? 16 : 8;
+    const int G16 = K / 128;
+    const int serial16 = (G16 + 4 * kMaxWaves - 1) / (4 * kMaxWaves);
+    p.lpr = ((long long)slots * cols16 >= SMOE_W4_MIN_WG &&
+             serial16 <= SMOE_W4_MAX_GROUPS_PER_SLOT) ? 16 : 8;
     const int NB = 4 * p.lpr;
     p.nCB = (phase == 1) ? I / (NB / 2) : (N + NB - 1) / NB;
     const int rpl = 64 / p.lpr;
@@ -386,6 +501,8 @@ PhasePlan plan_phase(int phase, int slots, int T, int K, int N, int I, int maxm)
 template <int PHASE, int MAXM>
 hipError_t launch_phase(const W4Args& a, int slots, const PhasePlan& p, hipStream_t s) {
     const dim3 grid(slots * p.nCB), block(64 * p.waves);
+    // the one-row kernel holds at most kRowChunksPerThread activation chunks per thread
+    if (MAXM == 1 && a.K / 8 > kRowChunksPerThread * 64 * p.waves) return hipErrorInvalidValue;
     if (p.lpr == 16)
         hipLaunchKernelGGL((w4_kernel<PHASE, 16, MAXM>), grid, block, p.lds, s, a);
     else

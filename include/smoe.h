@@ -161,6 +161,26 @@ smoe_status moe_gather(const int32_t* topk_ids, int T, int k, int E, int32_t* ex
                        int32_t* active, int32_t* n_active, int32_t* err_word, void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_route_plan -- moe_route_topk, elb_count and moe_gather of one step in a
+ * single launch, for decode-sized T ([S1] Key Contributions 3-4: the drafted
+ * tokens' expert choices come from the target router, are tallied in GPU
+ * counters and gathered by expert inside one fused launch).
+ *
+ * Arguments and outputs are those of the three calls (same meaning, layout
+ * and bit-identical values).  counters may be NULL (no ELB update; layer and
+ * L are then ignored).  Limits: T*k <= 1024 and T*(E+1) <= 4096 (one
+ * workgroup holds the pairs and logits); beyond them SMOE_ERR_SHAPE -- use the
+ * separate calls.  T == 0 writes empty maps.
+ * ---------------------------------------------------------------------- */
+smoe_status moe_route_plan(const uint16_t* x, const uint16_t* w_router,
+                           const uint16_t* w_shared_gate, int T, int H, int E, int k,
+                           int renormalize, int layer, int L, int32_t* counters,
+                           int32_t* topk_ids, float* topk_w, float* shared_gate,
+                           int32_t* expert_offsets, int32_t* sorted_token, int32_t* sorted_pair,
+                           int32_t* pair_pos, int32_t* active, int32_t* n_active,
+                           int32_t* err_word, void* stream);
+
+/* ------------------------------------------------------------------------
  * w4a16_grouped_ffn -- draft routed-expert SwiGLU FFN over GPTQ INT4 weights
  * for every touched expert, one launch per projection across all experts
  * ([S1] Key Contributions 4: fused multi-expert INT4 draft kernel, one GPU

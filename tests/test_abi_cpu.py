@@ -18,7 +18,7 @@ FAKE = V(0x1000)  # never dereferenced: the checks below fail before any use
 def test_exports_every_header_function():
     names = fve.header_functions()
     expected = {"smoe_abi_version", "smoe_last_error", "moe_route_topk", "elb_count",
-                "moe_gather", "w4a16_grouped_ffn", "verify_grouped_gemm", "moe_combine",
+                "moe_gather", "moe_route_plan", "w4a16_grouped_ffn", "verify_grouped_gemm", "moe_combine",
                 "expert_stage_async", "smoe_workspace_bytes"}
     assert set(names) == expected
     L = ctypes.CDLL(fve.LIB_PATH)
@@ -63,6 +63,28 @@ def test_gather_validation():
     assert L.moe_gather(FAKE, 1, 2, 8, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 1
     assert L.moe_gather(FAKE, 1 << 20, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 2
     assert L.moe_gather(FAKE, 1, 3, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 2
+
+
+def test_route_plan_validation():
+    L = fve.lib()
+    outs = [FAKE] * 3   # ids, w, gate
+    maps = [FAKE] * 6   # offsets, sorted_token, sorted_pair, pair_pos, active, n_active
+
+    def call(x=FAKE, wr=FAKE, wsg=None, T=1, H=256, E=8, k=2, layer=0, Lc=1, counters=FAKE,
+             gate=None, mp=None):
+        m = maps if mp is None else mp
+        return L.moe_route_plan(x, wr, wsg, T, H, E, k, 0, layer, Lc, counters, outs[0], outs[1],
+                                gate, *m, None, None)
+    assert call(x=None) == 1
+    assert call(wsg=FAKE) == 1                      # gate output missing
+    assert call(mp=[None] + maps[1:]) == 1          # offsets missing
+    assert call(H=200) == 2
+    assert call(k=9) == 2
+    assert call(T=513, k=2) == 2 and "1024" in _err()        # T*k > 1024
+    assert call(T=100, E=64, k=2) == 2 and "4096" in _err()  # T*(E+1) > 4096
+    assert call(layer=1, Lc=1) == 2                 # layer outside [0, L)
+    assert call(x=V(0x1002)) == 2 and "aligned" in _err()
+    assert call(T=-1) == 2
 
 
 def test_w4a16_validation():

@@ -159,3 +159,27 @@ def test_chunk_verify_residency_invariant(chunk):
     out2 = eng.verify(chunk["xv"])
     torch.cuda.synchronize()
     assert torch.equal(out2, chunk["out"])
+
+
+def test_chunk_draft_graph_matches_eager(chunk):
+    """The draft step captured as one HIP graph reproduces the eager step bit
+    for bit on every replay (replays interleaved with eager work and
+    synchronisations), and counts the same ELB choices."""
+    s = chunk["shape"]
+    eng = chunk["eng"]
+    saved = eng.counters.clone()
+    xs = [torch.from_numpy(synth.tokens(s, 1, step=50 + j)).cuda() for j in range(3)]
+    eng.clear_counters()
+    ref = [eng.draft_step(x).clone() for x in xs]
+    c_ref = eng.counters.clone()
+    eng.capture_draft()
+    eng.clear_counters()
+    for rep in range(3):
+        for j, x in enumerate(xs):
+            out = eng.draft_step_graph(x)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref[j]), (rep, j)
+            eng.snapshot()                       # eager work + a sync between replays
+    assert torch.equal(eng.counters, 3 * c_ref)
+    assert int(host(eng.err)[0]) == 0
+    eng.counters.copy_(saved)

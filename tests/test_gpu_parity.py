@@ -166,6 +166,68 @@ def test_gather_bad_ids_and_empty():
     assert host(m["active"]).tolist() == [-1] * 4
 
 
+# ------------------------------------------------ S1 + S2 + S3 fused ----
+
+PLAN_CASES = [(synth.TINY, 1), (synth.TINY, 37), (synth.TINY, 455), (synth.DS, 1),
+              (synth.DS, 16), (synth.DS, 62), (synth.QWEN, 1), (synth.QWEN, 17), (synth.PHI, 1),
+              (synth.PHI, 17)]
+
+
+@pytest.mark.parametrize("shape,T", PLAN_CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_route_plan_matches_separate_calls(shape, T):
+    """The fused plan equals routing + ELB + gather bit for bit, and the oracle."""
+    say(f"route plan {shape.name} T={T}")
+    E, k = shape.E, shape.k
+    wr = synth.router(shape)
+    x = synth.tokens(shape, T, step=5)
+    sh = synth.shared_expert(shape)
+    gvec = None if sh is None else sh.get("gate")
+    dgvec = None if gvec is None else dev(gvec)
+    c0 = np.random.default_rng(T).integers(0, 50, size=(3, E)).astype(np.int32)
+    counters = dev(c0)
+    err = _err()
+    ids, w, gate, m = fve.moe_route_plan(dev(x), dev(wr), k, shape.renormalize, dgvec,
+                                         counters=counters, layer=1, err_word=err)
+    ids2, w2, gate2 = fve.moe_route_topk(dev(x), dev(wr), k, shape.renormalize, dgvec)
+    counters2 = dev(c0)
+    fve.elb_count(ids2, E, 1, counters2)
+    m2 = fve.moe_gather(ids2, E)
+    n = T * k
+    assert torch.equal(ids, ids2)
+    assert torch.equal(w, w2)
+    if gvec is not None:
+        assert torch.equal(gate, gate2)
+    assert torch.equal(counters, counters2)
+    for key in ("offsets", "active", "n_active"):
+        assert torch.equal(m[key], m2[key]), key
+    for key in ("sorted_token", "sorted_pair", "pair_pos"):
+        assert torch.equal(m[key][:n], m2[key][:n]), key
+    ref = oracle.route_topk(x, wr, k, shape.renormalize, gvec)
+    assert np.array_equal(host(ids), ref["ids"])
+    assert np.array_equal(host(counters), oracle.elb_update(c0, ref["ids"], 1))
+    rm = oracle.gather_maps(ref["ids"], E)
+    assert np.array_equal(host(m["offsets"]), rm["offsets"])
+    assert np.array_equal(host(m["sorted_pair"])[:n], rm["sorted_pair"])
+    assert int(host(err)[0]) == 0
+
+
+def test_route_plan_empty_and_no_counters():
+    s = synth.TINY
+    wr = dev(synth.router(s))
+    _, _, _, m = fve.moe_route_plan(torch.zeros((0, s.H), dtype=torch.float16, device="cuda"),
+                                    wr, s.k)
+    assert host(m["offsets"]).tolist() == [0] * (s.E + 1)
+    assert int(host(m["n_active"])[0]) == 0
+    assert host(m["active"]).tolist() == [-1] * s.E
+    x = synth.tokens(s, 3, step=2)
+    ids, _, _, m = fve.moe_route_plan(dev(x), wr, s.k)
+    ref = oracle.route_topk(x, synth.router(s), s.k)
+    assert np.array_equal(host(ids), ref["ids"])
+    with pytest.raises(fve.SmoeError):   # beyond the one-workgroup limits
+        fve.moe_route_plan(dev(synth.tokens(synth.DS, 64)), dev(synth.router(synth.DS)),
+                           synth.DS.k)
+
+
 # ------------------------------------------------------------- S4 / S6 ----
 
 _layers = {}
