@@ -30,18 +30,10 @@ __global__ __launch_bounds__(kPlanThreads) void route_plan_kernel(
     __shared__ int32_t ids_s[kPlanThreads];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int nch = H >> 3;
     const int nvec = E + (wsg ? 1 : 0);
 
     // 1. logits: item i = t * nvec + e, wave w takes items w, w + 16, ...
-    for (int i = wave; i < T * nvec; i += kPlanWaves) {
-        const int t = i / nvec;
-        const int e = i - t * nvec;
-        const uint16_t* row = (e < E) ? wr + (size_t)e * H : wsg;
-        const float s = smoe_route::pinned_dot(reinterpret_cast<const uint4*>(x + (size_t)t * H),
-                                               reinterpret_cast<const uint4*>(row), nch, lane);
-        if (lane == 0) logit[i] = s;
-    }
+    smoe_route::wave_logits(x, wr, wsg, H, E, nvec, wave, T * nvec, kPlanWaves, logit, lane);
     __syncthreads();
 
     // 2. top-k and weights, wave w takes tokens w, w + 16, ...

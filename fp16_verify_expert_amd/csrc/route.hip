@@ -21,14 +21,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
-    const int nch = H >> 3;
-    const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)t * H);
     const int nvec = E + (wsg ? 1 : 0);
-    for (int e = wave; e < nvec; e += nw) {
-        const uint16_t* row = (e < E) ? wr + (size_t)e * H : wsg;
-        const float s = smoe_route::pinned_dot(xr, reinterpret_cast<const uint4*>(row), nch, lane);
-        if (lane == 0) logit[e] = s;
-    }
+    // wave w takes vectors w, w + nw, ... of this token
+    smoe_route::wave_logits(x + (size_t)t * H, wr, wsg, H, E, nvec, wave, nvec, nw, logit, lane);
     __syncthreads();
     if (wave != 0) return;
     smoe_route::topk_softmax_wave(logit, E, k, renorm, wsg != nullptr, lane, ids + (size_t)t * k,

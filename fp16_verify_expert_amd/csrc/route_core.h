@@ -61,6 +61,91 @@ SMOE_DEV float pinned_dot(const uint4* __restrict__ xr, const uint4* __restrict_
     return s;
 }
 
+// Logits of the items i = first, first + stride, ... < n_items handled by one
+// wave; item i is (token i / nvec, vector i % nvec), vector e < E being router
+// row e and vector E the shared-gate row.  Up to D items of one token are
+// evaluated together: the token's CPL chunks per lane are requested once and
+// the D weight rows' chunks are all in flight before any sum starts.  Every
+// sum is the pinned order of pinned_dot (a lane adds its chunks c = lane,
+// lane + 64, ... in increasing order, then the same butterfly), so the values
+// are identical.
+template <int D, int CPL>
+SMOE_DEV void wave_logits_batched(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                                  const uint16_t* __restrict__ wsg, int H, int E, int nvec,
+                                  int first, int n_items, int stride, float* out, int lane) {
+    const int nch = H >> 3;
+    for (int i = first; i < n_items;) {
+        const int t = i / nvec;
+        int nd = 0;
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int ii = i + d * stride;
+            if (ii < n_items && ii / nvec == t) nd = d + 1;  // a prefix: items increase
+        }
+        const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)t * H);
+        uint4 xv[CPL];
+        uint4 wv[D][CPL];
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) {
+            const int c = lane + 64 * u;
+            if (c < nch) xv[u] = xr[c];
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (d < nd) {
+                const int e = (i + d * stride) - t * nvec;
+                const uint4* row = reinterpret_cast<const uint4*>(e < E ? wr + (size_t)e * H : wsg);
+#pragma unroll
+                for (int u = 0; u < CPL; ++u) {
+                    const int c = lane + 64 * u;
+                    if (c < nch) wv[d][u] = row[c];
+                }
+            }
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (d < nd) {
+                float s = 0.0f;
+#pragma unroll
+                for (int u = 0; u < CPL; ++u) {
+                    const int c = lane + 64 * u;
+                    if (c < nch) s = acc_chunk(s, xv[u], wv[d][u]);
+                }
+#pragma unroll
+                for (int dd = 32; dd >= 1; dd >>= 1) s = s + __shfl_xor(s, dd);
+                if (lane == 0) out[i + d * stride] = s;
+            }
+        }
+        i += nd * stride;
+    }
+}
+
+// wave_logits_batched for any H: batches sized so that at most 16 weight
+// chunks per lane are in flight (H <= 4096); longer rows one item at a time.
+SMOE_DEV void wave_logits(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                          const uint16_t* __restrict__ wsg, int H, int E, int nvec, int first,
+                          int n_items, int stride, float* out, int lane) {
+    const int cpl = ((H >> 3) + 63) / 64;
+    if (cpl <= 1) {
+        wave_logits_batched<4, 1>(x, wr, wsg, H, E, nvec, first, n_items, stride, out, lane);
+    } else if (cpl <= 2) {
+        wave_logits_batched<4, 2>(x, wr, wsg, H, E, nvec, first, n_items, stride, out, lane);
+    } else if (cpl <= 4) {
+        wave_logits_batched<4, 4>(x, wr, wsg, H, E, nvec, first, n_items, stride, out, lane);
+    } else if (cpl <= 8) {
+        wave_logits_batched<2, 8>(x, wr, wsg, H, E, nvec, first, n_items, stride, out, lane);
+    } else {
+        for (int i = first; i < n_items; i += stride) {
+            const int t = i / nvec;
+            const int e = i - t * nvec;
+            const uint16_t* row = (e < E) ? wr + (size_t)e * H : wsg;
+            const float s = pinned_dot(reinterpret_cast<const uint4*>(x + (size_t)t * H),
+                                       reinterpret_cast<const uint4*>(row), H >> 3, lane);
+            if (lane == 0) out[i] = s;
+        }
+    }
+}
+
 // Ranking of (logit, expert id) pairs: larger logit first, NaN below every
 // number, equal logits (or two NaNs) lower id first.
 SMOE_DEV bool ranks_before(float va, int ia, float vb, int ib) {

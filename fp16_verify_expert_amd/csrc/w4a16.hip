@@ -331,7 +331,7 @@ __device__ __forceinline__ void run_groups(GroupLoad& cur, int g, int nslots, in
     }
 }
 
-constexpr int kRowChunksPerThread = 8;  // K/8 <= 2048 chunks over >= 256 threads
+constexpr int kRowChunksPerThread = 8;  // activation chunks per thread requested early
 
 template <int PHASE, int LPR, int MAXM>
 __global__ __launch_bounds__(64 * kMaxWaves) void w4_kernel(W4Args a) {
@@ -354,18 +354,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void w4_kernel(W4Args a) {
     float2* sums = reinterpret_cast<float2*>(smem + (size_t)a.XR * K8);     // [XR][G]
     float* red = reinterpret_cast<float*>(sums + (size_t)a.XR * G);  // [nslots][MAXM][NB]
 
-    const int e = a.active[slot];  // -1 past the touched experts
-    if (e < 0) return;
-    const smoe_w4_mat wm = (PHASE == 1) ? a.experts[e].w13 : a.experts[e].w2;
-    const int r0 = a.off[e];
-    const int r1 = a.off[e + 1];
-    if (!wm.qweight || !wm.scales || !wm.qzeros) {
-        if (tid == 0 && cb == 0) flag_error(a.err, SMOE_DERR_NULL_EXPERT);
-        return;
-    }
     const int nslots = nwaves * RPL;
     const int myslot = wave * RPL + rho;
-
     int col;
     bool colok;
     if (PHASE == 1) {
@@ -377,14 +367,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void w4_kernel(W4Args a) {
     }
     const uint32_t mlo = vgpr_const_lo();
     const uint32_t mhi = vgpr_const_hi();
-    const W4Src src = make_src(wm, K, N);
 
     if constexpr (MAXM == 1) {
-        // One activation row per expert (a one-token step): the row and the
-        // first group's weights are requested together, then the row is
-        // permuted into LDS while the weights are in flight.
-        const uint16_t* row = (PHASE == 1) ? a.xin + (size_t)a.sorted_token[r0] * K
-                                           : a.xin + (size_t)r0 * K;
+        // One token (T = 1): every pair's token is 0, and the touched experts
+        // in increasing id (the active list) own sorted rows 0, 1, ... in
+        // that order, so this slot's activation row is known before the maps
+        // are read: x row 0 (gate/up) or h row `slot` (down).  It is
+        // requested first, then the expert's first weights; the row is
+        // permuted into LDS while both are in flight.
+        const uint16_t* row = (PHASE == 1) ? a.xin : a.xin + (size_t)slot * K;
         const uint4* row4 = reinterpret_cast<const uint4*>(row);
         uint4 xv[kRowChunksPerThread];
 #pragma unroll
@@ -392,6 +383,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) void w4_kernel(W4Args a) {
             const int idx = tid + u * (int)blockDim.x;
             if (idx < K8) xv[u] = row4[idx];
         }
+        const int e = a.active[slot];  // -1 past the touched experts
+        if (e < 0) return;
+        const smoe_w4_mat wm = (PHASE == 1) ? a.experts[e].w13 : a.experts[e].w2;
+        if (!wm.qweight || !wm.scales || !wm.qzeros) {
+            if (tid == 0 && cb == 0) flag_error(a.err, SMOE_DERR_NULL_EXPERT);
+            return;
+        }
+        const W4Src src = make_src(wm, K, N);
         GroupLoad cur;
         const int g = myslot;
         if (g < G) load_group(cur, src, g, col, colok);
@@ -400,6 +399,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void w4_kernel(W4Args a) {
             const int idx = tid + u * (int)blockDim.x;
             if (idx < K8) xs[idx] = pair_permute(xv[u]);
         }
+        // rows longer than the early requests cover (small workgroups)
+        for (int idx = tid + kRowChunksPerThread * (int)blockDim.x; idx < K8; idx += blockDim.x)
+            xs[idx] = pair_permute(row4[idx]);
         __syncthreads();
         for (int gg = tid; gg < G; gg += blockDim.x) {
             const uint4* xr = xs + gg * kRowsPerGroup;
@@ -418,9 +420,19 @@ __global__ __launch_bounds__(64 * kMaxWaves) void w4_kernel(W4Args a) {
         const int xrow[1] = {0};
         run_groups<SMOE_W4_PREFETCH != 0, 1>(cur, g, nslots, G, src, col, colok, xs, sums, xrow,
                                              K8, 1, mlo, mhi, acc);
-        reduce_store<PHASE, 1, NB>(a, red, acc, myslot, nslots, q, cb, r0, 1);
+        reduce_store<PHASE, 1, NB>(a, red, acc, myslot, nslots, q, cb, slot, 1);
         return;
     } else {
+        const int e = a.active[slot];  // -1 past the touched experts
+        if (e < 0) return;
+        const smoe_w4_mat wm = (PHASE == 1) ? a.experts[e].w13 : a.experts[e].w2;
+        const int r0 = a.off[e];
+        const int r1 = a.off[e + 1];
+        if (!wm.qweight || !wm.scales || !wm.qzeros) {
+            if (tid == 0 && cb == 0) flag_error(a.err, SMOE_DERR_NULL_EXPERT);
+            return;
+        }
+        const W4Src src = make_src(wm, K, N);
         // The gate/up projection with every token fitting in LDS stages all
         // T activation rows once.
         const bool direct = (PHASE == 1) && a.direct;
@@ -484,7 +496,9 @@ PhasePlan plan_phase(int phase, int slots, int T, int K, int N, int I, int maxm)
     const int rpl = 64 / p.lpr;
     const int G = K / 128;
     p.waves = (G + rpl - 1) / rpl;
-    const int wmax = (maxm == 1) ? kMaxWaves : 4;  // register budget of the multi-row kernels
+    // the launch bound caps every kernel at kMaxWaves; the multi-row kernels'
+    // register budget at 4
+    const int wmax = (maxm == 1 || kMaxWaves < 4) ? kMaxWaves : 4;
     if (p.waves > wmax) p.waves = wmax;
     if (p.waves < 1) p.waves = 1;
     const size_t row_bytes = (size_t)K * 2 + (size_t)G * 8;  // pairs + group sums
@@ -501,8 +515,6 @@ PhasePlan plan_phase(int phase, int slots, int T, int K, int N, int I, int maxm)
 template <int PHASE, int MAXM>
 hipError_t launch_phase(const W4Args& a, int slots, const PhasePlan& p, hipStream_t s) {
     const dim3 grid(slots * p.nCB), block(64 * p.waves);
-    // the one-row kernel holds at most kRowChunksPerThread activation chunks per thread
-    if (MAXM == 1 && a.K / 8 > kRowChunksPerThread * 64 * p.waves) return hipErrorInvalidValue;
     if (p.lpr == 16)
         hipLaunchKernelGGL((w4_kernel<PHASE, 16, MAXM>), grid, block, p.lds, s, a);
     else

@@ -202,6 +202,9 @@ smoe_status moe_route_plan(const uint16_t* x, const uint16_t* w_router,
  *                  256-byte aligned: holds h (fp16 [T*k, I]) between the two
  *                  projections; no initialisation needed.
  *   H, I           at most 16384 each (activations are staged in LDS).
+ * The maps must be moe_gather's for these ids: with T == 1 the kernels use
+ * its ordering (the i-th touched expert by increasing id owns sorted row i)
+ * to request activation rows before reading the maps.
  * ---------------------------------------------------------------------- */
 smoe_status w4a16_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
                               const int32_t* expert_offsets, const int32_t* active,
