@@ -69,7 +69,8 @@ class ChunkEngine:
         self.t4 = [w4_expert_table(l.int4, device=dev) for l in self.layers]
         self.tsh = [None if l.shared is None else f16_expert_table([l.shared], device=dev)
                     for l in self.layers]
-        self.side = torch.cuda.Stream(device=dev)    # default priority
+        self.side = torch.cuda.Stream(device=dev)    # staging copies; default priority
+        self.side_sh = torch.cuda.Stream(device=dev)  # shared expert; default priority
         self.ev_staged = [torch.cuda.Event() for _ in range(2)]
         self.ev_free = [torch.cuda.Event() for _ in range(2)]
         # per-layer pinned upload buffers (an async upload must not see its
@@ -82,6 +83,8 @@ class ChunkEngine:
         self.ws_v = new_workspace(1, verify_T, k, H, I, E, device=dev)
         self.ws_sh = {T: new_workspace(1, T, 1, H, shared_I, 1, device=dev)
                       for T in (1, verify_T)} if shared_I else {}
+        self.sh_out = {T: torch.empty((T, H), dtype=torch.float16, device=dev)
+                       for T in (1, verify_T)} if shared_I else {}
         self.iota = torch.arange(max(verify_T, 1), dtype=torch.int32, device=dev)
         self.offs = {T: torch.tensor([0, T], dtype=torch.int32, device=dev) for T in (1, verify_T)}
         self.stats = dict(staged_experts=0, staged_bytes=0, hit_experts=0, miss_experts=0)
@@ -92,7 +95,27 @@ class ChunkEngine:
             return None
         T = x.shape[0]
         return verify_grouped_gemm(x, self.iota[:T], self.offs[T], self.tsh[l], T, T, self.H,
-                                   self.Is, 1, self.ws_sh[T], err_word=self.err)
+                                   self.Is, 1, self.ws_sh[T], y_sorted=self.sh_out[T],
+                                   err_word=self.err)
+
+    def _shared_fork(self, l: int, x: torch.Tensor):
+        """Start the shared expert of layer l on its own stream: it reads only
+        x, so it runs beside the routed experts (a dense FFN whose 16-column
+        blocks alone do not fill the chip).  _join makes the caller's stream
+        wait for it."""
+        if self.tsh[l] is None:
+            return None
+        main = torch.cuda.current_stream()
+        self.side_sh.wait_stream(main)
+        with torch.cuda.stream(self.side_sh):
+            # its output buffer is only rewritten by the next layer's fork,
+            # which waits for everything the caller's stream enqueued before
+            # it (this layer's combine included)
+            sh = self._shared(l, x)
+        return sh
+
+    def _join(self) -> None:
+        torch.cuda.current_stream().wait_stream(self.side_sh)
 
     def draft_step(self, x: torch.Tensor, record: Optional[list] = None) -> torch.Tensor:
         """One INT4 draft decode step (T = 1) through all layers, counting each
@@ -103,9 +126,10 @@ class ChunkEngine:
             ids, w, gate, maps = moe_route_plan(xn, ly.router, self.k, False, ly.shared_gate,
                                                 counters=self.counters, layer=l,
                                                 err_word=self.err)
+            sh = self._shared_fork(l, xn)
             y = w4a16_grouped_ffn(xn, maps, self.t4[l], 1, self.k, self.H, self.I, self.E,
                                   self.ws_d, err_word=self.err)
-            sh = self._shared(l, xn)
+            self._join()
             out, xn_next = moe_combine(y, maps["pair_pos"], w, sh, gate, x, norm_out=True)
             if record is not None:
                 record.append(dict(layer=l, x=x, xn=xn, ids=ids, out=out, xn_next=xn_next))
@@ -172,27 +196,40 @@ class ChunkEngine:
         for l, ly in enumerate(self.layers):
             ids, w, gate = moe_route_topk(xn, ly.router, self.k, False, ly.shared_gate)
             maps = moe_gather(ids, self.E, self.err)
+            sh = self._shared_fork(l, xn)
             rows = T * self.k
             y = torch.empty((rows, self.H), dtype=torch.float16, device=self.dev)
             if all_resident is not None:
-                tab = self.h_table[l]
-                base = all_resident[l]
-                for e in range(self.E):
-                    tab[e, 0] = base[e].data_ptr()
-                    tab[e, 1] = base[e].data_ptr() + self.w13_bytes
-                self.d_table[l].copy_(tab, non_blocking=True)
-                verify_grouped_gemm(xn, maps["sorted_token"], maps["offsets"], self.d_table[l],
+                verify_grouped_gemm(xn, maps["sorted_token"], maps["offsets"],
+                                    self._resident_table(all_resident, l),
                                     T, rows, self.H, self.I, self.E, self.ws_v,
                                     active=maps["active"], n_active=maps["n_active"],
                                     y_sorted=y, err_word=self.err)
             else:
                 self._verify_staged(l, xn, maps, y, main)
-            sh = self._shared(l, xn)
+            self._join()
             out, xn_next = moe_combine(y, maps["pair_pos"], w, sh, gate, x, norm_out=True)
             if record is not None:
                 record.append(dict(layer=l, x=x, xn=xn, ids=ids, out=out, xn_next=xn_next))
             x, xn = out, xn_next
         return x
+
+    def _resident_table(self, full: torch.Tensor, l: int) -> torch.Tensor:
+        """Device descriptor table of layer l pointing into `full` ([L, E,
+        3HI] in HBM), built once per buffer."""
+        key = (full.data_ptr(), full.shape[0])
+        if getattr(self, "_full_key", None) != key:
+            base = full.data_ptr()
+            step = full.stride(1) * full.element_size()
+            lay = full.stride(0) * full.element_size()
+            tab = torch.empty((self.L, self.E, 2), dtype=torch.int64)
+            for li in range(self.L):
+                for e in range(self.E):
+                    p = base + li * lay + e * step
+                    tab[li, e, 0], tab[li, e, 1] = p, p + self.w13_bytes
+            self._full_tab = tab.to(self.dev)
+            self._full_key = key
+        return self._full_tab[l]
 
     def _verify_staged(self, l, x, maps, y, main) -> None:
         T = x.shape[0]
