@@ -26,10 +26,12 @@ SMOE_DEV float acc_chunk(float s, uint4 xv, uint4 wv) {
         const float w0 = h2f((uint16_t)(ww[i] & 0xFFFFu));
         const float x1 = h2f((uint16_t)(xw[i] >> 16));
         const float w1 = h2f((uint16_t)(ww[i] >> 16));
-        const float p0 = x0 * w0;  // exact: 11-bit x 11-bit significands
-        s = s + p0;
-        const float p1 = x1 * w1;
-        s = s + p1;
+        // x*w is exact in fp32 (11-bit x 11-bit significands, no underflow),
+        // so a fused multiply-add rounds exactly like the separate add of the
+        // product; it lets the hardware take the fp16 operands directly
+        // (v_fma_mix), one instruction per element
+        s = __builtin_fmaf(x0, w0, s);
+        s = __builtin_fmaf(x1, w1, s);
     }
     return s;
 }
@@ -147,63 +149,81 @@ SMOE_DEV void wave_logits(const uint16_t* __restrict__ x, const uint16_t* __rest
 }
 
 // Ranking of (logit, expert id) pairs: larger logit first, NaN below every
-// number, equal logits (or two NaNs) lower id first.
-SMOE_DEV bool ranks_before(float va, int ia, float vb, int ib) {
-    const bool na = va != va, nb = vb != vb;
-    if (na != nb) return nb;
-    if (!na && va != vb) return va > vb;
-    return ia < ib;
+// number, equal logits (-0 equal to +0, or two NaNs) lower id first.  As a
+// 64-bit key: the logit's bits mapped to an unsigned order (NaN lowest), then
+// the complemented id; a pair ranks before another iff its key is larger.
+SMOE_DEV uint64_t rank_key(float v, int e) {
+    uint32_t u = __float_as_uint(v);
+    uint32_t ord;
+    if (v != v) {
+        ord = 0u;
+    } else {
+        if ((u << 1) == 0u) u = 0u;  // -0 as +0
+        ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    }
+    return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+// rank[i] += number of the E keys above key[i], for the NB key blocks held
+// (lane l holds key[i] of expert l + 64 i); keys are broadcast by readlane.
+template <int NB>
+SMOE_DEV void count_ranks(const uint64_t (&key)[4], int E, int (&rank)[4]) {
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib) {
+        const int nj = min(64, E - 64 * ib);
+        const uint32_t lo = (uint32_t)key[ib];
+        const uint32_t hi = (uint32_t)(key[ib] >> 32);
+#pragma unroll 4
+        for (int j = 0; j < nj; ++j) {
+            const uint64_t kj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, j) << 32) |
+                                (uint32_t)__builtin_amdgcn_readlane((int)lo, j);
+#pragma unroll
+            for (int i = 0; i < NB; ++i) rank[i] += (kj > key[i]) ? 1 : 0;
+        }
+    }
 }
 
 // One wave selects the top k of a token's E logits (lg, in LDS; lg[E] is the
 // shared-gate logit when has_gate) and writes ids, weights (softmax over all
 // E at the chosen ids, optionally renormalised over the k) and the gate.
-// ids_copy (nullable) receives the ids as well.
+// ids_copy (nullable) receives the ids as well.  Lane l holds experts
+// l + 64 i; each expert's rank is the number of keys above its own (every
+// key taken from its lane by readlane), and the experts of rank < k are the
+// selection, in rank order.
 SMOE_DEV void topk_softmax_wave(const float* lg, int E, int k, int renorm, bool has_gate,
                                 int lane, int32_t* ids, float* wout, float* gate,
                                 int32_t* ids_copy) {
     float v[4];
-    bool live[4];
-    float mysel[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // lane j%64 keeps winner j
+    uint64_t key[4];
+    int rank[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = lane + 64 * i;
-        live[i] = e < E;
-        v[i] = live[i] ? lg[e] : 0.0f;
+        const bool live = e < E;
+        v[i] = live ? lg[e] : 0.0f;
+        key[i] = live ? rank_key(v[i], e) : 0ull;
+        rank[i] = 0;
     }
-    float m = 0.0f;  // largest logit (the first winner)
-    for (int j = 0; j < k; ++j) {
-        float bv = 0.0f;
-        int bi = 0x7fffffff;  // no candidate
+    const int nblk = (E + 63) >> 6;  // key blocks actually held (uniform)
+    if (nblk == 1)
+        count_ranks<1>(key, E, rank);
+    else if (nblk == 2)
+        count_ranks<2>(key, E, rank);
+    else if (nblk == 3)
+        count_ranks<3>(key, E, rank);
+    else
+        count_ranks<4>(key, E, rank);
+    // the largest logit: the value of the rank-0 expert, from its lane
+    float v0 = 0.0f;
+    bool has0 = false;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = lane + 64 * i;
-            if (live[i] && (bi == 0x7fffffff || ranks_before(v[i], e, bv, bi))) {
-                bv = v[i];
-                bi = e;
-            }
+    for (int i = 0; i < 4; ++i)
+        if (lane + 64 * i < E && rank[i] == 0) {
+            v0 = v[i];
+            has0 = true;
         }
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) {
-            const float ov = __shfl_xor(bv, d);
-            const int oi = __shfl_xor(bi, d);
-            if (oi != 0x7fffffff && (bi == 0x7fffffff || ranks_before(ov, oi, bv, bi))) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        // every lane now holds the same winner
-        if (j == 0) m = bv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if ((bi & 63) == lane && (bi >> 6) == i) live[i] = false;
-            if ((j & 63) == lane && (j >> 6) == i) mysel[i] = bv;
-        }
-        if (lane == 0) {
-            ids[j] = bi;
-            if (ids_copy) ids_copy[j] = bi;
-        }
-    }
+    const uint64_t b0 = __ballot(has0);
+    const float m = __shfl(v0, __ffsll((unsigned long long)b0) - 1);
 
     // softmax over all E at the chosen ids
     float ssum = 0.0f;
@@ -216,7 +236,8 @@ SMOE_DEV void topk_softmax_wave(const float* lg, int E, int k, int renorm, bool 
     float part = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        p[i] = (lane + 64 * i < k) ? expf(mysel[i] - m) / ssum : 0.0f;
+        const bool sel = lane + 64 * i < E && rank[i] < k;
+        p[i] = sel ? expf(v[i] - m) / ssum : 0.0f;
         part += p[i];
     }
     if (renorm) {
@@ -225,8 +246,12 @@ SMOE_DEV void topk_softmax_wave(const float* lg, int E, int k, int renorm, bool 
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int j = lane + 64 * i;
-        if (j < k) wout[j] = renorm ? p[i] / part : p[i];
+        const int e = lane + 64 * i;
+        if (e < E && rank[i] < k) {
+            ids[rank[i]] = e;
+            if (ids_copy) ids_copy[rank[i]] = e;
+            wout[rank[i]] = renorm ? p[i] / part : p[i];
+        }
     }
     if (has_gate && lane == 0) *gate = 1.0f / (1.0f + expf(-lg[E]));
 }
