@@ -4,7 +4,8 @@
 Default workload: the Phi-3.5-MoE-shaped layer (hidden 4096, 16 experts,
 top-2, SwiGLU intermediate 6400, no shared expert).  One step is one INT4
 draft decode step (T = 1: fused route + ELB count + gather, W4A16 FFN,
-combine; replayed as a captured HIP graph unless --no-graph) followed by one
+combine; launched call by call, or replayed as a captured HIP graph with
+--graph on) followed by one
 FP16 verification of K+1 = 17 tokens (route, gather,
 regrouped verify FFN, combine), every step through the C ABI of libsmoe.so
 on seeded synthetic inputs already resident in HBM.  Steps cycle over a pool
@@ -52,14 +53,18 @@ def parse():
                          "layer; qwen_chunk: 24 Qwen-shaped layers, 16 draft steps, ELB snapshot, "
                          "top-16 residency, 17-token verify with staged misses")
     ap.add_argument("--layers", type=int, default=24, help="qwen_chunk: number of layers")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="launch the draft step's calls one by one instead of replaying it as "
-                         "a captured HIP graph")
+    ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
+                    help="replay the draft step as a captured HIP graph (on) or launch its calls "
+                         "one by one (off); auto = off for phi_layer (4 launches per step: "
+                         "measured faster eager) and on for qwen_chunk (8 launches per layer)")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.graph == "auto":
+        args.graph = "on" if args.workload == "qwen_chunk" else "off"
+    args.no_graph = args.graph == "off"
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
               "the path is single-GPU and no multi-GPU figure is produced.", file=sys.stderr)

@@ -309,3 +309,22 @@ def test_rms_norm_closed_forms():
     a = rng.standard_normal((5, 256))
     assert np.allclose(oracle.rms_norm(a * 7.0, eps=0.0), oracle.rms_norm(a, eps=0.0))
     assert np.allclose(np.mean(oracle.rms_norm(a, eps=0.0) ** 2, axis=1), 1.0)
+    # eps sits inside the root, added to the mean square: sqrt(1 + 3) = 2
+    assert np.allclose(oracle.rms_norm(np.ones((1, 4)), eps=3.0), 0.5, rtol=0, atol=1e-15)
+
+
+def test_moe_layer_residual_is_added_once():
+    """Zero expert weights: the pre-norm block returns its residual input
+    exactly (rounded to fp16), whichever way the residual is passed."""
+    s = synth.TINY
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((3, s.H)).astype(np.float16)
+    res = rng.standard_normal((3, s.H)).astype(np.float16)
+    zero = [(np.zeros((2 * s.I, s.H), np.float16), np.zeros((s.H, s.I), np.float16))] * s.E
+    wr = synth.router(s)
+    out = oracle.moe_layer(x, wr, s.k, zero, "f16", residual=res)["out"]
+    assert np.array_equal(out, res)
+    out = oracle.moe_layer(x, wr, s.k, zero, "f16", residual=True)["out"]
+    assert np.array_equal(out, x)
+    out = oracle.moe_layer(x, wr, s.k, zero, "f16")["out"]
+    assert np.array_equal(out, np.zeros_like(x))
