@@ -53,6 +53,8 @@ def parse():
                          "layer; qwen_chunk: 24 Qwen-shaped layers, 16 draft steps, ELB snapshot, "
                          "top-16 residency, 17-token verify with staged misses")
     ap.add_argument("--layers", type=int, default=24, help="qwen_chunk: number of layers")
+    ap.add_argument("--no-dense-point", dest="dense_point", action="store_false",
+                    help="phi_layer: skip the supplementary T=2048 verify point")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
                     help="replay the draft step as a captured HIP graph (on) or launch its calls "
                          "one by one (off); auto = off for phi_layer (4 launches per step: "
@@ -277,6 +279,46 @@ def main():
         "host_wall_s": round(wall, 4),
         "gen_s": round(gen_s, 2),
     }
+
+    # ---- supplementary dense point (outside the benchmark configurations):
+    #      the same layer's FP16 experts over T = 2048 tokens, k = 2, i.e. about
+    #      256 rows per expert, where the verify FFN is a real contraction ----
+    if args.dense_point:
+        T_X = 2048
+        xd = up(synth.tokens(s, T_X, step=500))
+        idsd, _, _ = fve.moe_route_topk(xd, router, k)
+        md = fve.moe_gather(idsd, E, err)
+        rows_d = T_X * k
+        ws_x = fve.new_workspace(1, T_X, k, H, I, E)
+        yd = torch.empty((rows_d, H), dtype=torch.float16, device=dev)
+        call = lambda: fve.verify_grouped_gemm(xd, md["sorted_token"], md["offsets"], t16, T_X,
+                                               rows_d, H, I, E, ws_x, active=md["active"],
+                                               n_active=md["n_active"], y_sorted=yd,
+                                               err_word=err)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        nd = 20
+        evd = [(mk(), mk()) for _ in range(nd)]
+        for i in range(nd):
+            evd[i][0].record()
+            call()
+            evd[i][1].record()
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0, "device error word set"
+        us_d = 1e3 * sum(a.elapsed_time(b) for a, b in evd) / nd
+        nact = int(md["n_active"].item())
+        fl = 2.0 * rows_d * 3 * H * I
+        res["dense_point"] = {
+            "note": "supplementary, outside the benchmark configurations: phi35 experts, T=2048 "
+                    "tokens, k=2 (verify_grouped_gemm in its tiled-GEMM regime)",
+            "rows": rows_d, "touched_experts": nact, "rows_per_expert": round(rows_d / nact, 1),
+            "us": round(us_d, 2), "tflops": round(fl / (us_d * 1e-6) / 1e12, 2),
+            "frac_mfma": round(fl / (us_d * 1e-6) / 1e12 / MFMA_F16_PEAK_TFS, 4),
+            "weight_gbps": round(nact * b16 / (us_d * 1e-6) / 1e9, 1),
+            "attainable_tflops": round(min(MFMA_F16_PEAK_TFS,
+                                           fl / (nact * b16) * HBM_PEAK_GBS / 1e3), 1)}
+        del xd, ws_x, yd
 
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

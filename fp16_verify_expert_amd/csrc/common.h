@@ -65,6 +65,13 @@ hipError_t launch_verify_ffn(const uint16_t* x, const int32_t* sorted_token, con
                              int H, int I, int E, uint16_t* y, void* ws, int32_t* err,
                              hipStream_t s);
 size_t verify_workspace_bytes(int T, int rows, int H, int I, int E);
+// dense regime of the verify FFN (many rows per expert)
+size_t dense_plan_bytes(int E);
+hipError_t launch_dense_ffn(const uint16_t* x, const int32_t* sorted_token, const int32_t* off,
+                            const int32_t* active, const int32_t* n_active,
+                            const smoe_f16_expert* experts, const uint8_t* mask, int rows, int H,
+                            int I, int E, uint16_t* y, uint16_t* h, int32_t* plan, int32_t* err,
+                            hipStream_t s);
 hipError_t launch_combine(const uint16_t* y, const int32_t* pp, const float* w,
                           const uint16_t* shared, const float* sscale, const uint16_t* resid,
                           int T, int k, int H, uint16_t* out, uint16_t* norm_out, float eps,

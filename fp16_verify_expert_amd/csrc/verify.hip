@@ -388,6 +388,9 @@ __global__ __launch_bounds__(64 * kVWaves) void f16_kernel(F16Args a) {
     }
 }
 
+#ifndef SMOE_DENSE_MIN_ROWS
+#define SMOE_DENSE_MIN_ROWS 64  // mean rows per expert from which the tiled GEMM is used
+#endif
 #ifndef SMOE_VF_LONG
 #define SMOE_VF_LONG 8
 #endif
@@ -417,8 +420,10 @@ hipError_t launch_phase(const F16Args& a, int slots, int RB, hipStream_t s) {
 }  // namespace
 
 namespace smoe {
-size_t verify_workspace_bytes(int /*T*/, int rows, int /*H*/, int I, int /*E*/) {
-    return (((size_t)rows * I * 2) + 255) & ~(size_t)255;
+// h [rows, I] fp16, then the dense regime's plan
+size_t verify_workspace_bytes(int /*T*/, int rows, int /*H*/, int I, int E) {
+    const size_t hb = (((size_t)rows * I * 2) + 255) & ~(size_t)255;
+    return hb + ((dense_plan_bytes(E) + 255) & ~(size_t)255);
 }
 
 hipError_t launch_verify_ffn(const uint16_t* x, const int32_t* sorted_token, const int32_t* off,
@@ -426,6 +431,18 @@ hipError_t launch_verify_ffn(const uint16_t* x, const int32_t* sorted_token, con
                              const smoe_f16_expert* experts, const uint8_t* mask, int T, int rows,
                              int H, int I, int E, uint16_t* y, void* ws, int32_t* err,
                              hipStream_t s) {
+    uint16_t* h = static_cast<uint16_t*>(ws);
+    // Many rows per expert: the tiled GEMM of dense.hip.
+    const int groups = (E < rows) ? E : rows;
+    const long long kMax32 = 0x7fffffffLL;  // its element offsets are 32-bit
+    const bool fits32 = (long long)T * H < kMax32 && (long long)rows * I < kMax32 &&
+                        2LL * I * H < kMax32 && (long long)rows * H < kMax32;
+    if (fits32 && rows >= SMOE_DENSE_MIN_ROWS * groups) {
+        int32_t* plan = reinterpret_cast<int32_t*>(
+            static_cast<char*>(ws) + ((((size_t)rows * I * 2) + 255) & ~(size_t)255));
+        return launch_dense_ffn(x, sorted_token, off, active, n_active, experts, mask, rows, H, I,
+                                E, y, h, plan, err, s);
+    }
     // row blocks of 16 held per weight stream, sized for the largest group
     // expected: all rows when there is one expert (a shared expert), else
     // about twice the mean plus slack (bigger groups take extra passes)
@@ -434,7 +451,6 @@ hipError_t launch_verify_ffn(const uint16_t* x, const int32_t* sorted_token, con
     if (est > T) est = T;
     const int RB = (est <= 16) ? 1 : 2;
     const int slots = active ? (E < rows ? E : rows) : E;
-    uint16_t* h = static_cast<uint16_t*>(ws);
     F16Args a1{};
     a1.xin = x;
     a1.sorted_token = sorted_token;

@@ -9,7 +9,7 @@ import torch
 import fp16_verify_expert_amd as fve
 import oracle
 import synth
-from gpu_util import (W_RTOL, Layer, assert_fp16_close, dev, host, run_layer, say)
+from gpu_util import (W_RTOL, Layer, assert_fp16_close, dev, host, run_layer, say, upload_f16)
 
 pytestmark = pytest.mark.gpu
 
@@ -306,6 +306,110 @@ def test_verify_grouped_gemm(shape, T):
     y2 = fve.verify_grouped_gemm(dx, gm["sorted_token"], gm["offsets"], L.t16, T, rows, shape.H,
                                  shape.I, shape.E, ws, err_word=err)
     assert torch.equal(y[:rows], y2[:rows])
+
+
+# dense regime (many rows per expert): the tiled grouped GEMM
+DENSE_CASES = [(synth.TINY, 512, None), (synth.TINY, 300, None), (synth.DS, 700, 40),
+               (synth.PHI, 2048, 24)]
+
+
+def _sample_tokens(T, n):
+    """n tokens spread over [0, T), first and last included (None = all)."""
+    if n is None or n >= T:
+        return np.arange(T)
+    return np.unique(np.linspace(0, T - 1, n).round().astype(np.int64))
+
+
+@pytest.mark.parametrize("shape,T,sample", DENSE_CASES,
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_verify_dense_regime(shape, T, sample):
+    """Mean rows per expert >= 64: the tiled GEMM.  Small cases against the
+    whole grouped oracle; the large ones (the Phi T = 2048 point timed by
+    bench.py among them) on sampled tokens computed one by one."""
+    say(f"verify dense {shape.name} T={T}")
+    L = _layer(shape, (T,), int4=False)
+    x = synth.tokens(shape, T, step=0)
+    r = oracle.route_topk(x, L.router, shape.k)
+    maps = oracle.gather_maps(r["ids"], shape.E)
+    err = _err()
+    dx = dev(x)
+    ids, _, _ = fve.moe_route_topk(dx, L.d_router, shape.k)
+    gm = fve.moe_gather(ids, shape.E, err)
+    assert np.array_equal(host(ids), r["ids"])
+    ws = fve.new_workspace(1, T, shape.k, shape.H, shape.I, shape.E)
+    rows = T * shape.k
+    y = fve.verify_grouped_gemm(dx, gm["sorted_token"], gm["offsets"], L.t16, T, rows, shape.H,
+                                shape.I, shape.E, ws, active=gm["active"],
+                                n_active=gm["n_active"], err_word=err)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) == 0
+    yy = host(y)
+    toks = _sample_tokens(T, sample)
+    if sample is None:
+        ref = oracle.grouped_ffn(x, maps, L.f16, "f16")
+        st = assert_fp16_close(yy[:rows], ref, f"dense {shape.name} T={T}")
+    else:
+        pt = oracle.per_token_ffn(x[toks], r["ids"][toks], L.f16, "f16")
+        got = np.stack([yy[maps["pair_pos"][t * shape.k:(t + 1) * shape.k]] for t in toks])
+        st = assert_fp16_close(got, pt, f"dense {shape.name} T={T} sampled")
+    say(f"  l2={st['l2']:.2e} maxabs={st['maxabs']:.2e}")
+    # deterministic, and the active list is optional
+    y2 = fve.verify_grouped_gemm(dx, gm["sorted_token"], gm["offsets"], L.t16, T, rows, shape.H,
+                                 shape.I, shape.E, ws, err_word=err)
+    assert torch.equal(y[:rows], y2[:rows])
+
+
+def test_verify_dense_mask_and_skew():
+    """Dense regime: hits then misses == all at once (bit-identical), and a
+    skewed routing where one expert holds most rows (many row tiles)."""
+    s, T = synth.TINY, 600
+    rng = np.random.default_rng(11)
+    ids = np.empty((T, s.k), np.int32)
+    for t in range(T):
+        a = 0 if rng.random() < 0.8 else int(rng.integers(1, s.E))
+        b = int(rng.integers(0, s.E - 1))
+        ids[t] = (a, b if b < a else b + 1)
+    data = synth.make_layer(s, 0, int4=False, f16=True)
+    t16, keep = upload_f16(data["f16"])
+    x = synth.tokens(s, T, step=4)
+    maps = oracle.gather_maps(ids, s.E)
+    assert maps["offsets"][1] - maps["offsets"][0] > 400          # expert 0: 4+ row tiles
+    ref = oracle.grouped_ffn(x, maps, data["f16"], "f16")
+    dx = dev(x)
+    gm = fve.moe_gather(dev(ids), s.E)
+    rows = T * s.k
+    ws = fve.new_workspace(1, T, s.k, s.H, s.I, s.E)
+    full = fve.verify_grouped_gemm(dx, gm["sorted_token"], gm["offsets"], t16, T, rows, s.H, s.I,
+                                   s.E, ws, active=gm["active"], n_active=gm["n_active"])
+    torch.cuda.synchronize()
+    assert_fp16_close(host(full)[:rows], ref, "dense skewed")
+    hit = torch.zeros(s.E, dtype=torch.uint8, device="cuda")
+    hit[0] = 1
+    hit[3] = 1
+    y = torch.full_like(full, float("nan"))
+    for m in (hit, 1 - hit):
+        fve.verify_grouped_gemm(dx, gm["sorted_token"], gm["offsets"], t16, T, rows, s.H, s.I,
+                                s.E, ws, active=gm["active"], n_active=gm["n_active"],
+                                expert_mask=m, y_sorted=y)
+    assert torch.equal(y[:rows], full[:rows])
+    del keep
+
+
+def test_shared_expert_dense():
+    """A shared expert over 128 rows (one group of T rows): dense regime."""
+    s, T = synth.QWEN, 128
+    sh = synth.shared_expert(s)
+    tsh, keep = upload_f16([(sh["w13"], sh["w2"])])
+    x = synth.tokens(s, T, step=6)
+    ws = fve.new_workspace(1, T, 1, s.H, s.shared_I, 1)
+    iota = torch.arange(T, dtype=torch.int32, device="cuda")
+    offs = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    y = fve.verify_grouped_gemm(dev(x), iota, offs, tsh, T, T, s.H, s.shared_I, 1, ws)
+    torch.cuda.synchronize()
+    toks = _sample_tokens(T, 32)
+    ref = oracle.expert_ffn_f16(x[toks], sh["w13"], sh["w2"])
+    assert_fp16_close(host(y)[toks], ref, "shared dense")
+    del keep
 
 
 def test_verify_expert_mask_hits_then_misses():
