@@ -48,10 +48,12 @@ def parse():
                     help="draft steps of the oracle timed for cpu_baseline (0 = skip)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
-    ap.add_argument("--workload", default="phi_layer", choices=["phi_layer", "qwen_chunk"],
+    ap.add_argument("--workload", default="phi_layer",
+                    choices=["phi_layer", "qwen_chunk", "route_fidelity"],
                     help="phi_layer (default): one draft + verify step of the Phi-3.5-MoE-shaped "
                          "layer; qwen_chunk: 24 Qwen-shaped layers, 16 draft steps, ELB snapshot, "
-                         "top-16 residency, 17-token verify with staged misses")
+                         "top-16 residency, 17-token verify with staged misses; route_fidelity: INT4 draft vs "
+                         "FP16 target routing agreement and distinct experts vs depth")
     ap.add_argument("--layers", type=int, default=24, help="qwen_chunk: number of layers")
     ap.add_argument("--no-dense-point", dest="dense_point", action="store_false",
                     help="phi_layer: skip the supplementary T=2048 verify point")
@@ -73,6 +75,8 @@ def main():
         sys.exit(2)
     if args.workload == "qwen_chunk":
         return bench_qwen_chunk(args)
+    if args.workload == "route_fidelity":
+        return bench_route_fidelity(args)
 
     import numpy as np
     import torch
@@ -333,6 +337,95 @@ def main():
     print(json.dumps(res), flush=True)
 
 
+def qwen_layers(L, dev):
+    """L Qwen-shaped layers generated on the device: ChunkLayer list (FP16
+    target experts also in page-locked host memory) and every FP16 expert in
+    HBM as [L, E, 3HI]."""
+    import torch
+
+    import synth
+    from fp16_verify_expert_amd.chunk import ChunkLayer
+    s = synth.QWEN_CHUNK
+    layers, full = [], torch.empty((L, s.E, 3 * s.H * s.I), dtype=torch.float16, device=dev)
+    for l in range(L):
+        g = synth.torch_layer(s, l, dev)
+        for e, (w13, w2) in enumerate(g["f16"]):
+            full[l, e, :2 * s.I * s.H].copy_(w13.reshape(-1))
+            full[l, e, 2 * s.I * s.H:].copy_(w2.reshape(-1))
+        del g["f16"]
+        host_f16 = torch.empty((s.E, 3 * s.H * s.I), dtype=torch.float16, pin_memory=True)
+        host_f16.copy_(full[l])
+        layers.append(ChunkLayer(router=g["router"], int4=g["int4"], host_f16=host_f16,
+                                 shared=(g["shared"]["w13"], g["shared"]["w2"]),
+                                 shared_gate=g["shared"]["gate"]))
+        print(f"generated layer {l}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    return layers, full
+
+
+def bench_route_fidelity(args):
+    """Draft/target routing agreement and expert demand vs speculation depth
+    on residual-chained synthetic Qwen-shaped layers ([S1] Key Contributions
+    1: the INT4 copy preserves expert routing; Main Findings: distinct experts
+    per layer grow with the depth).  For token streams of lag-one correlation
+    rho (a routing-locality knob), every token runs through all layers twice,
+    with the INT4 draft experts and with the FP16 target experts (each chain
+    on its own outputs, as in drafting and verification).  Reported per rho:
+    the mean top-k expert-ID overlap |draft ∩ target| / k per layer and
+    overall, and the distinct target experts per layer among K consecutive
+    tokens for K = 1..32.  Synthetic weights: the numbers describe this
+    kernel stack on random layers, not the pages' trained models."""
+    import numpy as np
+    import torch
+
+    import fp16_verify_expert_amd as fve
+    import synth
+    from fp16_verify_expert_amd.chunk import ChunkEngine
+
+    fve.lib()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda")
+    s = synth.QWEN_CHUNK
+    L, N = args.layers, 256
+    t0 = time.perf_counter()
+    layers, full = qwen_layers(L, dev)
+    eng = ChunkEngine(layers, s.H, s.E, s.k, s.I, s.shared_I, 16, 17, device=dev)
+    gen_s = time.perf_counter() - t0
+    depths = [1, 2, 4, 8, 16, 32]
+    per_rho = {}
+    t1 = time.perf_counter()
+    for rho in (0.0, 0.5, 0.8, 0.9, 0.95):
+        x = torch.from_numpy(synth.token_stream(s, N, rho)).to(dev)
+        rd, rt = [], []
+        eng.forward(x, "int4", record=rd)
+        eng.forward(x, "f16", full, record=rt)
+        torch.cuda.synchronize()
+        assert int(eng.err.item()) == 0, "device error word set"
+        d = torch.stack(rd).cpu().numpy()     # [L, N, k]
+        t = torch.stack(rt).cpu().numpy()
+        match = np.array([[len(set(d[l, i]) & set(t[l, i])) / s.k for i in range(N)]
+                          for l in range(L)])
+        distinct = {}
+        for K in depths:
+            nw = N // K
+            c = [[len(np.unique(t[l, w * K:(w + 1) * K])) for w in range(nw)] for l in range(L)]
+            distinct[K] = float(np.mean(c))
+        per_rho[str(rho)] = {
+            "topk_match_mean": round(float(match.mean()), 4),
+            "topk_match_per_layer": [round(float(v), 3) for v in match.mean(axis=1)],
+            "distinct_experts_vs_depth": {str(K): round(v, 2) for K, v in distinct.items()},
+            "growth_1_to_16": round(distinct[16] / distinct[1], 2)}
+    out = {"metric": "draft/target top-k expert-ID agreement; distinct experts vs depth",
+           "value": per_rho["0.0"]["topk_match_mean"], "unit": "fraction", "n_gpus": 1,
+           "higher_is_better": True, "vs_baseline": None, "data": "synthetic",
+           "config": {"workload": f"route_fidelity: {L} Qwen-shaped layers (H=2048 E=60 top-4 "
+                                  f"I=1408 + gated shared 5632), {N} tokens per stream, INT4 "
+                                  f"RTN g128 draft vs FP16 target, pre-norm residual chain"},
+           "per_rho": per_rho, "gen_s": round(gen_s, 1),
+           "run_s": round(time.perf_counter() - t1, 1)}
+    print(json.dumps(out), flush=True)
+
+
 def bench_qwen_chunk(args):
     """Draft chunk + verify over L Qwen-shaped layers with 16 of 60 FP16
     experts resident per layer.  One step = 16 INT4 draft decode steps through
@@ -353,20 +446,7 @@ def bench_qwen_chunk(args):
     s = synth.QWEN_CHUNK
     L, STEPS, TV, NRES = args.layers, 16, 17, 16
     t0 = time.perf_counter()
-    layers, full = [], torch.empty((L, s.E, 3 * s.H * s.I), dtype=torch.float16, device=dev)
-    for l in range(L):
-        g = synth.torch_layer(s, l, dev)
-        for e, (w13, w2) in enumerate(g["f16"]):
-            full[l, e, :2 * s.I * s.H].copy_(w13.reshape(-1))
-            full[l, e, 2 * s.I * s.H:].copy_(w2.reshape(-1))
-        del g["f16"]
-        host_f16 = torch.empty((s.E, 3 * s.H * s.I), dtype=torch.float16, pin_memory=True)
-        host_f16.copy_(full[l])
-        layers.append(ChunkLayer(router=g["router"], int4=g["int4"], host_f16=host_f16,
-                                 shared=(g["shared"]["w13"], g["shared"]["w2"]),
-                                 shared_gate=g["shared"]["gate"]))
-        print(f"generated layer {l}", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
+    layers, full = qwen_layers(L, dev)
     gen_s = time.perf_counter() - t0
     eng = ChunkEngine(layers, s.H, s.E, s.k, s.I, s.shared_I, NRES, TV, device=dev)
     mk = lambda: torch.cuda.Event(enable_timing=True)

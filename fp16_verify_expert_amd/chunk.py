@@ -166,6 +166,45 @@ class ChunkEngine:
         self.graph.replay()
         return self.out_static
 
+    # ------------------------------------------------------ any-T forward ----
+    def forward(self, x: torch.Tensor, kind: str, full: Optional[torch.Tensor] = None,
+                record: Optional[list] = None) -> torch.Tensor:
+        """All layers over T rows with every expert in HBM: kind "int4" runs
+        the draft's W4A16 experts, kind "f16" the target's FP16 experts read
+        from `full` ([L, E, 3HI]).  No ELB update, no staging.  Each layer's
+        ids are appended to `record` ([T, k] int32 tensors)."""
+        T = x.shape[0]
+        ws = new_workspace(0 if kind == "int4" else 1, T, self.k, self.H, self.I, self.E,
+                           device=self.dev)
+        xn = x
+        for l, ly in enumerate(self.layers):
+            ids, w, gate = moe_route_topk(xn, ly.router, self.k, False, ly.shared_gate)
+            maps = moe_gather(ids, self.E, self.err)
+            sh = None
+            if self.tsh[l] is not None:
+                wsh = new_workspace(1, T, 1, self.H, self.Is, 1, device=self.dev)
+                sh = verify_grouped_gemm(xn, self.iota_n(T), self.offs_n(T), self.tsh[l], T, T,
+                                         self.H, self.Is, 1, wsh, err_word=self.err)
+            if kind == "int4":
+                y = w4a16_grouped_ffn(xn, maps, self.t4[l], T, self.k, self.H, self.I, self.E, ws,
+                                      err_word=self.err)
+            else:
+                y = verify_grouped_gemm(xn, maps["sorted_token"], maps["offsets"],
+                                        self._resident_table(full, l), T, T * self.k, self.H,
+                                        self.I, self.E, ws, active=maps["active"],
+                                        n_active=maps["n_active"], err_word=self.err)
+            out, xn_next = moe_combine(y, maps["pair_pos"], w, sh, gate, x, norm_out=True)
+            if record is not None:
+                record.append(ids)
+            x, xn = out, xn_next
+        return x
+
+    def iota_n(self, T: int) -> torch.Tensor:
+        return torch.arange(T, dtype=torch.int32, device=self.dev)
+
+    def offs_n(self, T: int) -> torch.Tensor:
+        return torch.tensor([0, T], dtype=torch.int32, device=self.dev)
+
     def snapshot(self) -> np.ndarray:
         """Copy of the ELB table (synchronises)."""
         return self.counters.cpu().numpy()

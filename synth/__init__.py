@@ -216,6 +216,22 @@ def tokens(shape: LayerShape, T: int, step: int = 0, layer: int = 0, seed: int =
     return normal_f16((seed, shape.config_id, layer, 0, T_TOKENS, step), (T, shape.H), 1.0)
 
 
+def token_stream(shape: LayerShape, n: int, rho: float, step: int = 0,
+                 seed: int = BASE_SEED) -> np.ndarray:
+    """fp16 [n, H] token rows with N(0, 1) marginals and lag-one correlation
+    rho between consecutive rows (an AR(1) stream): consecutive tokens then
+    tend to route alike, a knob for the routing locality of real text.
+    rho = 0 gives independent rows."""
+    g = _rng(seed, shape.config_id, 0, 0, T_TOKENS, 1_000_000 + step)
+    eps = g.standard_normal((n, shape.H), dtype=np.float32)
+    out = np.empty_like(eps)
+    c = np.float32(np.sqrt(1.0 - rho * rho))
+    out[0] = eps[0]
+    for t in range(1, n):
+        out[t] = np.float32(rho) * out[t - 1] + c * eps[t]
+    return out.astype(np.float16)
+
+
 def make_layer(shape: LayerShape, layer: int = 0, seed: int = BASE_SEED,
                experts: Optional[Sequence[int]] = None, int4: bool = True,
                f16: bool = True, threads: Optional[int] = None) -> Dict:

@@ -183,3 +183,28 @@ def test_chunk_draft_graph_matches_eager(chunk):
     assert torch.equal(eng.counters, 3 * c_ref)
     assert int(host(eng.err)[0]) == 0
     eng.counters.copy_(saved)
+
+
+def test_chunk_forward_matches_draft_and_verify(chunk):
+    """The any-T forward used by the route-fidelity probe runs the very same
+    kernels: FP16 over 17 rows equals the all-resident verify bit for bit, and
+    INT4 over one row equals the draft step."""
+    s = chunk["shape"]
+    eng = chunk["eng"]
+    full = torch.empty((LAYERS, s.E, 3 * s.H * s.I), dtype=torch.float16, device="cuda")
+    for l in range(LAYERS):
+        full[l].copy_(eng.layers[l].host_f16)
+    ref = eng.verify(chunk["xv"], all_resident=full).clone()
+    rec = []
+    out = eng.forward(chunk["xv"], "f16", full, rec)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert len(rec) == LAYERS and all(r.shape == (17, s.k) for r in rec)
+    saved = eng.counters.clone()
+    x1 = chunk["xv"][:1].contiguous()
+    d = eng.draft_step(x1).clone()
+    f = eng.forward(x1, "int4")
+    torch.cuda.synchronize()
+    assert torch.equal(f, d)
+    eng.counters.copy_(saved)
+    assert int(host(eng.err)[0]) == 0

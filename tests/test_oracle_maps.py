@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
+import synth
 
 
 def _ids(T, k, E, seed):
@@ -101,3 +102,14 @@ def test_gather_drops_out_of_range():
     assert m["offsets"].tolist() == [0, 1, 2, 2]
     assert m["pair_pos"].tolist() == [1, -1, 0, -1]
     assert m["sorted_pair"][:2].tolist() == [2, 0]
+
+
+def test_token_stream_correlation():
+    """The AR(1) token stream: unit marginals, lag-one correlation rho,
+    independent rows at rho = 0 (input generator only)."""
+    s = synth.QWEN_CHUNK
+    for rho in (0.0, 0.8):
+        x = synth.token_stream(s, 400, rho).astype(np.float64)
+        assert abs(x.std() - 1.0) < 0.02
+        c = np.mean(np.sum(x[1:] * x[:-1], axis=1) / s.H)
+        assert abs(c - rho) < 0.02
