@@ -49,12 +49,17 @@ def parse():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--workload", default="phi_layer",
-                    choices=["phi_layer", "qwen_chunk", "route_fidelity"],
+                    choices=["phi_layer", "qwen_chunk", "route_fidelity", "qwen_rounds"],
                     help="phi_layer (default): one draft + verify step of the Phi-3.5-MoE-shaped "
                          "layer; qwen_chunk: 24 Qwen-shaped layers, 16 draft steps, ELB snapshot, "
                          "top-16 residency, 17-token verify with staged misses; route_fidelity: INT4 draft vs "
-                         "FP16 target routing agreement and distinct experts vs depth")
+                         "FP16 target routing agreement and distinct experts vs depth; qwen_rounds: speculation "
+                         "rounds with the prefetch planner vs boundary placement")
     ap.add_argument("--layers", type=int, default=24, help="qwen_chunk: number of layers")
+    ap.add_argument("--rounds", type=int, default=4, help="qwen_rounds: speculation rounds")
+    ap.add_argument("--rho", type=float, default=0.8,
+                    help="qwen_rounds: lag-one correlation of the token stream (0.8 gives about "
+                         "7x distinct experts from depth 1 to 16 on these layers)")
     ap.add_argument("--no-dense-point", dest="dense_point", action="store_false",
                     help="phi_layer: skip the supplementary T=2048 verify point")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
@@ -77,6 +82,8 @@ def main():
         return bench_qwen_chunk(args)
     if args.workload == "route_fidelity":
         return bench_route_fidelity(args)
+    if args.workload == "qwen_rounds":
+        return bench_qwen_rounds(args)
 
     import numpy as np
     import torch
@@ -423,6 +430,96 @@ def bench_route_fidelity(args):
                                   f"RTN g128 draft vs FP16 target, pre-norm residual chain"},
            "per_rho": per_rho, "gen_s": round(gen_s, 1),
            "run_s": round(time.perf_counter() - t1, 1)}
+    print(json.dumps(out), flush=True)
+
+
+def bench_qwen_rounds(args):
+    """Speculation rounds with offloaded FP16 target experts ([S1] Key
+    Contributions 3: the Layer-Aware Prefetch Planner with Cold Start,
+    Prefetch Overlap and Final Cleanup, then the residency manager computing
+    hits while misses load).  R consecutive rounds over one AR(1) token
+    stream (lag-one correlation --rho: a routing-locality knob); each round
+    drafts 16 tokens (INT4, graph-replayed) through 24 Qwen-shaped layers and
+    verifies 17 (FP16), with 16 of 60 experts per layer resident.  Two
+    policies: boundary placement (draft all, then place the top-16 per layer,
+    then verify) and the planner (chunked drafting with ELB-driven prefetch
+    overlapped, per-layer events, residency carried across rounds).  The same
+    rounds with every expert in HBM give the compute-only time; the exposed
+    H2D time of a round is its wall time minus that."""
+    import numpy as np
+    import torch
+
+    import fp16_verify_expert_amd as fve
+    import synth
+    from fp16_verify_expert_amd.chunk import ChunkEngine
+
+    fve.lib()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda")
+    s = synth.QWEN_CHUNK
+    L, STEPS, R = args.layers, 16, args.rounds
+    t0 = time.perf_counter()
+    layers, full = qwen_layers(L, dev)
+    eng = ChunkEngine(layers, s.H, s.E, s.k, s.I, s.shared_I, 16, 17, device=dev)
+    eng.capture_draft()
+    gen_s = time.perf_counter() - t0
+    stream = torch.from_numpy(synth.token_stream(s, STEPS * R + 1, args.rho)).to(dev)
+
+    def round_inputs(r):
+        xs = [stream[STEPS * r + st:STEPS * r + st + 1] for st in range(STEPS)]
+        return xs, stream[STEPS * r:STEPS * r + STEPS + 1]
+
+    # compute only: the same drafts and verifies with every expert in HBM
+    comp = []
+    for r in range(R):
+        xs, xv = round_inputs(r)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        for x in xs:
+            eng.draft_step_graph(x)
+        e[1].record()
+        eng.verify(xv, all_resident=full)
+        e[2].record()
+        torch.cuda.synchronize()
+        comp.append((e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])))
+    step_s = float(np.mean([c[0] for c in comp])) / STEPS * 1e-3
+    res = {}
+    for name, planner in (("boundary", False), ("planner", True)):
+        eng.resident = [[-1] * eng.nres for _ in range(L)]
+        eng.stats = dict(staged_experts=0, staged_bytes=0, hit_experts=0, miss_experts=0,
+                         prefetched_experts=0)
+        rounds = []
+        for r in range(R):
+            xs, xv = round_inputs(r)
+            before = dict(eng.stats)
+            tm = {}
+            eng.run_round(xs, xv, planner=planner, step_s=step_s, timing=tm)
+            torch.cuda.synchronize()
+            assert int(eng.err.item()) == 0, "device error word set"
+            d = {k2: eng.stats[k2] - before.get(k2, 0) for k2 in eng.stats}
+            wall = tm["start"].elapsed_time(tm["end"])
+            rounds.append(dict(ms=round(wall, 2),
+                               draft_ms=round(tm["start"].elapsed_time(tm["drafted"]), 2),
+                               exposed_h2d_ms=round(wall - sum(comp[r]), 2),
+                               placed_or_prefetched=(d.get("prefetched_experts", 0) if planner
+                                                     else L * eng.nres),
+                               hits=d["hit_experts"], misses=d["miss_experts"]))
+        warm = rounds[1:] if R > 1 else rounds
+        res[name] = {"rounds": rounds,
+                     "mean_ms_after_cold": round(float(np.mean([x["ms"] for x in warm])), 2),
+                     "mean_exposed_h2d_ms_after_cold":
+                         round(float(np.mean([x["exposed_h2d_ms"] for x in warm])), 2),
+                     "hit_rate": round(sum(x["hits"] for x in rounds) /
+                                       max(1, sum(x["hits"] + x["misses"] for x in rounds)), 3)}
+    out = {"metric": "exposed H2D time per speculation round (ms)",
+           "value": res["planner"]["mean_exposed_h2d_ms_after_cold"], "unit": "ms",
+           "n_gpus": 1, "higher_is_better": False, "vs_baseline": None,
+           "data": f"synthetic (AR(1) token stream, rho={args.rho})",
+           "config": {"workload": f"qwen_rounds: {R} rounds x (16 INT4 draft steps + 17-token "
+                                  f"FP16 verify), {L} Qwen-shaped layers, 16/60 experts resident "
+                                  f"per layer, pinned-host staging"},
+           "compute_only_ms": [round(a + b, 2) for a, b in comp],
+           "policies": res, "gen_s": round(gen_s, 1)}
     print(json.dumps(out), flush=True)
 
 

@@ -65,11 +65,18 @@ class ChunkEngine:
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
         self.pool = torch.empty((self.L, n_resident, 3 * H * I), dtype=torch.float16, device=dev)
         self.stage = torch.empty((2, E, 3 * H * I), dtype=torch.float16, device=dev)
-        self.resident: List[List[int]] = [[] for _ in range(self.L)]
+        # per layer: the expert held by each pool slot (-1 = empty)
+        self.resident: List[List[int]] = [[-1] * n_resident for _ in range(self.L)]
         self.t4 = [w4_expert_table(l.int4, device=dev) for l in self.layers]
         self.tsh = [None if l.shared is None else f16_expert_table([l.shared], device=dev)
                     for l in self.layers]
-        self.side = torch.cuda.Stream(device=dev)    # staging copies; default priority
+        self.side = torch.cuda.Stream(device=dev)    # staging of misses; default priority
+        self.copy = torch.cuda.Stream(device=dev)    # prefetch into the pools; default priority
+        self.ev_layer = [torch.cuda.Event() for _ in range(self.L)]  # prefetches of layer l landed
+        self.ev_round_done = torch.cuda.Event()      # the last verify read the pools
+        self.snap_host = [torch.zeros((self.L, E), dtype=torch.int32).pin_memory()
+                          for _ in range(2)]
+        self.snap_ev = [torch.cuda.Event() for _ in range(2)]
         self.side_sh = torch.cuda.Stream(device=dev)  # shared expert; default priority
         self.ev_staged = [torch.cuda.Event() for _ in range(2)]
         self.ev_free = [torch.cuda.Event() for _ in range(2)]
@@ -218,9 +225,101 @@ class ChunkEngine:
         resident (copied from pinned host memory into the layer's pool)."""
         for l in range(self.L):
             res = top_resident(counts[l], self.nres)
-            self.resident[l] = res
+            self.resident[l] = list(res)
             for j, e in enumerate(res):
                 self.pool[l, j].copy_(self.layers[l].host_f16[e], non_blocking=True)
+
+    # ----------------------------------------------------------- planner ----
+    def prefetch(self, counts: np.ndarray) -> int:
+        """Layer-aware prefetch from an ELB snapshot: in every layer the
+        experts with the largest counts (count > 0, at most the pool size)
+        should be resident; the missing ones are copied from pinned host
+        memory into pool slots on the copy stream, highest count first,
+        reusing the slots of residents that fell out of that set (empty slots
+        first, then the lowest count).  Layer l's event is recorded after its
+        copies, so it marks that every prefetch into its pool issued so far
+        has landed (the copy stream runs them in order).  Returns the number
+        of experts copied."""
+        n = 0
+        for l in range(self.L):
+            c = counts[l]
+            want = [e for e in sorted(top_resident(c, self.nres), key=lambda e: (-int(c[e]), e))
+                    if c[e] > 0]
+            res = self.resident[l]
+            have = set(e for e in res if e >= 0)
+            load = [e for e in want if e not in have]
+            if load:
+                wset = set(want)
+                free = [j for j, e in enumerate(res) if e < 0 or e not in wset]
+                free.sort(key=lambda j: (res[j] >= 0, int(c[res[j]]) if res[j] >= 0 else -1))
+                for e, j in zip(load, free):
+                    expert_stage_async(self.pool[l, j], self.layers[l].host_f16[e], self.copy)
+                    res[j] = e
+                    n += 1
+            self.ev_layer[l].record(self.copy)
+        self.stats["prefetched_experts"] = self.stats.get("prefetched_experts", 0) + n
+        return n
+
+    def _snapshot_async(self, i: int) -> None:
+        """Enqueue a copy of the ELB table into page-locked buffer i."""
+        self.snap_host[i].copy_(self.counters, non_blocking=True)
+        self.snap_ev[i].record()
+
+    def _snapshot_read(self, i: int) -> np.ndarray:
+        self.snap_ev[i].synchronize()
+        return self.snap_host[i].numpy().copy()
+
+    def run_round(self, xs: Sequence[torch.Tensor], xv: torch.Tensor, planner: bool = True,
+                  chunk0: int = 2, step_s: float = 1.3e-3, h2d_gbps: float = 55.0,
+                  timing: Optional[dict] = None) -> torch.Tensor:
+        """One speculation round: len(xs) INT4 draft steps (graph-replayed;
+        capture_draft first), then the FP16 verify of xv.
+
+        planner=True: Cold Start -- the first chunk of chunk0 steps is drafted
+        with no prediction; Prefetch Overlap -- while each next chunk drafts,
+        the snapshot of the chunk before it drives prefetches on the copy
+        stream, and the next chunk is sized so that its drafting roughly
+        covers the transfer just issued (step_s per step, h2d_gbps per
+        copy); Final Cleanup -- the last snapshot's prefetches, then the
+        verify, where each layer's hits wait only for that layer's
+        prefetches and misses are staged behind them.  Residency carries over
+        from round to round.  planner=False: draft every step, snapshot,
+        place the top experts of every layer, then verify (all copies exposed).
+        `timing` (dict) receives HIP events: start, drafted, end."""
+        main = torch.cuda.current_stream()
+        ev = {k: torch.cuda.Event(enable_timing=True) for k in ("start", "drafted", "end")}
+        self.clear_counters()
+        ev["start"].record(main)
+        steps = len(xs)
+        if not planner:
+            for x in xs:
+                self.draft_step_graph(x)
+            ev["drafted"].record(main)
+            self.place_residents(self.snapshot())
+        else:
+            # pools may be rewritten only once the previous round's verify read them
+            self.copy.wait_event(self.ev_round_done)
+            done, c, pending, k = 0, max(1, chunk0), None, 0
+            while done < steps:
+                n = min(c, steps - done)
+                for st in range(done, done + n):
+                    self.draft_step_graph(xs[st])
+                done += n
+                self._snapshot_async(k % 2)
+                if pending is not None:
+                    nload = self.prefetch(self._snapshot_read(pending))
+                    t_copy = nload * self.ebytes / (h2d_gbps * 1e9)
+                    c = max(1, int(round(t_copy / step_s)))
+                pending = k % 2
+                k += 1
+            ev["drafted"].record(main)
+            self.prefetch(self._snapshot_read(pending))
+        out = self.verify(xv)
+        self.ev_round_done.record(main)
+        ev["end"].record(main)
+        if timing is not None:
+            timing.update(ev)
+        return out
 
     # ------------------------------------------------------------ verify ----
     def verify(self, x: torch.Tensor, record: Optional[list] = None,
@@ -276,7 +375,7 @@ class ChunkEngine:
         act = maps["active"].cpu().numpy()          # the target router's decisions
         needed = [int(e) for e in act if e >= 0]
         res = self.resident[l]
-        slot = {e: j for j, e in enumerate(res)}
+        slot = {e: j for j, e in enumerate(res) if e >= 0}
         hits = [e for e in needed if e in slot]
         misses = [e for e in needed if e not in slot]
         b = l % 2
@@ -303,6 +402,7 @@ class ChunkEngine:
                                    self.ev_staged[b] if last else None)
         kw = dict(active=maps["active"], n_active=maps["n_active"], y_sorted=y, err_word=self.err)
         if hits:
+            main.wait_event(self.ev_layer[l])  # this layer's prefetches (if any) have landed
             verify_grouped_gemm(x, maps["sorted_token"], maps["offsets"], self.d_table[l], T, rows,
                                 self.H, self.I, self.E, self.ws_v, expert_mask=self.d_mask[l, 0],
                                 **kw)

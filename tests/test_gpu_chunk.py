@@ -208,3 +208,32 @@ def test_chunk_forward_matches_draft_and_verify(chunk):
     assert torch.equal(f, d)
     eng.counters.copy_(saved)
     assert int(host(eng.err)[0]) == 0
+
+
+def test_chunk_planner_rounds_residency_invariant(chunk):
+    """Speculation rounds with the prefetch planner (chunked drafting, ELB
+    snapshots driving prefetches on the copy stream, per-layer events, misses
+    staged at verify) and with boundary placement: every round's output is
+    bit-identical to the all-resident verify of the same rows."""
+    s = chunk["shape"]
+    eng = chunk["eng"]
+    full = torch.empty((LAYERS, s.E, 3 * s.H * s.I), dtype=torch.float16, device="cuda")
+    for l in range(LAYERS):
+        full[l].copy_(eng.layers[l].host_f16)
+    if not hasattr(eng, "graph"):
+        eng.capture_draft()
+    before = eng.stats.get("prefetched_experts", 0)
+    for r, planner in enumerate((True, True, False, True)):
+        xs = [torch.from_numpy(synth.tokens(s, 1, step=300 + 20 * r + st)).cuda()
+              for st in range(STEPS)]
+        xv = torch.cat(xs + [torch.from_numpy(synth.tokens(s, 1, step=300 + 20 * r + STEPS)).cuda()])
+        say(f"round {r} planner={planner}")
+        out = eng.run_round(xs, xv, planner=planner).clone()
+        ref = eng.verify(xv, all_resident=full)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), r
+        for l in range(LAYERS):
+            held = [e for e in eng.resident[l] if e >= 0]
+            assert len(set(held)) == len(held)
+    assert eng.stats["prefetched_experts"] > before
+    assert int(host(eng.err)[0]) == 0
