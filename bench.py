@@ -3,9 +3,10 @@
 
 Default workload: the Phi-3.5-MoE-shaped layer (hidden 4096, 16 experts,
 top-2, SwiGLU intermediate 6400, no shared expert).  One step is one INT4
-draft decode step (T = 1: fused route + ELB count + gather, W4A16 FFN,
-combine; launched call by call, or replayed as a captured HIP graph with
---graph on) followed by one
+draft decode step (T = 1: routing + ELB count + gather folded into the gate/up
+launch, the down projection, combine -- or with --draft split the fused
+routing plan, the W4A16 FFN and combine; launched call by call, or replayed
+as a captured HIP graph with --graph on) followed by one
 FP16 verification of K+1 = 17 tokens (route, gather,
 regrouped verify FFN, combine), every step through the C ABI of libsmoe.so
 on seeded synthetic inputs already resident in HBM.  Steps cycle over a pool
@@ -62,6 +63,10 @@ def parse():
                          "7x distinct experts from depth 1 to 16 on these layers)")
     ap.add_argument("--no-dense-point", dest="dense_point", action="store_false",
                     help="phi_layer: skip the supplementary T=2048 verify point")
+    ap.add_argument("--draft", choices=["fused", "split"], default="fused",
+                    help="phi_layer draft step: moe_draft_route_ffn + moe_combine (fused: routing "
+                         "folded into the gate/up launch, 3 launches) or moe_route_plan + "
+                         "w4a16_grouped_ffn + moe_combine (split, 4 launches)")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
                     help="replay the draft step as a captured HIP graph (on) or launch its calls "
                          "one by one (off); auto = off for phi_layer (4 launches per step: "
@@ -130,7 +135,7 @@ def main():
     counters = torch.zeros((1, E), dtype=torch.int32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
 
-    def draft(i, ev=None):
+    def draft_split(i, ev=None):
         x = xs_d[i % POOL]
         fve.moe_route_plan(x, router, k, counters=counters, layer=0, err_word=err,
                            topk_ids=bd["ids"], topk_w=bd["w"], maps=bd["maps"])
@@ -139,6 +144,17 @@ def main():
                               err_word=err)
         if ev: ev[1].record()
         fve.moe_combine(bd["y"], bd["maps"]["pair_pos"], bd["w"], out=bd["out"])
+
+    def draft_fused(i, ev=None):
+        x = xs_d[i % POOL]
+        if ev: ev[0].record()
+        fve.moe_draft_route_ffn(x, router, k, t4, I, ws_d, counters=counters, layer=0,
+                                err_word=err, topk_ids=bd["ids"], topk_w=bd["w"],
+                                maps=bd["maps"], y_sorted=bd["y"])
+        if ev: ev[1].record()
+        fve.moe_combine(bd["y"], bd["maps"]["pair_pos"], bd["w"], out=bd["out"])
+
+    draft = draft_fused if args.draft == "fused" else draft_split
 
     def verify(i, ev=None):
         x = xs_v[i % POOL]
@@ -151,12 +167,17 @@ def main():
         if ev: ev[1].record()
         fve.moe_combine(bv["y"], bv["maps"]["pair_pos"], bv["w"], out=bv["out"])
 
-    # ---- per-batch algorithmic work (routing is deterministic) ----
+    # ---- per-batch algorithmic work (routing is deterministic); the two
+    #      draft paths must agree bit for bit ----
     touched_d, touched_v = [], []
     for i in range(POOL):
+        draft_split(i)
+        torch.cuda.synchronize()
+        ref_out = bd["out"].clone()
         draft(i)
         verify(i)
         torch.cuda.synchronize()
+        assert torch.equal(bd["out"], ref_out), "fused and split draft steps differ"
         touched_d.append(int(bd["maps"]["n_active"].item()))
         touched_v.append(int(bv["maps"]["n_active"].item()))
     assert int(err.item()) == 0, "device error word set"
@@ -192,7 +213,7 @@ def main():
     K = args.steps
     mk = lambda: torch.cuda.Event(enable_timing=True)
     ph = [(mk(), mk(), mk()) for _ in range(K)]            # draft start / verify start / end
-    kd = [(mk(), mk()) for _ in range(K)]                  # w4a16 call
+    kd = [(mk(), mk()) for _ in range(K)]                  # w4a16 (split) or fused call
     kv = [(mk(), mk()) for _ in range(K)]                  # verify call
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -209,17 +230,23 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     assert int(err.item()) == 0, "device error word set"
-    if graphs is not None:
-        # the W4A16 kernel's own duration, from an eager pass with events
-        # around that call (a captured graph takes no per-call events)
+    # the W4A16 entry point's own duration, from an eager pass of the split
+    # step with events around that call (a captured graph takes no per-call
+    # events; the fused call also holds the routing)
+    kw = kd
+    if graphs is not None or args.draft == "fused":
+        kw = [(mk(), mk()) for _ in range(K)]
         for st in range(K):
-            draft(args.warmup + st, kd[st])
+            draft_split(args.warmup + st, kw[st])
+            verify(args.warmup + st)
         torch.cuda.synchronize()
 
     idx = [(args.warmup + st) % POOL for st in range(K)]
     draft_ms = sum(ph[st][0].elapsed_time(ph[st][1]) for st in range(K))
     verify_ms = sum(ph[st][1].elapsed_time(ph[st][2]) for st in range(K))
-    w4_ms = [kd[st][0].elapsed_time(kd[st][1]) for st in range(K)]
+    w4_ms = [kw[st][0].elapsed_time(kw[st][1]) for st in range(K)]
+    fused_ms = ([kd[st][0].elapsed_time(kd[st][1]) for st in range(K)]
+                if args.draft == "fused" and graphs is None else None)
     vg_ms = [kv[st][0].elapsed_time(kv[st][1]) for st in range(K)]
     bytes_d = sum(touched_d[i] * b4 for i in idx)
     bytes_v = sum(touched_v[i] * b16 for i in idx)
@@ -269,6 +296,10 @@ def main():
                    "draft_tokens": T_D, "verify_tokens": T_V, "batch_pool": POOL},
         "draft": {"ms": round(draft_ms / K, 4), "gbps": round(value, 2),
                   "launch": "hip_graph" if graphs is not None else "eager",
+                  "path": ("moe_draft_route_ffn + moe_combine" if args.draft == "fused" else
+                           "moe_route_plan + w4a16_grouped_ffn + moe_combine"),
+                  "fused_call_us": (None if fused_ms is None else
+                                    round(1e3 * sum(fused_ms) / K, 3)),
                   "frac_hbm": round(value / HBM_PEAK_GBS, 4),
                   "touched_experts_avg": round(sum(touched_d[i] for i in idx) / K, 3),
                   "int4_bytes_avg": round(bytes_d / K)},

@@ -48,6 +48,9 @@ _SIGS = {
                             _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "w4a16_grouped_ffn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp,
                                _sz, _vp, _vp]),
+    "moe_draft_route_ffn": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp,
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
+                                 _vp]),
     "verify_grouped_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp,
                                  _vp, _sz, _vp, _vp]),
     "moe_combine": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, ctypes.c_float,
@@ -235,6 +238,44 @@ def w4a16_grouped_ffn(x, maps, table, T: int, k: int, H: int, I: int, E: int, wo
           _p(y_sorted), _p(workspace), workspace.numel() * workspace.element_size(),
           _p(err_word), _s(stream))
     return y_sorted
+
+
+def moe_draft_route_ffn(x, w_router, k: int, table, I: int, workspace,
+                        renormalize: bool = False, w_shared_gate=None, *, counters=None,
+                        layer: int = 0, err_word=None, topk_ids=None, topk_w=None,
+                        shared_gate=None, maps=None, y_sorted=None, stream=None):
+    """One-token draft step: moe_route_plan and w4a16_grouped_ffn in two
+    launches.  Returns (topk_ids, topk_w, shared_gate, maps, y_sorted)."""
+    _check(x, torch.float16, "x")
+    _check(w_router, torch.float16, "w_router")
+    T, H = x.shape
+    if T != 1:
+        raise ValueError(f"moe_draft_route_ffn takes one token, got T={T}")
+    E = w_router.shape[0]
+    dev = x.device
+    if topk_ids is None:
+        topk_ids = torch.empty((1, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((1, k), dtype=torch.float32, device=dev)
+    if w_shared_gate is not None:
+        _check(w_shared_gate, torch.float16, "w_shared_gate")
+        if shared_gate is None:
+            shared_gate = torch.empty((1,), dtype=torch.float32, device=dev)
+    L = 0
+    if counters is not None:
+        _check(counters, torch.int32, "counters")
+        L = counters.shape[0]
+    if maps is None:
+        maps = _new_maps(1, k, E, dev)
+    if y_sorted is None:
+        y_sorted = torch.empty((k, H), dtype=torch.float16, device=dev)
+    _call("moe_draft_route_ffn", _p(x), _p(w_router), _p(w_shared_gate), H, I, E, k,
+          1 if renormalize else 0, layer, L, _p(counters), _p(table), 128, _p(topk_ids),
+          _p(topk_w), _p(shared_gate) if w_shared_gate is not None else None,
+          _p(maps["offsets"]), _p(maps["sorted_token"]), _p(maps["sorted_pair"]),
+          _p(maps["pair_pos"]), _p(maps["active"]), _p(maps["n_active"]), _p(y_sorted),
+          _p(workspace), workspace.numel() * workspace.element_size(), _p(err_word), _s(stream))
+    return topk_ids, topk_w, shared_gate, maps, y_sorted
 
 
 def verify_grouped_gemm(x, sorted_token, offsets, table, T: int, rows: int, H: int, I: int,

@@ -220,6 +220,50 @@ smoe_status w4a16_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
                       "w4a16_grouped_ffn launch");
 }
 
+smoe_status moe_draft_route_ffn(const uint16_t* x, const uint16_t* w_router,
+                                const uint16_t* w_shared_gate, int H, int I, int E, int k,
+                                int renormalize, int layer, int L, int32_t* counters,
+                                const smoe_w4_expert* experts, int group_size,
+                                int32_t* topk_ids, float* topk_w, float* shared_gate,
+                                int32_t* expert_offsets, int32_t* sorted_token,
+                                int32_t* sorted_pair, int32_t* pair_pos, int32_t* active,
+                                int32_t* n_active, uint16_t* y_sorted, void* workspace,
+                                size_t workspace_bytes, int32_t* err_word, void* stream) {
+    REQUIRE(x && w_router && experts && topk_ids && topk_w && expert_offsets && sorted_token &&
+                sorted_pair && pair_pos && active && n_active && y_sorted,
+            SMOE_ERR_NULL, "moe_draft_route_ffn: a required pointer is NULL");
+    REQUIRE(!w_shared_gate || shared_gate, SMOE_ERR_NULL,
+            "moe_draft_route_ffn: shared_gate output is required with w_shared_gate");
+    smoe_status st = check_hek(H, E, k);
+    if (st != SMOE_OK) return st;
+    REQUIRE(I > 0 && I % 128 == 0, SMOE_ERR_SHAPE,
+            "moe_draft_route_ffn: I=%d must be a positive multiple of 128", I);
+    REQUIRE(group_size == 128, SMOE_ERR_UNSUPPORTED,
+            "moe_draft_route_ffn: group_size=%d (only 128 is supported)", group_size);
+    REQUIRE(smoe::w4a16_shape_supported(H, I), SMOE_ERR_SHAPE,
+            "moe_draft_route_ffn: H=%d, I=%d (each must be <= 16384)", H, I);
+    REQUIRE(smoe::draft_route_ffn_supported(E, k), SMOE_ERR_SHAPE,
+            "moe_draft_route_ffn: k=%d exceeds 32", k);
+    REQUIRE(!counters || (L >= 1 && layer >= 0 && layer < L), SMOE_ERR_SHAPE,
+            "moe_draft_route_ffn: layer=%d must be in [0, L=%d)", layer, L);
+    REQUIRE(aligned(x, 16) && aligned(w_router, 16) && aligned(w_shared_gate, 16),
+            SMOE_ERR_SHAPE,
+            "moe_draft_route_ffn: x, w_router, w_shared_gate must be 16-byte aligned");
+    const size_t need = smoe::w4a16_workspace_bytes(1, k, H, I, E);
+    REQUIRE(workspace && workspace_bytes >= need && aligned(workspace, 256), SMOE_ERR_WORKSPACE,
+            "moe_draft_route_ffn: workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+            workspace_bytes);
+    CHECK_DEVICE();
+    return hip_result(
+        smoe::launch_draft_route_ffn(x, w_router, w_shared_gate, H, E, k, renormalize ? 1 : 0,
+                                     counters ? counters + (size_t)layer * E : nullptr, topk_ids,
+                                     topk_w, shared_gate, expert_offsets, sorted_token,
+                                     sorted_pair, pair_pos, active, n_active, experts, I,
+                                     y_sorted, workspace, err_word,
+                                     static_cast<hipStream_t>(stream)),
+        "moe_draft_route_ffn launch");
+}
+
 smoe_status verify_grouped_gemm(const uint16_t* x, const int32_t* sorted_token,
                                 const int32_t* expert_offsets, const int32_t* active,
                                 const int32_t* n_active, const smoe_f16_expert* experts,

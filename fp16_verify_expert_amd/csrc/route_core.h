@@ -8,16 +8,17 @@
 // rounds (distance 32 .. 1).  Contraction is switched off for every file that
 // includes this header: a fused multiply-add would give the same value (the
 // products are exact), but the compiler must not fold two products into one
-// dot instruction with a different rounding sequence.
+// dot instruction with a different rounding sequence.  The pragma sits in
+// each function so every file that includes this header compiles these
+// routines the same way.
 #pragma once
 
 #include "common.h"
 
-#pragma clang fp contract(off)
-
 namespace smoe_route {
 
 SMOE_DEV float acc_chunk(float s, uint4 xv, uint4 wv) {
+#pragma clang fp contract(off)
     const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
     const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
@@ -41,6 +42,7 @@ SMOE_DEV float acc_chunk(float s, uint4 xv, uint4 wv) {
 // first requests up to 8 of its chunks, then adds them in increasing order.
 SMOE_DEV float pinned_dot(const uint4* __restrict__ xr, const uint4* __restrict__ wrow, int nch,
                           int lane) {
+#pragma clang fp contract(off)
     float s = 0.0f;
     for (int c0 = 0; c0 < nch; c0 += 64 * 8) {
         uint4 xv[8], wv[8];
@@ -75,6 +77,7 @@ template <int D, int CPL>
 SMOE_DEV void wave_logits_batched(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
                                   const uint16_t* __restrict__ wsg, int H, int E, int nvec,
                                   int first, int n_items, int stride, float* out, int lane) {
+#pragma clang fp contract(off)
     const int nch = H >> 3;
     for (int i = first; i < n_items;) {
         const int t = i / nvec;
@@ -193,6 +196,7 @@ SMOE_DEV void count_ranks(const uint64_t (&key)[4], int E, int (&rank)[4]) {
 SMOE_DEV void topk_softmax_wave(const float* lg, int E, int k, int renorm, bool has_gate,
                                 int lane, int32_t* ids, float* wout, float* gate,
                                 int32_t* ids_copy) {
+#pragma clang fp contract(off)
     float v[4];
     uint64_t key[4];
     int rank[4];

@@ -41,6 +41,7 @@
 // The slots' partial sums are added in a fixed order through LDS: the output
 // is deterministic and no floating-point atomics are used.
 #include "common.h"
+#include "route_core.h"
 
 namespace {
 
@@ -64,6 +65,14 @@ constexpr int kRowsPerGroup = 16;     // packed rows (8 K each) per 128-K group
 constexpr int kMaxWaves = SMOE_W4_MAX_WAVES;  // waves per workgroup (upper bound)
 constexpr int kLdsBytes = 32 * 1024;  // activation staging budget per workgroup
 
+// Down-projection matrix of one slot's expert, written by the gate/up launch
+// of a one-token step for the down launch (e = -1: the slot has no expert).
+struct SlotDesc {
+    int32_t e, pad;
+    smoe_w4_mat w2;
+};
+static_assert(sizeof(SlotDesc) == 32, "SlotDesc layout");
+
 struct W4Args {
     const uint16_t* xin;          // phase 1: x [T, H]; phase 2: h [rows, I]
     const int32_t* sorted_token;  // phase 1 only
@@ -79,6 +88,8 @@ struct W4Args {
     int XR;     // activation rows held in LDS
     int direct; // 1: all T token rows of x staged up front (gate/up projection)
     int T;      // token rows of x
+    int E;      // experts in the table
+    SlotDesc* desc;  // one-token steps: per-slot down-projection matrices
     uint16_t* out;  // phase 1: h [rows, I]; phase 2: y [rows, H]
     int32_t* err;
 };
@@ -180,7 +191,22 @@ struct W4Src {
 constexpr int kBufWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 family
 constexpr int kAuxNT = 2;              // non-temporal (streamed once)
 
-__device__ __forceinline__ W4Src make_src(const smoe_w4_mat& m, int K, int N) {
+// A workgroup-uniform pointer as scalar registers (the matrix of one expert
+// is the same for every lane), so its buffer resource needs no per-lane
+// handling.
+template <typename T>
+SMOE_DEV T* uniform_ptr(T* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ W4Src make_src(const smoe_w4_mat& mm, int K, int N) {
+    smoe_w4_mat m;
+    m.qweight = uniform_ptr(mm.qweight);
+    m.scales = uniform_ptr(mm.scales);
+    m.qzeros = uniform_ptr(mm.qzeros);
     W4Src s;
     s.q = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(m.qweight), (short)0,
                                             (K >> 3) * N * 4, kBufWord3);
@@ -189,29 +215,31 @@ __device__ __forceinline__ W4Src make_src(const smoe_w4_mat& m, int K, int N) {
     return s;
 }
 
+// Every load is unconditional (a column past N reads column 0; its sums are
+// never stored), so the loads in flight are a static count and the waits the
+// compiler places for older loads (the activation row) leave them in flight.
 __device__ __forceinline__ void load_group(GroupLoad& L, const W4Src& src, int g, int col,
                                            bool colok) {
     const int N = src.N;
-    const int voff = ((g * kRowsPerGroup) * N + col) * 4;
+    const int c = colok ? col : 0;
+    const int voff = ((g * kRowsPerGroup) * N + c) * 4;
 #pragma unroll
     for (int i = 0; i < kRowsPerGroup; ++i)
-        L.w[i] = colok ? __builtin_amdgcn_raw_buffer_load_b128(src.q, voff, i * N * 4, kAuxNT)
-                       : u4_t{0, 0, 0, 0};
-    if (colok) {
-        const uint64_t sv =
-            *as_global(reinterpret_cast<const uint64_t*>(src.m.scales + (size_t)g * N + col));
-        L.s = make_uint2((uint32_t)sv, (uint32_t)(sv >> 32));
-        L.z = (uint32_t)*as_global(src.m.qzeros + (size_t)g * (N >> 3) + (col >> 3)) >> (4 * (col & 7));
-    } else {
-        L.s = make_uint2(0, 0);
-        L.z = 0;
-    }
+        L.w[i] = __builtin_amdgcn_raw_buffer_load_b128(src.q, voff, i * N * 4, kAuxNT);
+    const uint64_t sv =
+        *as_global(reinterpret_cast<const uint64_t*>(src.m.scales + (size_t)g * N + c));
+    L.s = make_uint2((uint32_t)sv, (uint32_t)(sv >> 32));
+    // the word holding this lane's 4 zeros (shifted when the group is
+    // consumed, so that issuing the loads waits for none of them)
+    L.z = (uint32_t)*as_global(src.m.qzeros + (size_t)g * (N >> 3) + (c >> 3));
 }
 
 template <int MAXM>
 __device__ __forceinline__ void group_step(const GroupLoad& L, const uint4* xs, const float2* sums,
                                            const int (&xrow)[MAXM], int g, int K8, int G, int M,
-                                           uint32_t mlo, uint32_t mhi, float (&acc)[MAXM][4]) {
+                                           int zsh, uint32_t mlo, uint32_t mhi,
+                                           float (&acc)[MAXM][4]) {
+    const uint32_t zw = L.z >> zsh;
     int xoff[MAXM], soff[MAXM];
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) {
@@ -219,13 +247,13 @@ __device__ __forceinline__ void group_step(const GroupLoad& L, const uint4* xs, 
         soff[m] = xrow[m] * G + g;
     }
     if (MAXM == 1) {
-        group_dot<1, MAXM>(L.w, xs, sums, xoff, soff, L.s, L.z, mlo, mhi, acc);
+        group_dot<1, MAXM>(L.w, xs, sums, xoff, soff, L.s, zw, mlo, mhi, acc);
     } else {
         switch (M) {
-            case 1: group_dot<1, MAXM>(L.w, xs, sums, xoff, soff, L.s, L.z, mlo, mhi, acc); break;
-            case 2: group_dot<(MAXM >= 2 ? 2 : 1), MAXM>(L.w, xs, sums, xoff, soff, L.s, L.z, mlo, mhi, acc); break;
-            case 3: group_dot<(MAXM >= 3 ? 3 : 1), MAXM>(L.w, xs, sums, xoff, soff, L.s, L.z, mlo, mhi, acc); break;
-            default: group_dot<MAXM, MAXM>(L.w, xs, sums, xoff, soff, L.s, L.z, mlo, mhi, acc); break;
+            case 1: group_dot<1, MAXM>(L.w, xs, sums, xoff, soff, L.s, zw, mlo, mhi, acc); break;
+            case 2: group_dot<(MAXM >= 2 ? 2 : 1), MAXM>(L.w, xs, sums, xoff, soff, L.s, zw, mlo, mhi, acc); break;
+            case 3: group_dot<(MAXM >= 3 ? 3 : 1), MAXM>(L.w, xs, sums, xoff, soff, L.s, zw, mlo, mhi, acc); break;
+            default: group_dot<MAXM, MAXM>(L.w, xs, sums, xoff, soff, L.s, zw, mlo, mhi, acc); break;
         }
     }
 }
@@ -323,7 +351,7 @@ __device__ __forceinline__ void run_groups(GroupLoad& cur, int g, int nslots, in
         const int gn = g + nslots;
         GroupLoad nxt;
         if (kPrefetch && gn < G) load_group(nxt, src, gn, col, colok);
-        group_step<MAXM>(cur, xs, sums, xrow, g, K8, G, M, mlo, mhi, acc);
+        group_step<MAXM>(cur, xs, sums, xrow, g, K8, G, M, 4 * (col & 7), mlo, mhi, acc);
         if (gn >= G) break;
         if (!kPrefetch) load_group(nxt, src, gn, col, colok);
         cur = nxt;
@@ -332,8 +360,178 @@ __device__ __forceinline__ void run_groups(GroupLoad& cur, int g, int nslots, in
 }
 
 constexpr int kRowChunksPerThread = 8;  // activation chunks per thread requested early
+constexpr int kSpecTable = 64;          // experts whose descriptors are read speculatively
 
-template <int PHASE, int LPR, int MAXM>
+SMOE_DEV const void* bcast_ptr(const void* p, int src_lane) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src_lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src_lane);
+    return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+}
+
+// The projection's matrix descriptor of every expert, one per lane, requested
+// before the active list is read (tables of at most kSpecTable experts), so
+// that the expert's weights are requested one memory round trip after the
+// launch instead of two.
+SMOE_DEV smoe_w4_expert spec_table(const W4Args& a, int lane) {
+    smoe_w4_expert m{{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}};
+    if (a.E <= kSpecTable && lane < a.E) m = a.experts[lane];
+    return m;
+}
+
+template <int PHASE>
+SMOE_DEV smoe_w4_mat pick_mat(const W4Args& a, const smoe_w4_expert& spec, int e) {
+    if (a.E > kSpecTable) {
+        // larger tables: the entry itself, through the scalar cache (the
+        // table is read-only here), so no vector-load wait is involved
+        using cptr = const __attribute__((address_space(4))) smoe_w4_expert*;
+        const cptr t = (cptr)a.experts;
+        return (PHASE == 1) ? t[e].w13 : t[e].w2;
+    }
+    const smoe_w4_mat& sm = (PHASE == 1) ? spec.w13 : spec.w2;
+    smoe_w4_mat m;
+    m.qweight = static_cast<const int32_t*>(bcast_ptr(sm.qweight, e));
+    m.scales = static_cast<const uint16_t*>(bcast_ptr(sm.scales, e));
+    m.qzeros = static_cast<const int32_t*>(bcast_ptr(sm.qzeros, e));
+    return m;
+}
+
+// The gate/up launch of a one-token step hands each slot's expert and its
+// down-projection matrix to the down launch, which thus reads them from a
+// recently written line instead of the expert table.
+SMOE_DEV void write_slot_desc(const W4Args& a, const smoe_w4_expert& spec, int slot, int e) {
+    smoe_w4_mat w2{nullptr, nullptr, nullptr};
+    if (e >= 0) w2 = pick_mat<2>(a, spec, e);
+    if (threadIdx.x == 0) {
+        SlotDesc d;
+        d.e = e;
+        d.pad = 0;
+        d.w2 = w2;
+        a.desc[slot] = d;
+    }
+}
+
+// LDS layout of a workgroup: the activation rows as dot2 pairs, their group
+// sums, then the slots' partial sums.
+struct W4Lds {
+    uint4* xs;     // [XR][K8]
+    float2* sums;  // [XR][G]
+    float* red;    // [nslots][MAXM][NB]
+};
+
+SMOE_DEV W4Lds carve_lds(uint4* smem, const W4Args& a) {
+    const int K8 = a.K >> 3, G = a.K >> 7;
+    W4Lds l;
+    l.xs = smem;
+    l.sums = reinterpret_cast<float2*>(smem + (size_t)a.XR * K8);
+    l.red = reinterpret_cast<float*>(l.sums + (size_t)a.XR * G);
+    return l;
+}
+
+// First weight column of a lane: in the gate/up projection lanes q < LPR/2
+// take gate columns and the others the matching up columns.
+template <int PHASE, int LPR>
+SMOE_DEV int lane_column(const W4Args& a, int cb, int q) {
+    constexpr int NB = 4 * LPR;
+    if (PHASE == 1)
+        return (q < LPR / 2) ? cb * (NB / 2) + 4 * q : a.I + cb * (NB / 2) + 4 * (q - LPR / 2);
+    return cb * NB + 4 * q;
+}
+
+// Group g of a one-token slot (g >= G: a slot past the reduction, whose loads
+// read group G - 1 and whose contribution is dropped).
+SMOE_DEV int clamp_group(int g, int G) { return g < G ? g : G - 1; }
+
+SMOE_DEV void step_if(const GroupLoad& L, const W4Lds& l, int g, int G, int K8, int zsh,
+                      uint32_t mlo, uint32_t mhi, float (&acc)[1][4]) {
+    float t[1][4] = {{0.0f, 0.0f, 0.0f, 0.0f}};
+    const int xrow[1] = {0};
+    group_step<1>(L, l.xs, l.sums, xrow, clamp_group(g, G), K8, G, 1, zsh, mlo, mhi, t);
+    const bool valid = g < G;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[0][c] += valid ? t[0][c] : 0.0f;
+}
+
+// One activation row (T = 1) against the column block cb of matrix wm; each
+// slot takes groups myslot + j * nslots, j < NG.  xv holds the row's chunks,
+// requested by the caller.  The slot's groups go through two register
+// buffers in straight-line code: the first two are requested before the row
+// is permuted into LDS, and buffer A is refilled as soon as it has been
+// consumed, so every wait is for one group while the next is in flight.
+template <int PHASE, int LPR, int NG>
+SMOE_DEV void one_token_block(const W4Args& a, const W4Lds& l, const smoe_w4_mat& wm,
+                              const uint4 (&xv)[kRowChunksPerThread], int slot, int cb) {
+    static_assert(NG >= 1 && NG <= 4, "groups per slot");
+    constexpr int RPL = 64 / LPR;
+    constexpr int NB = 4 * LPR;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int nslots = (int)(blockDim.x >> 6) * RPL;
+    const int myslot = (tid >> 6) * RPL + lane / LPR;
+    const int q = lane % LPR;
+    const int K = a.K, N = a.N;
+    const int G = K >> 7;
+    const int K8 = K >> 3;
+    const int col = lane_column<PHASE, LPR>(a, cb, q);
+    const bool colok = col < N;
+    const int zsh = 4 * (col & 7);
+    const uint32_t mlo = vgpr_const_lo();
+    const uint32_t mhi = vgpr_const_hi();
+    if (!wm.qweight || !wm.scales || !wm.qzeros) {
+        if (tid == 0 && cb == 0) flag_error(a.err, SMOE_DERR_NULL_EXPERT);
+        return;
+    }
+    const W4Src src = make_src(wm, K, N);
+    const int g0 = myslot;
+    GroupLoad A, B;
+    load_group(A, src, clamp_group(g0, G), col, colok);
+    if (NG >= 2) load_group(B, src, clamp_group(g0 + nslots, G), col, colok);
+    __builtin_amdgcn_sched_barrier(0);  // every request above is issued before the row is staged
+    // straight-line stores (indexes past the row rewrite its last chunk with
+    // the same value), so the wait for the row leaves the weights in flight;
+    // the launch guarantees kRowChunksPerThread * blockDim >= K8
+#pragma unroll
+    for (int u = 0; u < kRowChunksPerThread; ++u) {
+        const int idx = tid + u * (int)blockDim.x;
+        l.xs[idx < K8 ? idx : K8 - 1] = pair_permute(xv[u]);
+    }
+    __syncthreads();
+    for (int gg = tid; gg < G; gg += blockDim.x) {
+        const uint4* xr = l.xs + gg * kRowsPerGroup;
+        float se = 0.0f, so = 0.0f;
+#pragma unroll 4
+        for (int i = 0; i < kRowsPerGroup; ++i) {
+            const uint4 p = xr[i];
+            const h2_t x04 = as_h2(p.x), x15 = as_h2(p.y), x26 = as_h2(p.z), x37 = as_h2(p.w);
+            se += ((float)x04.x + (float)x04.y) + ((float)x26.x + (float)x26.y);
+            so += ((float)x15.x + (float)x15.y) + ((float)x37.x + (float)x37.y);
+        }
+        l.sums[gg] = make_float2(se, so);
+    }
+    __syncthreads();
+    float acc[1][4] = {{0.0f, 0.0f, 0.0f, 0.0f}};
+    step_if(A, l, g0, G, K8, zsh, mlo, mhi, acc);
+    if (NG >= 3) load_group(A, src, clamp_group(g0 + 2 * nslots, G), col, colok);
+    if (NG >= 2) step_if(B, l, g0 + nslots, G, K8, zsh, mlo, mhi, acc);
+    if (NG >= 4) load_group(B, src, clamp_group(g0 + 3 * nslots, G), col, colok);
+    if (NG >= 3) step_if(A, l, g0 + 2 * nslots, G, K8, zsh, mlo, mhi, acc);
+    if (NG >= 4) step_if(B, l, g0 + 3 * nslots, G, K8, zsh, mlo, mhi, acc);
+    reduce_store<PHASE, 1, NB>(a, l.red, acc, myslot, nslots, q, cb, slot, 1);
+}
+
+// Request the first kRowChunksPerThread chunks of an activation row per
+// thread.  The requests are unconditional (indexes past the row repeat its
+// last chunk) so that the number of loads in flight is static and a later
+// wait for older loads does not also wait for the row.
+SMOE_DEV void request_row(const uint4* row4, int K8, uint4 (&xv)[kRowChunksPerThread]) {
+#pragma unroll
+    for (int u = 0; u < kRowChunksPerThread; ++u) {
+        const int idx = threadIdx.x + u * (int)blockDim.x;
+        xv[u] = row4[idx < K8 ? idx : K8 - 1];
+    }
+}
+
+template <int PHASE, int LPR, int MAXM, int NG>
 __global__ __launch_bounds__(64 * kMaxWaves) void w4_kernel(W4Args a) {
     constexpr int RPL = 64 / LPR;  // lane groups (slots) per wave
     constexpr int NB = 4 * LPR;    // columns per block
@@ -350,21 +548,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void w4_kernel(W4Args a) {
     const int K = a.K, N = a.N;
     const int G = K >> 7;
     const int K8 = K >> 3;
-    uint4* xs = smem;                                                       // [XR][K8]
-    float2* sums = reinterpret_cast<float2*>(smem + (size_t)a.XR * K8);     // [XR][G]
-    float* red = reinterpret_cast<float*>(sums + (size_t)a.XR * G);  // [nslots][MAXM][NB]
+    const W4Lds l = carve_lds(smem, a);
+    uint4* xs = l.xs;
+    float2* sums = l.sums;
+    float* red = l.red;
 
     const int nslots = nwaves * RPL;
     const int myslot = wave * RPL + rho;
-    int col;
-    bool colok;
-    if (PHASE == 1) {
-        col = (q < LPR / 2) ? cb * (NB / 2) + 4 * q : a.I + cb * (NB / 2) + 4 * (q - LPR / 2);
-        colok = true;
-    } else {
-        col = cb * NB + 4 * q;
-        colok = col < N;
-    }
+    const int col = lane_column<PHASE, LPR>(a, cb, q);
+    const bool colok = col < N;
     const uint32_t mlo = vgpr_const_lo();
     const uint32_t mhi = vgpr_const_hi();
 
@@ -375,52 +567,26 @@ __global__ __launch_bounds__(64 * kMaxWaves) void w4_kernel(W4Args a) {
         // are read: x row 0 (gate/up) or h row `slot` (down).  It is
         // requested first, then the expert's first weights; the row is
         // permuted into LDS while both are in flight.
-        const uint16_t* row = (PHASE == 1) ? a.xin : a.xin + (size_t)slot * K;
-        const uint4* row4 = reinterpret_cast<const uint4*>(row);
+        const uint4* row4 =
+            reinterpret_cast<const uint4*>((PHASE == 1) ? a.xin : a.xin + (size_t)slot * K);
         uint4 xv[kRowChunksPerThread];
-#pragma unroll
-        for (int u = 0; u < kRowChunksPerThread; ++u) {
-            const int idx = tid + u * (int)blockDim.x;
-            if (idx < K8) xv[u] = row4[idx];
-        }
-        const int e = a.active[slot];  // -1 past the touched experts
-        if (e < 0) return;
-        const smoe_w4_mat wm = (PHASE == 1) ? a.experts[e].w13 : a.experts[e].w2;
-        if (!wm.qweight || !wm.scales || !wm.qzeros) {
-            if (tid == 0 && cb == 0) flag_error(a.err, SMOE_DERR_NULL_EXPERT);
-            return;
-        }
-        const W4Src src = make_src(wm, K, N);
-        GroupLoad cur;
-        const int g = myslot;
-        if (g < G) load_group(cur, src, g, col, colok);
-#pragma unroll
-        for (int u = 0; u < kRowChunksPerThread; ++u) {
-            const int idx = tid + u * (int)blockDim.x;
-            if (idx < K8) xs[idx] = pair_permute(xv[u]);
-        }
-        // rows longer than the early requests cover (small workgroups)
-        for (int idx = tid + kRowChunksPerThread * (int)blockDim.x; idx < K8; idx += blockDim.x)
-            xs[idx] = pair_permute(row4[idx]);
-        __syncthreads();
-        for (int gg = tid; gg < G; gg += blockDim.x) {
-            const uint4* xr = xs + gg * kRowsPerGroup;
-            float se = 0.0f, so = 0.0f;
-#pragma unroll 4
-            for (int i = 0; i < kRowsPerGroup; ++i) {
-                const uint4 p = xr[i];
-                const h2_t x04 = as_h2(p.x), x15 = as_h2(p.y), x26 = as_h2(p.z), x37 = as_h2(p.w);
-                se += ((float)x04.x + (float)x04.y) + ((float)x26.x + (float)x26.y);
-                so += ((float)x15.x + (float)x15.y) + ((float)x37.x + (float)x37.y);
+        if (PHASE == 1) {
+            const smoe_w4_expert spec = spec_table(a, lane);
+            int e = a.active[slot];  // -1 past the touched experts
+            request_row(row4, K8, xv);
+            if (e >= a.E) {
+                if (tid == 0 && cb == 0) flag_error(a.err, SMOE_DERR_BAD_ID);
+                e = -1;
             }
-            sums[gg] = make_float2(se, so);
+            if (cb == 0) write_slot_desc(a, spec, slot, e);
+            if (e < 0) return;
+            one_token_block<1, LPR, NG>(a, l, pick_mat<1>(a, spec, e), xv, slot, cb);
+        } else {
+            const SlotDesc d = a.desc[slot];
+            request_row(row4, K8, xv);
+            if (d.e < 0) return;
+            one_token_block<2, LPR, NG>(a, l, d.w2, xv, slot, cb);
         }
-        __syncthreads();
-        float acc[1][4] = {{0.0f, 0.0f, 0.0f, 0.0f}};
-        const int xrow[1] = {0};
-        run_groups<SMOE_W4_PREFETCH != 0, 1>(cur, g, nslots, G, src, col, colok, xs, sums, xrow,
-                                             K8, 1, mlo, mhi, acc);
-        reduce_store<PHASE, 1, NB>(a, red, acc, myslot, nslots, q, cb, slot, 1);
         return;
     } else {
         const int e = a.active[slot];  // -1 past the touched experts
@@ -472,10 +638,107 @@ __global__ __launch_bounds__(64 * kMaxWaves) void w4_kernel(W4Args a) {
     }
 }
 
+// --------------------------------------------- routing + gate/up, T = 1 ----
+//
+// The one-token draft step's routing, ELB update and gather maps folded into
+// the gate/up launch (Key Contributions 4 of the pages: routing, gathering and
+// the experts' FFN of a draft step in one fused launch).  Every workgroup
+// evaluates the token's E (+1 shared-gate) router logits with the pinned
+// routines of the routing kernels, so every workgroup reaches the same
+// selection, bit-identical to moe_route_topk / moe_route_plan; slot s then
+// takes the s-th smallest selected id, which is the expert moe_gather places
+// at sorted row s.  Workgroup 0 also writes the routing outputs, the ELB
+// increments and the maps, which the down projection and the combine read
+// after this launch.
+struct RouteArgs {
+    const uint16_t* wr;   // router [E, H]
+    const uint16_t* wsg;  // shared-expert gate row [H] or null
+    int k, renorm;
+    int32_t* counters_row;  // ELB row of the layer or null
+    int32_t* ids;
+    float* w;
+    float* gate;
+    int32_t* off;
+    int32_t* sorted_token;
+    int32_t* sorted_pair;
+    int32_t* pair_pos;
+    int32_t* active;
+    int32_t* n_active;
+};
+
+constexpr int kFusedMaxK = 32;
+
+template <int LPR, int NG>
+__global__ __launch_bounds__(64 * kMaxWaves) void route_w4_kernel(W4Args a, RouteArgs r) {
+    __shared__ float lg_s[257];
+    __shared__ int32_t ids_s[kFusedMaxK];
+    __shared__ float w_s[kFusedMaxK];
+    __shared__ float gate_s;
+    extern __shared__ uint4 smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int nwaves = blockDim.x >> 6;
+    const int cb = blockIdx.x % a.nCB;
+    const int slot = blockIdx.x / a.nCB;
+    const int E = a.E, k = r.k;
+
+    const smoe_w4_expert spec = spec_table(a, lane);
+    const uint4* row4 = reinterpret_cast<const uint4*>(a.xin);
+    uint4 xv[kRowChunksPerThread];
+    request_row(row4, a.K >> 3, xv);
+
+    // 1. router logits, wave w taking vectors w, w + nwaves, ...
+    const int nvec = E + (r.wsg ? 1 : 0);
+    smoe_route::wave_logits(a.xin, r.wr, r.wsg, a.K, E, nvec, wave, nvec, nwaves, lg_s, lane);
+    __syncthreads();
+    // 2. top-k, softmax weights and gate (wave 0)
+    if (wave == 0)
+        smoe_route::topk_softmax_wave(lg_s, E, k, r.renorm, r.wsg != nullptr, lane, ids_s, w_s,
+                                      &gate_s, nullptr);
+    __syncthreads();
+    // 3. sorted position of every selected id (ids of one token are distinct)
+    int e = -1;
+    for (int j = 0; j < k; ++j) {
+        int less = 0;
+        for (int i = 0; i < k; ++i) less += (ids_s[i] < ids_s[j]) ? 1 : 0;
+        if (less == slot) e = ids_s[j];
+    }
+    if (blockIdx.x == 0) {
+        for (int j = tid; j < k; j += blockDim.x) {
+            const int id = ids_s[j];
+            int pos = 0;
+            for (int i = 0; i < k; ++i) pos += (ids_s[i] < id) ? 1 : 0;
+            r.ids[j] = id;
+            r.w[j] = w_s[j];
+            if (r.counters_row) atomicAdd(r.counters_row + id, 1);
+            r.sorted_token[pos] = 0;
+            r.sorted_pair[pos] = j;
+            r.pair_pos[j] = pos;
+            r.active[pos] = id;
+        }
+        for (int ee = tid; ee <= E; ee += blockDim.x) {
+            int c = 0;
+            for (int i = 0; i < k; ++i) c += (ids_s[i] < ee) ? 1 : 0;
+            r.off[ee] = c;
+            if (ee >= k && ee < E) r.active[ee] = -1;
+        }
+        if (tid == 0) {
+            *r.n_active = k;
+            if (r.wsg && r.gate) *r.gate = gate_s;
+        }
+    }
+    // 4. this slot's block of the gate/up projection
+    if (cb == 0) write_slot_desc(a, spec, slot, e);
+    if (e < 0) return;  // not reached: every slot below k has an expert
+    one_token_block<1, LPR, NG>(a, carve_lds(smem, a), pick_mat<1>(a, spec, e), xv, slot, cb);
+}
+
 // ---------------------------------------------------------------- launch ----
 
 struct PhasePlan {
     int lpr, nCB, waves, mch, xr, direct;
+    int ng;  // one-token workgroups: groups per slot (ceil(G / slots per workgroup))
     size_t lds;
 };
 
@@ -500,6 +763,11 @@ PhasePlan plan_phase(int phase, int slots, int T, int K, int N, int I, int maxm)
     // register budget at 4
     const int wmax = (maxm == 1 || kMaxWaves < 4) ? kMaxWaves : 4;
     if (p.waves > wmax) p.waves = wmax;
+    // one-token workgroups request the whole activation row up front
+    if (maxm == 1) {
+        const int need = (K / 8 + 64 * kRowChunksPerThread - 1) / (64 * kRowChunksPerThread);
+        if (p.waves < need) p.waves = need;
+    }
     if (p.waves < 1) p.waves = 1;
     const size_t row_bytes = (size_t)K * 2 + (size_t)G * 8;  // pairs + group sums
     int cap = (int)(kLdsBytes / row_bytes);
@@ -509,16 +777,38 @@ PhasePlan plan_phase(int phase, int slots, int T, int K, int N, int I, int maxm)
     p.xr = p.direct ? T : p.mch;
     const size_t red_bytes = (size_t)p.waves * rpl * maxm * NB * 4;
     p.lds = (size_t)p.xr * row_bytes + red_bytes;
+    p.ng = (G + p.waves * rpl - 1) / (p.waves * rpl);
     return p;
+}
+
+template <int PHASE, int LPR, int NG>
+hipError_t launch_one_token(const W4Args& a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+    hipLaunchKernelGGL((w4_kernel<PHASE, LPR, 1, NG>), grid, block, lds, s, a);
+    return hipGetLastError();
+}
+
+template <int PHASE, int LPR>
+hipError_t launch_one_token_ng(const W4Args& a, dim3 grid, dim3 block, const PhasePlan& p,
+                               hipStream_t s) {
+    switch (p.ng) {
+        case 1: return launch_one_token<PHASE, LPR, 1>(a, grid, block, p.lds, s);
+        case 2: return launch_one_token<PHASE, LPR, 2>(a, grid, block, p.lds, s);
+        case 3: return launch_one_token<PHASE, LPR, 3>(a, grid, block, p.lds, s);
+        case 4: return launch_one_token<PHASE, LPR, 4>(a, grid, block, p.lds, s);
+        default: return hipErrorInvalidValue;  // excluded by w4a16_shape_supported
+    }
 }
 
 template <int PHASE, int MAXM>
 hipError_t launch_phase(const W4Args& a, int slots, const PhasePlan& p, hipStream_t s) {
     const dim3 grid(slots * p.nCB), block(64 * p.waves);
+    if (MAXM == 1)
+        return (p.lpr == 16) ? launch_one_token_ng<PHASE, 16>(a, grid, block, p, s)
+                             : launch_one_token_ng<PHASE, 8>(a, grid, block, p, s);
     if (p.lpr == 16)
-        hipLaunchKernelGGL((w4_kernel<PHASE, 16, MAXM>), grid, block, p.lds, s, a);
+        hipLaunchKernelGGL((w4_kernel<PHASE, 16, MAXM, 1>), grid, block, p.lds, s, a);
     else
-        hipLaunchKernelGGL((w4_kernel<PHASE, 8, MAXM>), grid, block, p.lds, s, a);
+        hipLaunchKernelGGL((w4_kernel<PHASE, 8, MAXM, 1>), grid, block, p.lds, s, a);
     return hipGetLastError();
 }
 
@@ -531,13 +821,49 @@ hipError_t launch_any(const W4Args& a, int slots, const PhasePlan& p, int maxm, 
 }  // namespace
 
 namespace smoe {
-size_t w4a16_workspace_bytes(int T, int k, int /*H*/, int I, int /*E*/) {
-    return ((size_t)T * k * I * 2 + 255) & ~(size_t)255;  // h [T*k, I] fp16
+// h [T*k, I] fp16, then (one-token steps) a SlotDesc per slot
+static size_t h_bytes(int T, int k, int I) { return ((size_t)T * k * I * 2 + 255) & ~(size_t)255; }
+
+size_t w4a16_workspace_bytes(int T, int k, int /*H*/, int I, int E) {
+    const int slots = E < T * k ? E : T * k;
+    return h_bytes(T, k, I) + (((size_t)slots * sizeof(SlotDesc) + 255) & ~(size_t)255);
 }
 
 bool w4a16_shape_supported(int H, int I) {
-    return (size_t)H * 2 <= (size_t)kLdsBytes && (size_t)I * 2 <= (size_t)kLdsBytes;
+    // activation rows staged in LDS; one-token workgroups request a whole row
+    // with kRowChunksPerThread chunks per thread
+    const int row_cap = 8 * 64 * kRowChunksPerThread * kMaxWaves;
+    return (size_t)H * 2 <= (size_t)kLdsBytes && (size_t)I * 2 <= (size_t)kLdsBytes &&
+           H <= row_cap && I <= row_cap;
 }
+
+namespace {
+W4Args phase_args(const PhasePlan& p, const uint16_t* xin, const int32_t* sorted_token,
+                  const int32_t* off, const int32_t* active, const int32_t* n_active,
+                  const smoe_w4_expert* experts, int K, int N, int I, int T, int E,
+                  uint16_t* out, int32_t* err, SlotDesc* desc) {
+    W4Args a{};
+    a.desc = desc;
+    a.xin = xin;
+    a.sorted_token = sorted_token;
+    a.off = off;
+    a.active = active;
+    a.n_active = n_active;
+    a.experts = experts;
+    a.K = K;
+    a.N = N;
+    a.I = I;
+    a.nCB = p.nCB;
+    a.MCH = p.mch;
+    a.XR = p.xr;
+    a.direct = p.direct;
+    a.T = T;
+    a.E = E;
+    a.out = out;
+    a.err = err;
+    return a;
+}
+}  // namespace
 
 hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, const int32_t* off,
                             const int32_t* active, const int32_t* n_active,
@@ -547,37 +873,52 @@ hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, cons
     const int slots = E < rows ? E : rows;
     const int maxm = (T == 1) ? 1 : 4;  // an expert holds at most T rows
     uint16_t* h = static_cast<uint16_t*>(ws);
+    SlotDesc* desc = reinterpret_cast<SlotDesc*>(static_cast<char*>(ws) + h_bytes(T, k, I));
     const PhasePlan p1 = plan_phase(1, slots, T, H, 2 * I, I, maxm);
-    W4Args a1{};
-    a1.xin = x;
-    a1.sorted_token = sorted_token;
-    a1.off = off;
-    a1.active = active;
-    a1.n_active = n_active;
-    a1.experts = experts;
-    a1.K = H;
-    a1.N = 2 * I;
-    a1.I = I;
-    a1.nCB = p1.nCB;
-    a1.MCH = p1.mch;
-    a1.XR = p1.xr;
-    a1.direct = p1.direct;
-    a1.T = T;
-    a1.out = h;
-    a1.err = err;
+    const W4Args a1 = phase_args(p1, x, sorted_token, off, active, n_active, experts, H, 2 * I, I,
+                                 T, E, h, err, desc);
     hipError_t st = launch_any<1>(a1, slots, p1, maxm, s);
     if (st != hipSuccess) return st;
     const PhasePlan p2 = plan_phase(2, slots, T, I, H, I, maxm);
-    W4Args a2 = a1;
-    a2.xin = h;
-    a2.sorted_token = nullptr;
-    a2.K = I;
-    a2.N = H;
-    a2.nCB = p2.nCB;
-    a2.MCH = p2.mch;
-    a2.XR = p2.xr;
-    a2.direct = 0;
-    a2.out = y;
+    const W4Args a2 =
+        phase_args(p2, h, nullptr, off, active, n_active, experts, I, H, I, T, E, y, err, desc);
     return launch_any<2>(a2, slots, p2, maxm, s);
+}
+
+bool draft_route_ffn_supported(int E, int k) { return E <= 256 && k <= kFusedMaxK; }
+
+hipError_t launch_draft_route_ffn(const uint16_t* x, const uint16_t* wr, const uint16_t* wsg,
+                                  int H, int E, int k, int renorm, int32_t* counters_row,
+                                  int32_t* ids, float* w, float* gate, int32_t* off, int32_t* st,
+                                  int32_t* sp, int32_t* pp, int32_t* active, int32_t* n_active,
+                                  const smoe_w4_expert* experts, int I, uint16_t* y, void* ws,
+                                  int32_t* err, hipStream_t s) {
+    uint16_t* h = static_cast<uint16_t*>(ws);
+    SlotDesc* desc = reinterpret_cast<SlotDesc*>(static_cast<char*>(ws) + h_bytes(1, k, I));
+    const PhasePlan p1 = plan_phase(1, k, 1, H, 2 * I, I, 1);
+    const W4Args a1 = phase_args(p1, x, st, off, active, n_active, experts, H, 2 * I, I, 1, E, h,
+                                 err, desc);
+    RouteArgs r{wr, wsg, k, renorm, counters_row, ids, w, gate, off, st, sp, pp, active, n_active};
+    const dim3 grid(k * p1.nCB), block(64 * p1.waves);
+#define SMOE_ROUTE_W4(L, NG) hipLaunchKernelGGL((route_w4_kernel<L, NG>), grid, block, p1.lds, s, a1, r)
+    if (p1.ng < 1 || p1.ng > 4) return hipErrorInvalidValue;  // excluded by the shape checks
+    if (p1.lpr == 16) {
+        if (p1.ng == 1) SMOE_ROUTE_W4(16, 1);
+        else if (p1.ng == 2) SMOE_ROUTE_W4(16, 2);
+        else if (p1.ng == 3) SMOE_ROUTE_W4(16, 3);
+        else SMOE_ROUTE_W4(16, 4);
+    } else {
+        if (p1.ng == 1) SMOE_ROUTE_W4(8, 1);
+        else if (p1.ng == 2) SMOE_ROUTE_W4(8, 2);
+        else if (p1.ng == 3) SMOE_ROUTE_W4(8, 3);
+        else SMOE_ROUTE_W4(8, 4);
+    }
+#undef SMOE_ROUTE_W4
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const PhasePlan p2 = plan_phase(2, k, 1, I, H, I, 1);
+    const W4Args a2 = phase_args(p2, h, nullptr, off, active, n_active, experts, I, H, I, 1, E, y,
+                                 err, desc);
+    return launch_any<2>(a2, k, p2, 1, s);
 }
 }  // namespace smoe

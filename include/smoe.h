@@ -214,6 +214,37 @@ smoe_status w4a16_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
                               void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_draft_route_ffn -- one-token (T = 1) draft step of a layer: the work
+ * of moe_route_plan followed by w4a16_grouped_ffn, in two launches instead of
+ * three ([S1] Key Contributions 4: routing, gathering and the experts' FFN of
+ * a draft step inside one fused launch; the routing is folded into the
+ * gate/up projection, whose every workgroup evaluates the router itself).
+ *
+ * Arguments keep the meaning and layout of those two calls with T = 1:
+ *   x              fp16 [1, H]
+ *   w_router, w_shared_gate, renormalize, layer, L, counters: moe_route_plan
+ *                  (counters may be NULL: no ELB update)
+ *   experts, group_size (128), I: w4a16_grouped_ffn
+ *   topk_ids [k], topk_w [k], shared_gate [1], expert_offsets [E+1],
+ *   sorted_token [k], sorted_pair [k], pair_pos [k], active [E],
+ *   n_active [1]   out: bit-identical to moe_route_plan's
+ *   y_sorted       fp16 [k, H] out: bit-identical to w4a16_grouped_ffn's
+ *   workspace      >= smoe_workspace_bytes(0, 1, k, H, I, E) bytes,
+ *                  256-byte aligned
+ * Limits: k <= 32, E <= 256, H and I at most 16384 (SMOE_ERR_SHAPE beyond).
+ * The caller owns every buffer; nothing is allocated.
+ * ---------------------------------------------------------------------- */
+smoe_status moe_draft_route_ffn(const uint16_t* x, const uint16_t* w_router,
+                                const uint16_t* w_shared_gate, int H, int I, int E, int k,
+                                int renormalize, int layer, int L, int32_t* counters,
+                                const smoe_w4_expert* experts, int group_size,
+                                int32_t* topk_ids, float* topk_w, float* shared_gate,
+                                int32_t* expert_offsets, int32_t* sorted_token,
+                                int32_t* sorted_pair, int32_t* pair_pos, int32_t* active,
+                                int32_t* n_active, uint16_t* y_sorted, void* workspace,
+                                size_t workspace_bytes, int32_t* err_word, void* stream);
+
+/* ------------------------------------------------------------------------
  * verify_grouped_gemm -- FP16 SwiGLU FFN of the target experts over the
  * rows grouped by expert: expert-wise verification regrouping ([S1] Key
  * Contributions 4 and Methodology: the tokens routed to one expert are packed

@@ -18,7 +18,8 @@ FAKE = V(0x1000)  # never dereferenced: the checks below fail before any use
 def test_exports_every_header_function():
     names = fve.header_functions()
     expected = {"smoe_abi_version", "smoe_last_error", "moe_route_topk", "elb_count",
-                "moe_gather", "moe_route_plan", "w4a16_grouped_ffn", "verify_grouped_gemm", "moe_combine",
+                "moe_gather", "moe_route_plan", "w4a16_grouped_ffn", "moe_draft_route_ffn",
+                "verify_grouped_gemm", "moe_combine",
                 "expert_stage_async", "smoe_workspace_bytes"}
     assert set(names) == expected
     L = ctypes.CDLL(fve.LIB_PATH)
@@ -85,6 +86,34 @@ def test_route_plan_validation():
     assert call(layer=1, Lc=1) == 2                 # layer outside [0, L)
     assert call(x=V(0x1002)) == 2 and "aligned" in _err()
     assert call(T=-1) == 2
+
+
+def test_draft_route_ffn_validation():
+    L = fve.lib()
+    maps = [FAKE] * 6   # offsets, sorted_token, sorted_pair, pair_pos, active, n_active
+    need = L.smoe_workspace_bytes(0, 1, 2, 256, 512, 8)
+    assert need > 0
+
+    def call(x=FAKE, wr=FAKE, wsg=None, H=256, I=512, E=8, k=2, layer=0, Lc=1, counters=FAKE,
+             table=FAKE, gs=128, gate=None, mp=None, y=FAKE, ws=FAKE, wsb=None):
+        m = maps if mp is None else mp
+        return L.moe_draft_route_ffn(x, wr, wsg, H, I, E, k, 0, layer, Lc, counters, table, gs,
+                                     FAKE, FAKE, gate, *m, y, ws, need if wsb is None else wsb,
+                                     None, None)
+    assert call(x=None) == 1
+    assert call(table=None) == 1
+    assert call(y=None) == 1
+    assert call(wsg=FAKE) == 1                      # gate output missing
+    assert call(mp=maps[:4] + [None, FAKE]) == 1    # active missing
+    assert call(H=200) == 2
+    assert call(I=500) == 2
+    assert call(k=9) == 2
+    assert call(E=64, k=33) == 2 and "32" in _err()
+    assert call(gs=64) == 3
+    assert call(layer=1, Lc=1) == 2                 # layer outside [0, L)
+    assert call(x=V(0x1002)) == 2 and "aligned" in _err()
+    assert call(wsb=need - 1) == 6
+    assert call(ws=None) == 6
 
 
 def test_w4a16_validation():

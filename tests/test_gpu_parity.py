@@ -2,6 +2,8 @@
 same seeded inputs.  Integer outputs (ids, counters, maps) must match exactly;
 FP16 outputs within normalised L2 5e-3 and max |err| 2e-2; routing weights
 within 1e-5 relative."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -269,6 +271,83 @@ def test_w4a16_grouped_ffn(shape, T):
     y2 = fve.w4a16_grouped_ffn(dx, gm, L.t4, T, shape.k, shape.H, shape.I, shape.E, ws,
                                err_word=err)
     assert torch.equal(y[:rows], y2[:rows])
+
+
+# One-token draft step with the routing folded into the gate/up launch.
+_WIDE = dataclasses.replace(synth.TINY, name="tiny_e128_k5", E=128, k=5)   # > 64 experts
+_ALL = dataclasses.replace(synth.TINY, name="tiny_k_eq_e", k=8)            # every expert
+_RENORM = dataclasses.replace(synth.TINY, name="tiny_renorm_k3", k=3, renormalize=True)
+DRAFT_FUSED_CASES = [(synth.TINY, 0), (synth.TINY, 7), (synth.DS, 0), (synth.DS, 3),
+                     (synth.QWEN, 0), (synth.PHI, 0), (synth.PHI, 5), (_WIDE, 0), (_ALL, 0),
+                     (_RENORM, 2)]
+
+
+@pytest.mark.parametrize("shape,step", DRAFT_FUSED_CASES,
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_draft_route_ffn_matches_separate_calls(shape, step):
+    """moe_draft_route_ffn equals moe_route_plan + w4a16_grouped_ffn bit for
+    bit (ids, weights, gate, ELB row, maps, y_sorted), and the oracle."""
+    say(f"draft route+ffn {shape.name} step={step}")
+    E, k = shape.E, shape.k
+    x = synth.tokens(shape, 1, step=step)
+    L = _layer(shape, (1,), steps=(step,), f16=False)
+    dx = dev(x)
+    c0 = np.random.default_rng(step).integers(0, 50, size=(3, E)).astype(np.int32)
+    counters, counters2 = dev(c0), dev(c0)
+    err = _err()
+    ws = fve.new_workspace(0, 1, k, shape.H, shape.I, E)
+    ids, w, gate, m, y = fve.moe_draft_route_ffn(dx, L.d_router, k, L.t4, shape.I, ws,
+                                                 shape.renormalize, L.d_gate,
+                                                 counters=counters, layer=2, err_word=err)
+    ids2, w2, gate2, m2 = fve.moe_route_plan(dx, L.d_router, k, shape.renormalize, L.d_gate,
+                                             counters=counters2, layer=2)
+    ws2 = fve.new_workspace(0, 1, k, shape.H, shape.I, E)
+    y2 = fve.w4a16_grouped_ffn(dx, m2, L.t4, 1, k, shape.H, shape.I, E, ws2)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) == 0
+    assert torch.equal(ids, ids2)
+    assert torch.equal(w, w2)
+    if L.d_gate is not None:
+        assert torch.equal(gate, gate2)
+    assert torch.equal(counters, counters2)
+    for key in ("offsets", "active", "n_active"):
+        assert torch.equal(m[key], m2[key]), key
+    for key in ("sorted_token", "sorted_pair", "pair_pos"):
+        assert torch.equal(m[key][:k], m2[key][:k]), key
+    assert torch.equal(y[:k], y2[:k])
+    ref = oracle.route_topk(x, L.router, k, shape.renormalize)
+    assert np.array_equal(host(ids), ref["ids"])
+    assert np.allclose(host(w), ref["weights"], rtol=W_RTOL, atol=1e-7)
+    assert np.array_equal(host(counters), oracle.elb_update(c0, ref["ids"], 2))
+    maps = oracle.gather_maps(ref["ids"], E)
+    assert np.array_equal(host(m["offsets"]), maps["offsets"])
+    assert np.array_equal(host(m["sorted_pair"])[:k], maps["sorted_pair"])
+    yref = oracle.grouped_ffn(x, maps, L.int4, "int4")
+    st = assert_fp16_close(host(y)[:k], yref, f"draft route+ffn {shape.name}")
+    say(f"  l2={st['l2']:.2e} maxabs={st['maxabs']:.2e}")
+
+
+def test_draft_route_ffn_nan_logit_and_repeat():
+    """A NaN logit ranks last in the fused routing too; a second call on the
+    same inputs gives the same bits and adds the same ELB increments again."""
+    s = _ALL
+    x = synth.tokens(s, 1, step=4)
+    L = _layer(s, (1,), steps=(4,), f16=False)
+    wr = L.router.copy()
+    wr[5, 0] = np.float16(np.inf)
+    x[:, 0] = 0.0                                     # 0 * inf: expert 5's logit is NaN
+    ws = fve.new_workspace(0, 1, s.k, s.H, s.I, s.E)
+    counters = torch.zeros((1, s.E), dtype=torch.int32, device="cuda")
+    ids, w, _, m, y = fve.moe_draft_route_ffn(dev(x), dev(wr), s.k, L.t4, s.I, ws,
+                                              counters=counters)
+    ref = oracle.route_topk(x, wr, s.k)
+    assert np.array_equal(host(ids), ref["ids"])
+    assert host(ids)[0, -1] == 5
+    y1 = y.clone()
+    fve.moe_draft_route_ffn(dev(x), dev(wr), s.k, L.t4, s.I, ws, counters=counters,
+                            topk_ids=ids, topk_w=w, maps=m, y_sorted=y)
+    assert torch.equal(y, y1)
+    assert host(counters).tolist() == [[2] * s.E]
 
 
 VERIFY_CASES = [(synth.TINY, 17), (synth.TINY, 40), (synth.QWEN, 9), (synth.PHI, 17),
