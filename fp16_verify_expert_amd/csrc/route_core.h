@@ -151,6 +151,27 @@ SMOE_DEV void wave_logits(const uint16_t* __restrict__ x, const uint16_t* __rest
     }
 }
 
+// wave_logits with up to 32 weight chunks per lane in flight (all the items
+// of a wave for a decode step's router at most shapes): one memory round trip
+// instead of one per batch.  Values are identical to wave_logits (same
+// per-item order).
+SMOE_DEV void wave_logits_wide(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                               const uint16_t* __restrict__ wsg, int H, int E, int nvec,
+                               int first, int n_items, int stride, float* out, int lane) {
+    const int cpl = ((H >> 3) + 63) / 64;
+    if (cpl <= 1) {
+        wave_logits_batched<16, 1>(x, wr, wsg, H, E, nvec, first, n_items, stride, out, lane);
+    } else if (cpl <= 2) {
+        wave_logits_batched<16, 2>(x, wr, wsg, H, E, nvec, first, n_items, stride, out, lane);
+    } else if (cpl <= 4) {
+        wave_logits_batched<8, 4>(x, wr, wsg, H, E, nvec, first, n_items, stride, out, lane);
+    } else if (cpl <= 8) {
+        wave_logits_batched<4, 8>(x, wr, wsg, H, E, nvec, first, n_items, stride, out, lane);
+    } else {
+        wave_logits(x, wr, wsg, H, E, nvec, first, n_items, stride, out, lane);
+    }
+}
+
 // Ranking of (logit, expert id) pairs: larger logit first, NaN below every
 // number, equal logits (-0 equal to +0, or two NaNs) lower id first.  As a
 // 64-bit key: the logit's bits mapped to an unsigned order (NaN lowest), then
@@ -193,13 +214,10 @@ SMOE_DEV void count_ranks(const uint64_t (&key)[4], int E, int (&rank)[4]) {
 // l + 64 i; each expert's rank is the number of keys above its own (every
 // key taken from its lane by readlane), and the experts of rank < k are the
 // selection, in rank order.
-SMOE_DEV void topk_softmax_wave(const float* lg, int E, int k, int renorm, bool has_gate,
-                                int lane, int32_t* ids, float* wout, float* gate,
-                                int32_t* ids_copy) {
-#pragma clang fp contract(off)
-    float v[4];
+// Rank of every expert's logit (lane l holds experts l + 64 i): the number
+// of keys above its own.
+SMOE_DEV void rank_experts(const float* lg, int E, int lane, float (&v)[4], int (&rank)[4]) {
     uint64_t key[4];
-    int rank[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = lane + 64 * i;
@@ -217,6 +235,28 @@ SMOE_DEV void topk_softmax_wave(const float* lg, int E, int k, int renorm, bool 
         count_ranks<3>(key, E, rank);
     else
         count_ranks<4>(key, E, rank);
+}
+
+// The top-k ids alone (ids[r] = the expert of rank r < k), as
+// topk_softmax_wave selects them.
+SMOE_DEV void topk_ids_wave(const float* lg, int E, int k, int lane, int32_t* ids) {
+    float v[4];
+    int rank[4];
+    rank_experts(lg, E, lane, v, rank);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E && rank[i] < k) ids[rank[i]] = e;
+    }
+}
+
+SMOE_DEV void topk_softmax_wave(const float* lg, int E, int k, int renorm, bool has_gate,
+                                int lane, int32_t* ids, float* wout, float* gate,
+                                int32_t* ids_copy) {
+#pragma clang fp contract(off)
+    float v[4];
+    int rank[4];
+    rank_experts(lg, E, lane, v, rank);
     // the largest logit: the value of the rank-0 expert, from its lane
     float v0 = 0.0f;
     bool has0 = false;

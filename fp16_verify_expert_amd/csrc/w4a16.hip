@@ -62,7 +62,18 @@ constexpr int kRowsPerGroup = 16;     // packed rows (8 K each) per 128-K group
 #ifndef SMOE_W4_PREFETCH
 #define SMOE_W4_PREFETCH 1
 #endif
+#ifndef SMOE_W4_T1_MAX_WAVES
+#define SMOE_W4_T1_MAX_WAVES 4
+#endif
+#ifndef SMOE_W4_T1_MIN_WG
+#define SMOE_W4_T1_MIN_WG 128
+#endif
 constexpr int kMaxWaves = SMOE_W4_MAX_WAVES;  // waves per workgroup (upper bound)
+// one-token (T = 1) workgroups: up to kT1MaxWaves waves, 64-column blocks
+// when they give at least kT1MinWG workgroups (measured on the decode shapes:
+// wider row runs beat more workgroups down to about half a workgroup per CU)
+constexpr int kT1MaxWaves = SMOE_W4_T1_MAX_WAVES;
+constexpr int kT1MinWG = SMOE_W4_T1_MIN_WG;
 constexpr int kLdsBytes = 32 * 1024;  // activation staging budget per workgroup
 
 // Down-projection matrix of one slot's expert, written by the gate/up launch
@@ -384,9 +395,15 @@ SMOE_DEV smoe_w4_mat pick_mat(const W4Args& a, const smoe_w4_expert& spec, int e
     if (a.E > kSpecTable) {
         // larger tables: the entry itself, through the scalar cache (the
         // table is read-only here), so no vector-load wait is involved
-        using cptr = const __attribute__((address_space(4))) smoe_w4_expert*;
+        using cptr = const __attribute__((address_space(4))) uint64_t*;
+        static_assert(sizeof(smoe_w4_expert) == 6 * sizeof(uint64_t), "expert table layout");
         const cptr t = (cptr)a.experts;
-        return (PHASE == 1) ? t[e].w13 : t[e].w2;
+        const int b = 6 * e + (PHASE == 1 ? 0 : 3);
+        smoe_w4_mat m;
+        m.qweight = reinterpret_cast<const int32_t*>(t[b]);
+        m.scales = reinterpret_cast<const uint16_t*>(t[b + 1]);
+        m.qzeros = reinterpret_cast<const int32_t*>(t[b + 2]);
+        return m;
     }
     const smoe_w4_mat& sm = (PHASE == 1) ? spec.w13 : spec.w2;
     smoe_w4_mat m;
@@ -531,8 +548,14 @@ SMOE_DEV void request_row(const uint4* row4, int K8, uint4 (&xv)[kRowChunksPerTh
     }
 }
 
+// Occupancy of the one-token kernels: four waves per SIMD with one group per
+// slot (at most 128 registers), two with two or more.
+template <int MAXM, int NG>
+constexpr int w4_waves_per_eu() { return (MAXM == 1 && NG == 1) ? 4 : 2; }
+
 template <int PHASE, int LPR, int MAXM, int NG>
-__global__ __launch_bounds__(64 * kMaxWaves) void w4_kernel(W4Args a) {
+__global__ __launch_bounds__(64 * (MAXM == 1 ? kT1MaxWaves : kMaxWaves))
+__attribute__((amdgpu_waves_per_eu(w4_waves_per_eu<MAXM, NG>()))) void w4_kernel(W4Args a) {
     constexpr int RPL = 64 / LPR;  // lane groups (slots) per wave
     constexpr int NB = 4 * LPR;    // columns per block
     extern __shared__ uint4 smem[];
@@ -669,11 +692,10 @@ struct RouteArgs {
 constexpr int kFusedMaxK = 32;
 
 template <int LPR, int NG>
-__global__ __launch_bounds__(64 * kMaxWaves) void route_w4_kernel(W4Args a, RouteArgs r) {
+__global__ __launch_bounds__(64 * kT1MaxWaves)
+__attribute__((amdgpu_waves_per_eu(2))) void route_w4_kernel(W4Args a, RouteArgs r) {
     __shared__ float lg_s[257];
     __shared__ int32_t ids_s[kFusedMaxK];
-    __shared__ float w_s[kFusedMaxK];
-    __shared__ float gate_s;
     extern __shared__ uint4 smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -684,54 +706,57 @@ __global__ __launch_bounds__(64 * kMaxWaves) void route_w4_kernel(W4Args a, Rout
     const int E = a.E, k = r.k;
 
     const smoe_w4_expert spec = spec_table(a, lane);
-    const uint4* row4 = reinterpret_cast<const uint4*>(a.xin);
-    uint4 xv[kRowChunksPerThread];
-    request_row(row4, a.K >> 3, xv);
 
-    // 1. router logits, wave w taking vectors w, w + nwaves, ...
+    // 1. router logits, wave w taking vectors w, w + nwaves, ..., with all
+    //    of its router rows in flight at once where registers allow
     const int nvec = E + (r.wsg ? 1 : 0);
-    smoe_route::wave_logits(a.xin, r.wr, r.wsg, a.K, E, nvec, wave, nvec, nwaves, lg_s, lane);
+    smoe_route::wave_logits_wide(a.xin, r.wr, r.wsg, a.K, E, nvec, wave, nvec, nwaves, lg_s,
+                                 lane);
     __syncthreads();
-    // 2. top-k, softmax weights and gate (wave 0)
-    if (wave == 0)
-        smoe_route::topk_softmax_wave(lg_s, E, k, r.renorm, r.wsg != nullptr, lane, ids_s, w_s,
-                                      &gate_s, nullptr);
+    // 2. the selected ids (wave 0); their weights are computed by workgroup 0
+    //    after its share of the projection
+    if (wave == 0) smoe_route::topk_ids_wave(lg_s, E, k, lane, ids_s);
     __syncthreads();
-    // 3. sorted position of every selected id (ids of one token are distinct)
+    // 3. this slot's expert: the slot-th smallest selected id (the ids of one
+    //    token are distinct), i.e. the expert moe_gather places at row slot
     int e = -1;
     for (int j = 0; j < k; ++j) {
         int less = 0;
         for (int i = 0; i < k; ++i) less += (ids_s[i] < ids_s[j]) ? 1 : 0;
         if (less == slot) e = ids_s[j];
     }
-    if (blockIdx.x == 0) {
-        for (int j = tid; j < k; j += blockDim.x) {
-            const int id = ids_s[j];
-            int pos = 0;
-            for (int i = 0; i < k; ++i) pos += (ids_s[i] < id) ? 1 : 0;
-            r.ids[j] = id;
-            r.w[j] = w_s[j];
-            if (r.counters_row) atomicAdd(r.counters_row + id, 1);
-            r.sorted_token[pos] = 0;
-            r.sorted_pair[pos] = j;
-            r.pair_pos[j] = pos;
-            r.active[pos] = id;
-        }
-        for (int ee = tid; ee <= E; ee += blockDim.x) {
-            int c = 0;
-            for (int i = 0; i < k; ++i) c += (ids_s[i] < ee) ? 1 : 0;
-            r.off[ee] = c;
-            if (ee >= k && ee < E) r.active[ee] = -1;
-        }
-        if (tid == 0) {
-            *r.n_active = k;
-            if (r.wsg && r.gate) *r.gate = gate_s;
-        }
-    }
-    // 4. this slot's block of the gate/up projection
+    // 4. this slot's block of the gate/up projection (the token row is in L2
+    //    after the logits; it is requested here to keep registers free)
     if (cb == 0) write_slot_desc(a, spec, slot, e);
-    if (e < 0) return;  // not reached: every slot below k has an expert
-    one_token_block<1, LPR, NG>(a, carve_lds(smem, a), pick_mat<1>(a, spec, e), xv, slot, cb);
+    if (e >= 0) {
+        uint4 xv[kRowChunksPerThread];
+        request_row(reinterpret_cast<const uint4*>(a.xin), a.K >> 3, xv);
+        one_token_block<1, LPR, NG>(a, carve_lds(smem, a), pick_mat<1>(a, spec, e), xv, slot,
+                                    cb);
+    }
+    // 5. workgroup 0: routing outputs (the routing kernels' own routine), the
+    //    ELB increments and the maps
+    if (blockIdx.x != 0) return;
+    if (wave == 0)
+        smoe_route::topk_softmax_wave(lg_s, E, k, r.renorm, r.wsg != nullptr, lane, r.ids, r.w,
+                                      r.gate, nullptr);
+    for (int j = tid; j < k; j += blockDim.x) {
+        const int id = ids_s[j];
+        int pos = 0;
+        for (int i = 0; i < k; ++i) pos += (ids_s[i] < id) ? 1 : 0;
+        if (r.counters_row) atomicAdd(r.counters_row + id, 1);
+        r.sorted_token[pos] = 0;
+        r.sorted_pair[pos] = j;
+        r.pair_pos[j] = pos;
+        r.active[pos] = id;
+    }
+    for (int ee = tid; ee <= E; ee += blockDim.x) {
+        int c = 0;
+        for (int i = 0; i < k; ++i) c += (ids_s[i] < ee) ? 1 : 0;
+        r.off[ee] = c;
+        if (ee >= k && ee < E) r.active[ee] = -1;
+    }
+    if (tid == 0) *r.n_active = k;
 }
 
 // ---------------------------------------------------------------- launch ----
@@ -751,8 +776,10 @@ PhasePlan plan_phase(int phase, int slots, int T, int K, int N, int I, int maxm)
     PhasePlan p{};
     const int cols16 = (phase == 1) ? I / 32 : (N + 63) / 64;
     const int G16 = K / 128;
-    const int serial16 = (G16 + 4 * kMaxWaves - 1) / (4 * kMaxWaves);
-    p.lpr = ((long long)slots * cols16 >= SMOE_W4_MIN_WG &&
+    const int maxw = (maxm == 1) ? kT1MaxWaves : kMaxWaves;
+    const int min_wg = (maxm == 1) ? kT1MinWG : SMOE_W4_MIN_WG;
+    const int serial16 = (G16 + 4 * maxw - 1) / (4 * maxw);
+    p.lpr = ((long long)slots * cols16 >= min_wg &&
              serial16 <= SMOE_W4_MAX_GROUPS_PER_SLOT) ? 16 : 8;
     const int NB = 4 * p.lpr;
     p.nCB = (phase == 1) ? I / (NB / 2) : (N + NB - 1) / NB;
@@ -761,7 +788,7 @@ PhasePlan plan_phase(int phase, int slots, int T, int K, int N, int I, int maxm)
     p.waves = (G + rpl - 1) / rpl;
     // the launch bound caps every kernel at kMaxWaves; the multi-row kernels'
     // register budget at 4
-    const int wmax = (maxm == 1 || kMaxWaves < 4) ? kMaxWaves : 4;
+    const int wmax = (maxm == 1) ? kT1MaxWaves : (kMaxWaves < 4 ? kMaxWaves : 4);
     if (p.waves > wmax) p.waves = wmax;
     // one-token workgroups request the whole activation row up front
     if (maxm == 1) {
@@ -832,7 +859,7 @@ size_t w4a16_workspace_bytes(int T, int k, int /*H*/, int I, int E) {
 bool w4a16_shape_supported(int H, int I) {
     // activation rows staged in LDS; one-token workgroups request a whole row
     // with kRowChunksPerThread chunks per thread
-    const int row_cap = 8 * 64 * kRowChunksPerThread * kMaxWaves;
+    const int row_cap = 8 * 64 * kRowChunksPerThread * kT1MaxWaves;
     return (size_t)H * 2 <= (size_t)kLdsBytes && (size_t)I * 2 <= (size_t)kLdsBytes &&
            H <= row_cap && I <= row_cap;
 }

@@ -243,8 +243,12 @@ def _layer(shape, Ts, steps=(0,), int4=True, f16=True):
     return _layers[key]
 
 
+# long reductions: three and four 128-K groups per slot in the one-token path
+_LONG_I = dataclasses.replace(synth.TINY, name="tiny_i12288", E=4, k=2, I=12288)
+_LONG_H = dataclasses.replace(synth.TINY, name="tiny_h16384", H=16384, E=4, k=2, I=256)
 W4_CASES = [(synth.TINY, 4), (synth.TINY, 40), (synth.DS, 1), (synth.DS, 4), (synth.DS, 16),
-            (synth.PHI, 1), (synth.QWEN, 1)]
+            (synth.PHI, 1), (synth.QWEN, 1), (_LONG_I, 1), (_LONG_I, 3), (_LONG_H, 1),
+            (_LONG_H, 2)]
 
 
 @pytest.mark.parametrize("shape,T", W4_CASES, ids=lambda v: getattr(v, "name", str(v)))
@@ -279,7 +283,7 @@ _ALL = dataclasses.replace(synth.TINY, name="tiny_k_eq_e", k=8)            # eve
 _RENORM = dataclasses.replace(synth.TINY, name="tiny_renorm_k3", k=3, renormalize=True)
 DRAFT_FUSED_CASES = [(synth.TINY, 0), (synth.TINY, 7), (synth.DS, 0), (synth.DS, 3),
                      (synth.QWEN, 0), (synth.PHI, 0), (synth.PHI, 5), (_WIDE, 0), (_ALL, 0),
-                     (_RENORM, 2)]
+                     (_RENORM, 2), (_LONG_I, 0), (_LONG_H, 1)]
 
 
 @pytest.mark.parametrize("shape,step", DRAFT_FUSED_CASES,
