@@ -26,7 +26,8 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (expert_stage_async, f16_expert_table, moe_combine, moe_gather, moe_route_plan,
+from . import (expert_stage_async, f16_expert_table, moe_combine, moe_draft_route_ffn,
+               moe_gather, moe_route_plan,
                moe_route_topk, new_workspace, verify_grouped_gemm, w4_expert_table,
                w4a16_grouped_ffn)
 
@@ -129,13 +130,13 @@ class ChunkEngine:
         layer's expert choices in the ELB table."""
         xn = x
         for l, ly in enumerate(self.layers):
-            # routing, ELB update and gather maps in one launch
-            ids, w, gate, maps = moe_route_plan(xn, ly.router, self.k, False, ly.shared_gate,
-                                                counters=self.counters, layer=l,
-                                                err_word=self.err)
             sh = self._shared_fork(l, xn)
-            y = w4a16_grouped_ffn(xn, maps, self.t4[l], 1, self.k, self.H, self.I, self.E,
-                                  self.ws_d, err_word=self.err)
+            # routing, ELB update and gather maps folded into the gate/up
+            # launch, then the down projection
+            ids, w, gate, maps, y = moe_draft_route_ffn(xn, ly.router, self.k, self.t4[l],
+                                                        self.I, self.ws_d, False, ly.shared_gate,
+                                                        counters=self.counters, layer=l,
+                                                        err_word=self.err)
             self._join()
             out, xn_next = moe_combine(y, maps["pair_pos"], w, sh, gate, x, norm_out=True)
             if record is not None:
