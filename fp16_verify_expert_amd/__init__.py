@@ -48,6 +48,8 @@ _SIGS = {
                             _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "w4a16_grouped_ffn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp,
                                _sz, _vp, _vp]),
+    "wq_grouped_ffn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
+                            _sz, _vp, _vp]),
     "moe_draft_route_ffn": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp,
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
                                  _vp]),
@@ -235,6 +237,19 @@ def w4a16_grouped_ffn(x, maps, table, T: int, k: int, H: int, I: int, E: int, wo
         y_sorted = torch.empty((max(T * k, 1), H), dtype=torch.float16, device=x.device)
     _call("w4a16_grouped_ffn", _p(x), _p(maps["sorted_token"]), _p(maps["offsets"]),
           _p(maps["active"]), _p(maps["n_active"]), _p(table), T, k, H, I, E, 128,
+          _p(y_sorted), _p(workspace), workspace.numel() * workspace.element_size(),
+          _p(err_word), _s(stream))
+    return y_sorted
+
+
+def wq_grouped_ffn(x, maps, table, T: int, k: int, H: int, I: int, E: int, workspace,
+                   bits: int, *, y_sorted=None, err_word=None, stream=None):
+    """w4a16_grouped_ffn for 2-, 4- or 8-bit GPTQ-layout experts."""
+    _check(x, torch.float16, "x")
+    if y_sorted is None:
+        y_sorted = torch.empty((max(T * k, 1), H), dtype=torch.float16, device=x.device)
+    _call("wq_grouped_ffn", _p(x), _p(maps["sorted_token"]), _p(maps["offsets"]),
+          _p(maps["active"]), _p(maps["n_active"]), _p(table), T, k, H, I, E, bits, 128,
           _p(y_sorted), _p(workspace), workspace.numel() * workspace.element_size(),
           _p(err_word), _s(stream))
     return y_sorted

@@ -189,35 +189,56 @@ smoe_status moe_route_plan(const uint16_t* x, const uint16_t* w_router,
                       "moe_route_plan launch");
 }
 
+smoe_status wq_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
+                           const int32_t* expert_offsets, const int32_t* active,
+                           const int32_t* n_active, const smoe_w4_expert* experts, int T, int k,
+                           int H, int I, int E, int bits, int group_size, uint16_t* y_sorted,
+                           void* workspace, size_t workspace_bytes, int32_t* err_word,
+                           void* stream) {
+    REQUIRE(x && sorted_token && expert_offsets && active && n_active && experts && y_sorted,
+            SMOE_ERR_NULL, "wq_grouped_ffn: a required pointer is NULL");
+    REQUIRE(T >= 0, SMOE_ERR_SHAPE, "wq_grouped_ffn: T=%d < 0", T);
+    REQUIRE(bits == 2 || bits == 4 || bits == 8, SMOE_ERR_UNSUPPORTED,
+            "wq_grouped_ffn: bits=%d (2, 4 or 8)", bits);
+    smoe_status st = check_hek(H, E, k);
+    if (st != SMOE_OK) return st;
+    REQUIRE(I > 0 && I % 128 == 0, SMOE_ERR_SHAPE,
+            "wq_grouped_ffn: I=%d must be a positive multiple of 128", I);
+    REQUIRE(group_size == 128, SMOE_ERR_UNSUPPORTED,
+            "wq_grouped_ffn: group_size=%d (only 128 is supported)", group_size);
+    REQUIRE((long long)T * k <= kMaxPairs, SMOE_ERR_SHAPE, "wq_grouped_ffn: T*k exceeds 2^20");
+    REQUIRE(smoe::w4a16_shape_supported(H, I), SMOE_ERR_SHAPE,
+            "wq_grouped_ffn: H=%d, I=%d (each must be <= 16384)", H, I);
+    REQUIRE(aligned(x, 16), SMOE_ERR_SHAPE, "wq_grouped_ffn: x must be 16-byte aligned");
+    if (T == 0) return ok();
+    const size_t need = smoe::w4a16_workspace_bytes(T, k, H, I, E);
+    REQUIRE(workspace && workspace_bytes >= need && aligned(workspace, 256), SMOE_ERR_WORKSPACE,
+            "wq_grouped_ffn: workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+            workspace_bytes);
+    CHECK_DEVICE();
+    return hip_result(smoe::launch_w4a16_ffn(x, sorted_token, expert_offsets, active, n_active,
+                                             experts, T, k, H, I, E, bits, y_sorted, workspace,
+                                             err_word, static_cast<hipStream_t>(stream)),
+                      "wq_grouped_ffn launch");
+}
+
 smoe_status w4a16_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
                               const int32_t* expert_offsets, const int32_t* active,
                               const int32_t* n_active, const smoe_w4_expert* experts, int T,
                               int k, int H, int I, int E, int group_size, uint16_t* y_sorted,
                               void* workspace, size_t workspace_bytes, int32_t* err_word,
                               void* stream) {
-    REQUIRE(x && sorted_token && expert_offsets && active && n_active && experts && y_sorted,
-            SMOE_ERR_NULL, "w4a16_grouped_ffn: a required pointer is NULL");
-    REQUIRE(T >= 0, SMOE_ERR_SHAPE, "w4a16_grouped_ffn: T=%d < 0", T);
-    smoe_status st = check_hek(H, E, k);
-    if (st != SMOE_OK) return st;
-    REQUIRE(I > 0 && I % 128 == 0, SMOE_ERR_SHAPE,
-            "w4a16_grouped_ffn: I=%d must be a positive multiple of 128", I);
-    REQUIRE(group_size == 128, SMOE_ERR_UNSUPPORTED,
-            "w4a16_grouped_ffn: group_size=%d (only 128 is supported)", group_size);
-    REQUIRE((long long)T * k <= kMaxPairs, SMOE_ERR_SHAPE, "w4a16_grouped_ffn: T*k exceeds 2^20");
-    REQUIRE(smoe::w4a16_shape_supported(H, I), SMOE_ERR_SHAPE,
-            "w4a16_grouped_ffn: H=%d, I=%d (each must be <= 16384)", H, I);
-    REQUIRE(aligned(x, 16), SMOE_ERR_SHAPE, "w4a16_grouped_ffn: x must be 16-byte aligned");
-    if (T == 0) return ok();
-    const size_t need = smoe::w4a16_workspace_bytes(T, k, H, I, E);
-    REQUIRE(workspace && workspace_bytes >= need && aligned(workspace, 256), SMOE_ERR_WORKSPACE,
-            "w4a16_grouped_ffn: workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
-            workspace_bytes);
-    CHECK_DEVICE();
-    return hip_result(smoe::launch_w4a16_ffn(x, sorted_token, expert_offsets, active, n_active,
-                                             experts, T, k, H, I, E, y_sorted, workspace,
-                                             err_word, static_cast<hipStream_t>(stream)),
-                      "w4a16_grouped_ffn launch");
+    const smoe_status st = wq_grouped_ffn(x, sorted_token, expert_offsets, active, n_active,
+                                          experts, T, k, H, I, E, 4, group_size, y_sorted,
+                                          workspace, workspace_bytes, err_word, stream);
+    if (st != SMOE_OK) {
+        // report under this entry point's name
+        std::string m = g_err;
+        const std::string from = "wq_grouped_ffn";
+        if (m.compare(0, from.size(), from) == 0) m = "w4a16_grouped_ffn" + m.substr(from.size());
+        g_err = m;
+    }
+    return st;
 }
 
 smoe_status moe_draft_route_ffn(const uint16_t* x, const uint16_t* w_router,

@@ -46,7 +46,20 @@
 namespace {
 
 constexpr uint32_t kMagic = 0x64006400u;
-constexpr int kRowsPerGroup = 16;     // packed rows (8 K each) per 128-K group
+
+// Geometry of a GPTQ-layout matrix with BITS-bit codes as a lane group walks
+// it: a "pseudo-group" is the run of packed rows one lane group holds in
+// registers at a time -- one 128-K quantisation group for 2 and 4 bits, half
+// of one for 8 bits (its 32 packed rows would not fit).
+template <int BITS>
+struct QF {
+    static_assert(BITS == 2 || BITS == 4 || BITS == 8, "code width");
+    static constexpr int kCodes = 32 / BITS;            // codes per packed word
+    static constexpr int kWords = (BITS == 2) ? 8 : 16;  // packed rows per pseudo-group
+    static constexpr int kK = kWords * kCodes;          // K per pseudo-group: 128, 128, 64
+    static constexpr int kChunks = kK / 8;              // 16-byte activation chunks per pseudo-group
+    static constexpr int kPerQG = 128 / kK;             // pseudo-groups per quantisation group
+};
 #ifndef SMOE_W4_MAX_WAVES
 #define SMOE_W4_MAX_WAVES 4
 #endif
@@ -111,81 +124,178 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g));
 // Masks held in VGPRs: with a VGPR mask and the magic constant in an SGPR the
 // compiler emits one v_and_or_b32 per code pair (a VOP3 op cannot take two
 // scalar/literal operands on this target).
-__device__ __forceinline__ uint32_t vgpr_const_lo() {
+template <uint32_t C>
+__device__ __forceinline__ uint32_t vgpr_const() {
     uint32_t v;
-    asm("v_mov_b32 %0, 0xf000f" : "=v"(v));
+    asm("v_mov_b32 %0, %1" : "=v"(v) : "i"(C));
     return v;
 }
-__device__ __forceinline__ uint32_t vgpr_const_hi() {
-    uint32_t v;
-    asm("v_mov_b32 %0, 0xf000f0" : "=v"(v));
-    return v;
-}
+__device__ __forceinline__ uint32_t vgpr_const_lo() { return vgpr_const<0x000F000Fu>(); }
+__device__ __forceinline__ uint32_t vgpr_const_hi() { return vgpr_const<0x00F000F0u>(); }
 
-// One 128-K group of M activation rows against this lane's 4 columns.
-//   A_even = sum over even k of (1024 + q_k) x_k,
-//   A_odd  = sum over odd  k of (1024 + 16 q_k) x_k,
-//   sum_k (q_k - z) x_k = A_even + A_odd/16 - (1024 + z) S_even - (64 + z) S_odd
-// with S_even, S_odd the group's activation sums (precomputed in LDS).
-template <int M, int MAXM>
-__device__ __forceinline__ void group_dot(const u4_t (&wv)[kRowsPerGroup],
+// The code masks of a BITS-bit word, held in VGPRs.  4 bits: (0x000F000F,
+// 0x00F000F0); 8 bits: 0x00FF00FF; 2 bits: 0x00030003 << 2j, j < 4.
+template <int BITS>
+struct Masks {
+    uint32_t m[4];
+    __device__ __forceinline__ Masks() {
+        if constexpr (BITS == 4) {
+            m[0] = vgpr_const_lo();
+            m[1] = vgpr_const_hi();
+        } else if constexpr (BITS == 8) {
+            m[0] = vgpr_const<0x00FF00FFu>();
+        } else {
+            m[0] = vgpr_const<0x00030003u>();
+            m[1] = vgpr_const<0x000C000Cu>();
+            m[2] = vgpr_const<0x00300030u>();
+            m[3] = vgpr_const<0x00C000C0u>();
+        }
+    }
+};
+
+// One pseudo-group of M activation rows against this lane's 4 columns.  The
+// codes of a word become fp16 pairs (1024 + 2^(BITS j) q) with one and-or
+// each and meet activation pairs staged to match (see permute_chunk).  With
+// A_j the dot over codes of class j (code index mod 2 for 4 bits, mod 4 for
+// 2 bits, a single class for 8 bits) and S_j the matching activation sums:
+//   4 bits: sum (q - z) x = A_0 + A_1/16 - (1024 + z) S_0 - (64 + z) S_1
+//   2 bits: sum (q - z) x = A_0 + A_1/4 + A_2/16 + A_3/64
+//                           - (1024 + z) S_0 - (256 + z) S_1 - (64 + z) S_2 - (16 + z) S_3
+//   8 bits: sum (q - z) x = A_0 - (1024 + z) S_0
+template <int BITS, int M, int MAXM>
+__device__ __forceinline__ void group_dot(const u4_t (&wv)[QF<BITS>::kWords],
                                           const uint4* __restrict__ xs,
-                                          const float2* __restrict__ sums,
+                                          const float4* __restrict__ sums,
                                           const int (&xoff)[MAXM], const int (&soff)[MAXM],
-                                          uint2 sv, uint32_t zw, uint32_t mlo, uint32_t mhi,
+                                          uint2 sv, uint32_t zw, const Masks<BITS>& mk,
                                           float (&acc)[MAXM][4]) {
-    float ae[M][4], ao[M][4];
+    constexpr int NCLS = (BITS == 2) ? 4 : (BITS == 4 ? 2 : 1);
+    float a[NCLS][M][4];
 #pragma unroll
-    for (int m = 0; m < M; ++m)
+    for (int j = 0; j < NCLS; ++j)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) ae[m][c] = ao[m][c] = 0.0f;
+        for (int m = 0; m < M; ++m)
 #pragma unroll
-    for (int i = 0; i < kRowsPerGroup; ++i) {
-        // one packed row at a time: keeps the activation reads from being
-        // hoisted ahead of the whole group (register pressure)
-        if (SMOE_W4_ROWFENCE) __builtin_amdgcn_sched_barrier(0);
-        uint4 xp[M];
+            for (int c = 0; c < 4; ++c) a[j][m][c] = 0.0f;
+    if constexpr (BITS == 4) {
 #pragma unroll
-        for (int m = 0; m < M; ++m) xp[m] = xs[xoff[m] + i];
+        for (int i = 0; i < QF<4>::kWords; ++i) {
+            // one packed row at a time: keeps the activation reads from being
+            // hoisted ahead of the whole group (register pressure)
+            if (SMOE_W4_ROWFENCE) __builtin_amdgcn_sched_barrier(0);
+            uint4 xp[M];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint32_t w = wv[i][c];
-            const uint32_t b = w >> 8;
-            const h2_t e0 = as_h2((w & mlo) | kMagic);  // 1024+q0, 1024+q4
-            const h2_t o0 = as_h2((w & mhi) | kMagic);  // 1024+16q1, 1024+16q5
-            const h2_t e1 = as_h2((b & mlo) | kMagic);  // 1024+q2, 1024+q6
-            const h2_t o1 = as_h2((b & mhi) | kMagic);  // 1024+16q3, 1024+16q7
+            for (int m = 0; m < M; ++m) xp[m] = xs[xoff[m] + i];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t w = wv[i][c];
+                const uint32_t b = w >> 8;
+                const h2_t e0 = as_h2((w & mk.m[0]) | kMagic);  // 1024+q0, 1024+q4
+                const h2_t o0 = as_h2((w & mk.m[1]) | kMagic);  // 1024+16q1, 1024+16q5
+                const h2_t e1 = as_h2((b & mk.m[0]) | kMagic);  // 1024+q2, 1024+q6
+                const h2_t o1 = as_h2((b & mk.m[1]) | kMagic);  // 1024+16q3, 1024+16q7
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    a[0][m][c] = __builtin_amdgcn_fdot2(e0, as_h2(xp[m].x), a[0][m][c], false);
+                    a[1][m][c] = __builtin_amdgcn_fdot2(o0, as_h2(xp[m].y), a[1][m][c], false);
+                    a[0][m][c] = __builtin_amdgcn_fdot2(e1, as_h2(xp[m].z), a[0][m][c], false);
+                    a[1][m][c] = __builtin_amdgcn_fdot2(o1, as_h2(xp[m].w), a[1][m][c], false);
+                }
+            }
+        }
+    } else if constexpr (BITS == 8) {
+        // two packed rows (8 K) per activation chunk
+#pragma unroll
+        for (int u = 0; u < QF<8>::kChunks; ++u) {
+            if (SMOE_W4_ROWFENCE) __builtin_amdgcn_sched_barrier(0);
+            uint4 xp[M];
+#pragma unroll
+            for (int m = 0; m < M; ++m) xp[m] = xs[xoff[m] + u];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t w0 = wv[2 * u][c];
+                const uint32_t w1 = wv[2 * u + 1][c];
+                const h2_t p0 = as_h2((w0 & mk.m[0]) | kMagic);         // 1024+q0, 1024+q2
+                const h2_t p1 = as_h2(((w0 >> 8) & mk.m[0]) | kMagic);  // 1024+q1, 1024+q3
+                const h2_t p2 = as_h2((w1 & mk.m[0]) | kMagic);         // 1024+q4, 1024+q6
+                const h2_t p3 = as_h2(((w1 >> 8) & mk.m[0]) | kMagic);  // 1024+q5, 1024+q7
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    a[0][m][c] = __builtin_amdgcn_fdot2(p0, as_h2(xp[m].x), a[0][m][c], false);
+                    a[0][m][c] = __builtin_amdgcn_fdot2(p1, as_h2(xp[m].y), a[0][m][c], false);
+                    a[0][m][c] = __builtin_amdgcn_fdot2(p2, as_h2(xp[m].z), a[0][m][c], false);
+                    a[0][m][c] = __builtin_amdgcn_fdot2(p3, as_h2(xp[m].w), a[0][m][c], false);
+                }
+            }
+        }
+    } else {
+        // one packed row (16 K) per two activation chunks
+#pragma unroll
+        for (int i = 0; i < QF<2>::kWords; ++i) {
+            if (SMOE_W4_ROWFENCE) __builtin_amdgcn_sched_barrier(0);
+            uint4 xa[M], xb[M];
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                ae[m][c] = __builtin_amdgcn_fdot2(e0, as_h2(xp[m].x), ae[m][c], false);
-                ao[m][c] = __builtin_amdgcn_fdot2(o0, as_h2(xp[m].y), ao[m][c], false);
-                ae[m][c] = __builtin_amdgcn_fdot2(e1, as_h2(xp[m].z), ae[m][c], false);
-                ao[m][c] = __builtin_amdgcn_fdot2(o1, as_h2(xp[m].w), ao[m][c], false);
+                xa[m] = xs[xoff[m] + 2 * i];
+                xb[m] = xs[xoff[m] + 2 * i + 1];
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t w = wv[i][c];
+                const uint32_t b = w >> 8;
+                h2_t pw[4], pb[4];  // class j: 1024 + 4^j q (codes j, j+8 and j+4, j+12)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pw[j] = as_h2((w & mk.m[j]) | kMagic);
+                    pb[j] = as_h2((b & mk.m[j]) | kMagic);
+                }
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    const uint32_t xav[4] = {xa[m].x, xa[m].y, xa[m].z, xa[m].w};
+                    const uint32_t xbv[4] = {xb[m].x, xb[m].y, xb[m].z, xb[m].w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        a[j][m][c] = __builtin_amdgcn_fdot2(pw[j], as_h2(xav[j]), a[j][m][c], false);
+                        a[j][m][c] = __builtin_amdgcn_fdot2(pb[j], as_h2(xbv[j]), a[j][m][c], false);
+                    }
+                }
             }
         }
     }
-    float2 se[M];
+    float4 se[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) se[m] = sums[soff[m]];
     const uint32_t sw[2] = {sv.x, sv.y};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const float s = h2f((uint16_t)(sw[c >> 1] >> (16 * (c & 1))));
-        const float z = (float)((zw >> (4 * c)) & 0xFu);
-        const float ce = 1024.0f + z;
-        const float co = 64.0f + z;
+        const float z = (float)((zw >> (BITS * c)) & ((1u << BITS) - 1u));
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            float t = ae[m][c] + 0.0625f * ao[m][c];
-            t -= ce * se[m].x;
-            t -= co * se[m].y;
+            float t;
+            if constexpr (BITS == 4) {
+                t = a[0][m][c] + 0.0625f * a[1][m][c];
+                t -= (1024.0f + z) * se[m].x;
+                t -= (64.0f + z) * se[m].y;
+            } else if constexpr (BITS == 8) {
+                t = a[0][m][c];
+                t -= (1024.0f + z) * se[m].x;
+            } else {
+                t = a[0][m][c] + 0.25f * a[1][m][c] + 0.0625f * a[2][m][c] +
+                    0.015625f * a[3][m][c];
+                t -= (1024.0f + z) * se[m].x;
+                t -= (256.0f + z) * se[m].y;
+                t -= (64.0f + z) * se[m].z;
+                t -= (16.0f + z) * se[m].w;
+            }
             acc[m][c] += s * t;
         }
     }
 }
 
+template <int BITS>
 struct GroupLoad {
-    u4_t w[kRowsPerGroup];
+    u4_t w[QF<BITS>::kWords];
     uint2 s;
     uint32_t z;
 };
@@ -194,7 +304,7 @@ struct GroupLoad {
 // (column and group) is one VGPR and the packed-row stride a scalar offset,
 // so a group's 16 row addresses cost no vector registers.
 struct W4Src {
-    __amdgpu_buffer_rsrc_t q;  // qweight [K/8, N] int32
+    __amdgpu_buffer_rsrc_t q;  // qweight [K*BITS/32, N] int32
     smoe_w4_mat m;
     int N;
 };
@@ -213,6 +323,7 @@ SMOE_DEV T* uniform_ptr(T* p) {
     return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
 }
 
+template <int BITS>
 __device__ __forceinline__ W4Src make_src(const smoe_w4_mat& mm, int K, int N) {
     smoe_w4_mat m;
     m.qweight = uniform_ptr(mm.qweight);
@@ -220,7 +331,7 @@ __device__ __forceinline__ W4Src make_src(const smoe_w4_mat& mm, int K, int N) {
     m.qzeros = uniform_ptr(mm.qzeros);
     W4Src s;
     s.q = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(m.qweight), (short)0,
-                                            (K >> 3) * N * 4, kBufWord3);
+                                            (K / QF<BITS>::kCodes) * N * 4, kBufWord3);
     s.m = m;
     s.N = N;
     return s;
@@ -229,85 +340,147 @@ __device__ __forceinline__ W4Src make_src(const smoe_w4_mat& mm, int K, int N) {
 // Every load is unconditional (a column past N reads column 0; its sums are
 // never stored), so the loads in flight are a static count and the waits the
 // compiler places for older loads (the activation row) leave them in flight.
-__device__ __forceinline__ void load_group(GroupLoad& L, const W4Src& src, int g, int col,
+template <int BITS>
+__device__ __forceinline__ void load_group(GroupLoad<BITS>& L, const W4Src& src, int g, int col,
                                            bool colok) {
+    using F = QF<BITS>;
     const int N = src.N;
     const int c = colok ? col : 0;
-    const int voff = ((g * kRowsPerGroup) * N + c) * 4;
+    const int qg = g / F::kPerQG;  // quantisation group
+    const int voff = ((g * F::kWords) * N + c) * 4;
 #pragma unroll
-    for (int i = 0; i < kRowsPerGroup; ++i)
+    for (int i = 0; i < F::kWords; ++i)
         L.w[i] = __builtin_amdgcn_raw_buffer_load_b128(src.q, voff, i * N * 4, kAuxNT);
     const uint64_t sv =
-        *as_global(reinterpret_cast<const uint64_t*>(src.m.scales + (size_t)g * N + c));
+        *as_global(reinterpret_cast<const uint64_t*>(src.m.scales + (size_t)qg * N + c));
     L.s = make_uint2((uint32_t)sv, (uint32_t)(sv >> 32));
     // the word holding this lane's 4 zeros (shifted when the group is
     // consumed, so that issuing the loads waits for none of them)
-    L.z = (uint32_t)*as_global(src.m.qzeros + (size_t)g * (N >> 3) + (c >> 3));
+    L.z = (uint32_t)*as_global(src.m.qzeros + (size_t)qg * (N / F::kCodes) + (c / F::kCodes));
 }
 
-template <int MAXM>
-__device__ __forceinline__ void group_step(const GroupLoad& L, const uint4* xs, const float2* sums,
-                                           const int (&xrow)[MAXM], int g, int K8, int G, int M,
-                                           int zsh, uint32_t mlo, uint32_t mhi,
+// Shift of a lane's first zero inside its zero word (columns are 4-aligned).
+template <int BITS>
+SMOE_DEV int zero_shift(int col) { return BITS * (col & (QF<BITS>::kCodes - 1)); }
+
+template <int BITS, int MAXM>
+__device__ __forceinline__ void group_step(const GroupLoad<BITS>& L, const uint4* xs,
+                                           const float4* sums, const int (&xrow)[MAXM], int g,
+                                           int K8, int G, int M, int zsh, const Masks<BITS>& mk,
                                            float (&acc)[MAXM][4]) {
     const uint32_t zw = L.z >> zsh;
     int xoff[MAXM], soff[MAXM];
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) {
-        xoff[m] = xrow[m] * K8 + g * kRowsPerGroup;
+        xoff[m] = xrow[m] * K8 + g * QF<BITS>::kChunks;
         soff[m] = xrow[m] * G + g;
     }
     if (MAXM == 1) {
-        group_dot<1, MAXM>(L.w, xs, sums, xoff, soff, L.s, zw, mlo, mhi, acc);
+        group_dot<BITS, 1, MAXM>(L.w, xs, sums, xoff, soff, L.s, zw, mk, acc);
     } else {
         switch (M) {
-            case 1: group_dot<1, MAXM>(L.w, xs, sums, xoff, soff, L.s, zw, mlo, mhi, acc); break;
-            case 2: group_dot<(MAXM >= 2 ? 2 : 1), MAXM>(L.w, xs, sums, xoff, soff, L.s, zw, mlo, mhi, acc); break;
-            case 3: group_dot<(MAXM >= 3 ? 3 : 1), MAXM>(L.w, xs, sums, xoff, soff, L.s, zw, mlo, mhi, acc); break;
-            default: group_dot<MAXM, MAXM>(L.w, xs, sums, xoff, soff, L.s, zw, mlo, mhi, acc); break;
+            case 1: group_dot<BITS, 1, MAXM>(L.w, xs, sums, xoff, soff, L.s, zw, mk, acc); break;
+            case 2: group_dot<BITS, (MAXM >= 2 ? 2 : 1), MAXM>(L.w, xs, sums, xoff, soff, L.s, zw, mk, acc); break;
+            case 3: group_dot<BITS, (MAXM >= 3 ? 3 : 1), MAXM>(L.w, xs, sums, xoff, soff, L.s, zw, mk, acc); break;
+            default: group_dot<BITS, MAXM, MAXM>(L.w, xs, sums, xoff, soff, L.s, zw, mk, acc); break;
         }
     }
 }
 
-// Activations as the dot2 pairs the dequantised codes meet: (x0,x4), (x1,x5),
-// (x2,x6), (x3,x7) of each 8-element chunk.
-__device__ __forceinline__ uint4 pair_permute(uint4 d) {
+// Activations as the dot2 pairs the dequantised codes meet.  4 bits: (x0,x4),
+// (x1,x5), (x2,x6), (x3,x7) of each 8-element chunk; 8 bits: (x0,x2),
+// (x1,x3), (x4,x6), (x5,x7).  2 bits pair elements 8 apart, so a pair of
+// chunks is permuted together (permute_chunk_pair).
+template <int BITS>
+__device__ __forceinline__ uint4 permute_chunk(uint4 d) {
     uint4 p;
-    p.x = (d.x & 0xFFFFu) | (d.z << 16);      // (x0, x4)
-    p.y = (d.x >> 16) | (d.z & 0xFFFF0000u);  // (x1, x5)
-    p.z = (d.y & 0xFFFFu) | (d.w << 16);      // (x2, x6)
-    p.w = (d.y >> 16) | (d.w & 0xFFFF0000u);  // (x3, x7)
+    if constexpr (BITS == 4) {
+        p.x = (d.x & 0xFFFFu) | (d.z << 16);      // (x0, x4)
+        p.y = (d.x >> 16) | (d.z & 0xFFFF0000u);  // (x1, x5)
+        p.z = (d.y & 0xFFFFu) | (d.w << 16);      // (x2, x6)
+        p.w = (d.y >> 16) | (d.w & 0xFFFF0000u);  // (x3, x7)
+    } else if constexpr (BITS == 8) {
+        p.x = (d.x & 0xFFFFu) | (d.y << 16);      // (x0, x2)
+        p.y = (d.x >> 16) | (d.y & 0xFFFF0000u);  // (x1, x3)
+        p.z = (d.z & 0xFFFFu) | (d.w << 16);      // (x4, x6)
+        p.w = (d.z >> 16) | (d.w & 0xFFFF0000u);  // (x5, x7)
+    } else {
+        p = d;  // 2 bits: natural order here, paired by permute_chunk_pair
+    }
     return p;
 }
 
-// Stage activation rows src_row(j), j < nrows, into LDS rows 0..nrows-1 as
-// dot2 pairs, then their per-group sums over even and odd k.
-template <typename RowPtr>
-__device__ __forceinline__ void stage_rows(uint4* xs, float2* sums, int nrows, int K8, int G,
-                                           RowPtr src_row) {
+// 2 bits: chunks d0 = x0..x7, d1 = x8..x15 of one packed row become
+// (x0,x8), (x1,x9), (x2,x10), (x3,x11) and (x4,x12), ..., (x7,x15).
+__device__ __forceinline__ void permute_chunk_pair(uint4 d0, uint4 d1, uint4& pa, uint4& pb) {
+    pa.x = (d0.x & 0xFFFFu) | (d1.x << 16);
+    pa.y = (d0.x >> 16) | (d1.x & 0xFFFF0000u);
+    pa.z = (d0.y & 0xFFFFu) | (d1.y << 16);
+    pa.w = (d0.y >> 16) | (d1.y & 0xFFFF0000u);
+    pb.x = (d0.z & 0xFFFFu) | (d1.z << 16);
+    pb.y = (d0.z >> 16) | (d1.z & 0xFFFF0000u);
+    pb.z = (d0.w & 0xFFFFu) | (d1.w << 16);
+    pb.w = (d0.w >> 16) | (d1.w & 0xFFFF0000u);
+}
+
+// After the chunks of `nrows` rows are in LDS (permuted for 4 and 8 bits,
+// natural for 2 bits): pair the 2-bit chunks in place, then the per-class
+// activation sums of every (row, pseudo-group).  Ends with a barrier.
+template <int BITS>
+__device__ __forceinline__ void finish_rows(uint4* xs, float4* sums, int nrows, int K8, int G) {
+    using F = QF<BITS>;
+    if constexpr (BITS == 2) {
+        __syncthreads();
 #pragma unroll 1
-    for (int idx = threadIdx.x; idx < nrows * K8; idx += blockDim.x) {
-        const int j = idx / K8;
-        const int rr = idx - j * K8;
-        xs[j * K8 + rr] = pair_permute(src_row(j)[rr]);
+        for (int idx = threadIdx.x; idx < nrows * (K8 / 2); idx += blockDim.x) {
+            uint4* c = xs + 2 * idx;  // rows hold K8 chunks, K8 even
+            uint4 pa, pb;
+            permute_chunk_pair(c[0], c[1], pa, pb);
+            c[0] = pa;
+            c[1] = pb;
+        }
     }
     __syncthreads();
 #pragma unroll 1
     for (int idx = threadIdx.x; idx < nrows * G; idx += blockDim.x) {
         const int j = idx / G;
         const int gg = idx - j * G;
-        const uint4* xr = xs + j * K8 + gg * kRowsPerGroup;
-        float se = 0.0f, so = 0.0f;
+        const uint4* xr = xs + j * K8 + gg * F::kChunks;
+        float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 4
-        for (int i = 0; i < kRowsPerGroup; ++i) {
+        for (int i = 0; i < F::kChunks; ++i) {
             const uint4 p = xr[i];
-            const h2_t x04 = as_h2(p.x), x15 = as_h2(p.y), x26 = as_h2(p.z), x37 = as_h2(p.w);
-            se += ((float)x04.x + (float)x04.y) + ((float)x26.x + (float)x26.y);
-            so += ((float)x15.x + (float)x15.y) + ((float)x37.x + (float)x37.y);
+            const h2_t x0 = as_h2(p.x), x1 = as_h2(p.y), x2 = as_h2(p.z), x3 = as_h2(p.w);
+            if constexpr (BITS == 4) {
+                s4[0] += ((float)x0.x + (float)x0.y) + ((float)x2.x + (float)x2.y);
+                s4[1] += ((float)x1.x + (float)x1.y) + ((float)x3.x + (float)x3.y);
+            } else if constexpr (BITS == 8) {
+                s4[0] += (((float)x0.x + (float)x0.y) + ((float)x1.x + (float)x1.y)) +
+                         (((float)x2.x + (float)x2.y) + ((float)x3.x + (float)x3.y));
+            } else {
+                s4[0] += (float)x0.x + (float)x0.y;
+                s4[1] += (float)x1.x + (float)x1.y;
+                s4[2] += (float)x2.x + (float)x2.y;
+                s4[3] += (float)x3.x + (float)x3.y;
+            }
         }
-        sums[j * G + gg] = make_float2(se, so);
+        sums[j * G + gg] = make_float4(s4[0], s4[1], s4[2], s4[3]);
     }
     __syncthreads();
+}
+
+// Stage activation rows src_row(j), j < nrows, into LDS rows 0..nrows-1 as
+// dot2 pairs, then their per-class sums.
+template <int BITS, typename RowPtr>
+__device__ __forceinline__ void stage_rows(uint4* xs, float4* sums, int nrows, int K8, int G,
+                                           RowPtr src_row) {
+#pragma unroll 1
+    for (int idx = threadIdx.x; idx < nrows * K8; idx += blockDim.x) {
+        const int j = idx / K8;
+        const int rr = idx - j * K8;
+        xs[j * K8 + rr] = permute_chunk<BITS>(src_row(j)[rr]);
+    }
+    finish_rows<BITS>(xs, sums, nrows, K8, G);
 }
 
 // Add the slots' partial sums of rows [mc, mc+M) in a fixed order and write
@@ -351,20 +524,20 @@ __device__ __forceinline__ void reduce_store(const W4Args& a, float* red, const 
 
 // A slot's groups g, g + nslots, ... of the reduction.  With kPrefetch the
 // next group's weights are requested before the current group is consumed.
-template <bool kPrefetch, int MAXM>
-__device__ __forceinline__ void run_groups(GroupLoad& cur, int g, int nslots, int G,
+template <int BITS, bool kPrefetch, int MAXM>
+__device__ __forceinline__ void run_groups(GroupLoad<BITS>& cur, int g, int nslots, int G,
                                            const W4Src& src, int col, bool colok,
-                                           const uint4* xs, const float2* sums,
-                                           const int (&xrow)[MAXM], int K8, int M, uint32_t mlo,
-                                           uint32_t mhi, float (&acc)[MAXM][4]) {
+                                           const uint4* xs, const float4* sums,
+                                           const int (&xrow)[MAXM], int K8, int M,
+                                           const Masks<BITS>& mk, float (&acc)[MAXM][4]) {
     if (g >= G) return;
     for (;;) {
         const int gn = g + nslots;
-        GroupLoad nxt;
-        if (kPrefetch && gn < G) load_group(nxt, src, gn, col, colok);
-        group_step<MAXM>(cur, xs, sums, xrow, g, K8, G, M, 4 * (col & 7), mlo, mhi, acc);
+        GroupLoad<BITS> nxt;
+        if (kPrefetch && gn < G) load_group<BITS>(nxt, src, gn, col, colok);
+        group_step<BITS, MAXM>(cur, xs, sums, xrow, g, K8, G, M, zero_shift<BITS>(col), mk, acc);
         if (gn >= G) break;
-        if (!kPrefetch) load_group(nxt, src, gn, col, colok);
+        if (!kPrefetch) load_group<BITS>(nxt, src, gn, col, colok);
         cur = nxt;
         g = gn;
     }
@@ -432,15 +605,16 @@ SMOE_DEV void write_slot_desc(const W4Args& a, const smoe_w4_expert& spec, int s
 // sums, then the slots' partial sums.
 struct W4Lds {
     uint4* xs;     // [XR][K8]
-    float2* sums;  // [XR][G]
+    float4* sums;  // [XR][G] per-class activation sums of each pseudo-group
     float* red;    // [nslots][MAXM][NB]
 };
 
+template <int BITS>
 SMOE_DEV W4Lds carve_lds(uint4* smem, const W4Args& a) {
-    const int K8 = a.K >> 3, G = a.K >> 7;
+    const int K8 = a.K >> 3, G = a.K / QF<BITS>::kK;
     W4Lds l;
     l.xs = smem;
-    l.sums = reinterpret_cast<float2*>(smem + (size_t)a.XR * K8);
+    l.sums = reinterpret_cast<float4*>(smem + (size_t)a.XR * K8);
     l.red = reinterpret_cast<float*>(l.sums + (size_t)a.XR * G);
     return l;
 }
@@ -459,11 +633,12 @@ SMOE_DEV int lane_column(const W4Args& a, int cb, int q) {
 // read group G - 1 and whose contribution is dropped).
 SMOE_DEV int clamp_group(int g, int G) { return g < G ? g : G - 1; }
 
-SMOE_DEV void step_if(const GroupLoad& L, const W4Lds& l, int g, int G, int K8, int zsh,
-                      uint32_t mlo, uint32_t mhi, float (&acc)[1][4]) {
+template <int BITS>
+SMOE_DEV void step_if(const GroupLoad<BITS>& L, const W4Lds& l, int g, int G, int K8, int zsh,
+                      const Masks<BITS>& mk, float (&acc)[1][4]) {
     float t[1][4] = {{0.0f, 0.0f, 0.0f, 0.0f}};
     const int xrow[1] = {0};
-    group_step<1>(L, l.xs, l.sums, xrow, clamp_group(g, G), K8, G, 1, zsh, mlo, mhi, t);
+    group_step<BITS, 1>(L, l.xs, l.sums, xrow, clamp_group(g, G), K8, G, 1, zsh, mk, t);
     const bool valid = g < G;
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[0][c] += valid ? t[0][c] : 0.0f;
@@ -475,7 +650,7 @@ SMOE_DEV void step_if(const GroupLoad& L, const W4Lds& l, int g, int G, int K8, 
 // buffers in straight-line code: the first two are requested before the row
 // is permuted into LDS, and buffer A is refilled as soon as it has been
 // consumed, so every wait is for one group while the next is in flight.
-template <int PHASE, int LPR, int NG>
+template <int BITS, int PHASE, int LPR, int NG>
 SMOE_DEV void one_token_block(const W4Args& a, const W4Lds& l, const smoe_w4_mat& wm,
                               const uint4 (&xv)[kRowChunksPerThread], int slot, int cb) {
     static_assert(NG >= 1 && NG <= 4, "groups per slot");
@@ -487,22 +662,21 @@ SMOE_DEV void one_token_block(const W4Args& a, const W4Lds& l, const smoe_w4_mat
     const int myslot = (tid >> 6) * RPL + lane / LPR;
     const int q = lane % LPR;
     const int K = a.K, N = a.N;
-    const int G = K >> 7;
+    const int G = K / QF<BITS>::kK;
     const int K8 = K >> 3;
     const int col = lane_column<PHASE, LPR>(a, cb, q);
     const bool colok = col < N;
-    const int zsh = 4 * (col & 7);
-    const uint32_t mlo = vgpr_const_lo();
-    const uint32_t mhi = vgpr_const_hi();
+    const int zsh = zero_shift<BITS>(col);
+    const Masks<BITS> mk;
     if (!wm.qweight || !wm.scales || !wm.qzeros) {
         if (tid == 0 && cb == 0) flag_error(a.err, SMOE_DERR_NULL_EXPERT);
         return;
     }
-    const W4Src src = make_src(wm, K, N);
+    const W4Src src = make_src<BITS>(wm, K, N);
     const int g0 = myslot;
-    GroupLoad A, B;
-    load_group(A, src, clamp_group(g0, G), col, colok);
-    if (NG >= 2) load_group(B, src, clamp_group(g0 + nslots, G), col, colok);
+    GroupLoad<BITS> A, B;
+    load_group<BITS>(A, src, clamp_group(g0, G), col, colok);
+    if (NG >= 2) load_group<BITS>(B, src, clamp_group(g0 + nslots, G), col, colok);
     __builtin_amdgcn_sched_barrier(0);  // every request above is issued before the row is staged
     // straight-line stores (indexes past the row rewrite its last chunk with
     // the same value), so the wait for the row leaves the weights in flight;
@@ -510,29 +684,16 @@ SMOE_DEV void one_token_block(const W4Args& a, const W4Lds& l, const smoe_w4_mat
 #pragma unroll
     for (int u = 0; u < kRowChunksPerThread; ++u) {
         const int idx = tid + u * (int)blockDim.x;
-        l.xs[idx < K8 ? idx : K8 - 1] = pair_permute(xv[u]);
+        l.xs[idx < K8 ? idx : K8 - 1] = permute_chunk<BITS>(xv[u]);
     }
-    __syncthreads();
-    for (int gg = tid; gg < G; gg += blockDim.x) {
-        const uint4* xr = l.xs + gg * kRowsPerGroup;
-        float se = 0.0f, so = 0.0f;
-#pragma unroll 4
-        for (int i = 0; i < kRowsPerGroup; ++i) {
-            const uint4 p = xr[i];
-            const h2_t x04 = as_h2(p.x), x15 = as_h2(p.y), x26 = as_h2(p.z), x37 = as_h2(p.w);
-            se += ((float)x04.x + (float)x04.y) + ((float)x26.x + (float)x26.y);
-            so += ((float)x15.x + (float)x15.y) + ((float)x37.x + (float)x37.y);
-        }
-        l.sums[gg] = make_float2(se, so);
-    }
-    __syncthreads();
+    finish_rows<BITS>(l.xs, l.sums, 1, K8, G);
     float acc[1][4] = {{0.0f, 0.0f, 0.0f, 0.0f}};
-    step_if(A, l, g0, G, K8, zsh, mlo, mhi, acc);
-    if (NG >= 3) load_group(A, src, clamp_group(g0 + 2 * nslots, G), col, colok);
-    if (NG >= 2) step_if(B, l, g0 + nslots, G, K8, zsh, mlo, mhi, acc);
-    if (NG >= 4) load_group(B, src, clamp_group(g0 + 3 * nslots, G), col, colok);
-    if (NG >= 3) step_if(A, l, g0 + 2 * nslots, G, K8, zsh, mlo, mhi, acc);
-    if (NG >= 4) step_if(B, l, g0 + 3 * nslots, G, K8, zsh, mlo, mhi, acc);
+    step_if<BITS>(A, l, g0, G, K8, zsh, mk, acc);
+    if (NG >= 3) load_group<BITS>(A, src, clamp_group(g0 + 2 * nslots, G), col, colok);
+    if (NG >= 2) step_if<BITS>(B, l, g0 + nslots, G, K8, zsh, mk, acc);
+    if (NG >= 4) load_group<BITS>(B, src, clamp_group(g0 + 3 * nslots, G), col, colok);
+    if (NG >= 3) step_if<BITS>(A, l, g0 + 2 * nslots, G, K8, zsh, mk, acc);
+    if (NG >= 4) step_if<BITS>(B, l, g0 + 3 * nslots, G, K8, zsh, mk, acc);
     reduce_store<PHASE, 1, NB>(a, l.red, acc, myslot, nslots, q, cb, slot, 1);
 }
 
@@ -553,7 +714,7 @@ SMOE_DEV void request_row(const uint4* row4, int K8, uint4 (&xv)[kRowChunksPerTh
 template <int MAXM, int NG>
 constexpr int w4_waves_per_eu() { return (MAXM == 1 && NG == 1) ? 4 : 2; }
 
-template <int PHASE, int LPR, int MAXM, int NG>
+template <int BITS, int PHASE, int LPR, int MAXM, int NG>
 __global__ __launch_bounds__(64 * (MAXM == 1 ? kT1MaxWaves : kMaxWaves))
 __attribute__((amdgpu_waves_per_eu(w4_waves_per_eu<MAXM, NG>()))) void w4_kernel(W4Args a) {
     constexpr int RPL = 64 / LPR;  // lane groups (slots) per wave
@@ -569,19 +730,17 @@ __attribute__((amdgpu_waves_per_eu(w4_waves_per_eu<MAXM, NG>()))) void w4_kernel
     const int cb = blockIdx.x % a.nCB;
     const int slot = blockIdx.x / a.nCB;
     const int K = a.K, N = a.N;
-    const int G = K >> 7;
+    const int G = K / QF<BITS>::kK;
     const int K8 = K >> 3;
-    const W4Lds l = carve_lds(smem, a);
+    const W4Lds l = carve_lds<BITS>(smem, a);
     uint4* xs = l.xs;
-    float2* sums = l.sums;
+    float4* sums = l.sums;
     float* red = l.red;
 
     const int nslots = nwaves * RPL;
     const int myslot = wave * RPL + rho;
     const int col = lane_column<PHASE, LPR>(a, cb, q);
     const bool colok = col < N;
-    const uint32_t mlo = vgpr_const_lo();
-    const uint32_t mhi = vgpr_const_hi();
 
     if constexpr (MAXM == 1) {
         // One token (T = 1): every pair's token is 0, and the touched experts
@@ -603,12 +762,12 @@ __attribute__((amdgpu_waves_per_eu(w4_waves_per_eu<MAXM, NG>()))) void w4_kernel
             }
             if (cb == 0) write_slot_desc(a, spec, slot, e);
             if (e < 0) return;
-            one_token_block<1, LPR, NG>(a, l, pick_mat<1>(a, spec, e), xv, slot, cb);
+            one_token_block<BITS, 1, LPR, NG>(a, l, pick_mat<1>(a, spec, e), xv, slot, cb);
         } else {
             const SlotDesc d = a.desc[slot];
             request_row(row4, K8, xv);
             if (d.e < 0) return;
-            one_token_block<2, LPR, NG>(a, l, d.w2, xv, slot, cb);
+            one_token_block<BITS, 2, LPR, NG>(a, l, d.w2, xv, slot, cb);
         }
         return;
     } else {
@@ -621,12 +780,13 @@ __attribute__((amdgpu_waves_per_eu(w4_waves_per_eu<MAXM, NG>()))) void w4_kernel
             if (tid == 0 && cb == 0) flag_error(a.err, SMOE_DERR_NULL_EXPERT);
             return;
         }
-        const W4Src src = make_src(wm, K, N);
+        const W4Src src = make_src<BITS>(wm, K, N);
+        const Masks<BITS> mk;
         // The gate/up projection with every token fitting in LDS stages all
         // T activation rows once.
         const bool direct = (PHASE == 1) && a.direct;
         if (direct)
-            stage_rows(xs, sums, a.T, K8, G, [&](int j) {
+            stage_rows<BITS>(xs, sums, a.T, K8, G, [&](int j) {
                 return reinterpret_cast<const uint4*>(a.xin + (size_t)j * K);
             });
         for (int mc = r0; mc < r1; mc += a.MCH) {
@@ -637,25 +797,25 @@ __attribute__((amdgpu_waves_per_eu(w4_waves_per_eu<MAXM, NG>()))) void w4_kernel
                 xrow[m] = direct ? a.sorted_token[mc + (m < M ? m : 0)] : m;
             if (!direct) {
                 if (PHASE == 1)
-                    stage_rows(xs, sums, M, K8, G, [&](int j) {
+                    stage_rows<BITS>(xs, sums, M, K8, G, [&](int j) {
                         return reinterpret_cast<const uint4*>(a.xin +
                                                               (size_t)a.sorted_token[mc + j] * K);
                     });
                 else
-                    stage_rows(xs, sums, M, K8, G, [&](int j) {
+                    stage_rows<BITS>(xs, sums, M, K8, G, [&](int j) {
                         return reinterpret_cast<const uint4*>(a.xin + (size_t)(mc + j) * K);
                     });
             }
-            GroupLoad cur;
+            GroupLoad<BITS> cur;
             const int g = myslot;
-            if (g < G) load_group(cur, src, g, col, colok);
+            if (g < G) load_group<BITS>(cur, src, g, col, colok);
             float acc[MAXM][4];
 #pragma unroll
             for (int m = 0; m < MAXM; ++m)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) acc[m][c] = 0.0f;
-            run_groups<false, MAXM>(cur, g, nslots, G, src, col, colok, xs, sums, xrow, K8, M, mlo,
-                                    mhi, acc);
+            run_groups<BITS, false, MAXM>(cur, g, nslots, G, src, col, colok, xs, sums, xrow, K8,
+                                          M, mk, acc);
             reduce_store<PHASE, MAXM, NB>(a, red, acc, myslot, nslots, q, cb, mc, M);
         }
     }
@@ -731,8 +891,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void route_w4_kernel(W4Args a, RouteArgs
     if (e >= 0) {
         uint4 xv[kRowChunksPerThread];
         request_row(reinterpret_cast<const uint4*>(a.xin), a.K >> 3, xv);
-        one_token_block<1, LPR, NG>(a, carve_lds(smem, a), pick_mat<1>(a, spec, e), xv, slot,
-                                    cb);
+        one_token_block<4, 1, LPR, NG>(a, carve_lds<4>(smem, a), pick_mat<1>(a, spec, e), xv,
+                                       slot, cb);
     }
     // 5. workgroup 0: routing outputs (the routing kernels' own routine), the
     //    ELB increments and the maps
@@ -767,7 +927,10 @@ struct PhasePlan {
     size_t lds;
 };
 
-PhasePlan plan_phase(int phase, int slots, int T, int K, int N, int I, int maxm) {
+// K per pseudo-group of a code width (QF<BITS>::kK).
+int pseudo_group_k(int bits) { return bits == 8 ? 64 : 128; }
+
+PhasePlan plan_phase(int phase, int slots, int T, int K, int N, int I, int maxm, int bits) {
     // LPR 16 (64-column blocks, 256-byte row runs) when that still gives
     // SMOE_W4_MIN_WG workgroups and no slot walks more than
     // SMOE_W4_MAX_GROUPS_PER_SLOT groups in sequence; else LPR 8 (32 columns,
@@ -775,7 +938,7 @@ PhasePlan plan_phase(int phase, int slots, int T, int K, int N, int I, int maxm)
     // and 4096, I 1408 and 6400, one to sixteen rows per expert).
     PhasePlan p{};
     const int cols16 = (phase == 1) ? I / 32 : (N + 63) / 64;
-    const int G16 = K / 128;
+    const int G16 = K / pseudo_group_k(bits);
     const int maxw = (maxm == 1) ? kT1MaxWaves : kMaxWaves;
     const int min_wg = (maxm == 1) ? kT1MinWG : SMOE_W4_MIN_WG;
     const int serial16 = (G16 + 4 * maxw - 1) / (4 * maxw);
@@ -784,7 +947,7 @@ PhasePlan plan_phase(int phase, int slots, int T, int K, int N, int I, int maxm)
     const int NB = 4 * p.lpr;
     p.nCB = (phase == 1) ? I / (NB / 2) : (N + NB - 1) / NB;
     const int rpl = 64 / p.lpr;
-    const int G = K / 128;
+    const int G = K / pseudo_group_k(bits);
     p.waves = (G + rpl - 1) / rpl;
     // the launch bound caps every kernel at kMaxWaves; the multi-row kernels'
     // register budget at 4
@@ -796,7 +959,7 @@ PhasePlan plan_phase(int phase, int slots, int T, int K, int N, int I, int maxm)
         if (p.waves < need) p.waves = need;
     }
     if (p.waves < 1) p.waves = 1;
-    const size_t row_bytes = (size_t)K * 2 + (size_t)G * 8;  // pairs + group sums
+    const size_t row_bytes = (size_t)K * 2 + (size_t)G * 16;  // pairs + per-class sums
     int cap = (int)(kLdsBytes / row_bytes);
     if (cap < 1) cap = 1;
     p.mch = cap < maxm ? cap : maxm;
@@ -808,41 +971,48 @@ PhasePlan plan_phase(int phase, int slots, int T, int K, int N, int I, int maxm)
     return p;
 }
 
-template <int PHASE, int LPR, int NG>
+template <int BITS, int PHASE, int LPR, int NG>
 hipError_t launch_one_token(const W4Args& a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
-    hipLaunchKernelGGL((w4_kernel<PHASE, LPR, 1, NG>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((w4_kernel<BITS, PHASE, LPR, 1, NG>), grid, block, lds, s, a);
     return hipGetLastError();
 }
 
-template <int PHASE, int LPR>
+template <int BITS, int PHASE, int LPR>
 hipError_t launch_one_token_ng(const W4Args& a, dim3 grid, dim3 block, const PhasePlan& p,
                                hipStream_t s) {
     switch (p.ng) {
-        case 1: return launch_one_token<PHASE, LPR, 1>(a, grid, block, p.lds, s);
-        case 2: return launch_one_token<PHASE, LPR, 2>(a, grid, block, p.lds, s);
-        case 3: return launch_one_token<PHASE, LPR, 3>(a, grid, block, p.lds, s);
-        case 4: return launch_one_token<PHASE, LPR, 4>(a, grid, block, p.lds, s);
-        default: return hipErrorInvalidValue;  // excluded by w4a16_shape_supported
+        case 1: return launch_one_token<BITS, PHASE, LPR, 1>(a, grid, block, p.lds, s);
+        case 2: return launch_one_token<BITS, PHASE, LPR, 2>(a, grid, block, p.lds, s);
+        case 3: return launch_one_token<BITS, PHASE, LPR, 3>(a, grid, block, p.lds, s);
+        case 4: return launch_one_token<BITS, PHASE, LPR, 4>(a, grid, block, p.lds, s);
+        default: return hipErrorInvalidValue;  // the caller falls back to the multi-row kernel
     }
 }
 
-template <int PHASE, int MAXM>
+template <int BITS, int PHASE, int MAXM>
 hipError_t launch_phase(const W4Args& a, int slots, const PhasePlan& p, hipStream_t s) {
     const dim3 grid(slots * p.nCB), block(64 * p.waves);
     if (MAXM == 1)
-        return (p.lpr == 16) ? launch_one_token_ng<PHASE, 16>(a, grid, block, p, s)
-                             : launch_one_token_ng<PHASE, 8>(a, grid, block, p, s);
+        return (p.lpr == 16) ? launch_one_token_ng<BITS, PHASE, 16>(a, grid, block, p, s)
+                             : launch_one_token_ng<BITS, PHASE, 8>(a, grid, block, p, s);
     if (p.lpr == 16)
-        hipLaunchKernelGGL((w4_kernel<PHASE, 16, MAXM, 1>), grid, block, p.lds, s, a);
+        hipLaunchKernelGGL((w4_kernel<BITS, PHASE, 16, MAXM, 1>), grid, block, p.lds, s, a);
     else
-        hipLaunchKernelGGL((w4_kernel<PHASE, 8, MAXM, 1>), grid, block, p.lds, s, a);
+        hipLaunchKernelGGL((w4_kernel<BITS, PHASE, 8, MAXM, 1>), grid, block, p.lds, s, a);
     return hipGetLastError();
 }
 
 template <int PHASE>
-hipError_t launch_any(const W4Args& a, int slots, const PhasePlan& p, int maxm, hipStream_t s) {
-    return (maxm == 1) ? launch_phase<PHASE, 1>(a, slots, p, s)
-                       : launch_phase<PHASE, 4>(a, slots, p, s);
+hipError_t launch_any(const W4Args& a, int slots, const PhasePlan& p, int maxm, int bits,
+                      hipStream_t s) {
+    if (bits == 2)
+        return (maxm == 1) ? launch_phase<2, PHASE, 1>(a, slots, p, s)
+                           : launch_phase<2, PHASE, 4>(a, slots, p, s);
+    if (bits == 8)
+        return (maxm == 1) ? launch_phase<8, PHASE, 1>(a, slots, p, s)
+                           : launch_phase<8, PHASE, 4>(a, slots, p, s);
+    return (maxm == 1) ? launch_phase<4, PHASE, 1>(a, slots, p, s)
+                       : launch_phase<4, PHASE, 4>(a, slots, p, s);
 }
 
 }  // namespace
@@ -895,21 +1065,28 @@ W4Args phase_args(const PhasePlan& p, const uint16_t* xin, const int32_t* sorted
 hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, const int32_t* off,
                             const int32_t* active, const int32_t* n_active,
                             const smoe_w4_expert* experts, int T, int k, int H, int I, int E,
-                            uint16_t* y, void* ws, int32_t* err, hipStream_t s) {
+                            int bits, uint16_t* y, void* ws, int32_t* err, hipStream_t s) {
     const int rows = T * k;
     const int slots = E < rows ? E : rows;
-    const int maxm = (T == 1) ? 1 : 4;  // an expert holds at most T rows
+    // an expert holds at most T rows; one-token kernels unless a slot would
+    // walk more than four pseudo-groups (long 8-bit reductions)
+    int maxm = (T == 1) ? 1 : 4;
+    PhasePlan p1 = plan_phase(1, slots, T, H, 2 * I, I, maxm, bits);
+    PhasePlan p2 = plan_phase(2, slots, T, I, H, I, maxm, bits);
+    if (maxm == 1 && (p1.ng > 4 || p2.ng > 4)) {
+        maxm = 4;
+        p1 = plan_phase(1, slots, T, H, 2 * I, I, maxm, bits);
+        p2 = plan_phase(2, slots, T, I, H, I, maxm, bits);
+    }
     uint16_t* h = static_cast<uint16_t*>(ws);
     SlotDesc* desc = reinterpret_cast<SlotDesc*>(static_cast<char*>(ws) + h_bytes(T, k, I));
-    const PhasePlan p1 = plan_phase(1, slots, T, H, 2 * I, I, maxm);
     const W4Args a1 = phase_args(p1, x, sorted_token, off, active, n_active, experts, H, 2 * I, I,
                                  T, E, h, err, desc);
-    hipError_t st = launch_any<1>(a1, slots, p1, maxm, s);
+    hipError_t st = launch_any<1>(a1, slots, p1, maxm, bits, s);
     if (st != hipSuccess) return st;
-    const PhasePlan p2 = plan_phase(2, slots, T, I, H, I, maxm);
     const W4Args a2 =
         phase_args(p2, h, nullptr, off, active, n_active, experts, I, H, I, T, E, y, err, desc);
-    return launch_any<2>(a2, slots, p2, maxm, s);
+    return launch_any<2>(a2, slots, p2, maxm, bits, s);
 }
 
 bool draft_route_ffn_supported(int E, int k) { return E <= 256 && k <= kFusedMaxK; }
@@ -922,7 +1099,7 @@ hipError_t launch_draft_route_ffn(const uint16_t* x, const uint16_t* wr, const u
                                   int32_t* err, hipStream_t s) {
     uint16_t* h = static_cast<uint16_t*>(ws);
     SlotDesc* desc = reinterpret_cast<SlotDesc*>(static_cast<char*>(ws) + h_bytes(1, k, I));
-    const PhasePlan p1 = plan_phase(1, k, 1, H, 2 * I, I, 1);
+    const PhasePlan p1 = plan_phase(1, k, 1, H, 2 * I, I, 1, 4);
     const W4Args a1 = phase_args(p1, x, st, off, active, n_active, experts, H, 2 * I, I, 1, E, h,
                                  err, desc);
     RouteArgs r{wr, wsg, k, renorm, counters_row, ids, w, gate, off, st, sp, pp, active, n_active};
@@ -943,9 +1120,9 @@ hipError_t launch_draft_route_ffn(const uint16_t* x, const uint16_t* wr, const u
 #undef SMOE_ROUTE_W4
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const PhasePlan p2 = plan_phase(2, k, 1, I, H, I, 1);
+    const PhasePlan p2 = plan_phase(2, k, 1, I, H, I, 1, 4);
     const W4Args a2 = phase_args(p2, h, nullptr, off, active, n_active, experts, I, H, I, 1, E, y,
                                  err, desc);
-    return launch_any<2>(a2, k, p2, 1, s);
+    return launch_any<2>(a2, k, p2, 1, 4, s);
 }
 }  // namespace smoe

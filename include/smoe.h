@@ -214,6 +214,30 @@ smoe_status w4a16_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
                               void* stream);
 
 /* ------------------------------------------------------------------------
+ * wq_grouped_ffn -- w4a16_grouped_ffn for other draft code widths ([S1] Main
+ * Findings and Future Directions: the draft's fidelity is compared across
+ * quantisation precisions, 2-, 4- and 8-bit, and the precision is a design
+ * lever).  The experts are in the GPTQ layout of the same group size (128)
+ * with `bits`-bit codes:
+ *   qweight int32 [K*bits/32, N]  code i (bits bits*i .. bits*i+bits-1) of
+ *                                 word [r, n] is row (32/bits)*r + i of
+ *                                 column n;
+ *   scales  fp16  [K/128, N];
+ *   qzeros  int32 [K/128, N*bits/32]  code i of word [g, c] is the zero of
+ *                                 column (32/bits)*c + i in group g;
+ *   W[kk, n] = (q[kk, n] - z[kk/128, n]) * s[kk/128, n].
+ * smoe_w4_expert/smoe_w4_mat hold the three pointers whatever the width.
+ * Arguments, outputs and workspace are those of w4a16_grouped_ffn; bits is
+ * 2, 4 or 8 (else SMOE_ERR_UNSUPPORTED), and bits == 4 is w4a16_grouped_ffn.
+ * ---------------------------------------------------------------------- */
+smoe_status wq_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
+                           const int32_t* expert_offsets, const int32_t* active,
+                           const int32_t* n_active, const smoe_w4_expert* experts, int T, int k,
+                           int H, int I, int E, int bits, int group_size, uint16_t* y_sorted,
+                           void* workspace, size_t workspace_bytes, int32_t* err_word,
+                           void* stream);
+
+/* ------------------------------------------------------------------------
  * moe_draft_route_ffn -- one-token (T = 1) draft step of a layer: the work
  * of moe_route_plan followed by w4a16_grouped_ffn, in two launches instead of
  * three ([S1] Key Contributions 4: routing, gathering and the experts' FFN of

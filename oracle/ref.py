@@ -13,6 +13,9 @@ Sources (the pages; cited by title and section):
        Methodology in Plain English.
   [S2] "Specter previews expert routing with an INT4 copy of the model
        itself": What shipped.
+  [S1] also, Main Findings and Future Directions: the draft's routing
+       fidelity is compared across 2-, 4- and 8-bit precisions (the 2/8-bit
+       draft FFN here).
 
 Readings taken where the pages are silent are named R1..R12 in each
 docstring; the design notes list all of them.
@@ -23,7 +26,8 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
   elb_update ....................... pinned (library bincount, sums)
   gather_maps ...................... pinned (permutation/inverse invariants,
                                      library stable argsort)
-  dequant_gptq ..................... pinned (hand-packed closed forms)
+  dequant_gptq ..................... pinned (hand-packed closed forms, 2/4/8-bit
+                                     codes)
   expert_ffn / grouped_ffn ......... pinned (textbook dense MLP at E=1,
                                      zero weights, masked brute force,
                                      shared-expert concatenation identity)
@@ -240,35 +244,42 @@ def gather_maps(ids: np.ndarray, E: int) -> Dict[str, np.ndarray]:
 # S4 / S6  expert FFNs
 # ---------------------------------------------------------------------------
 
-def unpack_gptq(qweight: np.ndarray, qzeros: np.ndarray):
+def unpack_gptq(qweight: np.ndarray, qzeros: np.ndarray, bits: int = 4):
     """Codes q [K, N] and zeros z [K/128, N] (uint8) from the GPTQ words.
 
     [S2 What shipped] the draft's routed experts are GPTQ INT4 with group
     size 128.  R8 (the usual GPTQ checkpoint layout): nibble i, bits 4i..4i+3,
     of qweight[r, n] is row 8r+i of column n; nibble i of qzeros[g, c] is the
     zero of column 8c+i in group g; zeros carry no offset; no act-order.
+    R21: the 2- and 8-bit drafts ([S1] Main Findings) use the same layout
+    with c = 32/bits codes per word: code i (bits bits*i ...) of qweight[r, n]
+    is row c*r+i, code i of qzeros[g, w] the zero of column c*w+i.
     """
+    assert bits in (2, 4, 8)
+    per = 32 // bits
+    mask = np.uint32((1 << bits) - 1)
     qw = np.asarray(qweight).view(np.uint32)
     R, N = qw.shape
-    q = np.empty((R * 8, N), dtype=np.uint8)
-    for i in range(8):
-        q[i::8, :] = (qw >> np.uint32(4 * i)) & np.uint32(0xF)
+    q = np.empty((R * per, N), dtype=np.uint8)
+    for i in range(per):
+        q[i::per, :] = (qw >> np.uint32(bits * i)) & mask
     qz = np.asarray(qzeros).view(np.uint32)
     G, C = qz.shape
-    z = np.empty((G, C * 8), dtype=np.uint8)
-    for i in range(8):
-        z[:, i::8] = (qz >> np.uint32(4 * i)) & np.uint32(0xF)
+    z = np.empty((G, C * per), dtype=np.uint8)
+    for i in range(per):
+        z[:, i::per] = (qz >> np.uint32(bits * i)) & mask
     return q, z
 
 
-def dequant_gptq(qweight, scales, qzeros, dtype=np.float64) -> np.ndarray:
+def dequant_gptq(qweight, scales, qzeros, dtype=np.float64, bits: int = 4) -> np.ndarray:
     """W[kk, n] = (q[kk, n] - z[kk // 128, n]) * s[kk // 128, n]  ([K, N]).
 
     [S2 What shipped] INT4 weight tiles are dequantised and the product is
     formed in higher precision.  In fp32 the result is exact: (q - z) lies in
-    [-15, 15] and s has an 11-bit significand.
+    [-(2^bits - 1), 2^bits - 1] (at most 9 significant bits) and s has an
+    11-bit significand.
     """
-    q, z = unpack_gptq(qweight, qzeros)
+    q, z = unpack_gptq(qweight, qzeros, bits)
     s = np.asarray(scales).astype(dtype)
     g = np.arange(q.shape[0]) // GROUP
     return (q.astype(dtype) - z[g, :].astype(dtype)) * s[g, :]
@@ -301,14 +312,18 @@ def expert_ffn_f16(xr: np.ndarray, w13: np.ndarray, w2: np.ndarray, dtype=np.flo
     return swiglu_ffn(a, w13f[:I].T, w13f[I:].T, w2.astype(dtype).T)
 
 
-def expert_ffn_int4(xr: np.ndarray, q13, q2, dtype=np.float64):
-    """INT4 draft expert on rows xr; q13/q2 = (qweight, scales, qzeros) of
-    w13^T [H, 2I] and w2^T [I, H] (GPTQ [K, N] layout)."""
-    W13 = dequant_gptq(*q13, dtype=dtype)        # [H, 2I]
-    W2 = dequant_gptq(*q2, dtype=dtype)          # [I, H]
+def expert_ffn_int4(xr: np.ndarray, q13, q2, dtype=np.float64, bits: int = 4):
+    """INT4 (or, with bits, 2/8-bit) draft expert on rows xr; q13/q2 =
+    (qweight, scales, qzeros) of w13^T [H, 2I] and w2^T [I, H] (GPTQ [K, N]
+    layout)."""
+    W13 = dequant_gptq(*q13, dtype=dtype, bits=bits)   # [H, 2I]
+    W2 = dequant_gptq(*q2, dtype=dtype, bits=bits)     # [I, H]
     I = W2.shape[0]
     a = np.asarray(xr).astype(dtype)
     return swiglu_ffn(a, W13[:, :I], W13[:, I:], W2)
+
+
+_QBITS = {"int2": 2, "int4": 4, "int8": 8}
 
 
 def grouped_ffn(x: np.ndarray, maps: Dict[str, np.ndarray], experts: Sequence, kind: str,
@@ -318,8 +333,9 @@ def grouped_ffn(x: np.ndarray, maps: Dict[str, np.ndarray], experts: Sequence, k
     [S1 Key Contributions 4; Methodology] tokens routed to one expert are
     packed and that expert is applied to all of them at once.  Row r of the
     result holds FFN_e(x[sorted_token[r]]) for the expert e owning row r.
-    `kind` is "int4" (experts[e] = dict(w13=(qw,s,qz), w2=(...))) or "f16"
-    (experts[e] = (w13, w2)).  Rows of experts outside `only` stay NaN.
+    `kind` is "int4" (experts[e] = dict(w13=(qw,s,qz), w2=(...))), "int2" /
+    "int8" (the same with 2/8-bit codes) or "f16" (experts[e] = (w13, w2)).
+    Rows of experts outside `only` stay NaN.
     """
     off = maps["offsets"]
     st = maps["sorted_token"]
@@ -332,8 +348,9 @@ def grouped_ffn(x: np.ndarray, maps: Dict[str, np.ndarray], experts: Sequence, k
         if r1 == r0 or (only is not None and e not in only):
             continue
         xr = x[st[r0:r1]]
-        if kind == "int4":
-            y[r0:r1] = expert_ffn_int4(xr, experts[e]["w13"], experts[e]["w2"], dtype)
+        if kind in _QBITS:
+            y[r0:r1] = expert_ffn_int4(xr, experts[e]["w13"], experts[e]["w2"], dtype,
+                                       bits=_QBITS[kind])
         else:
             y[r0:r1] = expert_ffn_f16(xr, experts[e][0], experts[e][1], dtype)
     return y
@@ -354,8 +371,9 @@ def per_token_ffn(x: np.ndarray, ids: np.ndarray, experts: Sequence, kind: str,
         for j in range(k):
             e = int(ids[t, j])
             xr = x[t:t + 1]
-            if kind == "int4":
-                out[t, j] = expert_ffn_int4(xr, experts[e]["w13"], experts[e]["w2"], dtype)[0]
+            if kind in _QBITS:
+                out[t, j] = expert_ffn_int4(xr, experts[e]["w13"], experts[e]["w2"], dtype,
+                                            bits=_QBITS[kind])[0]
             else:
                 out[t, j] = expert_ffn_f16(xr, experts[e][0], experts[e][1], dtype)[0]
     return out

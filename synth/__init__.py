@@ -113,45 +113,48 @@ def normal_f16(key: Sequence[int], shape, std: float) -> np.ndarray:
 # (zeros stored as-is, no "-1" offset; no act-order permutation.)
 # ---------------------------------------------------------------------------
 
-def rtn_quantize(w_kn: np.ndarray):
+def rtn_quantize(w_kn: np.ndarray, bits: int = 4):
     """Quantise a fp16 [K, N] matrix per (group of 128 rows, column).
 
-    Returns (q uint8 [K, N] in 0..15, scales fp16 [K/128, N], zeros uint8
-    [K/128, N]) with W ~= (q - z) * s.
+    Returns (q uint8 [K, N] in 0..2^bits-1, scales fp16 [K/128, N], zeros
+    uint8 [K/128, N]) with W ~= (q - z) * s.
     """
     K, N = w_kn.shape
     assert K % GROUP == 0
+    qmax = float((1 << bits) - 1)
     w = w_kn.astype(np.float32).reshape(K // GROUP, GROUP, N)
     lo = np.minimum(w.min(axis=1), np.float32(0))
     hi = np.maximum(w.max(axis=1), np.float32(0))
-    s16 = ((hi - lo) / np.float32(15)).astype(np.float16)
+    s16 = ((hi - lo) / np.float32(qmax)).astype(np.float16)
     s16 = np.where(hi == lo, np.float16(1), s16)
     s16 = np.where(s16 == 0, np.float16(1), s16)  # spans below fp16's range
     s = s16.astype(np.float32)
-    z = np.clip(np.rint(-lo / s), 0, 15).astype(np.float32)
-    q = np.clip(np.rint(w / s[:, None, :]) + z[:, None, :], 0, 15).astype(np.uint8)
+    z = np.clip(np.rint(-lo / s), 0, qmax).astype(np.float32)
+    q = np.clip(np.rint(w / s[:, None, :]) + z[:, None, :], 0, qmax).astype(np.uint8)
     return q.reshape(K, N), s16, z.astype(np.uint8)
 
 
-def pack_gptq(q: np.ndarray, s16: np.ndarray, z: np.ndarray):
-    """Pack 4-bit codes and zeros into the GPTQ int32 layout."""
+def pack_gptq(q: np.ndarray, s16: np.ndarray, z: np.ndarray, bits: int = 4):
+    """Pack bits-bit codes and zeros into the GPTQ int32 layout (32/bits codes
+    per word along K for the codes, along N for the zeros)."""
+    per = 32 // bits
     K, N = q.shape
-    q32 = q.astype(np.uint32).reshape(K // 8, 8, N)
-    qweight = np.zeros((K // 8, N), dtype=np.uint32)
-    for i in range(8):
-        qweight |= q32[:, i, :] << np.uint32(4 * i)
+    q32 = q.astype(np.uint32).reshape(K // per, per, N)
+    qweight = np.zeros((K // per, N), dtype=np.uint32)
+    for i in range(per):
+        qweight |= q32[:, i, :] << np.uint32(bits * i)
     G = z.shape[0]
-    z32 = z.astype(np.uint32).reshape(G, N // 8, 8)
-    qzeros = np.zeros((G, N // 8), dtype=np.uint32)
-    for i in range(8):
-        qzeros |= z32[:, :, i] << np.uint32(4 * i)
+    z32 = z.astype(np.uint32).reshape(G, N // per, per)
+    qzeros = np.zeros((G, N // per), dtype=np.uint32)
+    for i in range(per):
+        qzeros |= z32[:, :, i] << np.uint32(bits * i)
     return qweight.view(np.int32), np.ascontiguousarray(s16), qzeros.view(np.int32)
 
 
-def gptq_from_linear(w_nk: np.ndarray):
-    """GPTQ INT4 tensors for an nn.Linear-layout fp16 weight [N, K]."""
-    q, s, z = rtn_quantize(np.ascontiguousarray(w_nk.T))
-    return pack_gptq(q, s, z)
+def gptq_from_linear(w_nk: np.ndarray, bits: int = 4):
+    """GPTQ tensors (bits-bit codes) for an nn.Linear-layout fp16 weight [N, K]."""
+    q, s, z = rtn_quantize(np.ascontiguousarray(w_nk.T), bits)
+    return pack_gptq(q, s, z, bits)
 
 
 # ---------------------------------------------------------------------------
@@ -178,9 +181,18 @@ def expert_f16(shape: LayerShape, layer: int, expert: int, seed: int = BASE_SEED
     return w13, w2
 
 
-def expert_int4(w13: np.ndarray, w2: np.ndarray):
-    """Draft expert: GPTQ INT4 g128 of the target's w13 and w2."""
-    return dict(w13=gptq_from_linear(w13), w2=gptq_from_linear(w2))
+def expert_int4(w13: np.ndarray, w2: np.ndarray, bits: int = 4):
+    """Draft expert: GPTQ g128 (INT4 unless bits says 2 or 8) of the target's
+    w13 and w2."""
+    return dict(w13=gptq_from_linear(w13, bits), w2=gptq_from_linear(w2, bits))
+
+
+def quant_bytes_per_expert(shape: LayerShape, bits: int) -> int:
+    """Packed codes + fp16 scales + packed zeros of w13 and w2 at `bits`."""
+    H, I = shape.H, shape.I
+    mats = ((H, 2 * I), (I, H))  # (K, N)
+    return sum(K * N * bits // 8 + (K // GROUP) * N * 2 + (K // GROUP) * N * bits // 8
+               for K, N in mats)
 
 
 def shared_expert(shape: LayerShape, layer: int = 0, seed: int = BASE_SEED):

@@ -18,7 +18,8 @@ FAKE = V(0x1000)  # never dereferenced: the checks below fail before any use
 def test_exports_every_header_function():
     names = fve.header_functions()
     expected = {"smoe_abi_version", "smoe_last_error", "moe_route_topk", "elb_count",
-                "moe_gather", "moe_route_plan", "w4a16_grouped_ffn", "moe_draft_route_ffn",
+                "moe_gather", "moe_route_plan", "w4a16_grouped_ffn", "wq_grouped_ffn",
+                "moe_draft_route_ffn",
                 "verify_grouped_gemm", "moe_combine",
                 "expert_stage_async", "smoe_workspace_bytes"}
     assert set(names) == expected
@@ -86,6 +87,28 @@ def test_route_plan_validation():
     assert call(layer=1, Lc=1) == 2                 # layer outside [0, L)
     assert call(x=V(0x1002)) == 2 and "aligned" in _err()
     assert call(T=-1) == 2
+
+
+def test_wq_validation():
+    L = fve.lib()
+    args = [FAKE] * 6
+    need = L.smoe_workspace_bytes(0, 4, 2, 256, 512, 8)
+
+    def call(bits=8, gs=128, I=512, ws=FAKE, wsb=None, T=4):
+        return L.wq_grouped_ffn(*args, T, 2, 256, I, 8, bits, gs, FAKE, ws,
+                                need if wsb is None else wsb, None, None)
+    assert call(bits=3) == 3 and "bits=3" in _err()
+    assert call(bits=16) == 3
+    assert call(gs=64) == 3
+    assert call(I=500) == 2
+    assert call(wsb=need - 1) == 6
+    assert call(ws=None) == 6
+    assert L.wq_grouped_ffn(*args[:5], None, 4, 2, 256, 512, 8, 2, 128, FAKE, FAKE, need, None,
+                            None) == 1
+    # w4a16_grouped_ffn reports its own name
+    assert L.w4a16_grouped_ffn(*args, 1, 2, 256, 500, 8, 128, FAKE, FAKE, 1 << 20, None,
+                               None) == 2
+    assert _err().startswith("w4a16_grouped_ffn")
 
 
 def test_draft_route_ffn_validation():

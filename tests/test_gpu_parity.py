@@ -11,7 +11,8 @@ import torch
 import fp16_verify_expert_amd as fve
 import oracle
 import synth
-from gpu_util import (W_RTOL, Layer, assert_fp16_close, dev, host, run_layer, say, upload_f16)
+from gpu_util import (W_RTOL, Layer, assert_fp16_close, dev, host, run_layer, say, upload_f16,
+                      upload_int4)
 
 pytestmark = pytest.mark.gpu
 
@@ -275,6 +276,59 @@ def test_w4a16_grouped_ffn(shape, T):
     y2 = fve.w4a16_grouped_ffn(dx, gm, L.t4, T, shape.k, shape.H, shape.I, shape.E, ws,
                                err_word=err)
     assert torch.equal(y[:rows], y2[:rows])
+
+
+# Other draft code widths (2 and 8 bits, GPTQ layout).
+WQ_CASES = [(synth.TINY, 1, 2), (synth.TINY, 1, 8), (synth.TINY, 40, 2), (synth.TINY, 40, 8),
+            (synth.DS, 1, 8), (synth.DS, 4, 2), (synth.DS, 16, 8), (synth.PHI, 1, 2),
+            (synth.PHI, 1, 8), (synth.QWEN, 1, 8), (_LONG_I, 1, 8), (_LONG_H, 1, 2),
+            (_LONG_H, 3, 8)]
+
+
+@pytest.mark.parametrize("shape,T,bits", WQ_CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_wq_grouped_ffn(shape, T, bits):
+    """wq_grouped_ffn at 2 and 8 bits against the oracle (the long 8-bit
+    reductions take the multi-row kernels at T = 1: more than four
+    pseudo-groups per slot)."""
+    say(f"wq{bits} {shape.name} T={T}")
+    E, k = shape.E, shape.k
+    x = synth.tokens(shape, T, step=1)
+    router = synth.router(shape)
+    r = oracle.route_topk(x, router, k)
+    touched = sorted(set(int(e) for e in r["ids"].ravel()))
+    q = [None] * E
+    for e in touched:
+        q[e] = synth.expert_int4(*synth.expert_f16(shape, 0, e), bits=bits)
+    table, _keep = upload_int4(q)
+    maps = oracle.gather_maps(r["ids"], E)
+    ref = oracle.grouped_ffn(x, maps, q, f"int{bits}")
+    err = _err()
+    dx = dev(x)
+    ids, _, _ = fve.moe_route_topk(dx, dev(router), k)
+    gm = fve.moe_gather(ids, E, err)
+    ws = fve.new_workspace(0, T, k, shape.H, shape.I, E)
+    y = fve.wq_grouped_ffn(dx, gm, table, T, k, shape.H, shape.I, E, ws, bits, err_word=err)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) == 0
+    rows = T * k
+    st = assert_fp16_close(host(y)[:rows], ref, f"wq{bits} {shape.name} T={T}")
+    say(f"  l2={st['l2']:.2e} maxabs={st['maxabs']:.2e}")
+    y2 = fve.wq_grouped_ffn(dx, gm, table, T, k, shape.H, shape.I, E, ws, bits, err_word=err)
+    assert torch.equal(y[:rows], y2[:rows])
+
+
+def test_wq_bits4_is_w4a16():
+    s = synth.DS
+    L = _layer(s, (4,), f16=False)
+    x = dev(synth.tokens(s, 4, step=0))
+    ids, _, _ = fve.moe_route_topk(x, L.d_router, s.k)
+    gm = fve.moe_gather(ids, s.E)
+    ws = fve.new_workspace(0, 4, s.k, s.H, s.I, s.E)
+    a = fve.w4a16_grouped_ffn(x, gm, L.t4, 4, s.k, s.H, s.I, s.E, ws)
+    b = fve.wq_grouped_ffn(x, gm, L.t4, 4, s.k, s.H, s.I, s.E, ws, 4)
+    assert torch.equal(a[:4 * s.k], b[:4 * s.k])
+    with pytest.raises(fve.SmoeError):
+        fve.wq_grouped_ffn(x, gm, L.t4, 4, s.k, s.H, s.I, s.E, ws, 3)
 
 
 # One-token draft step with the routing folded into the gate/up launch.
