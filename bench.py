@@ -50,12 +50,14 @@ def parse():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--workload", default="phi_layer",
-                    choices=["phi_layer", "qwen_chunk", "route_fidelity", "qwen_rounds"],
+                    choices=["phi_layer", "qwen_chunk", "route_fidelity", "qwen_rounds",
+                             "draft_formats"],
                     help="phi_layer (default): one draft + verify step of the Phi-3.5-MoE-shaped "
                          "layer; qwen_chunk: 24 Qwen-shaped layers, 16 draft steps, ELB snapshot, "
                          "top-16 residency, 17-token verify with staged misses; route_fidelity: INT4 draft vs "
                          "FP16 target routing agreement and distinct experts vs depth; qwen_rounds: speculation "
-                         "rounds with the prefetch planner vs boundary placement")
+                         "rounds with the prefetch planner vs boundary placement; draft_formats: the "
+                         "one-token draft step with 2-, 4- and 8-bit experts (Phi and DeepSeek shapes)")
     ap.add_argument("--layers", type=int, default=24, help="qwen_chunk: number of layers")
     ap.add_argument("--rounds", type=int, default=4, help="qwen_rounds: speculation rounds")
     ap.add_argument("--rho", type=float, default=0.8,
@@ -89,6 +91,8 @@ def main():
         return bench_route_fidelity(args)
     if args.workload == "qwen_rounds":
         return bench_qwen_rounds(args)
+    if args.workload == "draft_formats":
+        return bench_draft_formats(args)
 
     import numpy as np
     import torch
@@ -399,6 +403,100 @@ def qwen_layers(L, dev):
         print(f"generated layer {l}", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     return layers, full
+
+
+def bench_draft_formats(args):
+    """The draft step at other code widths ([S1] Main Findings and Future
+    Directions: draft fidelity is compared at 2-, 4- and 8-bit precision, and
+    the precision trades prediction accuracy for memory).  For each width, on
+    the Phi-3.5-MoE shape (T = 1) and the DeepSeek-V2-Lite shape (T = 1, 4,
+    16): the draft step (moe_route_plan, wq_grouped_ffn, moe_combine) over
+    seeded synthetic inputs, every expert in HBM, RTN GPTQ-layout weights of
+    the same fp16 experts.  Reported: the weight bytes a step reads, the step
+    wall time and the FFN call time (HIP events), and GB/s of both."""
+    import numpy as np
+    import torch
+
+    import fp16_verify_expert_amd as fve
+    import synth
+
+    fve.lib()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda")
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    K = max(args.steps, 5)
+    results = []
+    t_all = time.perf_counter()
+    for shape, Ts in ((synth.PHI, (1,)), (synth.DS, (1, 4, 16))):
+        f16 = [synth.expert_f16(shape, 0, e) for e in range(shape.E)]
+        router = up(synth.router(shape))
+        for bits in (2, 4, 8):
+            q = [synth.expert_int4(w13, w2, bits) for w13, w2 in f16]
+            gq = [{key: tuple(up(t) for t in ex[key]) for key in ("w13", "w2")} for ex in q]
+            table = fve.w4_expert_table(gq)
+            bpe = synth.quant_bytes_per_expert(shape, bits)
+            for T in Ts:
+                xs = [up(synth.tokens(shape, T, step=i)) for i in range(POOL)]
+                ws = fve.new_workspace(0, T, shape.k, shape.H, shape.I, shape.E)
+                y = torch.empty((T * shape.k, shape.H), dtype=torch.float16, device=dev)
+                out = torch.empty((T, shape.H), dtype=torch.float16, device=dev)
+                ids_b = torch.empty((T, shape.k), dtype=torch.int32, device=dev)
+                w_b = torch.empty((T, shape.k), dtype=torch.float32, device=dev)
+                maps_b = fve._new_maps(T, shape.k, shape.E, dev)
+                touched = []
+
+                def step(i, ev=None):
+                    x = xs[i % POOL]
+                    ids, w, _, m = fve.moe_route_plan(x, router, shape.k, topk_ids=ids_b,
+                                                      topk_w=w_b, maps=maps_b)
+                    if ev: ev[0].record()
+                    fve.wq_grouped_ffn(x, m, table, T, shape.k, shape.H, shape.I, shape.E, ws,
+                                       bits, y_sorted=y)
+                    if ev: ev[1].record()
+                    fve.moe_combine(y, m["pair_pos"], w, out=out)
+                    return m
+
+                for i in range(POOL):
+                    m = step(i)
+                    torch.cuda.synchronize()
+                    touched.append(int(m["n_active"].item()))
+                for i in range(args.warmup):
+                    step(i)
+                ph = [(mk(), mk()) for _ in range(K)]
+                kf = [(mk(), mk()) for _ in range(K)]
+                torch.cuda.synchronize()
+                for st in range(K):
+                    ph[st][0].record()
+                    step(args.warmup + st, kf[st])
+                    ph[st][1].record()
+                torch.cuda.synchronize()
+                idx = [(args.warmup + st) % POOL for st in range(K)]
+                nbytes = sum(touched[i] * bpe for i in idx)
+                step_ms = sum(a.elapsed_time(b) for a, b in ph)
+                ffn_ms = sum(a.elapsed_time(b) for a, b in kf)
+                results.append({
+                    "shape": shape.name, "bits": bits, "T": T,
+                    "touched_experts_avg": round(sum(touched[i] for i in idx) / K, 2),
+                    "weight_bytes_avg": round(nbytes / K),
+                    "step_us": round(1e3 * step_ms / K, 2),
+                    "step_gbps": round(nbytes / (step_ms * 1e-3) / 1e9, 1),
+                    "ffn_us": round(1e3 * ffn_ms / K, 2),
+                    "ffn_gbps": round(nbytes / (ffn_ms * 1e-3) / 1e9, 1),
+                    "ffn_frac_hbm": round(nbytes / (ffn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+                print(json.dumps(results[-1]), file=sys.stderr, flush=True)
+            del gq, table
+            torch.cuda.empty_cache()
+    phi4 = next(r for r in results if r["shape"] == synth.PHI.name and r["bits"] == 4)
+    out = {"metric": "draft step weight GB/s by code width", "value": phi4["step_gbps"],
+           "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+           "higher_is_better": True, "vs_baseline": None,
+           "dtype": "int2/int4/int8-w (GPTQ layout, g128), fp16-a; fp32 accumulate",
+           "data": "synthetic (seeded N(0,0.02) fp16 experts, RTN at each width, N(0,1) tokens)",
+           "config": {"workload": "draft_formats: one draft step (route plan, wq_grouped_ffn, "
+                                  "combine) at 2/4/8 bits; phi35 T=1, ds_v2_lite T=1/4/16"},
+           "results": results, "run_s": round(time.perf_counter() - t_all, 1)}
+    print(json.dumps(out), flush=True)
 
 
 def bench_route_fidelity(args):
