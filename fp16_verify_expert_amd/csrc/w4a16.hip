@@ -75,6 +75,9 @@ struct QF {
 #ifndef SMOE_W4_PREFETCH
 #define SMOE_W4_PREFETCH 1
 #endif
+#ifndef SMOE_W4_MFMA
+#define SMOE_W4_MFMA 1  // multi-row 4-bit steps on the MFMA kernel
+#endif
 #ifndef SMOE_W4_T1_MAX_WAVES
 #define SMOE_W4_T1_MAX_WAVES 4
 #endif
@@ -821,6 +824,236 @@ __attribute__((amdgpu_waves_per_eu(w4_waves_per_eu<MAXM, NG>()))) void w4_kernel
     }
 }
 
+// ------------------------------------------ multi-row 4-bit path on MFMA ----
+//
+// With several rows per expert the dot products dominate the VALU path (four
+// dot2 per packed word and row).  Here the dequantised codes are the B
+// operand of v_mfma_f32_16x16x32_f16 and up to 16 activation rows its A
+// operand, so a word costs its 5 dequantisation ops whatever the row count.
+// Lane l holds columns 4(l%16)..+3 (one 16-byte load per packed row) at
+// packed row 4j + l/16 of each 32-K step j: word c of the load is exactly
+// the B fragment (8 K of one column) of the c-th MFMA, whose 16 columns are
+// 4(l%16) + c.  The fp16 pairs (1024+q, 1024+16q) meet activation pairs
+// staged as for the VALU path, with the (1024+16q) halves' activations
+// scaled by 1/16 in registers, so one accumulator per column set sums
+//   sum_even (1024+q) x + sum_odd (64+q) x;
+// the constant parts and the zero come off per 128-K group with the group's
+// activation sums, then the fp16 scale.  The 4 waves take groups g = wave,
+// wave + 4, ... through two register buffers (loads of the next two groups
+// in flight while one is multiplied) and add their tiles through LDS.
+#ifndef SMOE_W4_MFMA_WAVES
+#define SMOE_W4_MFMA_WAVES 4
+#endif
+#ifndef SMOE_W4_MFMA_WPE
+#define SMOE_W4_MFMA_WPE 2
+#endif
+constexpr int kMfmaWaves = SMOE_W4_MFMA_WAVES;
+constexpr int kMfmaRows = 16;
+constexpr int kMfmaLdsBytes = 32 * 1024;  // activation staging budget
+
+struct MfmaLoad {
+    u4_t w[4];  // packed rows 4j + l/16 of the group, 4 columns each
+    uint2 s;
+    uint32_t z;
+};
+
+__device__ __forceinline__ void mfma_load(MfmaLoad& L, const W4Src& src, int g, int col, int kq) {
+    const int N = src.N;
+    const int voff = ((g * 16 + kq) * N + col) * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        L.w[j] = __builtin_amdgcn_raw_buffer_load_b128(src.q, voff, 4 * j * N * 4, kAuxNT);
+    const uint64_t sv =
+        *as_global(reinterpret_cast<const uint64_t*>(src.m.scales + (size_t)g * N + col));
+    L.s = make_uint2((uint32_t)sv, (uint32_t)(sv >> 32));
+    L.z = (uint32_t)*as_global(src.m.qzeros + (size_t)g * (N >> 3) + (col >> 3));
+}
+
+// One 128-K group into acc (acc[c][i]: row 4(l/16)+i, column 4(l%16)+c).
+__device__ __forceinline__ void mfma_group(const MfmaLoad& L, const uint4* __restrict__ xs,
+                                           const float4* __restrict__ sums, int arow, bool aok,
+                                           const int (&drow)[4], int g, int K8, int G, int kq,
+                                           int zsh, const Masks<4>& mk, f4_t (&acc)[4]) {
+    f4_t d[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) d[c] = f4_t{0.f, 0.f, 0.f, 0.f};
+    const h2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint4 xp = aok ? xs[arow * K8 + g * 16 + 4 * j + kq] : make_uint4(0, 0, 0, 0);
+        xp.y = __builtin_bit_cast(uint32_t, as_h2(xp.y) * sixteenth);
+        xp.w = __builtin_bit_cast(uint32_t, as_h2(xp.w) * sixteenth);
+        const h8_t av = __builtin_bit_cast(h8_t, xp);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t w = L.w[j][c];
+            const uint32_t b = w >> 8;
+            const u4_t bw = {(w & mk.m[0]) | kMagic, (w & mk.m[1]) | kMagic,
+                             (b & mk.m[0]) | kMagic, (b & mk.m[1]) | kMagic};
+            d[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8_t, bw), d[c],
+                                                          0, 0, 0);
+        }
+    }
+    float4 se[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) se[i] = sums[drow[i] * G + g];
+    const uint32_t zw = L.z >> zsh;
+    const uint32_t sw[2] = {L.s.x, L.s.y};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float s = h2f((uint16_t)(sw[c >> 1] >> (16 * (c & 1))));
+        const float z = (float)((zw >> (4 * c)) & 0xFu);
+        const float ce = 1024.0f + z, co = 64.0f + z;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float t = d[c][i];
+            t -= ce * se[i].x;
+            t -= co * se[i].y;
+            acc[c][i] += s * t;
+        }
+    }
+}
+
+template <int PHASE>
+__global__ __launch_bounds__(64 * kMfmaWaves)
+__attribute__((amdgpu_waves_per_eu(SMOE_W4_MFMA_WPE))) void w4_mfma_kernel(W4Args a) {
+    extern __shared__ uint4 smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int q = lane & 15;
+    const int kq = lane >> 4;
+    const int cb = blockIdx.x % a.nCB;
+    const int slot = blockIdx.x / a.nCB;
+    const int K = a.K, N = a.N;
+    const int G = K >> 7;
+    const int K8 = K >> 3;
+    const W4Lds l = carve_lds<4>(smem, a);
+    const int e = a.active[slot];  // -1 past the touched experts
+    if (e < 0) return;
+    if (e >= a.E) {
+        if (tid == 0 && cb == 0) flag_error(a.err, SMOE_DERR_BAD_ID);
+        return;
+    }
+    const smoe_w4_mat wm = (PHASE == 1) ? a.experts[e].w13 : a.experts[e].w2;
+    const int r0 = a.off[e];
+    const int r1 = a.off[e + 1];
+    if (!wm.qweight || !wm.scales || !wm.qzeros) {
+        if (tid == 0 && cb == 0) flag_error(a.err, SMOE_DERR_NULL_EXPERT);
+        return;
+    }
+    // 64 columns per block: gate cb*32.. and up I + cb*32.. (gate/up), or cb*64..
+    const int col = (PHASE == 1) ? ((q < 8) ? cb * 32 + 4 * q : a.I + cb * 32 + 4 * (q - 8))
+                                 : cb * 64 + 4 * q;
+    const int colc = col < N ? col : 0;  // columns past N read column 0 (never stored)
+    const int zsh = zero_shift<4>(colc);
+    const W4Src src = make_src<4>(wm, K, N);
+    const Masks<4> mk;
+    float* red = l.red;  // [kMfmaWaves][MCH][64]
+    const bool direct = (PHASE == 1) && a.direct;
+    const int g0 = wave;
+    MfmaLoad A, B;
+    for (int mc = r0; mc < r1; mc += a.MCH) {
+        const int M = min(a.MCH, r1 - mc);
+        const bool stage = !direct || mc == r0;
+        // rows of this chunk (all T tokens in the direct mode): source row j
+        const int nrows = direct ? a.T : M;
+        auto src_row = [&](int j) -> const uint4* {
+            size_t r;
+            if (direct) r = j;
+            else r = (PHASE == 1) ? (size_t)a.sorted_token[mc + j] : (size_t)(mc + j);
+            return reinterpret_cast<const uint4*>(a.xin + r * K);
+        };
+        // the rows' first chunks are requested, then this wave's first two
+        // groups, and the rows are written to LDS while the weights are in
+        // flight (requests are unconditional, so the wait for the rows is an
+        // exact count that leaves the weights outstanding)
+        uint4 xv[kRowChunksPerThread];
+        const int nch = nrows * K8;
+        if (stage) {
+#pragma unroll
+            for (int u = 0; u < kRowChunksPerThread; ++u) {
+                int idx = tid + u * (int)blockDim.x;
+                idx = idx < nch ? idx : nch - 1;
+                const int j = idx / K8;
+                xv[u] = src_row(j)[idx - j * K8];
+            }
+        }
+        // (unconditional: groups past G read group G - 1, not multiplied)
+        mfma_load(A, src, clamp_group(g0, G), colc, kq);
+        mfma_load(B, src, clamp_group(g0 + kMfmaWaves, G), colc, kq);
+        __builtin_amdgcn_sched_barrier(0);
+        if (stage) {
+#pragma unroll
+            for (int u = 0; u < kRowChunksPerThread; ++u) {
+                int idx = tid + u * (int)blockDim.x;
+                idx = idx < nch ? idx : nch - 1;
+                l.xs[idx] = permute_chunk<4>(xv[u]);
+            }
+            // rows longer than the early requests cover
+            for (int idx = tid + kRowChunksPerThread * (int)blockDim.x; idx < nch;
+                 idx += blockDim.x) {
+                const int j = idx / K8;
+                l.xs[idx] = permute_chunk<4>(src_row(j)[idx - j * K8]);
+            }
+            finish_rows<4>(l.xs, l.sums, nrows, K8, G);
+        }
+        // A operand row (MFMA row l%16) and the LDS rows of this lane's D rows
+        const bool aok = q < M;
+        const int ar = direct ? a.sorted_token[mc + (aok ? q : 0)] : (aok ? q : 0);
+        int drow[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * kq + i;
+            const int rr = r < M ? r : 0;
+            drow[i] = direct ? a.sorted_token[mc + rr] : rr;
+        }
+        f4_t acc[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = f4_t{0.f, 0.f, 0.f, 0.f};
+        // groups wave, wave + 4, ... through the two buffers (branches on the
+        // group index are wave-uniform)
+        for (int g = g0; g < G; g += 2 * kMfmaWaves) {
+            mfma_group(A, l.xs, l.sums, ar, aok, drow, g, K8, G, kq, zsh, mk, acc);
+            mfma_load(A, src, clamp_group(g + 2 * kMfmaWaves, G), colc, kq);
+            if (g + kMfmaWaves < G)
+                mfma_group(B, l.xs, l.sums, ar, aok, drow, g + kMfmaWaves, K8, G, kq, zsh, mk,
+                           acc);
+            mfma_load(B, src, clamp_group(g + 3 * kMfmaWaves, G), colc, kq);
+        }
+        // the waves' tiles, added in a fixed order
+        __syncthreads();  // every wave is done with the staged rows
+        const int MCH = a.MCH;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * kq + i < M) red[(wave * MCH + 4 * kq + i) * 64 + 4 * q + c] = acc[c][i];
+        __syncthreads();
+        if (PHASE == 1) {
+            for (int idx = tid; idx < M * 32; idx += blockDim.x) {
+                const int m = idx >> 5, j = idx & 31;
+                float gv = 0.0f, uv = 0.0f;
+                for (int w = 0; w < kMfmaWaves; ++w) {
+                    gv += red[(w * MCH + m) * 64 + j];
+                    uv += red[(w * MCH + m) * 64 + 32 + j];
+                }
+                a.out[(size_t)(mc + m) * a.I + cb * 32 + j] = f2h(silu_f(gv) * uv);
+            }
+        } else {
+            for (int idx = tid; idx < M * 64; idx += blockDim.x) {
+                const int m = idx >> 6, j = idx & 63;
+                if (cb * 64 + j < N) {
+                    float v = 0.0f;
+                    for (int w = 0; w < kMfmaWaves; ++w) v += red[(w * MCH + m) * 64 + j];
+                    a.out[(size_t)(mc + m) * N + cb * 64 + j] = f2h(v);
+                }
+            }
+        }
+        __syncthreads();  // red and the staged rows are rewritten by the next chunk
+    }
+}
+
 // --------------------------------------------- routing + gate/up, T = 1 ----
 //
 // The one-token draft step's routing, ELB update and gather maps folded into
@@ -971,6 +1204,26 @@ PhasePlan plan_phase(int phase, int slots, int T, int K, int N, int I, int maxm,
     return p;
 }
 
+// The MFMA multi-row kernel: 64-column blocks, chunks of up to 16 rows within
+// the staging budget (all T rows at once for the gate/up projection when they
+// fit).
+PhasePlan plan_mfma(int phase, int T, int K, int N, int I) {
+    PhasePlan p{};
+    p.lpr = 16;
+    p.nCB = (phase == 1) ? I / 32 : (N + 63) / 64;
+    p.waves = kMfmaWaves;
+    const int G = K / 128;
+    const size_t row_bytes = (size_t)K * 2 + (size_t)G * 16;
+    int cap = (int)(kMfmaLdsBytes / row_bytes);
+    if (cap < 1) cap = 1;
+    p.mch = cap < kMfmaRows ? cap : kMfmaRows;
+    p.direct = (phase == 1 && T <= cap) ? 1 : 0;
+    p.xr = p.direct ? T : p.mch;
+    p.lds = (size_t)p.xr * row_bytes + (size_t)kMfmaWaves * p.mch * 64 * 4;
+    p.ng = 1;
+    return p;
+}
+
 template <int BITS, int PHASE, int LPR, int NG>
 hipError_t launch_one_token(const W4Args& a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
     hipLaunchKernelGGL((w4_kernel<BITS, PHASE, LPR, 1, NG>), grid, block, lds, s, a);
@@ -1080,6 +1333,21 @@ hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, cons
     }
     uint16_t* h = static_cast<uint16_t*>(ws);
     SlotDesc* desc = reinterpret_cast<SlotDesc*>(static_cast<char*>(ws) + h_bytes(T, k, I));
+    if (maxm > 1 && bits == 4 && SMOE_W4_MFMA) {
+        const PhasePlan m1 = plan_mfma(1, T, H, 2 * I, I);
+        const W4Args b1 = phase_args(m1, x, sorted_token, off, active, n_active, experts, H,
+                                     2 * I, I, T, E, h, err, desc);
+        hipLaunchKernelGGL((w4_mfma_kernel<1>), dim3(slots * m1.nCB), dim3(64 * kMfmaWaves),
+                           m1.lds, s, b1);
+        hipError_t e1 = hipGetLastError();
+        if (e1 != hipSuccess) return e1;
+        const PhasePlan m2 = plan_mfma(2, T, I, H, I);
+        const W4Args b2 =
+            phase_args(m2, h, nullptr, off, active, n_active, experts, I, H, I, T, E, y, err, desc);
+        hipLaunchKernelGGL((w4_mfma_kernel<2>), dim3(slots * m2.nCB), dim3(64 * kMfmaWaves),
+                           m2.lds, s, b2);
+        return hipGetLastError();
+    }
     const W4Args a1 = phase_args(p1, x, sorted_token, off, active, n_active, experts, H, 2 * I, I,
                                  T, E, h, err, desc);
     hipError_t st = launch_any<1>(a1, slots, p1, maxm, bits, s);
