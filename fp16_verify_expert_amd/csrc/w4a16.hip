@@ -1359,12 +1359,28 @@ hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, cons
 
 bool draft_route_ffn_supported(int E, int k) { return E <= 256 && k <= kFusedMaxK; }
 
+// Router size up to which the routing is folded into the gate/up launch.
+// Every workgroup reads the whole router from L2; measured on the decode
+// shapes (one token): folded is faster with a 139 KB router (Phi-3.5-MoE:
+// 38.3 against 42.6 us for routing + both projections) and slower with
+// 250-262 KB (Qwen1.5-MoE 32.3 against 29.4 us, DeepSeek-V2-Lite 35.8 against
+// 33.3 us), where the single-workgroup routing plan runs first instead.
+constexpr size_t kFoldedRouterBytes = 192 * 1024;
+
 hipError_t launch_draft_route_ffn(const uint16_t* x, const uint16_t* wr, const uint16_t* wsg,
                                   int H, int E, int k, int renorm, int32_t* counters_row,
                                   int32_t* ids, float* w, float* gate, int32_t* off, int32_t* st,
                                   int32_t* sp, int32_t* pp, int32_t* active, int32_t* n_active,
                                   const smoe_w4_expert* experts, int I, uint16_t* y, void* ws,
                                   int32_t* err, hipStream_t s) {
+    const size_t router_bytes = (size_t)(E + (wsg ? 1 : 0)) * H * 2;
+    if (router_bytes > kFoldedRouterBytes) {
+        hipError_t e0 = launch_route_plan_row(x, wr, wsg, 1, H, E, k, renorm, counters_row, ids,
+                                              w, gate, off, st, sp, pp, active, n_active, err, s);
+        if (e0 != hipSuccess) return e0;
+        return launch_w4a16_ffn(x, st, off, active, n_active, experts, 1, k, H, I, E, 4, y, ws,
+                                err, s);
+    }
     uint16_t* h = static_cast<uint16_t*>(ws);
     SlotDesc* desc = reinterpret_cast<SlotDesc*>(static_cast<char*>(ws) + h_bytes(1, k, I));
     const PhasePlan p1 = plan_phase(1, k, 1, H, 2 * I, I, 1, 4);

@@ -243,6 +243,9 @@ smoe_status wq_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
  * three ([S1] Key Contributions 4: routing, gathering and the experts' FFN of
  * a draft step inside one fused launch; the routing is folded into the
  * gate/up projection, whose every workgroup evaluates the router itself).
+ * With a router ((E + shared gate) x H fp16) above 192 KB the routing plan
+ * runs as its own launch first (three launches; measured faster there: every
+ * workgroup would read the whole router).  The outputs are the same.
  *
  * Arguments keep the meaning and layout of those two calls with T = 1:
  *   x              fp16 [1, H]

@@ -279,10 +279,11 @@ def test_w4a16_grouped_ffn(shape, T):
 
 
 # Other draft code widths (2 and 8 bits, GPTQ layout).
+_WIDE_Q = dataclasses.replace(synth.TINY, name="tiny_e128_k5", E=128, k=5)   # > 64 experts
 WQ_CASES = [(synth.TINY, 1, 2), (synth.TINY, 1, 8), (synth.TINY, 40, 2), (synth.TINY, 40, 8),
             (synth.DS, 1, 8), (synth.DS, 4, 2), (synth.DS, 16, 8), (synth.PHI, 1, 2),
             (synth.PHI, 1, 8), (synth.QWEN, 1, 8), (_LONG_I, 1, 8), (_LONG_H, 1, 2),
-            (_LONG_H, 3, 8)]
+            (_LONG_H, 3, 8), (_WIDE_Q, 1, 8), (_WIDE_Q, 5, 2)]
 
 
 @pytest.mark.parametrize("shape,T,bits", WQ_CASES, ids=lambda v: getattr(v, "name", str(v)))
@@ -406,6 +407,10 @@ def test_draft_route_ffn_nan_logit_and_repeat():
                             topk_ids=ids, topk_w=w, maps=m, y_sorted=y)
     assert torch.equal(y, y1)
     assert host(counters).tolist() == [[2] * s.E]
+    # without counters: no ELB update, the same outputs
+    ids2, w2, _, m2, y2 = fve.moe_draft_route_ffn(dev(x), dev(wr), s.k, L.t4, s.I, ws)
+    assert torch.equal(ids2, ids) and torch.equal(w2, w) and torch.equal(y2[:s.k], y1[:s.k])
+    assert torch.equal(m2["offsets"], m["offsets"])
 
 
 VERIFY_CASES = [(synth.TINY, 17), (synth.TINY, 40), (synth.QWEN, 9), (synth.PHI, 17),
