@@ -168,4 +168,31 @@ SMOE_DEV void gather_block(const int32_t* ids, int n, int k, int E, int32_t* __r
     }
 }
 
+// The maps and ELB increments of one token's k distinct ids (ids in LDS), by
+// any number of threads of a workgroup: the pair of rank j sits at sorted row
+// #{i : ids[i] < ids[j]}, which is where the stable counting sort puts it
+// (gather_block); the ELB row gets +1 per selected expert.
+SMOE_DEV void one_token_maps(const int32_t* ids, int k, int E, int32_t* __restrict__ counters_row,
+                             int32_t* __restrict__ off, int32_t* __restrict__ sorted_token,
+                             int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos,
+                             int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
+    for (int j = threadIdx.x; j < k; j += blockDim.x) {
+        const int id = ids[j];
+        int pos = 0;
+        for (int i = 0; i < k; ++i) pos += (ids[i] < id) ? 1 : 0;
+        if (counters_row) atomicAdd(counters_row + id, 1);
+        sorted_token[pos] = 0;
+        sorted_pair[pos] = j;
+        pair_pos[j] = pos;
+        active[pos] = id;
+    }
+    for (int ee = threadIdx.x; ee <= E; ee += blockDim.x) {
+        int c = 0;
+        for (int i = 0; i < k; ++i) c += (ids[i] < ee) ? 1 : 0;
+        off[ee] = c;
+        if (ee >= k && ee < E) active[ee] = -1;
+    }
+    if (threadIdx.x == 0) *n_active = k;
+}
+
 }  // namespace smoe_maps

@@ -43,7 +43,13 @@ __global__ __launch_bounds__(kPlanThreads) void route_plan_kernel(
                                       gate ? gate + t : nullptr, ids_s + t * k);
     __syncthreads();
 
-    // 3. ELB update and 4. the maps, from the ids in LDS
+    // 3. ELB update and 4. the maps, from the ids in LDS (one token: its k
+    //    ids are distinct and their sorted rows are their ranks by id)
+    if (T == 1) {
+        smoe_maps::one_token_maps(ids_s, k, E, counters_row, off, sorted_token, sorted_pair,
+                                  pair_pos, active, n_active);
+        return;
+    }
     const int n = T * k;
     if (counters_row)
         smoe_maps::elb_accumulate(ids_s, n, threadIdx.x, kPlanThreads, E, counters_row, err);

@@ -41,6 +41,7 @@
 // The slots' partial sums are added in a fixed order through LDS: the output
 // is deterministic and no floating-point atomics are used.
 #include "common.h"
+#include "maps_core.h"
 #include "route_core.h"
 
 namespace {
@@ -1133,23 +1134,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void route_w4_kernel(W4Args a, RouteArgs
     if (wave == 0)
         smoe_route::topk_softmax_wave(lg_s, E, k, r.renorm, r.wsg != nullptr, lane, r.ids, r.w,
                                       r.gate, nullptr);
-    for (int j = tid; j < k; j += blockDim.x) {
-        const int id = ids_s[j];
-        int pos = 0;
-        for (int i = 0; i < k; ++i) pos += (ids_s[i] < id) ? 1 : 0;
-        if (r.counters_row) atomicAdd(r.counters_row + id, 1);
-        r.sorted_token[pos] = 0;
-        r.sorted_pair[pos] = j;
-        r.pair_pos[j] = pos;
-        r.active[pos] = id;
-    }
-    for (int ee = tid; ee <= E; ee += blockDim.x) {
-        int c = 0;
-        for (int i = 0; i < k; ++i) c += (ids_s[i] < ee) ? 1 : 0;
-        r.off[ee] = c;
-        if (ee >= k && ee < E) r.active[ee] = -1;
-    }
-    if (tid == 0) *r.n_active = k;
+    smoe_maps::one_token_maps(ids_s, k, E, r.counters_row, r.off, r.sorted_token, r.sorted_pair,
+                              r.pair_pos, r.active, r.n_active);
 }
 
 // ---------------------------------------------------------------- launch ----
