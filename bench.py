@@ -245,6 +245,47 @@ def main():
             verify(args.warmup + st)
         torch.cuda.synchronize()
 
+    # every call of the split draft step and of the verify step on its own
+    # (HIP events around each; launch gaps excluded)
+    nl = min(K, 20)
+    calls = {n: [(mk(), mk()) for _ in range(nl)] for n in
+             ("moe_route_plan", "w4a16_grouped_ffn", "moe_combine_draft", "moe_route_topk",
+              "moe_gather", "verify_grouped_gemm", "moe_combine_verify")}
+    for st in range(nl):
+        i = args.warmup + st
+        x = xs_d[i % POOL]
+        ev = lambda n: calls[n][st]
+        ev("moe_route_plan")[0].record()
+        fve.moe_route_plan(x, router, k, counters=counters, layer=0, err_word=err,
+                           topk_ids=bd["ids"], topk_w=bd["w"], maps=bd["maps"])
+        ev("moe_route_plan")[1].record()
+        ev("w4a16_grouped_ffn")[0].record()
+        fve.w4a16_grouped_ffn(x, bd["maps"], t4, T_D, k, H, I, E, ws_d, y_sorted=bd["y"],
+                              err_word=err)
+        ev("w4a16_grouped_ffn")[1].record()
+        ev("moe_combine_draft")[0].record()
+        fve.moe_combine(bd["y"], bd["maps"]["pair_pos"], bd["w"], out=bd["out"])
+        ev("moe_combine_draft")[1].record()
+        xv = xs_v[i % POOL]
+        ev("moe_route_topk")[0].record()
+        fve.moe_route_topk(xv, router, k, topk_ids=bv["ids"], topk_w=bv["w"])
+        ev("moe_route_topk")[1].record()
+        ev("moe_gather")[0].record()
+        fve.moe_gather(bv["ids"], E, err, out=bv["maps"])
+        ev("moe_gather")[1].record()
+        ev("verify_grouped_gemm")[0].record()
+        fve.verify_grouped_gemm(xv, bv["maps"]["sorted_token"], bv["maps"]["offsets"], t16,
+                                T_V, T_V * k, H, I, E, ws_v, active=bv["maps"]["active"],
+                                n_active=bv["maps"]["n_active"], y_sorted=bv["y"],
+                                err_word=err)
+        ev("verify_grouped_gemm")[1].record()
+        ev("moe_combine_verify")[0].record()
+        fve.moe_combine(bv["y"], bv["maps"]["pair_pos"], bv["w"], out=bv["out"])
+        ev("moe_combine_verify")[1].record()
+    torch.cuda.synchronize()
+    call_us = {n: round(1e3 * sum(a.elapsed_time(b) for a, b in v) / nl, 2)
+               for n, v in calls.items()}
+
     idx = [(args.warmup + st) % POOL for st in range(K)]
     draft_ms = sum(ph[st][0].elapsed_time(ph[st][1]) for st in range(K))
     verify_ms = sum(ph[st][1].elapsed_time(ph[st][2]) for st in range(K))
@@ -258,6 +299,8 @@ def main():
     step_ms = (draft_ms + verify_ms) / K
 
     value = bytes_d / (draft_ms * 1e-3) / 1e9
+    # attainable verify roofline: min(MFMA peak, arithmetic intensity x HBM peak)
+    v_attain = min(MFMA_F16_PEAK_TFS, flops_v / bytes_v * HBM_PEAK_GBS / 1e3)
     v_tfs = flops_v / (verify_ms * 1e-3) / 1e12
     v_gbs = bytes_v / (verify_ms * 1e-3) / 1e9
     rv_ach = bytes_v / (sum(vg_ms) * 1e-3) / 1e9
@@ -309,6 +352,8 @@ def main():
                   "int4_bytes_avg": round(bytes_d / K)},
         "verify": {"ms": round(verify_ms / K, 4), "tflops": round(v_tfs, 3),
                    "frac_mfma": round(v_tfs / MFMA_F16_PEAK_TFS, 5), "gbps": round(v_gbs, 2),
+                   "attainable_tflops": round(v_attain, 2),
+                   "frac_attainable": round(v_tfs / v_attain, 4),
                    "frac_hbm": round(v_gbs / HBM_PEAK_GBS, 4),
                    "touched_experts_avg": round(sum(touched_v[i] for i in idx) / K, 3),
                    "f16_bytes_avg": round(bytes_v / K)},
@@ -322,6 +367,7 @@ def main():
                            "unit": "GB/s", "frac": round(rd_ach / HBM_PEAK_GBS, 4),
                            "avg_us": round(1e3 * sum(w4_ms) / K, 3),
                            "traffic": pmc_traffic("w4a16_grouped_ffn")},
+        "call_us": call_us,
         "host_wall_s": round(wall, 4),
         "gen_s": round(gen_s, 2),
     }
@@ -775,10 +821,45 @@ def cpu_baseline(layer, s, n):
         oracle.combine(y, m["pair_pos"], r["weights"])
         nbytes += int(m["n_active"]) * s.int4_bytes_per_expert
     dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{n} INT4 draft steps (T=1, route+gather+dequant+fp64 FFN+combine) of the "
-                      f"phi35 layer in {dt:.1f} s"}
+    out = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+           "kind": "oracle",
+           "sample": f"{n} INT4 draft steps (T=1, route+gather+dequant+fp64 FFN+combine) of the "
+                     f"phi35 layer in {dt:.1f} s"}
+    try:
+        model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
+                     if l.startswith("model name"))
+    except Exception:
+        model = None
+    out["cpu_model"] = model
+    # context: one step single-threaded, and the matmuls alone on pre-dequantised
+    # fp32 weights (the touched experts of one step)
+    try:
+        from threadpoolctl import threadpool_limits
+        x = synth.tokens(s, 1, step=0)
+        r = oracle.route_topk(x, layer["router"], s.k)
+        m = oracle.gather_maps(r["ids"], s.E)
+        b1 = int(m["n_active"]) * s.int4_bytes_per_expert
+        with threadpool_limits(1):
+            t1 = time.perf_counter()
+            oracle.grouped_ffn(x, m, layer["int4"], "int4")
+            d1 = time.perf_counter() - t1
+        out["single_thread_gbps"] = round(b1 / d1 / 1e9, 4)
+        ws = []
+        for e in [int(v) for v in m["active"] if v >= 0]:
+            q = layer["int4"][e]
+            ws.append((oracle.dequant_gptq(*q["w13"], dtype=np.float32),
+                       oracle.dequant_gptq(*q["w2"], dtype=np.float32)))
+        xf = x.astype(np.float32)
+        t2 = time.perf_counter()
+        for w13, w2 in ws:
+            oracle.swiglu_ffn(xf, w13[:, :s.I], w13[:, s.I:], w2)
+        d2 = time.perf_counter() - t2
+        out["matmul_only_gbps"] = round(b1 / d2 / 1e9, 4)
+        out["matmul_only_note"] = ("fp32 BLAS on pre-dequantised weights of one step's touched "
+                                   "experts, same algorithmic INT4 bytes")
+    except Exception as exc:  # context only
+        out["extra_error"] = str(exc)[:200]
+    return out
 
 
 if __name__ == "__main__":
