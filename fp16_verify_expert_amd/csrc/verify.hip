@@ -37,7 +37,7 @@ struct F16Args {
     int Ncol;   // output columns: I (phase 1) or H (phase 2)
     int I;
     int H;
-    int nCB;    // 16-column blocks
+    int nCB;    // column blocks: 16 columns, kGemvWaves in the matrix-vector kernel
     uint16_t* out;  // phase 1: h [rows, I]; phase 2: y [rows, H]
     int32_t* err;
 };
@@ -388,8 +388,164 @@ __global__ __launch_bounds__(64 * kVWaves) void f16_kernel(F16Args a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-vector variant (a few rows per expert: the shared expert of a
+// one-token draft step, any call with T <= kGemvMaxT).  With one row the
+// MFMA tiles would idle 15 of their 16 rows and the 16-column work units
+// leave most of the weight stream waiting on short per-wave pipelines; here
+// every weight byte of the launch is requested at once instead.  One wave
+// per output column: lane l holds the 16-byte chunks l, l + 64, ... of the
+// column's weight row (and of its up row in the gate/up projection), so each
+// load is 1 KB of one row, and the same chunks of the expert's rows, one row
+// at a time (the weights stay in registers for the next row).  Each lane
+// dots its chunks (v_dot2_f32_f16, fp32 sums in chunk order) and the wave's
+// 64 lane sums are added in a fixed order (wave_sum).  Measured against
+// staging RB rows in LDS per workgroup: one row at a time is faster up to
+// four rows (the LDS staging waits for every load of the launch first).
+constexpr int kGemvWaves = 4;      // columns per workgroup
+constexpr int kGemvMaxT = 4;       // tokens per call at or below which it runs
+constexpr int kGemvMaxChunks = 16; // 16-byte chunks per lane and row: K <= 8192
+
+__device__ __forceinline__ h2_t as_h2v(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
+
+__device__ __forceinline__ float dot8(u4_t w, uint4 x, float acc) {
+    acc = __builtin_amdgcn_fdot2(as_h2v(w.x), as_h2v(x.x), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2v(w.y), as_h2v(x.y), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2v(w.z), as_h2v(x.z), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2v(w.w), as_h2v(x.w), acc, false);
+    return acc;
+}
+
+// Sum over the wave in a fixed order: within each row of 16 lanes by DPP
+// (swap neighbours, swap pairs, rotate by 4, rotate by 8), then the four row
+// sums read from lanes 0, 16, 32 and 48.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
+    return v + __builtin_bit_cast(float, t);
+}
+__device__ __forceinline__ float lane_value(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
+    v = dpp_add<0x124>(v);  // row_ror 4
+    v = dpp_add<0x128>(v);  // row_ror 8
+    return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
+template <int PHASE, int CPL>
+__global__ __launch_bounds__(64 * kGemvWaves) void f16_gemv_kernel(F16Args a) {
+    constexpr int NM = (PHASE == 1) ? 2 : 1;  // weight rows per column
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int cb = blockIdx.x % a.nCB;
+    const int slot = blockIdx.x / a.nCB;
+    int e;
+    if (a.active) {
+        e = a.active[slot];  // -1 past the touched experts
+        if (e < 0) return;
+    } else {
+        e = slot;
+    }
+    if (a.mask && !a.mask[e]) return;
+    const int r0 = a.off[e];
+    const int r1 = a.off[e + 1];
+    if (r1 <= r0) return;
+    const uint16_t* W = (PHASE == 1) ? a.experts[e].w13 : a.experts[e].w2;
+    if (!W) {
+        if (tid == 0 && cb == 0) flag_error(a.err, SMOE_DERR_NULL_EXPERT);
+        return;
+    }
+    const int K = a.K;
+    const int kc = K >> 3;  // 16-byte chunks per row
+    const int n = cb * kGemvWaves + wave;
+    const int nc = (n < a.Ncol) ? n : a.Ncol - 1;  // clamped column: loads stay in the matrix
+    const u4_t wzero = {0u, 0u, 0u, 0u};
+
+    // chunk j of this lane: lane + 64 j, clamped into the row (the clamped
+    // ones are masked where used)
+    auto load_row = [&](int r, uint4 (&xr)[CPL]) {
+        const size_t src = (PHASE == 1) ? (size_t)a.sorted_token[r] : (size_t)r;
+        const uint4* xrow = reinterpret_cast<const uint4*>(a.xin + src * K);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = lane + 64 * j;
+            xr[j] = xrow[c < kc ? c : kc - 1];
+        }
+    };
+    // the column's weight chunks, all of them, then the first row
+    u4_t wv[NM][CPL];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        const size_t row = (m == 0) ? (size_t)nc : (size_t)a.I + nc;
+        gptr<u4_t> wr = as_global(reinterpret_cast<const u4_t*>(W + row * K));
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = lane + 64 * j;
+            wv[m][j] = __builtin_nontemporal_load(wr + (c < kc ? c : kc - 1));
+        }
+    }
+    uint4 xr[CPL];
+    load_row(r0, xr);
+    // keep every load above ahead of the first use (the scheduler would
+    // otherwise start on the first chunks and issue the last ones a round
+    // trip later)
+    __builtin_amdgcn_sched_barrier(0);
+
+    auto one_row = [&](int r) {
+        float acc[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) acc[m] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const bool in = lane + 64 * j < kc;
+#pragma unroll
+            for (int m = 0; m < NM; ++m) acc[m] = dot8(in ? wv[m][j] : wzero, xr[j], acc[m]);
+        }
+        float tot[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) tot[m] = wave_sum(acc[m]);
+        if (lane == 0 && n < a.Ncol) {
+            const float v = (PHASE == 1) ? silu_f(tot[0]) * tot[NM - 1] : tot[0];
+            a.out[(size_t)r * a.Ncol + n] = f2h(v);
+        }
+    };
+    // the first row straight-line (its waits then cover only what each step
+    // needs), further rows of the group in a loop
+    one_row(r0);
+    for (int r = r0 + 1; r < r1; ++r) {
+        load_row(r, xr);
+        one_row(r);
+    }
+}
+
+template <int PHASE, int CPL>
+hipError_t launch_gemv_cpl(const F16Args& a, int slots, hipStream_t s) {
+    hipLaunchKernelGGL((f16_gemv_kernel<PHASE, CPL>), dim3(slots * a.nCB),
+                       dim3(64 * kGemvWaves), 0, s, a);
+    return hipGetLastError();
+}
+
+// a.nCB must be ceil(Ncol / kGemvWaves) and K at most 512 * kGemvMaxChunks.
+template <int PHASE>
+hipError_t launch_gemv_phase(const F16Args& a, int slots, hipStream_t s) {
+    const int need = (a.K / 8 + 63) / 64;  // chunks per lane and row
+    if (need <= 2) return launch_gemv_cpl<PHASE, 2>(a, slots, s);
+    if (need <= 4) return launch_gemv_cpl<PHASE, 4>(a, slots, s);
+    if (need <= 6) return launch_gemv_cpl<PHASE, 6>(a, slots, s);
+    if (need <= 8) return launch_gemv_cpl<PHASE, 8>(a, slots, s);
+    if (need <= 12) return launch_gemv_cpl<PHASE, 12>(a, slots, s);
+    return launch_gemv_cpl<PHASE, kGemvMaxChunks>(a, slots, s);
+}
+
 #ifndef SMOE_DENSE_MIN_ROWS
 #define SMOE_DENSE_MIN_ROWS 64  // mean rows per expert from which the tiled GEMM is used
+#endif
+#ifndef SMOE_VF_GEMV
+#define SMOE_VF_GEMV 1  // the one-wave-per-column kernel for T <= kGemvMaxT
 #endif
 #ifndef SMOE_VF_LONG
 #define SMOE_VF_LONG 8
@@ -443,14 +599,6 @@ hipError_t launch_verify_ffn(const uint16_t* x, const int32_t* sorted_token, con
         return launch_dense_ffn(x, sorted_token, off, active, n_active, experts, mask, rows, H, I,
                                 E, y, h, plan, err, s);
     }
-    // row blocks of 16 held per weight stream, sized for the largest group
-    // expected: all rows when there is one expert (a shared expert), else
-    // about twice the mean plus slack (bigger groups take extra passes)
-    const int mean = (rows + E - 1) / E;
-    int est = (E == 1) ? rows : 2 * mean + 8;
-    if (est > T) est = T;
-    const int RB = (est <= 16) ? 1 : 2;
-    const int slots = active ? (E < rows ? E : rows) : E;
     F16Args a1{};
     a1.xin = x;
     a1.sorted_token = sorted_token;
@@ -463,18 +611,36 @@ hipError_t launch_verify_ffn(const uint16_t* x, const int32_t* sorted_token, con
     a1.Ncol = I;
     a1.I = I;
     a1.H = H;
-    a1.nCB = I / 16;
     a1.out = h;
     a1.err = err;
-    hipError_t st = launch_phase<1>(a1, slots, RB, s);
-    if (st != hipSuccess) return st;
     F16Args a2 = a1;
     a2.xin = h;
     a2.sorted_token = nullptr;
     a2.K = I;
     a2.Ncol = H;
-    a2.nCB = H / 16;
     a2.out = y;
+    const int slots = active ? (E < rows ? E : rows) : E;
+    // A few tokens (each at most once per expert, so at most T rows per
+    // group; a longer group just takes more rows in turn): one wave per column.
+    if (SMOE_VF_GEMV && T <= kGemvMaxT && H <= 512 * kGemvMaxChunks &&
+        I <= 512 * kGemvMaxChunks) {
+        a1.nCB = (I + kGemvWaves - 1) / kGemvWaves;
+        a2.nCB = (H + kGemvWaves - 1) / kGemvWaves;
+        hipError_t st = launch_gemv_phase<1>(a1, slots, s);
+        if (st != hipSuccess) return st;
+        return launch_gemv_phase<2>(a2, slots, s);
+    }
+    // row blocks of 16 held per weight stream, sized for the largest group
+    // expected: all rows when there is one expert (a shared expert), else
+    // about twice the mean plus slack (bigger groups take extra passes)
+    const int mean = (rows + E - 1) / E;
+    int est = (E == 1) ? rows : 2 * mean + 8;
+    if (est > T) est = T;
+    const int RB = (est <= 16) ? 1 : 2;
+    a1.nCB = I / 16;
+    a2.nCB = H / 16;
+    hipError_t st = launch_phase<1>(a1, slots, RB, s);
+    if (st != hipSuccess) return st;
     return launch_phase<2>(a2, slots, RB, s);
 }
 }  // namespace smoe

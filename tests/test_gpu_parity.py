@@ -416,7 +416,10 @@ def test_draft_route_ffn_nan_logit_and_repeat():
 
 
 VERIFY_CASES = [(synth.TINY, 17), (synth.TINY, 40), (synth.QWEN, 9), (synth.PHI, 17),
-                (synth.DS, 16)]
+                (synth.DS, 16),
+                # T <= 4: the one-wave-per-column kernel (1, 2 and 4 rows per block)
+                (synth.TINY, 1), (synth.TINY, 3), (synth.QWEN, 1), (synth.DS, 2),
+                (synth.QWEN, 4), (synth.PHI, 1)]
 
 
 @pytest.mark.parametrize("shape,T", VERIFY_CASES, ids=lambda v: getattr(v, "name", str(v)))
@@ -605,8 +608,13 @@ def test_null_expert_flagged():
 
 # ---------------------------------------------------------------- S5 ----
 
+_TINY_SH = dataclasses.replace(synth.TINY, name="tiny_shared", shared_I=384)
+
+
 @pytest.mark.parametrize("shape,T", [(synth.DS, 1), (synth.DS, 16), (synth.QWEN, 9),
-                                     (synth.QWEN, 17)], ids=lambda v: getattr(v, "name", str(v)))
+                                     (synth.QWEN, 17), (synth.QWEN, 1), (synth.QWEN, 4),
+                                     (synth.DS, 3), (_TINY_SH, 1), (_TINY_SH, 2)],
+                         ids=lambda v: getattr(v, "name", str(v)))
 def test_shared_expert(shape, T):
     sh = synth.shared_expert(shape)
     x = synth.tokens(shape, T, step=1)
@@ -619,6 +627,24 @@ def test_shared_expert(shape, T):
     ws = fve.new_workspace(1, T, 1, shape.H, shape.shared_I, 1)
     y = fve.verify_grouped_gemm(dx, iota, offs, tab, T, T, shape.H, shape.shared_I, 1, ws)
     assert_fp16_close(host(y)[:T], ref, f"shared {shape.name} T={T}")
+
+
+@pytest.mark.parametrize("T,rows", [(1, 3), (2, 5), (3, 9), (4, 4)])
+def test_verify_few_tokens_long_groups(T, rows):
+    """T <= 4 with an expert group longer than the kernel's row block (a
+    token listed several times): every row is still FFN(x[token])."""
+    shape = _TINY_SH
+    sh = synth.shared_expert(shape)
+    x = synth.tokens(shape, T, step=3)
+    st = (np.arange(rows) * 7 + 1) % T
+    ref = oracle.expert_ffn_f16(x[st], sh["w13"], sh["w2"])
+    tab, keep = upload_f16([(sh["w13"], sh["w2"])])
+    offs = torch.tensor([0, rows], dtype=torch.int32, device="cuda")
+    ws = fve.new_workspace(1, T, rows, shape.H, shape.shared_I, 1)
+    y = fve.verify_grouped_gemm(dev(x), dev(st.astype(np.int32)), offs, tab, T, rows, shape.H,
+                                shape.shared_I, 1, ws)
+    assert_fp16_close(host(y)[:rows], ref, f"few tokens T={T} rows={rows}")
+    del keep
 
 
 # ---------------------------------------------------------------- S7 ----
