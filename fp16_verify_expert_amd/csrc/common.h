@@ -48,12 +48,6 @@ hipError_t launch_route_plan(const uint16_t* x, const uint16_t* wr, const uint16
                              int32_t* ids, float* w, float* gate, int32_t* off, int32_t* st,
                              int32_t* sp, int32_t* pp, int32_t* active, int32_t* n_active,
                              int32_t* err, hipStream_t s);
-// the same with the layer's ELB row (nullable) given directly
-hipError_t launch_route_plan_row(const uint16_t* x, const uint16_t* wr, const uint16_t* wsg,
-                                 int T, int H, int E, int k, int renorm, int32_t* counters_row,
-                                 int32_t* ids, float* w, float* gate, int32_t* off, int32_t* st,
-                                 int32_t* sp, int32_t* pp, int32_t* active, int32_t* n_active,
-                                 int32_t* err, hipStream_t s);
 hipError_t launch_elb_count(const int32_t* ids, int n, int E, int layer, int32_t* counters,
                             int32_t* err, hipStream_t s);
 hipError_t launch_gather(const int32_t* ids, int n, int k, int E, int32_t* off, int32_t* st,
@@ -64,8 +58,8 @@ hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, cons
                             const smoe_w4_expert* experts, int T, int k, int H, int I, int E,
                             int bits, uint16_t* y, void* ws, int32_t* err, hipStream_t s);
 size_t w4a16_workspace_bytes(int T, int k, int H, int I, int E);
-// One-token draft step: routing, ELB, maps and the gate/up projection in one
-// launch, then the down projection.
+// One-token draft step: the router logits, then routing, ELB, maps and the
+// gate/up projection in one launch, then the down projection.
 bool draft_route_ffn_supported(int E, int k);
 hipError_t launch_draft_route_ffn(const uint16_t* x, const uint16_t* wr, const uint16_t* wsg,
                                   int H, int E, int k, int renorm, int32_t* counters_row,

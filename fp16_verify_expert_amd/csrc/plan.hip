@@ -60,24 +60,15 @@ __global__ __launch_bounds__(kPlanThreads) void route_plan_kernel(
 }  // namespace
 
 namespace smoe {
-hipError_t launch_route_plan_row(const uint16_t* x, const uint16_t* wr, const uint16_t* wsg,
-                                 int T, int H, int E, int k, int renorm, int32_t* counters_row,
-                                 int32_t* ids, float* w, float* gate, int32_t* off, int32_t* st,
-                                 int32_t* sp, int32_t* pp, int32_t* active, int32_t* n_active,
-                                 int32_t* err, hipStream_t s) {
-    route_plan_kernel<<<dim3(1), dim3(kPlanThreads), 0, s>>>(x, wr, wsg, T, H, E, k, renorm,
-                                                             counters_row, ids, w, gate, off, st,
-                                                             sp, pp, active, n_active, err);
-    return hipGetLastError();
-}
-
 hipError_t launch_route_plan(const uint16_t* x, const uint16_t* wr, const uint16_t* wsg, int T,
                              int H, int E, int k, int renorm, int layer, int32_t* counters,
                              int32_t* ids, float* w, float* gate, int32_t* off, int32_t* st,
                              int32_t* sp, int32_t* pp, int32_t* active, int32_t* n_active,
                              int32_t* err, hipStream_t s) {
-    return launch_route_plan_row(x, wr, wsg, T, H, E, k, renorm,
-                                 counters ? counters + (size_t)layer * E : nullptr, ids, w, gate,
-                                 off, st, sp, pp, active, n_active, err, s);
+    int32_t* counters_row = counters ? counters + (size_t)layer * E : nullptr;
+    route_plan_kernel<<<dim3(1), dim3(kPlanThreads), 0, s>>>(x, wr, wsg, T, H, E, k, renorm,
+                                                             counters_row, ids, w, gate, off, st,
+                                                             sp, pp, active, n_active, err);
+    return hipGetLastError();
 }
 }  // namespace smoe

@@ -151,27 +151,6 @@ SMOE_DEV void wave_logits(const uint16_t* __restrict__ x, const uint16_t* __rest
     }
 }
 
-// wave_logits with up to 32 weight chunks per lane in flight (all the items
-// of a wave for a decode step's router at most shapes): one memory round trip
-// instead of one per batch.  Values are identical to wave_logits (same
-// per-item order).
-SMOE_DEV void wave_logits_wide(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-                               const uint16_t* __restrict__ wsg, int H, int E, int nvec,
-                               int first, int n_items, int stride, float* out, int lane) {
-    const int cpl = ((H >> 3) + 63) / 64;
-    if (cpl <= 1) {
-        wave_logits_batched<16, 1>(x, wr, wsg, H, E, nvec, first, n_items, stride, out, lane);
-    } else if (cpl <= 2) {
-        wave_logits_batched<16, 2>(x, wr, wsg, H, E, nvec, first, n_items, stride, out, lane);
-    } else if (cpl <= 4) {
-        wave_logits_batched<8, 4>(x, wr, wsg, H, E, nvec, first, n_items, stride, out, lane);
-    } else if (cpl <= 8) {
-        wave_logits_batched<4, 8>(x, wr, wsg, H, E, nvec, first, n_items, stride, out, lane);
-    } else {
-        wave_logits(x, wr, wsg, H, E, nvec, first, n_items, stride, out, lane);
-    }
-}
-
 // Ranking of (logit, expert id) pairs: larger logit first, NaN below every
 // number, equal logits (-0 equal to +0, or two NaNs) lower id first.  As a
 // 64-bit key: the logit's bits mapped to an unsigned order (NaN lowest), then

@@ -1058,18 +1058,20 @@ __attribute__((amdgpu_waves_per_eu(SMOE_W4_MFMA_WPE))) void w4_mfma_kernel(W4Arg
 // --------------------------------------------- routing + gate/up, T = 1 ----
 //
 // The one-token draft step's routing, ELB update and gather maps folded into
-// the gate/up launch (Key Contributions 4 of the pages: routing, gathering and
-// the experts' FFN of a draft step in one fused launch).  Every workgroup
-// evaluates the token's E (+1 shared-gate) router logits with the pinned
-// routines of the routing kernels, so every workgroup reaches the same
-// selection, bit-identical to moe_route_topk / moe_route_plan; slot s then
-// takes the s-th smallest selected id, which is the expert moe_gather places
-// at sorted row s.  Workgroup 0 also writes the routing outputs, the ELB
-// increments and the maps, which the down projection and the combine read
-// after this launch.
+// the gate/up launch (Specter, Key Contributions 4: routing, gathering and the
+// experts' FFN of a draft step in one fused launch).  Every workgroup reads
+// the token's E (+1 shared-gate) router logits, computed just before by
+// route_logits_kernel with the pinned routine of the routing kernels, and
+// takes the top k itself, so every workgroup reaches the same selection,
+// bit-identical to moe_route_topk / moe_route_plan; slot s then takes the
+// s-th smallest selected id, which is the expert moe_gather places at sorted
+// row s.  One extra workgroup writes the routing outputs, the ELB increments
+// and the maps, which the down projection and the combine read after this
+// launch.
 struct RouteArgs {
     const uint16_t* wr;   // router [E, H]
     const uint16_t* wsg;  // shared-expert gate row [H] or null
+    const float* logits;  // the E (+1) logits from route_logits_kernel
     int k, renorm;
     int32_t* counters_row;  // ELB row of the layer or null
     int32_t* ids;
@@ -1085,6 +1087,21 @@ struct RouteArgs {
 
 constexpr int kFusedMaxK = 32;
 
+// The token's router logits, one per wave, for route_w4_kernel (every one of
+// its workgroups needs all of them; reading the whole router in each, from
+// L2, measured slower than this extra launch at every decode shape, by 1-3
+// us for a 131 KB router and more for larger ones).  Same routine and order
+// as the routing kernels, so the logits are bit-identical.
+__global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ wr,
+                                                           const uint16_t* __restrict__ wsg,
+                                                           int H, int E, int nvec,
+                                                           float* __restrict__ lg) {
+    const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int nwaves = gridDim.x * (blockDim.x >> 6);
+    smoe_route::wave_logits(x, wr, wsg, H, E, nvec, wave, nvec, nwaves, lg, threadIdx.x & 63);
+}
+
 template <int LPR, int NG>
 __global__ __launch_bounds__(64 * kT1MaxWaves)
 __attribute__((amdgpu_waves_per_eu(2))) void route_w4_kernel(W4Args a, RouteArgs r) {
@@ -1094,24 +1111,32 @@ __attribute__((amdgpu_waves_per_eu(2))) void route_w4_kernel(W4Args a, RouteArgs
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int nwaves = blockDim.x >> 6;
     const int cb = blockIdx.x % a.nCB;
     const int slot = blockIdx.x / a.nCB;
     const int E = a.E, k = r.k;
 
     const smoe_w4_expert spec = spec_table(a, lane);
 
-    // 1. router logits, wave w taking vectors w, w + nwaves, ..., with all
-    //    of its router rows in flight at once where registers allow
+    // 1. the router logits of the launch before
     const int nvec = E + (r.wsg ? 1 : 0);
-    smoe_route::wave_logits_wide(a.xin, r.wr, r.wsg, a.K, E, nvec, wave, nvec, nwaves, lg_s,
-                                 lane);
+    for (int i = tid; i < nvec; i += blockDim.x) lg_s[i] = r.logits[i];
     __syncthreads();
-    // 2. the selected ids (wave 0); their weights are computed by workgroup 0
-    //    after its share of the projection
+    // 2. the last workgroup (beyond the projection's): routing outputs (the
+    //    routing kernels' own routine), the ELB increments and the maps,
+    //    beside the projection rather than after a share of it
+    if (blockIdx.x == (unsigned)(k * a.nCB)) {
+        if (wave == 0)
+            smoe_route::topk_softmax_wave(lg_s, E, k, r.renorm, r.wsg != nullptr, lane, r.ids,
+                                          r.w, r.gate, ids_s);
+        __syncthreads();
+        smoe_maps::one_token_maps(ids_s, k, E, r.counters_row, r.off, r.sorted_token,
+                                  r.sorted_pair, r.pair_pos, r.active, r.n_active);
+        return;
+    }
+    // 3. the selected ids (wave 0)
     if (wave == 0) smoe_route::topk_ids_wave(lg_s, E, k, lane, ids_s);
     __syncthreads();
-    // 3. this slot's expert: the slot-th smallest selected id (the ids of one
+    // 4. this slot's expert: the slot-th smallest selected id (the ids of one
     //    token are distinct), i.e. the expert moe_gather places at row slot
     int e = -1;
     for (int j = 0; j < k; ++j) {
@@ -1119,7 +1144,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void route_w4_kernel(W4Args a, RouteArgs
         for (int i = 0; i < k; ++i) less += (ids_s[i] < ids_s[j]) ? 1 : 0;
         if (less == slot) e = ids_s[j];
     }
-    // 4. this slot's block of the gate/up projection (the token row is in L2
+    // 5. this slot's block of the gate/up projection (the token row is in L2
     //    after the logits; it is requested here to keep registers free)
     if (cb == 0) write_slot_desc(a, spec, slot, e);
     if (e >= 0) {
@@ -1128,14 +1153,6 @@ __attribute__((amdgpu_waves_per_eu(2))) void route_w4_kernel(W4Args a, RouteArgs
         one_token_block<4, 1, LPR, NG>(a, carve_lds<4>(smem, a), pick_mat<1>(a, spec, e), xv,
                                        slot, cb);
     }
-    // 5. workgroup 0: routing outputs (the routing kernels' own routine), the
-    //    ELB increments and the maps
-    if (blockIdx.x != 0) return;
-    if (wave == 0)
-        smoe_route::topk_softmax_wave(lg_s, E, k, r.renorm, r.wsg != nullptr, lane, r.ids, r.w,
-                                      r.gate, nullptr);
-    smoe_maps::one_token_maps(ids_s, k, E, r.counters_row, r.off, r.sorted_token, r.sorted_pair,
-                              r.pair_pos, r.active, r.n_active);
 }
 
 // ---------------------------------------------------------------- launch ----
@@ -1260,9 +1277,14 @@ namespace smoe {
 // h [T*k, I] fp16, then (one-token steps) a SlotDesc per slot
 static size_t h_bytes(int T, int k, int I) { return ((size_t)T * k * I * 2 + 255) & ~(size_t)255; }
 
-size_t w4a16_workspace_bytes(int T, int k, int /*H*/, int I, int E) {
+static size_t desc_bytes(int T, int k, int E) {
     const int slots = E < T * k ? E : T * k;
-    return h_bytes(T, k, I) + (((size_t)slots * sizeof(SlotDesc) + 255) & ~(size_t)255);
+    return ((size_t)slots * sizeof(SlotDesc) + 255) & ~(size_t)255;
+}
+
+// h, the slot descriptors, then the router logits of a one-token step
+size_t w4a16_workspace_bytes(int T, int k, int /*H*/, int I, int E) {
+    return h_bytes(T, k, I) + desc_bytes(T, k, E) + (((size_t)(E + 1) * 4 + 255) & ~(size_t)255);
 }
 
 bool w4a16_shape_supported(int H, int I) {
@@ -1345,37 +1367,30 @@ hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, cons
 
 bool draft_route_ffn_supported(int E, int k) { return E <= 256 && k <= kFusedMaxK; }
 
-// Router size up to which the routing is folded into the gate/up launch.
-// Every workgroup reads the whole router from L2; measured on the decode
-// shapes (one token): folded is faster with a 139 KB router (Phi-3.5-MoE:
-// 38.3 against 42.6 us for routing + both projections) and slower with
-// 250-262 KB (Qwen1.5-MoE 32.3 against 29.4 us, DeepSeek-V2-Lite 35.8 against
-// 33.3 us), where the single-workgroup routing plan runs first instead.
-constexpr size_t kFoldedRouterBytes = 192 * 1024;
-
 hipError_t launch_draft_route_ffn(const uint16_t* x, const uint16_t* wr, const uint16_t* wsg,
                                   int H, int E, int k, int renorm, int32_t* counters_row,
                                   int32_t* ids, float* w, float* gate, int32_t* off, int32_t* st,
                                   int32_t* sp, int32_t* pp, int32_t* active, int32_t* n_active,
                                   const smoe_w4_expert* experts, int I, uint16_t* y, void* ws,
                                   int32_t* err, hipStream_t s) {
-    const size_t router_bytes = (size_t)(E + (wsg ? 1 : 0)) * H * 2;
-    if (router_bytes > kFoldedRouterBytes) {
-        hipError_t e0 = launch_route_plan_row(x, wr, wsg, 1, H, E, k, renorm, counters_row, ids,
-                                              w, gate, off, st, sp, pp, active, n_active, err, s);
-        if (e0 != hipSuccess) return e0;
-        return launch_w4a16_ffn(x, st, off, active, n_active, experts, 1, k, H, I, E, 4, y, ws,
-                                err, s);
-    }
+    const int nvec = E + (wsg ? 1 : 0);
     uint16_t* h = static_cast<uint16_t*>(ws);
     SlotDesc* desc = reinterpret_cast<SlotDesc*>(static_cast<char*>(ws) + h_bytes(1, k, I));
+    float* logits = reinterpret_cast<float*>(static_cast<char*>(ws) + h_bytes(1, k, I) +
+                                             desc_bytes(1, k, E));
+    constexpr int kLogitWaves = 4;
+    route_logits_kernel<<<dim3((nvec + kLogitWaves - 1) / kLogitWaves), dim3(64 * kLogitWaves),
+                          0, s>>>(x, wr, wsg, H, E, nvec, logits);
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
     const PhasePlan p1 = plan_phase(1, k, 1, H, 2 * I, I, 1, 4);
     const W4Args a1 = phase_args(p1, x, st, off, active, n_active, experts, H, 2 * I, I, 1, E, h,
                                  err, desc);
-    RouteArgs r{wr, wsg, k, renorm, counters_row, ids, w, gate, off, st, sp, pp, active, n_active};
-    const dim3 grid(k * p1.nCB), block(64 * p1.waves);
-#define SMOE_ROUTE_W4(L, NG) hipLaunchKernelGGL((route_w4_kernel<L, NG>), grid, block, p1.lds, s, a1, r)
+    RouteArgs r{wr,  wsg, logits, k,  renorm, counters_row, ids,    w,
+                gate, off, st,     sp, pp,     active,       n_active};
+    const dim3 grid(k * p1.nCB + 1), block(64 * p1.waves);  // + the routing workgroup
     if (p1.ng < 1 || p1.ng > 4) return hipErrorInvalidValue;  // excluded by the shape checks
+#define SMOE_ROUTE_W4(L, NG) hipLaunchKernelGGL((route_w4_kernel<L, NG>), grid, block, p1.lds, s, a1, r)
     if (p1.lpr == 16) {
         if (p1.ng == 1) SMOE_ROUTE_W4(16, 1);
         else if (p1.ng == 2) SMOE_ROUTE_W4(16, 2);

@@ -239,13 +239,12 @@ smoe_status wq_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
 
 /* ------------------------------------------------------------------------
  * moe_draft_route_ffn -- one-token (T = 1) draft step of a layer: the work
- * of moe_route_plan followed by w4a16_grouped_ffn, in two launches instead of
- * three ([S1] Key Contributions 4: routing, gathering and the experts' FFN of
- * a draft step inside one fused launch; the routing is folded into the
- * gate/up projection, whose every workgroup evaluates the router itself).
- * With a router ((E + shared gate) x H fp16) above 192 KB the routing plan
- * runs as its own launch first (three launches; measured faster there: every
- * workgroup would read the whole router).  The outputs are the same.
+ * of moe_route_plan followed by w4a16_grouped_ffn ([S1] Key Contributions 4:
+ * routing, gathering and the experts' FFN of a draft step inside one fused
+ * launch).  Three launches: the router logits (one wave per router row),
+ * then the gate/up projection, whose every workgroup takes the top k of
+ * those logits itself (one extra workgroup writes the routing outputs, the
+ * ELB increments and the maps), then the down projection.
  *
  * Arguments keep the meaning and layout of those two calls with T = 1:
  *   x              fp16 [1, H]
