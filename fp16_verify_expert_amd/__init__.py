@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsmoe.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "smoe.h")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 SMOE_DERR_BAD_ID = 1
 SMOE_DERR_NULL_EXPERT = 2
@@ -51,8 +51,9 @@ _SIGS = {
     "wq_grouped_ffn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
                             _sz, _vp, _vp]),
     "moe_draft_route_ffn": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp,
-                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
-                                 _vp]),
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _vp, _i, _vp, _vp,
+                                 _vp, _sz, _vp, _vp]),
     "verify_grouped_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp,
                                  _vp, _sz, _vp, _vp]),
     "moe_combine": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, ctypes.c_float,
@@ -258,9 +259,13 @@ def wq_grouped_ffn(x, maps, table, T: int, k: int, H: int, I: int, E: int, works
 def moe_draft_route_ffn(x, w_router, k: int, table, I: int, workspace,
                         renormalize: bool = False, w_shared_gate=None, *, counters=None,
                         layer: int = 0, err_word=None, topk_ids=None, topk_w=None,
-                        shared_gate=None, maps=None, y_sorted=None, stream=None):
-    """One-token draft step: moe_route_plan and w4a16_grouped_ffn in two
-    launches.  Returns (topk_ids, topk_w, shared_gate, maps, y_sorted)."""
+                        shared_gate=None, maps=None, y_sorted=None, shared=None, shared_h=None,
+                        shared_out=None, stream=None):
+    """One-token draft step: moe_route_plan and w4a16_grouped_ffn in three
+    launches.  With shared = (w13 [2 Is, H], w2 [H, Is]) fp16, a dense shared
+    expert computed in the same launches (shared_h: [Is] fp16 scratch,
+    shared_out: [1, H] fp16 out).  Returns (topk_ids, topk_w, shared_gate,
+    maps, y_sorted), plus shared_out when a shared expert is given."""
     _check(x, torch.float16, "x")
     _check(w_router, torch.float16, "w_router")
     T, H = x.shape
@@ -284,12 +289,27 @@ def moe_draft_route_ffn(x, w_router, k: int, table, I: int, workspace,
         maps = _new_maps(1, k, E, dev)
     if y_sorted is None:
         y_sorted = torch.empty((k, H), dtype=torch.float16, device=dev)
+    sw13 = sw2 = None
+    Is = 0
+    if shared is not None:
+        sw13, sw2 = shared
+        _check(sw13, torch.float16, "shared w13")
+        _check(sw2, torch.float16, "shared w2")
+        Is = sw2.shape[1]
+        if shared_h is None:
+            shared_h = torch.empty((Is,), dtype=torch.float16, device=dev)
+        if shared_out is None:
+            shared_out = torch.empty((1, H), dtype=torch.float16, device=dev)
     _call("moe_draft_route_ffn", _p(x), _p(w_router), _p(w_shared_gate), H, I, E, k,
           1 if renormalize else 0, layer, L, _p(counters), _p(table), 128, _p(topk_ids),
           _p(topk_w), _p(shared_gate) if w_shared_gate is not None else None,
           _p(maps["offsets"]), _p(maps["sorted_token"]), _p(maps["sorted_pair"]),
           _p(maps["pair_pos"]), _p(maps["active"]), _p(maps["n_active"]), _p(y_sorted),
+          _p(sw13), _p(sw2), Is, _p(shared_h) if shared is not None else None,
+          _p(shared_out) if shared is not None else None,
           _p(workspace), workspace.numel() * workspace.element_size(), _p(err_word), _s(stream))
+    if shared is not None:
+        return topk_ids, topk_w, shared_gate, maps, y_sorted, shared_out
     return topk_ids, topk_w, shared_gate, maps, y_sorted
 
 

@@ -93,6 +93,9 @@ class ChunkEngine:
                       for T in (1, verify_T)} if shared_I else {}
         self.sh_out = {T: torch.empty((T, H), dtype=torch.float16, device=dev)
                        for T in (1, verify_T)} if shared_I else {}
+        # the draft step's shared expert rides in the routed launches: its h
+        # between the projections
+        self.sh_h = torch.empty((max(shared_I, 1),), dtype=torch.float16, device=dev)
         self.iota = torch.arange(max(verify_T, 1), dtype=torch.int32, device=dev)
         self.offs = {T: torch.tensor([0, T], dtype=torch.int32, device=dev) for T in (1, verify_T)}
         self.stats = dict(staged_experts=0, staged_bytes=0, hit_experts=0, miss_experts=0)
@@ -130,14 +133,17 @@ class ChunkEngine:
         layer's expert choices in the ELB table."""
         xn = x
         for l, ly in enumerate(self.layers):
-            sh = self._shared_fork(l, xn)
             # routing, ELB update and gather maps folded into the gate/up
-            # launch, then the down projection
-            ids, w, gate, maps, y = moe_draft_route_ffn(xn, ly.router, self.k, self.t4[l],
-                                                        self.I, self.ws_d, False, ly.shared_gate,
-                                                        counters=self.counters, layer=l,
-                                                        err_word=self.err)
-            self._join()
+            # launch, then the down projection; the FP16 shared expert's
+            # columns in the same two launches (measured: as two launches of
+            # its own on a side stream it overlapped nothing, 15.6 us of a
+            # 39.5 us layer-step)
+            res = moe_draft_route_ffn(xn, ly.router, self.k, self.t4[l], self.I, self.ws_d, False,
+                                      ly.shared_gate, counters=self.counters, layer=l,
+                                      err_word=self.err, shared=ly.shared, shared_h=self.sh_h,
+                                      shared_out=self.sh_out[1] if ly.shared is not None else None)
+            ids, w, gate, maps, y = res[:5]
+            sh = res[5] if ly.shared is not None else None
             out, xn_next = moe_combine(y, maps["pair_pos"], w, sh, gate, x, norm_out=True)
             if record is not None:
                 record.append(dict(layer=l, x=x, xn=xn, ids=ids, out=out, xn_next=xn_next))

@@ -78,6 +78,9 @@ smoe_status check_hek(int H, int E, int k) {
 }
 
 constexpr long long kMaxPairs = 1 << 20;
+// one-row matrix-vector reductions of a shared expert: 16 chunks of 16 bytes
+// per lane and row
+constexpr int kSharedMaxK = 8192;
 
 }  // namespace
 
@@ -248,11 +251,25 @@ smoe_status moe_draft_route_ffn(const uint16_t* x, const uint16_t* w_router,
                                 int32_t* topk_ids, float* topk_w, float* shared_gate,
                                 int32_t* expert_offsets, int32_t* sorted_token,
                                 int32_t* sorted_pair, int32_t* pair_pos, int32_t* active,
-                                int32_t* n_active, uint16_t* y_sorted, void* workspace,
-                                size_t workspace_bytes, int32_t* err_word, void* stream) {
+                                int32_t* n_active, uint16_t* y_sorted,
+                                const uint16_t* shared_w13, const uint16_t* shared_w2,
+                                int shared_I, uint16_t* shared_h, uint16_t* shared_out,
+                                void* workspace, size_t workspace_bytes, int32_t* err_word,
+                                void* stream) {
     REQUIRE(x && w_router && experts && topk_ids && topk_w && expert_offsets && sorted_token &&
                 sorted_pair && pair_pos && active && n_active && y_sorted,
             SMOE_ERR_NULL, "moe_draft_route_ffn: a required pointer is NULL");
+    REQUIRE(!shared_w13 || (shared_w2 && shared_h && shared_out), SMOE_ERR_NULL,
+            "moe_draft_route_ffn: shared_w2, shared_h and shared_out are required with shared_w13");
+    REQUIRE(!shared_w13 || (shared_I > 0 && shared_I % 128 == 0 &&
+                            shared_I <= kSharedMaxK && H <= kSharedMaxK),
+            SMOE_ERR_SHAPE,
+            "moe_draft_route_ffn: shared_I=%d must be a positive multiple of 128, and shared_I "
+            "and H at most %d", shared_I, kSharedMaxK);
+    REQUIRE(!shared_w13 || (aligned(shared_w13, 16) && aligned(shared_w2, 16) &&
+                            aligned(shared_h, 16)),
+            SMOE_ERR_SHAPE,
+            "moe_draft_route_ffn: shared_w13, shared_w2 and shared_h must be 16-byte aligned");
     REQUIRE(!w_shared_gate || shared_gate, SMOE_ERR_NULL,
             "moe_draft_route_ffn: shared_gate output is required with w_shared_gate");
     smoe_status st = check_hek(H, E, k);
@@ -280,7 +297,9 @@ smoe_status moe_draft_route_ffn(const uint16_t* x, const uint16_t* w_router,
                                      counters ? counters + (size_t)layer * E : nullptr, topk_ids,
                                      topk_w, shared_gate, expert_offsets, sorted_token,
                                      sorted_pair, pair_pos, active, n_active, experts, I,
-                                     y_sorted, workspace, err_word,
+                                     y_sorted, workspace, shared_w13,
+                                     shared_w13 ? shared_w2 : nullptr, shared_w13 ? shared_I : 0,
+                                     shared_h, shared_out, err_word,
                                      static_cast<hipStream_t>(stream)),
         "moe_draft_route_ffn launch");
 }

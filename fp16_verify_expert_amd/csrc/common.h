@@ -59,14 +59,16 @@ hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, cons
                             int bits, uint16_t* y, void* ws, int32_t* err, hipStream_t s);
 size_t w4a16_workspace_bytes(int T, int k, int H, int I, int E);
 // One-token draft step: the router logits, then routing, ELB, maps and the
-// gate/up projection in one launch, then the down projection.
+// gate/up projection in one launch, then the down projection; an optional
+// dense shared expert (sw13 non-null) computed in the same two launches.
 bool draft_route_ffn_supported(int E, int k);
 hipError_t launch_draft_route_ffn(const uint16_t* x, const uint16_t* wr, const uint16_t* wsg,
                                   int H, int E, int k, int renorm, int32_t* counters_row,
                                   int32_t* ids, float* w, float* gate, int32_t* off, int32_t* st,
                                   int32_t* sp, int32_t* pp, int32_t* active, int32_t* n_active,
                                   const smoe_w4_expert* experts, int I, uint16_t* y, void* ws,
-                                  int32_t* err, hipStream_t s);
+                                  const uint16_t* sw13, const uint16_t* sw2, int Is,
+                                  uint16_t* sh_h, uint16_t* sh_out, int32_t* err, hipStream_t s);
 bool w4a16_shape_supported(int H, int I);
 hipError_t launch_verify_ffn(const uint16_t* x, const int32_t* sorted_token, const int32_t* off,
                              const int32_t* active, const int32_t* n_active,

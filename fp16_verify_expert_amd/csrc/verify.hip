@@ -19,6 +19,7 @@
 // stream.  The gate/up projection applies SwiGLU in registers and writes h as
 // fp16; the down projection writes y_sorted.
 #include "common.h"
+#include "gemv_core.h"
 
 namespace {
 
@@ -399,41 +400,13 @@ __global__ __launch_bounds__(64 * kVWaves) void f16_kernel(F16Args a) {
 // load is 1 KB of one row, and the same chunks of the expert's rows, one row
 // at a time (the weights stay in registers for the next row).  Each lane
 // dots its chunks (v_dot2_f32_f16, fp32 sums in chunk order) and the wave's
-// 64 lane sums are added in a fixed order (wave_sum).  Measured against
-// staging RB rows in LDS per workgroup: one row at a time is faster up to
-// four rows (the LDS staging waits for every load of the launch first).
+// 64 lane sums are added in a fixed order (the routines of gemv_core.h, also
+// used by the one-token draft launches for a dense shared expert).  Measured
+// against staging RB rows in LDS per workgroup: one row at a time is faster
+// up to four rows (the LDS staging waits for every load of the launch first).
 constexpr int kGemvWaves = 4;      // columns per workgroup
 constexpr int kGemvMaxT = 4;       // tokens per call at or below which it runs
-constexpr int kGemvMaxChunks = 16; // 16-byte chunks per lane and row: K <= 8192
-
-__device__ __forceinline__ h2_t as_h2v(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
-
-__device__ __forceinline__ float dot8(u4_t w, uint4 x, float acc) {
-    acc = __builtin_amdgcn_fdot2(as_h2v(w.x), as_h2v(x.x), acc, false);
-    acc = __builtin_amdgcn_fdot2(as_h2v(w.y), as_h2v(x.y), acc, false);
-    acc = __builtin_amdgcn_fdot2(as_h2v(w.z), as_h2v(x.z), acc, false);
-    acc = __builtin_amdgcn_fdot2(as_h2v(w.w), as_h2v(x.w), acc, false);
-    return acc;
-}
-
-// Sum over the wave in a fixed order: within each row of 16 lanes by DPP
-// (swap neighbours, swap pairs, rotate by 4, rotate by 8), then the four row
-// sums read from lanes 0, 16, 32 and 48.
-template <int CTRL>
-__device__ __forceinline__ float dpp_add(float v) {
-    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
-    return v + __builtin_bit_cast(float, t);
-}
-__device__ __forceinline__ float lane_value(float v, int l) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
-}
-__device__ __forceinline__ float wave_sum(float v) {
-    v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
-    v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
-    v = dpp_add<0x124>(v);  // row_ror 4
-    v = dpp_add<0x128>(v);  // row_ror 8
-    return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
-}
+constexpr int kGemvMaxChunks = smoe_gemv::kMaxChunks; // 16-byte chunks per lane and row
 
 template <int PHASE, int CPL>
 __global__ __launch_bounds__(64 * kGemvWaves) void f16_gemv_kernel(F16Args a) {
@@ -460,64 +433,31 @@ __global__ __launch_bounds__(64 * kGemvWaves) void f16_gemv_kernel(F16Args a) {
         return;
     }
     const int K = a.K;
-    const int kc = K >> 3;  // 16-byte chunks per row
     const int n = cb * kGemvWaves + wave;
     const int nc = (n < a.Ncol) ? n : a.Ncol - 1;  // clamped column: loads stay in the matrix
-    const u4_t wzero = {0u, 0u, 0u, 0u};
-
-    // chunk j of this lane: lane + 64 j, clamped into the row (the clamped
-    // ones are masked where used)
-    auto load_row = [&](int r, uint4 (&xr)[CPL]) {
+    auto xrow = [&](int r) {
         const size_t src = (PHASE == 1) ? (size_t)a.sorted_token[r] : (size_t)r;
-        const uint4* xrow = reinterpret_cast<const uint4*>(a.xin + src * K);
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            const int c = lane + 64 * j;
-            xr[j] = xrow[c < kc ? c : kc - 1];
-        }
+        return a.xin + src * K;
     };
     // the column's weight chunks, all of them, then the first row
     u4_t wv[NM][CPL];
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-        const size_t row = (m == 0) ? (size_t)nc : (size_t)a.I + nc;
-        gptr<u4_t> wr = as_global(reinterpret_cast<const u4_t*>(W + row * K));
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            const int c = lane + 64 * j;
-            wv[m][j] = __builtin_nontemporal_load(wr + (c < kc ? c : kc - 1));
-        }
-    }
+    smoe_gemv::gemv_load_w<NM, CPL>(W, K, a.I, nc, lane, wv);
     uint4 xr[CPL];
-    load_row(r0, xr);
+    smoe_gemv::gemv_load_x<CPL>(xrow(r0), K, lane, xr);
     // keep every load above ahead of the first use (the scheduler would
     // otherwise start on the first chunks and issue the last ones a round
     // trip later)
     __builtin_amdgcn_sched_barrier(0);
 
     auto one_row = [&](int r) {
-        float acc[NM];
-#pragma unroll
-        for (int m = 0; m < NM; ++m) acc[m] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            const bool in = lane + 64 * j < kc;
-#pragma unroll
-            for (int m = 0; m < NM; ++m) acc[m] = dot8(in ? wv[m][j] : wzero, xr[j], acc[m]);
-        }
-        float tot[NM];
-#pragma unroll
-        for (int m = 0; m < NM; ++m) tot[m] = wave_sum(acc[m]);
-        if (lane == 0 && n < a.Ncol) {
-            const float v = (PHASE == 1) ? silu_f(tot[0]) * tot[NM - 1] : tot[0];
-            a.out[(size_t)r * a.Ncol + n] = f2h(v);
-        }
+        const uint16_t v = smoe_gemv::gemv_dot<NM, CPL>(wv, xr, K, lane);
+        if (lane == 0 && n < a.Ncol) a.out[(size_t)r * a.Ncol + n] = v;
     };
     // the first row straight-line (its waits then cover only what each step
     // needs), further rows of the group in a loop
     one_row(r0);
     for (int r = r0 + 1; r < r1; ++r) {
-        load_row(r, xr);
+        smoe_gemv::gemv_load_x<CPL>(xrow(r), K, lane, xr);
         one_row(r);
     }
 }

@@ -41,6 +41,7 @@
 // The slots' partial sums are added in a fixed order through LDS: the output
 // is deterministic and no floating-point atomics are used.
 #include "common.h"
+#include "gemv_core.h"
 #include "maps_core.h"
 #include "route_core.h"
 
@@ -1068,6 +1069,61 @@ __attribute__((amdgpu_waves_per_eu(SMOE_W4_MFMA_WPE))) void w4_mfma_kernel(W4Arg
 // row s.  One extra workgroup writes the routing outputs, the ELB increments
 // and the maps, which the down projection and the combine read after this
 // launch.
+// A dense shared expert folded into the one-token draft launches (FP16 w13
+// [2 Is, H], w2 [H, Is], the nn.Linear layout of the verify path): the
+// workgroups from wg0 on compute its columns with the matrix-vector routine
+// of gemv_core.h, so its output is bit-identical to verify_grouped_gemm's on
+// the same row.  They read only the token row (gate/up) or the shared h
+// written by the gate/up launch (down), so they need nothing from the routed
+// workgroups beside them.
+struct SharedArgs {
+    const uint16_t* w13;
+    const uint16_t* w2;
+    int Is;         // shared intermediate
+    int wg0;        // first shared workgroup of the launch
+    uint16_t* h;    // [Is] fp16
+    uint16_t* out;  // [H] fp16
+};
+
+// Columns (b * waves + wave) * CPW + c, c < CPW, of the shared expert's
+// projection: all their weight chunks are requested, then the row, then each
+// column is reduced.  Phase 1: K = H, Ncol = Is, gate row n and up row Is + n
+// of w13, output h; phase 2: K = Is, Ncol = H, row n of w2, output y.
+template <int PHASE, int CPL, int CPW>
+SMOE_DEV void shared_gemv_block(const uint16_t* xrow, const uint16_t* W, int K, int I, int Ncol,
+                                int b, uint16_t* out) {
+    constexpr int NM = (PHASE == 1) ? 2 : 1;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+    int n[CPW];
+    u4_t wv[CPW][NM][CPL];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        n[c] = (b * nw + wave) * CPW + c;
+        const int nc = (n[c] < Ncol) ? n[c] : Ncol - 1;  // loads stay in the matrix
+        smoe_gemv::gemv_load_w<NM, CPL>(W, K, I, nc, lane, wv[c]);
+    }
+    uint4 xr[CPL];
+    smoe_gemv::gemv_load_x<CPL>(xrow, K, lane, xr);
+    __builtin_amdgcn_sched_barrier(0);  // every request above before the first use
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        const uint16_t v = smoe_gemv::gemv_dot<NM, CPL>(wv[c], xr, K, lane);
+        if (lane == 0 && n[c] < Ncol) out[n[c]] = v;
+    }
+}
+
+// The shared expert's projection as a launch of its own (shapes without a
+// fused instantiation): 4 waves per workgroup, one column per wave.
+template <int PHASE, int CPL>
+__global__ __launch_bounds__(256) void shared_gemv_kernel(SharedArgs sh, const uint16_t* x, int H) {
+    if (PHASE == 1)
+        shared_gemv_block<1, CPL, 1>(x, sh.w13, H, sh.Is, sh.Is, blockIdx.x, sh.h);
+    else
+        shared_gemv_block<2, CPL, 1>(sh.h, sh.w2, sh.Is, 0, H, blockIdx.x, sh.out);
+}
+
 struct RouteArgs {
     const uint16_t* wr;   // router [E, H]
     const uint16_t* wsg;  // shared-expert gate row [H] or null
@@ -1102,12 +1158,20 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t* __res
     smoe_route::wave_logits(x, wr, wsg, H, E, nvec, wave, nvec, nwaves, lg, threadIdx.x & 63);
 }
 
-template <int LPR, int NG>
+template <int LPR, int NG, int CPLS>
 __global__ __launch_bounds__(64 * kT1MaxWaves)
-__attribute__((amdgpu_waves_per_eu(2))) void route_w4_kernel(W4Args a, RouteArgs r) {
+__attribute__((amdgpu_waves_per_eu(2))) void route_w4_kernel(W4Args a, RouteArgs r, SharedArgs sh) {
     __shared__ float lg_s[257];
     __shared__ int32_t ids_s[kFusedMaxK];
     extern __shared__ uint4 smem[];
+    if constexpr (CPLS > 0) {
+        // the shared expert's gate/up columns, two per wave
+        if ((int)blockIdx.x >= sh.wg0) {
+            shared_gemv_block<1, CPLS, 2>(a.xin, sh.w13, a.K, sh.Is, sh.Is,
+                                          (int)blockIdx.x - sh.wg0, sh.h);
+            return;
+        }
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -1153,6 +1217,28 @@ __attribute__((amdgpu_waves_per_eu(2))) void route_w4_kernel(W4Args a, RouteArgs
         one_token_block<4, 1, LPR, NG>(a, carve_lds<4>(smem, a), pick_mat<1>(a, spec, e), xv,
                                        slot, cb);
     }
+}
+
+// The down projection of a one-token step (as w4_kernel's) with the shared
+// expert's down columns in the workgroups from sh.wg0 on, one per wave.
+template <int LPR, int NG, int CPLS>
+__global__ __launch_bounds__(64 * kT1MaxWaves)
+__attribute__((amdgpu_waves_per_eu(w4_waves_per_eu<1, NG>()))) void w4_down_shared_kernel(
+    W4Args a, SharedArgs sh) {
+    extern __shared__ uint4 smem[];
+    if ((int)blockIdx.x >= sh.wg0) {
+        shared_gemv_block<2, CPLS, 1>(sh.h, sh.w2, sh.Is, 0, a.N, (int)blockIdx.x - sh.wg0,
+                                      sh.out);
+        return;
+    }
+    const int cb = blockIdx.x % a.nCB;
+    const int slot = blockIdx.x / a.nCB;
+    const uint4* row4 = reinterpret_cast<const uint4*>(a.xin + (size_t)slot * a.K);
+    uint4 xv[kRowChunksPerThread];
+    const SlotDesc d = a.desc[slot];
+    request_row(row4, a.K >> 3, xv);
+    if (d.e < 0) return;
+    one_token_block<4, 2, LPR, NG>(a, carve_lds<4>(smem, a), d.w2, xv, slot, cb);
 }
 
 // ---------------------------------------------------------------- launch ----
@@ -1367,12 +1453,31 @@ hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, cons
 
 bool draft_route_ffn_supported(int E, int k) { return E <= 256 && k <= kFusedMaxK; }
 
+// The shared expert's projection as its own launch (no fused instantiation
+// for its chunk count).
+template <int PHASE>
+hipError_t launch_shared_gemv(const SharedArgs& sh, const uint16_t* x, int H, int cpl,
+                              hipStream_t s) {
+    const int ncol = (PHASE == 1) ? sh.Is : H;
+    const dim3 grid((ncol + 3) / 4), block(256);
+    switch (cpl) {
+        case 2: shared_gemv_kernel<PHASE, 2><<<grid, block, 0, s>>>(sh, x, H); break;
+        case 4: shared_gemv_kernel<PHASE, 4><<<grid, block, 0, s>>>(sh, x, H); break;
+        case 6: shared_gemv_kernel<PHASE, 6><<<grid, block, 0, s>>>(sh, x, H); break;
+        case 8: shared_gemv_kernel<PHASE, 8><<<grid, block, 0, s>>>(sh, x, H); break;
+        case 12: shared_gemv_kernel<PHASE, 12><<<grid, block, 0, s>>>(sh, x, H); break;
+        default: shared_gemv_kernel<PHASE, 16><<<grid, block, 0, s>>>(sh, x, H); break;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_draft_route_ffn(const uint16_t* x, const uint16_t* wr, const uint16_t* wsg,
                                   int H, int E, int k, int renorm, int32_t* counters_row,
                                   int32_t* ids, float* w, float* gate, int32_t* off, int32_t* st,
                                   int32_t* sp, int32_t* pp, int32_t* active, int32_t* n_active,
                                   const smoe_w4_expert* experts, int I, uint16_t* y, void* ws,
-                                  int32_t* err, hipStream_t s) {
+                                  const uint16_t* sw13, const uint16_t* sw2, int Is,
+                                  uint16_t* sh_h, uint16_t* sh_out, int32_t* err, hipStream_t s) {
     const int nvec = E + (wsg ? 1 : 0);
     uint16_t* h = static_cast<uint16_t*>(ws);
     SlotDesc* desc = reinterpret_cast<SlotDesc*>(static_cast<char*>(ws) + h_bytes(1, k, I));
@@ -1388,9 +1493,22 @@ hipError_t launch_draft_route_ffn(const uint16_t* x, const uint16_t* wr, const u
                                  err, desc);
     RouteArgs r{wr,  wsg, logits, k,  renorm, counters_row, ids,    w,
                 gate, off, st,     sp, pp,     active,       n_active};
-    const dim3 grid(k * p1.nCB + 1), block(64 * p1.waves);  // + the routing workgroup
     if (p1.ng < 1 || p1.ng > 4) return hipErrorInvalidValue;  // excluded by the shape checks
-#define SMOE_ROUTE_W4(L, NG) hipLaunchKernelGGL((route_w4_kernel<L, NG>), grid, block, p1.lds, s, a1, r)
+    // The shared expert (if any): its gate/up columns ride in the gate/up
+    // launch when H takes 4 or 8 chunks per lane (two columns per wave), its
+    // down columns in the down launch when Is takes 6, 8 or 12; other shapes
+    // run the same routine as launches of their own.
+    SharedArgs sh{sw13, sw2, Is, k * p1.nCB + 1, sh_h, sh_out};
+    const int c1 = sw13 ? smoe_gemv::chunks_for(H) : 0;
+    const int cs1 = (c1 == 4 || c1 == 8) ? c1 : 0;
+    const int nsh1 = cs1 ? (Is + 2 * p1.waves - 1) / (2 * p1.waves) : 0;
+    const dim3 grid(k * p1.nCB + 1 + nsh1), block(64 * p1.waves);  // + the routing workgroup
+#define SMOE_ROUTE_W4(L, NG)                                                                     \
+    do {                                                                                         \
+        if (cs1 == 4) hipLaunchKernelGGL((route_w4_kernel<L, NG, 4>), grid, block, p1.lds, s, a1, r, sh); \
+        else if (cs1 == 8) hipLaunchKernelGGL((route_w4_kernel<L, NG, 8>), grid, block, p1.lds, s, a1, r, sh); \
+        else hipLaunchKernelGGL((route_w4_kernel<L, NG, 0>), grid, block, p1.lds, s, a1, r, sh); \
+    } while (0)
     if (p1.lpr == 16) {
         if (p1.ng == 1) SMOE_ROUTE_W4(16, 1);
         else if (p1.ng == 2) SMOE_ROUTE_W4(16, 2);
@@ -1405,9 +1523,36 @@ hipError_t launch_draft_route_ffn(const uint16_t* x, const uint16_t* wr, const u
 #undef SMOE_ROUTE_W4
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (sw13 && !cs1) {
+        e = launch_shared_gemv<1>(sh, x, H, c1, s);
+        if (e != hipSuccess) return e;
+    }
     const PhasePlan p2 = plan_phase(2, k, 1, I, H, I, 1, 4);
     const W4Args a2 = phase_args(p2, h, nullptr, off, active, n_active, experts, I, H, I, 1, E, y,
                                  err, desc);
-    return launch_any<2>(a2, k, p2, 1, 4, s);
+    const int c2 = sw13 ? smoe_gemv::chunks_for(Is) : 0;
+    const bool fuse2 = (c2 == 6 || c2 == 8 || c2 == 12) && p2.ng <= 2;
+    if (!fuse2) {
+        e = launch_any<2>(a2, k, p2, 1, 4, s);
+        if (e != hipSuccess || !sw13) return e;
+        return launch_shared_gemv<2>(sh, x, H, c2, s);
+    }
+    sh.wg0 = k * p2.nCB;
+    const dim3 grid2(k * p2.nCB + (H + p2.waves - 1) / p2.waves), block2(64 * p2.waves);
+#define SMOE_DOWN_SH(L, NG)                                                                      \
+    do {                                                                                         \
+        if (c2 == 6) hipLaunchKernelGGL((w4_down_shared_kernel<L, NG, 6>), grid2, block2, p2.lds, s, a2, sh); \
+        else if (c2 == 8) hipLaunchKernelGGL((w4_down_shared_kernel<L, NG, 8>), grid2, block2, p2.lds, s, a2, sh); \
+        else hipLaunchKernelGGL((w4_down_shared_kernel<L, NG, 12>), grid2, block2, p2.lds, s, a2, sh); \
+    } while (0)
+    if (p2.lpr == 16) {
+        if (p2.ng == 1) SMOE_DOWN_SH(16, 1);
+        else SMOE_DOWN_SH(16, 2);
+    } else {
+        if (p2.ng == 1) SMOE_DOWN_SH(8, 1);
+        else SMOE_DOWN_SH(8, 2);
+    }
+#undef SMOE_DOWN_SH
+    return hipGetLastError();
 }
 }  // namespace smoe

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SMOE_ABI_VERSION 1
+#define SMOE_ABI_VERSION 2
 
 typedef enum {
     SMOE_OK = 0,
@@ -255,9 +255,22 @@ smoe_status wq_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
  *   sorted_token [k], sorted_pair [k], pair_pos [k], active [E],
  *   n_active [1]   out: bit-identical to moe_route_plan's
  *   y_sorted       fp16 [k, H] out: bit-identical to w4a16_grouped_ffn's
+ *   shared_w13, shared_w2, shared_I, shared_h, shared_out: an optional dense
+ *                  FP16 shared expert ([S2] What shipped: the draft reuses
+ *                  the target's shared experts in FP16) computed inside the
+ *                  same gate/up and down launches: shared_w13 fp16 [2*shared_I,
+ *                  H] (gate rows, then up rows), shared_w2 fp16 [H, shared_I],
+ *                  shared_h fp16 [shared_I] (caller-owned scratch between the
+ *                  projections), shared_out fp16 [1, H] out, bit-identical to
+ *                  verify_grouped_gemm on the same row as one always-on group.
+ *                  shared_w13 NULL = no shared expert (the other four are then
+ *                  ignored).  Several shared experts of one layer pass as one
+ *                  of their summed intermediate.
  *   workspace      >= smoe_workspace_bytes(0, 1, k, H, I, E) bytes,
  *                  256-byte aligned
- * Limits: k <= 32, E <= 256, H and I at most 16384 (SMOE_ERR_SHAPE beyond).
+ * Limits: k <= 32, E <= 256, H and I at most 16384; with a shared expert,
+ * shared_I a positive multiple of 128 and H, shared_I at most 8192
+ * (SMOE_ERR_SHAPE beyond); shared_w13, shared_w2, shared_h 16-byte aligned.
  * The caller owns every buffer; nothing is allocated.
  * ---------------------------------------------------------------------- */
 smoe_status moe_draft_route_ffn(const uint16_t* x, const uint16_t* w_router,
@@ -267,8 +280,11 @@ smoe_status moe_draft_route_ffn(const uint16_t* x, const uint16_t* w_router,
                                 int32_t* topk_ids, float* topk_w, float* shared_gate,
                                 int32_t* expert_offsets, int32_t* sorted_token,
                                 int32_t* sorted_pair, int32_t* pair_pos, int32_t* active,
-                                int32_t* n_active, uint16_t* y_sorted, void* workspace,
-                                size_t workspace_bytes, int32_t* err_word, void* stream);
+                                int32_t* n_active, uint16_t* y_sorted,
+                                const uint16_t* shared_w13, const uint16_t* shared_w2,
+                                int shared_I, uint16_t* shared_h, uint16_t* shared_out,
+                                void* workspace, size_t workspace_bytes, int32_t* err_word,
+                                void* stream);
 
 /* ------------------------------------------------------------------------
  * verify_grouped_gemm -- FP16 SwiGLU FFN of the target experts over the

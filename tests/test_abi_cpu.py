@@ -118,11 +118,12 @@ def test_draft_route_ffn_validation():
     assert need > 0
 
     def call(x=FAKE, wr=FAKE, wsg=None, H=256, I=512, E=8, k=2, layer=0, Lc=1, counters=FAKE,
-             table=FAKE, gs=128, gate=None, mp=None, y=FAKE, ws=FAKE, wsb=None):
+             table=FAKE, gs=128, gate=None, mp=None, y=FAKE, ws=FAKE, wsb=None,
+             sh=(None, None, 0, None, None)):
         m = maps if mp is None else mp
         return L.moe_draft_route_ffn(x, wr, wsg, H, I, E, k, 0, layer, Lc, counters, table, gs,
-                                     FAKE, FAKE, gate, *m, y, ws, need if wsb is None else wsb,
-                                     None, None)
+                                     FAKE, FAKE, gate, *m, y, *sh, ws,
+                                     need if wsb is None else wsb, None, None)
     assert call(x=None) == 1
     assert call(table=None) == 1
     assert call(y=None) == 1
@@ -137,6 +138,14 @@ def test_draft_route_ffn_validation():
     assert call(x=V(0x1002)) == 2 and "aligned" in _err()
     assert call(wsb=need - 1) == 6
     assert call(ws=None) == 6
+    # the optional dense shared expert
+    assert call(sh=(FAKE, FAKE, 1024, FAKE, None)) == 1 and "shared_out" in _err()
+    assert call(sh=(FAKE, None, 1024, FAKE, FAKE)) == 1
+    assert call(sh=(FAKE, FAKE, 1000, FAKE, FAKE)) == 2 and "shared_I" in _err()
+    assert call(sh=(FAKE, FAKE, 0, FAKE, FAKE)) == 2
+    assert call(sh=(FAKE, FAKE, 8320, FAKE, FAKE)) == 2 and "8192" in _err()
+    assert call(sh=(FAKE, FAKE, 1024, V(0x1002), FAKE)) == 2 and "aligned" in _err()
+    assert call(sh=(None, FAKE, 1000, None, None), wsb=need - 1) == 6  # ignored without shared_w13
 
 
 def test_w4a16_validation():

@@ -415,6 +415,61 @@ def test_draft_route_ffn_nan_logit_and_repeat():
     assert torch.equal(m2["offsets"], m["offsets"])
 
 
+# The dense shared expert inside the one-token draft launches: fused into the
+# gate/up and down launches at the DeepSeek, Qwen and (H = 4096) Phi-like
+# shapes, launches of its own for the tiny one (no fused instantiation).
+_TINY_SHD = dataclasses.replace(synth.TINY, name="tiny_shared_draft", shared_I=384)
+_PHI_SHD = dataclasses.replace(synth.PHI, name="phi_shared_draft", shared_I=4096,
+                               shared_gate=True)
+DRAFT_SHARED_CASES = [(synth.DS, 0), (synth.DS, 2), (synth.QWEN, 0), (synth.QWEN, 5),
+                      (_TINY_SHD, 1), (_PHI_SHD, 0)]
+
+
+@pytest.mark.parametrize("shape,step", DRAFT_SHARED_CASES,
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_draft_route_ffn_shared_expert(shape, step):
+    """With a shared expert, moe_draft_route_ffn leaves every routed output
+    bit-identical to the call without one, and its shared output equals
+    verify_grouped_gemm on the same row bit for bit (and the oracle)."""
+    say(f"draft route+ffn with shared expert {shape.name} step={step}")
+    E, k, H, I, Is = shape.E, shape.k, shape.H, shape.I, shape.shared_I
+    x = synth.tokens(shape, 1, step=step)
+    L = _layer(shape, (1,), steps=(step,), f16=False)
+    assert L.shared is not None
+    dx = dev(x)
+    err = _err()
+    counters = torch.zeros((1, E), dtype=torch.int32, device="cuda")
+    counters2 = torch.zeros((1, E), dtype=torch.int32, device="cuda")
+    ws = fve.new_workspace(0, 1, k, H, I, E)
+    shared = (dev(L.shared["w13"]), dev(L.shared["w2"]))
+    ids, w, gate, m, y, so = fve.moe_draft_route_ffn(dx, L.d_router, k, L.t4, I, ws,
+                                                     shape.renormalize, L.d_gate,
+                                                     counters=counters, err_word=err,
+                                                     shared=shared)
+    ws2 = fve.new_workspace(0, 1, k, H, I, E)
+    ids2, w2, gate2, m2, y2 = fve.moe_draft_route_ffn(dx, L.d_router, k, L.t4, I, ws2,
+                                                      shape.renormalize, L.d_gate,
+                                                      counters=counters2)
+    iota = torch.zeros(1, dtype=torch.int32, device="cuda")
+    offs = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    wsv = fve.new_workspace(1, 1, 1, H, Is, 1)
+    yv = fve.verify_grouped_gemm(dx, iota, offs, L.tsh, 1, 1, H, Is, 1, wsv)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) == 0
+    assert torch.equal(ids, ids2) and torch.equal(w, w2) and torch.equal(counters, counters2)
+    if L.d_gate is not None:
+        assert torch.equal(gate, gate2)
+    for key in ("offsets", "active", "n_active"):
+        assert torch.equal(m[key], m2[key]), key
+    for key in ("sorted_token", "sorted_pair", "pair_pos"):
+        assert torch.equal(m[key][:k], m2[key][:k]), key
+    assert torch.equal(y[:k], y2[:k])
+    assert torch.equal(so, yv[:1]), "shared output differs from verify_grouped_gemm"
+    ref = oracle.expert_ffn_f16(x, L.shared["w13"], L.shared["w2"])
+    st = assert_fp16_close(host(so), ref, f"draft shared {shape.name}")
+    say(f"  shared l2={st['l2']:.2e} maxabs={st['maxabs']:.2e}")
+
+
 VERIFY_CASES = [(synth.TINY, 17), (synth.TINY, 40), (synth.QWEN, 9), (synth.PHI, 17),
                 (synth.DS, 16),
                 # T <= 4: the one-wave-per-column kernel (1, 2 and 4 rows per block)
