@@ -1,15 +1,19 @@
 // Weighted combine of the routed experts' outputs (plus shared expert and an
 // optional residual).  The pages leave this step implicit; it is the usual
-// routed-MoE weighted sum.  One workgroup per token; a thread owns 8 adjacent
-// hidden elements at a time (16-byte loads and stores); sums are fp32 in a
-// fixed order (slots in increasing j, then the shared term, then the
-// residual), rounded once.  Optionally the epilogue also writes the row
-// RMS-normalised (the next pre-norm layer's input), from the rounded values.
+// routed-MoE weighted sum.  A thread owns 8 adjacent hidden elements at a
+// time (16-byte loads and stores); sums are fp32 in a fixed order (slots in
+// increasing j, then the shared term, then the residual), rounded once.  The
+// slots' row positions and weights are read first, 8 at a time, then their
+// rows are requested together.  Without the norm epilogue a token's row is
+// split over several workgroups (one chunk per thread); with it, one
+// workgroup per token also writes the row RMS-normalised (the next pre-norm
+// layer's input), from the rounded values.
 #include "common.h"
 
 namespace {
 
 constexpr int kCombThreads = 256;
+constexpr int kBatch = 8;  // slots whose rows are requested together
 
 __device__ __forceinline__ void add8(float (&acc)[8], uint4 v, float w) {
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
@@ -29,13 +33,26 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     const int t = blockIdx.x;
     const int nch = H / 8;
     float sq = 0.0f;  // sum of squares of the rounded outputs (norm_out only)
-    for (int c8 = threadIdx.x; c8 < nch; c8 += kCombThreads) {
+    for (int c8 = blockIdx.y * kCombThreads + threadIdx.x; c8 < nch;
+         c8 += gridDim.y * kCombThreads) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < k; ++j) {
-            const int r = pp[(size_t)t * k + j];
-            if (r < 0) continue;
-            const uint4 v = reinterpret_cast<const uint4*>(y + (size_t)r * H)[c8];
-            add8(acc, v, w[(size_t)t * k + j]);
+        for (int j0 = 0; j0 < k; j0 += kBatch) {
+            int r[kBatch];
+            float wj[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                const int j = j0 + i;
+                r[i] = (j < k) ? pp[(size_t)t * k + j] : -1;
+                wj[i] = (j < k) ? w[(size_t)t * k + j] : 0.0f;
+            }
+            uint4 v[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i)
+                v[i] = (r[i] >= 0) ? reinterpret_cast<const uint4*>(y + (size_t)r[i] * H)[c8]
+                                   : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i)
+                if (r[i] >= 0) add8(acc, v[i], wj[i]);
         }
         if (shared) {
             const float c = sscale ? sscale[t] : 1.0f;
@@ -87,8 +104,12 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* pp, const float* w,
                           const uint16_t* shared, const float* sscale, const uint16_t* resid,
                           int T, int k, int H, uint16_t* out, uint16_t* norm_out, float eps,
                           hipStream_t s) {
-    combine_kernel<<<dim3(T), dim3(kCombThreads), 0, s>>>(y, pp, w, shared, sscale, resid, k, H,
-                                                           out, norm_out, eps);
+    // the norm epilogue needs the whole row in one workgroup
+    const int nch = H / 8;
+    const int split = norm_out ? 1 : (nch + kCombThreads - 1) / kCombThreads;
+    if (T == 0) return hipSuccess;
+    combine_kernel<<<dim3(T, split), dim3(kCombThreads), 0, s>>>(y, pp, w, shared, sscale, resid,
+                                                                  k, H, out, norm_out, eps);
     return hipGetLastError();
 }
 }  // namespace smoe

@@ -234,6 +234,37 @@ __device__ __forceinline__ void lds_read_tiles(uint32_t addr, h8_t (&v)[NT]) {
     }
 }
 
+// NM weight-tile fragments at addr (+4096) and one activation-tile fragment
+// at aaddr, completed before the block ends (as lds_read_tiles).
+template <int NM>
+__device__ __forceinline__ void lds_read_tiles_light(uint32_t addr, uint32_t aaddr,
+                                                     h8_t (&v)[NM + 1]) {
+    static_assert(NM == 1 || NM == 2, "weight tiles per step");
+    if constexpr (NM == 1) {
+        asm volatile(
+            "ds_read_b128 %0, %2\n\t"
+            "ds_read_b128 %1, %3\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(v[0]), "=&v"(v[1])
+            : "v"(addr), "v"(aaddr)
+            : "memory");
+    } else {
+        asm volatile(
+            "ds_read_b128 %0, %3\n\t"
+            "ds_read_b128 %1, %3 offset:4096\n\t"
+            "ds_read_b128 %2, %4\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2])
+            : "v"(addr), "v"(aaddr)
+            : "memory");
+    }
+}
+
+template <int N>
+struct IntC {
+    static constexpr int value = N;
+};
+
 // One workgroup = one (expert, 16-column block); its waves split the
 // reduction into contiguous step ranges.  Each wave streams its tiles through
 // a private NSTAGE-deep LDS ring with direct global->LDS loads: a load
@@ -247,7 +278,6 @@ __global__ __launch_bounds__(64 * kVWaves) void f16_kernel(F16Args a) {
     constexpr int NM = (PHASE == 1) ? 2 : 1;            // weight matrices per step
     constexpr int NT = NM + RB;                          // tiles per step
     constexpr int STAGE = NT * kTileBytes;
-    constexpr int LOADS = 4 * NT;                        // load instructions per step
     constexpr int D = NSTAGE - 1;                        // steps in flight ahead
     __shared__ __attribute__((aligned(16))) char ring[kVWaves][NSTAGE][STAGE];
     __shared__ f4_t part[kVWaves][NM][RB][64];
@@ -294,7 +324,15 @@ __global__ __launch_bounds__(64 * kVWaves) void f16_kernel(F16Args a) {
         if (PHASE == 1) wrow[NM - 1][j] = W + (size_t)(a.I + n0 + r) * K;
     }
 
-    for (int mb = r0; mb < r1; mb += 16 * RB) {
+    // One row block; AQ = activation load instructions per tile and step (4
+    // rows each).  A block of at most 4 rows (the usual case at K+1 <= 33:
+    // about 2.3 rows per touched expert) takes AQ = 1: its rows land in the
+    // tile's first 1 KB, and the A operand repeats them in rows 4-15, whose
+    // outputs are not stored (measured 2% faster on the Phi-shaped verify
+    // than loading all 16 rows).
+    auto row_block = [&](int mb, auto aq) {
+        constexpr int AQ = decltype(aq)::value;
+        constexpr int LOADS = 4 * NM + AQ * RB;  // load instructions per step
         // activation rows of this lane's loads (rows past the group repeat a
         // valid row; they only feed output rows that are not stored)
         const uint16_t* arow[RB][4];
@@ -321,9 +359,10 @@ __global__ __launch_bounds__(64 * kVWaves) void f16_kernel(F16Args a) {
                         (lds_ptr_t)(stage + m * kTileBytes + j * 1024), 16, 0, 0);
 #pragma unroll
                 for (int b = 0; b < RB; ++b)
-                    __builtin_amdgcn_global_load_lds(
-                        (const void*)(arow[b][j] + koff),
-                        (lds_ptr_t)(stage + (NM + b) * kTileBytes + j * 1024), 16, 0, 0);
+                    if (j < AQ)
+                        __builtin_amdgcn_global_load_lds(
+                            (const void*)(arow[b][j] + koff),
+                            (lds_ptr_t)(stage + (NM + b) * kTileBytes + j * 1024), 16, 0, 0);
             }
         };
 
@@ -352,7 +391,15 @@ __global__ __launch_bounds__(64 * kVWaves) void f16_kernel(F16Args a) {
             for (int u = 0; u < 4; ++u) {
                 const uint32_t off = rrow * 256 + (((4 * u + rq) ^ rrow) << 4);
                 h8_t t[NT];  // weight tile(s), then RB activation tiles
-                lds_read_tiles<NT>(stage_addr + off, t);
+                if constexpr (AQ == 4) {
+                    lds_read_tiles<NT>(stage_addr + off, t);
+                } else {
+                    static_assert(RB == 1, "short row blocks hold one tile of rows");
+                    const int ar = rrow & 3;  // the block's rows 0-3, repeated
+                    const uint32_t aoff = NM * kTileBytes + ar * 256 + (((4 * u + rq) ^ ar) << 4);
+                    lds_read_tiles_light<NM>(stage_addr + off, stage_addr + aoff,
+                                             *reinterpret_cast<h8_t(*)[NM + 1]>(&t[0]));
+                }
 #pragma unroll
                 for (int b = 0; b < RB; ++b) {
                     accg[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(t[NM + b], t[0], accg[b], 0, 0, 0);
@@ -386,6 +433,15 @@ __global__ __launch_bounds__(64 * kVWaves) void f16_kernel(F16Args a) {
             }
         }
         __syncthreads();  // part is reused by the next row block
+    };
+    for (int mb = r0; mb < r1; mb += 16 * RB) {
+        if constexpr (RB == 1) {
+            if (r1 - mb <= 4) {
+                row_block(mb, IntC<1>{});
+                continue;
+            }
+        }
+        row_block(mb, IntC<4>{});
     }
 }
 
