@@ -51,13 +51,15 @@ def parse():
                     help="also run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--workload", default="phi_layer",
                     choices=["phi_layer", "qwen_chunk", "route_fidelity", "qwen_rounds",
-                             "draft_formats"],
+                             "draft_formats", "ds_draft"],
                     help="phi_layer (default): one draft + verify step of the Phi-3.5-MoE-shaped "
                          "layer; qwen_chunk: 24 Qwen-shaped layers, 16 draft steps, ELB snapshot, "
                          "top-16 residency, 17-token verify with staged misses; route_fidelity: INT4 draft vs "
                          "FP16 target routing agreement and distinct experts vs depth; qwen_rounds: speculation "
                          "rounds with the prefetch planner vs boundary placement; draft_formats: the "
-                         "one-token draft step with 2-, 4- and 8-bit experts (Phi and DeepSeek shapes)")
+                         "one-token draft step with 2-, 4- and 8-bit experts (Phi and DeepSeek shapes); "
+                         "ds_draft: the DeepSeek-V2-Lite-shaped draft layer step (routing, ELB, INT4 "
+                         "experts, 2 FP16 shared experts, combine) at T = 1, 4 and 16")
     ap.add_argument("--layers", type=int, default=24, help="qwen_chunk: number of layers")
     ap.add_argument("--rounds", type=int, default=4, help="qwen_rounds: speculation rounds")
     ap.add_argument("--rho", type=float, default=0.8,
@@ -93,6 +95,8 @@ def main():
         return bench_qwen_rounds(args)
     if args.workload == "draft_formats":
         return bench_draft_formats(args)
+    if args.workload == "ds_draft":
+        return bench_ds_draft(args)
 
     import numpy as np
     import torch
@@ -547,6 +551,119 @@ def bench_draft_formats(args):
                                   "combine) at 2/4/8 bits; phi35 T=1, ds_v2_lite T=1/4/16"},
            "results": results, "run_s": round(time.perf_counter() - t_all, 1)}
     print(json.dumps(out), flush=True)
+
+
+def bench_ds_draft(args):
+    """The DeepSeek-V2-Lite-shaped draft layer step (hidden 2048, 64 routed
+    experts, top-6, intermediate 1408, 2 FP16 shared experts run as one of
+    intermediate 2816, ELB counters over one layer) at T = 1, 4 and 16 tokens,
+    every weight in HBM.  T = 1: moe_draft_route_ffn (routing, ELB, maps,
+    routed INT4 FFN and the shared experts in three launches) + moe_combine;
+    T > 1: moe_route_plan + w4a16_grouped_ffn + the shared experts through
+    verify_grouped_gemm + moe_combine.  A read of 1 GiB runs before each timed
+    step, outside its events, so the weights come from HBM.  Reported per T:
+    the step's wall time (HIP events around its calls, no markers inside),
+    the INT4 bytes of the touched experts and the shared experts' FP16 bytes,
+    and GB/s of the INT4 bytes and of all weight bytes."""
+    import numpy as np
+    import torch
+
+    import fp16_verify_expert_amd as fve
+    import synth
+
+    fve.lib()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda")
+    s = synth.DS
+    H, E, k, I, Is = s.H, s.E, s.k, s.I, s.shared_I
+    t0 = time.perf_counter()
+    g = synth.torch_layer(s, 0, dev)
+    del g["f16"]
+    table = fve.w4_expert_table(g["int4"])
+    router = g["router"]
+    shared = (g["shared"]["w13"], g["shared"]["w2"])
+    tsh = fve.f16_expert_table([shared])
+    gen_s = time.perf_counter() - t0
+    scrub = torch.empty(1 << 29, dtype=torch.float16, device=dev)  # 1 GiB
+    counters = torch.zeros((1, E), dtype=torch.int32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    K = max(args.steps, 5)
+    b4 = s.int4_bytes_per_expert
+    results = []
+    for T in (1, 4, 16):
+        xs = [torch.from_numpy(synth.tokens(s, T, step=i)).to(dev) for i in range(POOL)]
+        ws = fve.new_workspace(0, T, k, H, I, E)
+        wsv = fve.new_workspace(1, T, 1, H, Is, 1)
+        iota = torch.arange(T, dtype=torch.int32, device=dev)
+        offs = torch.tensor([0, T], dtype=torch.int32, device=dev)
+        sh_h = torch.empty(Is, dtype=torch.float16, device=dev)
+        sh_out = torch.empty((T, H), dtype=torch.float16, device=dev)
+        y = torch.empty((T * k, H), dtype=torch.float16, device=dev)
+        out = torch.empty((T, H), dtype=torch.float16, device=dev)
+        ids_b = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w_b = torch.empty((T, k), dtype=torch.float32, device=dev)
+        maps_b = fve._new_maps(T, k, E, dev)
+
+        def step(i):
+            x = xs[i % POOL]
+            if T == 1:
+                fve.moe_draft_route_ffn(x, router, k, table, I, ws, counters=counters,
+                                        err_word=err, topk_ids=ids_b, topk_w=w_b, maps=maps_b,
+                                        y_sorted=y, shared=shared, shared_h=sh_h,
+                                        shared_out=sh_out)
+            else:
+                fve.moe_route_plan(x, router, k, counters=counters, err_word=err,
+                                   topk_ids=ids_b, topk_w=w_b, maps=maps_b)
+                fve.w4a16_grouped_ffn(x, maps_b, table, T, k, H, I, E, ws, y_sorted=y,
+                                      err_word=err)
+                fve.verify_grouped_gemm(x, iota, offs, tsh, T, T, H, Is, 1, wsv,
+                                        y_sorted=sh_out, err_word=err)
+            fve.moe_combine(y, maps_b["pair_pos"], w_b, sh_out, out=out)
+
+        touched = []
+        for i in range(POOL):
+            step(i)
+            torch.cuda.synchronize()
+            touched.append(int(maps_b["n_active"].item()))
+        for i in range(args.warmup):
+            step(i)
+        ev = [(mk(), mk()) for _ in range(K)]
+        torch.cuda.synchronize()
+        for st in range(K):
+            scrub.sum()  # read-only: leaves no dirty lines to write back during the step
+            ev[st][0].record()
+            step(args.warmup + st)
+            ev[st][1].record()
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0, "device error word set"
+        idx = [(args.warmup + st) % POOL for st in range(K)]
+        b_int4 = sum(touched[i] * b4 for i in idx) / K
+        b_sh = s.shared_f16_bytes
+        us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / K
+        results.append({"T": T, "touched_experts_avg": round(sum(touched[i] for i in idx) / K, 2),
+                        "int4_bytes_avg": round(b_int4), "shared_f16_bytes": b_sh,
+                        "step_us": round(us, 2),
+                        "int4_gbps": round(b_int4 / us / 1e3, 1),
+                        "all_weight_gbps": round((b_int4 + b_sh) / us / 1e3, 1),
+                        "all_weight_frac_hbm": round((b_int4 + b_sh) / us / 1e3 / HBM_PEAK_GBS, 4),
+                        "path": ("moe_draft_route_ffn (shared experts inside) + moe_combine"
+                                 if T == 1 else "moe_route_plan + w4a16_grouped_ffn + "
+                                 "verify_grouped_gemm (shared) + moe_combine")})
+        print(json.dumps(results[-1]), file=sys.stderr, flush=True)
+    r1 = results[0]
+    res = {"metric": "MoE-layer INT4 draft weight GB/s (% HBM peak); verify TFLOP/s (% MFMA)",
+           "value": r1["int4_gbps"], "unit": "GB/s", "n_gpus": 1, "steps": K,
+           "warmup": args.warmup, "ms_per_step": round(r1["step_us"] / 1e3, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "int4-w/fp16-a (routed experts), fp16 (shared experts); fp32 accumulate",
+           "data": "synthetic (seeded N(0,0.02) weights from torch Philox, RTN GPTQ INT4 g128; "
+                   "N(0,1) tokens)",
+           "config": {"workload": "ds_v2_lite draft layer step: H=2048 E=64 top-6 I=1408 + 2 "
+                                  "shared experts (as one of I=2816); T=1/4/16; ELB [1,64]; "
+                                  "1 GiB read before each timed step"},
+           "results": results, "gen_s": round(gen_s, 1)}
+    print(json.dumps(res), flush=True)
 
 
 def bench_route_fidelity(args):

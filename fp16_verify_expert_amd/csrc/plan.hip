@@ -10,7 +10,11 @@
 // dot products, then take the tokens' top-k selections, then the ELB update
 // and the stable counting sort run on the ids held in LDS.  Every output is
 // bit-identical to the separate routing, ELB and gather kernels (they run the
-// same device routines).
+// same device routines).  One CU reads the whole router for every token, so
+// beyond about one token's worth of dot products (T*(E+1)*H above 2^18) the
+// plan runs as two launches instead: the routing kernel (a workgroup per
+// token), then one workgroup for the ELB update and the maps (measured at the
+// DeepSeek-V2-Lite shape, T = 16: 75 us in one workgroup).
 #include "maps_core.h"
 #include "route_core.h"
 
@@ -57,6 +61,20 @@ __global__ __launch_bounds__(kPlanThreads) void route_plan_kernel(
                             n_active, err);
 }
 
+// The ELB update and the maps of a routed step (ids in memory).
+__global__ __launch_bounds__(kPlanThreads) void plan_tail_kernel(
+    const int32_t* __restrict__ ids, int n, int k, int E, int32_t* __restrict__ counters_row,
+    int32_t* __restrict__ off, int32_t* __restrict__ sorted_token,
+    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos,
+    int32_t* __restrict__ active, int32_t* __restrict__ n_active, int32_t* __restrict__ err) {
+    if (counters_row)
+        smoe_maps::elb_accumulate(ids, n, threadIdx.x, kPlanThreads, E, counters_row, err);
+    smoe_maps::gather_block(ids, n, k, E, off, sorted_token, sorted_pair, pair_pos, active,
+                            n_active, err);
+}
+
+constexpr long long kPlanOneGroupElems = 1 << 18;  // T*(E+1)*H run in one workgroup
+
 }  // namespace
 
 namespace smoe {
@@ -66,6 +84,15 @@ hipError_t launch_route_plan(const uint16_t* x, const uint16_t* wr, const uint16
                              int32_t* sp, int32_t* pp, int32_t* active, int32_t* n_active,
                              int32_t* err, hipStream_t s) {
     int32_t* counters_row = counters ? counters + (size_t)layer * E : nullptr;
+    const int nvec = E + (wsg ? 1 : 0);
+    if (T > 1 && (long long)T * nvec * H > kPlanOneGroupElems) {
+        hipError_t e = launch_route_topk(x, wr, wsg, T, H, E, k, renorm, ids, w, gate, s);
+        if (e != hipSuccess) return e;
+        plan_tail_kernel<<<dim3(1), dim3(kPlanThreads), 0, s>>>(ids, T * k, k, E, counters_row,
+                                                                 off, st, sp, pp, active,
+                                                                 n_active, err);
+        return hipGetLastError();
+    }
     route_plan_kernel<<<dim3(1), dim3(kPlanThreads), 0, s>>>(x, wr, wsg, T, H, E, k, renorm,
                                                              counters_row, ids, w, gate, off, st,
                                                              sp, pp, active, n_active, err);

@@ -164,7 +164,10 @@ smoe_status moe_gather(const int32_t* topk_ids, int T, int k, int E, int32_t* ex
  * moe_route_plan -- moe_route_topk, elb_count and moe_gather of one step in a
  * single launch, for decode-sized T ([S1] Key Contributions 3-4: the drafted
  * tokens' expert choices come from the target router, are tallied in GPU
- * counters and gathered by expert inside one fused launch).
+ * counters and gathered by expert inside one fused launch).  One workgroup
+ * evaluates every router dot product, so steps with more than one token and
+ * T*(E+1)*H above 2^18 run as two launches (the routing kernel, then the ELB
+ * update and the maps in one workgroup).
  *
  * Arguments and outputs are those of the three calls (same meaning, layout
  * and bit-identical values).  counters may be NULL (no ELB update; layer and
