@@ -556,13 +556,19 @@ template <int PHASE>
 hipError_t launch_phase(const F16Args& a, int slots, int RB, hipStream_t s) {
     // Reductions with at least SMOE_VF_LONG 128-K steps per wave take the
     // LDS-ring kernel (4 waves; LDS per workgroup: 4 x NSTAGE x (NM + RB) x
-    // 4 KB <= 160 KB); those that reach it with 2 waves the same kernel with
-    // 2 waves (half the LDS, so two or three workgroups share a CU: measured
-    // 3-4% faster than the register kernel on the Qwen1.5-MoE-shaped down
-    // projection, K = 1408); shorter ones the register-pipelined kernel.
+    // 4 KB <= 160 KB), shorter ones the register-pipelined kernel.  Reductions
+    // of 8-16 steps run the ring kernel with 2 waves instead (half the LDS, so
+    // two or three workgroups share a CU), 16 steps only over more than 1024
+    // work units.  Measured on the Qwen1.5-MoE shapes: the routed down
+    // projection (K = 1408) 3-4% faster than the register kernel, the routed
+    // gate/up projection (K = 2048) 5-7% faster than 4 waves; with 4 waves
+    // the Phi-shaped reductions (32 and 50 steps) stay 7% faster and the
+    // shared expert (352 workgroups) 6% faster.
     const int nsteps = a.K / kKStep;
     const bool ring = nsteps / 4 >= SMOE_VF_LONG;
-    if (!ring && nsteps / 2 >= SMOE_VF_LONG) {
+    const long long wgs = (long long)slots * a.nCB;
+    const bool two = nsteps / 2 >= SMOE_VF_LONG && (nsteps < 16 || (nsteps == 16 && wgs > 1024));
+    if (two) {
         const dim3 grid2(slots * a.nCB), block2(128);
         if (RB == 1)
             hipLaunchKernelGGL((f16_kernel<PHASE, 1, 3, 2>), grid2, block2, 0, s, a);
