@@ -511,8 +511,10 @@ def test_verify_grouped_gemm(shape, T):
 
 
 # dense regime (many rows per expert): the tiled grouped GEMM
+# hidden 384: a last, partial 256-column block in the down projection
+_H384 = dataclasses.replace(synth.TINY, name="tiny_h384", H=384, E=4, k=2, I=256)
 DENSE_CASES = [(synth.TINY, 512, None), (synth.TINY, 300, None), (synth.DS, 700, 40),
-               (synth.PHI, 2048, 24)]
+               (synth.PHI, 2048, 24), (_H384, 512, None)]
 
 
 def _sample_tokens(T, n):
