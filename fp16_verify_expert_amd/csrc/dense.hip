@@ -10,38 +10,36 @@
 // keeps the matrix cores busy.
 //
 // Work decomposition.  A small planning kernel lists the touched experts
-// with their row-tile counts; the GEMM grid covers every (expert, 256-column
+// with their row-tile counts; the GEMM grid covers every (expert, column
 // block, 128-row tile) item, expert-major with an expert's row tiles
 // innermost, so a weight tile is read from HBM once and re-read from L2 by
 // the expert's other row tiles.  Workgroup b takes item (b mod 8) * W/8 +
 // b / 8: blocks on one XCD (b mod 8) walk a contiguous run of items, which
 // keeps an expert's activation rows and weight tiles in that XCD's L2.
 //
-// Tile.  128 rows x 256 columns x 64 K per step, 4 waves in a 2 x 2 layout,
-// each wave 64 x 128 = 4 x 8 MFMA 16x16x32 f16 blocks with fp32 accumulators
-// (a wave reads 12 fragments from LDS per 32 MFMAs; with 64 x 64 wave tiles,
-// 8 per 16, the kernel measured 4.5% slower).
+// Tile.  128 rows x BN columns x 64 K per step, 4 waves in a 2 x 2 layout,
+// each wave 64 x BN/2 = 4 x BN/32 MFMA 16x16x32 f16 blocks with fp32
+// accumulators.  The gate/up projection takes BN = 256 (a wave reads 12
+// fragments from LDS per 32 MFMAs instead of 8 per 16: 916 -> 815 us at the
+// Phi-3.5-MoE shape, T = 2048), the down projection BN = 128.
 // Operands are staged global -> registers -> LDS (rows padded to 144 bytes so
 // the fragment reads of 16 rows hit 16 different bank groups); the next step's
 // loads are in flight while the current step is multiplied.  In the gate/up
-// projection the 256 tile columns are 8 pairs of (16 gate, 16 up) columns of
+// projection the tile columns are pairs of (16 gate, 16 up) columns of
 // the same h columns, so every lane holds the gate and up value of its
 // outputs and applies SwiGLU in registers.  In the down projection a last,
-// partial column block (H a multiple of 128 only) re-reads the last weight
+// partial column block (H not a multiple of BN) re-reads the last weight
 // row for the missing columns and does not store them.
 #include "common.h"
 
 namespace {
 
 constexpr int kBM = 128;             // rows per tile
-constexpr int kBN = 256;             // tile columns
+// tile columns BN: 256 in the gate/up projection, 128 in the down projection
 constexpr int kBK = 64;              // K per step
 constexpr int kLdsRow = kBK + 8;     // halves per LDS row (144 bytes)
 constexpr int kThreads = 256;
 constexpr int kChunksA = kBM * kBK / 8 / kThreads;  // 16-byte chunks per thread: activations
-constexpr int kChunksB = kBN * kBK / 8 / kThreads;  // and weights
-constexpr int kWN = kBN / 2;                        // columns per wave (2 x 2 waves)
-constexpr int kNB = kWN / 16;                       // 16-column MFMA blocks per wave
 
 struct DenseArgs {
     const uint16_t* xin;          // phase 1: x [T, H]; phase 2: h [rows, I]
@@ -52,7 +50,7 @@ struct DenseArgs {
     int K;
     int Ncol;   // output columns: I (phase 1, h) or H (phase 2, y)
     int I;
-    int nNT;    // column blocks: I/128 (phase 1) or ceil(H/256) (phase 2)
+    int nNT;    // column blocks: I/(BN/2) (phase 1) or ceil(H/BN) (phase 2)
     int Wpad;   // grid size (a multiple of 8)
     uint16_t* out;
     int32_t* err;
@@ -108,11 +106,17 @@ __global__ __launch_bounds__(64) void dense_plan_kernel(const int32_t* __restric
     }
 }
 
-// Two waves per SIMD (256 registers: 128 accumulators, the 12 fragments of a
-// 32-K step and the next step's 12 staged chunks); two 54 KB workgroups per CU.
-template <int PHASE>
+// 256-column tiles: two waves per SIMD (256 registers: 128 accumulators, the
+// 12 fragments of a 32-K step and the next step's 12 staged chunks), two 54 KB
+// workgroups per CU.  128-column tiles: three waves per SIMD (at most 168
+// registers), three workgroups per CU.
+template <int PHASE, int BN>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(2))) void dense_gemm_kernel(DenseArgs a) {
+__attribute__((amdgpu_waves_per_eu(BN == 256 ? 2 : 3))) void dense_gemm_kernel(DenseArgs a) {
+    constexpr int kBN = BN;
+    constexpr int kChunksB = kBN * kBK / 8 / kThreads;  // 16-byte chunks per thread: weights
+    constexpr int kWN = kBN / 2;                        // columns per wave (2 x 2 waves)
+    constexpr int kNB = kWN / 16;                       // 16-column MFMA blocks per wave
     __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kLdsRow];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[kBN * kLdsRow];
 
@@ -271,6 +275,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void dense_gemm_kernel(DenseArgs a) {
 }  // namespace
 
 namespace smoe {
+// Tile widths: the gate/up projection (2I weight rows, many column blocks)
+// takes 256-column tiles; the down projection (H columns, a few hundred work
+// items at the Phi-3.5-MoE shape) keeps 128, whose twice as many items fill
+// the CUs better (measured 460 vs 507 us at T = 2048).
+constexpr int kBN1 = 256, kBN2 = 128;
 size_t dense_plan_bytes(int E) { return (size_t)2 * (2 + 4 * E) * 4; }  // both projections
 
 hipError_t launch_dense_ffn(const uint16_t* x, const int32_t* sorted_token, const int32_t* off,
@@ -289,7 +298,7 @@ hipError_t launch_dense_ffn(const uint16_t* x, const int32_t* sorted_token, cons
     a1.K = H;
     a1.Ncol = I;
     a1.I = I;
-    a1.nNT = I / (kBN / 2);
+    a1.nNT = I / (kBN1 / 2);
     a1.Wpad = ((mt_bound * a1.nNT) + 7) & ~7;
     a1.out = h;
     a1.err = err;
@@ -298,7 +307,7 @@ hipError_t launch_dense_ffn(const uint16_t* x, const int32_t* sorted_token, cons
     a2.sorted_token = nullptr;
     a2.K = I;
     a2.Ncol = H;
-    a2.nNT = (H + kBN - 1) / kBN;
+    a2.nNT = (H + kBN2 - 1) / kBN2;
     a2.Wpad = ((mt_bound * a2.nNT) + 7) & ~7;
     a2.out = y;
     // the two projections list the same experts; each plan holds its own item bases
@@ -308,10 +317,10 @@ hipError_t launch_dense_ffn(const uint16_t* x, const int32_t* sorted_token, cons
     dense_plan_kernel<<<1, 64, 0, s>>>(off, active, n_active, mask, E, a2.nNT, plan2);
     hipError_t st = hipGetLastError();
     if (st != hipSuccess) return st;
-    dense_gemm_kernel<1><<<a1.Wpad, kThreads, 0, s>>>(a1);
+    dense_gemm_kernel<1, kBN1><<<a1.Wpad, kThreads, 0, s>>>(a1);
     st = hipGetLastError();
     if (st != hipSuccess) return st;
-    dense_gemm_kernel<2><<<a2.Wpad, kThreads, 0, s>>>(a2);
+    dense_gemm_kernel<2, kBN2><<<a2.Wpad, kThreads, 0, s>>>(a2);
     return hipGetLastError();
 }
 }  // namespace smoe
