@@ -226,6 +226,17 @@ def test_route_plan_empty_and_no_counters():
     ids, _, _, m = fve.moe_route_plan(dev(x), wr, s.k)
     ref = oracle.route_topk(x, synth.router(s), s.k)
     assert np.array_equal(host(ids), ref["ids"])
+    # the two-launch form (T * (E+1) * H above 2^18) without counters: the same
+    # maps as moe_gather on the same ids
+    xd = synth.tokens(synth.DS, 16, step=5)
+    wd = dev(synth.router(synth.DS))
+    ids2, _, _, m2 = fve.moe_route_plan(dev(xd), wd, synth.DS.k)
+    g2 = fve.moe_gather(ids2, synth.DS.E)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(ids2), oracle.route_topk(xd, synth.router(synth.DS),
+                                                        synth.DS.k)["ids"])
+    for key in ("offsets", "active", "n_active", "sorted_token", "sorted_pair", "pair_pos"):
+        assert torch.equal(m2[key], g2[key]), key
     with pytest.raises(fve.SmoeError):   # beyond the one-workgroup limits
         fve.moe_route_plan(dev(synth.tokens(synth.DS, 64)), dev(synth.router(synth.DS)),
                            synth.DS.k)
