@@ -32,6 +32,29 @@ def test_abi_version():
     assert fve.lib().smoe_abi_version() == fve.ABI_VERSION
 
 
+def _header_param_counts():
+    """Parameter count of every function declared in include/smoe.h."""
+    import re
+    txt = open(fve.HEADER_PATH).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    out = {}
+    for m in re.finditer(r"^\s*(?:smoe_status|int|const char\*|size_t)\s+(\w+)\s*\(([^)]*)\)\s*;",
+                         txt, re.M | re.S):
+        params = m.group(2).strip()
+        out[m.group(1)] = 0 if params in ("", "void") else len(params.split(","))
+    return out
+
+
+def test_binding_signatures_match_header():
+    """The binding's ctypes argument lists have the header's parameter counts
+    (a drifted declaration would pass arguments in the wrong slots)."""
+    counts = _header_param_counts()
+    assert set(counts) == set(fve.header_functions())
+    for name, (_, args) in fve._SIGS.items():
+        assert name in counts, name
+        assert len(args) == counts[name], (name, len(args), counts[name])
+
+
 def _err():
     return fve.lib().smoe_last_error().decode()
 
