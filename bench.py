@@ -253,12 +253,12 @@ def main():
             verify(args.warmup + st)
         torch.cuda.synchronize()
 
-    # every call of the split draft step and of the verify step on its own
-    # (HIP events around each; launch gaps excluded)
+    # every call of the split draft step and of the verify step on its own,
+    # and the ELB update (HIP events around each; launch gaps excluded)
     nl = min(K, 20)
     calls = {n: [(mk(), mk()) for _ in range(nl)] for n in
              ("moe_route_plan", "w4a16_grouped_ffn", "moe_combine_draft", "moe_route_topk",
-              "moe_gather", "verify_grouped_gemm", "moe_combine_verify")}
+              "elb_count", "moe_gather", "verify_grouped_gemm", "moe_combine_verify")}
     for st in range(nl):
         i = args.warmup + st
         x = xs_d[i % POOL]
@@ -278,6 +278,11 @@ def main():
         ev("moe_route_topk")[0].record()
         fve.moe_route_topk(xv, router, k, topk_ids=bv["ids"], topk_w=bv["w"])
         ev("moe_route_topk")[1].record()
+        # the ELB update of the same ids on its own (the draft steps fold it
+        # into their routing launch)
+        ev("elb_count")[0].record()
+        fve.elb_count(bv["ids"], E, 0, counters, err)
+        ev("elb_count")[1].record()
         ev("moe_gather")[0].record()
         fve.moe_gather(bv["ids"], E, err, out=bv["maps"])
         ev("moe_gather")[1].record()
