@@ -29,8 +29,11 @@ def _err():
 
 # ---------------------------------------------------------------- S1 ----
 
+# the ABI's largest routers: 256 experts, top-32 (the fused draft step's limit)
+_E256 = dataclasses.replace(synth.TINY, name="tiny_e256_k32", E=256, k=32)
 ROUTE_CASES = [(synth.TINY, 4), (synth.TINY, 1), (synth.DS, 1), (synth.DS, 16), (synth.QWEN, 9),
-               (synth.QWEN, 17), (synth.PHI, 1), (synth.PHI, 17), (synth.DS, 257)]
+               (synth.QWEN, 17), (synth.PHI, 1), (synth.PHI, 17), (synth.DS, 257), (_E256, 1),
+               (_E256, 5)]
 
 
 @pytest.mark.parametrize("shape,T", ROUTE_CASES, ids=lambda v: getattr(v, "name", str(v)))
@@ -173,7 +176,7 @@ def test_gather_bad_ids_and_empty():
 
 PLAN_CASES = [(synth.TINY, 1), (synth.TINY, 37), (synth.TINY, 455), (synth.DS, 1),
               (synth.DS, 16), (synth.DS, 62), (synth.QWEN, 1), (synth.QWEN, 17), (synth.PHI, 1),
-              (synth.PHI, 17)]
+              (synth.PHI, 17), (_E256, 1), (_E256, 3)]
 
 
 @pytest.mark.parametrize("shape,T", PLAN_CASES, ids=lambda v: getattr(v, "name", str(v)))
@@ -349,7 +352,7 @@ _ALL = dataclasses.replace(synth.TINY, name="tiny_k_eq_e", k=8)            # eve
 _RENORM = dataclasses.replace(synth.TINY, name="tiny_renorm_k3", k=3, renormalize=True)
 DRAFT_FUSED_CASES = [(synth.TINY, 0), (synth.TINY, 7), (synth.DS, 0), (synth.DS, 3),
                      (synth.QWEN, 0), (synth.PHI, 0), (synth.PHI, 5), (_WIDE, 0), (_ALL, 0),
-                     (_RENORM, 2), (_LONG_I, 0), (_LONG_H, 1)]
+                     (_RENORM, 2), (_LONG_I, 0), (_LONG_H, 1), (_E256, 0), (_E256, 4)]
 
 
 @pytest.mark.parametrize("shape,step", DRAFT_FUSED_CASES,
