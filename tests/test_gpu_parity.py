@@ -488,7 +488,10 @@ VERIFY_CASES = [(synth.TINY, 17), (synth.TINY, 40), (synth.QWEN, 9), (synth.PHI,
                 (synth.DS, 16),
                 # T <= 4: the one-wave-per-column kernel (1, 2 and 4 rows per block)
                 (synth.TINY, 1), (synth.TINY, 3), (synth.QWEN, 1), (synth.DS, 2),
-                (synth.QWEN, 4), (synth.PHI, 1)]
+                (synth.QWEN, 4), (synth.PHI, 1),
+                # the largest reductions: hidden 16384 (past the matrix-vector
+                # kernel's 8192, so MFMA even at T = 1) and intermediate 12288
+                (_LONG_H, 1), (_LONG_H, 9), (_LONG_I, 3), (_LONG_I, 17)]
 
 
 @pytest.mark.parametrize("shape,T", VERIFY_CASES, ids=lambda v: getattr(v, "name", str(v)))
