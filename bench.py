@@ -136,7 +136,8 @@ def main():
                               active=torch.empty(E, dtype=torch.int32, device=dev),
                               n_active=torch.empty(1, dtype=torch.int32, device=dev)),
                     y=torch.empty((n, H), dtype=torch.float16, device=dev),
-                    out=torch.empty((T, H), dtype=torch.float16, device=dev))
+                    out=torch.empty((T, H), dtype=torch.float16, device=dev),
+                    lg=torch.empty(T * (E + 1), dtype=torch.float32, device=dev))
     bd, bv = bufs(T_D), bufs(T_V)
     ws_d = fve.new_workspace(0, T_D, k, H, I, E)
     ws_v = fve.new_workspace(1, T_V, k, H, I, E)
@@ -146,7 +147,8 @@ def main():
     def draft_split(i, ev=None):
         x = xs_d[i % POOL]
         fve.moe_route_plan(x, router, k, counters=counters, layer=0, err_word=err,
-                           topk_ids=bd["ids"], topk_w=bd["w"], maps=bd["maps"])
+                           topk_ids=bd["ids"], topk_w=bd["w"], maps=bd["maps"],
+                           logits_ws=bd["lg"])
         if ev: ev[0].record()
         fve.w4a16_grouped_ffn(x, bd["maps"], t4, T_D, k, H, I, E, ws_d, y_sorted=bd["y"],
                               err_word=err)
@@ -265,7 +267,8 @@ def main():
         ev = lambda n: calls[n][st]
         ev("moe_route_plan")[0].record()
         fve.moe_route_plan(x, router, k, counters=counters, layer=0, err_word=err,
-                           topk_ids=bd["ids"], topk_w=bd["w"], maps=bd["maps"])
+                           topk_ids=bd["ids"], topk_w=bd["w"], maps=bd["maps"],
+                           logits_ws=bd["lg"])
         ev("moe_route_plan")[1].record()
         ev("w4a16_grouped_ffn")[0].record()
         fve.w4a16_grouped_ffn(x, bd["maps"], t4, T_D, k, H, I, E, ws_d, y_sorted=bd["y"],
@@ -503,12 +506,13 @@ def bench_draft_formats(args):
                 ids_b = torch.empty((T, shape.k), dtype=torch.int32, device=dev)
                 w_b = torch.empty((T, shape.k), dtype=torch.float32, device=dev)
                 maps_b = fve._new_maps(T, shape.k, shape.E, dev)
+                lg_b = torch.empty(T * (shape.E + 1), dtype=torch.float32, device=dev)
                 touched = []
 
                 def step(i, ev=None):
                     x = xs[i % POOL]
                     ids, w, _, m = fve.moe_route_plan(x, router, shape.k, topk_ids=ids_b,
-                                                      topk_w=w_b, maps=maps_b)
+                                                      topk_w=w_b, maps=maps_b, logits_ws=lg_b)
                     if ev: ev[0].record()
                     fve.wq_grouped_ffn(x, m, table, T, shape.k, shape.H, shape.I, shape.E, ws,
                                        bits, y_sorted=y)
@@ -564,8 +568,8 @@ def bench_ds_draft(args):
     intermediate 2816, ELB counters over one layer) at T = 1, 4 and 16 tokens,
     every weight in HBM.  T = 1: moe_draft_route_ffn (routing, ELB, maps,
     routed INT4 FFN and the shared experts in three launches) + moe_combine;
-    T > 1: moe_route_plan + w4a16_grouped_ffn + the shared experts through
-    verify_grouped_gemm + moe_combine.  A read of 1 GiB runs before each timed
+    T > 1: moe_route_plan + w4a16_grouped_ffn, beside them on a side stream
+    the shared experts through verify_grouped_gemm, then moe_combine.  A read of 1 GiB runs before each timed
     step, outside its events, so the weights come from HBM.  Reported per T:
     the step's wall time (HIP events around its calls, no markers inside),
     the INT4 bytes of the touched experts and the shared experts' FP16 bytes,
@@ -592,6 +596,8 @@ def bench_ds_draft(args):
     scrub = torch.empty(1 << 29, dtype=torch.float16, device=dev)  # 1 GiB
     counters = torch.zeros((1, E), dtype=torch.int32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
+    err_sh = torch.zeros(1, dtype=torch.int32, device=dev)  # the side stream's error word
+    side = torch.cuda.Stream(device=dev)  # default priority
     mk = lambda: torch.cuda.Event(enable_timing=True)
     K = max(args.steps, 5)
     b4 = s.int4_bytes_per_expert
@@ -609,6 +615,7 @@ def bench_ds_draft(args):
         ids_b = torch.empty((T, k), dtype=torch.int32, device=dev)
         w_b = torch.empty((T, k), dtype=torch.float32, device=dev)
         maps_b = fve._new_maps(T, k, E, dev)
+        lg_b = torch.empty(T * (E + 1), dtype=torch.float32, device=dev)
 
         def step(i):
             x = xs[i % POOL]
@@ -618,12 +625,18 @@ def bench_ds_draft(args):
                                         y_sorted=y, shared=shared, shared_h=sh_h,
                                         shared_out=sh_out)
             else:
+                # the shared experts read only x: they run on a side stream
+                # beside routing and the routed INT4 launches
+                main = torch.cuda.current_stream()
+                side.wait_stream(main)
+                with torch.cuda.stream(side):
+                    fve.verify_grouped_gemm(x, iota, offs, tsh, T, T, H, Is, 1, wsv,
+                                            y_sorted=sh_out, err_word=err_sh)
                 fve.moe_route_plan(x, router, k, counters=counters, err_word=err,
-                                   topk_ids=ids_b, topk_w=w_b, maps=maps_b)
+                                   topk_ids=ids_b, topk_w=w_b, maps=maps_b, logits_ws=lg_b)
                 fve.w4a16_grouped_ffn(x, maps_b, table, T, k, H, I, E, ws, y_sorted=y,
                                       err_word=err)
-                fve.verify_grouped_gemm(x, iota, offs, tsh, T, T, H, Is, 1, wsv,
-                                        y_sorted=sh_out, err_word=err)
+                main.wait_stream(side)
             fve.moe_combine(y, maps_b["pair_pos"], w_b, sh_out, out=out)
 
         touched = []
@@ -641,7 +654,7 @@ def bench_ds_draft(args):
             step(args.warmup + st)
             ev[st][1].record()
         torch.cuda.synchronize()
-        assert int(err.item()) == 0, "device error word set"
+        assert int(err.item()) == 0 and int(err_sh.item()) == 0, "device error word set"
         idx = [(args.warmup + st) % POOL for st in range(K)]
         b_int4 = sum(touched[i] * b4 for i in idx) / K
         b_sh = s.shared_f16_bytes
@@ -654,7 +667,7 @@ def bench_ds_draft(args):
                         "all_weight_frac_hbm": round((b_int4 + b_sh) / us / 1e3 / HBM_PEAK_GBS, 4),
                         "path": ("moe_draft_route_ffn (shared experts inside) + moe_combine"
                                  if T == 1 else "moe_route_plan + w4a16_grouped_ffn + "
-                                 "verify_grouped_gemm (shared) + moe_combine")})
+                                 "verify_grouped_gemm (shared, side stream) + moe_combine")})
         print(json.dumps(results[-1]), file=sys.stderr, flush=True)
     r1 = results[0]
     res = {"metric": "MoE-layer INT4 draft weight GB/s (% HBM peak); verify TFLOP/s (% MFMA)",

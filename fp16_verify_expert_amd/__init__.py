@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsmoe.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "smoe.h")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 SMOE_DERR_BAD_ID = 1
 SMOE_DERR_NULL_EXPERT = 2
@@ -45,7 +45,7 @@ _SIGS = {
     "elb_count": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
     "moe_gather": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_route_plan": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
-                            _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+                            _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
     "w4a16_grouped_ffn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp,
                                _sz, _vp, _vp]),
     "wq_grouped_ffn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
@@ -177,10 +177,14 @@ def _new_maps(T: int, k: int, E: int, dev) -> dict:
 
 def moe_route_plan(x, w_router, k: int, renormalize: bool = False, w_shared_gate=None, *,
                    counters=None, layer: int = 0, err_word=None, topk_ids=None, topk_w=None,
-                   shared_gate=None, maps=None, stream=None):
-    """Routing, ELB update (when counters is given) and gather maps in one
-    launch.  Returns (topk_ids, topk_w, shared_gate, maps) with maps as from
-    moe_gather."""
+                   shared_gate=None, maps=None, logits_ws=None, spread: bool = True,
+                   stream=None):
+    """Routing, ELB update (when counters is given) and gather maps.  With
+    spread (the default) the call passes the library a logits workspace
+    (logits_ws, a device tensor of at least T*(E+1) fp32, allocated here when
+    None), so large steps spread the router dot products over the chip;
+    spread=False passes none.  Returns (topk_ids, topk_w, shared_gate, maps)
+    with maps as from moe_gather."""
     _check(x, torch.float16, "x")
     _check(w_router, torch.float16, "w_router")
     T, H = x.shape
@@ -200,11 +204,19 @@ def moe_route_plan(x, w_router, k: int, renormalize: bool = False, w_shared_gate
         L = counters.shape[0]
     if maps is None:
         maps = _new_maps(T, k, E, dev)
+    if not spread:
+        logits_ws = None
+    elif logits_ws is None:
+        logits_ws = torch.empty(max(1, T * (E + 1)), dtype=torch.float32, device=dev)
+    else:
+        _check(logits_ws, torch.float32, "logits_ws")
+    ws_bytes = logits_ws.numel() * logits_ws.element_size() if logits_ws is not None else 0
     _call("moe_route_plan", _p(x), _p(w_router), _p(w_shared_gate), T, H, E, k,
           1 if renormalize else 0, layer, L, _p(counters), _p(topk_ids), _p(topk_w),
           _p(shared_gate) if w_shared_gate is not None else None, _p(maps["offsets"]),
           _p(maps["sorted_token"]), _p(maps["sorted_pair"]), _p(maps["pair_pos"]),
-          _p(maps["active"]), _p(maps["n_active"]), _p(err_word), _s(stream))
+          _p(maps["active"]), _p(maps["n_active"]), _p(logits_ws), ws_bytes, _p(err_word),
+          _s(stream))
     return topk_ids, topk_w, shared_gate, maps
 
 

@@ -160,7 +160,8 @@ smoe_status moe_route_plan(const uint16_t* x, const uint16_t* w_router,
                            int32_t* topk_ids, float* topk_w, float* shared_gate,
                            int32_t* expert_offsets, int32_t* sorted_token, int32_t* sorted_pair,
                            int32_t* pair_pos, int32_t* active, int32_t* n_active,
-                           int32_t* err_word, void* stream) {
+                           void* workspace, size_t workspace_bytes, int32_t* err_word,
+                           void* stream) {
     REQUIRE(expert_offsets && active && n_active, SMOE_ERR_NULL,
             "moe_route_plan: expert_offsets, active and n_active are required");
     REQUIRE(T == 0 || (x && w_router && topk_ids && topk_w && sorted_token && sorted_pair &&
@@ -182,12 +183,18 @@ smoe_status moe_route_plan(const uint16_t* x, const uint16_t* w_router,
             "moe_route_plan: layer=%d must be in [0, L=%d)", layer, L);
     REQUIRE(aligned(x, 16) && aligned(w_router, 16) && aligned(w_shared_gate, 16),
             SMOE_ERR_SHAPE, "moe_route_plan: x, w_router, w_shared_gate must be 16-byte aligned");
+    const size_t lg_bytes = (size_t)T * (E + (w_shared_gate ? 1 : 0)) * sizeof(float);
+    REQUIRE(!workspace || (workspace_bytes >= lg_bytes && aligned(workspace, 16)),
+            SMOE_ERR_WORKSPACE,
+            "moe_route_plan: workspace of %zu bytes, %zu needed (T*(E+1) fp32 logits, "
+            "16-byte aligned)", workspace_bytes, lg_bytes);
     CHECK_DEVICE();
     // T == 0 still writes empty maps (zero offsets, no active experts).
     return hip_result(smoe::launch_route_plan(x, w_router, w_shared_gate, T, H, E, k,
                                               renormalize ? 1 : 0, layer, counters, topk_ids,
                                               topk_w, shared_gate, expert_offsets, sorted_token,
                                               sorted_pair, pair_pos, active, n_active, err_word,
+                                              static_cast<float*>(workspace),
                                               static_cast<hipStream_t>(stream)),
                       "moe_route_plan launch");
 }

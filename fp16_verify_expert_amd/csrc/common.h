@@ -47,7 +47,7 @@ hipError_t launch_route_plan(const uint16_t* x, const uint16_t* wr, const uint16
                              int H, int E, int k, int renorm, int layer, int32_t* counters,
                              int32_t* ids, float* w, float* gate, int32_t* off, int32_t* st,
                              int32_t* sp, int32_t* pp, int32_t* active, int32_t* n_active,
-                             int32_t* err, hipStream_t s);
+                             int32_t* err, float* lg, hipStream_t s);
 hipError_t launch_elb_count(const int32_t* ids, int n, int E, int layer, int32_t* counters,
                             int32_t* err, hipStream_t s);
 hipError_t launch_gather(const int32_t* ids, int n, int k, int E, int32_t* off, int32_t* st,

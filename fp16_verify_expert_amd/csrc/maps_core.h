@@ -168,6 +168,107 @@ SMOE_DEV void gather_block(const int32_t* ids, int n, int k, int E, int32_t* __r
     }
 }
 
+// The ELB update and the maps of n <= kGatherThreads pairs whose ids are in
+// LDS, by one workgroup of kGatherThreads threads (all of which must call
+// it): thread e < E counts the pairs of expert e (and adds that count to the
+// ELB row), thread p counts the earlier pairs with its id, so no loop runs
+// over the distinct ids of a wave.  The same stable counting sort as
+// gather_block, so the same maps.
+SMOE_DEV void small_maps(const int32_t* ids_s, int n, int k, int E,
+                         int32_t* __restrict__ counters_row, int32_t* __restrict__ off,
+                         int32_t* __restrict__ sorted_token, int32_t* __restrict__ sorted_pair,
+                         int32_t* __restrict__ pair_pos, int32_t* __restrict__ active,
+                         int32_t* __restrict__ n_active, int32_t* __restrict__ err) {
+    __shared__ int cnt_s[256];
+    __shared__ int base_s[256];
+    __shared__ int nvalid_s;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    // 1. per-expert counts (and the ELB increments); invalid ids flagged
+    if (tid < E) {
+        int c = 0;
+#pragma unroll 8
+        for (int q = 0; q < n; ++q) c += (ids_s[q] == tid) ? 1 : 0;
+        cnt_s[tid] = c;
+        if (counters_row && c) atomicAdd(counters_row + tid, c);
+    }
+    if (tid < n) {
+        const int e = ids_s[tid];
+        if (e < 0 || e >= E) flag_error(err, SMOE_DERR_BAD_ID);
+    }
+    __syncthreads();
+
+    // 2. exclusive scan of the counts and the active list (wave 0; E <= 256,
+    //    4 consecutive experts per lane)
+    if (wave == 0) {
+        int c[4], a[4];
+        int sum = 0, na = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * lane + i;
+            c[i] = (e < E) ? cnt_s[e] : 0;
+            a[i] = (c[i] > 0) ? 1 : 0;
+            sum += c[i];
+            na += a[i];
+        }
+        int incl = sum, inca = na;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int o = __shfl_up(incl, d);
+            const int oa = __shfl_up(inca, d);
+            if (lane >= d) {
+                incl += o;
+                inca += oa;
+            }
+        }
+        int run = incl - sum, runa = inca - na;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * lane + i;
+            if (e < E) {
+                base_s[e] = run;
+                off[e] = run;
+                if (a[i]) active[runa] = e;
+            }
+            run += c[i];
+            runa += a[i];
+        }
+        const int total = __shfl(incl, 63);
+        const int total_a = __shfl(inca, 63);
+        if (lane == 0) {
+            off[E] = total;
+            *n_active = total_a;
+            nvalid_s = total;
+        }
+        for (int e = total_a + lane; e < E; e += 64) active[e] = -1;
+    }
+    __syncthreads();
+
+    // 3. placement: sorted row = base of the expert + earlier pairs of it
+    if (tid < n) {
+        const int p = tid;
+        const int e = ids_s[p];
+        if (e >= 0 && e < E) {
+            int r = 0;
+#pragma unroll 8
+            for (int q = 0; q < p; ++q) r += (ids_s[q] == e) ? 1 : 0;
+            const int pos = base_s[e] + r;
+            sorted_pair[pos] = p;
+            sorted_token[pos] = p / k;
+            pair_pos[p] = pos;
+        } else {
+            pair_pos[p] = -1;
+        }
+    }
+    // rows past the last valid one (dropped pairs) carry -1
+    for (int r = nvalid_s + tid; r < n; r += kGatherThreads) {
+        sorted_pair[r] = -1;
+        sorted_token[r] = -1;
+    }
+}
+
 // The maps and ELB increments of one token's k distinct ids (ids in LDS), by
 // any number of threads of a workgroup: the pair of rank j sits at sorted row
 // #{i : ids[i] < ids[j]}, which is where the stable counting sort puts it

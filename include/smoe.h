@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SMOE_ABI_VERSION 2
+#define SMOE_ABI_VERSION 3
 
 typedef enum {
     SMOE_OK = 0,
@@ -165,15 +165,24 @@ smoe_status moe_gather(const int32_t* topk_ids, int T, int k, int E, int32_t* ex
  * single launch, for decode-sized T ([S1] Key Contributions 3-4: the drafted
  * tokens' expert choices come from the target router, are tallied in GPU
  * counters and gathered by expert inside one fused launch).  One workgroup
- * evaluates every router dot product, so steps with more than one token and
- * T*(E+1)*H above 2^18 run as two launches (the routing kernel, then the ELB
- * update and the maps in one workgroup).
+ * evaluates every router dot product of a small step.  Larger steps
+ * (T*(E+1)*H above 2^16) run as two launches when a workspace is given: the
+ * router dot products one per wave across the chip into the workspace, then
+ * one workgroup for the top k, the ELB update and the maps.  Without one,
+ * steps with more than one token and T*(E+1)*H above 2^18 run the routing
+ * kernel, then the ELB update and the maps in one workgroup.
  *
  * Arguments and outputs are those of the three calls (same meaning, layout
- * and bit-identical values).  counters may be NULL (no ELB update; layer and
- * L are then ignored).  Limits: T*k <= 1024 and T*(E+1) <= 4096 (one
- * workgroup holds the pairs and logits); beyond them SMOE_ERR_SHAPE -- use the
- * separate calls.  T == 0 writes empty maps.
+ * and bit-identical values, whichever form runs).  counters may be NULL (no
+ * ELB update; layer and L are then ignored).
+ *   workspace        device, NULL or >= 4*T*(E+1) bytes (E+1 with a shared
+ *                    gate, else E), 16-byte aligned; caller-owned, holds the
+ *                    step's fp32 logits until the call's kernels end; a
+ *                    smaller workspace_bytes or a misaligned workspace is
+ *                    SMOE_ERR_WORKSPACE.
+ * Limits: T*k <= 1024 and T*(E+1) <= 4096 (one workgroup holds the pairs and
+ * logits); beyond them SMOE_ERR_SHAPE -- use the separate calls.  T == 0
+ * writes empty maps.
  * ---------------------------------------------------------------------- */
 smoe_status moe_route_plan(const uint16_t* x, const uint16_t* w_router,
                            const uint16_t* w_shared_gate, int T, int H, int E, int k,
@@ -181,7 +190,8 @@ smoe_status moe_route_plan(const uint16_t* x, const uint16_t* w_router,
                            int32_t* topk_ids, float* topk_w, float* shared_gate,
                            int32_t* expert_offsets, int32_t* sorted_token, int32_t* sorted_pair,
                            int32_t* pair_pos, int32_t* active, int32_t* n_active,
-                           int32_t* err_word, void* stream);
+                           void* workspace, size_t workspace_bytes, int32_t* err_word,
+                           void* stream);
 
 /* ------------------------------------------------------------------------
  * w4a16_grouped_ffn -- draft routed-expert SwiGLU FFN over GPTQ INT4 weights

@@ -96,10 +96,10 @@ def test_route_plan_validation():
     maps = [FAKE] * 6   # offsets, sorted_token, sorted_pair, pair_pos, active, n_active
 
     def call(x=FAKE, wr=FAKE, wsg=None, T=1, H=256, E=8, k=2, layer=0, Lc=1, counters=FAKE,
-             gate=None, mp=None):
+             gate=None, mp=None, ws=None, wsb=0):
         m = maps if mp is None else mp
         return L.moe_route_plan(x, wr, wsg, T, H, E, k, 0, layer, Lc, counters, outs[0], outs[1],
-                                gate, *m, None, None)
+                                gate, *m, ws, wsb, None, None)
     assert call(x=None) == 1
     assert call(wsg=FAKE) == 1                      # gate output missing
     assert call(mp=[None] + maps[1:]) == 1          # offsets missing
@@ -110,6 +110,10 @@ def test_route_plan_validation():
     assert call(layer=1, Lc=1) == 2                 # layer outside [0, L)
     assert call(x=V(0x1002)) == 2 and "aligned" in _err()
     assert call(T=-1) == 2
+    # the logits workspace: T*E fp32 (T*(E+1) with a shared gate), 16-byte aligned
+    assert call(T=4, E=8, ws=FAKE, wsb=4 * 4 * 8 - 1) == 6 and "128 needed" in _err()
+    assert call(T=4, E=8, wsg=FAKE, gate=FAKE, ws=FAKE, wsb=4 * 4 * 8) == 6 and "144" in _err()
+    assert call(T=4, E=8, ws=V(0x1004), wsb=1 << 10) == 6 and "aligned" in _err()
 
 
 def test_wq_validation():

@@ -179,10 +179,14 @@ PLAN_CASES = [(synth.TINY, 1), (synth.TINY, 37), (synth.TINY, 455), (synth.DS, 1
               (synth.PHI, 17), (_E256, 1), (_E256, 3)]
 
 
+@pytest.mark.parametrize("spread", [True, False], ids=["logits_ws", "no_ws"])
 @pytest.mark.parametrize("shape,T", PLAN_CASES, ids=lambda v: getattr(v, "name", str(v)))
-def test_route_plan_matches_separate_calls(shape, T):
-    """The fused plan equals routing + ELB + gather bit for bit, and the oracle."""
-    say(f"route plan {shape.name} T={T}")
+def test_route_plan_matches_separate_calls(shape, T, spread):
+    """The fused plan equals routing + ELB + gather bit for bit, and the oracle,
+    with a logits workspace (steps with T*(E+1)*H above 2^16 spread their dot
+    products over the chip; the workspace starts as NaN so nothing depends on
+    its contents) and without one."""
+    say(f"route plan {shape.name} T={T} spread={spread}")
     E, k = shape.E, shape.k
     wr = synth.router(shape)
     x = synth.tokens(shape, T, step=5)
@@ -192,8 +196,12 @@ def test_route_plan_matches_separate_calls(shape, T):
     c0 = np.random.default_rng(T).integers(0, 50, size=(3, E)).astype(np.int32)
     counters = dev(c0)
     err = _err()
+    lws = None
+    if spread:
+        lws = torch.full((T * (E + 1),), float("nan"), dtype=torch.float32, device="cuda")
     ids, w, gate, m = fve.moe_route_plan(dev(x), dev(wr), k, shape.renormalize, dgvec,
-                                         counters=counters, layer=1, err_word=err)
+                                         counters=counters, layer=1, err_word=err,
+                                         logits_ws=lws, spread=spread)
     ids2, w2, gate2 = fve.moe_route_topk(dev(x), dev(wr), k, shape.renormalize, dgvec)
     counters2 = dev(c0)
     fve.elb_count(ids2, E, 1, counters2)
@@ -229,17 +237,19 @@ def test_route_plan_empty_and_no_counters():
     ids, _, _, m = fve.moe_route_plan(dev(x), wr, s.k)
     ref = oracle.route_topk(x, synth.router(s), s.k)
     assert np.array_equal(host(ids), ref["ids"])
-    # the two-launch form (T * (E+1) * H above 2^18) without counters: the same
-    # maps as moe_gather on the same ids
+    # the two-launch forms (spread logits, or the routing kernel when no
+    # workspace is given) without counters: the same maps as moe_gather on the
+    # same ids
     xd = synth.tokens(synth.DS, 16, step=5)
     wd = dev(synth.router(synth.DS))
-    ids2, _, _, m2 = fve.moe_route_plan(dev(xd), wd, synth.DS.k)
-    g2 = fve.moe_gather(ids2, synth.DS.E)
-    torch.cuda.synchronize()
-    assert np.array_equal(host(ids2), oracle.route_topk(xd, synth.router(synth.DS),
-                                                        synth.DS.k)["ids"])
-    for key in ("offsets", "active", "n_active", "sorted_token", "sorted_pair", "pair_pos"):
-        assert torch.equal(m2[key], g2[key]), key
+    for spread in (True, False):
+        ids2, _, _, m2 = fve.moe_route_plan(dev(xd), wd, synth.DS.k, spread=spread)
+        g2 = fve.moe_gather(ids2, synth.DS.E)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(ids2), oracle.route_topk(xd, synth.router(synth.DS),
+                                                            synth.DS.k)["ids"])
+        for key in ("offsets", "active", "n_active", "sorted_token", "sorted_pair", "pair_pos"):
+            assert torch.equal(m2[key], g2[key]), key
     with pytest.raises(fve.SmoeError):   # beyond the one-workgroup limits
         fve.moe_route_plan(dev(synth.tokens(synth.DS, 64)), dev(synth.router(synth.DS)),
                            synth.DS.k)
