@@ -168,8 +168,9 @@ def main():
 
     def verify(i, ev=None):
         x = xs_v[i % POOL]
-        fve.moe_route_topk(x, router, k, topk_ids=bv["ids"], topk_w=bv["w"])
-        fve.moe_gather(bv["ids"], E, err, out=bv["maps"])
+        # routing and maps in one plan (no ELB update for verification)
+        fve.moe_route_plan(x, router, k, err_word=err, topk_ids=bv["ids"], topk_w=bv["w"],
+                           maps=bv["maps"], logits_ws=bv["lg"])
         if ev: ev[0].record()
         fve.verify_grouped_gemm(x, bv["maps"]["sorted_token"], bv["maps"]["offsets"], t16, T_V,
                                 T_V * k, H, I, E, ws_v, active=bv["maps"]["active"],

@@ -338,9 +338,17 @@ class ChunkEngine:
         main = torch.cuda.current_stream()
         T = x.shape[0]
         xn = x
+        # routing and maps in one plan (no ELB update: verification does not
+        # tally draft choices) while it fits one workgroup's limits
+        plan = T * self.k <= 1024 and T * (self.E + 1) <= 4096
+        lg = torch.empty(max(1, T * (self.E + 1)), dtype=torch.float32, device=self.dev)
         for l, ly in enumerate(self.layers):
-            ids, w, gate = moe_route_topk(xn, ly.router, self.k, False, ly.shared_gate)
-            maps = moe_gather(ids, self.E, self.err)
+            if plan:
+                ids, w, gate, maps = moe_route_plan(xn, ly.router, self.k, False, ly.shared_gate,
+                                                    err_word=self.err, logits_ws=lg)
+            else:
+                ids, w, gate = moe_route_topk(xn, ly.router, self.k, False, ly.shared_gate)
+                maps = moe_gather(ids, self.E, self.err)
             sh = self._shared_fork(l, xn)
             rows = T * self.k
             y = torch.empty((rows, self.H), dtype=torch.float16, device=self.dev)
