@@ -337,6 +337,8 @@ smoe_status verify_grouped_gemm(const uint16_t* x, const int32_t* sorted_token,
  *   out[t] = fp16( sum_j topk_w[t,j] * y_sorted[pair_pos[t*k+j]]
  *                  + c_t * shared_out[t] + residual[t] )
  * summed in fp32 in that order (j increasing), one rounding to fp16.
+ *   y_sorted     fp16 [T*k, H]
+ *   pair_pos     int32 [T, k], rows of y_sorted
  *   shared_out   fp16 [T, H] optional (NULL = no shared term)
  *   shared_scale fp32 [T]    optional (NULL = 1), c_t
  *   residual     fp16 [T, H] optional (NULL = none)

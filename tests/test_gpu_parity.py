@@ -759,6 +759,38 @@ def test_combine():
     assert np.array_equal(host(out2), y[:T][pp1])
 
 
+@pytest.mark.parametrize("T,k", [(1, 2), (1, 6), (1, 8), (2, 4)])
+def test_combine_few_rows(T, k):
+    """Steps of at most 8 rows (one batch of slots): the oracle's sums, with a
+    dropped pair and with the norm epilogue, and the same bits as the same
+    tokens inside a step of more rows."""
+    rng = np.random.default_rng(10 * T + k)
+    H = 2048
+    n = T * k
+    y = rng.standard_normal((n, H)).astype(np.float16)
+    pp = rng.permutation(n).astype(np.int32)
+    pp[n - 1] = -1
+    w = rng.random((T, k)).astype(np.float32)
+    sh = rng.standard_normal((T, H)).astype(np.float16)
+    c = rng.random(T).astype(np.float32)
+    out, nrm = fve.moe_combine(dev(y), dev(pp), dev(w), dev(sh), dev(c), norm_out=True)
+    ref = oracle.combine(y, pp, w.astype(np.float64), sh, c)
+    assert_fp16_close(host(out), ref, "combine few rows", l2=1e-3, maxabs=4e-3)
+    assert_fp16_close(host(nrm), oracle.rms_norm(host(out)), "combine few rows norm", l2=1e-3,
+                      maxabs=4e-3)
+    # the same tokens first in a step of more than 8 rows: the extra tokens'
+    # rows follow, so the first T tokens' positions are unchanged
+    X = 8 // k + 1
+    y3 = np.concatenate([y, rng.standard_normal((X * k, H)).astype(np.float16)])
+    pp3 = np.concatenate([pp, n + rng.permutation(X * k).astype(np.int32)])
+    w3 = np.concatenate([w, rng.random((X, k)).astype(np.float32)])
+    sh3 = np.concatenate([sh, rng.standard_normal((X, H)).astype(np.float16)])
+    c3 = np.concatenate([c, rng.random(X).astype(np.float32)])
+    assert (T + X) * k > 8
+    out3 = fve.moe_combine(dev(y3), dev(pp3), dev(w3), dev(sh3), dev(c3))
+    assert np.array_equal(host(out3)[:T], host(out))
+
+
 # ----------------------------------------------------------- whole layer ----
 
 LAYER_CASES = [(synth.TINY, 4, "int4"), (synth.DS, 1, "int4"), (synth.DS, 16, "int4"),
