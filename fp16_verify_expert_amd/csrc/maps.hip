@@ -27,6 +27,20 @@ __global__ __launch_bounds__(smoe_maps::kGatherThreads) void gather_kernel(
                             n_active, err);
 }
 
+// At most kGatherThreads pairs: the ids are read once into LDS and sorted
+// with the per-thread counting sort (no loops over a wave's distinct ids).
+__global__ __launch_bounds__(smoe_maps::kGatherThreads) void gather_small_kernel(
+    const int32_t* __restrict__ ids, int n, int k, int E, int32_t* __restrict__ off,
+    int32_t* __restrict__ sorted_token, int32_t* __restrict__ sorted_pair,
+    int32_t* __restrict__ pair_pos, int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+    int32_t* __restrict__ err) {
+    __shared__ int32_t ids_s[smoe_maps::kGatherThreads];
+    if ((int)threadIdx.x < n) ids_s[threadIdx.x] = ids[threadIdx.x];
+    __syncthreads();
+    smoe_maps::small_maps(ids_s, n, k, E, nullptr, off, sorted_token, sorted_pair, pair_pos,
+                          active, n_active, err);
+}
+
 }  // namespace
 
 namespace smoe {
@@ -42,8 +56,12 @@ hipError_t launch_elb_count(const int32_t* ids, int n, int E, int layer, int32_t
 hipError_t launch_gather(const int32_t* ids, int n, int k, int E, int32_t* off, int32_t* st,
                          int32_t* sp, int32_t* pp, int32_t* active, int32_t* n_active,
                          int32_t* err, hipStream_t s) {
-    gather_kernel<<<dim3(1), dim3(smoe_maps::kGatherThreads), 0, s>>>(ids, n, k, E, off, st, sp,
-                                                                       pp, active, n_active, err);
+    if (n <= smoe_maps::kGatherThreads)
+        gather_small_kernel<<<dim3(1), dim3(smoe_maps::kGatherThreads), 0, s>>>(
+            ids, n, k, E, off, st, sp, pp, active, n_active, err);
+    else
+        gather_kernel<<<dim3(1), dim3(smoe_maps::kGatherThreads), 0, s>>>(
+            ids, n, k, E, off, st, sp, pp, active, n_active, err);
     return hipGetLastError();
 }
 }  // namespace smoe

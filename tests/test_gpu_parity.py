@@ -136,15 +136,17 @@ def test_elb_count_bad_ids_flagged():
 
 # ---------------------------------------------------------------- S3 ----
 
+# up to 1024 pairs the ids are sorted in LDS by one kernel, above by chunks
 GATHER_CASES = [(4, 2, 8), (1, 6, 64), (16, 6, 64), (17, 4, 60), (9, 4, 60), (17, 2, 16),
-                (300, 8, 64), (2000, 2, 16), (1, 1, 1), (5, 256, 256)]
+                (300, 8, 64), (2000, 2, 16), (1, 1, 1), (5, 256, 256), (128, 8, 64),
+                (512, 2, 16)]
 
 
 @pytest.mark.parametrize("T,k,E", GATHER_CASES)
 def test_gather_maps(T, k, E):
     rng = np.random.default_rng(T * 1000 + k * 10 + E)
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
-    if T == 2000:  # heavily skewed: most pairs on two experts
+    if T in (2000, 512):  # heavily skewed: most pairs on two experts
         ids[:, 0] = rng.integers(0, 2, size=T)
         ids[:, 1] = np.where(ids[:, 0] == 0, 1, 0)
     ref = oracle.gather_maps(ids, E)
