@@ -1,14 +1,14 @@
 """Draft chunk + verify over several MoE layers with offloaded target experts.
 
-"Specter: Fast MoE Inference via Quantization-Enabled Multi-Step Speculative
-Offloading" (AI summary), Key Contributions 3-4 and Methodology: while the INT4
-draft runs, GPU counters tally each layer's expert choices; at the chunk
-boundary their snapshot decides which FP16 target experts are placed in HBM;
-during verification the experts already resident are computed first while the
-missing ones are copied from pinned host memory on a dedicated stream, and the
-rest of the layer waits on an event.  "Specter previews expert routing with an
-INT4 copy of the model itself", What shipped: the draft runs entirely in GPU
-memory.
+Cited: "Specter: Fast MoE Inference via Quantization-Enabled Multi-Step
+Speculative Offloading" (AI summary), Key Contributions 3-4 and Methodology in
+Plain English; "Specter previews expert routing with an INT4 copy of the model
+itself", What shipped.  The INT4 draft lives wholly in device memory.  Each
+draft step adds its expert choices to a per-layer counter table on the GPU; a
+copy of that table taken when the chunk ends picks the FP16 target experts to
+place in HBM.  The verify then runs a layer's on-device experts first, while
+the others are copied from page-locked host memory on a separate stream, and
+the layer's remaining work waits on the copy's event.
 
 This module only sequences calls of the C ABI (routing, ELB counters, gather,
 W4A16 draft FFN, FP16 verify FFN with an expert mask, combine, expert staging)

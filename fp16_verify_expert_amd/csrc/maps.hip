@@ -1,10 +1,12 @@
 // Expert Lookahead Buffer counters and the stable gather-by-expert maps.
 //
-// "Specter: Fast MoE Inference via Quantization-Enabled Multi-Step Speculative
-// Offloading" (AI summary), Key Contributions 3 and Methodology: per-layer
-// GPU-side counters tally how often each expert is selected while drafting.
-// Key Contributions 4: the fused draft kernel gathers tokens by expert;
-// verification packs the tokens of one expert together.
+// Cited: "Specter: Fast MoE Inference via Quantization-Enabled Multi-Step
+// Speculative Offloading" (AI summary), Key Contributions 3-4 and Methodology
+// in Plain English.  The Expert Lookahead Buffer is an int32 table indexed by
+// (layer, expert) in device memory; every routing choice of a draft step adds
+// one to its entry.  The gather maps order a step's (token, slot) pairs by
+// expert, so both the draft and the verification FFN see each expert's rows
+// as one contiguous block.
 //
 // The device routines live in maps_core.h.
 #include "maps_core.h"

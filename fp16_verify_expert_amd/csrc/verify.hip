@@ -1,12 +1,13 @@
 // FP16 verification FFN over rows grouped by expert, on MFMA.
 //
-// "Specter: Fast MoE Inference via Quantization-Enabled Multi-Step Speculative
-// Offloading" (AI summary), Key Contributions 4 and Methodology: the K+1 tokens
-// routed to one expert are packed together so that the per-token
-// matrix-vector products become one matrix-matrix product per expert (same
-// result, the routing and masking being unchanged).  Key Contributions 3:
-// experts already resident are computed first while missing ones load, hence
-// the optional expert mask.
+// Cited: "Specter: Fast MoE Inference via Quantization-Enabled Multi-Step
+// Speculative Offloading" (AI summary), Key Contributions 3-4 and Methodology
+// in Plain English.  In verification each touched expert is evaluated once
+// over all of its rows, a matrix product per expert in place of a
+// matrix-vector product per (token, expert), with values equal to the
+// per-token evaluation.  The optional expert mask lets the caller run the
+// experts whose weights are already on the device while other experts'
+// weights are still being copied in.
 //
 // A workgroup owns 16 output columns of one touched expert; its waves split
 // the reduction and stream the weight rows of those columns, feeding

@@ -1,12 +1,13 @@
 // Draft routed-expert SwiGLU FFN over GPTQ INT4 (group 128) weights, one
 // launch per projection across every touched expert.
 //
-// "Specter: Fast MoE Inference via Quantization-Enabled Multi-Step Speculative
-// Offloading" (AI summary), Key Contributions 4: a fused multi-expert INT4
-// draft kernel that gathers tokens by expert and runs all experts in one
-// launch.  "Specter previews expert routing with an INT4 copy of the model
-// itself", What shipped: W4A16, i.e. INT4 weight tiles are dequantised while
-// the products are formed in higher precision; GPTQ, group size 128.
+// Cited: "Specter: Fast MoE Inference via Quantization-Enabled Multi-Step
+// Speculative Offloading" (AI summary), Key Contributions 4, and "Specter
+// previews expert routing with an INT4 copy of the model itself", What
+// shipped.  The draft's routed experts hold 4-bit GPTQ codes (group 128, fp16
+// scales); each projection of every touched expert runs in a single launch
+// over rows already grouped by expert, the codes being expanded to fp16 inside
+// the kernel and the products summed in fp32.
 //
 // At draft shapes (one to a few rows per expert) this is a weight-streaming
 // GEMV: every packed byte is read from HBM once, so the design is about bytes

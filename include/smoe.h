@@ -126,8 +126,9 @@ smoe_status moe_route_topk(const uint16_t* x, const uint16_t* w_router,
 
 /* ------------------------------------------------------------------------
  * elb_count -- Expert Lookahead Buffer update ([S1] Key Contributions 3 and
- * Methodology: GPU-resident, layer-indexed counters tallying how often each
- * expert is chosen while drafting; snapshots of them drive prefetch).
+ * Methodology in Plain English: a per-layer table of expert counts kept in
+ * device memory and bumped by each draft step's routing; copies of it taken
+ * at chunk boundaries decide what to prefetch).
  *
  *   topk_ids  int32 [T, k]
  *   counters  int32 [L, E]  in/out: counters[layer, e] += number of (t, j)
@@ -142,8 +143,8 @@ smoe_status elb_count(const int32_t* topk_ids, int T, int k, int E, int layer, i
 
 /* ------------------------------------------------------------------------
  * moe_gather -- group the T*k (token, slot) pairs by expert ([S1] Key
- * Contributions 4: the draft kernel gathers tokens by expert; Methodology:
- * verification packs the tokens of one expert together).  Pair p = t*k + j.
+ * Contributions 4 and Methodology: both the draft and the verification FFN
+ * process each expert's rows as one block).  Pair p = t*k + j.
  * Stable: inside one expert, rows follow increasing p.
  *
  *   expert_offsets int32 [E+1]  out: rows of expert e are [off[e], off[e+1])
@@ -315,8 +316,8 @@ smoe_status moe_draft_route_ffn(const uint16_t* x, const uint16_t* w_router,
  *                  or staging slots)
  *   expert_mask    optional uint8 [E]; experts with mask 0 are skipped, so
  *                  cache hits can run before misses arrive ([S1] Key
- *                  Contributions 3 and Methodology: experts already resident
- *                  are computed first while the missing ones load)
+ *                  Contributions 3 and Methodology: on-device experts run
+ *                  while the weights of the others are still being copied)
  *   rows           number of sorted rows (T*k for routed experts; T for a
  *                  shared expert run as one group with offsets {0, T})
  *   y_sorted       fp16 [rows, H] out

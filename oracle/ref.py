@@ -28,11 +28,22 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
                                      library stable argsort)
   dequant_gptq ..................... pinned (hand-packed closed forms, 2/4/8-bit
                                      codes)
-  expert_ffn / grouped_ffn ......... pinned (textbook dense MLP at E=1,
-                                     zero weights, masked brute force,
-                                     shared-expert concatenation identity)
+  expert_ffn_f16 ................... pinned (one-hot closed form with known
+                                     SiLU values, zero weights, textbook
+                                     dense MLP at E=1, shared-expert
+                                     concatenation identity)
+  expert_ffn_int4 .................. pinned (hand-packed one-hot closed form;
+                                     equals expert_ffn_f16 on weights placed
+                                     exactly on the quantisation grid)
+  grouped_ffn ...................... pinned (masked brute force; the grid
+                                     identity above through the loop)
+  moe_layer ........................ pinned (zero routed experts leave
+                                     sigmoid(x . w_sg) * shared expert, in
+                                     closed form; routed + gated shared
+                                     closed form; residual added once)
   per_token_ffn .................... pinned (equals grouped_ffn, the pages'
-                                     "mathematically identical" claim)
+                                     claim that grouping by expert
+                                     leaves the values unchanged)
   combine .......................... pinned (k=1 identity, hand sums)
   rms_norm ......................... pinned (constant rows, scale invariance)
 """
@@ -173,10 +184,10 @@ def route_topk(x: np.ndarray, w_router: np.ndarray, k: int, renormalize: bool = 
 def elb_update(counters: np.ndarray, ids: np.ndarray, layer: int) -> np.ndarray:
     """Add one to counters[layer, e] for every (token, slot) routed to e.
 
-    [S1 Key Contributions 3] the ELB is a set of GPU-resident activation
-    counters indexed by layer; [S1 Methodology] the counters tally how often
-    each expert of each layer is chosen while drafting, and snapshots of them
-    drive prefetch.  R6: one count per (token, selected expert), unweighted,
+    [S1 Key Contributions 3; Methodology in Plain English] the Expert
+    Lookahead Buffer keeps, per layer and expert, a count of draft routing
+    choices in device memory; copies taken at chunk boundaries drive
+    prefetch.  R6: one count per (token, selected expert), unweighted,
     accumulated across calls until the caller snapshots or clears it.
     Ids outside [0, E) are not counted.
     """
@@ -195,9 +206,8 @@ def elb_update(counters: np.ndarray, ids: np.ndarray, layer: int) -> np.ndarray:
 def gather_maps(ids: np.ndarray, E: int) -> Dict[str, np.ndarray]:
     """Stable grouping of the T*k (token, slot) pairs by expert.
 
-    [S1 Key Contributions 4] the draft kernel gathers tokens by expert;
-    [S1 Methodology] verification packs the tokens routed to one expert
-    together.  R7: pair p = t*k + j; pairs are ordered by expert and, inside
+    [S1 Key Contributions 4; Methodology] draft and verification both
+    process each expert's rows as one block.  R7: pair p = t*k + j; pairs are ordered by expert and, inside
     one expert, by increasing p (a stable counting sort).
 
     Returns offsets [E+1] (exclusive prefix sum of per-expert counts),
@@ -361,8 +371,8 @@ def per_token_ffn(x: np.ndarray, ids: np.ndarray, experts: Sequence, kind: str,
     """The unregrouped ordering: token by token, slot by slot, one
     vector-matrix product per (token, expert).  Returns [T, k, H].
 
-    [S1 Methodology] regrouping by expert is mathematically identical to
-    this ordering; the tests hold the two to each other.
+    [S1 Methodology] grouping rows by expert changes the evaluation order
+    only, not the values; the tests hold the two orderings to each other.
     """
     T, k = ids.shape
     H = x.shape[1]
