@@ -48,6 +48,8 @@ _SIGS = {
                             _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
     "w4a16_grouped_ffn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp,
                                _sz, _vp, _vp]),
+    "w4a16_grouped_ffn_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                       _vp, _vp, _vp]),
     "wq_grouped_ffn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
                             _sz, _vp, _vp]),
     "moe_draft_route_ffn": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp,
@@ -116,7 +118,8 @@ def workspace_bytes(which: int, T: int, k: int, H: int, I: int, E: int) -> int:
 
 def new_workspace(which: int, T: int, k: int, H: int, I: int, E: int,
                   device="cuda") -> torch.Tensor:
-    """Zero-filled workspace (the w4a16 counters must start at zero)."""
+    """Zero-filled workspace (the kernels need no initialisation; zeroed so
+    unused bytes are deterministic)."""
     n = max(256, workspace_bytes(which, T, k, H, I, E))
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
@@ -253,6 +256,23 @@ def w4a16_grouped_ffn(x, maps, table, T: int, k: int, H: int, I: int, E: int, wo
           _p(y_sorted), _p(workspace), workspace.numel() * workspace.element_size(),
           _p(err_word), _s(stream))
     return y_sorted
+
+
+def w4a16_grouped_ffn_noalloc(x, maps, table, T: int, k: int, H: int, I: int, E: int, *,
+                              y_sorted=None, err_word=None, stream=None):
+    """w4a16_grouped_ffn with the library's own scratch in place of a
+    workspace (allocates nothing inside the library; y_sorted is allocated
+    here only when not passed)."""
+    _check(x, torch.float16, "x")
+    if y_sorted is None:
+        y_sorted = torch.empty((max(T * k, 1), H), dtype=torch.float16, device=x.device)
+    _call("w4a16_grouped_ffn_noalloc", _p(x), _p(maps["sorted_token"]), _p(maps["offsets"]),
+          _p(maps["active"]), _p(maps["n_active"]), _p(table), T, k, H, I, E, 128,
+          _p(y_sorted), _p(err_word), _s(stream))
+    return y_sorted
+
+
+NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
 def wq_grouped_ffn(x, maps, table, T: int, k: int, H: int, I: int, E: int, workspace,

@@ -78,6 +78,68 @@ smoe_status check_hek(int H, int E, int k) {
 }
 
 constexpr long long kMaxPairs = 1 << 20;
+
+// Host checks shared by the grouped draft-FFN entry points (everything but
+// the workspace); `name` prefixes the error message.
+smoe_status check_wq(const char* name, const uint16_t* x, const int32_t* sorted_token,
+                     const int32_t* expert_offsets, const int32_t* active,
+                     const int32_t* n_active, const smoe_w4_expert* experts, int T, int k, int H,
+                     int I, int E, int bits, int group_size, const uint16_t* y_sorted) {
+    REQUIRE(x && sorted_token && expert_offsets && active && n_active && experts && y_sorted,
+            SMOE_ERR_NULL, "%s: a required pointer is NULL", name);
+    REQUIRE(T >= 0, SMOE_ERR_SHAPE, "%s: T=%d < 0", name, T);
+    REQUIRE(bits == 2 || bits == 4 || bits == 8, SMOE_ERR_UNSUPPORTED, "%s: bits=%d (2, 4 or 8)",
+            name, bits);
+    smoe_status st = check_hek(H, E, k);
+    if (st != SMOE_OK) return st;
+    REQUIRE(I > 0 && I % 128 == 0, SMOE_ERR_SHAPE, "%s: I=%d must be a positive multiple of 128",
+            name, I);
+    REQUIRE(group_size == 128, SMOE_ERR_UNSUPPORTED,
+            "%s: group_size=%d (only 128 is supported)", name, group_size);
+    REQUIRE((long long)T * k <= kMaxPairs, SMOE_ERR_SHAPE, "%s: T*k exceeds 2^20", name);
+    REQUIRE(smoe::w4a16_shape_supported(H, I), SMOE_ERR_SHAPE,
+            "%s: H=%d, I=%d (each must be <= 16384)", name, H, I);
+    REQUIRE(aligned(x, 16), SMOE_ERR_SHAPE, "%s: x must be 16-byte aligned", name);
+    return SMOE_OK;
+}
+
+// Rewrites the thread's error message so it names `to` instead of `from`
+// (entry points that forward to another one report under their own name).
+void rename_error(const char* from, const char* to) {
+    const size_t n = strlen(from);
+    if (g_err.compare(0, n, from) == 0) g_err = std::string(to) + g_err.substr(n);
+}
+
+// Scratch memory of w4a16_grouped_ffn_noalloc: a file-scope device array, so
+// the call needs no allocation.  Each GPU the library runs on holds its own
+// copy, at its own address, until the process ends.  Host code never passes
+// the array's name to a kernel (on the host it is only a stand-in for the
+// symbol); it passes the device address looked up once per device below.
+constexpr size_t kNoAllocScratch = SMOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratch];
+
+// Device address of `scratch` on the current device, looked up with
+// hipGetSymbolAddress on the first call made with that device current.
+smoe_status scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SMOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 256) return fail(SMOE_ERR_UNSUPPORTED, "device index %d", dev);
+    static std::mutex mu;
+    static void* addr[256];
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(SMOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return SMOE_OK;
+}
+
 // one-row matrix-vector reductions of a shared expert: 16 chunks of 16 bytes
 // per lane and row
 constexpr int kSharedMaxK = 8192;
@@ -205,21 +267,9 @@ smoe_status wq_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
                            int H, int I, int E, int bits, int group_size, uint16_t* y_sorted,
                            void* workspace, size_t workspace_bytes, int32_t* err_word,
                            void* stream) {
-    REQUIRE(x && sorted_token && expert_offsets && active && n_active && experts && y_sorted,
-            SMOE_ERR_NULL, "wq_grouped_ffn: a required pointer is NULL");
-    REQUIRE(T >= 0, SMOE_ERR_SHAPE, "wq_grouped_ffn: T=%d < 0", T);
-    REQUIRE(bits == 2 || bits == 4 || bits == 8, SMOE_ERR_UNSUPPORTED,
-            "wq_grouped_ffn: bits=%d (2, 4 or 8)", bits);
-    smoe_status st = check_hek(H, E, k);
+    smoe_status st = check_wq("wq_grouped_ffn", x, sorted_token, expert_offsets, active,
+                              n_active, experts, T, k, H, I, E, bits, group_size, y_sorted);
     if (st != SMOE_OK) return st;
-    REQUIRE(I > 0 && I % 128 == 0, SMOE_ERR_SHAPE,
-            "wq_grouped_ffn: I=%d must be a positive multiple of 128", I);
-    REQUIRE(group_size == 128, SMOE_ERR_UNSUPPORTED,
-            "wq_grouped_ffn: group_size=%d (only 128 is supported)", group_size);
-    REQUIRE((long long)T * k <= kMaxPairs, SMOE_ERR_SHAPE, "wq_grouped_ffn: T*k exceeds 2^20");
-    REQUIRE(smoe::w4a16_shape_supported(H, I), SMOE_ERR_SHAPE,
-            "wq_grouped_ffn: H=%d, I=%d (each must be <= 16384)", H, I);
-    REQUIRE(aligned(x, 16), SMOE_ERR_SHAPE, "wq_grouped_ffn: x must be 16-byte aligned");
     if (T == 0) return ok();
     const size_t need = smoe::w4a16_workspace_bytes(T, k, H, I, E);
     REQUIRE(workspace && workspace_bytes >= need && aligned(workspace, 256), SMOE_ERR_WORKSPACE,
@@ -241,14 +291,32 @@ smoe_status w4a16_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
     const smoe_status st = wq_grouped_ffn(x, sorted_token, expert_offsets, active, n_active,
                                           experts, T, k, H, I, E, 4, group_size, y_sorted,
                                           workspace, workspace_bytes, err_word, stream);
-    if (st != SMOE_OK) {
-        // report under this entry point's name
-        std::string m = g_err;
-        const std::string from = "wq_grouped_ffn";
-        if (m.compare(0, from.size(), from) == 0) m = "w4a16_grouped_ffn" + m.substr(from.size());
-        g_err = m;
-    }
+    if (st != SMOE_OK) rename_error("wq_grouped_ffn", "w4a16_grouped_ffn");
     return st;
+}
+
+smoe_status w4a16_grouped_ffn_noalloc(const uint16_t* x, const int32_t* sorted_token,
+                                      const int32_t* expert_offsets, const int32_t* active,
+                                      const int32_t* n_active, const smoe_w4_expert* experts,
+                                      int T, int k, int H, int I, int E, int group_size,
+                                      uint16_t* y_sorted, int32_t* err_word, void* stream) {
+    const char* name = "w4a16_grouped_ffn_noalloc";
+    smoe_status st = check_wq(name, x, sorted_token, expert_offsets, active, n_active, experts,
+                              T, k, H, I, E, 4, group_size, y_sorted);
+    if (st != SMOE_OK) return st;
+    if (T == 0) return ok();
+    const size_t need = smoe::w4a16_workspace_bytes(T, k, H, I, E);
+    REQUIRE(need <= kNoAllocScratch, SMOE_ERR_SHAPE,
+            "%s: T=%d, k=%d, I=%d needs %zu bytes of scratch; the library holds %zu (use "
+            "w4a16_grouped_ffn with a workspace)", name, T, k, I, need, kNoAllocScratch);
+    CHECK_DEVICE();
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != SMOE_OK) return st;
+    return hip_result(smoe::launch_w4a16_ffn(x, sorted_token, expert_offsets, active, n_active,
+                                             experts, T, k, H, I, E, 4, y_sorted, ws, err_word,
+                                             static_cast<hipStream_t>(stream)),
+                      "w4a16_grouped_ffn_noalloc launch");
 }
 
 smoe_status moe_draft_route_ffn(const uint16_t* x, const uint16_t* w_router,

@@ -228,6 +228,33 @@ smoe_status w4a16_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
                               void* stream);
 
 /* ------------------------------------------------------------------------
+ * w4a16_grouped_ffn_noalloc -- w4a16_grouped_ffn without a workspace
+ * argument, for callers that cannot allocate device memory around the call
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The workspace lives in a scratch array that the library
+ * holds in device memory, SMOE_NOALLOC_SCRATCH_BYTES on each GPU it runs on,
+ * from the library's load until the process ends.  The call allocates and
+ * frees nothing.
+ *
+ * Arguments, outputs and errors are those of w4a16_grouped_ffn (same kernels,
+ * bit-identical results), without workspace / workspace_bytes.  A request
+ * whose workspace, smoe_workspace_bytes(0, T, k, H, I, E), exceeds
+ * SMOE_NOALLOC_SCRATCH_BYTES returns SMOE_ERR_SHAPE before anything is
+ * enqueued (h takes T*k*I*2 bytes: e.g. T*k <= 256 rows at I = 6400).
+ * Every call on one GPU shares that GPU's scratch: calls whose executions
+ * overlap on one GPU (on different streams, or from different threads)
+ * race; calls on one stream are ordered and safe.  The scratch keeps the
+ * last call's contents; the kernels need no initialised scratch.
+ * ---------------------------------------------------------------------- */
+#define SMOE_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+
+smoe_status w4a16_grouped_ffn_noalloc(const uint16_t* x, const int32_t* sorted_token,
+                                      const int32_t* expert_offsets, const int32_t* active,
+                                      const int32_t* n_active, const smoe_w4_expert* experts,
+                                      int T, int k, int H, int I, int E, int group_size,
+                                      uint16_t* y_sorted, int32_t* err_word, void* stream);
+
+/* ------------------------------------------------------------------------
  * wq_grouped_ffn -- w4a16_grouped_ffn for other draft code widths ([S1] Main
  * Findings and Future Directions: the draft's fidelity is compared across
  * quantisation precisions, 2-, 4- and 8-bit, and the precision is a design

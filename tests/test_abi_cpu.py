@@ -19,7 +19,7 @@ def test_exports_every_header_function():
     names = fve.header_functions()
     expected = {"smoe_abi_version", "smoe_last_error", "moe_route_topk", "elb_count",
                 "moe_gather", "moe_route_plan", "w4a16_grouped_ffn", "wq_grouped_ffn",
-                "moe_draft_route_ffn",
+                "moe_draft_route_ffn", "w4a16_grouped_ffn_noalloc",
                 "verify_grouped_gemm", "moe_combine",
                 "expert_stage_async", "smoe_workspace_bytes"}
     assert set(names) == expected
@@ -189,6 +189,30 @@ def test_w4a16_validation():
     assert L.w4a16_grouped_ffn(*args[:5], None, 4, 2, 256, 512, 8, 128, FAKE, FAKE, need, None,
                                None) == 1
     assert L.w4a16_grouped_ffn(*args, 0, 2, 256, 512, 8, 128, FAKE, None, 0, None, None) == 0
+
+
+def test_w4a16_noalloc_validation():
+    """Host checks of the allocation-free variant; none reaches a device."""
+    L = fve.lib()
+    args = [FAKE] * 6
+    # h alone needs T*k*I*2 bytes: 600 rows at I = 6400 exceed the 4 MiB scratch
+    assert L.w4a16_grouped_ffn_noalloc(*args, 300, 2, 4096, 6400, 16, 128, FAKE, None,
+                                       None) == 2
+    msg = _err()
+    assert msg.startswith("w4a16_grouped_ffn_noalloc") and "scratch" in msg
+    assert fve.NOALLOC_SCRATCH_BYTES == 4 << 20
+    # 256 rows at I = 6400 fit (the limit the header names); 330 rows do not
+    assert L.smoe_workspace_bytes(0, 256, 1, 4096, 6400, 16) <= fve.NOALLOC_SCRATCH_BYTES
+    assert L.smoe_workspace_bytes(0, 330, 1, 4096, 6400, 16) > fve.NOALLOC_SCRATCH_BYTES
+    # the checks of w4a16_grouped_ffn, reported under this entry point's name
+    assert L.w4a16_grouped_ffn_noalloc(*args, 1, 2, 256, 512, 8, 64, FAKE, None, None) == 3
+    assert _err().startswith("w4a16_grouped_ffn_noalloc") and "group_size" in _err()
+    assert L.w4a16_grouped_ffn_noalloc(*args, 1, 2, 256, 500, 8, 128, FAKE, None, None) == 2
+    assert L.w4a16_grouped_ffn_noalloc(*args[:5], None, 4, 2, 256, 512, 8, 128, FAKE, None,
+                                       None) == 1
+    assert L.w4a16_grouped_ffn_noalloc(*args, 4, 2, 256, 512, 8, 128, None, None, None) == 1
+    assert L.w4a16_grouped_ffn_noalloc(*args, -1, 2, 256, 512, 8, 128, FAKE, None, None) == 2
+    assert L.w4a16_grouped_ffn_noalloc(*args, 0, 2, 256, 512, 8, 128, FAKE, None, None) == 0
 
 
 def test_verify_validation():
