@@ -700,7 +700,7 @@ def bench_route_fidelity(args):
 
     import fp16_verify_expert_amd as fve
     import synth
-    from fp16_verify_expert_amd.chunk import ChunkEngine
+    from fp16_verify_expert_amd.chunk import ChunkEngine, distinct_experts, topk_agreement
 
     fve.lib()
     torch.cuda.set_device(0)
@@ -721,15 +721,10 @@ def bench_route_fidelity(args):
         eng.forward(x, "f16", full, record=rt)
         torch.cuda.synchronize()
         assert int(eng.err.item()) == 0, "device error word set"
-        d = torch.stack(rd).cpu().numpy()     # [L, N, k]
-        t = torch.stack(rt).cpu().numpy()
-        match = np.array([[len(set(d[l, i]) & set(t[l, i])) / s.k for i in range(N)]
-                          for l in range(L)])
-        distinct = {}
-        for K in depths:
-            nw = N // K
-            c = [[len(np.unique(t[l, w * K:(w + 1) * K])) for w in range(nw)] for l in range(L)]
-            distinct[K] = float(np.mean(c))
+        d = torch.stack([r["ids"] for r in rd]).cpu().numpy()     # [L, N, k]
+        t = torch.stack([r["ids"] for r in rt]).cpu().numpy()
+        match = topk_agreement(d, t)
+        distinct = distinct_experts(t, depths)
         per_rho[str(rho)] = {
             "topk_match_mean": round(float(match.mean()), 4),
             "topk_match_per_layer": [round(float(v), 3) for v in match.mean(axis=1)],

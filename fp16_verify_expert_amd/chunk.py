@@ -44,10 +44,68 @@ class ChunkLayer:
     shared_gate: Optional[torch.Tensor] = None   # fp16 [H] cuda
 
 
+class _StepBuffers:
+    """Device buffers of one row count T, allocated once and reused by every
+    layer and call: routing outputs, gather maps, expert outputs, the logits
+    workspace of the routing plan, both FFN workspaces, the shared expert's
+    output and workspace, and two ping-pong pairs for a layer's output and
+    its normalised copy (the next layer's input)."""
+
+    def __init__(self, T: int, H: int, E: int, k: int, I: int, Is: int, dev):
+        i32, f32, f16 = torch.int32, torch.float32, torch.float16
+        self.ids = torch.empty((T, k), dtype=i32, device=dev)
+        self.w = torch.empty((T, k), dtype=f32, device=dev)
+        self.gate = torch.empty((T,), dtype=f32, device=dev)
+        n = max(T * k, 1)
+        self.maps = dict(offsets=torch.empty(E + 1, dtype=i32, device=dev),
+                         sorted_token=torch.empty(n, dtype=i32, device=dev),
+                         sorted_pair=torch.empty(n, dtype=i32, device=dev),
+                         pair_pos=torch.empty(n, dtype=i32, device=dev),
+                         active=torch.empty(E, dtype=i32, device=dev),
+                         n_active=torch.empty(1, dtype=i32, device=dev))
+        self.y = torch.empty((n, H), dtype=f16, device=dev)
+        self.lg = torch.empty(max(1, T * (E + 1)), dtype=f32, device=dev)
+        self.ws_w4 = new_workspace(0, T, k, H, I, E, device=dev)
+        self.ws_f16 = new_workspace(1, T, k, H, I, E, device=dev)
+        self.sh_out = torch.empty((T, H), dtype=f16, device=dev) if Is else None
+        self.ws_sh = new_workspace(1, T, 1, H, Is, 1, device=dev) if Is else None
+        self.iota = torch.arange(T, dtype=i32, device=dev)
+        self.offs = torch.tensor([0, T], dtype=i32, device=dev)
+        self.out = [torch.empty((T, H), dtype=f16, device=dev) for _ in range(2)]
+        self.xn = [torch.empty((T, H), dtype=f16, device=dev) for _ in range(2)]
+
+
 def top_resident(counts: np.ndarray, n: int) -> List[int]:
     """The n experts with the largest ELB counts, ties to the lower id."""
     order = np.lexsort((np.arange(counts.shape[0]), -counts.astype(np.int64)))
     return sorted(int(e) for e in order[:n])
+
+
+def topk_agreement(draft_ids: np.ndarray, target_ids: np.ndarray) -> np.ndarray:
+    """|draft ids & target ids| / k for every (layer, token) of two [L, N, k]
+    id arrays: the draft/target routing agreement of [S1] Key Contributions
+    1 and Main Findings (an INT4 copy keeps the experts its target chooses)."""
+    L, N, k = target_ids.shape
+    out = np.empty((L, N))
+    for l in range(L):
+        for t in range(N):
+            out[l, t] = len(set(draft_ids[l, t].tolist()) & set(target_ids[l, t].tolist())) / k
+    return out
+
+
+def distinct_experts(ids: np.ndarray, depths: Sequence[int]) -> Dict[int, float]:
+    """For each depth K, the mean over layers and non-overlapping windows of
+    K consecutive tokens of the number of distinct experts a window routes
+    to, from [L, N, k] ids: the demand a K-token speculation puts on one
+    layer ([S1] Main Findings: distinct experts per layer grow with the
+    depth)."""
+    L, N, _ = ids.shape
+    out = {}
+    for K in depths:
+        counts = [len(np.unique(ids[l, w * K:(w + 1) * K])) for l in range(L)
+                  for w in range(N // K)]
+        out[K] = float(np.mean(counts))
+    return out
 
 
 class ChunkEngine:
@@ -86,31 +144,53 @@ class ChunkEngine:
         self.h_mask = torch.zeros((self.L, 2, E), dtype=torch.uint8).pin_memory()
         self.d_table = torch.zeros((self.L, E, 2), dtype=torch.int64, device=dev)
         self.d_mask = torch.zeros((self.L, 2, E), dtype=torch.uint8, device=dev)
-        self.ws_d = new_workspace(0, 1, k, H, I, E, device=dev)
-        self.ws_v = new_workspace(1, verify_T, k, H, I, E, device=dev)
-        self.ws_sh = {T: new_workspace(1, T, 1, H, shared_I, 1, device=dev)
-                      for T in (1, verify_T)} if shared_I else {}
-        self.sh_out = {T: torch.empty((T, H), dtype=torch.float16, device=dev)
-                       for T in (1, verify_T)} if shared_I else {}
+        # per row count, buffers reused by every layer and call (the draft
+        # step's T = 1 and the verify's T are made here, others on first use)
+        self._buf: Dict[int, _StepBuffers] = {}
+        for T in (1, verify_T):
+            self.bufs(T)
         # the draft step's shared expert rides in the routed launches: its h
         # between the projections
         self.sh_h = torch.empty((max(shared_I, 1),), dtype=torch.float16, device=dev)
-        self.iota = torch.arange(max(verify_T, 1), dtype=torch.int32, device=dev)
-        self.offs = {T: torch.tensor([0, T], dtype=torch.int32, device=dev) for T in (1, verify_T)}
         self.stats = dict(staged_experts=0, staged_bytes=0, hit_experts=0, miss_experts=0)
+
+    def bufs(self, T: int) -> _StepBuffers:
+        """The reusable buffers of row count T (allocated on first use)."""
+        b = self._buf.get(T)
+        if b is None:
+            b = _StepBuffers(T, self.H, self.E, self.k, self.I, self.Is, self.dev)
+            self._buf[T] = b
+        return b
+
+    def _combine(self, l: int, b: _StepBuffers, y, sh, gate, x, fresh: bool):
+        """moe_combine of layer l with the residual x and the next layer's
+        normalised input.  The outputs go to b's ping-pong buffers, or to new
+        tensors when `fresh` (recorded layers, and the last layer, whose
+        output the caller keeps)."""
+        last = l == self.L - 1
+        out = None if (fresh or last) else b.out[l % 2]
+        xn = True if fresh else b.xn[l % 2]
+        return moe_combine(y, b.maps["pair_pos"], b.w, sh, gate, x, out=out, norm_out=xn)
 
     # ------------------------------------------------------------- draft ----
     def _shared(self, l: int, x: torch.Tensor):
         if self.tsh[l] is None:
             return None
         T = x.shape[0]
-        return verify_grouped_gemm(x, self.iota[:T], self.offs[T], self.tsh[l], T, T, self.H,
-                                   self.Is, 1, self.ws_sh[T], y_sorted=self.sh_out[T],
-                                   err_word=self.err)
+        b = self.bufs(T)
+        return verify_grouped_gemm(x, b.iota, b.offs, self.tsh[l], T, T, self.H, self.Is, 1,
+                                   b.ws_sh, y_sorted=b.sh_out, err_word=self.err)
+
+    @staticmethod
+    def _record(record, l, x, xn, ids, out, xn_next) -> None:
+        if record is not None:
+            record.append(dict(layer=l, x=x, xn=xn, ids=ids.clone(), out=out, xn_next=xn_next))
 
     def draft_step(self, x: torch.Tensor, record: Optional[list] = None) -> torch.Tensor:
         """One INT4 draft decode step (T = 1) through all layers, counting each
         layer's expert choices in the ELB table."""
+        b = self.bufs(1)
+        fresh = record is not None
         xn = x
         for l, ly in enumerate(self.layers):
             # routing, ELB update and gather maps folded into the gate/up
@@ -118,15 +198,17 @@ class ChunkEngine:
             # columns in the same two launches (measured: as two launches of
             # its own on a side stream it overlapped nothing, 15.6 us of a
             # 39.5 us layer-step)
-            res = moe_draft_route_ffn(xn, ly.router, self.k, self.t4[l], self.I, self.ws_d, False,
+            has_sh = ly.shared is not None
+            res = moe_draft_route_ffn(xn, ly.router, self.k, self.t4[l], self.I, b.ws_w4, False,
                                       ly.shared_gate, counters=self.counters, layer=l,
-                                      err_word=self.err, shared=ly.shared, shared_h=self.sh_h,
-                                      shared_out=self.sh_out[1] if ly.shared is not None else None)
-            ids, w, gate, maps, y = res[:5]
-            sh = res[5] if ly.shared is not None else None
-            out, xn_next = moe_combine(y, maps["pair_pos"], w, sh, gate, x, norm_out=True)
-            if record is not None:
-                record.append(dict(layer=l, x=x, xn=xn, ids=ids, out=out, xn_next=xn_next))
+                                      err_word=self.err, topk_ids=b.ids, topk_w=b.w,
+                                      shared_gate=b.gate if ly.shared_gate is not None else None,
+                                      maps=b.maps, y_sorted=b.y, shared=ly.shared,
+                                      shared_h=self.sh_h, shared_out=b.sh_out if has_sh else None)
+            gate = res[2]
+            sh = res[5] if has_sh else None
+            out, xn_next = self._combine(l, b, b.y, sh, gate, x, fresh)
+            self._record(record, l, x, xn, b.ids, out, xn_next)
             x, xn = out, xn_next
         return x
 
@@ -165,39 +247,31 @@ class ChunkEngine:
                 record: Optional[list] = None) -> torch.Tensor:
         """All layers over T rows with every expert in HBM: kind "int4" runs
         the draft's W4A16 experts, kind "f16" the target's FP16 experts read
-        from `full` ([L, E, 3HI]).  No ELB update, no staging.  Each layer's
-        ids are appended to `record` ([T, k] int32 tensors)."""
+        from `full` ([L, E, 3HI]).  No ELB update, no staging.  `record`
+        receives one dict per layer (layer, x, xn, ids [T, k], out,
+        xn_next)."""
         T = x.shape[0]
-        ws = new_workspace(0 if kind == "int4" else 1, T, self.k, self.H, self.I, self.E,
-                           device=self.dev)
+        b = self.bufs(T)
+        fresh = record is not None
         xn = x
         for l, ly in enumerate(self.layers):
-            ids, w, gate = moe_route_topk(xn, ly.router, self.k, False, ly.shared_gate)
-            maps = moe_gather(ids, self.E, self.err)
-            sh = None
-            if self.tsh[l] is not None:
-                wsh = new_workspace(1, T, 1, self.H, self.Is, 1, device=self.dev)
-                sh = verify_grouped_gemm(xn, self.iota_n(T), self.offs_n(T), self.tsh[l], T, T,
-                                         self.H, self.Is, 1, wsh, err_word=self.err)
+            _, _, gate = moe_route_topk(xn, ly.router, self.k, False, ly.shared_gate,
+                                        topk_ids=b.ids, topk_w=b.w,
+                                        shared_gate=b.gate if ly.shared_gate is not None else None)
+            moe_gather(b.ids, self.E, self.err, out=b.maps)
+            sh = self._shared(l, xn)
             if kind == "int4":
-                y = w4a16_grouped_ffn(xn, maps, self.t4[l], T, self.k, self.H, self.I, self.E, ws,
-                                      err_word=self.err)
+                w4a16_grouped_ffn(xn, b.maps, self.t4[l], T, self.k, self.H, self.I, self.E,
+                                  b.ws_w4, y_sorted=b.y, err_word=self.err)
             else:
-                y = verify_grouped_gemm(xn, maps["sorted_token"], maps["offsets"],
-                                        self._resident_table(full, l), T, T * self.k, self.H,
-                                        self.I, self.E, ws, active=maps["active"],
-                                        n_active=maps["n_active"], err_word=self.err)
-            out, xn_next = moe_combine(y, maps["pair_pos"], w, sh, gate, x, norm_out=True)
-            if record is not None:
-                record.append(ids)
+                verify_grouped_gemm(xn, b.maps["sorted_token"], b.maps["offsets"],
+                                    self._resident_table(full, l), T, T * self.k, self.H, self.I,
+                                    self.E, b.ws_f16, active=b.maps["active"],
+                                    n_active=b.maps["n_active"], y_sorted=b.y, err_word=self.err)
+            out, xn_next = self._combine(l, b, b.y, sh, gate, x, fresh)
+            self._record(record, l, x, xn, b.ids, out, xn_next)
             x, xn = out, xn_next
         return x
-
-    def iota_n(self, T: int) -> torch.Tensor:
-        return torch.arange(T, dtype=torch.int32, device=self.dev)
-
-    def offs_n(self, T: int) -> torch.Tensor:
-        return torch.tensor([0, T], dtype=torch.int32, device=self.dev)
 
     def snapshot(self) -> np.ndarray:
         """Copy of the ELB table (synchronises)."""
@@ -258,7 +332,7 @@ class ChunkEngine:
 
     def run_round(self, xs: Sequence[torch.Tensor], xv: torch.Tensor, planner: bool = True,
                   chunk0: int = 2, step_s: float = 1.3e-3, h2d_gbps: float = 55.0,
-                  timing: Optional[dict] = None) -> torch.Tensor:
+                  timing: Optional[dict] = None, record: Optional[dict] = None) -> torch.Tensor:
         """One speculation round: len(xs) INT4 draft steps (graph-replayed;
         capture_draft first), then the FP16 verify of xv.
 
@@ -272,36 +346,58 @@ class ChunkEngine:
         prefetches and misses are staged behind them.  Residency carries over
         from round to round.  planner=False: draft every step, snapshot,
         place the top experts of every layer, then verify (all copies exposed).
-        `timing` (dict) receives HIP events: start, drafted, end."""
+        `timing` (dict) receives HIP events: start, drafted, end.
+        `record` (dict) receives the draft steps' per-layer records under
+        "draft" (the steps then run eagerly, which is bit-identical to the
+        graph replays), every ELB snapshot the round acted on under
+        "snapshots" as (draft steps done, [L, E] counts), and the verify's
+        per-layer records under "verify"."""
         main = torch.cuda.current_stream()
         ev = {k: torch.cuda.Event(enable_timing=True) for k in ("start", "drafted", "end")}
         self.clear_counters()
         ev["start"].record(main)
         steps = len(xs)
+        draft = self.draft_step_graph
+        snaps = None
+        if record is not None:
+            rec_d = record.setdefault("draft", [])
+            snaps = record.setdefault("snapshots", [])
+            draft = lambda x: self.draft_step(x, rec_d)
         if not planner:
             for x in xs:
-                self.draft_step_graph(x)
+                draft(x)
             ev["drafted"].record(main)
-            self.place_residents(self.snapshot())
+            counts = self.snapshot()
+            if snaps is not None:
+                snaps.append((steps, counts))
+            self.place_residents(counts)
         else:
             # pools may be rewritten only once the previous round's verify read them
             self.copy.wait_event(self.ev_round_done)
             done, c, pending, k = 0, max(1, chunk0), None, 0
+            pending_done = 0
+
+            def read(i, n_done):
+                counts = self._snapshot_read(i)
+                if snaps is not None:
+                    snaps.append((n_done, counts))
+                return counts
+
             while done < steps:
                 n = min(c, steps - done)
                 for st in range(done, done + n):
-                    self.draft_step_graph(xs[st])
+                    draft(xs[st])
                 done += n
                 self._snapshot_async(k % 2)
                 if pending is not None:
-                    nload = self.prefetch(self._snapshot_read(pending))
+                    nload = self.prefetch(read(pending, pending_done))
                     t_copy = nload * self.ebytes / (h2d_gbps * 1e9)
                     c = max(1, int(round(t_copy / step_s)))
-                pending = k % 2
+                pending, pending_done = k % 2, done
                 k += 1
             ev["drafted"].record(main)
-            self.prefetch(self._snapshot_read(pending))
-        out = self.verify(xv)
+            self.prefetch(read(pending, pending_done))
+        out = self.verify(xv, None if record is None else record.setdefault("verify", []))
         self.ev_round_done.record(main)
         ev["end"].record(main)
         if timing is not None:
@@ -317,36 +413,39 @@ class ChunkEngine:
         from there instead (the reference for residency invariance)."""
         main = torch.cuda.current_stream()
         T = x.shape[0]
+        b = self.bufs(T)
+        fresh = record is not None
         xn = x
         # routing and maps in one plan (no ELB update: verification does not
-        # tally draft choices) while it fits one workgroup's limits
+        # count draft choices) while it fits one workgroup's limits
         plan = T * self.k <= 1024 and T * (self.E + 1) <= 4096
-        lg = torch.empty(max(1, T * (self.E + 1)), dtype=torch.float32, device=self.dev)
         for l, ly in enumerate(self.layers):
+            g_out = b.gate if ly.shared_gate is not None else None
             if plan:
-                ids, w, gate, maps = moe_route_plan(xn, ly.router, self.k, False, ly.shared_gate,
-                                                    err_word=self.err, logits_ws=lg)
+                _, _, gate, _ = moe_route_plan(xn, ly.router, self.k, False, ly.shared_gate,
+                                               err_word=self.err, topk_ids=b.ids, topk_w=b.w,
+                                               shared_gate=g_out, maps=b.maps, logits_ws=b.lg)
             else:
-                ids, w, gate = moe_route_topk(xn, ly.router, self.k, False, ly.shared_gate)
-                maps = moe_gather(ids, self.E, self.err)
+                _, _, gate = moe_route_topk(xn, ly.router, self.k, False, ly.shared_gate,
+                                            topk_ids=b.ids, topk_w=b.w, shared_gate=g_out)
+                moe_gather(b.ids, self.E, self.err, out=b.maps)
+            maps = b.maps
             # the shared expert in line on the caller's stream: on a side
             # stream beside the routed experts the 17-token verify was slower
             # (4.25 against 4.17 ms over 24 layers; a cross-stream join costs
             # about 6 us and the concurrent launches slow each other)
             sh = self._shared(l, xn)
             rows = T * self.k
-            y = torch.empty((rows, self.H), dtype=torch.float16, device=self.dev)
             if all_resident is not None:
                 verify_grouped_gemm(xn, maps["sorted_token"], maps["offsets"],
                                     self._resident_table(all_resident, l),
-                                    T, rows, self.H, self.I, self.E, self.ws_v,
+                                    T, rows, self.H, self.I, self.E, b.ws_f16,
                                     active=maps["active"], n_active=maps["n_active"],
-                                    y_sorted=y, err_word=self.err)
+                                    y_sorted=b.y, err_word=self.err)
             else:
-                self._verify_staged(l, xn, maps, y, main)
-            out, xn_next = moe_combine(y, maps["pair_pos"], w, sh, gate, x, norm_out=True)
-            if record is not None:
-                record.append(dict(layer=l, x=x, xn=xn, ids=ids, out=out, xn_next=xn_next))
+                self._verify_staged(l, xn, maps, b.y, b.ws_f16, main)
+            out, xn_next = self._combine(l, b, b.y, sh, gate, x, fresh)
+            self._record(record, l, x, xn, b.ids, out, xn_next)
             x, xn = out, xn_next
         return x
 
@@ -367,7 +466,7 @@ class ChunkEngine:
             self._full_key = key
         return self._full_tab[l]
 
-    def _verify_staged(self, l, x, maps, y, main) -> None:
+    def _verify_staged(self, l, x, maps, y, ws, main) -> None:
         T = x.shape[0]
         rows = T * self.k
         act = maps["active"].cpu().numpy()          # the target router's decisions
@@ -402,12 +501,12 @@ class ChunkEngine:
         if hits:
             main.wait_event(self.ev_layer[l])  # this layer's prefetches (if any) have landed
             verify_grouped_gemm(x, maps["sorted_token"], maps["offsets"], self.d_table[l], T, rows,
-                                self.H, self.I, self.E, self.ws_v, expert_mask=self.d_mask[l, 0],
+                                self.H, self.I, self.E, ws, expert_mask=self.d_mask[l, 0],
                                 **kw)
         if misses:
             main.wait_event(self.ev_staged[b])
             verify_grouped_gemm(x, maps["sorted_token"], maps["offsets"], self.d_table[l], T, rows,
-                                self.H, self.I, self.E, self.ws_v, expert_mask=self.d_mask[l, 1],
+                                self.H, self.I, self.E, ws, expert_mask=self.d_mask[l, 1],
                                 **kw)
             self.ev_free[b].record(main)
         self.stats["hit_experts"] += len(hits)

@@ -132,3 +132,49 @@ def run_layer(L: Layer, x: torch.Tensor, kind: str, err: Optional[torch.Tensor] 
         sh = fve.verify_grouped_gemm(x, iota, offs, L.tsh, T, T, s.H, Is, 1, wsh, err_word=err)
     out = fve.moe_combine(y, maps["pair_pos"], w, sh, gate, x if residual else None)
     return dict(ids=ids, w=w, gate=gate, maps=maps, y=y, shared=sh, out=out)
+
+
+def qwen_chunk_layers(L: int, dev) -> tuple:
+    """L Qwen-shaped chunk layers generated on the device (torch Philox
+    streams of the input recipe): ChunkLayer list, each with its FP16 target
+    experts in page-locked host memory as [E, 3HI] (w13 [2I, H] then
+    w2 [H, I]), and the same experts in HBM as [L, E, 3HI]."""
+    from fp16_verify_expert_amd.chunk import ChunkLayer
+    s = synth.QWEN_CHUNK
+    full = torch.empty((L, s.E, 3 * s.H * s.I), dtype=torch.float16, device=dev)
+    layers = []
+    for l in range(L):
+        g = synth.torch_layer(s, l, dev)
+        for e, (w13, w2) in enumerate(g["f16"]):
+            full[l, e, :2 * s.I * s.H].copy_(w13.reshape(-1))
+            full[l, e, 2 * s.I * s.H:].copy_(w2.reshape(-1))
+        del g["f16"]
+        host_f16 = torch.empty((s.E, 3 * s.H * s.I), dtype=torch.float16, pin_memory=True)
+        host_f16.copy_(full[l])
+        layers.append(ChunkLayer(router=g["router"], int4=g["int4"], host_f16=host_f16,
+                                 shared=(g["shared"]["w13"], g["shared"]["w2"]),
+                                 shared_gate=g["shared"]["gate"]))
+        if l % 6 == 5:
+            say(f"  generated {l + 1}/{L} layers")
+    torch.cuda.synchronize()
+    return layers, full
+
+
+def chunk_layer_np(layer, experts: Sequence[int], kind: str, H: int, I: int) -> list:
+    """numpy copies of a ChunkLayer's experts for the oracle (others None):
+    kind "int4" the draft's GPTQ tensors, "f16" the target's (w13, w2) from
+    the page-locked host copy."""
+    E = layer.host_f16.shape[0]
+    out = [None] * E
+    for e in experts:
+        if kind == "int4":
+            out[e] = {key: tuple(host(t) for t in layer.int4[e][key]) for key in ("w13", "w2")}
+        else:
+            row = layer.host_f16[e].numpy()
+            out[e] = (row[:2 * I * H].reshape(2 * I, H), row[2 * I * H:].reshape(H, I))
+    return out
+
+
+def chunk_shared_np(layer) -> dict:
+    return dict(w13=host(layer.shared[0]), w2=host(layer.shared[1]),
+                gate=host(layer.shared_gate))

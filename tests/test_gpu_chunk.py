@@ -1,15 +1,17 @@
-"""GPU parity of the multi-layer draft chunk + verify with offloaded experts
-(Qwen-shaped layers: H 2048, 60 experts, top-4, I 1408, shared expert 5632
-with a sigmoid gate; 16 resident experts per layer, the rest staged from
-pinned host memory).
+"""GPU parity of the 24-layer draft chunk + verify with offloaded experts, at
+the configuration's stated size: 24 Qwen-shaped layers (H 2048, 60 experts,
+top-4, I 1408, shared expert 5632 with a sigmoid gate), 16 INT4 draft steps
+with an ELB table [24, 60], 16 of 60 FP16 experts resident per layer, the
+rest staged from pinned host memory, then a 17-token FP16 verify.
 
 Layers are pre-norm residual blocks x <- x + MoE(rms(x)).  Parity is
 teacher-forced per layer: the oracle recomputes layer l from the GPU's own
-layer-l input (normalised input and residual), and the fused normalisation
-of each layer's output against the oracle's rms_norm.  The ELB table must equal the oracle's counts of the
-same inputs exactly; the verify output must be bit-identical to a run with
-every expert resident (staging changes where weights come from, never what is
-computed)."""
+layer-l input (normalised input and residual).  Routing ids and the ELB table
+must equal the oracle's exactly over all 384 layer-steps; FP16 outputs meet
+the normalised-L2 / max-abs bars on sampled layers; the verify output must be
+bit-identical to a run with every expert resident.  The prefetch planner's
+snapshots and the route-fidelity probe's routing are held to the oracle too.
+"""
 import numpy as np
 import pytest
 import torch
@@ -17,15 +19,18 @@ import torch
 import fp16_verify_expert_amd as fve
 import oracle
 import synth
-from fp16_verify_expert_amd.chunk import ChunkEngine, ChunkLayer, top_resident
-from gpu_util import assert_fp16_close, host, say
+from fp16_verify_expert_amd.chunk import (ChunkEngine, distinct_experts, top_resident,
+                                          topk_agreement)
+from gpu_util import (assert_fp16_close, chunk_layer_np, chunk_shared_np, host,
+                      qwen_chunk_layers, say)
 
 pytestmark = pytest.mark.gpu
 
-LAYERS = 3
+LAYERS = 24
 STEPS = 16
 RESIDENT = 16
 TV = 17
+SAMPLED = (0, 11, 23)           # layers held to the full oracle layer
 
 
 @pytest.fixture(scope="module")
@@ -33,17 +38,8 @@ def chunk():
     fve.lib()
     s = synth.QWEN_CHUNK
     dev = torch.device("cuda")
-    layers, gen = [], []
-    for l in range(LAYERS):
-        g = synth.torch_layer(s, l, dev)
-        host_f16 = torch.empty((s.E, 3 * s.H * s.I), dtype=torch.float16, pin_memory=True)
-        for e, (w13, w2) in enumerate(g["f16"]):
-            host_f16[e, :2 * s.I * s.H].copy_(w13.reshape(-1))
-            host_f16[e, 2 * s.I * s.H:].copy_(w2.reshape(-1))
-        layers.append(ChunkLayer(router=g["router"], int4=g["int4"], host_f16=host_f16,
-                                 shared=(g["shared"]["w13"], g["shared"]["w2"]),
-                                 shared_gate=g["shared"]["gate"]))
-        gen.append(g)
+    say(f"chunk: generating {LAYERS} layers")
+    layers, full = qwen_chunk_layers(LAYERS, dev)
     eng = ChunkEngine(layers, s.H, s.E, s.k, s.I, s.shared_I, RESIDENT, TV, device=dev)
     xs = [torch.from_numpy(synth.tokens(s, 1, step=st)).to(dev) for st in range(STEPS)]
     rec_d = []
@@ -58,42 +54,60 @@ def chunk():
     out = eng.verify(xv, rec_v)
     torch.cuda.synchronize()
     say(f"chunk: staged {eng.stats['staged_experts']} experts, hits {eng.stats['hit_experts']}")
-    return dict(shape=s, eng=eng, gen=gen, counts=counts, rec_d=rec_d, rec_v=rec_v, xv=xv,
-                out=out)
+    yield dict(shape=s, eng=eng, layers=layers, full=full, counts=counts, rec_d=rec_d,
+               rec_v=rec_v, xv=xv, out=out)
+    del eng, layers, full
+    torch.cuda.empty_cache()
 
 
-def _np_layer(g, experts, kind):
-    """numpy copies of the given experts (others None) for the oracle."""
-    E = len(g["f16"])
-    out = [None] * E
-    for e in experts:
-        if kind == "int4":
-            out[e] = {key: tuple(host(t) for t in g["int4"][e][key]) for key in ("w13", "w2")}
-        else:
-            out[e] = tuple(host(t) for t in g["f16"][e])
+def _oracle_ids(s, layer, xn):
+    return oracle.route_topk(host(xn), host(layer.router), s.k, False,
+                             host(layer.shared_gate))["ids"]
+
+
+def _check_layer(s, layer, r, kind, what):
+    """Teacher-forced oracle layer on the GPU's own inputs of record r."""
+    xn = host(r["xn"])
+    ids = host(r["ids"])
+    experts = chunk_layer_np(layer, sorted(set(ids.ravel().tolist())), kind, s.H, s.I)
+    ref = oracle.moe_layer(xn, host(layer.router), s.k, experts, kind, chunk_shared_np(layer),
+                           residual=host(r["x"]))
+    assert np.array_equal(ids, ref["route"]["ids"]), what
+    st = assert_fp16_close(host(r["out"]), ref["out"], what)
+    assert_fp16_close(host(r["xn_next"]), oracle.rms_norm(host(r["out"])), what + " norm")
+    return st
+
+
+def _oracle_counts(s, layers, rec, steps):
+    """ELB tables from the oracle's routing of the recorded draft inputs
+    (records are step-major, layer-minor): {n: table after the first n
+    steps} for every n in `steps`; every recorded id must equal the
+    oracle's."""
+    ref = np.zeros((LAYERS, s.E), np.int32)
+    out = {0: ref.copy()} if 0 in steps else {}
+    for i, r in enumerate(rec[:max(steps) * LAYERS]):
+        l = r["layer"]
+        ids = _oracle_ids(s, layers[l], r["xn"])
+        assert np.array_equal(host(r["ids"]), ids), f"step {i // LAYERS} layer {l} ids"
+        ref = oracle.elb_update(ref, ids, l)
+        if (i + 1) % LAYERS == 0 and (i + 1) // LAYERS in steps:
+            out[(i + 1) // LAYERS] = ref.copy()
     return out
-
-
-def _shared_np(g):
-    sh = g["shared"]
-    return dict(w13=host(sh["w13"]), w2=host(sh["w2"]), gate=host(sh["gate"]))
 
 
 def test_chunk_error_word_clear(chunk):
     assert int(host(chunk["eng"].err)[0]) == 0
+    assert len(chunk["rec_d"]) == STEPS * LAYERS and len(chunk["rec_v"]) == LAYERS
     for r in chunk["rec_d"] + chunk["rec_v"]:
         assert torch.isfinite(r["out"]).all()
 
 
 def test_chunk_elb_counters_exact(chunk):
+    """All 384 layer-steps: ids exact, and the [24, 60] table equal to the
+    oracle's counts; every layer's row sums to 16 steps x top-4."""
     s = chunk["shape"]
-    ref = np.zeros((LAYERS, s.E), np.int32)
-    for r in chunk["rec_d"]:
-        g = chunk["gen"][r["layer"]]
-        x = host(r["xn"])
-        ro = oracle.route_topk(x, host(g["router"]), s.k, False, host(g["shared"]["gate"]))
-        assert np.array_equal(host(r["ids"]), ro["ids"])
-        ref = oracle.elb_update(ref, ro["ids"], r["layer"])
+    ref = _oracle_counts(s, chunk["layers"], chunk["rec_d"], [STEPS])[STEPS]
+    assert chunk["counts"].shape == (LAYERS, s.E)
     assert np.array_equal(chunk["counts"], ref)
     assert np.all(ref.sum(axis=1) == STEPS * s.k)
 
@@ -101,18 +115,11 @@ def test_chunk_elb_counters_exact(chunk):
 @pytest.mark.parametrize("step", [0, 7, 15])
 def test_chunk_draft_layers_teacher_forced(chunk, step):
     s = chunk["shape"]
-    for l in range(LAYERS):
+    for l in SAMPLED:
         r = chunk["rec_d"][step * LAYERS + l]
-        g = chunk["gen"][l]
-        xn = host(r["xn"])
-        ids = host(r["ids"])
-        experts = _np_layer(g, sorted(set(ids.ravel().tolist())), "int4")
-        ref = oracle.moe_layer(xn, host(g["router"]), s.k, experts, "int4", _shared_np(g),
-                               residual=host(r["x"]))
-        assert np.array_equal(ids, ref["route"]["ids"])
-        assert_fp16_close(host(r["out"]), ref["out"], f"draft step {step} layer {l}")
-        assert_fp16_close(host(r["xn_next"]), oracle.rms_norm(host(r["out"])),
-                          f"draft step {step} layer {l} norm")
+        assert r["layer"] == l
+        st = _check_layer(s, chunk["layers"][l], r, "int4", f"draft step {step} layer {l}")
+        say(f"draft step {step} layer {l}: l2={st['l2']:.2e}")
 
 
 def test_chunk_residency_from_snapshot(chunk):
@@ -129,28 +136,17 @@ def test_chunk_verify_teacher_forced(chunk):
     s = chunk["shape"]
     for r in chunk["rec_v"]:
         l = r["layer"]
-        g = chunk["gen"][l]
-        xn = host(r["xn"])
-        ids = host(r["ids"])
-        experts = _np_layer(g, sorted(set(ids.ravel().tolist())), "f16")
-        ref = oracle.moe_layer(xn, host(g["router"]), s.k, experts, "f16", _shared_np(g),
-                               residual=host(r["x"]))
-        assert np.array_equal(ids, ref["route"]["ids"])
-        st = assert_fp16_close(host(r["out"]), ref["out"], f"verify layer {l}")
-        assert_fp16_close(host(r["xn_next"]), oracle.rms_norm(host(r["out"])),
-                          f"verify layer {l} norm")
+        assert np.array_equal(host(r["ids"]), _oracle_ids(s, chunk["layers"][l], r["xn"]))
+    for l in SAMPLED:
+        st = _check_layer(s, chunk["layers"][l], chunk["rec_v"][l], "f16", f"verify layer {l}")
         say(f"verify layer {l}: l2={st['l2']:.2e}")
     assert chunk["eng"].stats["staged_experts"] > 0
 
 
 def test_chunk_verify_residency_invariant(chunk):
-    s = chunk["shape"]
     eng = chunk["eng"]
-    full = torch.empty((LAYERS, s.E, 3 * s.H * s.I), dtype=torch.float16, device="cuda")
-    for l in range(LAYERS):
-        full[l].copy_(eng.layers[l].host_f16)
     rec = []
-    out = eng.verify(chunk["xv"], rec, all_resident=full)
+    out = eng.verify(chunk["xv"], rec, all_resident=chunk["full"])
     torch.cuda.synchronize()
     assert torch.equal(out, chunk["out"])
     for a, b in zip(rec, chunk["rec_v"]):
@@ -191,15 +187,12 @@ def test_chunk_forward_matches_draft_and_verify(chunk):
     INT4 over one row equals the draft step."""
     s = chunk["shape"]
     eng = chunk["eng"]
-    full = torch.empty((LAYERS, s.E, 3 * s.H * s.I), dtype=torch.float16, device="cuda")
-    for l in range(LAYERS):
-        full[l].copy_(eng.layers[l].host_f16)
-    ref = eng.verify(chunk["xv"], all_resident=full).clone()
+    ref = eng.verify(chunk["xv"], all_resident=chunk["full"]).clone()
     rec = []
-    out = eng.forward(chunk["xv"], "f16", full, rec)
+    out = eng.forward(chunk["xv"], "f16", chunk["full"], rec)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
-    assert len(rec) == LAYERS and all(r.shape == (17, s.k) for r in rec)
+    assert len(rec) == LAYERS and all(r["ids"].shape == (17, s.k) for r in rec)
     saved = eng.counters.clone()
     x1 = chunk["xv"][:1].contiguous()
     d = eng.draft_step(x1).clone()
@@ -210,6 +203,47 @@ def test_chunk_forward_matches_draft_and_verify(chunk):
     assert int(host(eng.err)[0]) == 0
 
 
+def test_chunk_route_fidelity_probe_against_oracle(chunk):
+    """The route-fidelity probe on a short correlated token stream: every
+    layer's draft and target ids equal the oracle's routing of the recorded
+    layer inputs, and the agreement and distinct-expert figures computed from
+    the GPU ids equal those recomputed here, by plain loops, from the
+    oracle's ids."""
+    s = chunk["shape"]
+    eng = chunk["eng"]
+    N = 32
+    x = torch.from_numpy(synth.token_stream(s, N, 0.8, step=7)).cuda()
+    rd, rt = [], []
+    eng.forward(x, "int4", record=rd)
+    eng.forward(x, "f16", chunk["full"], record=rt)
+    torch.cuda.synchronize()
+    assert int(host(eng.err)[0]) == 0
+    o_d = np.stack([_oracle_ids(s, chunk["layers"][r["layer"]], r["xn"]) for r in rd])
+    o_t = np.stack([_oracle_ids(s, chunk["layers"][r["layer"]], r["xn"]) for r in rt])
+    g_d = np.stack([host(r["ids"]) for r in rd])
+    g_t = np.stack([host(r["ids"]) for r in rt])
+    assert np.array_equal(g_d, o_d) and np.array_equal(g_t, o_t)
+    # the probe's statistics from the GPU ids ...
+    agree = topk_agreement(g_d, g_t)
+    depths = [1, 2, 4, 8, 16, 32]
+    dist = distinct_experts(g_t, depths)
+    # ... against plain recomputations from the oracle's ids
+    for l in range(LAYERS):
+        for t in range(N):
+            same = sum(1 for e in o_d[l, t] if e in set(o_t[l, t].tolist()))
+            assert agree[l, t] == same / s.k
+    for K in depths:
+        total, n = 0, 0
+        for l in range(LAYERS):
+            for w in range(N // K):
+                total += len(set(o_t[l, w * K:(w + 1) * K].ravel().tolist()))
+                n += 1
+        assert abs(dist[K] - total / n) <= 1e-12 * dist[K]
+    assert dist[1] == s.k and dist[32] > dist[1]
+    say(f"route fidelity: agreement {agree.mean():.3f}, distinct K=1/16/32 "
+        f"{dist[1]:.1f}/{dist[16]:.1f}/{dist[32]:.1f}")
+
+
 def test_chunk_planner_rounds_residency_invariant(chunk):
     """Speculation rounds with the prefetch planner (chunked drafting, ELB
     snapshots driving prefetches on the copy stream, per-layer events, misses
@@ -217,9 +251,6 @@ def test_chunk_planner_rounds_residency_invariant(chunk):
     bit-identical to the all-resident verify of the same rows."""
     s = chunk["shape"]
     eng = chunk["eng"]
-    full = torch.empty((LAYERS, s.E, 3 * s.H * s.I), dtype=torch.float16, device="cuda")
-    for l in range(LAYERS):
-        full[l].copy_(eng.layers[l].host_f16)
     if not hasattr(eng, "graph"):
         eng.capture_draft()
     before = eng.stats.get("prefetched_experts", 0)
@@ -229,7 +260,7 @@ def test_chunk_planner_rounds_residency_invariant(chunk):
         xv = torch.cat(xs + [torch.from_numpy(synth.tokens(s, 1, step=300 + 20 * r + STEPS)).cuda()])
         say(f"round {r} planner={planner}")
         out = eng.run_round(xs, xv, planner=planner).clone()
-        ref = eng.verify(xv, all_resident=full)
+        ref = eng.verify(xv, all_resident=chunk["full"])
         torch.cuda.synchronize()
         assert torch.equal(out, ref), r
         for l in range(LAYERS):
@@ -237,3 +268,30 @@ def test_chunk_planner_rounds_residency_invariant(chunk):
             assert len(set(held)) == len(held)
     assert eng.stats["prefetched_experts"] > before
     assert int(host(eng.err)[0]) == 0
+
+
+def test_chunk_planner_round_against_oracle(chunk):
+    """One planner round (residency carried over from earlier rounds) held to
+    the oracle: every ELB snapshot the planner acted on equals the oracle's
+    counts over the draft steps done by then, sampled verify layers match the
+    teacher-forced oracle layer, and the output is bit-identical to the
+    all-resident verify."""
+    s = chunk["shape"]
+    eng = chunk["eng"]
+    xs = [torch.from_numpy(synth.tokens(s, 1, step=700 + st)).cuda() for st in range(STEPS)]
+    xv = torch.cat(xs + [torch.from_numpy(synth.tokens(s, 1, step=700 + STEPS)).cuda()])
+    rec = {}
+    out = eng.run_round(xs, xv, planner=True, record=rec).clone()
+    ref = eng.verify(xv, all_resident=chunk["full"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert int(host(eng.err)[0]) == 0
+    snaps = rec["snapshots"]
+    assert len(snaps) >= 2 and snaps[-1][0] == STEPS
+    assert [n for n, _ in snaps] == sorted(n for n, _ in snaps)
+    ref = _oracle_counts(s, chunk["layers"], rec["draft"], [n for n, _ in snaps])
+    for n_done, counts in snaps:
+        assert np.array_equal(counts, ref[n_done]), n_done
+    say(f"planner round: snapshots after {[n for n, _ in snaps]} draft steps")
+    for l in SAMPLED:
+        _check_layer(s, chunk["layers"][l], rec["verify"][l], "f16", f"planner verify layer {l}")
