@@ -38,6 +38,12 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFS = 2516.6   # dense FP16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 POOL = 8                     # distinct seeded batches
+STREAM_BLOCKS = 2048         # workgroups of the streaming-read ceiling (best of 1024/2048/4096)
+
+
+def idx_all(args, K):
+    """Pool indexes of the K timed steps."""
+    return [(args.warmup + st) % POOL for st in range(K)]
 
 
 def parse():
@@ -67,6 +73,9 @@ def parse():
                          "7x distinct experts from depth 1 to 16 on these layers)")
     ap.add_argument("--no-dense-point", dest="dense_point", action="store_false",
                     help="phi_layer: skip the supplementary T=2048 verify point")
+    ap.add_argument("--no-other-configs", dest="other_configs", action="store_false",
+                    help="phi_layer: skip the DeepSeek-V2-Lite draft (T=1/4/16) and Qwen1.5-MoE "
+                         "verify (T=9) sub-objects of the line")
     ap.add_argument("--draft", choices=["fused", "split"], default="fused",
                     help="phi_layer draft step: moe_draft_route_ffn + moe_combine (fused: routing "
                          "folded into the gate/up launch, 3 launches) or moe_route_plan + "
@@ -306,7 +315,32 @@ def main():
     call_us = {n: round(1e3 * sum(a.elapsed_time(b) for a, b in v) / nl, 2)
                for n, v in calls.items()}
 
-    idx = [(args.warmup + st) % POOL for st in range(K)]
+    # ---- attainable ceiling of the draft FFN: streaming reads of the same
+    #      gate/up and down byte counts (the touched experts' INT4 bytes of
+    #      each projection) in two dependent launches, HIP events around
+    #      both, each preceded by a verify step as in the per-call pass ----
+    def int4_bytes(Kd, N):
+        return Kd * N // 2 + (Kd // 128) * N * 2 + (Kd // 128) * (N // 8) * 4
+    nt = sum(touched_d[i] for i in idx_all(args, K)) / K
+    gu_b = int(round(nt * int4_bytes(H, 2 * I))) // 16 * 16
+    dn_b = int(round(nt * int4_bytes(I, H))) // 16 * 16
+    src_gu = torch.empty(gu_b // 2, dtype=torch.float16, device=dev)
+    src_dn = torch.empty(dn_b // 2, dtype=torch.float16, device=dev)
+    sink = torch.zeros(STREAM_BLOCKS, dtype=torch.int32, device=dev)
+    ev_st = [(mk(), mk()) for _ in range(nl)]
+    for st in range(nl + 1):
+        verify(args.warmup + st)
+        if st:
+            ev_st[st - 1][0].record()
+        fve.smoe_stream_read(src_gu, sink, STREAM_BLOCKS)
+        fve.smoe_stream_read(src_dn, sink, STREAM_BLOCKS)
+        if st:
+            ev_st[st - 1][1].record()
+    torch.cuda.synchronize()
+    stream_us = 1e3 * sum(a.elapsed_time(b) for a, b in ev_st) / nl
+    del src_gu, src_dn
+
+    idx = idx_all(args, K)
     draft_ms = sum(ph[st][0].elapsed_time(ph[st][1]) for st in range(K))
     verify_ms = sum(ph[st][1].elapsed_time(ph[st][2]) for st in range(K))
     w4_ms = [kw[st][0].elapsed_time(kw[st][1]) for st in range(K)]
@@ -386,7 +420,17 @@ def main():
                            "bound": "hbm", "achieved": round(rd_ach, 2), "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": round(rd_ach / HBM_PEAK_GBS, 4),
                            "avg_us": round(1e3 * sum(w4_ms) / K, 3),
-                           "traffic": pmc_traffic("w4a16_grouped_ffn")},
+                           "traffic": pmc_traffic("w4a16_grouped_ffn"),
+                           "attainable": {
+                               "what": "smoe_stream_read of the same gate/up and down byte "
+                                       "counts in two dependent launches, HIP events around "
+                                       "both, after a verify step",
+                               "bytes": gu_b + dn_b, "us": round(stream_us, 3),
+                               "gbps": round((gu_b + dn_b) / stream_us / 1e3, 1),
+                               "frac_hbm": round((gu_b + dn_b) / stream_us / 1e3
+                                                 / HBM_PEAK_GBS, 4)},
+                           "frac_attainable": round(rd_ach / ((gu_b + dn_b) / stream_us / 1e3),
+                                                    4)},
         "call_us": call_us,
         "host_wall_s": round(wall, 4),
         "gen_s": round(gen_s, 2),
@@ -431,6 +475,15 @@ def main():
             "attainable_tflops": round(min(MFMA_F16_PEAK_TFS,
                                            fl / (nact * b16) * HBM_PEAK_GBS / 1e3), 1)}
         del xd, ws_x, yd
+
+    # ---- the other configurations' layers, for the same line: the
+    #      DeepSeek-V2-Lite draft step and the Qwen1.5-MoE verify layer ----
+    if args.other_configs:
+        K_o = min(max(K, 5), 20)
+        ds_res, _, _ = ds_draft_results(K_o, min(args.warmup, 3))
+        res["ds_draft"] = {"config": DS_WORKLOAD, "steps": K_o, "results": ds_res}
+        res["qwen_verify"] = {"config": QWEN_VERIFY_WORKLOAD, "steps": K_o,
+                              **qwen_verify_results(K_o, min(args.warmup, 3))}
 
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -567,6 +620,27 @@ def bench_draft_formats(args):
 
 
 def bench_ds_draft(args):
+    """The DeepSeek-V2-Lite-shaped draft layer step as a line of its own
+    (ds_draft_results)."""
+    results, gen_s, K = ds_draft_results(max(args.steps, 5), args.warmup)
+    r1 = results[0]
+    res = {"metric": "MoE-layer INT4 draft weight GB/s (% HBM peak); verify TFLOP/s (% MFMA)",
+           "value": r1["int4_gbps"], "unit": "GB/s", "n_gpus": 1, "steps": K,
+           "warmup": args.warmup, "ms_per_step": round(r1["step_us"] / 1e3, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "int4-w/fp16-a (routed experts), fp16 (shared experts); fp32 accumulate",
+           "data": "synthetic (seeded N(0,0.02) weights from torch Philox, RTN GPTQ INT4 g128; "
+                   "N(0,1) tokens)",
+           "config": {"workload": DS_WORKLOAD},
+           "results": results, "gen_s": round(gen_s, 1)}
+    print(json.dumps(res), flush=True)
+
+
+DS_WORKLOAD = ("ds_v2_lite draft layer step: H=2048 E=64 top-6 I=1408 + 2 shared experts (as one "
+               "of I=2816); T=1/4/16; ELB [1,64]; 1 GiB read before each timed step")
+
+
+def ds_draft_results(K, warmup):
     """The DeepSeek-V2-Lite-shaped draft layer step (hidden 2048, 64 routed
     experts, top-6, intermediate 1408, 2 FP16 shared experts run as one of
     intermediate 2816, ELB counters over one layer) at T = 1, 4 and 16 tokens,
@@ -601,7 +675,6 @@ def bench_ds_draft(args):
     counters = torch.zeros((1, E), dtype=torch.int32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     mk = lambda: torch.cuda.Event(enable_timing=True)
-    K = max(args.steps, 5)
     b4 = s.int4_bytes_per_expert
     results = []
     for T in (1, 4, 16):
@@ -643,18 +716,18 @@ def bench_ds_draft(args):
             step(i)
             torch.cuda.synchronize()
             touched.append(int(maps_b["n_active"].item()))
-        for i in range(args.warmup):
+        for i in range(warmup):
             step(i)
         ev = [(mk(), mk()) for _ in range(K)]
         torch.cuda.synchronize()
         for st in range(K):
             scrub.sum()  # read-only: leaves no dirty lines to write back during the step
             ev[st][0].record()
-            step(args.warmup + st)
+            step(warmup + st)
             ev[st][1].record()
         torch.cuda.synchronize()
         assert int(err.item()) == 0, "device error word set"
-        idx = [(args.warmup + st) % POOL for st in range(K)]
+        idx = [(warmup + st) % POOL for st in range(K)]
         b_int4 = sum(touched[i] * b4 for i in idx) / K
         b_sh = s.shared_f16_bytes
         us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / K
@@ -668,19 +741,106 @@ def bench_ds_draft(args):
                                  if T == 1 else "moe_route_plan + w4a16_grouped_ffn + "
                                  "verify_grouped_gemm (shared) + moe_combine")})
         print(json.dumps(results[-1]), file=sys.stderr, flush=True)
-    r1 = results[0]
-    res = {"metric": "MoE-layer INT4 draft weight GB/s (% HBM peak); verify TFLOP/s (% MFMA)",
-           "value": r1["int4_gbps"], "unit": "GB/s", "n_gpus": 1, "steps": K,
-           "warmup": args.warmup, "ms_per_step": round(r1["step_us"] / 1e3, 5),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "int4-w/fp16-a (routed experts), fp16 (shared experts); fp32 accumulate",
-           "data": "synthetic (seeded N(0,0.02) weights from torch Philox, RTN GPTQ INT4 g128; "
-                   "N(0,1) tokens)",
-           "config": {"workload": "ds_v2_lite draft layer step: H=2048 E=64 top-6 I=1408 + 2 "
-                                  "shared experts (as one of I=2816); T=1/4/16; ELB [1,64]; "
-                                  "1 GiB read before each timed step"},
-           "results": results, "gen_s": round(gen_s, 1)}
-    print(json.dumps(res), flush=True)
+    del g, table, scrub
+    torch.cuda.empty_cache()
+    return results, gen_s, K
+
+
+QWEN_VERIFY_WORKLOAD = ("qwen15_moe verify layer: H=2048 E=60 top-4 I=1408 + gated shared expert "
+                        "I=5632; K+1=9 tokens; 1 GiB read before each timed step")
+
+
+def qwen_verify_results(K, warmup):
+    """The Qwen1.5-MoE-shaped verification layer at K+1 = 9 tokens, every
+    weight in HBM: routing plan, verify_grouped_gemm over the routed experts,
+    verify_grouped_gemm over the gated shared expert (one always-on group),
+    combine.  A read of 1 GiB runs before each timed step, outside its
+    events.  Reported: the routed and the shared expert's verify calls
+    (HIP events around each) as FP16 weight TB/s, fraction of HBM peak,
+    TFLOP/s and fraction of FP16 MFMA peak, and the layer step's wall time."""
+    import torch
+
+    import fp16_verify_expert_amd as fve
+    import synth
+
+    dev = torch.device("cuda")
+    s = synth.QWEN
+    H, E, k, I, Is, T = s.H, s.E, s.k, s.I, s.shared_I, 9
+    g = synth.torch_layer(s, 0, dev, int4=False)
+    table = fve.f16_expert_table(g["f16"])
+    shared = (g["shared"]["w13"], g["shared"]["w2"])
+    tsh = fve.f16_expert_table([shared])
+    gate = g["shared"]["gate"]
+    router = g["router"]
+    scrub = torch.empty(1 << 29, dtype=torch.float16, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    xs = [torch.from_numpy(synth.tokens(s, T, step=200 + i)).to(dev) for i in range(POOL)]
+    ws = fve.new_workspace(1, T, k, H, I, E)
+    wsv = fve.new_workspace(1, T, 1, H, Is, 1)
+    iota = torch.arange(T, dtype=torch.int32, device=dev)
+    offs = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    ids_b = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w_b = torch.empty((T, k), dtype=torch.float32, device=dev)
+    gate_b = torch.empty((T,), dtype=torch.float32, device=dev)
+    maps_b = fve._new_maps(T, k, E, dev)
+    lg_b = torch.empty(T * (E + 1), dtype=torch.float32, device=dev)
+    y = torch.empty((T * k, H), dtype=torch.float16, device=dev)
+    sh_out = torch.empty((T, H), dtype=torch.float16, device=dev)
+    out = torch.empty((T, H), dtype=torch.float16, device=dev)
+
+    def step(i, ev=None):
+        x = xs[i % POOL]
+        fve.moe_route_plan(x, router, k, False, gate, err_word=err, topk_ids=ids_b, topk_w=w_b,
+                           shared_gate=gate_b, maps=maps_b, logits_ws=lg_b)
+        if ev: ev[1].record()
+        fve.verify_grouped_gemm(x, maps_b["sorted_token"], maps_b["offsets"], table, T, T * k,
+                                H, I, E, ws, active=maps_b["active"],
+                                n_active=maps_b["n_active"], y_sorted=y, err_word=err)
+        if ev: ev[2].record()
+        fve.verify_grouped_gemm(x, iota, offs, tsh, T, T, H, Is, 1, wsv, y_sorted=sh_out,
+                                err_word=err)
+        if ev: ev[3].record()
+        fve.moe_combine(y, maps_b["pair_pos"], w_b, sh_out, gate_b, out=out)
+
+    touched = []
+    for i in range(POOL):
+        step(i)
+        torch.cuda.synchronize()
+        touched.append(int(maps_b["n_active"].item()))
+    for i in range(warmup):
+        step(i)
+    evs = [[mk() for _ in range(5)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for st in range(K):
+        scrub.sum()
+        evs[st][0].record()
+        step(warmup + st, evs[st])
+        evs[st][4].record()
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0, "device error word set"
+    idx = [(warmup + st) % POOL for st in range(K)]
+    avg = lambda a, b: 1e3 * sum(e[a].elapsed_time(e[b]) for e in evs) / K
+    routed_us, shared_us, step_us = avg(1, 2), avg(2, 3), avg(0, 4)
+    nt = sum(touched[i] for i in idx) / K
+    rb = nt * s.f16_bytes_per_expert
+    sb = s.shared_f16_bytes
+    rf = 2.0 * T * k * 3 * H * I
+    sf = 2.0 * T * 3 * H * Is
+
+    def part(nbytes, flops, us):
+        return {"bytes": round(nbytes), "us": round(us, 2),
+                "tbps": round(nbytes / us / 1e6, 3),
+                "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                "tflops": round(flops / us / 1e6, 3),
+                "frac_mfma": round(flops / us / 1e6 / MFMA_F16_PEAK_TFS, 5)}
+    res = {"T": T, "touched_experts_avg": round(nt, 2),
+           "routed": part(rb, rf, routed_us), "shared": part(sb, sf, shared_us),
+           "layer_step_us": round(step_us, 2),
+           "note": "HIP events around each call inside the step (about 2-4 us each)"}
+    del g, table, scrub
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_route_fidelity(args):

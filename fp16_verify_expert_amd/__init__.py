@@ -61,6 +61,7 @@ _SIGS = {
     "moe_combine": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, ctypes.c_float,
                          _vp]),
     "expert_stage_async": (_i, [_vp, _vp, _sz, _vp, _vp]),
+    "smoe_stream_read": (_i, [_vp, _sz, _vp, _i, _vp]),
 }
 
 
@@ -385,3 +386,15 @@ def expert_stage_async(dst: torch.Tensor, src_pinned: torch.Tensor, side_stream=
             done_event.record(side_stream if side_stream is not None else None)
         ev = _vp(done_event.cuda_event)
     _call("expert_stage_async", _p(dst), _vp(src_pinned.data_ptr()), nbytes, _s(side_stream), ev)
+
+
+def smoe_stream_read(src: torch.Tensor, sink: torch.Tensor, blocks: int = 2048,
+                     stream=None) -> torch.Tensor:
+    """Measurement aid: one streaming read of `src` (XOR per workgroup into
+    sink, uint32/int32 [blocks])."""
+    _check(sink, torch.int32, "sink")
+    if sink.numel() < blocks:
+        raise ValueError("smoe_stream_read: sink holds fewer words than blocks")
+    _call("smoe_stream_read", _p(src), src.numel() * src.element_size(), _p(sink), blocks,
+          _s(stream))
+    return sink

@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsmoe.so")
 OBJ = os.path.join(PKG, "_build")
 SOURCES = ["abi.hip", "route.hip", "maps.hip", "plan.hip", "w4a16.hip", "verify.hip",
-           "dense.hip", "combine.hip"]
+           "dense.hip", "combine.hip", "stream.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -152,6 +152,20 @@ int smoe_abi_version(void) { return SMOE_ABI_VERSION; }
 
 const char* smoe_last_error(void) { return g_err.c_str(); }
 
+smoe_status smoe_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks,
+                             void* stream) {
+    REQUIRE(src && sink, SMOE_ERR_NULL, "smoe_stream_read: src and sink are required");
+    REQUIRE(bytes % 16 == 0 && aligned(src, 16), SMOE_ERR_SHAPE,
+            "smoe_stream_read: bytes=%zu must be a multiple of 16 and src 16-byte aligned", bytes);
+    REQUIRE(blocks >= 1 && blocks <= 65535, SMOE_ERR_SHAPE,
+            "smoe_stream_read: blocks=%d must be in [1, 65535]", blocks);
+    if (bytes == 0) return ok();
+    CHECK_DEVICE();
+    return hip_result(smoe::launch_stream_read(src, bytes, sink, blocks,
+                                               static_cast<hipStream_t>(stream)),
+                      "smoe_stream_read launch");
+}
+
 size_t smoe_workspace_bytes(int which, int T, int k, int H, int I, int E) {
     if (T < 0 || k < 1 || E < 1 || E > 256 || H <= 0 || I <= 0 || H % 128 || I % 128) return 0;
     if ((long long)T * k > kMaxPairs) return 0;

@@ -87,4 +87,6 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* pp, const float* w,
                           const uint16_t* shared, const float* sscale, const uint16_t* resid,
                           int T, int k, int H, uint16_t* out, uint16_t* norm_out, float eps,
                           hipStream_t s);
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks,
+                              hipStream_t s);
 }  // namespace smoe

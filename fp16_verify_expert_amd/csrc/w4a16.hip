@@ -650,11 +650,54 @@ SMOE_DEV void step_if(const GroupLoad<BITS>& L, const W4Lds& l, int g, int G, in
     for (int c = 0; c < 4; ++c) acc[0][c] += valid ? t[0][c] : 0.0f;
 }
 
+// Epilogue of a one-token block: the lane groups' partial sums of the column
+// block added in a fixed order -- inside each wave across its 64 / LPR lane
+// groups by a butterfly over lane distances LPR, 2 LPR, ..., then the waves'
+// sums in increasing wave order through LDS -- and SwiGLU (gate/up projection,
+// into h) or the plain sum (down projection, into y) stored.  One barrier; no
+// thread adds more than one partial per wave.
+template <int PHASE, int LPR>
+SMOE_DEV void reduce_store_t1(const W4Args& a, float* red, float (&acc)[1][4], int q, int cb,
+                              int slot) {
+    constexpr int NB = 4 * LPR;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int nw = (int)(blockDim.x >> 6);
+#pragma unroll
+    for (int d = LPR; d < 64; d *= 2)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[0][c] += __shfl_xor(acc[0][c], d);
+    if (lane < LPR)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) red[wave * NB + 4 * q + c] = acc[0][c];
+    __syncthreads();
+    if (PHASE == 1) {
+        // red[w][j] is gate column j, red[w][NB/2 + j] the matching up column
+        if (tid < NB / 2) {
+            float gv = 0.0f, uv = 0.0f;
+            for (int w = 0; w < nw; ++w) {
+                gv += red[w * NB + tid];
+                uv += red[w * NB + NB / 2 + tid];
+            }
+            a.out[(size_t)slot * a.I + cb * (NB / 2) + tid] = f2h(silu_f(gv) * uv);
+        }
+    } else if (tid < NB && cb * NB + tid < a.N) {
+        float v = 0.0f;
+        for (int w = 0; w < nw; ++w) v += red[w * NB + tid];
+        a.out[(size_t)slot * a.N + cb * NB + tid] = f2h(v);
+    }
+}
+
 // One activation row (T = 1) against the column block cb of matrix wm; each
 // slot takes groups myslot + j * nslots, j < NG.  xv holds the row's chunks,
 // requested by the caller.  The slot's groups go through two register
-// buffers in straight-line code: the first two are requested before the row
-// is permuted into LDS, and buffer A is refilled as soon as it has been
+// buffers in straight-line code.  The first group is requested before the
+// row is permuted into LDS; the second only after the first has been
+// consumed when NG == 2 (a wave whose requests stall for the memory pipeline
+// to drain would otherwise reach its arithmetic only once every group of it
+// is in flight, late in the launch); with three or four groups the second is
+// requested up front and a buffer is refilled as soon as it has been
 // consumed, so every wait is for one group while the next is in flight.
 template <int BITS, int PHASE, int LPR, int NG>
 SMOE_DEV void one_token_block(const W4Args& a, const W4Lds& l, const smoe_w4_mat& wm,
@@ -682,7 +725,7 @@ SMOE_DEV void one_token_block(const W4Args& a, const W4Lds& l, const smoe_w4_mat
     const int g0 = myslot;
     GroupLoad<BITS> A, B;
     load_group<BITS>(A, src, clamp_group(g0, G), col, colok);
-    if (NG >= 2) load_group<BITS>(B, src, clamp_group(g0 + nslots, G), col, colok);
+    if (NG >= 3) load_group<BITS>(B, src, clamp_group(g0 + nslots, G), col, colok);
     __builtin_amdgcn_sched_barrier(0);  // every request above is issued before the row is staged
     // straight-line stores (indexes past the row rewrite its last chunk with
     // the same value), so the wait for the row leaves the weights in flight;
@@ -695,12 +738,16 @@ SMOE_DEV void one_token_block(const W4Args& a, const W4Lds& l, const smoe_w4_mat
     finish_rows<BITS>(l.xs, l.sums, 1, K8, G);
     float acc[1][4] = {{0.0f, 0.0f, 0.0f, 0.0f}};
     step_if<BITS>(A, l, g0, G, K8, zsh, mk, acc);
+    if (NG == 2) {
+        load_group<BITS>(B, src, clamp_group(g0 + nslots, G), col, colok);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     if (NG >= 3) load_group<BITS>(A, src, clamp_group(g0 + 2 * nslots, G), col, colok);
     if (NG >= 2) step_if<BITS>(B, l, g0 + nslots, G, K8, zsh, mk, acc);
     if (NG >= 4) load_group<BITS>(B, src, clamp_group(g0 + 3 * nslots, G), col, colok);
     if (NG >= 3) step_if<BITS>(A, l, g0 + 2 * nslots, G, K8, zsh, mk, acc);
     if (NG >= 4) step_if<BITS>(B, l, g0 + 3 * nslots, G, K8, zsh, mk, acc);
-    reduce_store<PHASE, 1, NB>(a, l.red, acc, myslot, nslots, q, cb, slot, 1);
+    reduce_store_t1<PHASE, LPR>(a, l.red, acc, q, cb, slot);
 }
 
 // Request the first kRowChunksPerThread chunks of an activation row per

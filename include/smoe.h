@@ -400,6 +400,20 @@ smoe_status moe_combine(const uint16_t* y_sorted, const int32_t* pair_pos, const
 smoe_status expert_stage_async(void* dst_device, const void* src_pinned_host, size_t bytes,
                                void* side_stream, void* done_event);
 
+/* ------------------------------------------------------------------------
+ * smoe_stream_read -- measurement aid, not a step of the path: reads `bytes`
+ * of device memory at `src` once, grid-stride over `blocks` workgroups of
+ * 256 threads, with the 16-byte non-temporal loads the weight-streaming
+ * kernels use, and writes the XOR of the 32-bit words each workgroup read to
+ * sink[workgroup] (uint32 [blocks]).  Its duration is the memory-bound
+ * ceiling for streaming that many bytes in one launch; the throughput of the
+ * draft FFN is reported against a sequence of such reads of the same byte
+ * counts.  bytes must be a multiple of 16, src 16-byte aligned, 1 <= blocks
+ * <= 65535.
+ * ---------------------------------------------------------------------- */
+smoe_status smoe_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks,
+                             void* stream);
+
 /* Workspace size in bytes for which = 0 (w4a16_grouped_ffn) or
  * 1 (verify_grouped_gemm); 0 for an invalid request. */
 size_t smoe_workspace_bytes(int which, int T, int k, int H, int I, int E);

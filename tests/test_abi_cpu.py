@@ -21,7 +21,7 @@ def test_exports_every_header_function():
                 "moe_gather", "moe_route_plan", "w4a16_grouped_ffn", "wq_grouped_ffn",
                 "moe_draft_route_ffn", "w4a16_grouped_ffn_noalloc",
                 "verify_grouped_gemm", "moe_combine",
-                "expert_stage_async", "smoe_workspace_bytes"}
+                "expert_stage_async", "smoe_workspace_bytes", "smoe_stream_read"}
     assert set(names) == expected
     L = ctypes.CDLL(fve.LIB_PATH)
     for n in names:
@@ -213,6 +213,17 @@ def test_w4a16_noalloc_validation():
     assert L.w4a16_grouped_ffn_noalloc(*args, 4, 2, 256, 512, 8, 128, None, None, None) == 1
     assert L.w4a16_grouped_ffn_noalloc(*args, -1, 2, 256, 512, 8, 128, FAKE, None, None) == 2
     assert L.w4a16_grouped_ffn_noalloc(*args, 0, 2, 256, 512, 8, 128, FAKE, None, None) == 0
+
+
+def test_stream_read_validation():
+    L = fve.lib()
+    assert L.smoe_stream_read(None, 16, FAKE, 1, None) == 1
+    assert L.smoe_stream_read(FAKE, 16, None, 1, None) == 1
+    assert L.smoe_stream_read(FAKE, 20, FAKE, 1, None) == 2
+    assert L.smoe_stream_read(V(0x1008), 16, FAKE, 1, None) == 2
+    assert L.smoe_stream_read(FAKE, 16, FAKE, 0, None) == 2
+    assert L.smoe_stream_read(FAKE, 16, FAKE, 65536, None) == 2
+    assert L.smoe_stream_read(FAKE, 0, FAKE, 4, None) == 0
 
 
 def test_verify_validation():
