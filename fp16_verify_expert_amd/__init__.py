@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsmoe.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "smoe.h")
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 SMOE_DERR_BAD_ID = 1
 SMOE_DERR_NULL_EXPERT = 2
@@ -55,7 +55,9 @@ _SIGS = {
     "moe_draft_route_ffn": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp,
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _vp, _vp, _i, _vp, _vp,
-                                 _vp, _sz, _vp, _vp]),
+                                 _vp, _vp, _sz, _vp, _vp]),
+    "moe_combine_route_logits": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp,
+                                      ctypes.c_float, _vp, _vp, _i, _vp, _vp]),
     "verify_grouped_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp,
                                  _vp, _sz, _vp, _vp]),
     "moe_combine": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, ctypes.c_float,
@@ -293,12 +295,14 @@ def moe_draft_route_ffn(x, w_router, k: int, table, I: int, workspace,
                         renormalize: bool = False, w_shared_gate=None, *, counters=None,
                         layer: int = 0, err_word=None, topk_ids=None, topk_w=None,
                         shared_gate=None, maps=None, y_sorted=None, shared=None, shared_h=None,
-                        shared_out=None, stream=None):
+                        shared_out=None, logits=None, stream=None):
     """One-token draft step: moe_route_plan and w4a16_grouped_ffn in three
     launches.  With shared = (w13 [2 Is, H], w2 [H, Is]) fp16, a dense shared
     expert computed in the same launches (shared_h: [Is] fp16 scratch,
     shared_out: [1, H] fp16 out).  Returns (topk_ids, topk_w, shared_gate,
-    maps, y_sorted), plus shared_out when a shared expert is given."""
+    maps, y_sorted), plus shared_out when a shared expert is given.  logits
+    (fp32 [E (+1)], optional): the router logits of x from
+    moe_combine_route_logits, taken instead of a logits launch."""
     _check(x, torch.float16, "x")
     _check(w_router, torch.float16, "w_router")
     T, H = x.shape
@@ -339,7 +343,7 @@ def moe_draft_route_ffn(x, w_router, k: int, table, I: int, workspace,
           _p(maps["offsets"]), _p(maps["sorted_token"]), _p(maps["sorted_pair"]),
           _p(maps["pair_pos"]), _p(maps["active"]), _p(maps["n_active"]), _p(y_sorted),
           _p(sw13), _p(sw2), Is, _p(shared_h) if shared is not None else None,
-          _p(shared_out) if shared is not None else None,
+          _p(shared_out) if shared is not None else None, _p(logits),
           _p(workspace), workspace.numel() * workspace.element_size(), _p(err_word), _s(stream))
     if shared is not None:
         return topk_ids, topk_w, shared_gate, maps, y_sorted, shared_out
@@ -373,6 +377,32 @@ def moe_combine(y_sorted, pair_pos, topk_w, shared_out=None, shared_scale=None, 
           _p(shared_scale), _p(residual), T, k, H, _p(out),
           _p(norm_out) if want_norm else None, float(norm_eps), _s(stream))
     return (out, norm_out) if want_norm else out
+
+
+def moe_combine_route_logits(y_sorted, pair_pos, topk_w, w_router, shared_out=None,
+                             shared_scale=None, residual=None, w_shared_gate=None, *, out=None,
+                             norm_out=None, logits=None, norm_eps: float = 1e-6, stream=None):
+    """One token: moe_combine (with the norm epilogue) and the next layer's
+    router logits of the normalised row.  Returns (out, norm_out, logits)."""
+    _check(y_sorted, torch.float16, "y_sorted")
+    _check(w_router, torch.float16, "w_router")
+    T, k = topk_w.shape
+    if T != 1:
+        raise ValueError(f"moe_combine_route_logits takes one token, got T={T}")
+    H = y_sorted.shape[1]
+    E = w_router.shape[0]
+    dev = y_sorted.device
+    if out is None:
+        out = torch.empty((1, H), dtype=torch.float16, device=dev)
+    if norm_out is None:
+        norm_out = torch.empty((1, H), dtype=torch.float16, device=dev)
+    if logits is None:
+        logits = torch.empty(E + (1 if w_shared_gate is not None else 0), dtype=torch.float32,
+                             device=dev)
+    _call("moe_combine_route_logits", _p(y_sorted), _p(pair_pos), _p(topk_w), _p(shared_out),
+          _p(shared_scale), _p(residual), k, H, _p(out), _p(norm_out), float(norm_eps),
+          _p(w_router), _p(w_shared_gate), E, _p(logits), _s(stream))
+    return out, norm_out, logits
 
 
 def expert_stage_async(dst: torch.Tensor, src_pinned: torch.Tensor, side_stream=None,

@@ -26,8 +26,8 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (expert_stage_async, f16_expert_table, moe_combine, moe_draft_route_ffn,
-               moe_gather, moe_route_plan,
+from . import (expert_stage_async, f16_expert_table, moe_combine, moe_combine_route_logits,
+               moe_draft_route_ffn, moe_gather, moe_route_plan,
                moe_route_topk, new_workspace, verify_grouped_gemm, w4_expert_table,
                w4a16_grouped_ffn)
 
@@ -73,6 +73,8 @@ class _StepBuffers:
         self.offs = torch.tensor([0, T], dtype=i32, device=dev)
         self.out = [torch.empty((T, H), dtype=f16, device=dev) for _ in range(2)]
         self.xn = [torch.empty((T, H), dtype=f16, device=dev) for _ in range(2)]
+        # router logits of the next layer (draft chain, one token)
+        self.next_lg = torch.empty(E + 1, dtype=f32, device=dev)
 
 
 def top_resident(counts: np.ndarray, n: int) -> List[int]:
@@ -186,12 +188,17 @@ class ChunkEngine:
         if record is not None:
             record.append(dict(layer=l, x=x, xn=xn, ids=ids.clone(), out=out, xn_next=xn_next))
 
-    def draft_step(self, x: torch.Tensor, record: Optional[list] = None) -> torch.Tensor:
+    def draft_step(self, x: torch.Tensor, record: Optional[list] = None,
+                   fuse_combine: bool = True) -> torch.Tensor:
         """One INT4 draft decode step (T = 1) through all layers, counting each
-        layer's expert choices in the ELB table."""
+        layer's expert choices in the ELB table.  With fuse_combine, the
+        combine of layer l and the router logits of layer l+1 run as one
+        launch (moe_combine_route_logits), so a layer takes three launches
+        instead of four; outputs are bit-identical either way."""
         b = self.bufs(1)
         fresh = record is not None
         xn = x
+        lg = None
         for l, ly in enumerate(self.layers):
             # routing, ELB update and gather maps folded into the gate/up
             # launch, then the down projection; the FP16 shared expert's
@@ -204,10 +211,19 @@ class ChunkEngine:
                                       err_word=self.err, topk_ids=b.ids, topk_w=b.w,
                                       shared_gate=b.gate if ly.shared_gate is not None else None,
                                       maps=b.maps, y_sorted=b.y, shared=ly.shared,
-                                      shared_h=self.sh_h, shared_out=b.sh_out if has_sh else None)
+                                      shared_h=self.sh_h, shared_out=b.sh_out if has_sh else None,
+                                      logits=lg)
             gate = res[2]
             sh = res[5] if has_sh else None
-            out, xn_next = self._combine(l, b, b.y, sh, gate, x, fresh)
+            if fuse_combine and l < self.L - 1:
+                nxt = self.layers[l + 1]
+                out = None if fresh else b.out[l % 2]
+                xnn = None if fresh else b.xn[l % 2]
+                out, xn_next, lg = moe_combine_route_logits(
+                    b.y, b.maps["pair_pos"], b.w, nxt.router, sh, gate, x, nxt.shared_gate,
+                    out=out, norm_out=xnn, logits=b.next_lg)
+            else:
+                out, xn_next = self._combine(l, b, b.y, sh, gate, x, fresh)
             self._record(record, l, x, xn, b.ids, out, xn_next)
             x, xn = out, xn_next
         return x

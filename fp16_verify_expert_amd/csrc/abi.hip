@@ -343,8 +343,8 @@ smoe_status moe_draft_route_ffn(const uint16_t* x, const uint16_t* w_router,
                                 int32_t* n_active, uint16_t* y_sorted,
                                 const uint16_t* shared_w13, const uint16_t* shared_w2,
                                 int shared_I, uint16_t* shared_h, uint16_t* shared_out,
-                                void* workspace, size_t workspace_bytes, int32_t* err_word,
-                                void* stream) {
+                                const float* logits, void* workspace, size_t workspace_bytes,
+                                int32_t* err_word, void* stream) {
     REQUIRE(x && w_router && experts && topk_ids && topk_w && expert_offsets && sorted_token &&
                 sorted_pair && pair_pos && active && n_active && y_sorted,
             SMOE_ERR_NULL, "moe_draft_route_ffn: a required pointer is NULL");
@@ -373,9 +373,10 @@ smoe_status moe_draft_route_ffn(const uint16_t* x, const uint16_t* w_router,
             "moe_draft_route_ffn: k=%d exceeds 32", k);
     REQUIRE(!counters || (L >= 1 && layer >= 0 && layer < L), SMOE_ERR_SHAPE,
             "moe_draft_route_ffn: layer=%d must be in [0, L=%d)", layer, L);
-    REQUIRE(aligned(x, 16) && aligned(w_router, 16) && aligned(w_shared_gate, 16),
+    REQUIRE(aligned(x, 16) && aligned(w_router, 16) && aligned(w_shared_gate, 16) &&
+                aligned(logits, 4),
             SMOE_ERR_SHAPE,
-            "moe_draft_route_ffn: x, w_router, w_shared_gate must be 16-byte aligned");
+            "moe_draft_route_ffn: x, w_router, w_shared_gate must be 16-byte aligned (logits 4)");
     const size_t need = smoe::w4a16_workspace_bytes(1, k, H, I, E);
     REQUIRE(workspace && workspace_bytes >= need && aligned(workspace, 256), SMOE_ERR_WORKSPACE,
             "moe_draft_route_ffn: workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
@@ -388,9 +389,39 @@ smoe_status moe_draft_route_ffn(const uint16_t* x, const uint16_t* w_router,
                                      sorted_pair, pair_pos, active, n_active, experts, I,
                                      y_sorted, workspace, shared_w13,
                                      shared_w13 ? shared_w2 : nullptr, shared_w13 ? shared_I : 0,
-                                     shared_h, shared_out, err_word,
+                                     shared_h, shared_out, logits, err_word,
                                      static_cast<hipStream_t>(stream)),
         "moe_draft_route_ffn launch");
+}
+
+smoe_status moe_combine_route_logits(const uint16_t* y_sorted, const int32_t* pair_pos,
+                                     const float* topk_w, const uint16_t* shared_out,
+                                     const float* shared_scale, const uint16_t* residual, int k,
+                                     int H, uint16_t* out, uint16_t* norm_out, float norm_eps,
+                                     const uint16_t* w_router, const uint16_t* w_shared_gate,
+                                     int E, float* logits, void* stream) {
+    REQUIRE(y_sorted && pair_pos && topk_w && out && norm_out && w_router && logits,
+            SMOE_ERR_NULL,
+            "moe_combine_route_logits: y_sorted, pair_pos, topk_w, out, norm_out, w_router and "
+            "logits are required");
+    REQUIRE(k >= 1 && k <= 256, SMOE_ERR_SHAPE, "moe_combine_route_logits: k=%d must be in [1, 256]",
+            k);
+    REQUIRE(E >= 1 && E <= 256, SMOE_ERR_SHAPE, "moe_combine_route_logits: E=%d must be in [1, 256]",
+            E);
+    REQUIRE(H > 0 && H % 128 == 0 && smoe::combine_logits_supported(H), SMOE_ERR_SHAPE,
+            "moe_combine_route_logits: H=%d must be a multiple of 128 and at most 8192", H);
+    REQUIRE(aligned(y_sorted, 16) && aligned(shared_out, 16) && aligned(residual, 16) &&
+                aligned(out, 16) && aligned(norm_out, 16) && aligned(w_router, 16) &&
+                aligned(w_shared_gate, 16),
+            SMOE_ERR_SHAPE, "moe_combine_route_logits: fp16 tensors must be 16-byte aligned");
+    REQUIRE(norm_eps >= 0.0f && norm_out != out, SMOE_ERR_SHAPE,
+            "moe_combine_route_logits: norm_eps must be >= 0 and norm_out must not alias out");
+    CHECK_DEVICE();
+    return hip_result(smoe::launch_combine_logits(y_sorted, pair_pos, topk_w, shared_out,
+                                                  shared_scale, residual, k, H, out, norm_out,
+                                                  norm_eps, w_router, w_shared_gate, E, logits,
+                                                  static_cast<hipStream_t>(stream)),
+                      "moe_combine_route_logits launch");
 }
 
 smoe_status verify_grouped_gemm(const uint16_t* x, const int32_t* sorted_token,

@@ -68,7 +68,8 @@ hipError_t launch_draft_route_ffn(const uint16_t* x, const uint16_t* wr, const u
                                   int32_t* sp, int32_t* pp, int32_t* active, int32_t* n_active,
                                   const smoe_w4_expert* experts, int I, uint16_t* y, void* ws,
                                   const uint16_t* sw13, const uint16_t* sw2, int Is,
-                                  uint16_t* sh_h, uint16_t* sh_out, int32_t* err, hipStream_t s);
+                                  uint16_t* sh_h, uint16_t* sh_out, const float* logits_in,
+                                  int32_t* err, hipStream_t s);
 bool w4a16_shape_supported(int H, int I);
 hipError_t launch_verify_ffn(const uint16_t* x, const int32_t* sorted_token, const int32_t* off,
                              const int32_t* active, const int32_t* n_active,
@@ -87,6 +88,12 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* pp, const float* w,
                           const uint16_t* shared, const float* sscale, const uint16_t* resid,
                           int T, int k, int H, uint16_t* out, uint16_t* norm_out, float eps,
                           hipStream_t s);
+bool combine_logits_supported(int H);
+hipError_t launch_combine_logits(const uint16_t* y, const int32_t* pp, const float* w,
+                                 const uint16_t* shared, const float* sscale,
+                                 const uint16_t* resid, int k, int H, uint16_t* out,
+                                 uint16_t* norm_out, float eps, const uint16_t* wr,
+                                 const uint16_t* wsg, int E, float* lg, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks,
                               hipStream_t s);
 }  // namespace smoe

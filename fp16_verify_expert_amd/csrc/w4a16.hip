@@ -1525,17 +1525,24 @@ hipError_t launch_draft_route_ffn(const uint16_t* x, const uint16_t* wr, const u
                                   int32_t* sp, int32_t* pp, int32_t* active, int32_t* n_active,
                                   const smoe_w4_expert* experts, int I, uint16_t* y, void* ws,
                                   const uint16_t* sw13, const uint16_t* sw2, int Is,
-                                  uint16_t* sh_h, uint16_t* sh_out, int32_t* err, hipStream_t s) {
+                                  uint16_t* sh_h, uint16_t* sh_out, const float* logits_in,
+                                  int32_t* err, hipStream_t s) {
     const int nvec = E + (wsg ? 1 : 0);
     uint16_t* h = static_cast<uint16_t*>(ws);
     SlotDesc* desc = reinterpret_cast<SlotDesc*>(static_cast<char*>(ws) + h_bytes(1, k, I));
-    float* logits = reinterpret_cast<float*>(static_cast<char*>(ws) + h_bytes(1, k, I) +
+    const float* logits = logits_in;
+    if (!logits) {
+        // the token's router logits, one wave per router row (the caller
+        // passes them when an earlier launch computed them)
+        float* lg = reinterpret_cast<float*>(static_cast<char*>(ws) + h_bytes(1, k, I) +
                                              desc_bytes(1, k, E));
-    constexpr int kLogitWaves = 4;
-    route_logits_kernel<<<dim3((nvec + kLogitWaves - 1) / kLogitWaves), dim3(64 * kLogitWaves),
-                          0, s>>>(x, wr, wsg, H, E, nvec, logits);
-    hipError_t e0 = hipGetLastError();
-    if (e0 != hipSuccess) return e0;
+        constexpr int kLogitWaves = 4;
+        route_logits_kernel<<<dim3((nvec + kLogitWaves - 1) / kLogitWaves),
+                              dim3(64 * kLogitWaves), 0, s>>>(x, wr, wsg, H, E, nvec, lg);
+        hipError_t e0 = hipGetLastError();
+        if (e0 != hipSuccess) return e0;
+        logits = lg;
+    }
     const PhasePlan p1 = plan_phase(1, k, 1, H, 2 * I, I, 1, 4);
     const W4Args a1 = phase_args(p1, x, st, off, active, n_active, experts, H, 2 * I, I, 1, E, h,
                                  err, desc);

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SMOE_ABI_VERSION 3
+#define SMOE_ABI_VERSION 4
 
 typedef enum {
     SMOE_OK = 0,
@@ -307,6 +307,11 @@ smoe_status wq_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
  *                  shared_w13 NULL = no shared expert (the other four are then
  *                  ignored).  Several shared experts of one layer pass as one
  *                  of their summed intermediate.
+ *   logits         fp32 [E] (+1 with w_shared_gate: the gate's logit last),
+ *                  optional: the router logits of x in the pinned order, as
+ *                  moe_combine_route_logits writes them; when given the call
+ *                  takes them instead of computing them (two launches) and
+ *                  every output is the same as without.  NULL: computed here.
  *   workspace      >= smoe_workspace_bytes(0, 1, k, H, I, E) bytes,
  *                  256-byte aligned
  * Limits: k <= 32, E <= 256, H and I at most 16384; with a shared expert,
@@ -324,8 +329,33 @@ smoe_status moe_draft_route_ffn(const uint16_t* x, const uint16_t* w_router,
                                 int32_t* n_active, uint16_t* y_sorted,
                                 const uint16_t* shared_w13, const uint16_t* shared_w2,
                                 int shared_I, uint16_t* shared_h, uint16_t* shared_out,
-                                void* workspace, size_t workspace_bytes, int32_t* err_word,
-                                void* stream);
+                                const float* logits, void* workspace, size_t workspace_bytes,
+                                int32_t* err_word, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_combine_route_logits -- one token (T = 1): moe_combine of a layer's
+ * expert outputs with its norm epilogue, and in the same launch the next
+ * layer's router logits of the normalised row ([S1] Key Contributions 4:
+ * fewer launches per draft step; in a chain of pre-norm layers the combine
+ * of layer l and the routing of layer l+1 read the same row).
+ *
+ *   y_sorted, pair_pos, topk_w, shared_out, shared_scale, residual, k, H,
+ *   out, norm_out, norm_eps: moe_combine with T = 1 (norm_out required);
+ *                  out and norm_out are bit-identical to moe_combine's
+ *   w_router       fp16 [E, H] router of the next layer
+ *   w_shared_gate  fp16 [H] optional shared-expert gate row of that layer
+ *   logits         fp32 [E] (+1 with w_shared_gate) out: the pinned-order
+ *                  logits of norm_out, bit-identical to those
+ *                  moe_draft_route_ffn computes from norm_out (pass them to
+ *                  it as its logits argument)
+ * Limits: H a multiple of 128, at most 8192; 1 <= k, E <= 256.
+ * ---------------------------------------------------------------------- */
+smoe_status moe_combine_route_logits(const uint16_t* y_sorted, const int32_t* pair_pos,
+                                     const float* topk_w, const uint16_t* shared_out,
+                                     const float* shared_scale, const uint16_t* residual, int k,
+                                     int H, uint16_t* out, uint16_t* norm_out, float norm_eps,
+                                     const uint16_t* w_router, const uint16_t* w_shared_gate,
+                                     int E, float* logits, void* stream);
 
 /* ------------------------------------------------------------------------
  * verify_grouped_gemm -- FP16 SwiGLU FFN of the target experts over the

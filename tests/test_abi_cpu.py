@@ -19,7 +19,7 @@ def test_exports_every_header_function():
     names = fve.header_functions()
     expected = {"smoe_abi_version", "smoe_last_error", "moe_route_topk", "elb_count",
                 "moe_gather", "moe_route_plan", "w4a16_grouped_ffn", "wq_grouped_ffn",
-                "moe_draft_route_ffn", "w4a16_grouped_ffn_noalloc",
+                "moe_draft_route_ffn", "w4a16_grouped_ffn_noalloc", "moe_combine_route_logits",
                 "verify_grouped_gemm", "moe_combine",
                 "expert_stage_async", "smoe_workspace_bytes", "smoe_stream_read"}
     assert set(names) == expected
@@ -146,10 +146,10 @@ def test_draft_route_ffn_validation():
 
     def call(x=FAKE, wr=FAKE, wsg=None, H=256, I=512, E=8, k=2, layer=0, Lc=1, counters=FAKE,
              table=FAKE, gs=128, gate=None, mp=None, y=FAKE, ws=FAKE, wsb=None,
-             sh=(None, None, 0, None, None)):
+             sh=(None, None, 0, None, None), lg=None):
         m = maps if mp is None else mp
         return L.moe_draft_route_ffn(x, wr, wsg, H, I, E, k, 0, layer, Lc, counters, table, gs,
-                                     FAKE, FAKE, gate, *m, y, *sh, ws,
+                                     FAKE, FAKE, gate, *m, y, *sh, lg, ws,
                                      need if wsb is None else wsb, None, None)
     assert call(x=None) == 1
     assert call(table=None) == 1
@@ -173,6 +173,29 @@ def test_draft_route_ffn_validation():
     assert call(sh=(FAKE, FAKE, 8320, FAKE, FAKE)) == 2 and "8192" in _err()
     assert call(sh=(FAKE, FAKE, 1024, V(0x1002), FAKE)) == 2 and "aligned" in _err()
     assert call(sh=(None, FAKE, 1000, None, None), wsb=need - 1) == 6  # ignored without shared_w13
+    # precomputed logits: checked like the other inputs (alignment), no device use here
+    assert call(lg=V(0x1002)) == 2 and "aligned" in _err()
+    assert call(lg=FAKE, ws=None) == 6
+
+
+def test_combine_route_logits_validation():
+    L = fve.lib()
+
+    def call(y=FAKE, pp=FAKE, w=FAKE, sh=None, sc=None, res=None, k=2, H=256, out=FAKE,
+             nrm=V(0x2000), eps=1e-6, wr=FAKE, wsg=None, E=8, lg=FAKE):
+        return L.moe_combine_route_logits(y, pp, w, sh, sc, res, k, H, out, nrm, eps, wr, wsg, E,
+                                          lg, None)
+    assert call(y=None) == 1
+    assert call(nrm=None) == 1
+    assert call(wr=None) == 1 and "w_router" in _err()
+    assert call(lg=None) == 1
+    assert call(k=0) == 2
+    assert call(E=257) == 2
+    assert call(H=200) == 2
+    assert call(H=8320) == 2 and "8192" in _err()
+    assert call(y=V(0x1002)) == 2 and "aligned" in _err()
+    assert call(nrm=FAKE) == 2                      # norm_out aliases out
+    assert call(eps=-1.0) == 2
 
 
 def test_w4a16_validation():

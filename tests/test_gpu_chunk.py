@@ -181,6 +181,32 @@ def test_chunk_draft_graph_matches_eager(chunk):
     eng.counters.copy_(saved)
 
 
+def test_chunk_draft_fused_combine_matches_four_launch_chain(chunk):
+    """The draft step with each layer's combine fused with the next layer's
+    router logits (three launches per layer) equals the four-launch chain bit
+    for bit: every layer's input, ids, output and normalised output, and the
+    ELB counts."""
+    s = chunk["shape"]
+    eng = chunk["eng"]
+    saved = eng.counters.clone()
+    for j in range(2):
+        x = torch.from_numpy(synth.tokens(s, 1, step=80 + j)).cuda()
+        eng.clear_counters()
+        ra = []
+        oa = eng.draft_step(x, ra, fuse_combine=False).clone()
+        ca = eng.counters.clone()
+        eng.clear_counters()
+        rb = []
+        ob = eng.draft_step(x, rb, fuse_combine=True).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob) and torch.equal(ca, eng.counters)
+        for a, b in zip(ra, rb):
+            for key in ("x", "xn", "ids", "out", "xn_next"):
+                assert torch.equal(a[key], b[key]), (j, a["layer"], key)
+    assert int(host(eng.err)[0]) == 0
+    eng.counters.copy_(saved)
+
+
 def test_chunk_forward_matches_draft_and_verify(chunk):
     """The any-T forward used by the route-fidelity probe runs the very same
     kernels: FP16 over 17 rows equals the all-resident verify bit for bit, and

@@ -496,6 +496,72 @@ def test_draft_route_ffn_shared_expert(shape, step):
     say(f"  shared l2={st['l2']:.2e} maxabs={st['maxabs']:.2e}")
 
 
+# The combine of one layer fused with the next layer's router logits.
+COMBINE_LOGITS_CASES = [(synth.TINY, 0), (synth.DS, 1), (synth.QWEN, 2), (synth.PHI, 3),
+                        (_E256, 4)]
+
+
+@pytest.mark.parametrize("shape,step", COMBINE_LOGITS_CASES,
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_combine_route_logits_matches_separate_calls(shape, step):
+    """moe_combine_route_logits: out and norm_out bit-identical to
+    moe_combine's; the logits bit-identical to the oracle's pinned-order fp32
+    logits of norm_out and to those moe_draft_route_ffn computes itself; and
+    the next layer's draft step from the passed logits bit-identical to the
+    step that computes them."""
+    say(f"combine + next logits {shape.name} step={step}")
+    E, k, H, I = shape.E, shape.k, shape.H, shape.I
+    g = synth.torch_layer(shape, 0, "cuda", int4=True)
+    g2 = synth.torch_layer(shape, 1, "cuda", int4=True)
+    t4, t4b = fve.w4_expert_table(g["int4"]), fve.w4_expert_table(g2["int4"])
+    sh = None if g["shared"] is None else (g["shared"]["w13"], g["shared"]["w2"])
+    gate = None if g["shared"] is None else g["shared"]["gate"]
+    sh2 = None if g2["shared"] is None else (g2["shared"]["w13"], g2["shared"]["w2"])
+    gate2 = None if g2["shared"] is None else g2["shared"]["gate"]
+    x = dev(synth.tokens(shape, 1, step=step))
+    err = _err()
+    ws = fve.new_workspace(0, 1, k, H, I, E)
+    res = fve.moe_draft_route_ffn(x, g["router"], k, t4, I, ws, shape.renormalize, gate,
+                                  err_word=err, shared=sh)
+    ids, w, gt, m, y = res[:5]
+    so = res[5] if sh is not None else None
+    out_r, xn_r = fve.moe_combine(y, m["pair_pos"], w, so, gt, x, norm_out=True)
+    out_f, xn_f, lg = fve.moe_combine_route_logits(y, m["pair_pos"], w, g2["router"], so, gt, x,
+                                                   gate2)
+    torch.cuda.synchronize()
+    assert torch.equal(out_f, out_r) and torch.equal(xn_f, xn_r)
+    ref_lg = oracle.logits_pinned_f32(host(xn_r), host(g2["router"]))[0]
+    nv = E + (1 if gate2 is not None else 0)
+    assert lg.shape[0] == nv
+    assert np.array_equal(host(lg)[:E].view(np.uint32), ref_lg.view(np.uint32))
+    if gate2 is not None:
+        ref_g = oracle.logits_pinned_f32(host(xn_r), host(gate2))
+        assert host(lg)[E].view(np.uint32) == np.float32(ref_g[0]).view(np.uint32)
+    # the next layer's draft step with and without the passed logits
+    c1 = torch.zeros((1, E), dtype=torch.int32, device="cuda")
+    c2 = torch.zeros((1, E), dtype=torch.int32, device="cuda")
+    wsa = fve.new_workspace(0, 1, k, H, I, E)
+    wsb = fve.new_workspace(0, 1, k, H, I, E)
+    ra = fve.moe_draft_route_ffn(xn_r, g2["router"], k, t4b, I, wsa, shape.renormalize, gate2,
+                                 counters=c1, err_word=err, shared=sh2)
+    rb = fve.moe_draft_route_ffn(xn_f, g2["router"], k, t4b, I, wsb, shape.renormalize, gate2,
+                                 counters=c2, err_word=err, shared=sh2, logits=lg)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) == 0
+    # the logits the step computed itself sit in its workspace after h and the slot table
+    off = ((k * I * 2 + 255) // 256) * 256 + ((min(E, k) * 32 + 255) // 256) * 256
+    own = wsa[off:off + 4 * nv].view(torch.float32)
+    assert torch.equal(own, lg)
+    assert torch.equal(ra[0], rb[0]) and torch.equal(ra[1], rb[1]) and torch.equal(c1, c2)
+    if gate2 is not None:
+        assert torch.equal(ra[2], rb[2])
+    for key in ("offsets", "active", "n_active"):
+        assert torch.equal(ra[3][key], rb[3][key]), key
+    assert torch.equal(ra[4][:k], rb[4][:k])
+    if sh2 is not None:
+        assert torch.equal(ra[5], rb[5])
+
+
 VERIFY_CASES = [(synth.TINY, 17), (synth.TINY, 40), (synth.QWEN, 9), (synth.PHI, 17),
                 (synth.DS, 16),
                 # T <= 4: the one-wave-per-column kernel (1, 2 and 4 rows per block)
