@@ -550,11 +550,20 @@ def bench_draft_formats(args):
     for shape, Ts in ((synth.PHI, (1,)), (synth.DS, (1, 4, 16))):
         f16 = [synth.expert_f16(shape, 0, e) for e in range(shape.E)]
         router = up(synth.router(shape))
-        for bits in (2, 4, 8):
-            q = [synth.expert_int4(w13, w2, bits) for w13, w2 in f16]
+        for fmt in (2, 4, 8, "awq4"):
+            awq = fmt == "awq4"
+            bits = 4 if awq else fmt
+            if awq:
+                q = [synth.expert_awq(shape, 0, e, w13, w2) for e, (w13, w2) in enumerate(f16)]
+            else:
+                q = [synth.expert_int4(w13, w2, bits) for w13, w2 in f16]
             gq = [{key: tuple(up(t) for t in ex[key]) for key in ("w13", "w2")} for ex in q]
             table = fve.w4_expert_table(gq)
-            bpe = synth.quant_bytes_per_expert(shape, bits)
+            sc = [(up(ex["a13"]), up(ex["a2"])) for ex in q] if awq else None
+            stab = fve.awq_scale_table(sc) if awq else None
+            # codes + scales + zeros (+ the fp16 input-channel factors of AWQ)
+            bpe = synth.quant_bytes_per_expert(shape, bits) + (
+                2 * (shape.H + shape.I) if awq else 0)
             for T in Ts:
                 xs = [up(synth.tokens(shape, T, step=i)) for i in range(POOL)]
                 ws = fve.new_workspace(0, T, shape.k, shape.H, shape.I, shape.E)
@@ -571,8 +580,12 @@ def bench_draft_formats(args):
                     ids, w, _, m = fve.moe_route_plan(x, router, shape.k, topk_ids=ids_b,
                                                       topk_w=w_b, maps=maps_b, logits_ws=lg_b)
                     if ev: ev[0].record()
-                    fve.wq_grouped_ffn(x, m, table, T, shape.k, shape.H, shape.I, shape.E, ws,
-                                       bits, y_sorted=y)
+                    if awq:
+                        fve.awq_grouped_ffn(x, m, table, stab, T, shape.k, shape.H, shape.I,
+                                            shape.E, ws, y_sorted=y)
+                    else:
+                        fve.wq_grouped_ffn(x, m, table, T, shape.k, shape.H, shape.I, shape.E,
+                                           ws, bits, y_sorted=y)
                     if ev: ev[1].record()
                     fve.moe_combine(y, m["pair_pos"], w, out=out)
                     return m
@@ -596,7 +609,8 @@ def bench_draft_formats(args):
                 step_ms = sum(a.elapsed_time(b) for a, b in ph)
                 ffn_ms = sum(a.elapsed_time(b) for a, b in kf)
                 results.append({
-                    "shape": shape.name, "bits": bits, "T": T,
+                    "shape": shape.name, "bits": bits, "format": "awq" if awq else "gptq",
+                    "T": T,
                     "touched_experts_avg": round(sum(touched[i] for i in idx) / K, 2),
                     "weight_bytes_avg": round(nbytes / K),
                     "step_us": round(1e3 * step_ms / K, 2),
@@ -605,16 +619,18 @@ def bench_draft_formats(args):
                     "ffn_gbps": round(nbytes / (ffn_ms * 1e-3) / 1e9, 1),
                     "ffn_frac_hbm": round(nbytes / (ffn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
                 print(json.dumps(results[-1]), file=sys.stderr, flush=True)
-            del gq, table
+            del gq, table, sc, stab
             torch.cuda.empty_cache()
     phi4 = next(r for r in results if r["shape"] == synth.PHI.name and r["bits"] == 4)
     out = {"metric": "draft step weight GB/s by code width", "value": phi4["step_gbps"],
            "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
            "higher_is_better": True, "vs_baseline": None,
-           "dtype": "int2/int4/int8-w (GPTQ layout, g128), fp16-a; fp32 accumulate",
+           "dtype": "int2/int4/int8-w (GPTQ layout, g128; AWQ-style int4 with fp16 input-channel "
+                    "divisors), fp16-a; fp32 accumulate",
            "data": "synthetic (seeded N(0,0.02) fp16 experts, RTN at each width, N(0,1) tokens)",
-           "config": {"workload": "draft_formats: one draft step (route plan, wq_grouped_ffn, "
-                                  "combine) at 2/4/8 bits; phi35 T=1, ds_v2_lite T=1/4/16"},
+           "config": {"workload": "draft_formats: one draft step (route plan, wq_grouped_ffn or "
+                                  "awq_grouped_ffn, combine) at 2/4/8 bits and AWQ-style 4 "
+                                  "bits; phi35 T=1, ds_v2_lite T=1/4/16"},
            "results": results, "run_s": round(time.perf_counter() - t_all, 1)}
     print(json.dumps(out), flush=True)
 

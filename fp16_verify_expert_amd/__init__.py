@@ -50,6 +50,8 @@ _SIGS = {
                                _sz, _vp, _vp]),
     "w4a16_grouped_ffn_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
                                        _vp, _vp, _vp]),
+    "awq_grouped_ffn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp,
+                             _vp, _sz, _vp, _vp]),
     "wq_grouped_ffn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
                             _sz, _vp, _vp]),
     "moe_draft_route_ffn": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp,
@@ -276,6 +278,29 @@ def w4a16_grouped_ffn_noalloc(x, maps, table, T: int, k: int, H: int, I: int, E:
 
 
 NOALLOC_SCRATCH_BYTES = 4 << 20
+
+
+def awq_scale_table(scales: Sequence, device="cuda") -> torch.Tensor:
+    """Device array of 2E fp16 pointers from per-expert (a13 [H], a2 [I])
+    CUDA tensors (None = absent)."""
+    rows = []
+    for sc in scales:
+        rows += [0, 0] if sc is None else [sc[0].data_ptr(), sc[1].data_ptr()]
+    return torch.tensor(rows, dtype=torch.int64).to(device)
+
+
+def awq_grouped_ffn(x, maps, table, scale_table, T: int, k: int, H: int, I: int, E: int,
+                    workspace, *, y_sorted=None, err_word=None, stream=None):
+    """w4a16_grouped_ffn for AWQ-style experts: per-input-channel divisors
+    (scale_table from awq_scale_table) applied to each projection's input."""
+    _check(x, torch.float16, "x")
+    if y_sorted is None:
+        y_sorted = torch.empty((max(T * k, 1), H), dtype=torch.float16, device=x.device)
+    _call("awq_grouped_ffn", _p(x), _p(maps["sorted_token"]), _p(maps["offsets"]),
+          _p(maps["active"]), _p(maps["n_active"]), _p(table), _p(scale_table), T, k, H, I, E,
+          128, _p(y_sorted), _p(workspace), workspace.numel() * workspace.element_size(),
+          _p(err_word), _s(stream))
+    return y_sorted
 
 
 def wq_grouped_ffn(x, maps, table, T: int, k: int, H: int, I: int, E: int, workspace,

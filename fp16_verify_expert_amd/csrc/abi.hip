@@ -309,6 +309,30 @@ smoe_status w4a16_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
     return st;
 }
 
+smoe_status awq_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
+                            const int32_t* expert_offsets, const int32_t* active,
+                            const int32_t* n_active, const smoe_w4_expert* experts,
+                            const uint16_t* const* act_scales, int T, int k, int H, int I, int E,
+                            int group_size, uint16_t* y_sorted, void* workspace,
+                            size_t workspace_bytes, int32_t* err_word, void* stream) {
+    const char* name = "awq_grouped_ffn";
+    REQUIRE(act_scales, SMOE_ERR_NULL, "%s: act_scales is required", name);
+    smoe_status st = check_wq(name, x, sorted_token, expert_offsets, active, n_active, experts, T,
+                              k, H, I, E, 4, group_size, y_sorted);
+    if (st != SMOE_OK) return st;
+    if (T == 0) return ok();
+    const size_t need = smoe::w4a16_workspace_bytes(T, k, H, I, E);
+    REQUIRE(workspace && workspace_bytes >= need && aligned(workspace, 256), SMOE_ERR_WORKSPACE,
+            "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", name, need,
+            workspace_bytes);
+    CHECK_DEVICE();
+    return hip_result(smoe::launch_w4a16_ffn(x, sorted_token, expert_offsets, active, n_active,
+                                             experts, T, k, H, I, E, 4, y_sorted, workspace,
+                                             err_word, static_cast<hipStream_t>(stream),
+                                             act_scales),
+                      "awq_grouped_ffn launch");
+}
+
 smoe_status w4a16_grouped_ffn_noalloc(const uint16_t* x, const int32_t* sorted_token,
                                       const int32_t* expert_offsets, const int32_t* active,
                                       const int32_t* n_active, const smoe_w4_expert* experts,

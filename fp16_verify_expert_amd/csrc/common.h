@@ -56,7 +56,8 @@ hipError_t launch_gather(const int32_t* ids, int n, int k, int E, int32_t* off, 
 hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, const int32_t* off,
                             const int32_t* active, const int32_t* n_active,
                             const smoe_w4_expert* experts, int T, int k, int H, int I, int E,
-                            int bits, uint16_t* y, void* ws, int32_t* err, hipStream_t s);
+                            int bits, uint16_t* y, void* ws, int32_t* err, hipStream_t s,
+                            const uint16_t* const* ascale = nullptr);
 size_t w4a16_workspace_bytes(int T, int k, int H, int I, int E);
 // One-token draft step: the router logits, then routing, ELB, maps and the
 // gate/up projection in one launch, then the down projection; an optional

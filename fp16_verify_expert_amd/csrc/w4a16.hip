@@ -122,7 +122,39 @@ struct W4Args {
     SlotDesc* desc;  // one-token steps: per-slot down-projection matrices
     uint16_t* out;  // phase 1: h [rows, I]; phase 2: y [rows, H]
     int32_t* err;
+    // per-input-channel activation divisors (AWQ-style experts) or null:
+    // ascale[2 e] is expert e's fp16 [H] for w13, ascale[2 e + 1] its [I] for w2
+    const uint16_t* const* ascale;
 };
+
+SMOE_DEV const uint16_t* uniform_ptr_c(const uint16_t* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
+}
+
+// A chunk of 8 activations divided elementwise by the channels' divisors,
+// each quotient rounded to fp16 (AWQ-style experts: the weights were
+// quantised after scaling their input channels by these factors).
+SMOE_DEV uint4 div_chunk(uint4 x, uint4 sv) {
+    const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+    const uint32_t ss[4] = {sv.x, sv.y, sv.z, sv.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint16_t lo = f2h(h2f((uint16_t)(xs[i] & 0xFFFFu)) / h2f((uint16_t)(ss[i] & 0xFFFFu)));
+        const uint16_t hi = f2h(h2f((uint16_t)(xs[i] >> 16)) / h2f((uint16_t)(ss[i] >> 16)));
+        o[i] = (uint32_t)lo | ((uint32_t)hi << 16);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// The activation divisors of expert e for projection PHASE (null without).
+template <int PHASE>
+SMOE_DEV const uint16_t* expert_ascale(const W4Args& a, int e) {
+    return a.ascale ? uniform_ptr_c(a.ascale[2 * e + (PHASE - 1)]) : nullptr;
+}
 
 __device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
@@ -479,12 +511,15 @@ __device__ __forceinline__ void finish_rows(uint4* xs, float4* sums, int nrows, 
 // dot2 pairs, then their per-class sums.
 template <int BITS, typename RowPtr>
 __device__ __forceinline__ void stage_rows(uint4* xs, float4* sums, int nrows, int K8, int G,
-                                           RowPtr src_row) {
+                                           RowPtr src_row, const uint16_t* as = nullptr) {
+    const uint4* as4 = reinterpret_cast<const uint4*>(as);
 #pragma unroll 1
     for (int idx = threadIdx.x; idx < nrows * K8; idx += blockDim.x) {
         const int j = idx / K8;
         const int rr = idx - j * K8;
-        xs[j * K8 + rr] = permute_chunk<BITS>(src_row(j)[rr]);
+        uint4 v = src_row(j)[rr];
+        if (as4) v = div_chunk(v, as4[rr]);
+        xs[j * K8 + rr] = permute_chunk<BITS>(v);
     }
     finish_rows<BITS>(xs, sums, nrows, K8, G);
 }
@@ -551,6 +586,18 @@ __device__ __forceinline__ void run_groups(GroupLoad<BITS>& cur, int g, int nslo
 
 constexpr int kRowChunksPerThread = 8;  // activation chunks per thread requested early
 constexpr int kSpecTable = 64;          // experts whose descriptors are read speculatively
+
+// Request the first kRowChunksPerThread chunks of an activation row per
+// thread.  The requests are unconditional (indexes past the row repeat its
+// last chunk) so that the number of loads in flight is static and a later
+// wait for older loads does not also wait for the row.
+SMOE_DEV void request_row(const uint4* row4, int K8, uint4 (&xv)[kRowChunksPerThread]) {
+#pragma unroll
+    for (int u = 0; u < kRowChunksPerThread; ++u) {
+        const int idx = threadIdx.x + u * (int)blockDim.x;
+        xv[u] = row4[idx < K8 ? idx : K8 - 1];
+    }
+}
 
 SMOE_DEV const void* bcast_ptr(const void* p, int src_lane) {
     const uint64_t v = reinterpret_cast<uint64_t>(p);
@@ -701,7 +748,8 @@ SMOE_DEV void reduce_store_t1(const W4Args& a, float* red, float (&acc)[1][4], i
 // consumed, so every wait is for one group while the next is in flight.
 template <int BITS, int PHASE, int LPR, int NG>
 SMOE_DEV void one_token_block(const W4Args& a, const W4Lds& l, const smoe_w4_mat& wm,
-                              const uint4 (&xv)[kRowChunksPerThread], int slot, int cb) {
+                              uint4 (&xv)[kRowChunksPerThread], int slot, int cb,
+                              const uint16_t* as = nullptr) {
     static_assert(NG >= 1 && NG <= 4, "groups per slot");
     constexpr int RPL = 64 / LPR;
     constexpr int NB = 4 * LPR;
@@ -717,9 +765,16 @@ SMOE_DEV void one_token_block(const W4Args& a, const W4Lds& l, const smoe_w4_mat
     const bool colok = col < N;
     const int zsh = zero_shift<BITS>(col);
     const Masks<BITS> mk;
-    if (!wm.qweight || !wm.scales || !wm.qzeros) {
+    if (!wm.qweight || !wm.scales || !wm.qzeros || (a.ascale && !as)) {
         if (tid == 0 && cb == 0) flag_error(a.err, SMOE_DERR_NULL_EXPERT);
         return;
+    }
+    if (as) {
+        // AWQ-style divisors: requested with the row, before any weight
+        uint4 sv[kRowChunksPerThread];
+        request_row(reinterpret_cast<const uint4*>(as), K8, sv);
+#pragma unroll
+        for (int u = 0; u < kRowChunksPerThread; ++u) xv[u] = div_chunk(xv[u], sv[u]);
     }
     const W4Src src = make_src<BITS>(wm, K, N);
     const int g0 = myslot;
@@ -748,18 +803,6 @@ SMOE_DEV void one_token_block(const W4Args& a, const W4Lds& l, const smoe_w4_mat
     if (NG >= 3) step_if<BITS>(A, l, g0 + 2 * nslots, G, K8, zsh, mk, acc);
     if (NG >= 4) step_if<BITS>(B, l, g0 + 3 * nslots, G, K8, zsh, mk, acc);
     reduce_store_t1<PHASE, LPR>(a, l.red, acc, q, cb, slot);
-}
-
-// Request the first kRowChunksPerThread chunks of an activation row per
-// thread.  The requests are unconditional (indexes past the row repeat its
-// last chunk) so that the number of loads in flight is static and a later
-// wait for older loads does not also wait for the row.
-SMOE_DEV void request_row(const uint4* row4, int K8, uint4 (&xv)[kRowChunksPerThread]) {
-#pragma unroll
-    for (int u = 0; u < kRowChunksPerThread; ++u) {
-        const int idx = threadIdx.x + u * (int)blockDim.x;
-        xv[u] = row4[idx < K8 ? idx : K8 - 1];
-    }
 }
 
 // Occupancy of the one-token kernels: four waves per SIMD with one group per
@@ -815,21 +858,23 @@ __attribute__((amdgpu_waves_per_eu(w4_waves_per_eu<MAXM, NG>()))) void w4_kernel
             }
             if (cb == 0) write_slot_desc(a, spec, slot, e);
             if (e < 0) return;
-            one_token_block<BITS, 1, LPR, NG>(a, l, pick_mat<1>(a, spec, e), xv, slot, cb);
+            one_token_block<BITS, 1, LPR, NG>(a, l, pick_mat<1>(a, spec, e), xv, slot, cb,
+                                              expert_ascale<1>(a, e));
         } else {
             const SlotDesc d = a.desc[slot];
             request_row(row4, K8, xv);
             if (d.e < 0) return;
-            one_token_block<BITS, 2, LPR, NG>(a, l, d.w2, xv, slot, cb);
+            one_token_block<BITS, 2, LPR, NG>(a, l, d.w2, xv, slot, cb, expert_ascale<2>(a, d.e));
         }
         return;
     } else {
         const int e = a.active[slot];  // -1 past the touched experts
         if (e < 0) return;
         const smoe_w4_mat wm = (PHASE == 1) ? a.experts[e].w13 : a.experts[e].w2;
+        const uint16_t* as = expert_ascale<PHASE>(a, e);
         const int r0 = a.off[e];
         const int r1 = a.off[e + 1];
-        if (!wm.qweight || !wm.scales || !wm.qzeros) {
+        if (!wm.qweight || !wm.scales || !wm.qzeros || (a.ascale && !as)) {
             if (tid == 0 && cb == 0) flag_error(a.err, SMOE_DERR_NULL_EXPERT);
             return;
         }
@@ -841,7 +886,7 @@ __attribute__((amdgpu_waves_per_eu(w4_waves_per_eu<MAXM, NG>()))) void w4_kernel
         if (direct)
             stage_rows<BITS>(xs, sums, a.T, K8, G, [&](int j) {
                 return reinterpret_cast<const uint4*>(a.xin + (size_t)j * K);
-            });
+            }, as);
         for (int mc = r0; mc < r1; mc += a.MCH) {
             const int M = min(a.MCH, r1 - mc);
             int xrow[MAXM];
@@ -853,11 +898,11 @@ __attribute__((amdgpu_waves_per_eu(w4_waves_per_eu<MAXM, NG>()))) void w4_kernel
                     stage_rows<BITS>(xs, sums, M, K8, G, [&](int j) {
                         return reinterpret_cast<const uint4*>(a.xin +
                                                               (size_t)a.sorted_token[mc + j] * K);
-                    });
+                    }, as);
                 else
                     stage_rows<BITS>(xs, sums, M, K8, G, [&](int j) {
                         return reinterpret_cast<const uint4*>(a.xin + (size_t)(mc + j) * K);
-                    });
+                    }, as);
             }
             GroupLoad<BITS> cur;
             const int g = myslot;
@@ -1460,7 +1505,8 @@ W4Args phase_args(const PhasePlan& p, const uint16_t* xin, const int32_t* sorted
 hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, const int32_t* off,
                             const int32_t* active, const int32_t* n_active,
                             const smoe_w4_expert* experts, int T, int k, int H, int I, int E,
-                            int bits, uint16_t* y, void* ws, int32_t* err, hipStream_t s) {
+                            int bits, uint16_t* y, void* ws, int32_t* err, hipStream_t s,
+                            const uint16_t* const* ascale) {
     const int rows = T * k;
     const int slots = E < rows ? E : rows;
     // an expert holds at most T rows; one-token kernels unless a slot would
@@ -1475,7 +1521,9 @@ hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, cons
     }
     uint16_t* h = static_cast<uint16_t*>(ws);
     SlotDesc* desc = reinterpret_cast<SlotDesc*>(static_cast<char*>(ws) + h_bytes(T, k, I));
-    if (maxm > 1 && bits == 4 && SMOE_W4_MFMA) {
+    // multi-row 4-bit steps take the MFMA kernel, except with AWQ-style
+    // divisors (applied where the VALU kernels stage their rows)
+    if (maxm > 1 && bits == 4 && SMOE_W4_MFMA && !ascale) {
         const PhasePlan m1 = plan_mfma(1, T, H, 2 * I, I);
         const W4Args b1 = phase_args(m1, x, sorted_token, off, active, n_active, experts, H,
                                      2 * I, I, T, E, h, err, desc);
@@ -1490,12 +1538,14 @@ hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, cons
                            m2.lds, s, b2);
         return hipGetLastError();
     }
-    const W4Args a1 = phase_args(p1, x, sorted_token, off, active, n_active, experts, H, 2 * I, I,
-                                 T, E, h, err, desc);
+    W4Args a1 = phase_args(p1, x, sorted_token, off, active, n_active, experts, H, 2 * I, I, T, E,
+                           h, err, desc);
+    a1.ascale = ascale;
     hipError_t st = launch_any<1>(a1, slots, p1, maxm, bits, s);
     if (st != hipSuccess) return st;
-    const W4Args a2 =
+    W4Args a2 =
         phase_args(p2, h, nullptr, off, active, n_active, experts, I, H, I, T, E, y, err, desc);
+    a2.ascale = ascale;
     return launch_any<2>(a2, slots, p2, maxm, bits, s);
 }
 

@@ -255,6 +255,34 @@ smoe_status w4a16_grouped_ffn_noalloc(const uint16_t* x, const int32_t* sorted_t
                                       uint16_t* y_sorted, int32_t* err_word, void* stream);
 
 /* ------------------------------------------------------------------------
+ * awq_grouped_ffn -- w4a16_grouped_ffn for AWQ-style draft experts ([S1]
+ * Main Findings: the draft's routing fidelity is compared across GGUF, GPTQ
+ * and AWQ 4-bit copies).  An AWQ-style expert was quantised after each input
+ * channel c of a projection had been multiplied by a positive factor a[c]
+ * (chosen from activation statistics), so the product takes the activation
+ * divided by the same factor:
+ *   h = silu((x / a13) . Wg) * ((x / a13) . Wu),   y = (h / a2) . Wd,
+ * with W dequantised from the GPTQ layout of w4a16_grouped_ffn (same
+ * group 128, codes, scales and zeros).  Each quotient is rounded to fp16, as
+ * the activations are.
+ *
+ *   act_scales     device array of 2*E pointers: act_scales[2e] is expert
+ *                  e's fp16 [H] divisors of the gate/up input, act_scales[2e
+ *                  + 1] its fp16 [I] divisors of the down input (16-byte
+ *                  aligned, positive, finite; a touched expert with a NULL
+ *                  entry is skipped and flagged SMOE_DERR_NULL_EXPERT)
+ * Every other argument, output and limit is that of w4a16_grouped_ffn.
+ * Multi-row steps run the VALU kernels (the divisors are applied where those
+ * stage their rows), not the MFMA kernel of w4a16_grouped_ffn.
+ * ---------------------------------------------------------------------- */
+smoe_status awq_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
+                            const int32_t* expert_offsets, const int32_t* active,
+                            const int32_t* n_active, const smoe_w4_expert* experts,
+                            const uint16_t* const* act_scales, int T, int k, int H, int I, int E,
+                            int group_size, uint16_t* y_sorted, void* workspace,
+                            size_t workspace_bytes, int32_t* err_word, void* stream);
+
+/* ------------------------------------------------------------------------
  * wq_grouped_ffn -- w4a16_grouped_ffn for other draft code widths ([S1] Main
  * Findings and Future Directions: the draft's fidelity is compared across
  * quantisation precisions, 2-, 4- and 8-bit, and the precision is a design

@@ -35,6 +35,9 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
   expert_ffn_int4 .................. pinned (hand-packed one-hot closed form;
                                      equals expert_ffn_f16 on weights placed
                                      exactly on the quantisation grid)
+  expert_ffn_awq ................... pinned (unit factors give expert_ffn_int4
+                                     exactly; hand-packed one-hot closed form
+                                     with factors 2 and 4 on both inputs)
   grouped_ffn ...................... pinned (masked brute force; the grid
                                      identity above through the loop)
   moe_layer ........................ pinned (zero routed experts leave
@@ -60,7 +63,7 @@ CHUNK = 8           # consecutive hidden elements owned together by a lane
 __all__ = [
     "logits_pinned_f32", "logits_f64", "route_topk", "elb_update", "gather_maps",
     "unpack_gptq", "dequant_gptq", "silu", "swiglu_ffn", "expert_ffn_f16",
-    "expert_ffn_int4", "grouped_ffn", "per_token_ffn", "combine", "moe_layer",
+    "expert_ffn_int4", "expert_ffn_awq", "grouped_ffn", "per_token_ffn", "combine", "moe_layer",
     "to_f16", "rms_norm",
 ]
 
@@ -333,6 +336,26 @@ def expert_ffn_int4(xr: np.ndarray, q13, q2, dtype=np.float64, bits: int = 4):
     return swiglu_ffn(a, W13[:, :I], W13[:, I:], W2)
 
 
+def expert_ffn_awq(xr: np.ndarray, q13, q2, a13, a2, dtype=np.float64):
+    """AWQ-style INT4 draft expert on rows xr ([S1] Main Findings compare
+    AWQ, GPTQ and GGUF 4-bit drafts).  Reading R22: an AWQ-style expert was
+    quantised after input channel c of each projection had been multiplied
+    by a positive factor a[c]; the product then takes the activation divided
+    by that factor.  q13/q2 are GPTQ tensors of w13^T [H, 2I] and w2^T [I, H]
+    as in expert_ffn_int4; a13 [H] and a2 [I] the factors of the gate/up and
+    the down projection's inputs.
+      h = silu((x / a13) Wg) * ((x / a13) Wu);   y = (h / a2) Wd
+    """
+    W13 = dequant_gptq(*q13, dtype=dtype)   # [H, 2I]
+    W2 = dequant_gptq(*q2, dtype=dtype)     # [I, H]
+    I = W2.shape[0]
+    xa = np.asarray(xr).astype(dtype) / np.asarray(a13).astype(dtype)
+    g = xa @ W13[:, :I]
+    u = xa @ W13[:, I:]
+    h = silu(g) * u
+    return (h / np.asarray(a2).astype(dtype)) @ W2
+
+
 _QBITS = {"int2": 2, "int4": 4, "int8": 8}
 
 
@@ -344,7 +367,8 @@ def grouped_ffn(x: np.ndarray, maps: Dict[str, np.ndarray], experts: Sequence, k
     packed and that expert is applied to all of them at once.  Row r of the
     result holds FFN_e(x[sorted_token[r]]) for the expert e owning row r.
     `kind` is "int4" (experts[e] = dict(w13=(qw,s,qz), w2=(...))), "int2" /
-    "int8" (the same with 2/8-bit codes) or "f16" (experts[e] = (w13, w2)).
+    "int8" (the same with 2/8-bit codes), "awq" (the int4 dict with the
+    input-channel factors a13, a2 added) or "f16" (experts[e] = (w13, w2)).
     Rows of experts outside `only` stay NaN.
     """
     off = maps["offsets"]
@@ -358,7 +382,10 @@ def grouped_ffn(x: np.ndarray, maps: Dict[str, np.ndarray], experts: Sequence, k
         if r1 == r0 or (only is not None and e not in only):
             continue
         xr = x[st[r0:r1]]
-        if kind in _QBITS:
+        if kind == "awq":
+            ex = experts[e]
+            y[r0:r1] = expert_ffn_awq(xr, ex["w13"], ex["w2"], ex["a13"], ex["a2"], dtype)
+        elif kind in _QBITS:
             y[r0:r1] = expert_ffn_int4(xr, experts[e]["w13"], experts[e]["w2"], dtype,
                                        bits=_QBITS[kind])
         else:

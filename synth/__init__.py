@@ -37,7 +37,7 @@ BASE_SEED = 0
 GROUP = 128
 
 # tensor ids inside the seed key
-T_ROUTER, T_W13, T_W2, T_SH_W13, T_SH_W2, T_SH_GATE, T_TOKENS = range(7)
+T_ROUTER, T_W13, T_W2, T_SH_W13, T_SH_W2, T_SH_GATE, T_TOKENS, T_AWQ13, T_AWQ2 = range(9)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -185,6 +185,27 @@ def expert_int4(w13: np.ndarray, w2: np.ndarray, bits: int = 4):
     """Draft expert: GPTQ g128 (INT4 unless bits says 2 or 8) of the target's
     w13 and w2."""
     return dict(w13=gptq_from_linear(w13, bits), w2=gptq_from_linear(w2, bits))
+
+
+def awq_factors(key: Sequence[int], n: int) -> np.ndarray:
+    """Positive per-input-channel factors 2^u, u ~ U(-1, 1), rounded to fp16
+    (stand-ins for the activation-statistics factors AWQ chooses, which need
+    calibration data)."""
+    u = _rng(*key).uniform(-1.0, 1.0, n).astype(np.float32)
+    return np.exp2(u).astype(np.float16)
+
+
+def expert_awq(shape: LayerShape, layer: int, expert: int, w13: np.ndarray, w2: np.ndarray,
+               seed: int = BASE_SEED):
+    """AWQ-style draft expert: input channel c of w13 (hidden) and of w2
+    (intermediate) multiplied by its factor a[c] before the same RTN GPTQ
+    INT4 g128 quantisation; returns the GPTQ tensors and the factors
+    (a13 [H], a2 [I]), by which the kernels divide the activations."""
+    a13 = awq_factors((seed, shape.config_id, layer, expert, T_AWQ13, 0), w13.shape[1])
+    a2 = awq_factors((seed, shape.config_id, layer, expert, T_AWQ2, 0), w2.shape[1])
+    s13 = (w13.astype(np.float32) * a13.astype(np.float32)[None, :]).astype(np.float16)
+    s2 = (w2.astype(np.float32) * a2.astype(np.float32)[None, :]).astype(np.float16)
+    return dict(w13=gptq_from_linear(s13), w2=gptq_from_linear(s2), a13=a13, a2=a2)
 
 
 def quant_bytes_per_expert(shape: LayerShape, bits: int) -> int:

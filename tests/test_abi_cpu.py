@@ -20,6 +20,7 @@ def test_exports_every_header_function():
     expected = {"smoe_abi_version", "smoe_last_error", "moe_route_topk", "elb_count",
                 "moe_gather", "moe_route_plan", "w4a16_grouped_ffn", "wq_grouped_ffn",
                 "moe_draft_route_ffn", "w4a16_grouped_ffn_noalloc", "moe_combine_route_logits",
+                "awq_grouped_ffn",
                 "verify_grouped_gemm", "moe_combine",
                 "expert_stage_async", "smoe_workspace_bytes", "smoe_stream_read"}
     assert set(names) == expected
@@ -236,6 +237,23 @@ def test_w4a16_noalloc_validation():
     assert L.w4a16_grouped_ffn_noalloc(*args, 4, 2, 256, 512, 8, 128, None, None, None) == 1
     assert L.w4a16_grouped_ffn_noalloc(*args, -1, 2, 256, 512, 8, 128, FAKE, None, None) == 2
     assert L.w4a16_grouped_ffn_noalloc(*args, 0, 2, 256, 512, 8, 128, FAKE, None, None) == 0
+
+
+def test_awq_validation():
+    L = fve.lib()
+    args = [FAKE] * 6
+    need = L.smoe_workspace_bytes(0, 4, 2, 256, 512, 8)
+    assert L.awq_grouped_ffn(*args, None, 4, 2, 256, 512, 8, 128, FAKE, FAKE, need, None,
+                             None) == 1 and "act_scales" in _err()
+    assert L.awq_grouped_ffn(*args, FAKE, 4, 2, 256, 512, 8, 64, FAKE, FAKE, need, None,
+                             None) == 3
+    assert _err().startswith("awq_grouped_ffn")
+    assert L.awq_grouped_ffn(*args, FAKE, 4, 2, 256, 500, 8, 128, FAKE, FAKE, need, None,
+                             None) == 2
+    assert L.awq_grouped_ffn(*args, FAKE, 4, 2, 256, 512, 8, 128, FAKE, FAKE, need - 1, None,
+                             None) == 6
+    assert L.awq_grouped_ffn(*args, FAKE, 0, 2, 256, 512, 8, 128, FAKE, None, 0, None,
+                             None) == 0
 
 
 def test_stream_read_validation():

@@ -496,6 +496,77 @@ def test_draft_route_ffn_shared_expert(shape, step):
     say(f"  shared l2={st['l2']:.2e} maxabs={st['maxabs']:.2e}")
 
 
+# AWQ-style experts: per-input-channel divisors on both projections' inputs.
+AWQ_CASES = [(synth.TINY, 1), (synth.TINY, 4), (synth.TINY, 40), (synth.DS, 1), (synth.DS, 4),
+             (synth.PHI, 1), (synth.QWEN, 1)]
+
+
+def _awq_layer(shape, T, step):
+    L = _layer(shape, (T,), steps=(step,), f16=False)
+    ex = [None] * shape.E
+    for e in L.touched:
+        ex[e] = synth.expert_awq(shape, 0, e, *L.f16[e])
+    gpu = [None if a is None else {key: tuple(dev(t) for t in a[key]) for key in ("w13", "w2")}
+           for a in ex]
+    sc = [None if a is None else (dev(a["a13"]), dev(a["a2"])) for a in ex]
+    return L, ex, gpu, sc
+
+
+@pytest.mark.parametrize("shape,T", AWQ_CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_awq_grouped_ffn(shape, T):
+    say(f"awq {shape.name} T={T}")
+    E, k, H, I = shape.E, shape.k, shape.H, shape.I
+    step = 5
+    L, ex, gpu, sc = _awq_layer(shape, T, step)
+    table = fve.w4_expert_table(gpu)
+    stab = fve.awq_scale_table(sc)
+    x = synth.tokens(shape, T, step=step)
+    r = oracle.route_topk(x, L.router, k)
+    ref = oracle.grouped_ffn(x, oracle.gather_maps(r["ids"], E), ex, "awq")
+    dx = dev(x)
+    err = _err()
+    ids, _, _ = fve.moe_route_topk(dx, L.d_router, k)
+    gm = fve.moe_gather(ids, E, err)
+    ws = fve.new_workspace(0, T, k, H, I, E)
+    y = fve.awq_grouped_ffn(dx, gm, table, stab, T, k, H, I, E, ws, err_word=err)
+    y2 = fve.awq_grouped_ffn(dx, gm, table, stab, T, k, H, I, E, ws, err_word=err)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) == 0
+    rows = T * k
+    st = assert_fp16_close(host(y)[:rows], ref, f"awq {shape.name} T={T}")
+    assert torch.equal(y[:rows], y2[:rows])
+    say(f"  l2={st['l2']:.2e} maxabs={st['maxabs']:.2e}")
+
+
+def test_awq_unit_factors_are_w4a16_and_null_flagged():
+    """Unit divisors leave the one-token step bit-identical to
+    w4a16_grouped_ffn on the same codes; a touched expert without divisors is
+    skipped and flagged."""
+    s = synth.DS
+    E, k, H, I = s.E, s.k, s.H, s.I
+    L = _layer(s, (1,), steps=(0,), f16=False)
+    ones = (torch.ones(H, dtype=torch.float16, device="cuda"),
+            torch.ones(I, dtype=torch.float16, device="cuda"))
+    stab = fve.awq_scale_table([ones if e in L.touched else None for e in range(E)])
+    x = dev(synth.tokens(s, 1, step=0))
+    err = _err()
+    ids, _, _ = fve.moe_route_topk(x, L.d_router, k)
+    gm = fve.moe_gather(ids, E, err)
+    ws = fve.new_workspace(0, 1, k, H, I, E)
+    a = fve.awq_grouped_ffn(x, gm, L.t4, stab, 1, k, H, I, E, ws, err_word=err)
+    b = fve.w4a16_grouped_ffn(x, gm, L.t4, 1, k, H, I, E, ws, err_word=err)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) == 0
+    assert torch.equal(a[:k], b[:k])
+    # the first touched expert loses its divisors
+    first = int(host(ids).ravel().min())
+    stab2 = fve.awq_scale_table([ones if (e in L.touched and e != first) else None
+                                 for e in range(E)])
+    fve.awq_grouped_ffn(x, gm, L.t4, stab2, 1, k, H, I, E, ws, err_word=err)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) & fve.SMOE_DERR_NULL_EXPERT
+
+
 # The combine of one layer fused with the next layer's router logits.
 COMBINE_LOGITS_CASES = [(synth.TINY, 0), (synth.DS, 1), (synth.QWEN, 2), (synth.PHI, 3),
                         (_E256, 4)]

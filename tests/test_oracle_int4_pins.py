@@ -184,3 +184,67 @@ def test_layer_routed_plus_gated_shared_closed_form():
     assert np.isclose(y[H - 3], SILU_M1 * 4.0, rtol=1e-14, atol=0)
     assert np.isclose(y[3], SIGMOID_2 * SILU_1 * 2.0, rtol=1e-14, atol=0)
     assert np.isclose(out["route"]["gate"][0], SIGMOID_2, rtol=1e-15, atol=0)
+
+
+# silu at the points the AWQ one-hot case reaches, written out
+SILU_Q = 0.14054412522144952         # 0.25 / (1 + e^-0.25)
+SILU_MHALF = -0.1887703343990727     # -0.5 / (1 + e^0.5)
+
+
+def test_awq_unit_factors_equal_gptq_expert():
+    rng = np.random.default_rng(41)
+    H, I = 256, 128
+    m13, _ = _grid_matrix(rng, H, 2 * I)
+    m2, _ = _grid_matrix(rng, I, H)
+    x = rng.standard_normal((3, H)).astype(np.float16)
+    a = oracle.expert_ffn_awq(x, m13, m2, np.ones(H, np.float16), np.ones(I, np.float16))
+    b = oracle.expert_ffn_int4(x, m13, m2)
+    assert np.array_equal(a, b)
+
+
+def test_awq_one_hot_closed_form():
+    """The one-hot INT4 expert above with factor 2 on hidden channel 0 and 4
+    on intermediate channel 0: g = a/2, u = b/2, h = silu(g) u, and h_0 / 4
+    reaches output column H-1."""
+    H, I = 256, 128
+    m13, m2 = _one_hot_int4_expert(H, I)
+    a13 = np.full(H, 3.0, np.float16)
+    a13[0] = 2.0
+    a2 = np.ones(I, np.float16)
+    a2[0] = 4.0
+    x = np.zeros((1, H), np.float16)
+    x[0, 0] = 1.0
+    y = oracle.expert_ffn_awq(x, m13, m2, a13, a2)[0]
+    expect = np.zeros(H)
+    expect[H - 1] = SILU_HALF * 1.0 / 4.0      # g = 1/2, u = 2/2;  0.07780741640023182
+    expect[H - 2] = 0.0                         # silu(0) * 3/2
+    expect[H - 3] = SILU_MHALF * 2.0            # g = -1/2, u = 4/2; -0.3775406687981454
+    expect[H - 4] = SILU_Q * -0.5               # g = 1/4, u = -1/2; -0.07027206261072476
+    assert np.allclose(y, expect, rtol=1e-14, atol=1e-15)
+
+
+def test_awq_generator_approximates_target():
+    """The AWQ-style draft of a target expert: its codes are the RTN
+    quantisation of the input-channel-scaled weights (error within half a
+    step), and through the expert it still approximates the FP16 expert at
+    4-bit accuracy.  Random factors make it somewhat less accurate than the
+    plain GPTQ draft (scaled-up channels widen their groups' ranges); AWQ's
+    own factors come from activation statistics, which need data."""
+    import synth
+    s = synth.TINY
+    w13, w2 = synth.expert_f16(s, 0, 1)
+    ex = synth.expert_awq(s, 0, 1, w13, w2)
+    assert ex["a13"].shape == (s.H,) and ex["a2"].shape == (s.I,)
+    assert np.all(ex["a13"] >= 0.5) and np.all(ex["a13"] <= 2.0)
+    W = oracle.dequant_gptq(*ex["w13"])                        # [H, 2I]
+    scaled = w13.T.astype(np.float64) * ex["a13"].astype(np.float64)[:, None]
+    step = np.repeat(ex["w13"][1].astype(np.float64), 128, axis=0)
+    assert np.all(np.abs(W - scaled) <= 0.51 * step + 1e-3 * np.abs(scaled))
+    x = synth.tokens(s, 4, step=3)
+    ref = oracle.expert_ffn_f16(x, w13, w2)
+    a = oracle.expert_ffn_awq(x, ex["w13"], ex["w2"], ex["a13"], ex["a2"])
+    g = synth.expert_int4(w13, w2)
+    b = oracle.expert_ffn_int4(x, g["w13"], g["w2"])
+    ea = np.linalg.norm(a - ref) / np.linalg.norm(ref)
+    eb = np.linalg.norm(b - ref) / np.linalg.norm(ref)
+    assert ea < 0.5 and eb < 0.5 and ea < 2.5 * eb

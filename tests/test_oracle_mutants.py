@@ -75,6 +75,12 @@ MUTANTS = [
     ("shared expert dropped from the layer",
      "sh = expert_ffn_f16(x, shared[\"w13\"], shared[\"w2\"], dtype)",
      "sh = 0 * expert_ffn_f16(x, shared[\"w13\"], shared[\"w2\"], dtype)"),
+    ("AWQ factors multiplied instead of divided",
+     "xa = np.asarray(xr).astype(dtype) / np.asarray(a13).astype(dtype)",
+     "xa = np.asarray(xr).astype(dtype) * np.asarray(a13).astype(dtype)"),
+    ("AWQ down-input factors dropped",
+     "return (h / np.asarray(a2).astype(dtype)) @ W2",
+     "return h @ W2"),
     ("rms eps outside the root",
      "return a / np.sqrt(np.mean(a * a, axis=-1, keepdims=True) + eps)",
      "return a / (np.sqrt(np.mean(a * a, axis=-1, keepdims=True)) + eps)"),
