@@ -553,8 +553,49 @@ hipError_t launch_gemv_phase(const F16Args& a, int slots, hipStream_t s) {
 #define SMOE_VF_LONG 4
 #endif
 
+// One always-on group (a shared expert): waves per workgroup and ring depth
+// of each projection (gate/up, down).  Measured on the Qwen1.5-MoE shared
+// expert (intermediate 5632, 352 gate/up and 128 down workgroups; kernel
+// trace, weights from HBM): gate/up with 2 waves and 2 stages (48 KB of LDS,
+// three workgroups per CU, so all 352 start in one round) 12.3 us against
+// 15.2 us with 4 waves and 3 stages (144 KB: one per CU, a second round of
+// 96); the down projection stays at 4 waves and 3 stages (2, 6 or 8 waves,
+// 2 or 3 stages: no better).
+#ifndef SMOE_SH_GU_WAVES
+#define SMOE_SH_GU_WAVES 2
+#endif
+#ifndef SMOE_SH_GU_STAGES
+#define SMOE_SH_GU_STAGES 2
+#endif
+#ifndef SMOE_SH_DN_WAVES
+#define SMOE_SH_DN_WAVES 4
+#endif
+#ifndef SMOE_SH_DN_STAGES
+#define SMOE_SH_DN_STAGES 3
+#endif
+
+template <int PHASE, int W, int S>
+hipError_t launch_ring(const F16Args& a, int slots, int RB, hipStream_t s) {
+    const dim3 grid(slots * a.nCB);
+    if (RB == 1) {
+        hipLaunchKernelGGL((f16_kernel<PHASE, 1, S, W>), grid, dim3(64 * W), 0, s, a);
+    } else {
+        // two row blocks: two stages, and at most the waves whose rings fit
+        // in LDS (4 x 2 x 16 KB for gate/up, 6 x 2 x 12 KB for down)
+        constexpr int W2 = (PHASE == 1) ? (W > 4 ? 4 : W) : (W > 6 ? 6 : W);
+        hipLaunchKernelGGL((f16_kernel<PHASE, 2, 2, W2>), grid, dim3(64 * W2), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
 template <int PHASE>
 hipError_t launch_phase(const F16Args& a, int slots, int RB, hipStream_t s) {
+    if (slots == 1 && a.K / kKStep >= 8) {
+        if constexpr (PHASE == 1)
+            return launch_ring<PHASE, SMOE_SH_GU_WAVES, SMOE_SH_GU_STAGES>(a, slots, RB, s);
+        else
+            return launch_ring<PHASE, SMOE_SH_DN_WAVES, SMOE_SH_DN_STAGES>(a, slots, RB, s);
+    }
     // Reductions with at least SMOE_VF_LONG 128-K steps per wave take the
     // LDS-ring kernel (4 waves; LDS per workgroup: 4 x NSTAGE x (NM + RB) x
     // 4 KB <= 160 KB), shorter ones the register-pipelined kernel.  Reductions
