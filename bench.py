@@ -57,7 +57,7 @@ def parse():
                     help="also run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--workload", default="phi_layer",
                     choices=["phi_layer", "qwen_chunk", "route_fidelity", "qwen_rounds",
-                             "draft_formats", "ds_draft"],
+                             "draft_formats", "ds_draft", "qwen_verify"],
                     help="phi_layer (default): one draft + verify step of the Phi-3.5-MoE-shaped "
                          "layer; qwen_chunk: 24 Qwen-shaped layers, 16 draft steps, ELB snapshot, "
                          "top-16 residency, 17-token verify with staged misses; route_fidelity: INT4 draft vs "
@@ -65,7 +65,8 @@ def parse():
                          "rounds with the prefetch planner vs boundary placement; draft_formats: the "
                          "one-token draft step with 2-, 4- and 8-bit experts (Phi and DeepSeek shapes); "
                          "ds_draft: the DeepSeek-V2-Lite-shaped draft layer step (routing, ELB, INT4 "
-                         "experts, 2 FP16 shared experts, combine) at T = 1, 4 and 16")
+                         "experts, 2 FP16 shared experts, combine) at T = 1, 4 and 16; qwen_verify: "
+                         "the Qwen1.5-MoE-shaped verify layer at K+1 = 9 (routed and shared expert)")
     ap.add_argument("--layers", type=int, default=24, help="qwen_chunk: number of layers")
     ap.add_argument("--rounds", type=int, default=4, help="qwen_rounds: speculation rounds")
     ap.add_argument("--rho", type=float, default=0.8,
@@ -106,6 +107,8 @@ def main():
         return bench_draft_formats(args)
     if args.workload == "ds_draft":
         return bench_ds_draft(args)
+    if args.workload == "qwen_verify":
+        return bench_qwen_verify(args)
 
     import numpy as np
     import torch
@@ -760,6 +763,28 @@ def ds_draft_results(K, warmup):
     del g, table, scrub
     torch.cuda.empty_cache()
     return results, gen_s, K
+
+
+def bench_qwen_verify(args):
+    """The Qwen1.5-MoE-shaped verify layer (qwen_verify_results) as a line of
+    its own."""
+    import torch
+
+    import fp16_verify_expert_amd as fve
+    fve.lib()
+    torch.cuda.set_device(0)
+    K = max(args.steps, 5)
+    r = qwen_verify_results(K, args.warmup)
+    tot_b = r["routed"]["bytes"] + r["shared"]["bytes"]
+    tot_us = r["routed"]["us"] + r["shared"]["us"]
+    res = {"metric": "MoE-layer INT4 draft weight GB/s (% HBM peak); verify TFLOP/s (% MFMA)",
+           "value": round(tot_b / tot_us / 1e3, 2), "unit": "GB/s (verify FP16 weights)",
+           "n_gpus": 1, "steps": K, "warmup": args.warmup,
+           "ms_per_step": round(r["layer_step_us"] / 1e3, 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "fp16; fp32 accumulate",
+           "data": "synthetic (seeded N(0,0.02) weights from torch Philox, N(0,1) tokens)",
+           "config": {"workload": QWEN_VERIFY_WORKLOAD}, **r}
+    print(json.dumps(res), flush=True)
 
 
 QWEN_VERIFY_WORKLOAD = ("qwen15_moe verify layer: H=2048 E=60 top-4 I=1408 + gated shared expert "
