@@ -343,6 +343,40 @@ def main():
     stream_us = 1e3 * sum(a.elapsed_time(b) for a, b in ev_st) / nl
     del src_gu, src_dn
 
+    # ---- the layer's draft step as one launch (moe_draft_layer: routing,
+    #      INT4 FFN and combine, logits computed inside) against the split
+    #      step on the same batches, HIP events around each, each after a
+    #      verify step; outputs bit-identical ----
+    single = None
+    if fve.draft_layer_supported(H, I, E, k):
+        wsl = fve.new_layer_workspace(k, H, I, E)
+        out1 = torch.empty((1, H), dtype=torch.float16, device=dev)
+        ev_sl = [(mk(), mk()) for _ in range(nl)]
+        ev_sp = [(mk(), mk()) for _ in range(nl)]
+        for st in range(nl + 1):
+            i = args.warmup + st
+            verify(i)
+            if st:
+                ev_sp[st - 1][0].record()
+            draft_fused(i)
+            if st:
+                ev_sp[st - 1][1].record()
+            verify(i)
+            if st:
+                ev_sl[st - 1][0].record()
+            fve.moe_draft_layer(xs_d[i % POOL], router, k, t4, I, wsl, err_word=err, out=out1)
+            if st:
+                ev_sl[st - 1][1].record()
+            torch.cuda.synchronize()
+            assert torch.equal(out1, bd["out"]), "one-launch layer differs from the split step"
+        assert int(err.item()) == 0, "device error word set"
+        single = {"what": "moe_draft_layer (one launch: logits, routing, ELB, INT4 FFN, combine) "
+                          "vs moe_draft_route_ffn + moe_combine, HIP events around each, after "
+                          "a verify step; bit-identical outputs",
+                  "one_launch_us": round(1e3 * sum(a.elapsed_time(b) for a, b in ev_sl) / nl, 2),
+                  "split_us": round(1e3 * sum(a.elapsed_time(b) for a, b in ev_sp) / nl, 2)}
+        del wsl
+
     idx = idx_all(args, K)
     draft_ms = sum(ph[st][0].elapsed_time(ph[st][1]) for st in range(K))
     verify_ms = sum(ph[st][1].elapsed_time(ph[st][2]) for st in range(K))
@@ -435,6 +469,7 @@ def main():
                            "frac_attainable": round(rd_ach / ((gu_b + dn_b) / stream_us / 1e3),
                                                     4)},
         "call_us": call_us,
+        "draft_single_launch": single,
         "host_wall_s": round(wall, 4),
         "gen_s": round(gen_s, 2),
     }

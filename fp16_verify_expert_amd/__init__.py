@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsmoe.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "smoe.h")
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 SMOE_DERR_BAD_ID = 1
 SMOE_DERR_NULL_EXPERT = 2
@@ -60,6 +60,16 @@ _SIGS = {
                                  _vp, _vp, _sz, _vp, _vp]),
     "moe_combine_route_logits": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp,
                                       ctypes.c_float, _vp, _vp, _i, _vp, _vp]),
+    # x, w_router, w_shared_gate, logits, H, I, E, k, renorm, layer, L, counters, experts,
+    # group_size, ids, w, gate, off, sorted_token, sorted_pair, pair_pos, active, n_active,
+    # y_sorted, shared_w13, shared_w2, shared_I, shared_h, shared_out, residual, out,
+    # norm_out, eps, next_router, next_shared_gate, next_E, next_logits, ws, ws_bytes, err,
+    # stream
+    "moe_draft_layer": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _i,
+                             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
+                             _vp, _vp, _i, _vp, _vp, _sz, _vp, _vp]),
+    "smoe_draft_layer_supported": (_i, [_i, _i, _i, _i, _i]),
     "verify_grouped_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp,
                                  _vp, _sz, _vp, _vp]),
     "moe_combine": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, ctypes.c_float,
@@ -373,6 +383,97 @@ def moe_draft_route_ffn(x, w_router, k: int, table, I: int, workspace,
     if shared is not None:
         return topk_ids, topk_w, shared_gate, maps, y_sorted, shared_out
     return topk_ids, topk_w, shared_gate, maps, y_sorted
+
+
+def draft_layer_supported(H: int, I: int, E: int, k: int, shared_I: int = 0) -> bool:
+    """True when moe_draft_layer has a one-launch geometry for this layer
+    shape on the current device."""
+    return bool(lib().smoe_draft_layer_supported(H, I, E, k, shared_I))
+
+
+def new_layer_workspace(k: int, H: int, I: int, E: int, device="cuda") -> torch.Tensor:
+    """Zero-filled moe_draft_layer workspace (its barrier counters start at
+    zero; every completed call leaves them zero)."""
+    n = max(256, workspace_bytes(2, 1, k, H, I, E))
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def moe_draft_layer(x, w_router, k: int, table, I: int, workspace, renormalize: bool = False,
+                    w_shared_gate=None, *, logits=None, counters=None, layer: int = 0,
+                    err_word=None, topk_ids=None, topk_w=None, shared_gate=None, maps=None,
+                    y_sorted=None, shared=None, shared_h=None, shared_out=None, residual=None,
+                    out=None, norm_out=None, norm_eps: float = 1e-6, next_router=None,
+                    next_shared_gate=None, next_logits=None, stream=None):
+    """One-token draft step of a whole MoE layer in one launch:
+    moe_draft_route_ffn followed by moe_combine (norm_out None) or
+    moe_combine_route_logits (next_router given), with bit-identical
+    outputs.  logits: the router logits of x from the launch before (None:
+    computed in the launch).  norm_out: a tensor, True to allocate one, or
+    None.  Returns a dict with topk_ids, topk_w, shared_gate, maps, y_sorted,
+    shared_out, out, norm_out and next_logits (None where not computed)."""
+    _check(x, torch.float16, "x")
+    _check(w_router, torch.float16, "w_router")
+    T, H = x.shape
+    if T != 1:
+        raise ValueError(f"moe_draft_layer takes one token, got T={T}")
+    E = w_router.shape[0]
+    dev = x.device
+    if topk_ids is None:
+        topk_ids = torch.empty((1, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((1, k), dtype=torch.float32, device=dev)
+    if w_shared_gate is not None:
+        _check(w_shared_gate, torch.float16, "w_shared_gate")
+        if shared_gate is None:
+            shared_gate = torch.empty((1,), dtype=torch.float32, device=dev)
+    L = 0
+    if counters is not None:
+        _check(counters, torch.int32, "counters")
+        L = counters.shape[0]
+    if maps is None:
+        maps = _new_maps(1, k, E, dev)
+    if y_sorted is None:
+        y_sorted = torch.empty((k, H), dtype=torch.float16, device=dev)
+    sw13 = sw2 = None
+    Is = 0
+    if shared is not None:
+        sw13, sw2 = shared
+        _check(sw13, torch.float16, "shared w13")
+        _check(sw2, torch.float16, "shared w2")
+        Is = sw2.shape[1]
+        if shared_h is None:
+            shared_h = torch.empty((Is,), dtype=torch.float16, device=dev)
+        if shared_out is None:
+            shared_out = torch.empty((1, H), dtype=torch.float16, device=dev)
+    if residual is not None:
+        _check(residual, torch.float16, "residual")
+    if out is None:
+        out = torch.empty((1, H), dtype=torch.float16, device=dev)
+    if norm_out is True or (norm_out is None and next_router is not None):
+        norm_out = torch.empty((1, H), dtype=torch.float16, device=dev)
+    nE = 0
+    if next_router is not None:
+        _check(next_router, torch.float16, "next_router")
+        nE = next_router.shape[0]
+        if next_shared_gate is not None:
+            _check(next_shared_gate, torch.float16, "next_shared_gate")
+        if next_logits is None:
+            next_logits = torch.empty(nE + (1 if next_shared_gate is not None else 0),
+                                      dtype=torch.float32, device=dev)
+    _call("moe_draft_layer", _p(x), _p(w_router), _p(w_shared_gate), _p(logits), H, I, E, k,
+          1 if renormalize else 0, layer, L, _p(counters), _p(table), 128, _p(topk_ids),
+          _p(topk_w), _p(shared_gate) if w_shared_gate is not None else None,
+          _p(maps["offsets"]), _p(maps["sorted_token"]), _p(maps["sorted_pair"]),
+          _p(maps["pair_pos"]), _p(maps["active"]), _p(maps["n_active"]), _p(y_sorted),
+          _p(sw13), _p(sw2), Is, _p(shared_h) if shared is not None else None,
+          _p(shared_out) if shared is not None else None, _p(residual), _p(out),
+          _p(norm_out), float(norm_eps), _p(next_router), _p(next_shared_gate), nE,
+          _p(next_logits) if next_router is not None else None,
+          _p(workspace), workspace.numel() * workspace.element_size(), _p(err_word), _s(stream))
+    return dict(topk_ids=topk_ids, topk_w=topk_w, shared_gate=shared_gate, maps=maps,
+                y_sorted=y_sorted, shared_out=shared_out if shared is not None else None,
+                out=out, norm_out=norm_out,
+                next_logits=next_logits if next_router is not None else None)
 
 
 def verify_grouped_gemm(x, sorted_token, offsets, table, T: int, rows: int, H: int, I: int,

@@ -171,6 +171,7 @@ size_t smoe_workspace_bytes(int which, int T, int k, int H, int I, int E) {
     if ((long long)T * k > kMaxPairs) return 0;
     if (which == 0) return smoe::w4a16_workspace_bytes(T, k, H, I, E);
     if (which == 1) return smoe::verify_workspace_bytes(T, T * k, H, I, E);
+    if (which == 2) return T == 1 ? smoe::draft_layer_workspace_bytes(k, I, E) : 0;
     return 0;
 }
 
@@ -416,6 +417,103 @@ smoe_status moe_draft_route_ffn(const uint16_t* x, const uint16_t* w_router,
                                      shared_h, shared_out, logits, err_word,
                                      static_cast<hipStream_t>(stream)),
         "moe_draft_route_ffn launch");
+}
+
+int smoe_draft_layer_supported(int H, int I, int E, int k, int shared_I) {
+    return smoe::draft_layer_supported(H, I, E, k, shared_I) ? 1 : 0;
+}
+
+smoe_status moe_draft_layer(const uint16_t* x, const uint16_t* w_router,
+                            const uint16_t* w_shared_gate, const float* logits, int H, int I,
+                            int E, int k, int renormalize, int layer, int L, int32_t* counters,
+                            const smoe_w4_expert* experts, int group_size, int32_t* topk_ids,
+                            float* topk_w, float* shared_gate, int32_t* expert_offsets,
+                            int32_t* sorted_token, int32_t* sorted_pair, int32_t* pair_pos,
+                            int32_t* active, int32_t* n_active, uint16_t* y_sorted,
+                            const uint16_t* shared_w13, const uint16_t* shared_w2, int shared_I,
+                            uint16_t* shared_h, uint16_t* shared_out, const uint16_t* residual,
+                            uint16_t* out, uint16_t* norm_out, float norm_eps,
+                            const uint16_t* next_w_router, const uint16_t* next_w_shared_gate,
+                            int next_E, float* next_logits, void* workspace,
+                            size_t workspace_bytes, int32_t* err_word, void* stream) {
+    REQUIRE(x && w_router && experts && topk_ids && topk_w && expert_offsets && sorted_token &&
+                sorted_pair && pair_pos && active && n_active && y_sorted && out,
+            SMOE_ERR_NULL, "moe_draft_layer: a required pointer is NULL");
+    REQUIRE(!shared_w13 || (shared_w2 && shared_h && shared_out), SMOE_ERR_NULL,
+            "moe_draft_layer: shared_w2, shared_h and shared_out are required with shared_w13");
+    REQUIRE(!w_shared_gate || shared_gate, SMOE_ERR_NULL,
+            "moe_draft_layer: shared_gate output is required with w_shared_gate");
+    REQUIRE(!next_w_router || (norm_out && next_logits), SMOE_ERR_NULL,
+            "moe_draft_layer: norm_out and next_logits are required with next_w_router");
+    smoe_status st = check_hek(H, E, k);
+    if (st != SMOE_OK) return st;
+    REQUIRE(I > 0 && I % 128 == 0, SMOE_ERR_SHAPE,
+            "moe_draft_layer: I=%d must be a positive multiple of 128", I);
+    REQUIRE(!shared_w13 || (shared_I > 0 && shared_I % 128 == 0), SMOE_ERR_SHAPE,
+            "moe_draft_layer: shared_I=%d must be a positive multiple of 128", shared_I);
+    REQUIRE(!next_w_router || (next_E >= 1 && next_E <= 256), SMOE_ERR_SHAPE,
+            "moe_draft_layer: next_E=%d must be in [1, 256]", next_E);
+    REQUIRE(group_size == 128, SMOE_ERR_UNSUPPORTED,
+            "moe_draft_layer: group_size=%d (only 128 is supported)", group_size);
+    REQUIRE(!counters || (L >= 1 && layer >= 0 && layer < L), SMOE_ERR_SHAPE,
+            "moe_draft_layer: layer=%d must be in [0, L=%d)", layer, L);
+    REQUIRE(norm_eps >= 0.0f && (!norm_out || norm_out != out), SMOE_ERR_SHAPE,
+            "moe_draft_layer: norm_eps must be >= 0 and norm_out must not alias out");
+    REQUIRE(aligned(x, 16) && aligned(w_router, 16) && aligned(w_shared_gate, 16) &&
+                aligned(logits, 4) && aligned(y_sorted, 16) && aligned(shared_w13, 16) &&
+                aligned(shared_w2, 16) && aligned(shared_h, 16) && aligned(shared_out, 16) &&
+                aligned(residual, 16) && aligned(out, 16) && aligned(norm_out, 16) &&
+                aligned(next_w_router, 16) && aligned(next_w_shared_gate, 16) &&
+                aligned(next_logits, 4),
+            SMOE_ERR_SHAPE, "moe_draft_layer: fp16 tensors must be 16-byte aligned (fp32 4)");
+    const size_t need = smoe::draft_layer_workspace_bytes(k, I, E);
+    REQUIRE(workspace && workspace_bytes >= need && aligned(workspace, 256), SMOE_ERR_WORKSPACE,
+            "moe_draft_layer: workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+            workspace_bytes);
+    CHECK_DEVICE();
+    REQUIRE(smoe::draft_layer_supported(H, I, E, k, shared_w13 ? shared_I : 0),
+            SMOE_ERR_UNSUPPORTED,
+            "moe_draft_layer: no one-launch geometry for H=%d I=%d E=%d k=%d shared_I=%d", H, I,
+            E, k, shared_w13 ? shared_I : 0);
+    smoe::DraftLayerCall c{};
+    c.x = x;
+    c.wr = w_router;
+    c.wsg = w_shared_gate;
+    c.logits = logits;
+    c.H = H;
+    c.I = I;
+    c.E = E;
+    c.k = k;
+    c.renorm = renormalize ? 1 : 0;
+    c.counters_row = counters ? counters + (size_t)layer * E : nullptr;
+    c.ids = topk_ids;
+    c.w = topk_w;
+    c.gate = shared_gate;
+    c.off = expert_offsets;
+    c.st = sorted_token;
+    c.sp = sorted_pair;
+    c.pp = pair_pos;
+    c.active = active;
+    c.n_active = n_active;
+    c.experts = experts;
+    c.y = y_sorted;
+    c.sw13 = shared_w13;
+    c.sw2 = shared_w2;
+    c.Is = shared_w13 ? shared_I : 0;
+    c.sh_h = shared_h;
+    c.sh_out = shared_out;
+    c.resid = residual;
+    c.out = out;
+    c.norm_out = norm_out;
+    c.eps = norm_eps;
+    c.wr_next = next_w_router;
+    c.wsg_next = next_w_shared_gate;
+    c.E_next = next_E;
+    c.lg_next = next_logits;
+    c.ws = workspace;
+    c.err = err_word;
+    return hip_result(smoe::launch_draft_layer(c, static_cast<hipStream_t>(stream)),
+                      "moe_draft_layer launch");
 }
 
 smoe_status moe_combine_route_logits(const uint16_t* y_sorted, const int32_t* pair_pos,

@@ -53,6 +53,45 @@ hipError_t launch_elb_count(const int32_t* ids, int n, int E, int layer, int32_t
 hipError_t launch_gather(const int32_t* ids, int n, int k, int E, int32_t* off, int32_t* st,
                          int32_t* sp, int32_t* pp, int32_t* active, int32_t* n_active,
                          int32_t* err, hipStream_t s);
+// The one-launch draft layer (T = 1): routing, routed INT4 FFN, optional
+// FP16 shared expert, combine and the next layer's logits.
+struct DraftLayerCall {
+    const uint16_t* x;
+    const uint16_t* wr;
+    const uint16_t* wsg;
+    const float* logits;
+    int H, I, E, k, renorm;
+    int32_t* counters_row;
+    int32_t* ids;
+    float* w;
+    float* gate;
+    int32_t* off;
+    int32_t* st;
+    int32_t* sp;
+    int32_t* pp;
+    int32_t* active;
+    int32_t* n_active;
+    const smoe_w4_expert* experts;
+    uint16_t* y;
+    const uint16_t* sw13;
+    const uint16_t* sw2;
+    int Is;
+    uint16_t* sh_h;
+    uint16_t* sh_out;
+    const uint16_t* resid;
+    uint16_t* out;
+    uint16_t* norm_out;
+    float eps;
+    const uint16_t* wr_next;
+    const uint16_t* wsg_next;
+    int E_next;
+    float* lg_next;
+    void* ws;
+    int32_t* err;
+};
+bool draft_layer_supported(int H, int I, int E, int k, int Is);
+size_t draft_layer_workspace_bytes(int k, int I, int E);
+hipError_t launch_draft_layer(const DraftLayerCall& c, hipStream_t s);
 hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, const int32_t* off,
                             const int32_t* active, const int32_t* n_active,
                             const smoe_w4_expert* experts, int T, int k, int H, int I, int E,

@@ -41,10 +41,13 @@
 //
 // The slots' partial sums are added in a fixed order through LDS: the output
 // is deterministic and no floating-point atomics are used.
+#include <algorithm>
+
 #include "common.h"
 #include "gemv_core.h"
 #include "maps_core.h"
 #include "route_core.h"
+#include "combine_core.h"
 
 namespace {
 
@@ -1336,6 +1339,595 @@ __attribute__((amdgpu_waves_per_eu(w4_waves_per_eu<1, NG>()))) void w4_down_shar
 
 // ---------------------------------------------------------------- launch ----
 
+// ============================================= one-launch draft layer (T = 1) ===
+//
+// [S1] Key Contributions 4 and Methodology in Plain English: the draft's
+// routing, expert FFN and combine of a decode step are dispatched inside a
+// single GPU launch.  moe_draft_layer does a whole one-token MoE layer in one
+// persistent launch of one 8-wave workgroup per CU, every workgroup resident:
+//
+//   0 (no logits given): the router logits of x, one per wave across the
+//     chip, into the workspace; grid barrier.
+//   A every workgroup takes the top k of the logits itself (the routing
+//     kernels' routine) and keeps its slots' matrices in LDS; the last
+//     workgroup also writes the routing outputs, the ELB increments and the
+//     maps.
+//   B gate/up items -- routed INT4 blocks and the FP16 shared expert's
+//     columns -- against x staged once per workgroup; h stored; grid barrier.
+//   D down items: each requests its block's first weights, then stages the h
+//     row it needs; y stored; grid barrier.
+//   F combine (+ residual, + the norm epilogue, + the next layer's router
+//     logits) by the first workgroups, as moe_combine_route_logits.
+//
+// Each item runs on a sub-group of 4 waves with the same geometry, loads and
+// reduction order as the two one-token launches of moe_draft_route_ffn, so
+// y_sorted, h and every later value are bit-identical to those launches.
+// Values one workgroup writes for another (logits, h, y, the shared
+// expert's h and output) are stored and loaded with device-scope accesses,
+// which are coherent across the XCDs' separate L2 caches; a grid barrier is
+// an atomic counter that each workgroup increments after its stores have
+// completed and then polls.  Every poll is bounded in time: on expiry the
+// workgroup flags SMOE_DERR_SYNC and skips to the end, so no wave can wait
+// forever.  The last workgroup to finish resets the counters.
+//
+// Measured on MI355X this one launch is slower than the three launches plus
+// combine it replaces (each grid barrier costs about 3.5 us, about two memory
+// round trips between XCDs, more than a kernel boundary on one stream); it
+// is kept as the single-launch form of the layer, bit-identical to the split
+// form.  Staging the down weights in LDS during B measured slower still:
+// the extra stream competes with gate/up, and the compiler orders every LDS
+// access after outstanding LDS-DMA loads.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+SMOE_DEV smoe_w4_expert spec_table_e(const smoe_w4_expert* experts, int E, int lane) {
+    W4Args t{};
+    t.experts = experts;
+    t.E = E;
+    return spec_table(t, lane);
+}
+template <int PHASE>
+SMOE_DEV smoe_w4_mat pick_mat_e(const smoe_w4_expert* experts, int E, const smoe_w4_expert& spec,
+                                int e) {
+    W4Args t{};
+    t.experts = experts;
+    t.E = E;
+    return pick_mat<PHASE>(t, spec, e);
+}
+
+constexpr int kLayerWaves = 8;  // two sub-groups of four
+constexpr int kSubWaves = 4;
+constexpr int kLayerRed = kSubWaves * 64;           // floats per sub-group (waves x NB <= 64)
+constexpr uint64_t kSyncSpinTicks = 10000000ull;    // 100 ms of the 100 MHz real-time clock
+
+struct LayerArgs {
+    const uint16_t* x;      // [H] the layer's (normalised) input row
+    const uint16_t* wr;     // router [E, H] (phase 0 only)
+    const uint16_t* wsg;    // shared-expert gate row [H] or null
+    const float* logits;    // [nvec] logits of x, or null: phase 0
+    float* lg_ws;           // [nvec] workspace (phase 0)
+    int H, I, E, k, renorm, nvec;
+    const smoe_w4_expert* experts;
+    int32_t* counters_row;
+    int32_t* ids;
+    float* w;
+    float* gate;
+    int32_t* off;
+    int32_t* sorted_token;
+    int32_t* sorted_pair;
+    int32_t* pair_pos;
+    int32_t* active;
+    int32_t* n_active;
+    const uint16_t* sw13;   // shared expert [2 Is, H] or null
+    const uint16_t* sw2;    // [H, Is]
+    int Is;
+    uint16_t* h;            // [k, I] workspace
+    uint16_t* sh_h;         // [Is]
+    uint16_t* y;            // [k, H] y_sorted
+    uint16_t* sh_out;       // [H]
+    uint32_t* sync;         // [2] zero between calls
+    const uint16_t* resid;
+    uint16_t* out;
+    uint16_t* norm_out;     // or null
+    float eps;
+    const uint16_t* wr_next;   // next layer's router [E_next, H] or null
+    const uint16_t* wsg_next;
+    int E_next, nvec_next;
+    float* lg_next;
+    int32_t* err;
+    // plan
+    int P;                   // workgroups (one per CU)
+    int nCB1, na1;           // gate/up: column blocks per slot, active waves per item
+    int nCB2, na2, G2;       // down: column blocks per slot, active waves, groups
+    int n_gu, n_dn;          // gate/up items (routed, then shared), down items
+    int R1, R2;              // rounds of gate/up and down items
+    int nF;                  // workgroups of phase F
+    int row_bytes;           // dynamic LDS: staged rows
+};
+
+template <typename T>
+SMOE_DEV void st_dev(T* p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+SMOE_DEV T ld_dev(const T* p) {
+    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+SMOE_DEV uint4 ld_dev4(const void* p) {
+    const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+    const uint64_t a = ld_dev(q), b = ld_dev(q + 1);
+    return make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32));
+}
+struct DevRows {
+    SMOE_DEV uint4 operator()(const uint16_t* p) const { return ld_dev4(p); }
+};
+
+// vmcnt(0): this wave's loads, stores and LDS-DMA loads have completed.
+SMOE_DEV void wait_vm0() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); }
+
+// Grid barrier number `nb` (1, 2, ...) of the launch: returns false when the
+// wait expired (flagged), after which the workgroup only runs layer_exit.
+SMOE_DEV bool layer_sync(const LayerArgs& a, int nb, int* flag_s) {
+    wait_vm0();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t target = (uint32_t)nb * (uint32_t)a.P;
+        const uint32_t old = __hip_atomic_fetch_add(a.sync, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        int ok = 1;
+        if (old + 1 < target) {
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            while (ld_dev(a.sync) < target) {
+                __builtin_amdgcn_s_sleep(1);
+                if (__builtin_amdgcn_s_memrealtime() - t0 > kSyncSpinTicks) {
+                    ok = 0;
+                    flag_error(a.err, SMOE_DERR_SYNC);
+                    break;
+                }
+            }
+        }
+        *flag_s = ok;
+    }
+    __syncthreads();
+    return *flag_s != 0;
+}
+
+// Every workgroup ends here: the last one to arrive (all others have left
+// every barrier) returns both counters to zero for the next call.
+SMOE_DEV void layer_exit(const LayerArgs& a) {
+    if (threadIdx.x == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(a.sync + 1, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        if (old + 1 == (uint32_t)a.P) {
+            st_dev(a.sync, 0u);
+            st_dev(a.sync + 1, 0u);
+        }
+    }
+}
+
+// One item's place: workgroup i mod P, sub-group (i / P) mod 2, round i / 2P.
+SMOE_DEV int layer_item(int P, int b, int sub, int r) { return (2 * r + sub) * P + b; }
+
+// A source whose loads fetch nothing: an empty buffer (loads return zero)
+// and scale / zero reads of `safe` (N = 0 keeps every offset at 0).
+SMOE_DEV W4Src empty_src(const void* safe) {
+    W4Src s;
+    s.q = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(safe), (short)0, 0, kBufWord3);
+    s.m.qweight = static_cast<const int32_t*>(safe);
+    s.m.scales = static_cast<const uint16_t*>(safe);
+    s.m.qzeros = static_cast<const int32_t*>(safe);
+    s.N = 0;
+    return s;
+}
+
+constexpr int kAuxDev = 16;  // sc1: device-scope (coherent across the XCDs)
+
+// The matrices of expert slot `slot` kept in LDS after routing (w13 in words
+// 0-2, w2 in 3-5), as workgroup-uniform pointers.
+template <int PHASE>
+SMOE_DEV smoe_w4_mat slot_mat(const uint64_t (*mat)[6], int slot) {
+    const uint64_t* m = mat[slot] + (PHASE == 1 ? 0 : 3);
+    smoe_w4_mat r;
+    r.qweight = uniform_ptr(reinterpret_cast<const int32_t*>(m[0]));
+    r.scales = uniform_ptr(reinterpret_cast<const uint16_t*>(m[1]));
+    r.qzeros = uniform_ptr(reinterpret_cast<const int32_t*>(m[2]));
+    return r;
+}
+
+// Sums of a sub-group item's slots for its four columns (as one_token_block):
+// groups myslot, myslot + nslots, ... through two register buffers.
+template <int NG, typename Load>
+SMOE_DEV void item_groups(Load load, const uint4* xs, const float4* sums, int myslot, int nslots,
+                          int G, int K8, int zsh, float (&acc)[1][4], GroupLoad<4>& A) {
+    const Masks<4> mk;
+    const W4Lds l{const_cast<uint4*>(xs), const_cast<float4*>(sums), nullptr};
+    GroupLoad<4> B;
+    const int g0 = myslot;
+    if (NG >= 3) load(B, clamp_group(g0 + nslots, G));
+    step_if<4>(A, l, g0, G, K8, zsh, mk, acc);
+    if (NG == 2) {
+        load(B, clamp_group(g0 + nslots, G));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (NG >= 3) load(A, clamp_group(g0 + 2 * nslots, G));
+    if (NG >= 2) step_if<4>(B, l, g0 + nslots, G, K8, zsh, mk, acc);
+    if (NG >= 4) load(B, clamp_group(g0 + 3 * nslots, G));
+    if (NG >= 3) step_if<4>(A, l, g0 + 2 * nslots, G, K8, zsh, mk, acc);
+    if (NG >= 4) step_if<4>(B, l, g0 + 3 * nslots, G, K8, zsh, mk, acc);
+}
+
+// Butterfly of a wave's slot partials (lane distances LPR, 2 LPR, ...) into
+// the sub-group's LDS row; wave ws of the sub-group writes red[ws * NB + .].
+template <int LPR>
+SMOE_DEV void item_partials(float (&acc)[1][4], float* red, int ws, int lane) {
+    constexpr int NB = 4 * LPR;
+#pragma unroll
+    for (int d = LPR; d < 64; d *= 2)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[0][c] += __shfl_xor(acc[0][c], d);
+    if (lane < LPR)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) red[ws * NB + 4 * lane + c] = acc[0][c];
+}
+
+// The shared expert's projection columns of one sub-group item (one or two
+// per wave, shared_gemv_block's arithmetic), the row read device-coherently
+// when it was written in this launch.
+template <int PHASE, int CPL, int CPW, bool kDevRow>
+SMOE_DEV void shared_item(const uint16_t* xrow, const uint16_t* W, int K, int I, int Ncol, int b,
+                          int ws, int lane, uint16_t* out) {
+    constexpr int NM = (PHASE == 1) ? 2 : 1;
+    int n[CPW];
+    u4_t wv[CPW][NM][CPL];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        n[c] = (b * kSubWaves + ws) * CPW + c;
+        const int nc = (n[c] < Ncol) ? n[c] : Ncol - 1;
+        smoe_gemv::gemv_load_w<NM, CPL>(W, K, I, nc, lane, wv[c]);
+    }
+    uint4 xr[CPL];
+    if constexpr (kDevRow) {
+        const int kc = K >> 3;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = lane + 64 * j;
+            xr[j] = ld_dev4(xrow + 8 * (c < kc ? c : kc - 1));
+        }
+    } else {
+        smoe_gemv::gemv_load_x<CPL>(xrow, K, lane, xr);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        const uint16_t v = smoe_gemv::gemv_dot<NM, CPL>(wv[c], xr, K, lane);
+        if (lane == 0 && n[c] < Ncol) st_dev(out + n[c], v);
+    }
+}
+
+template <int LPR1, int NG1, int LPR2, int NG2, int CPLS1, int CPLS2>
+__global__ __launch_bounds__(64 * kLayerWaves) void draft_layer_kernel(LayerArgs a) {
+    constexpr int RPL1 = 64 / LPR1, NB1 = 4 * LPR1;
+    constexpr int RPL2 = 64 / LPR2, NB2 = 4 * LPR2;
+    __shared__ float lg_s[257];
+    __shared__ int32_t ids_s[kFusedMaxK];   // top-k ids by rank
+    __shared__ int32_t e_s[kFusedMaxK];     // expert of each slot (increasing id)
+    __shared__ uint64_t mat_s[kFusedMaxK][6];  // each slot's w13 and w2 matrices
+    __shared__ int32_t ids_w[kFusedMaxK];
+    __shared__ int32_t pp_s[kFusedMaxK];
+    __shared__ float w_s[kFusedMaxK];
+    __shared__ float gate_s;
+    __shared__ float redf[kLayerWaves];
+    __shared__ int flag_s;
+    extern __shared__ uint4 smem[];
+    char* dyn = reinterpret_cast<char*>(smem);
+    float* red = reinterpret_cast<float*>(dyn + a.row_bytes);  // [2][kLayerRed]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int sub = wave / kSubWaves;
+    const int ws = wave % kSubWaves;
+    const int b = blockIdx.x;
+    const int P = a.P;
+    const int H = a.H, I = a.I, E = a.E, k = a.k;
+    const int K8_1 = H >> 3, G1 = H / 128;
+    const int K8_2 = I >> 3;
+    const int n_rt1 = k * a.nCB1, n_rt2 = k * a.nCB2;
+    int nbar = 0;
+    bool ok = true;
+
+    const smoe_w4_expert spec = spec_table_e(a.experts, E, lane);
+
+    // ---- 0: router logits of x, one per wave across the chip ----
+    if (!a.logits) {
+        const int item = b * kLayerWaves + wave;
+        if (item < a.nvec)
+            smoe_route::wave_logits(a.x, a.wr, a.wsg, H, E, a.nvec, item, a.nvec,
+                                    P * kLayerWaves, lg_s, lane);
+        __syncthreads();
+        if (tid < kLayerWaves && b * kLayerWaves + tid < a.nvec)
+            st_dev(reinterpret_cast<uint32_t*>(a.lg_ws) + b * kLayerWaves + tid,
+                   __float_as_uint(lg_s[b * kLayerWaves + tid]));
+        ok = layer_sync(a, ++nbar, &flag_s);
+        if (ok)
+            for (int i = tid; i < a.nvec; i += blockDim.x)
+                lg_s[i] = __uint_as_float(ld_dev(reinterpret_cast<const uint32_t*>(a.lg_ws) + i));
+    } else {
+        for (int i = tid; i < a.nvec; i += blockDim.x) lg_s[i] = a.logits[i];
+    }
+    if (!ok) {
+        layer_exit(a);
+        return;
+    }
+    __syncthreads();
+
+    // ---- A: routing ----
+    if (wave == 0) smoe_route::topk_ids_wave(lg_s, E, k, lane, ids_s);
+    __syncthreads();
+    if (tid < k) {
+        const int id = ids_s[tid];
+        int pos = 0;
+        for (int i = 0; i < k; ++i) pos += (ids_s[i] < id) ? 1 : 0;
+        e_s[pos] = id;
+        pp_s[tid] = pos;
+    }
+    if (b == P - 1) {
+        if (wave == 0)
+            smoe_route::topk_softmax_wave(lg_s, E, k, a.renorm, a.wsg != nullptr, lane, a.ids,
+                                          a.w, a.gate, ids_w);
+        __syncthreads();
+        smoe_maps::one_token_maps(ids_w, k, E, a.counters_row, a.off, a.sorted_token,
+                                  a.sorted_pair, a.pair_pos, a.active, a.n_active);
+    }
+    __syncthreads();
+    if (wave == 0)
+        for (int j = 0; j < k; ++j) {
+            const int e = __builtin_amdgcn_readfirstlane(e_s[j]);
+            const smoe_w4_mat m1 = pick_mat_e<1>(a.experts, E, spec, e);
+            const smoe_w4_mat m2 = pick_mat_e<2>(a.experts, E, spec, e);
+            if (lane == 0) {
+                mat_s[j][0] = reinterpret_cast<uint64_t>(m1.qweight);
+                mat_s[j][1] = reinterpret_cast<uint64_t>(m1.scales);
+                mat_s[j][2] = reinterpret_cast<uint64_t>(m1.qzeros);
+                mat_s[j][3] = reinterpret_cast<uint64_t>(m2.qweight);
+                mat_s[j][4] = reinterpret_cast<uint64_t>(m2.scales);
+                mat_s[j][5] = reinterpret_cast<uint64_t>(m2.qzeros);
+            }
+        }
+    __syncthreads();
+
+    // ---- B: gate/up items (routed INT4 blocks, then shared FP16 columns) ----
+    uint4* xs = reinterpret_cast<uint4*>(dyn);
+    float4* sums = reinterpret_cast<float4*>(dyn + (size_t)K8_1 * 16);
+    auto gu_src = [&](int i, int& cb, int& slot) {
+        slot = i / a.nCB1;
+        cb = i - slot * a.nCB1;
+        return slot_mat<1>(mat_s, slot);
+    };
+    const int q1 = lane % LPR1;
+    const int myslot1 = ws * RPL1 + lane / LPR1;
+    const int nslots1 = a.na1 * RPL1;
+    // the token row, then round 0's first group (an empty source where the
+    // wave has no routed item: a fixed load count), then x is staged
+    uint4 xv[kRowChunksPerThread];
+    {
+        const uint4* x4 = reinterpret_cast<const uint4*>(a.x);
+#pragma unroll
+        for (int u = 0; u < kRowChunksPerThread; ++u) {
+            const int idx = tid + u * 64 * kLayerWaves;
+            xv[u] = x4[idx < K8_1 ? idx : K8_1 - 1];
+        }
+    }
+    GroupLoad<4> A1;
+    {
+        const int i0 = layer_item(P, b, sub, 0);
+        const bool rt0 = i0 < n_rt1;
+        const int slot0 = rt0 ? i0 / a.nCB1 : 0;
+        const int cb0 = i0 - slot0 * a.nCB1;
+        const smoe_w4_mat wm0 = slot_mat<1>(mat_s, slot0);
+        const bool v0 = rt0 && ws < a.na1 && wm0.qweight && wm0.scales && wm0.qzeros;
+        const int col0 = !v0 ? 0
+                         : (q1 < LPR1 / 2) ? cb0 * (NB1 / 2) + 4 * q1
+                                           : I + cb0 * (NB1 / 2) + 4 * (q1 - LPR1 / 2);
+        const W4Src src0 = v0 ? make_src<4>(wm0, H, 2 * I) : empty_src(a.x);
+        load_group<4>(A1, src0, clamp_group(myslot1, G1), col0, true);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kRowChunksPerThread; ++u) {
+        const int idx = tid + u * 64 * kLayerWaves;
+        if (idx < K8_1) xs[idx] = permute_chunk<4>(xv[u]);
+    }
+    // the group sums of x (finish_rows' arithmetic)
+    __syncthreads();
+    for (int gg = tid; gg < G1; gg += 64 * kLayerWaves) {
+        const uint4* xr = xs + gg * QF<4>::kChunks;
+        float s4[2] = {0.0f, 0.0f};
+#pragma unroll 4
+        for (int c = 0; c < QF<4>::kChunks; ++c) {
+            const uint4 p = xr[c];
+            const h2_t x0 = as_h2(p.x), x1 = as_h2(p.y), x2 = as_h2(p.z), x3 = as_h2(p.w);
+            s4[0] += ((float)x0.x + (float)x0.y) + ((float)x2.x + (float)x2.y);
+            s4[1] += ((float)x1.x + (float)x1.y) + ((float)x3.x + (float)x3.y);
+        }
+        sums[gg] = make_float4(s4[0], s4[1], 0.0f, 0.0f);
+    }
+    __syncthreads();
+    for (int r = 0; r < a.R1; ++r) {
+        const int i = layer_item(P, b, sub, r);
+        float* rd = red + sub * kLayerRed;
+        if (i < n_rt1) {
+            int cb, slot;
+            const smoe_w4_mat wm = gu_src(i, cb, slot);
+            const bool good = wm.qweight && wm.scales && wm.qzeros;
+            if (!good && tid % (64 * kSubWaves) == 0 && cb == 0)
+                flag_error(a.err, SMOE_DERR_NULL_EXPERT);
+            if (ws < a.na1 && good) {
+                const int col = (q1 < LPR1 / 2) ? cb * (NB1 / 2) + 4 * q1
+                                                : I + cb * (NB1 / 2) + 4 * (q1 - LPR1 / 2);
+                const W4Src src = make_src<4>(wm, H, 2 * I);
+                if (r > 0) load_group<4>(A1, src, clamp_group(myslot1, G1), col, true);
+                float acc[1][4] = {{0.0f, 0.0f, 0.0f, 0.0f}};
+                auto ld = [&](GroupLoad<4>& L, int g) { load_group<4>(L, src, g, col, true); };
+                item_groups<NG1>(ld, xs, sums, myslot1, nslots1, G1, K8_1, zero_shift<4>(col),
+                                 acc, A1);
+                item_partials<LPR1>(acc, rd, ws, lane);
+            }
+        } else {
+            if constexpr (CPLS1 > 0) {
+                if (i < a.n_gu)
+                    shared_item<1, CPLS1, 2, false>(a.x, a.sw13, H, a.Is, a.Is, i - n_rt1, ws,
+                                                    lane, a.sh_h);
+            }
+        }
+        __syncthreads();
+        if (i < n_rt1) {
+            const int slot = i / a.nCB1;
+            const int cb = i - slot * a.nCB1;
+            const smoe_w4_mat wm = slot_mat<1>(mat_s, slot);
+            const int ts = tid % (64 * kSubWaves);
+            if (wm.qweight && wm.scales && wm.qzeros && ts < NB1 / 2) {
+                float gv = 0.0f, uv = 0.0f;
+                for (int w = 0; w < a.na1; ++w) {
+                    gv += rd[w * NB1 + ts];
+                    uv += rd[w * NB1 + NB1 / 2 + ts];
+                }
+                st_dev(a.h + (size_t)slot * I + cb * (NB1 / 2) + ts, f2h(silu_f(gv) * uv));
+            }
+        }
+        __syncthreads();
+    }
+    ok = layer_sync(a, ++nbar, &flag_s);
+
+    // ---- D: down items (routed blocks from LDS, shared columns) ----
+    if (ok) {
+        const int q2 = lane % LPR2;
+        const int myslot2 = ws * RPL2 + lane / LPR2;
+        const int nslots2 = a.na2 * RPL2;
+        const int G2 = a.G2;
+        for (int r = 0; r < a.R2; ++r) {
+            const int i = layer_item(P, b, sub, r);
+            float* rd = red + sub * kLayerRed;
+            uint4* hs = reinterpret_cast<uint4*>(dyn) + (size_t)sub * K8_2;
+            float4* hsum = reinterpret_cast<float4*>(dyn + (size_t)2 * K8_2 * 16) + sub * G2;
+            // the h rows of both sub-groups' routed items, staged together
+            const bool rt = i < n_rt2;
+            const int slot = rt ? i / a.nCB2 : 0;
+            const int cb2 = rt ? i - slot * a.nCB2 : 0;
+            const int col2 = cb2 * NB2 + 4 * q2;
+            const smoe_w4_mat wm2 = slot_mat<2>(mat_s, slot);
+            const bool good2 = rt && wm2.qweight && wm2.scales && wm2.qzeros;
+            // the block's first group, requested before h is staged (an empty
+            // source where the wave has nothing to compute)
+            const bool v2 = good2 && ws < a.na2;
+            const W4Src src2 = v2 ? make_src<4>(wm2, I, H) : empty_src(a.x);
+            GroupLoad<4> A2;
+            load_group<4>(A2, src2, clamp_group(myslot2, G2), v2 ? col2 : 0, true);
+            __builtin_amdgcn_sched_barrier(0);
+            if (rt) {
+                // the whole row requested at once (16-byte device-scope loads)
+                const int srow = __builtin_amdgcn_readfirstlane(slot);
+                const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
+                    a.h + (size_t)srow * I, (short)0, I * 2, kBufWord3);
+                const int ts = tid % (64 * kSubWaves);
+                u4_t hv[kRowChunksPerThread];
+#pragma unroll
+                for (int u = 0; u < kRowChunksPerThread; ++u)
+                    hv[u] = __builtin_amdgcn_raw_buffer_load_b128(
+                        hr, (ts + u * 64 * kSubWaves) * 16, 0, kAuxDev);
+#pragma unroll
+                for (int u = 0; u < kRowChunksPerThread; ++u) {
+                    const int c = ts + u * 64 * kSubWaves;
+                    if (c < K8_2) hs[c] = permute_chunk<4>(__builtin_bit_cast(uint4, hv[u]));
+                }
+            }
+            __syncthreads();
+            if (rt) {
+                for (int gg = tid % (64 * kSubWaves); gg < G2; gg += 64 * kSubWaves) {
+                    const uint4* xr = hs + gg * QF<4>::kChunks;
+                    float s4[2] = {0.0f, 0.0f};
+#pragma unroll 4
+                    for (int c = 0; c < QF<4>::kChunks; ++c) {
+                        const uint4 p = xr[c];
+                        const h2_t x0 = as_h2(p.x), x1 = as_h2(p.y), x2 = as_h2(p.z), x3 = as_h2(p.w);
+                        s4[0] += ((float)x0.x + (float)x0.y) + ((float)x2.x + (float)x2.y);
+                        s4[1] += ((float)x1.x + (float)x1.y) + ((float)x3.x + (float)x3.y);
+                    }
+                    hsum[gg] = make_float4(s4[0], s4[1], 0.0f, 0.0f);
+                }
+            }
+            __syncthreads();
+            if (rt) {
+                if (!good2 && tid % (64 * kSubWaves) == 0 && cb2 == 0)
+                    flag_error(a.err, SMOE_DERR_NULL_EXPERT);
+                if (v2) {
+                    float acc[1][4] = {{0.0f, 0.0f, 0.0f, 0.0f}};
+                    auto ld = [&](GroupLoad<4>& L, int g) { load_group<4>(L, src2, g, col2, true); };
+                    item_groups<NG2>(ld, hs, hsum, myslot2, nslots2, G2, K8_2, zero_shift<4>(col2),
+                                     acc, A2);
+                    item_partials<LPR2>(acc, rd, ws, lane);
+                }
+            } else {
+                if constexpr (CPLS2 > 0) {
+                    if (i < a.n_dn)
+                        shared_item<2, CPLS2, 1, true>(a.sh_h, a.sw2, a.Is, 0, H, i - n_rt2, ws,
+                                                       lane, a.sh_out);
+                }
+            }
+            __syncthreads();
+            if (rt) {
+                const int cb = i - slot * a.nCB2;
+                const smoe_w4_mat wm = slot_mat<2>(mat_s, slot);
+                const int ts = tid % (64 * kSubWaves);
+                if (wm.qweight && wm.scales && wm.qzeros && ts < NB2 && cb * NB2 + ts < H) {
+                    float v = 0.0f;
+                    for (int w = 0; w < a.na2; ++w) v += rd[w * NB2 + ts];
+                    st_dev(a.y + (size_t)slot * H + cb * NB2 + ts, f2h(v));
+                }
+            }
+            __syncthreads();
+        }
+        ok = layer_sync(a, ++nbar, &flag_s);
+    }
+
+    // ---- F: combine (+ norm, + the next layer's router logits) ----
+    if (ok && b < a.nF) {
+        if (wave == 0)
+            smoe_route::topk_softmax_wave(lg_s, E, k, a.renorm, a.wsg != nullptr, lane, ids_w,
+                                          w_s, &gate_s, nullptr);
+        __syncthreads();
+        const int nch = H / 8;
+        uint4* row = reinterpret_cast<uint4*>(dyn);
+        const bool writer = b == 0;
+        float sq = 0.0f;
+        if (tid < smoe_comb::kCombThreads)
+            for (int c8 = tid; c8 < nch; c8 += smoe_comb::kCombThreads) {
+                float acc[8];
+                smoe_comb::combine_chunk(a.y, pp_s, w_s, a.sw13 ? a.sh_out : nullptr,
+                                         a.wsg ? &gate_s : nullptr, a.resid, 0, k, H, c8, acc,
+                                         DevRows());
+                const uint4 ov = smoe_comb::round_chunk(acc, sq);
+                row[c8] = ov;
+                if (writer) reinterpret_cast<uint4*>(a.out)[c8] = ov;
+            }
+        if (a.norm_out) {
+            const float inv = smoe_comb::row_inv_rms(sq, H, a.eps, redf);
+            if (tid < smoe_comb::kCombThreads)
+                for (int c8 = tid; c8 < nch; c8 += smoe_comb::kCombThreads) {
+                    const uint4 qv = smoe_comb::norm_chunk(row[c8], inv);
+                    row[c8] = qv;
+                    if (writer) reinterpret_cast<uint4*>(a.norm_out)[c8] = qv;
+                }
+            __syncthreads();
+            if (a.wr_next)
+                smoe_route::wave_logits(reinterpret_cast<const uint16_t*>(row), a.wr_next,
+                                        a.wsg_next, H, a.E_next, a.nvec_next,
+                                        b * kLayerWaves + wave, a.nvec_next, a.nF * kLayerWaves,
+                                        a.lg_next, lane);
+        }
+    }
+    layer_exit(a);
+}
+
 struct PhasePlan {
     int lpr, nCB, waves, mch, xr, direct;
     int ng;  // one-token workgroups: groups per slot (ceil(G / slots per workgroup))
@@ -1659,5 +2251,166 @@ hipError_t launch_draft_route_ffn(const uint16_t* x, const uint16_t* wr, const u
     }
 #undef SMOE_DOWN_SH
     return hipGetLastError();
+}
+}  // namespace smoe
+
+// ------------------------------------------------ one-launch draft layer ----
+namespace {
+
+struct LayerPlan {
+    PhasePlan p1, p2;
+    int P, row_bytes, lds, cs1, cs2, nsh1, nsh2, variant;
+};
+
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (!cus[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// Instantiated geometries (gate/up LPR and groups per slot, down LPR and
+// groups per slot, shared-expert chunks per lane of gate/up and down):
+//   0: 16/2, 8/2, none       (H 4096, I 6400: the Phi-3.5-MoE layer)
+//   1: 16/1, 16/1, none      (H 2048, I 1408)
+//   2: 16/1, 16/1, 4 / 6     (H 2048, I 1408, shared I 2816: DeepSeek-V2-Lite)
+//   3: 16/1, 16/1, 4 / 12    (H 2048, I 1408, shared I 5632: Qwen1.5-MoE)
+constexpr int kLayerStatic = 4096;            // the kernel's static arrays (< 4 KB)
+constexpr int kLayerLdsMax = 160 * 1024;
+constexpr int kLayerLdsOnePerCU = 84 * 1024;  // more than half a CU's LDS
+
+bool plan_layer(int H, int I, int E, int k, int Is, LayerPlan& L) {
+    if (E < 1 || E > kSpecTable || k < 1 || k > kFusedMaxK || k > E) return false;
+    if (H % 128 || I % 128 || H > 8192 || I > 16384 || H <= 0 || I <= 0) return false;
+    L.p1 = plan_phase(1, k, 1, H, 2 * I, I, 1, 4);
+    L.p2 = plan_phase(2, k, 1, I, H, I, 1, 4);
+    if (L.p1.waves > kSubWaves || L.p2.waves > kSubWaves) return false;
+    L.cs1 = Is ? smoe_gemv::chunks_for(H) : 0;
+    L.cs2 = Is ? smoe_gemv::chunks_for(Is) : 0;
+    const int g1 = L.p1.lpr * 10 + L.p1.ng, g2 = L.p2.lpr * 10 + L.p2.ng;
+    L.variant = -1;
+    if (g1 == 162 && g2 == 82 && !Is) L.variant = 0;
+    if (g1 == 161 && g2 == 161) {
+        if (!Is) L.variant = 1;
+        else if (L.cs1 == 4 && L.cs2 == 6) L.variant = 2;
+        else if (L.cs1 == 4 && L.cs2 == 12) L.variant = 3;
+    }
+    if (L.variant < 0) return false;
+    const int NB2 = 4 * L.p2.lpr;
+    if (H % NB2) return false;
+    L.P = device_cus();
+    if (L.P <= 0) return false;
+    const int G2 = I / 128, G1 = H / 128;
+    int rb = H / 8 * 16 + G1 * 16;
+    rb = std::max(rb, 2 * (I / 8) * 16 + 2 * G2 * 16);
+    rb = std::max(rb, 2 * H);
+    L.row_bytes = (rb + 255) & ~255;
+    L.lds = L.row_bytes + 2 * kLayerRed * 4;  // dynamic part
+    if (kLayerStatic + L.lds > kLayerLdsMax) return false;
+    // one workgroup per CU: every CU streams its share
+    L.lds = std::max(L.lds, kLayerLdsOnePerCU - kLayerStatic);
+    L.nsh1 = Is ? (Is + 2 * kSubWaves - 1) / (2 * kSubWaves) : 0;
+    L.nsh2 = Is ? (H + kSubWaves - 1) / kSubWaves : 0;
+    return true;
+}
+
+template <int LPR1, int NG1, int LPR2, int NG2, int CPLS1, int CPLS2>
+hipError_t launch_layer_variant(const LayerArgs& a, int lds, hipStream_t s) {
+    static int lds_set = 0;  // the dynamic LDS limit raised for this instantiation
+    auto fn = draft_layer_kernel<LPR1, NG1, LPR2, NG2, CPLS1, CPLS2>;
+    if (lds > lds_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        lds_set = lds;
+    }
+    hipLaunchKernelGGL(fn, dim3(a.P), dim3(64 * kLayerWaves), lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+namespace smoe {
+bool draft_layer_supported(int H, int I, int E, int k, int Is) {
+    LayerPlan L;
+    return plan_layer(H, I, E, k, Is, L);
+}
+
+size_t draft_layer_workspace_bytes(int k, int I, int E) {
+    const size_t lg = ((size_t)4 * (E + 1) + 255) & ~(size_t)255;
+    return 256 + lg + h_bytes(1, k, I);
+}
+
+hipError_t launch_draft_layer(const DraftLayerCall& c, hipStream_t s) {
+    LayerPlan L;
+    if (!plan_layer(c.H, c.I, c.E, c.k, c.sw13 ? c.Is : 0, L)) return hipErrorNotSupported;
+    LayerArgs a{};
+    char* ws = static_cast<char*>(c.ws);
+    a.sync = reinterpret_cast<uint32_t*>(ws);
+    a.lg_ws = reinterpret_cast<float*>(ws + 256);
+    a.h = reinterpret_cast<uint16_t*>(ws + 256 + (((size_t)4 * (c.E + 1) + 255) & ~(size_t)255));
+    a.x = c.x;
+    a.wr = c.wr;
+    a.wsg = c.wsg;
+    a.logits = c.logits;
+    a.H = c.H;
+    a.I = c.I;
+    a.E = c.E;
+    a.k = c.k;
+    a.renorm = c.renorm;
+    a.nvec = c.E + (c.wsg ? 1 : 0);
+    a.experts = c.experts;
+    a.counters_row = c.counters_row;
+    a.ids = c.ids;
+    a.w = c.w;
+    a.gate = c.gate;
+    a.off = c.off;
+    a.sorted_token = c.st;
+    a.sorted_pair = c.sp;
+    a.pair_pos = c.pp;
+    a.active = c.active;
+    a.n_active = c.n_active;
+    a.sw13 = c.sw13;
+    a.sw2 = c.sw13 ? c.sw2 : nullptr;
+    a.Is = c.sw13 ? c.Is : 0;
+    a.sh_h = c.sh_h;
+    a.y = c.y;
+    a.sh_out = c.sh_out;
+    a.resid = c.resid;
+    a.out = c.out;
+    a.norm_out = c.norm_out;
+    a.eps = c.eps;
+    a.wr_next = c.norm_out ? c.wr_next : nullptr;
+    a.wsg_next = a.wr_next ? c.wsg_next : nullptr;
+    a.E_next = c.E_next;
+    a.nvec_next = a.wr_next ? c.E_next + (c.wsg_next ? 1 : 0) : 0;
+    a.lg_next = c.lg_next;
+    a.err = c.err;
+    a.P = L.P;
+    a.nCB1 = L.p1.nCB;
+    a.na1 = L.p1.waves;
+    a.nCB2 = L.p2.nCB;
+    a.na2 = L.p2.waves;
+    a.G2 = c.I / 128;
+    a.n_gu = c.k * L.p1.nCB + L.nsh1;
+    a.n_dn = c.k * L.p2.nCB + L.nsh2;
+    a.R1 = (a.n_gu + 2 * L.P - 1) / (2 * L.P);
+    a.R2 = (a.n_dn + 2 * L.P - 1) / (2 * L.P);
+    a.nF = a.wr_next ? (a.nvec_next + kLayerWaves - 1) / kLayerWaves : 1;
+    if (a.nF > L.P) return hipErrorNotSupported;
+    a.row_bytes = L.row_bytes;
+    switch (L.variant) {
+        case 0: return launch_layer_variant<16, 2, 8, 2, 0, 0>(a, L.lds, s);
+        case 1: return launch_layer_variant<16, 1, 16, 1, 0, 0>(a, L.lds, s);
+        case 2: return launch_layer_variant<16, 1, 16, 1, 4, 6>(a, L.lds, s);
+        case 3: return launch_layer_variant<16, 1, 16, 1, 4, 12>(a, L.lds, s);
+        default: return hipErrorNotSupported;
+    }
 }
 }  // namespace smoe

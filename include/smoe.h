@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SMOE_ABI_VERSION 4
+#define SMOE_ABI_VERSION 5
 
 typedef enum {
     SMOE_OK = 0,
@@ -56,6 +56,7 @@ typedef enum {
 /* device-side data error bits (OR-ed into err_word) */
 #define SMOE_DERR_BAD_ID      1   /* an expert id outside [0, E)            */
 #define SMOE_DERR_NULL_EXPERT 2   /* a touched expert has a NULL weight     */
+#define SMOE_DERR_SYNC        4   /* moe_draft_layer: a grid barrier timed out */
 
 /* Version of this header's ABI; the binding refuses a mismatched library. */
 int smoe_abi_version(void);
@@ -361,6 +362,68 @@ smoe_status moe_draft_route_ffn(const uint16_t* x, const uint16_t* w_router,
                                 int32_t* err_word, void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_draft_layer -- one-token (T = 1) draft step of a whole MoE layer in a
+ * single launch ([S1] Key Contributions 4 and Methodology in Plain English:
+ * the draft's routing and expert sub-computations are dispatched inside one
+ * fused GPU launch): the router logits (unless given), the top-k routing
+ * with the ELB update and the maps, the routed INT4 experts' FFN, the
+ * optional FP16 shared expert, and the combine with residual, norm epilogue
+ * and the next layer's router logits.  One workgroup per CU, all resident;
+ * phases are separated by grid barriers inside the launch.
+ *
+ * Arguments keep the meaning and layout of moe_draft_route_ffn (x,
+ * w_router, w_shared_gate, logits, H, I, E, k, renormalize, layer, L,
+ * counters, experts, group_size, the routing outputs, y_sorted, the shared
+ * expert and shared_h) followed by those of moe_combine_route_logits
+ * (residual, out, norm_out, norm_eps, next_w_router, next_w_shared_gate,
+ * next_E, next_logits), all for this one token:
+ *   logits         fp32 [E (+1)] of x from the launch before, or NULL: the
+ *                  call computes them itself (one more grid barrier)
+ *   y_sorted       fp16 [k, H] out, shared_out fp16 [1, H] out, shared_h
+ *                  fp16 [shared_I] scratch: written inside the launch
+ *   residual       fp16 [1, H] or NULL; out fp16 [1, H] out (required)
+ *   norm_out       fp16 [1, H] out or NULL (no norm epilogue)
+ *   next_w_router  fp16 [next_E, H] or NULL; with it norm_out and
+ *                  next_logits (fp32 [next_E (+1)]) are required
+ *   workspace      >= smoe_workspace_bytes(2, 1, k, H, I, E) bytes,
+ *                  256-byte aligned; its first 8 bytes are the barrier
+ *                  counters and must be zero before the first call (every
+ *                  completed call leaves them zero; new workspaces from the
+ *                  binding are zero-filled).
+ * Every output is bit-identical to moe_draft_route_ffn followed by
+ * moe_combine (or moe_combine_route_logits): same kernels' arithmetic and
+ * summation orders.
+ * Limits: E <= 64, k <= 32, H and I multiples of 128 with H <= 8192; the
+ * instantiated geometries are those of the Phi-3.5-MoE (H 4096, I 6400, no
+ * shared expert), DeepSeek-V2-Lite (H 2048, I 1408, shared I 2816) and
+ * Qwen1.5-MoE (H 2048, I 1408, shared I 5632) layers, and H 2048, I 1408
+ * without a shared expert.  Any other shape returns SMOE_ERR_UNSUPPORTED
+ * before anything is enqueued (use moe_draft_route_ffn and
+ * moe_combine_route_logits instead).  smoe_draft_layer_supported tells.
+ * Device errors: SMOE_DERR_SYNC when a grid barrier waited longer than
+ * 100 ms (a workgroup was not resident: another kernel held its CU); the
+ * outputs are then undefined and the workspace's counters must be zeroed
+ * before the next call.  Calls sharing a workspace must not overlap.
+ * ---------------------------------------------------------------------- */
+smoe_status moe_draft_layer(const uint16_t* x, const uint16_t* w_router,
+                            const uint16_t* w_shared_gate, const float* logits, int H, int I,
+                            int E, int k, int renormalize, int layer, int L, int32_t* counters,
+                            const smoe_w4_expert* experts, int group_size, int32_t* topk_ids,
+                            float* topk_w, float* shared_gate, int32_t* expert_offsets,
+                            int32_t* sorted_token, int32_t* sorted_pair, int32_t* pair_pos,
+                            int32_t* active, int32_t* n_active, uint16_t* y_sorted,
+                            const uint16_t* shared_w13, const uint16_t* shared_w2, int shared_I,
+                            uint16_t* shared_h, uint16_t* shared_out, const uint16_t* residual,
+                            uint16_t* out, uint16_t* norm_out, float norm_eps,
+                            const uint16_t* next_w_router, const uint16_t* next_w_shared_gate,
+                            int next_E, float* next_logits, void* workspace,
+                            size_t workspace_bytes, int32_t* err_word, void* stream);
+
+/* 1 when moe_draft_layer has an instantiation for this shape (shared_I = 0:
+ * no shared expert) on the current device, else 0. */
+int smoe_draft_layer_supported(int H, int I, int E, int k, int shared_I);
+
+/* ------------------------------------------------------------------------
  * moe_combine_route_logits -- one token (T = 1): moe_combine of a layer's
  * expert outputs with its norm epilogue, and in the same launch the next
  * layer's router logits of the normalised row ([S1] Key Contributions 4:
@@ -472,8 +535,9 @@ smoe_status expert_stage_async(void* dst_device, const void* src_pinned_host, si
 smoe_status smoe_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks,
                              void* stream);
 
-/* Workspace size in bytes for which = 0 (w4a16_grouped_ffn) or
- * 1 (verify_grouped_gemm); 0 for an invalid request. */
+/* Workspace size in bytes for which = 0 (w4a16_grouped_ffn), 1
+ * (verify_grouped_gemm) or 2 (moe_draft_layer, T = 1); 0 for an invalid
+ * request. */
 size_t smoe_workspace_bytes(int which, int T, int k, int H, int I, int E);
 
 #ifdef __cplusplus

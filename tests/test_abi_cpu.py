@@ -20,7 +20,7 @@ def test_exports_every_header_function():
     expected = {"smoe_abi_version", "smoe_last_error", "moe_route_topk", "elb_count",
                 "moe_gather", "moe_route_plan", "w4a16_grouped_ffn", "wq_grouped_ffn",
                 "moe_draft_route_ffn", "w4a16_grouped_ffn_noalloc", "moe_combine_route_logits",
-                "awq_grouped_ffn",
+                "awq_grouped_ffn", "moe_draft_layer", "smoe_draft_layer_supported",
                 "verify_grouped_gemm", "moe_combine",
                 "expert_stage_async", "smoe_workspace_bytes", "smoe_stream_read"}
     assert set(names) == expected
@@ -179,6 +179,45 @@ def test_draft_route_ffn_validation():
     assert call(lg=FAKE, ws=None) == 6
 
 
+def test_draft_layer_validation():
+    L = fve.lib()
+    maps = [FAKE] * 6   # offsets, sorted_token, sorted_pair, pair_pos, active, n_active
+    need = L.smoe_workspace_bytes(2, 1, 2, 256, 512, 8)
+    assert need > 0
+
+    def call(x=FAKE, wr=FAKE, wsg=None, lg=None, H=256, I=512, E=8, k=2, layer=0, Lc=1,
+             counters=FAKE, table=FAKE, gs=128, gate=None, y=FAKE, sh=(None, None, 0, None, None),
+             res=None, out=V(0x3000), nrm=None, eps=1e-6, nxt=(None, None, 0, None), ws=FAKE,
+             wsb=None):
+        return L.moe_draft_layer(x, wr, wsg, lg, H, I, E, k, 0, layer, Lc, counters, table, gs,
+                                 FAKE, FAKE, gate, *maps, y, *sh, res, out, nrm, eps, *nxt, ws,
+                                 need if wsb is None else wsb, None, None)
+    assert call(x=None) == 1
+    assert call(table=None) == 1
+    assert call(y=None) == 1
+    assert call(out=None) == 1 and "required" in _err()
+    assert call(wsg=FAKE) == 1                      # gate output missing
+    assert call(sh=(FAKE, FAKE, 1024, FAKE, None)) == 1 and "shared_out" in _err()
+    assert call(nxt=(FAKE, None, 8, V(0x4000))) == 1 and "norm_out" in _err()
+    assert call(nxt=(FAKE, None, 8, None), nrm=V(0x5000)) == 1
+    assert call(H=200) == 2
+    assert call(I=500) == 2
+    assert call(k=9) == 2
+    assert call(sh=(FAKE, FAKE, 1000, FAKE, FAKE)) == 2 and "shared_I" in _err()
+    assert call(nxt=(FAKE, None, 0, V(0x4000)), nrm=V(0x5000)) == 2 and "next_E" in _err()
+    assert call(gs=64) == 3
+    assert call(layer=1, Lc=1) == 2                 # layer outside [0, L)
+    assert call(nrm=V(0x3000)) == 2                 # norm_out aliases out
+    assert call(eps=-1.0) == 2
+    assert call(x=V(0x1002)) == 2 and "aligned" in _err()
+    assert call(lg=V(0x1002)) == 2 and "aligned" in _err()
+    assert call(res=V(0x1002)) == 2 and "aligned" in _err()
+    assert call(wsb=need - 1) == 6
+    assert call(ws=None) == 6
+    # no device here: the shape query answers no
+    assert L.smoe_draft_layer_supported(4096, 6400, 16, 2, 0) == 0
+
+
 def test_combine_route_logits_validation():
     L = fve.lib()
 
@@ -306,5 +345,8 @@ def test_workspace_sizes():
     L = fve.lib()
     assert L.smoe_workspace_bytes(0, 1, 6, 2048, 1408, 64) > 0
     assert L.smoe_workspace_bytes(0, 1, 6, 2000, 1408, 64) == 0
-    assert L.smoe_workspace_bytes(2, 1, 6, 2048, 1408, 64) == 0
+    # moe_draft_layer (T = 1 only): barrier words, the logits, h [k, I]
+    assert L.smoe_workspace_bytes(2, 1, 6, 2048, 1408, 64) == 256 + 512 + 6 * 1408 * 2
+    assert L.smoe_workspace_bytes(2, 2, 6, 2048, 1408, 64) == 0
+    assert L.smoe_workspace_bytes(3, 1, 6, 2048, 1408, 64) == 0
     assert L.smoe_workspace_bytes(1, 17, 2, 4096, 6400, 16) >= 34 * 6400 * 2
