@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsmoe.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "smoe.h")
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 SMOE_DERR_BAD_ID = 1
 SMOE_DERR_NULL_EXPERT = 2
@@ -72,6 +72,8 @@ _SIGS = {
     "smoe_draft_layer_supported": (_i, [_i, _i, _i, _i, _i]),
     "verify_grouped_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp,
                                  _vp, _sz, _vp, _vp]),
+    "verify_grouped_gemm_shared": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                        _vp, _vp, _vp, _i, _vp, _vp, _vp, _sz, _vp, _vp]),
     "moe_combine": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, ctypes.c_float,
                          _vp]),
     "expert_stage_async": (_i, [_vp, _vp, _sz, _vp, _vp]),
@@ -486,6 +488,32 @@ def verify_grouped_gemm(x, sorted_token, offsets, table, T: int, rows: int, H: i
           _p(n_active), _p(table), _p(expert_mask), T, rows, H, I, E, _p(y_sorted),
           _p(workspace), workspace.numel() * workspace.element_size(), _p(err_word), _s(stream))
     return y_sorted
+
+
+def verify_grouped_gemm_shared(x, sorted_token, offsets, table, T: int, rows: int, H: int,
+                               I: int, E: int, workspace, shared, *, active=None, n_active=None,
+                               expert_mask=None, y_sorted=None, shared_h=None, shared_out=None,
+                               err_word=None, stream=None):
+    """verify_grouped_gemm over the routed experts and the dense shared
+    expert shared = (w13 [2 Is, H], w2 [H, Is]) over all T rows of x in the
+    same launches.  Returns (y_sorted, shared_out [T, H])."""
+    _check(x, torch.float16, "x")
+    sw13, sw2 = shared
+    _check(sw13, torch.float16, "shared w13")
+    _check(sw2, torch.float16, "shared w2")
+    Is = sw2.shape[1]
+    dev = x.device
+    if y_sorted is None:
+        y_sorted = torch.empty((max(rows, 1), H), dtype=torch.float16, device=dev)
+    if shared_h is None:
+        shared_h = torch.empty((T, Is), dtype=torch.float16, device=dev)
+    if shared_out is None:
+        shared_out = torch.empty((T, H), dtype=torch.float16, device=dev)
+    _call("verify_grouped_gemm_shared", _p(x), _p(sorted_token), _p(offsets), _p(active),
+          _p(n_active), _p(table), _p(expert_mask), T, rows, H, I, E, _p(y_sorted), _p(sw13),
+          _p(sw2), Is, _p(shared_h), _p(shared_out), _p(workspace),
+          workspace.numel() * workspace.element_size(), _p(err_word), _s(stream))
+    return y_sorted, shared_out
 
 
 def moe_combine(y_sorted, pair_pos, topk_w, shared_out=None, shared_scale=None, residual=None,

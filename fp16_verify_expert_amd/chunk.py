@@ -28,7 +28,8 @@ import torch
 
 from . import (expert_stage_async, f16_expert_table, moe_combine, moe_combine_route_logits,
                moe_draft_route_ffn, moe_gather, moe_route_plan,
-               moe_route_topk, new_workspace, verify_grouped_gemm, w4_expert_table,
+               moe_route_topk, new_workspace, verify_grouped_gemm, verify_grouped_gemm_shared,
+               w4_expert_table,
                w4a16_grouped_ffn)
 
 
@@ -68,6 +69,7 @@ class _StepBuffers:
         self.ws_w4 = new_workspace(0, T, k, H, I, E, device=dev)
         self.ws_f16 = new_workspace(1, T, k, H, I, E, device=dev)
         self.sh_out = torch.empty((T, H), dtype=f16, device=dev) if Is else None
+        self.sh_h = torch.empty((T, Is), dtype=f16, device=dev) if Is else None
         self.ws_sh = new_workspace(1, T, 1, H, Is, 1, device=dev) if Is else None
         self.iota = torch.arange(T, dtype=i32, device=dev)
         self.offs = torch.tensor([0, T], dtype=i32, device=dev)
@@ -275,15 +277,12 @@ class ChunkEngine:
                                         topk_ids=b.ids, topk_w=b.w,
                                         shared_gate=b.gate if ly.shared_gate is not None else None)
             moe_gather(b.ids, self.E, self.err, out=b.maps)
-            sh = self._shared(l, xn)
             if kind == "int4":
+                sh = self._shared(l, xn)
                 w4a16_grouped_ffn(xn, b.maps, self.t4[l], T, self.k, self.H, self.I, self.E,
                                   b.ws_w4, y_sorted=b.y, err_word=self.err)
             else:
-                verify_grouped_gemm(xn, b.maps["sorted_token"], b.maps["offsets"],
-                                    self._resident_table(full, l), T, T * self.k, self.H, self.I,
-                                    self.E, b.ws_f16, active=b.maps["active"],
-                                    n_active=b.maps["n_active"], y_sorted=b.y, err_word=self.err)
+                sh = self._verify_f16(l, xn, b, self._resident_table(full, l))
             out, xn_next = self._combine(l, b, b.y, sh, gate, x, fresh)
             self._record(record, l, x, xn, b.ids, out, xn_next)
             x, xn = out, xn_next
@@ -446,20 +445,13 @@ class ChunkEngine:
                                             topk_ids=b.ids, topk_w=b.w, shared_gate=g_out)
                 moe_gather(b.ids, self.E, self.err, out=b.maps)
             maps = b.maps
-            # the shared expert in line on the caller's stream: on a side
-            # stream beside the routed experts the 17-token verify was slower
-            # (4.25 against 4.17 ms over 24 layers; a cross-stream join costs
-            # about 6 us and the concurrent launches slow each other)
-            sh = self._shared(l, xn)
-            rows = T * self.k
+            # the shared expert's items ride in the routed experts' launches
+            # (verify_grouped_gemm_shared): as launches of their own after
+            # them, or on a side stream beside them, the layer was slower
             if all_resident is not None:
-                verify_grouped_gemm(xn, maps["sorted_token"], maps["offsets"],
-                                    self._resident_table(all_resident, l),
-                                    T, rows, self.H, self.I, self.E, b.ws_f16,
-                                    active=maps["active"], n_active=maps["n_active"],
-                                    y_sorted=b.y, err_word=self.err)
+                sh = self._verify_f16(l, xn, b, self._resident_table(all_resident, l))
             else:
-                self._verify_staged(l, xn, maps, b.y, b.ws_f16, main)
+                sh = self._verify_staged(l, xn, maps, b, main)
             out, xn_next = self._combine(l, b, b.y, sh, gate, x, fresh)
             self._record(record, l, x, xn, b.ids, out, xn_next)
             x, xn = out, xn_next
@@ -482,9 +474,27 @@ class ChunkEngine:
             self._full_key = key
         return self._full_tab[l]
 
-    def _verify_staged(self, l, x, maps, y, ws, main) -> None:
+    def _verify_f16(self, l, x, b, table, mask=None):
+        """The FP16 routed experts of layer l from `table` (optionally only
+        those with mask 1) and its shared expert in the same launches; returns
+        the shared output (None without one)."""
+        T = x.shape[0]
+        kw = dict(active=b.maps["active"], n_active=b.maps["n_active"], expert_mask=mask,
+                  y_sorted=b.y, err_word=self.err)
+        sh = self.layers[l].shared
+        if sh is None:
+            verify_grouped_gemm(x, b.maps["sorted_token"], b.maps["offsets"], table, T,
+                                T * self.k, self.H, self.I, self.E, b.ws_f16, **kw)
+            return None
+        verify_grouped_gemm_shared(x, b.maps["sorted_token"], b.maps["offsets"], table, T,
+                                   T * self.k, self.H, self.I, self.E, b.ws_f16, sh,
+                                   shared_h=b.sh_h, shared_out=b.sh_out, **kw)
+        return b.sh_out
+
+    def _verify_staged(self, l, x, maps, bufs, main):
         T = x.shape[0]
         rows = T * self.k
+        y, ws = bufs.y, bufs.ws_f16
         act = maps["active"].cpu().numpy()          # the target router's decisions
         needed = [int(e) for e in act if e >= 0]
         res = self.resident[l]
@@ -513,19 +523,23 @@ class ChunkEngine:
                 last = j == len(misses) - 1
                 expert_stage_async(self.stage[b, j], self.layers[l].host_f16[e], self.side,
                                    self.ev_staged[b] if last else None)
-        kw = dict(active=maps["active"], n_active=maps["n_active"], y_sorted=y, err_word=self.err)
+        # the shared expert rides in the first of the two launches
+        sh = None
         if hits:
             main.wait_event(self.ev_layer[l])  # this layer's prefetches (if any) have landed
-            verify_grouped_gemm(x, maps["sorted_token"], maps["offsets"], self.d_table[l], T, rows,
-                                self.H, self.I, self.E, ws, expert_mask=self.d_mask[l, 0],
-                                **kw)
+            sh = self._verify_f16(l, x, bufs, self.d_table[l], self.d_mask[l, 0])
         if misses:
             main.wait_event(self.ev_staged[b])
-            verify_grouped_gemm(x, maps["sorted_token"], maps["offsets"], self.d_table[l], T, rows,
-                                self.H, self.I, self.E, ws, expert_mask=self.d_mask[l, 1],
-                                **kw)
+            if hits:
+                verify_grouped_gemm(x, maps["sorted_token"], maps["offsets"], self.d_table[l], T,
+                                    rows, self.H, self.I, self.E, ws, active=maps["active"],
+                                    n_active=maps["n_active"], expert_mask=self.d_mask[l, 1],
+                                    y_sorted=y, err_word=self.err)
+            else:
+                sh = self._verify_f16(l, x, bufs, self.d_table[l], self.d_mask[l, 1])
             self.ev_free[b].record(main)
         self.stats["hit_experts"] += len(hits)
         self.stats["miss_experts"] += len(misses)
         self.stats["staged_experts"] += len(misses)
         self.stats["staged_bytes"] += len(misses) * self.ebytes
+        return sh

@@ -1,5 +1,6 @@
 // C ABI of libsmoe.so: host-side argument checks, device check, dispatch.
 // Every check runs before anything is enqueued; no call allocates memory.
+#include <atomic>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -145,6 +146,22 @@ smoe_status scratch_address(void** out) {
 constexpr int kSharedMaxK = 8192;
 
 }  // namespace
+
+namespace smoe {
+// CUs of the current device (cached per device); 0 if it cannot be queried.
+int device_cu_count() {
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (!n) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+}  // namespace smoe
 
 extern "C" {
 
@@ -574,6 +591,47 @@ smoe_status verify_grouped_gemm(const uint16_t* x, const int32_t* sorted_token,
                                               workspace, err_word,
                                               static_cast<hipStream_t>(stream)),
                       "verify_grouped_gemm launch");
+}
+
+smoe_status verify_grouped_gemm_shared(const uint16_t* x, const int32_t* sorted_token,
+                                       const int32_t* expert_offsets, const int32_t* active,
+                                       const int32_t* n_active, const smoe_f16_expert* experts,
+                                       const uint8_t* expert_mask, int T, int rows, int H, int I,
+                                       int E, uint16_t* y_sorted, const uint16_t* shared_w13,
+                                       const uint16_t* shared_w2, int shared_I,
+                                       uint16_t* shared_h, uint16_t* shared_out, void* workspace,
+                                       size_t workspace_bytes, int32_t* err_word, void* stream) {
+    REQUIRE(x && sorted_token && expert_offsets && experts && y_sorted, SMOE_ERR_NULL,
+            "verify_grouped_gemm_shared: a required pointer is NULL");
+    REQUIRE(shared_w13 && shared_w2 && shared_h && shared_out, SMOE_ERR_NULL,
+            "verify_grouped_gemm_shared: shared_w13, shared_w2, shared_h and shared_out are "
+            "required");
+    REQUIRE((active == nullptr) == (n_active == nullptr), SMOE_ERR_NULL,
+            "verify_grouped_gemm_shared: pass both active and n_active, or neither");
+    REQUIRE(T >= 0 && rows >= 0, SMOE_ERR_SHAPE, "verify_grouped_gemm_shared: T=%d, rows=%d", T,
+            rows);
+    REQUIRE(H > 0 && H % 128 == 0 && I > 0 && I % 128 == 0, SMOE_ERR_SHAPE,
+            "verify_grouped_gemm_shared: H=%d and I=%d must be positive multiples of 128", H, I);
+    REQUIRE(shared_I > 0 && shared_I % 128 == 0, SMOE_ERR_SHAPE,
+            "verify_grouped_gemm_shared: shared_I=%d must be a positive multiple of 128",
+            shared_I);
+    REQUIRE(E >= 1 && E <= 256, SMOE_ERR_SHAPE,
+            "verify_grouped_gemm_shared: E=%d must be in [1, 256]", E);
+    REQUIRE(rows <= kMaxPairs, SMOE_ERR_SHAPE, "verify_grouped_gemm_shared: rows exceeds 2^20");
+    REQUIRE(aligned(x, 16) && aligned(shared_w13, 16) && aligned(shared_w2, 16) &&
+                aligned(shared_h, 16) && aligned(shared_out, 16),
+            SMOE_ERR_SHAPE, "verify_grouped_gemm_shared: fp16 tensors must be 16-byte aligned");
+    if (T == 0) return ok();
+    const size_t need = smoe::verify_workspace_bytes(T, rows, H, I, E);
+    REQUIRE(workspace && workspace_bytes >= need && aligned(workspace, 256), SMOE_ERR_WORKSPACE,
+            "verify_grouped_gemm_shared: workspace needs %zu bytes, 256-byte aligned (got %zu)",
+            need, workspace_bytes);
+    CHECK_DEVICE();
+    return hip_result(smoe::launch_verify_ffn_shared(
+                          x, sorted_token, expert_offsets, active, n_active, experts, expert_mask,
+                          T, rows, H, I, E, y_sorted, workspace, shared_w13, shared_w2, shared_I,
+                          shared_h, shared_out, err_word, static_cast<hipStream_t>(stream)),
+                      "verify_grouped_gemm_shared launch");
 }
 
 smoe_status moe_combine(const uint16_t* y_sorted, const int32_t* pair_pos, const float* topk_w,

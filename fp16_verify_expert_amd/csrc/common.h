@@ -29,6 +29,22 @@ SMOE_DEV void flag_error(int32_t* err, int32_t bit) {
     if (err) atomicOr(err, bit);
 }
 
+// Device-scope (agent) accesses: coherent across the XCDs' separate L2
+// caches, for values one workgroup hands to another inside a launch.
+template <typename T>
+SMOE_DEV void st_dev(T* p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+SMOE_DEV T ld_dev(const T* p) {
+    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+SMOE_DEV uint4 ld_dev4(const void* p) {
+    const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+    const uint64_t a = ld_dev(q), b = ld_dev(q + 1);
+    return make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32));
+}
+
 // Number of sorted rows in [0, rows) that belong to expert slot bounds.
 struct RowRange {
     int r0, r1;
@@ -53,6 +69,7 @@ hipError_t launch_elb_count(const int32_t* ids, int n, int E, int layer, int32_t
 hipError_t launch_gather(const int32_t* ids, int n, int k, int E, int32_t* off, int32_t* st,
                          int32_t* sp, int32_t* pp, int32_t* active, int32_t* n_active,
                          int32_t* err, hipStream_t s);
+int device_cu_count();
 // The one-launch draft layer (T = 1): routing, routed INT4 FFN, optional
 // FP16 shared expert, combine and the next layer's logits.
 struct DraftLayerCall {
@@ -116,6 +133,13 @@ hipError_t launch_verify_ffn(const uint16_t* x, const int32_t* sorted_token, con
                              const smoe_f16_expert* experts, const uint8_t* mask, int T, int rows,
                              int H, int I, int E, uint16_t* y, void* ws, int32_t* err,
                              hipStream_t s);
+hipError_t launch_verify_ffn_shared(const uint16_t* x, const int32_t* sorted_token,
+                                    const int32_t* off, const int32_t* active,
+                                    const int32_t* n_active, const smoe_f16_expert* experts,
+                                    const uint8_t* mask, int T, int rows, int H, int I, int E,
+                                    uint16_t* y, void* ws, const uint16_t* sw13,
+                                    const uint16_t* sw2, int Is, uint16_t* sh_h,
+                                    uint16_t* sh_out, int32_t* err, hipStream_t s);
 size_t verify_workspace_bytes(int T, int rows, int H, int I, int E);
 // dense regime of the verify FFN (many rows per expert)
 size_t dense_plan_bytes(int E);

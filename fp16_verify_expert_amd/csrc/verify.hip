@@ -42,6 +42,12 @@ struct F16Args {
     int nCB;    // column blocks: 16 columns, kGemvWaves in the matrix-vector kernel
     uint16_t* out;  // phase 1: h [rows, I]; phase 2: y [rows, H]
     int32_t* err;
+    // an always-on dense group (the shared expert) as the launch's first
+    // ex_nCB work items, over token rows 0..ex_T-1: null ex_w = none
+    const uint16_t* ex_w;   // phase 1: w13 [2 ex_I, H]; phase 2: w2 [H, ex_I]
+    const uint16_t* ex_in;  // phase 2: its h [ex_T, ex_I]
+    uint16_t* ex_out;       // phase 1: its h; phase 2: its output [ex_T, H]
+    int ex_I, ex_nCB, ex_T;
 };
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
@@ -285,25 +291,43 @@ __global__ __launch_bounds__(64 * kVWaves) void f16_kernel(F16Args a) {
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int cb = blockIdx.x % a.nCB;
-    const int slot = blockIdx.x / a.nCB;
-    int e;
-    if (a.active) {
-        e = a.active[slot];  // -1 past the touched experts
-        if (e < 0) return;
+    // the dense group's items first, then the routed (expert, block) items
+    const int exn = a.ex_w ? a.ex_nCB : 0;
+    const bool ex = (int)blockIdx.x < exn;
+    const int item = ex ? (int)blockIdx.x : (int)blockIdx.x - exn;
+    int cb, r0, r1;
+    const uint16_t* W;
+    if (ex) {
+        cb = item;
+        r0 = 0;
+        r1 = a.ex_T;
+        W = a.ex_w;
     } else {
-        e = slot;
+        cb = item % a.nCB;
+        const int slot = item / a.nCB;
+        int e;
+        if (a.active) {
+            e = a.active[slot];  // -1 past the touched experts
+            if (e < 0) return;
+        } else {
+            e = slot;
+        }
+        if (a.mask && !a.mask[e]) return;
+        r0 = a.off[e];
+        r1 = a.off[e + 1];
+        if (r1 <= r0) return;
+        W = (PHASE == 1) ? a.experts[e].w13 : a.experts[e].w2;
+        if (!W) {
+            if (threadIdx.x == 0 && cb == 0) flag_error(a.err, SMOE_DERR_NULL_EXPERT);
+            return;
+        }
     }
-    if (a.mask && !a.mask[e]) return;
-    const int r0 = a.off[e];
-    const int r1 = a.off[e + 1];
-    if (r1 <= r0) return;
-    const uint16_t* W = (PHASE == 1) ? a.experts[e].w13 : a.experts[e].w2;
-    if (!W) {
-        if (threadIdx.x == 0 && cb == 0) flag_error(a.err, SMOE_DERR_NULL_EXPERT);
-        return;
-    }
-    const int K = a.K;
+    const int K = (ex && PHASE == 2) ? a.ex_I : a.K;
+    const int Iup = ex ? a.ex_I : a.I;                  // up rows of w13 start here
+    const int Ncol = (ex && PHASE == 1) ? a.ex_I : a.Ncol;
+    const uint16_t* xin = (ex && PHASE == 2) ? a.ex_in : a.xin;
+    const int32_t* tok = ex ? nullptr : a.sorted_token;
+    uint16_t* out = ex ? a.ex_out : a.out;
     const int nsteps = K / kKStep;
     const int s0 = (nsteps * wave) / kVWaves;
     const int s1 = (nsteps * (wave + 1)) / kVWaves;
@@ -322,7 +346,7 @@ __global__ __launch_bounds__(64 * kVWaves) void f16_kernel(F16Args a) {
     for (int j = 0; j < 4; ++j) {
         const int r = 4 * j + lrow;
         wrow[0][j] = W + (size_t)(n0 + r) * K;
-        if (PHASE == 1) wrow[NM - 1][j] = W + (size_t)(a.I + n0 + r) * K;
+        if (PHASE == 1) wrow[NM - 1][j] = W + (size_t)(Iup + n0 + r) * K;
     }
 
     // One row block; AQ = activation load instructions per tile and step (4
@@ -343,8 +367,8 @@ __global__ __launch_bounds__(64 * kVWaves) void f16_kernel(F16Args a) {
             for (int j = 0; j < 4; ++j) {
                 int r = mb + 16 * b + 4 * j + lrow;
                 if (r >= r1) r = r0;
-                arow[b][j] = (PHASE == 1) ? a.xin + (size_t)a.sorted_token[r] * K
-                                          : a.xin + (size_t)r * K;
+                arow[b][j] = (PHASE == 1) ? xin + (size_t)(tok ? tok[r] : r) * K
+                                          : xin + (size_t)r * K;
             }
         auto issue = [&](int st) {
             char* stage = &ring[wave][st % NSTAGE][0];
@@ -429,7 +453,7 @@ __global__ __launch_bounds__(64 * kVWaves) void f16_kernel(F16Args a) {
                 const int r = mb + 16 * b + 4 * (lane >> 4) + i;
                 if (r < r1) {
                     const float v = (PHASE == 1) ? silu_f(g[i]) * u[i] : g[i];
-                    a.out[(size_t)r * a.Ncol + n0 + (lane & 15)] = f2h(v);
+                    out[(size_t)r * Ncol + n0 + (lane & 15)] = f2h(v);
                 }
             }
         }
@@ -576,7 +600,7 @@ hipError_t launch_gemv_phase(const F16Args& a, int slots, hipStream_t s) {
 
 template <int PHASE, int W, int S>
 hipError_t launch_ring(const F16Args& a, int slots, int RB, hipStream_t s) {
-    const dim3 grid(slots * a.nCB);
+    const dim3 grid(slots * a.nCB + (a.ex_w ? a.ex_nCB : 0));
     if (RB == 1) {
         hipLaunchKernelGGL((f16_kernel<PHASE, 1, S, W>), grid, dim3(64 * W), 0, s, a);
     } else {
@@ -588,8 +612,19 @@ hipError_t launch_ring(const F16Args& a, int slots, int RB, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Which kernel launch_phase runs for the routed items: 0 the register
+// kernel, 1 the 2-wave ring, 2 the 4-wave ring, 3 the one-group ring.
+int phase_kernel(const F16Args& a, int slots) {
+    if (slots == 1 && a.K / kKStep >= 8) return 3;
+    const int nsteps = a.K / kKStep;
+    const long long wgs = (long long)slots * a.nCB;
+    if (nsteps / 2 >= SMOE_VF_LONG && (nsteps < 16 || (nsteps == 16 && wgs > 1024))) return 1;
+    return (nsteps / 4 >= SMOE_VF_LONG) ? 2 : 0;
+}
+
 template <int PHASE>
 hipError_t launch_phase(const F16Args& a, int slots, int RB, hipStream_t s) {
+    const int exn = a.ex_w ? a.ex_nCB : 0;  // ring kernels only (see launch_verify_ffn_shared)
     if (slots == 1 && a.K / kKStep >= 8) {
         if constexpr (PHASE == 1)
             return launch_ring<PHASE, SMOE_SH_GU_WAVES, SMOE_SH_GU_STAGES>(a, slots, RB, s);
@@ -611,14 +646,14 @@ hipError_t launch_phase(const F16Args& a, int slots, int RB, hipStream_t s) {
     const long long wgs = (long long)slots * a.nCB;
     const bool two = nsteps / 2 >= SMOE_VF_LONG && (nsteps < 16 || (nsteps == 16 && wgs > 1024));
     if (two) {
-        const dim3 grid2(slots * a.nCB), block2(128);
+        const dim3 grid2(slots * a.nCB + exn), block2(128);
         if (RB == 1)
             hipLaunchKernelGGL((f16_kernel<PHASE, 1, 3, 2>), grid2, block2, 0, s, a);
         else
             hipLaunchKernelGGL((f16_kernel<PHASE, 2, 2, 2>), grid2, block2, 0, s, a);
         return hipGetLastError();
     }
-    const dim3 grid(slots * a.nCB), block(256);
+    const dim3 grid(slots * a.nCB + (ring ? exn : 0)), block(256);
     if (ring) {
         if (RB == 1)
             hipLaunchKernelGGL((f16_kernel<PHASE, 1, 3, 4>), grid, block, 0, s, a);
@@ -702,5 +737,101 @@ hipError_t launch_verify_ffn(const uint16_t* x, const int32_t* sorted_token, con
     hipError_t st = launch_phase<1>(a1, slots, RB, s);
     if (st != hipSuccess) return st;
     return launch_phase<2>(a2, slots, RB, s);
+}
+
+// The dense shared expert's two projections on their own: launches of its
+// items only (token rows 0..T-1 of x), the one-group ring geometry.
+static hipError_t launch_dense_group(const uint16_t* x, int T, int H, const uint16_t* w13,
+                                     const uint16_t* w2, int Is, uint16_t* sh_h,
+                                     uint16_t* sh_out, int32_t* err, hipStream_t s) {
+    F16Args g{};
+    g.xin = x;
+    g.K = H;
+    g.H = H;
+    g.err = err;
+    g.ex_w = w13;
+    g.ex_out = sh_h;
+    g.ex_I = Is;
+    g.ex_nCB = Is / 16;
+    g.ex_T = T;
+    const int RB = (T <= 16) ? 1 : 2;
+    hipError_t st = launch_ring<1, SMOE_SH_GU_WAVES, SMOE_SH_GU_STAGES>(g, 0, RB, s);
+    if (st != hipSuccess) return st;
+    g.Ncol = H;
+    g.ex_w = w2;
+    g.ex_in = sh_h;
+    g.ex_out = sh_out;
+    g.ex_nCB = H / 16;
+    return launch_ring<2, SMOE_SH_DN_WAVES, SMOE_SH_DN_STAGES>(g, 0, RB, s);
+}
+
+hipError_t launch_verify_ffn_shared(const uint16_t* x, const int32_t* sorted_token,
+                                    const int32_t* off, const int32_t* active,
+                                    const int32_t* n_active, const smoe_f16_expert* experts,
+                                    const uint8_t* mask, int T, int rows, int H, int I, int E,
+                                    uint16_t* y, void* ws, const uint16_t* sw13,
+                                    const uint16_t* sw2, int Is, uint16_t* sh_h,
+                                    uint16_t* sh_out, int32_t* err, hipStream_t s) {
+    // the routed launches' geometry, as launch_verify_ffn picks it
+    const int groups = (E < rows) ? E : rows;
+    const long long kMax32 = 0x7fffffffLL;
+    const bool fits32 = (long long)T * H < kMax32 && (long long)rows * I < kMax32 &&
+                        2LL * I * H < kMax32 && (long long)rows * H < kMax32;
+    const bool dense = fits32 && rows >= SMOE_DENSE_MIN_ROWS * groups;
+    const bool gemv = SMOE_VF_GEMV && T <= kGemvMaxT && H <= 512 * kGemvMaxChunks &&
+                      I <= 512 * kGemvMaxChunks;
+    const int slots = active ? (E < rows ? E : rows) : E;
+    const int mean = (rows + E - 1) / E;
+    int est = (E == 1) ? rows : 2 * mean + 8;
+    if (est > T) est = T;
+    const int RB = (est <= 16) ? 1 : 2;
+    F16Args a1{};
+    a1.xin = x;
+    a1.sorted_token = sorted_token;
+    a1.off = off;
+    a1.active = active;
+    a1.n_active = n_active;
+    a1.experts = experts;
+    a1.mask = mask;
+    a1.K = H;
+    a1.Ncol = I;
+    a1.I = I;
+    a1.H = H;
+    a1.out = static_cast<uint16_t*>(ws);
+    a1.err = err;
+    a1.nCB = I / 16;
+    F16Args a2 = a1;
+    a2.xin = a1.out;
+    a2.sorted_token = nullptr;
+    a2.K = I;
+    a2.Ncol = H;
+    a2.out = y;
+    a2.nCB = H / 16;
+    // fused: the shared expert's items lead the routed ring launches when
+    // both projections run a ring kernel and its rows take no extra pass
+    const int k1 = phase_kernel(a1, slots), k2 = phase_kernel(a2, slots);
+    // a shared group of 17-32 rows: the launches take 32-row blocks
+    const int RBf = (T > 16 && T <= 32) ? 2 : RB;
+    if (!dense && !gemv && slots > 1 && (k1 == 1 || k1 == 2) && (k2 == 1 || k2 == 2) &&
+        T <= 16 * RBf) {
+        a1.ex_w = sw13;
+        a1.ex_out = sh_h;
+        a1.ex_I = Is;
+        a1.ex_nCB = Is / 16;
+        a1.ex_T = T;
+        a2.ex_w = sw2;
+        a2.ex_in = sh_h;
+        a2.ex_out = sh_out;
+        a2.ex_I = Is;
+        a2.ex_nCB = H / 16;
+        a2.ex_T = T;
+        hipError_t st = launch_phase<1>(a1, slots, RBf, s);
+        if (st != hipSuccess) return st;
+        return launch_phase<2>(a2, slots, RBf, s);
+    }
+    hipError_t st = launch_verify_ffn(x, sorted_token, off, active, n_active, experts, mask, T,
+                                      rows, H, I, E, y, ws, err, s);
+    if (st != hipSuccess) return st;
+    return launch_dense_group(x, T, H, sw13, sw2, Is, sh_h, sh_out, err, s);
 }
 }  // namespace smoe

@@ -1444,19 +1444,6 @@ struct LayerArgs {
     int row_bytes;           // dynamic LDS: staged rows
 };
 
-template <typename T>
-SMOE_DEV void st_dev(T* p, T v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-SMOE_DEV T ld_dev(const T* p) {
-    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-SMOE_DEV uint4 ld_dev4(const void* p) {
-    const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
-    const uint64_t a = ld_dev(q), b = ld_dev(q + 1);
-    return make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32));
-}
 struct DevRows {
     SMOE_DEV uint4 operator()(const uint16_t* p) const { return ld_dev4(p); }
 };
@@ -2262,19 +2249,6 @@ struct LayerPlan {
     int P, row_bytes, lds, cs1, cs2, nsh1, nsh2, variant;
 };
 
-int device_cus() {
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (!cus[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return 0;
-        cus[dev] = n;
-    }
-    return cus[dev];
-}
-
 // Instantiated geometries (gate/up LPR and groups per slot, down LPR and
 // groups per slot, shared-expert chunks per lane of gate/up and down):
 //   0: 16/2, 8/2, none       (H 4096, I 6400: the Phi-3.5-MoE layer)
@@ -2304,7 +2278,7 @@ bool plan_layer(int H, int I, int E, int k, int Is, LayerPlan& L) {
     if (L.variant < 0) return false;
     const int NB2 = 4 * L.p2.lpr;
     if (H % NB2) return false;
-    L.P = device_cus();
+    L.P = smoe::device_cu_count();
     if (L.P <= 0) return false;
     const int G2 = I / 128, G1 = H / 128;
     int rb = H / 8 * 16 + G1 * 16;

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SMOE_ABI_VERSION 5
+#define SMOE_ABI_VERSION 6
 
 typedef enum {
     SMOE_OK = 0,
@@ -478,6 +478,37 @@ smoe_status verify_grouped_gemm(const uint16_t* x, const int32_t* sorted_token,
                                 const uint8_t* expert_mask, int T, int rows, int H, int I,
                                 int E, uint16_t* y_sorted, void* workspace,
                                 size_t workspace_bytes, int32_t* err_word, void* stream);
+
+/* ------------------------------------------------------------------------
+ * verify_grouped_gemm_shared -- verify_grouped_gemm over the routed experts
+ * and, in the same two launches, the FFN of a dense FP16 shared expert over
+ * all T tokens ([S1] Key Contributions 2: shared experts stay FP16 and run
+ * for every token; the verification step covers the whole layer).  The
+ * shared expert's work items lead each launch, so its short, latency-bound
+ * items overlap the routed experts' stream instead of running as launches of
+ * their own afterwards.  Shapes whose routed launches do not run the ring
+ * kernels (very few tokens, the tiled many-row regime, short reductions)
+ * take the routed call followed by launches of the shared expert alone;
+ * the outputs have the same meaning either way.
+ *
+ * Arguments: those of verify_grouped_gemm, then
+ *   shared_w13     fp16 [2*shared_I, H] (gate rows, then up rows)
+ *   shared_w2      fp16 [H, shared_I]
+ *   shared_I       multiple of 128
+ *   shared_h       fp16 [T, shared_I] caller-owned scratch
+ *   shared_out     fp16 [T, H] out: the shared expert's output, rounded to
+ *                  fp16 (fp32 accumulation; h rounded between projections),
+ *                  to pass to moe_combine as shared_out
+ * All shared pointers are required and 16-byte aligned.
+ * ---------------------------------------------------------------------- */
+smoe_status verify_grouped_gemm_shared(const uint16_t* x, const int32_t* sorted_token,
+                                       const int32_t* expert_offsets, const int32_t* active,
+                                       const int32_t* n_active, const smoe_f16_expert* experts,
+                                       const uint8_t* expert_mask, int T, int rows, int H, int I,
+                                       int E, uint16_t* y_sorted, const uint16_t* shared_w13,
+                                       const uint16_t* shared_w2, int shared_I,
+                                       uint16_t* shared_h, uint16_t* shared_out, void* workspace,
+                                       size_t workspace_bytes, int32_t* err_word, void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_combine -- weighted sum of the chosen experts' outputs plus the shared

@@ -852,6 +852,52 @@ def test_shared_expert(shape, T):
     assert_fp16_close(host(y)[:T], ref, f"shared {shape.name} T={T}")
 
 
+# verify_grouped_gemm_shared: the shared expert's items inside the routed
+# ring launches (Qwen T = 9, DeepSeek T = 16, a Phi-like H = 4096 layer with
+# a shared expert: 2- and 4-wave rings), and the fallbacks (T = 3: the
+# matrix-vector kernel; Qwen T = 17: a shared group longer than the routed
+# launches' row block)
+_PHI_SHV = dataclasses.replace(synth.PHI, name="phi_shared_verify", shared_I=4096,
+                               shared_gate=True)
+VERIFY_SHARED_CASES = [(synth.QWEN, 9), (synth.DS, 16), (_PHI_SHV, 9), (synth.QWEN, 3),
+                       (synth.QWEN, 17)]
+
+
+@pytest.mark.parametrize("shape,T", VERIFY_SHARED_CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_verify_grouped_gemm_shared(shape, T):
+    """The routed output bit-identical to verify_grouped_gemm's, the shared
+    output within the bars of the oracle's FP16 shared expert; twice in a row
+    on the same buffers (the second call may not depend on the first's)."""
+    say(f"verify + shared {shape.name} T={T}")
+    E, k, H, I, Is = shape.E, shape.k, shape.H, shape.I, shape.shared_I
+    L = _layer(shape, (T,), steps=(2,), int4=False)
+    x = synth.tokens(shape, T, step=2)
+    dx = dev(x)
+    err = _err()
+    ids, _, _ = fve.moe_route_topk(dx, L.d_router, k)
+    gm = fve.moe_gather(ids, E, err)
+    ws = fve.new_workspace(1, T, k, H, I, E)
+    y_ref = fve.verify_grouped_gemm(dx, gm["sorted_token"], gm["offsets"], L.t16, T, T * k, H, I,
+                                    E, ws, active=gm["active"], n_active=gm["n_active"])
+    y_ref = y_ref.clone()
+    shared = (dev(L.shared["w13"]), dev(L.shared["w2"]))
+    ws2 = fve.new_workspace(1, T, k, H, I, E)
+    ref_sh = oracle.expert_ffn_f16(x, L.shared["w13"], L.shared["w2"])
+    for rep in range(2):
+        y, so = fve.verify_grouped_gemm_shared(dx, gm["sorted_token"], gm["offsets"], L.t16, T,
+                                               T * k, H, I, E, ws2, shared, active=gm["active"],
+                                               n_active=gm["n_active"], err_word=err)
+        torch.cuda.synchronize()
+        assert int(host(err)[0]) == 0
+        assert torch.equal(y[:T * k], y_ref[:T * k]), "routed rows differ from verify_grouped_gemm"
+        st = assert_fp16_close(host(so), ref_sh, f"verify shared {shape.name} T={T}")
+        if rep == 0:
+            first = so.clone()
+        else:
+            assert torch.equal(so, first), "second call differs"
+    say(f"  shared l2={st['l2']:.2e} maxabs={st['maxabs']:.2e}")
+
+
 @pytest.mark.parametrize("T,rows", [(1, 3), (2, 5), (3, 9), (4, 4)])
 def test_verify_few_tokens_long_groups(T, rows):
     """T <= 4 with an expert group longer than the kernel's row block (a
