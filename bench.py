@@ -74,6 +74,9 @@ def parse():
                          "7x distinct experts from depth 1 to 16 on these layers)")
     ap.add_argument("--no-dense-point", dest="dense_point", action="store_false",
                     help="phi_layer: skip the supplementary T=2048 verify point")
+    ap.add_argument("--no-context", dest="context", action="store_false",
+                    help="qwen_verify: skip the context pass that times the routed and the "
+                         "shared expert as separate calls (a clean kernel trace of the step)")
     ap.add_argument("--no-other-configs", dest="other_configs", action="store_false",
                     help="phi_layer: skip the DeepSeek-V2-Lite draft (T=1/4/16) and Qwen1.5-MoE "
                          "verify (T=9) sub-objects of the line")
@@ -809,7 +812,7 @@ def bench_qwen_verify(args):
     fve.lib()
     torch.cuda.set_device(0)
     K = max(args.steps, 5)
-    r = qwen_verify_results(K, args.warmup)
+    r = qwen_verify_results(K, args.warmup, args.context)
     res = {"metric": "MoE-layer INT4 draft weight GB/s (% HBM peak); verify TFLOP/s (% MFMA)",
            "value": round(r["verify"]["bytes"] / r["verify"]["us"] / 1e3, 2),
            "unit": "GB/s (verify FP16 weights)",
@@ -825,7 +828,7 @@ QWEN_VERIFY_WORKLOAD = ("qwen15_moe verify layer: H=2048 E=60 top-4 I=1408 + gat
                         "I=5632; K+1=9 tokens; 1 GiB read before each timed step")
 
 
-def qwen_verify_results(K, warmup):
+def qwen_verify_results(K, warmup, context=True):
     """The Qwen1.5-MoE-shaped verification layer at K+1 = 9 tokens, every
     weight in HBM: routing plan, verify_grouped_gemm_shared (the routed
     experts and the gated shared expert in the same two launches), combine.
@@ -896,8 +899,8 @@ def qwen_verify_results(K, warmup):
         step(warmup + st, evs[st])
         evs[st][3].record()
     # context: the routed experts and the shared expert as separate calls
-    sep = [[mk() for _ in range(3)] for _ in range(K)]
-    for st in range(K):
+    sep = [[mk() for _ in range(3)] for _ in range(K)] if context else []
+    for st in range(len(sep)):
         i = warmup + st
         x = xs[i % POOL]
         plan(i)
@@ -930,9 +933,9 @@ def qwen_verify_results(K, warmup):
     res = {"T": T, "touched_experts_avg": round(nt, 2),
            "verify": dict(part(rb + sb, rf + sf, verify_us),
                           call="verify_grouped_gemm_shared (routed + shared expert)"),
-           "separate": {"routed": part(rb, rf, avg(sep, 0, 1)),
-                        "shared": part(sb, sf, avg(sep, 1, 2)),
-                        "note": "the same work as two verify_grouped_gemm calls (context)"},
+           "separate": None if not context else {
+               "routed": part(rb, rf, avg(sep, 0, 1)), "shared": part(sb, sf, avg(sep, 1, 2)),
+               "note": "the same work as two verify_grouped_gemm calls (context)"},
            "layer_step_us": round(step_us, 2),
            "note": "HIP events around each call inside the step (about 2-4 us each)"}
     del g, table, scrub
