@@ -42,6 +42,9 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
 // workgroup 0 writes out and norm_out.  The same routines as combine_kernel
 // and the routing kernels, so every value is bit-identical to those calls.
 constexpr int kMaxFusedH = 8192;
+// Each wave first requests its router row (it does not depend on the combine),
+// then evaluates the combine and the norm, then its logit against the row.
+template <int CPL>
 __global__ __launch_bounds__(kCombThreads) void combine_logits_kernel(
     const uint16_t* __restrict__ y, const int32_t* __restrict__ pp, const float* __restrict__ w,
     const uint16_t* __restrict__ shared, const float* __restrict__ sscale,
@@ -52,6 +55,11 @@ __global__ __launch_bounds__(kCombThreads) void combine_logits_kernel(
     __shared__ uint4 xs[kMaxFusedH / 8];
     const int nch = H / 8;
     const bool writer = blockIdx.x == 0;
+    const int wave = blockIdx.x * (kCombThreads / 64) + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    uint4 wv[CPL];
+    const bool has = wave < nvec;  // one logit per wave (the grid covers nvec)
+    smoe_route::pinned_row<CPL>(has ? (wave < E ? wr + (size_t)wave * H : wsg) : wr, H, lane, wv);
     float sq = 0.0f;
     for (int c8 = threadIdx.x; c8 < nch; c8 += kCombThreads) {
         float acc[8];
@@ -67,9 +75,10 @@ __global__ __launch_bounds__(kCombThreads) void combine_logits_kernel(
         if (writer) reinterpret_cast<uint4*>(norm_out)[c8] = q;
     }
     __syncthreads();
-    const int wave = blockIdx.x * (kCombThreads / 64) + (threadIdx.x >> 6);
-    smoe_route::wave_logits(reinterpret_cast<const uint16_t*>(xs), wr, wsg, H, E, nvec, wave,
-                            nvec, gridDim.x * (kCombThreads / 64), lg, threadIdx.x & 63);
+    if (has) {
+        const float s = smoe_route::pinned_dot_regs<CPL>(xs, wv, H, lane);
+        if (lane == 0) lg[wave] = s;
+    }
 }
 
 }  // namespace
@@ -97,8 +106,13 @@ hipError_t launch_combine_logits(const uint16_t* y, const int32_t* pp, const flo
                                  const uint16_t* wsg, int E, float* lg, hipStream_t s) {
     const int nvec = E + (wsg ? 1 : 0);
     const int wg = (nvec + kCombThreads / 64 - 1) / (kCombThreads / 64);
-    combine_logits_kernel<<<dim3(wg), dim3(kCombThreads), 0, s>>>(
-        y, pp, w, shared, sscale, resid, k, H, out, norm_out, eps, wr, wsg, E, nvec, lg);
+    const int cpl = (H / 8 + 63) / 64;  // chunks per lane of a row (H <= 8192: <= 16)
+#define SMOE_CL(C) combine_logits_kernel<C><<<dim3(wg), dim3(kCombThreads), 0, s>>>( \
+        y, pp, w, shared, sscale, resid, k, H, out, norm_out, eps, wr, wsg, E, nvec, lg)
+    if (cpl <= 4) SMOE_CL(4);
+    else if (cpl <= 8) SMOE_CL(8);
+    else SMOE_CL(16);
+#undef SMOE_CL
     return hipGetLastError();
 }
 }  // namespace smoe

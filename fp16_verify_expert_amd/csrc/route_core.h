@@ -65,6 +65,38 @@ SMOE_DEV float pinned_dot(const uint4* __restrict__ xr, const uint4* __restrict_
     return s;
 }
 
+// One wave's copy of a weight row for a later pinned-order dot product:
+// lane l requests chunks l, l + 64, ... (u < CPL) into registers.
+template <int CPL>
+SMOE_DEV void pinned_row(const uint16_t* __restrict__ row, int H, int lane, uint4 (&wv)[CPL]) {
+    const uint4* r4 = reinterpret_cast<const uint4*>(row);
+    const int nch = H >> 3;
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+        const int c = lane + 64 * u;
+        if (c < nch) wv[u] = r4[c];
+    }
+}
+
+// pinned_dot of the row x (in LDS or memory) with a row fetched by
+// pinned_row (CPL * 64 * 8 >= H): the same chunks, added in the same order,
+// so the value equals pinned_dot's and wave_logits'.
+template <int CPL>
+SMOE_DEV float pinned_dot_regs(const uint4* __restrict__ xr, const uint4 (&wv)[CPL], int H,
+                               int lane) {
+#pragma clang fp contract(off)
+    const int nch = H >> 3;
+    float s = 0.0f;
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+        const int c = lane + 64 * u;
+        if (c < nch) s = acc_chunk(s, xr[c], wv[u]);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) s = s + __shfl_xor(s, d);
+    return s;
+}
+
 // Logits of the items i = first, first + stride, ... < n_items handled by one
 // wave; item i is (token i / nvec, vector i % nvec), vector e < E being router
 // row e and vector E the shared-gate row.  Up to D items of one token are
