@@ -218,6 +218,60 @@ SMOE_DEV void count_ranks(const uint64_t (&key)[4], int E, int (&rank)[4]) {
     }
 }
 
+// The largest 64-bit value over the wave (every lane's v, all 64 lanes
+// active; result uniform):
+// DPP exchanges within each row of 16 lanes (quad xor 1, xor 2, then the
+// half-row and row mirrors), then the four row maxima through readlane.
+SMOE_DEV uint64_t wave_max_u64(uint64_t v) {
+    auto step = [&](auto ctrl) {
+        constexpr int C = decltype(ctrl)::value;
+        const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+        const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, C, 0xF, 0xF, false);
+        const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, C, 0xF, 0xF, false);
+        const uint64_t o = ((uint64_t)ohi << 32) | olo;
+        v = o > v ? o : v;
+    };
+    step(std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+    step(std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+    step(std::integral_constant<int, 0x141>{});  // row_half_mirror
+    step(std::integral_constant<int, 0x140>{});  // row_mirror
+    const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+    uint64_t m = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint64_t c = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
+        m = c > m ? c : m;
+    }
+    return m;
+}
+
+// rank[i] = r for the key selected in round r < k (the largest remaining key
+// of the wave each round), k for every other key; the same ranks below k as
+// count_ranks.  Dead slots hold key 0, below every live key (whose low word,
+// the complemented id, is never 0).
+template <int NB>
+SMOE_DEV void select_ranks(const uint64_t (&key)[4], int k, int (&rank)[4]) {
+    uint64_t kk[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        kk[i] = key[i];
+        rank[i] = k;
+    }
+    for (int r = 0; r < k; ++r) {
+        uint64_t best = kk[0];
+#pragma unroll
+        for (int i = 1; i < NB; ++i) best = kk[i] > best ? kk[i] : best;
+        const uint64_t w = wave_max_u64(best);
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            if (kk[i] == w) {
+                rank[i] = r;
+                kk[i] = 0;
+            }
+    }
+}
+
 // One wave selects the top k of a token's E logits (lg, in LDS; lg[E] is the
 // shared-gate logit when has_gate) and writes ids, weights (softmax over all
 // E at the chosen ids, optionally renormalised over the k) and the gate.
@@ -227,7 +281,14 @@ SMOE_DEV void count_ranks(const uint64_t (&key)[4], int E, int (&rank)[4]) {
 // selection, in rank order.
 // Rank of every expert's logit (lane l holds experts l + 64 i): the number
 // of keys above its own.
-SMOE_DEV void rank_experts(const float* lg, int E, int lane, float (&v)[4], int (&rank)[4]) {
+// Selections of up to kSelectMaxK experts take k rounds of a wave maximum;
+// larger ones count, for every key, the keys above it.
+#ifndef SMOE_SELECT_MAX_K
+#define SMOE_SELECT_MAX_K 16
+#endif
+constexpr int kSelectMaxK = SMOE_SELECT_MAX_K;
+SMOE_DEV void rank_experts(const float* lg, int E, int k, int lane, float (&v)[4],
+                           int (&rank)[4]) {
     uint64_t key[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -238,6 +299,17 @@ SMOE_DEV void rank_experts(const float* lg, int E, int lane, float (&v)[4], int 
         rank[i] = 0;
     }
     const int nblk = (E + 63) >> 6;  // key blocks actually held (uniform)
+    if (k <= kSelectMaxK) {
+        if (nblk == 1)
+            select_ranks<1>(key, k, rank);
+        else if (nblk == 2)
+            select_ranks<2>(key, k, rank);
+        else if (nblk == 3)
+            select_ranks<3>(key, k, rank);
+        else
+            select_ranks<4>(key, k, rank);
+        return;
+    }
     if (nblk == 1)
         count_ranks<1>(key, E, rank);
     else if (nblk == 2)
@@ -253,7 +325,7 @@ SMOE_DEV void rank_experts(const float* lg, int E, int lane, float (&v)[4], int 
 SMOE_DEV void topk_ids_wave(const float* lg, int E, int k, int lane, int32_t* ids) {
     float v[4];
     int rank[4];
-    rank_experts(lg, E, lane, v, rank);
+    rank_experts(lg, E, k, lane, v, rank);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = lane + 64 * i;
@@ -267,7 +339,7 @@ SMOE_DEV void topk_softmax_wave(const float* lg, int E, int k, int renorm, bool 
 #pragma clang fp contract(off)
     float v[4];
     int rank[4];
-    rank_experts(lg, E, lane, v, rank);
+    rank_experts(lg, E, k, lane, v, rank);
     // the largest logit: the value of the rank-0 expert, from its lane
     float v0 = 0.0f;
     bool has0 = false;

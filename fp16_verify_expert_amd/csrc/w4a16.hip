@@ -130,6 +130,11 @@ struct W4Args {
     const uint16_t* const* ascale;
 };
 
+// A read-only int32 through the scalar cache (constant address space: the
+// address must be wave-uniform; the data was written by an earlier launch).
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+SMOE_DEV int32_t ld_const(const int32_t* p) { return *(const_i32_ptr)(p); }
+
 SMOE_DEV const uint16_t* uniform_ptr_c(const uint16_t* p) {
     const uint64_t v = reinterpret_cast<uint64_t>(p);
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
@@ -939,13 +944,28 @@ __attribute__((amdgpu_waves_per_eu(w4_waves_per_eu<MAXM, NG>()))) void w4_kernel
 // activation sums, then the fp16 scale.  The 4 waves take groups g = wave,
 // wave + 4, ... through two register buffers (loads of the next two groups
 // in flight while one is multiplied) and add their tiles through LDS.
+// Gathered activation rows take their token indices through scalar loads
+// issued together, so staging a chunk costs one dependent round trip (with
+// vector loads each row's index load waited for the row loads before it).
+// Measured against the form with vector index loads, on the DeepSeek-V2-Lite
+// draft layer step: T = 16 104.0 -> 99.4 us, T = 4 65.5 -> 64.0 us; the down
+// projection at four waves per SIMD (127 VGPRs) a further 2.6 us at T = 16.
+// Four buffers (every group of a wave requested up front; 201 VGPRs, two
+// waves per SIMD) were slower: 72.2 and 119.7 us.
 #ifndef SMOE_W4_MFMA_WAVES
 #define SMOE_W4_MFMA_WAVES 4
 #endif
 #ifndef SMOE_W4_MFMA_WPE
 #define SMOE_W4_MFMA_WPE 2
 #endif
+#ifndef SMOE_W4_MFMA_WPE2
+#define SMOE_W4_MFMA_WPE2 4  // down projection (127 VGPRs)
+#endif
+#ifndef SMOE_W4_MFMA_BUFS
+#define SMOE_W4_MFMA_BUFS 2
+#endif
 constexpr int kMfmaWaves = SMOE_W4_MFMA_WAVES;
+constexpr int kMfmaBufs = SMOE_W4_MFMA_BUFS;  // groups of a wave in flight
 constexpr int kMfmaRows = 16;
 constexpr int kMfmaLdsBytes = 32 * 1024;  // activation staging budget
 
@@ -955,16 +975,24 @@ struct MfmaLoad {
     uint32_t z;
 };
 
-__device__ __forceinline__ void mfma_load(MfmaLoad& L, const W4Src& src, int g, int col, int kq) {
+// Group g of this lane's columns; a group past the reduction (g >= G) reads
+// nothing: its packed words come from an offset past the buffer's records,
+// which returns zeros without a memory access (they are never multiplied),
+// and its scale and zero words from group G - 1.  The request count is the
+// same either way, so the compiler's waits stay exact.
+__device__ __forceinline__ void mfma_load(MfmaLoad& L, const W4Src& src, int g, int G, int col,
+                                          int kq) {
     const int N = src.N;
-    const int voff = ((g * 16 + kq) * N + col) * 4;
+    const bool live = g < G;
+    const int gc = live ? g : G - 1;
+    const int voff = live ? ((gc * 16 + kq) * N + col) * 4 : 0x7FFFFFF0;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
         L.w[j] = __builtin_amdgcn_raw_buffer_load_b128(src.q, voff, 4 * j * N * 4, kAuxNT);
     const uint64_t sv =
-        *as_global(reinterpret_cast<const uint64_t*>(src.m.scales + (size_t)g * N + col));
+        *as_global(reinterpret_cast<const uint64_t*>(src.m.scales + (size_t)gc * N + col));
     L.s = make_uint2((uint32_t)sv, (uint32_t)(sv >> 32));
-    L.z = (uint32_t)*as_global(src.m.qzeros + (size_t)g * (N >> 3) + (col >> 3));
+    L.z = (uint32_t)*as_global(src.m.qzeros + (size_t)gc * (N >> 3) + (col >> 3));
 }
 
 // One 128-K group into acc (acc[c][i]: row 4(l/16)+i, column 4(l%16)+c).
@@ -1014,11 +1042,13 @@ __device__ __forceinline__ void mfma_group(const MfmaLoad& L, const uint4* __res
 
 template <int PHASE>
 __global__ __launch_bounds__(64 * kMfmaWaves)
-__attribute__((amdgpu_waves_per_eu(SMOE_W4_MFMA_WPE))) void w4_mfma_kernel(W4Args a) {
+__attribute__((amdgpu_waves_per_eu(PHASE == 1 ? SMOE_W4_MFMA_WPE : SMOE_W4_MFMA_WPE2))) void
+w4_mfma_kernel(W4Args a) {
     extern __shared__ uint4 smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int q = lane & 15;
     const int kq = lane >> 4;
     const int cb = blockIdx.x % a.nCB;
@@ -1050,7 +1080,7 @@ __attribute__((amdgpu_waves_per_eu(SMOE_W4_MFMA_WPE))) void w4_mfma_kernel(W4Arg
     float* red = l.red;  // [kMfmaWaves][MCH][64]
     const bool direct = (PHASE == 1) && a.direct;
     const int g0 = wave;
-    MfmaLoad A, B;
+    MfmaLoad L[kMfmaBufs];
     for (int mc = r0; mc < r1; mc += a.MCH) {
         const int M = min(a.MCH, r1 - mc);
         const bool stage = !direct || mc == r0;
@@ -1068,7 +1098,29 @@ __attribute__((amdgpu_waves_per_eu(SMOE_W4_MFMA_WPE))) void w4_mfma_kernel(W4Arg
         // exact count that leaves the weights outstanding)
         uint4 xv[kRowChunksPerThread];
         const int nch = nrows * K8;
-        if (stage) {
+        if (stage && PHASE == 1 && !direct && K8 >= 64) {
+            // gathered rows: a wave's 64 consecutive chunks span at most two
+            // rows, whose tokens come through scalar loads issued together
+            // (one wait for all of them, none for the vector loads)
+            int jlo[kRowChunksPerThread], tlo[kRowChunksPerThread], thi[kRowChunksPerThread];
+#pragma unroll
+            for (int u = 0; u < kRowChunksPerThread; ++u) {
+                int b0 = wave_u * 64 + u * (int)blockDim.x;
+                b0 = b0 < nch ? b0 : nch - 1;
+                jlo[u] = b0 / K8;
+                const int jhi = jlo[u] + 1 < nrows ? jlo[u] + 1 : nrows - 1;
+                tlo[u] = ld_const(a.sorted_token + mc + jlo[u]);
+                thi[u] = ld_const(a.sorted_token + mc + jhi);
+            }
+#pragma unroll
+            for (int u = 0; u < kRowChunksPerThread; ++u) {
+                int idx = tid + u * (int)blockDim.x;
+                idx = idx < nch ? idx : nch - 1;
+                const int j = idx / K8;
+                const int t = (j == jlo[u]) ? tlo[u] : thi[u];
+                xv[u] = reinterpret_cast<const uint4*>(a.xin + (size_t)t * K)[idx - j * K8];
+            }
+        } else if (stage) {
 #pragma unroll
             for (int u = 0; u < kRowChunksPerThread; ++u) {
                 int idx = tid + u * (int)blockDim.x;
@@ -1077,9 +1129,9 @@ __attribute__((amdgpu_waves_per_eu(SMOE_W4_MFMA_WPE))) void w4_mfma_kernel(W4Arg
                 xv[u] = src_row(j)[idx - j * K8];
             }
         }
-        // (unconditional: groups past G read group G - 1, not multiplied)
-        mfma_load(A, src, clamp_group(g0, G), colc, kq);
-        mfma_load(B, src, clamp_group(g0 + kMfmaWaves, G), colc, kq);
+        // (unconditional: groups past G read nothing and are not multiplied)
+#pragma unroll
+        for (int b = 0; b < kMfmaBufs; ++b) mfma_load(L[b], src, g0 + b * kMfmaWaves, G, colc, kq);
         __builtin_amdgcn_sched_barrier(0);
         if (stage) {
 #pragma unroll
@@ -1109,15 +1161,17 @@ __attribute__((amdgpu_waves_per_eu(SMOE_W4_MFMA_WPE))) void w4_mfma_kernel(W4Arg
         f4_t acc[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[c] = f4_t{0.f, 0.f, 0.f, 0.f};
-        // groups wave, wave + 4, ... through the two buffers (branches on the
-        // group index are wave-uniform)
-        for (int g = g0; g < G; g += 2 * kMfmaWaves) {
-            mfma_group(A, l.xs, l.sums, ar, aok, drow, g, K8, G, kq, zsh, mk, acc);
-            mfma_load(A, src, clamp_group(g + 2 * kMfmaWaves, G), colc, kq);
-            if (g + kMfmaWaves < G)
-                mfma_group(B, l.xs, l.sums, ar, aok, drow, g + kMfmaWaves, K8, G, kq, zsh, mk,
-                           acc);
-            mfma_load(B, src, clamp_group(g + 3 * kMfmaWaves, G), colc, kq);
+        // groups wave, wave + 4, ... through the buffers, each refilled with
+        // the group kMfmaBufs further on as soon as it has been multiplied
+        // (branches on the group index are wave-uniform)
+        for (int g = g0; g < G; g += kMfmaBufs * kMfmaWaves) {
+#pragma unroll
+            for (int b = 0; b < kMfmaBufs; ++b) {
+                const int gb = g + b * kMfmaWaves;
+                if (b == 0 || gb < G)
+                    mfma_group(L[b], l.xs, l.sums, ar, aok, drow, gb, K8, G, kq, zsh, mk, acc);
+                mfma_load(L[b], src, gb + kMfmaBufs * kMfmaWaves, G, colc, kq);
+            }
         }
         // the waves' tiles, added in a fixed order
         __syncthreads();  // every wave is done with the staged rows
