@@ -703,8 +703,9 @@ def ds_draft_results(K, warmup):
     intermediate 2816, ELB counters over one layer) at T = 1, 4 and 16 tokens,
     every weight in HBM.  T = 1: moe_draft_route_ffn (routing, ELB, maps,
     routed INT4 FFN and the shared experts in three launches) + moe_combine;
-    T > 1: moe_route_plan + w4a16_grouped_ffn + the shared experts through
-    verify_grouped_gemm + moe_combine.  A read of 1 GiB runs before each timed
+    T > 1: moe_route_plan + w4a16_grouped_ffn_shared (the routed INT4 FFN and
+    the shared experts; up to 4 rows the shared columns ride in the two
+    multi-row launches) + moe_combine.  A read of 1 GiB runs before each timed
     step, outside its events, so the weights come from HBM.  Reported per T:
     the step's wall time (HIP events around its calls, no markers inside),
     the INT4 bytes of the touched experts and the shared experts' FP16 bytes,
@@ -726,7 +727,6 @@ def ds_draft_results(K, warmup):
     table = fve.w4_expert_table(g["int4"])
     router = g["router"]
     shared = (g["shared"]["w13"], g["shared"]["w2"])
-    tsh = fve.f16_expert_table([shared])
     gen_s = time.perf_counter() - t0
     scrub = torch.empty(1 << 29, dtype=torch.float16, device=dev)  # 1 GiB
     counters = torch.zeros((1, E), dtype=torch.int32, device=dev)
@@ -737,10 +737,7 @@ def ds_draft_results(K, warmup):
     for T in (1, 4, 16):
         xs = [torch.from_numpy(synth.tokens(s, T, step=i)).to(dev) for i in range(POOL)]
         ws = fve.new_workspace(0, T, k, H, I, E)
-        wsv = fve.new_workspace(1, T, 1, H, Is, 1)
-        iota = torch.arange(T, dtype=torch.int32, device=dev)
-        offs = torch.tensor([0, T], dtype=torch.int32, device=dev)
-        sh_h = torch.empty(Is, dtype=torch.float16, device=dev)
+        sh_h = torch.empty((T, Is), dtype=torch.float16, device=dev)
         sh_out = torch.empty((T, H), dtype=torch.float16, device=dev)
         y = torch.empty((T * k, H), dtype=torch.float16, device=dev)
         out = torch.empty((T, H), dtype=torch.float16, device=dev)
@@ -762,10 +759,9 @@ def ds_draft_results(K, warmup):
                 # streams slowed each other's kernels)
                 fve.moe_route_plan(x, router, k, counters=counters, err_word=err,
                                    topk_ids=ids_b, topk_w=w_b, maps=maps_b, logits_ws=lg_b)
-                fve.w4a16_grouped_ffn(x, maps_b, table, T, k, H, I, E, ws, y_sorted=y,
-                                      err_word=err)
-                fve.verify_grouped_gemm(x, iota, offs, tsh, T, T, H, Is, 1, wsv,
-                                        y_sorted=sh_out, err_word=err)
+                fve.w4a16_grouped_ffn_shared(x, maps_b, table, T, k, H, I, E, ws, shared,
+                                             y_sorted=y, shared_h=sh_h, shared_out=sh_out,
+                                             err_word=err)
             fve.moe_combine(y, maps_b["pair_pos"], w_b, sh_out, out=out)
 
         touched = []
@@ -795,8 +791,8 @@ def ds_draft_results(K, warmup):
                         "all_weight_gbps": round((b_int4 + b_sh) / us / 1e3, 1),
                         "all_weight_frac_hbm": round((b_int4 + b_sh) / us / 1e3 / HBM_PEAK_GBS, 4),
                         "path": ("moe_draft_route_ffn (shared experts inside) + moe_combine"
-                                 if T == 1 else "moe_route_plan + w4a16_grouped_ffn + "
-                                 "verify_grouped_gemm (shared) + moe_combine")})
+                                 if T == 1 else "moe_route_plan + w4a16_grouped_ffn_shared + "
+                                 "moe_combine")})
         print(json.dumps(results[-1]), file=sys.stderr, flush=True)
     del g, table, scrub
     torch.cuda.empty_cache()

@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsmoe.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "smoe.h")
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 SMOE_DERR_BAD_ID = 1
 SMOE_DERR_NULL_EXPERT = 2
@@ -50,6 +50,8 @@ _SIGS = {
                                _sz, _vp, _vp]),
     "w4a16_grouped_ffn_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
                                        _vp, _vp, _vp]),
+    "w4a16_grouped_ffn_shared": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                      _vp, _vp, _vp, _i, _vp, _vp, _vp, _sz, _vp, _vp]),
     "awq_grouped_ffn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp,
                              _vp, _sz, _vp, _vp]),
     "wq_grouped_ffn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
@@ -273,6 +275,31 @@ def w4a16_grouped_ffn(x, maps, table, T: int, k: int, H: int, I: int, E: int, wo
           _p(y_sorted), _p(workspace), workspace.numel() * workspace.element_size(),
           _p(err_word), _s(stream))
     return y_sorted
+
+
+def w4a16_grouped_ffn_shared(x, maps, table, T: int, k: int, H: int, I: int, E: int, workspace,
+                             shared, *, y_sorted=None, shared_h=None, shared_out=None,
+                             err_word=None, stream=None):
+    """w4a16_grouped_ffn plus the dense FP16 shared expert shared = (w13
+    [2 Is, H], w2 [H, Is]) over all T rows of x.  Returns (y_sorted,
+    shared_out [T, H])."""
+    _check(x, torch.float16, "x")
+    sw13, sw2 = shared
+    _check(sw13, torch.float16, "shared w13")
+    _check(sw2, torch.float16, "shared w2")
+    Is = sw2.shape[1]
+    dev = x.device
+    if y_sorted is None:
+        y_sorted = torch.empty((max(T * k, 1), H), dtype=torch.float16, device=dev)
+    if shared_h is None:
+        shared_h = torch.empty((T, Is), dtype=torch.float16, device=dev)
+    if shared_out is None:
+        shared_out = torch.empty((T, H), dtype=torch.float16, device=dev)
+    _call("w4a16_grouped_ffn_shared", _p(x), _p(maps["sorted_token"]), _p(maps["offsets"]),
+          _p(maps["active"]), _p(maps["n_active"]), _p(table), T, k, H, I, E, 128,
+          _p(y_sorted), _p(sw13), _p(sw2), Is, _p(shared_h), _p(shared_out), _p(workspace),
+          workspace.numel() * workspace.element_size(), _p(err_word), _s(stream))
+    return y_sorted, shared_out
 
 
 def w4a16_grouped_ffn_noalloc(x, maps, table, T: int, k: int, H: int, I: int, E: int, *,

@@ -375,6 +375,38 @@ smoe_status w4a16_grouped_ffn_noalloc(const uint16_t* x, const int32_t* sorted_t
                       "w4a16_grouped_ffn_noalloc launch");
 }
 
+smoe_status w4a16_grouped_ffn_shared(const uint16_t* x, const int32_t* sorted_token,
+                                     const int32_t* expert_offsets, const int32_t* active,
+                                     const int32_t* n_active, const smoe_w4_expert* experts,
+                                     int T, int k, int H, int I, int E, int group_size,
+                                     uint16_t* y_sorted, const uint16_t* shared_w13,
+                                     const uint16_t* shared_w2, int shared_I,
+                                     uint16_t* shared_h, uint16_t* shared_out, void* workspace,
+                                     size_t workspace_bytes, int32_t* err_word, void* stream) {
+    const char* name = "w4a16_grouped_ffn_shared";
+    smoe_status st = check_wq(name, x, sorted_token, expert_offsets, active, n_active, experts,
+                              T, k, H, I, E, 4, group_size, y_sorted);
+    if (st != SMOE_OK) return st;
+    REQUIRE(shared_w13 && shared_w2 && shared_h && shared_out, SMOE_ERR_NULL,
+            "%s: shared_w13, shared_w2, shared_h and shared_out are required", name);
+    REQUIRE(shared_I > 0 && shared_I % 128 == 0, SMOE_ERR_SHAPE,
+            "%s: shared_I=%d must be a positive multiple of 128", name, shared_I);
+    REQUIRE(aligned(shared_w13, 16) && aligned(shared_w2, 16) && aligned(shared_h, 16) &&
+                aligned(shared_out, 16),
+            SMOE_ERR_SHAPE, "%s: the shared expert's fp16 tensors must be 16-byte aligned", name);
+    if (T == 0) return ok();
+    const size_t need = smoe::w4a16_workspace_bytes(T, k, H, I, E);
+    REQUIRE(workspace && workspace_bytes >= need && aligned(workspace, 256), SMOE_ERR_WORKSPACE,
+            "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", name, need,
+            workspace_bytes);
+    CHECK_DEVICE();
+    return hip_result(smoe::launch_w4a16_ffn_shared(
+                          x, sorted_token, expert_offsets, active, n_active, experts, T, k, H, I,
+                          E, y_sorted, workspace, shared_w13, shared_w2, shared_I, shared_h,
+                          shared_out, err_word, static_cast<hipStream_t>(stream)),
+                      "w4a16_grouped_ffn_shared launch");
+}
+
 smoe_status moe_draft_route_ffn(const uint16_t* x, const uint16_t* w_router,
                                 const uint16_t* w_shared_gate, int H, int I, int E, int k,
                                 int renormalize, int layer, int L, int32_t* counters,

@@ -115,6 +115,20 @@ hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, cons
                             int bits, uint16_t* y, void* ws, int32_t* err, hipStream_t s,
                             const uint16_t* const* ascale = nullptr);
 size_t w4a16_workspace_bytes(int T, int k, int H, int I, int E);
+// w4a16_grouped_ffn (4-bit) and a dense FP16 shared expert over all T rows,
+// the shared columns inside the multi-row launches where they fit
+hipError_t launch_w4a16_ffn_shared(const uint16_t* x, const int32_t* sorted_token,
+                                   const int32_t* off, const int32_t* active,
+                                   const int32_t* n_active, const smoe_w4_expert* experts, int T,
+                                   int k, int H, int I, int E, uint16_t* y, void* ws,
+                                   const uint16_t* sw13, const uint16_t* sw2, int Is,
+                                   uint16_t* sh_h, uint16_t* sh_out, int32_t* err,
+                                   hipStream_t s);
+// the dense shared expert alone as verify_grouped_gemm's one-group ring
+// launches over token rows 0..T-1 of x
+hipError_t launch_dense_group(const uint16_t* x, int T, int H, const uint16_t* w13,
+                              const uint16_t* w2, int Is, uint16_t* sh_h, uint16_t* sh_out,
+                              int32_t* err, hipStream_t s);
 // One-token draft step: the router logits, then routing, ELB, maps and the
 // gate/up projection in one launch, then the down projection; an optional
 // dense shared expert (sw13 non-null) computed in the same two launches.

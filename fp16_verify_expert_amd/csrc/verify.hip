@@ -741,7 +741,7 @@ hipError_t launch_verify_ffn(const uint16_t* x, const int32_t* sorted_token, con
 
 // The dense shared expert's two projections on their own: launches of its
 // items only (token rows 0..T-1 of x), the one-group ring geometry.
-static hipError_t launch_dense_group(const uint16_t* x, int T, int H, const uint16_t* w13,
+hipError_t launch_dense_group(const uint16_t* x, int T, int H, const uint16_t* w13,
                                      const uint16_t* w2, int Is, uint16_t* sh_h,
                                      uint16_t* sh_out, int32_t* err, hipStream_t s) {
     F16Args g{};

@@ -1040,10 +1040,62 @@ __device__ __forceinline__ void mfma_group(const MfmaLoad& L, const uint4* __res
     }
 }
 
-template <int PHASE>
+// A dense shared expert (FP16 w13 [2 Is, H], w2 [H, Is], the nn.Linear
+// layout of the verify path) over the T rows of a multi-row step, as extra
+// workgroups of the multi-row launches (from workgroup wg0 on) or as launches
+// of its own.
+struct RowsShared {
+    const uint16_t* w;    // phase 1: w13; phase 2: w2
+    const uint16_t* xin;  // phase 1: x [T, H]; phase 2: the shared h [T, Is]
+    uint16_t* out;        // phase 1: h [T, Is]; phase 2: the shared output [T, H]
+    int K, Ncol, Is;      // reduction length, output columns, shared intermediate
+    int rows;             // T
+    int wg0;              // first shared workgroup of the launch
+};
+
+// Column b * waves + wave of the shared projection, one column per wave,
+// through verify_grouped_gemm's matrix-vector routine (every weight chunk of
+// the column requested at once, then the rows one at a time; gemv_core.h), so
+// the values are bit-identical to that call's over the same rows.
+template <int PHASE, int CPL>
+SMOE_DEV void shared_rows_item(const RowsShared& sh, int b) {
+    constexpr int NM = (PHASE == 1) ? 2 : 1;
+    const int lane = threadIdx.x & 63;
+    const int n = b * (int)(blockDim.x >> 6) + (int)(threadIdx.x >> 6);
+    const int nc = n < sh.Ncol ? n : sh.Ncol - 1;  // loads stay in the matrix
+    u4_t wv[NM][CPL];
+    smoe_gemv::gemv_load_w<NM, CPL>(sh.w, sh.K, sh.Is, nc, lane, wv);
+    uint4 xr[CPL];
+    smoe_gemv::gemv_load_x<CPL>(sh.xin, sh.K, lane, xr);
+    __builtin_amdgcn_sched_barrier(0);  // every request above before the first use
+    auto one_row = [&](int r) {
+        const uint16_t v = smoe_gemv::gemv_dot<NM, CPL>(wv, xr, sh.K, lane);
+        if (lane == 0 && n < sh.Ncol) sh.out[(size_t)r * sh.Ncol + n] = v;
+    };
+    one_row(0);
+    for (int r = 1; r < sh.rows; ++r) {
+        smoe_gemv::gemv_load_x<CPL>(sh.xin + (size_t)r * sh.K, sh.K, lane, xr);
+        one_row(r);
+    }
+}
+
+template <int PHASE, int CPL>
+__global__ __launch_bounds__(256) void shared_rows_kernel(RowsShared sh) {
+    shared_rows_item<PHASE, CPL>(sh, (int)blockIdx.x);
+}
+
+// CPLS > 0: the workgroups from sh.wg0 on are the shared expert's columns
+// (4 per workgroup), chunks per lane CPLS.
+template <int PHASE, int CPLS = 0>
 __global__ __launch_bounds__(64 * kMfmaWaves)
 __attribute__((amdgpu_waves_per_eu(PHASE == 1 ? SMOE_W4_MFMA_WPE : SMOE_W4_MFMA_WPE2))) void
-w4_mfma_kernel(W4Args a) {
+w4_mfma_kernel(W4Args a, RowsShared sh) {
+    if constexpr (CPLS > 0) {
+        if ((int)blockIdx.x >= sh.wg0) {
+            shared_rows_item<PHASE, CPLS>(sh, (int)blockIdx.x - sh.wg0);
+            return;
+        }
+    }
     extern __shared__ uint4 smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -2161,14 +2213,14 @@ hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, cons
         const W4Args b1 = phase_args(m1, x, sorted_token, off, active, n_active, experts, H,
                                      2 * I, I, T, E, h, err, desc);
         hipLaunchKernelGGL((w4_mfma_kernel<1>), dim3(slots * m1.nCB), dim3(64 * kMfmaWaves),
-                           m1.lds, s, b1);
+                           m1.lds, s, b1, RowsShared{});
         hipError_t e1 = hipGetLastError();
         if (e1 != hipSuccess) return e1;
         const PhasePlan m2 = plan_mfma(2, T, I, H, I);
         const W4Args b2 =
             phase_args(m2, h, nullptr, off, active, n_active, experts, I, H, I, T, E, y, err, desc);
         hipLaunchKernelGGL((w4_mfma_kernel<2>), dim3(slots * m2.nCB), dim3(64 * kMfmaWaves),
-                           m2.lds, s, b2);
+                           m2.lds, s, b2, RowsShared{});
         return hipGetLastError();
     }
     W4Args a1 = phase_args(p1, x, sorted_token, off, active, n_active, experts, H, 2 * I, I, T, E,
@@ -2180,6 +2232,75 @@ hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, cons
         phase_args(p2, h, nullptr, off, active, n_active, experts, I, H, I, T, E, y, err, desc);
     a2.ascale = ascale;
     return launch_any<2>(a2, slots, p2, maxm, bits, s);
+}
+
+// The shared expert's projection as launches of its own (4 columns per
+// workgroup), any chunk count of the matrix-vector routine.
+template <int PHASE>
+static hipError_t launch_shared_rows(const RowsShared& sh, int cpl, hipStream_t s) {
+    const dim3 grid((sh.Ncol + 3) / 4), block(256);
+    switch (cpl) {
+        case 2: shared_rows_kernel<PHASE, 2><<<grid, block, 0, s>>>(sh); break;
+        case 4: shared_rows_kernel<PHASE, 4><<<grid, block, 0, s>>>(sh); break;
+        case 6: shared_rows_kernel<PHASE, 6><<<grid, block, 0, s>>>(sh); break;
+        case 8: shared_rows_kernel<PHASE, 8><<<grid, block, 0, s>>>(sh); break;
+        case 12: shared_rows_kernel<PHASE, 12><<<grid, block, 0, s>>>(sh); break;
+        default: shared_rows_kernel<PHASE, 16><<<grid, block, 0, s>>>(sh); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_w4a16_ffn_shared(const uint16_t* x, const int32_t* sorted_token,
+                                   const int32_t* off, const int32_t* active,
+                                   const int32_t* n_active, const smoe_w4_expert* experts, int T,
+                                   int k, int H, int I, int E, uint16_t* y, void* ws,
+                                   const uint16_t* sw13, const uint16_t* sw2, int Is,
+                                   uint16_t* sh_h, uint16_t* sh_out, int32_t* err,
+                                   hipStream_t s) {
+    // the shared expert as verify_grouped_gemm computes one group of all T
+    // rows: the matrix-vector routine up to 4 rows, else the one-group ring
+    const bool gemv = T <= 4 && H <= 512 * smoe_gemv::kMaxChunks &&
+                      Is <= 512 * smoe_gemv::kMaxChunks;
+    const RowsShared g1{sw13, x, sh_h, H, Is, Is, T, 0};
+    const RowsShared g2{sw2, sh_h, sh_out, Is, H, Is, T, 0};
+    const int c1 = smoe_gemv::chunks_for(H), c2 = smoe_gemv::chunks_for(Is);
+    const bool mfma = T > 1 && SMOE_W4_MFMA;  // launch_w4a16_ffn's multi-row 4-bit path
+    // (fused chunk counts: those whose item fits the launches' register
+    // budget; 12 for the down projection spilled)
+    if (gemv && mfma && (c1 == 4 || c1 == 8) && (c2 == 6 || c2 == 8)) {
+        // its columns as the last workgroups of the two multi-row launches
+        const int rows = T * k;
+        const int slots = E < rows ? E : rows;
+        uint16_t* h = static_cast<uint16_t*>(ws);
+        SlotDesc* desc =
+            reinterpret_cast<SlotDesc*>(static_cast<char*>(ws) + h_bytes(T, k, I));
+        const PhasePlan m1 = plan_mfma(1, T, H, 2 * I, I);
+        const W4Args b1 = phase_args(m1, x, sorted_token, off, active, n_active, experts, H,
+                                     2 * I, I, T, E, h, err, desc);
+        RowsShared s1 = g1;
+        s1.wg0 = slots * m1.nCB;
+        const dim3 grid1(slots * m1.nCB + (Is + 3) / 4), block(64 * kMfmaWaves);
+        if (c1 == 4) hipLaunchKernelGGL((w4_mfma_kernel<1, 4>), grid1, block, m1.lds, s, b1, s1);
+        else hipLaunchKernelGGL((w4_mfma_kernel<1, 8>), grid1, block, m1.lds, s, b1, s1);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const PhasePlan m2 = plan_mfma(2, T, I, H, I);
+        const W4Args b2 =
+            phase_args(m2, h, nullptr, off, active, n_active, experts, I, H, I, T, E, y, err, desc);
+        RowsShared s2 = g2;
+        s2.wg0 = slots * m2.nCB;
+        const dim3 grid2(slots * m2.nCB + (H + 3) / 4);
+        if (c2 == 6) hipLaunchKernelGGL((w4_mfma_kernel<2, 6>), grid2, block, m2.lds, s, b2, s2);
+        else hipLaunchKernelGGL((w4_mfma_kernel<2, 8>), grid2, block, m2.lds, s, b2, s2);
+        return hipGetLastError();
+    }
+    hipError_t e = launch_w4a16_ffn(x, sorted_token, off, active, n_active, experts, T, k, H, I,
+                                    E, 4, y, ws, err, s);
+    if (e != hipSuccess) return e;
+    if (!gemv) return launch_dense_group(x, T, H, sw13, sw2, Is, sh_h, sh_out, err, s);
+    e = launch_shared_rows<1>(g1, c1, s);
+    if (e != hipSuccess) return e;
+    return launch_shared_rows<2>(g2, c2, s);
 }
 
 bool draft_route_ffn_supported(int E, int k) { return E <= 256 && k <= kFusedMaxK; }

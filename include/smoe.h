@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SMOE_ABI_VERSION 6
+#define SMOE_ABI_VERSION 7
 
 typedef enum {
     SMOE_OK = 0,
@@ -227,6 +227,40 @@ smoe_status w4a16_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
                               int k, int H, int I, int E, int group_size, uint16_t* y_sorted,
                               void* workspace, size_t workspace_bytes, int32_t* err_word,
                               void* stream);
+
+/* ------------------------------------------------------------------------
+ * w4a16_grouped_ffn_shared -- w4a16_grouped_ffn plus the layer's dense FP16
+ * shared expert over all T rows of x ([S1] Key Contributions 2: the draft
+ * keeps the shared experts at FP16 beside the INT4 routed experts; Key
+ * Contributions 4: the draft step's sub-computations batched into few
+ * launches).  With 2..4 rows its columns run as extra workgroups of the two
+ * multi-row INT4 launches where the column routine's registers fit them (H
+ * in 1544-2048 or 3592-4096, shared_I in 2568-3072 or 3592-4096), else in
+ * launches of their own after them.
+ *
+ *   x .. workspace, err_word, stream: as w4a16_grouped_ffn (y_sorted is
+ *                  bit-identical to that call's)
+ *   shared_w13     fp16 [2*shared_I, H]: gate rows, then up rows (nn.Linear)
+ *   shared_w2      fp16 [H, shared_I]
+ *   shared_I       positive multiple of 128
+ *   shared_h       fp16 [T, shared_I] out: silu(x . gate) * (x . up), fp16
+ *   shared_out     fp16 [T, H] out: shared_h . w2^T (unscaled: a sigmoid gate
+ *                  is the combine's shared_scale)
+ * shared_h and shared_out are bit-identical to verify_grouped_gemm's outputs
+ * for the shared expert as its only expert with all T rows in order (the
+ * matrix-vector routine up to 4 rows, the one-expert ring kernels above),
+ * as long as that call stays out of its dense regime (T < 64).  All four
+ * shared pointers are required (SMOE_ERR_NULL), 16-byte aligned
+ * (SMOE_ERR_SHAPE).
+ * ---------------------------------------------------------------------- */
+smoe_status w4a16_grouped_ffn_shared(const uint16_t* x, const int32_t* sorted_token,
+                                     const int32_t* expert_offsets, const int32_t* active,
+                                     const int32_t* n_active, const smoe_w4_expert* experts,
+                                     int T, int k, int H, int I, int E, int group_size,
+                                     uint16_t* y_sorted, const uint16_t* shared_w13,
+                                     const uint16_t* shared_w2, int shared_I,
+                                     uint16_t* shared_h, uint16_t* shared_out, void* workspace,
+                                     size_t workspace_bytes, int32_t* err_word, void* stream);
 
 /* ------------------------------------------------------------------------
  * w4a16_grouped_ffn_noalloc -- w4a16_grouped_ffn without a workspace

@@ -21,7 +21,7 @@ def test_exports_every_header_function():
                 "moe_gather", "moe_route_plan", "w4a16_grouped_ffn", "wq_grouped_ffn",
                 "moe_draft_route_ffn", "w4a16_grouped_ffn_noalloc", "moe_combine_route_logits",
                 "awq_grouped_ffn", "moe_draft_layer", "smoe_draft_layer_supported",
-                "verify_grouped_gemm_shared",
+                "verify_grouped_gemm_shared", "w4a16_grouped_ffn_shared",
                 "verify_grouped_gemm", "moe_combine",
                 "expert_stage_async", "smoe_workspace_bytes", "smoe_stream_read"}
     assert set(names) == expected
@@ -342,6 +342,29 @@ def test_verify_shared_validation():
     assert call(T=0) == 0                           # nothing to do
     assert call(wsb=need - 1) == 6
     assert call(ws=None) == 6
+
+
+def test_w4_shared_validation():
+    L = fve.lib()
+    need = L.smoe_workspace_bytes(0, 4, 2, 256, 512, 8)
+
+    def call(x=FAKE, act=FAKE, T=4, H=256, gs=128, y=FAKE, w13=FAKE, w2=FAKE, Is=1024, sh=FAKE,
+             so=FAKE, ws=FAKE, wsb=None):
+        return L.w4a16_grouped_ffn_shared(x, FAKE, FAKE, act, FAKE, FAKE, T, 2, H, 512, 8, gs, y,
+                                          w13, w2, Is, sh, so, ws,
+                                          need if wsb is None else wsb, None, None)
+    assert call(x=None) == 1
+    assert call(act=None) == 1                      # the maps' active list is required
+    assert call(w13=None) == 1 and "shared" in _err()
+    assert call(so=None) == 1
+    assert call(Is=1000) == 2 and "shared_I" in _err()
+    assert call(H=200) == 2
+    assert call(gs=64) == 3
+    assert call(sh=V(0x1002)) == 2 and "aligned" in _err()
+    assert call(T=0) == 0                           # nothing to do
+    assert call(wsb=need - 1) == 6
+    assert call(ws=None) == 6
+    assert _err().startswith("w4a16_grouped_ffn_shared")
 
 
 def test_combine_validation():

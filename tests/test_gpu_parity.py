@@ -898,6 +898,52 @@ def test_verify_grouped_gemm_shared(shape, T):
     say(f"  shared l2={st['l2']:.2e} maxabs={st['maxabs']:.2e}")
 
 
+# DeepSeek: the shared columns inside the multi-row launches (T 2-4), then
+# the one-expert ring kernels after them (T 9, 16); Qwen (shared intermediate
+# 5632): launches of their own after the multi-row (T 4) or one-token (T 1)
+# launches.
+W4_SHARED_CASES = [(synth.DS, 2), (synth.DS, 4), (synth.DS, 9), (synth.DS, 16),
+                   (synth.QWEN, 4), (synth.QWEN, 1)]
+
+
+@pytest.mark.parametrize("shape,T", W4_SHARED_CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_w4a16_grouped_ffn_shared(shape, T):
+    """The routed output bit-identical to w4a16_grouped_ffn's; the shared
+    expert's output bit-identical to verify_grouped_gemm's with the shared
+    expert as its only expert over the T rows in order, and within the bars of
+    the oracle's FP16 shared expert; twice in a row on the same buffers."""
+    say(f"w4a16 + shared {shape.name} T={T}")
+    E, k, H, I, Is = shape.E, shape.k, shape.H, shape.I, shape.shared_I
+    L = _layer(shape, (T,), steps=(2,), f16=False)
+    x = synth.tokens(shape, T, step=2)
+    dx = dev(x)
+    err = _err()
+    ids, _, _ = fve.moe_route_topk(dx, L.d_router, k)
+    gm = fve.moe_gather(ids, E, err)
+    ws = fve.new_workspace(0, T, k, H, I, E)
+    y_ref = fve.w4a16_grouped_ffn(dx, gm, L.t4, T, k, H, I, E, ws).clone()
+    shared = (dev(L.shared["w13"]), dev(L.shared["w2"]))
+    iota = torch.arange(T, dtype=torch.int32, device="cuda")
+    offs = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    wsv = fve.new_workspace(1, T, 1, H, Is, 1)
+    so_ref = fve.verify_grouped_gemm(dx, iota, offs, L.tsh, T, T, H, Is, 1, wsv).clone()
+    ref_sh = oracle.expert_ffn_f16(x, L.shared["w13"], L.shared["w2"])
+    ws2 = fve.new_workspace(0, T, k, H, I, E)
+    for rep in range(2):
+        y, so = fve.w4a16_grouped_ffn_shared(dx, gm, L.t4, T, k, H, I, E, ws2, shared,
+                                             err_word=err)
+        torch.cuda.synchronize()
+        assert int(host(err)[0]) == 0
+        assert torch.equal(y[:T * k], y_ref[:T * k]), "routed rows differ from w4a16_grouped_ffn"
+        assert torch.equal(so, so_ref[:T]), "shared expert differs from verify_grouped_gemm"
+        st = assert_fp16_close(host(so), ref_sh, f"w4a16 shared {shape.name} T={T}")
+        if rep == 0:
+            first = so.clone()
+        else:
+            assert torch.equal(so, first), "second call differs"
+    say(f"  shared l2={st['l2']:.2e} maxabs={st['maxabs']:.2e}")
+
+
 @pytest.mark.parametrize("T,rows", [(1, 3), (2, 5), (3, 9), (4, 4)])
 def test_verify_few_tokens_long_groups(T, rows):
     """T <= 4 with an expert group longer than the kernel's row block (a
