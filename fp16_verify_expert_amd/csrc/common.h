@@ -124,6 +124,14 @@ hipError_t launch_w4a16_ffn_shared(const uint16_t* x, const int32_t* sorted_toke
                                    const uint16_t* sw13, const uint16_t* sw2, int Is,
                                    uint16_t* sh_h, uint16_t* sh_out, int32_t* err,
                                    hipStream_t s);
+// Waves per workgroup of the one-group (shared expert) ring launches, gate/up
+// and down; each wave takes a contiguous range of the 128-K steps.
+#ifndef SMOE_SH_GU_WAVES
+#define SMOE_SH_GU_WAVES 2
+#endif
+#ifndef SMOE_SH_DN_WAVES
+#define SMOE_SH_DN_WAVES 4
+#endif
 // the dense shared expert alone as verify_grouped_gemm's one-group ring
 // launches over token rows 0..T-1 of x
 hipError_t launch_dense_group(const uint16_t* x, int T, int H, const uint16_t* w13,

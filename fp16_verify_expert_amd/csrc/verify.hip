@@ -585,14 +585,10 @@ hipError_t launch_gemv_phase(const F16Args& a, int slots, hipStream_t s) {
 // 15.2 us with 4 waves and 3 stages (144 KB: one per CU, a second round of
 // 96); the down projection stays at 4 waves and 3 stages (2, 6 or 8 waves,
 // 2 or 3 stages: no better).
-#ifndef SMOE_SH_GU_WAVES
-#define SMOE_SH_GU_WAVES 2
-#endif
+// (SMOE_SH_GU_WAVES and SMOE_SH_DN_WAVES live in common.h: the multi-row
+// draft launches compute the same items with the same wave split.)
 #ifndef SMOE_SH_GU_STAGES
 #define SMOE_SH_GU_STAGES 2
-#endif
-#ifndef SMOE_SH_DN_WAVES
-#define SMOE_SH_DN_WAVES 4
 #endif
 #ifndef SMOE_SH_DN_STAGES
 #define SMOE_SH_DN_STAGES 3

@@ -1050,7 +1050,8 @@ struct RowsShared {
     uint16_t* out;        // phase 1: h [T, Is]; phase 2: the shared output [T, H]
     int K, Ncol, Is;      // reduction length, output columns, shared intermediate
     int rows;             // T
-    int wg0;              // first shared workgroup of the launch
+    int wg0;              // first shared workgroup of the launch (nfront == 0)
+    int nfront;           // > 0: the launch's first nfront workgroups are the shared ones
 };
 
 // Column b * waves + wave of the shared projection, one column per wave,
@@ -1084,27 +1085,131 @@ __global__ __launch_bounds__(256) void shared_rows_kernel(RowsShared sh) {
     shared_rows_item<PHASE, CPL>(sh, (int)blockIdx.x);
 }
 
+// The shared projection's 16-column items over 5-16 rows on MFMA, the
+// arithmetic of verify_grouped_gemm's one-group ring launches item for item
+// (waves per item and their contiguous step ranges, the order of the MFMAs,
+// the partial tiles added in wave order), so the values are bit-identical to
+// them; the operands come straight from memory in the MFMA layout (lane l:
+// row l%16, 8 K at 8(l/16) + 32u of each 128-K step u-th quarter) through
+// two register buffers, a step ahead, instead of an LDS ring.  Rows past
+// the T feed output rows that are not stored.  Loads past a wave's range
+// read past the buffers' records (zeros, no memory access).  red: LDS of
+// 4 waves x NM x 64 x 16 bytes.
+template <int PHASE>
+SMOE_DEV void shared_mfma_item(const RowsShared& sh, int b, f4_t* red) {
+    constexpr int NM = (PHASE == 1) ? 2 : 1;
+    constexpr int WPI = (PHASE == 1) ? SMOE_SH_GU_WAVES : SMOE_SH_DN_WAVES;  // waves per item
+    static_assert(WPI >= 1 && kMfmaWaves % WPI == 0, "items per workgroup");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int sub = wave % WPI;
+    const int item = b * (kMfmaWaves / WPI) + wave / WPI;
+    const bool live = item * 16 < sh.Ncol;
+    const int n0 = live ? item * 16 : 0;
+    const int K = sh.K;
+    const int nsteps = K / 128;
+    const int s0 = (nsteps * sub) / WPI, s1 = (nsteps * (sub + 1)) / WPI;
+    const int q = lane & 15, kq = lane >> 4;
+    const int arow = q < sh.rows ? q : 0;
+    const __amdgpu_buffer_rsrc_t ax = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(sh.xin), (short)0, sh.rows * K * 2, kBufWord3);
+    const __amdgpu_buffer_rsrc_t wx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(sh.w), (short)0,
+        (PHASE == 1 ? 2 * sh.Is : sh.Ncol) * K * 2, kBufWord3);
+    const int aoff = (arow * K + 8 * kq) * 2;
+    const int boff0 = ((n0 + q) * K + 8 * kq) * 2;
+    const int boff1 = ((sh.Is + n0 + q) * K + 8 * kq) * 2;  // up rows (gate/up)
+    struct Buf {
+        h8_t a[4];
+        h8_t w[NM][4];
+    };
+    auto load = [&](Buf& B, int st) {
+        const bool in = st < s1;
+        const int k2 = st * 256;  // byte offset of the step
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int o = k2 + 64 * u;
+            B.a[u] = __builtin_bit_cast(h8_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  ax, in ? aoff + o : 0x7FFFFFF0, 0, 0));
+            B.w[0][u] = __builtin_bit_cast(h8_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     wx, in ? boff0 + o : 0x7FFFFFF0, 0, kAuxNT));
+            if constexpr (NM == 2)
+                B.w[1][u] = __builtin_bit_cast(h8_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         wx, in ? boff1 + o : 0x7FFFFFF0, 0,
+                                                         kAuxNT));
+        }
+    };
+    f4_t accg = f4_t{0.f, 0.f, 0.f, 0.f}, accu = f4_t{0.f, 0.f, 0.f, 0.f};
+    auto mul = [&](const Buf& B) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(B.a[u], B.w[0][u], accg, 0, 0, 0);
+            if constexpr (NM == 2)
+                accu = __builtin_amdgcn_mfma_f32_16x16x32_f16(B.a[u], B.w[1][u], accu, 0, 0, 0);
+        }
+    };
+    Buf P, Q;
+    load(P, s0);
+    load(Q, s0 + 1);
+    for (int st = s0; st < s1; st += 2) {
+        mul(P);
+        load(P, st + 2);
+        if (st + 1 < s1) mul(Q);
+        load(Q, st + 3);
+    }
+    // the item's partial tiles, added in wave order
+    red[(wave * NM) * 64 + lane] = accg;
+    if constexpr (NM == 2) red[(wave * NM + 1) * 64 + lane] = accu;
+    __syncthreads();
+    if (sub == 0 && live) {
+        const int w0 = wave;
+        f4_t g = red[(w0 * NM) * 64 + lane];
+        f4_t uu = (NM == 2) ? red[(w0 * NM + NM - 1) * 64 + lane] : g;
+#pragma unroll
+        for (int w = 1; w < WPI; ++w) {
+            g += red[((w0 + w) * NM) * 64 + lane];
+            if constexpr (NM == 2) uu += red[((w0 + w) * NM + 1) * 64 + lane];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * kq + i;
+            if (r < sh.rows) {
+                const float v = (PHASE == 1) ? silu_f(g[i]) * uu[i] : g[i];
+                sh.out[(size_t)r * sh.Ncol + n0 + q] = f2h(v);
+            }
+        }
+    }
+}
+
 // CPLS > 0: the workgroups from sh.wg0 on are the shared expert's columns
-// (4 per workgroup), chunks per lane CPLS.
+// (4 per workgroup, the matrix-vector routine with CPLS chunks per lane);
+// CPLS < 0: its 16-column MFMA items (shared_mfma_item).
 template <int PHASE, int CPLS = 0>
 __global__ __launch_bounds__(64 * kMfmaWaves)
 __attribute__((amdgpu_waves_per_eu(PHASE == 1 ? SMOE_W4_MFMA_WPE : SMOE_W4_MFMA_WPE2))) void
 w4_mfma_kernel(W4Args a, RowsShared sh) {
-    if constexpr (CPLS > 0) {
-        if ((int)blockIdx.x >= sh.wg0) {
-            shared_rows_item<PHASE, CPLS>(sh, (int)blockIdx.x - sh.wg0);
+    extern __shared__ uint4 smem[];
+    int bid = (int)blockIdx.x;
+    if constexpr (CPLS != 0) {
+        const bool shw = sh.nfront ? bid < sh.nfront : bid >= sh.wg0;
+        if (shw) {
+            const int b = sh.nfront ? bid : bid - sh.wg0;
+            if constexpr (CPLS > 0)
+                shared_rows_item<PHASE, CPLS>(sh, b);
+            else
+                shared_mfma_item<PHASE>(sh, b, reinterpret_cast<f4_t*>(smem));
             return;
         }
+        bid -= sh.nfront;
     }
-    extern __shared__ uint4 smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int q = lane & 15;
     const int kq = lane >> 4;
-    const int cb = blockIdx.x % a.nCB;
-    const int slot = blockIdx.x / a.nCB;
+    const int cb = bid % a.nCB;
+    const int slot = bid / a.nCB;
     const int K = a.K, N = a.N;
     const int G = K >> 7;
     const int K8 = K >> 3;
@@ -2234,6 +2339,13 @@ hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, cons
     return launch_any<2>(a2, slots, p2, maxm, bits, s);
 }
 
+#ifndef SMOE_SH_FRONT_ROWS
+#define SMOE_SH_FRONT_ROWS 0  // matrix-vector shared items first in the multi-row launches
+#endif
+#ifndef SMOE_SH_FRONT_MFMA
+#define SMOE_SH_FRONT_MFMA 1  // MFMA shared items first
+#endif
+
 // The shared expert's projection as launches of its own (4 columns per
 // workgroup), any chunk count of the matrix-vector routine.
 template <int PHASE>
@@ -2279,6 +2391,7 @@ hipError_t launch_w4a16_ffn_shared(const uint16_t* x, const int32_t* sorted_toke
                                      2 * I, I, T, E, h, err, desc);
         RowsShared s1 = g1;
         s1.wg0 = slots * m1.nCB;
+        if (SMOE_SH_FRONT_ROWS) s1.nfront = (Is + 3) / 4;
         const dim3 grid1(slots * m1.nCB + (Is + 3) / 4), block(64 * kMfmaWaves);
         if (c1 == 4) hipLaunchKernelGGL((w4_mfma_kernel<1, 4>), grid1, block, m1.lds, s, b1, s1);
         else hipLaunchKernelGGL((w4_mfma_kernel<1, 8>), grid1, block, m1.lds, s, b1, s1);
@@ -2289,9 +2402,44 @@ hipError_t launch_w4a16_ffn_shared(const uint16_t* x, const int32_t* sorted_toke
             phase_args(m2, h, nullptr, off, active, n_active, experts, I, H, I, T, E, y, err, desc);
         RowsShared s2 = g2;
         s2.wg0 = slots * m2.nCB;
+        if (SMOE_SH_FRONT_ROWS) s2.nfront = (H + 3) / 4;
         const dim3 grid2(slots * m2.nCB + (H + 3) / 4);
         if (c2 == 6) hipLaunchKernelGGL((w4_mfma_kernel<2, 6>), grid2, block, m2.lds, s, b2, s2);
         else hipLaunchKernelGGL((w4_mfma_kernel<2, 8>), grid2, block, m2.lds, s, b2, s2);
+        return hipGetLastError();
+    }
+    // 5-16 rows: 16-column MFMA items with the one-group ring launches'
+    // arithmetic (those launches' geometry needs at least 8 steps of 128 K)
+    if (!gemv && mfma && T <= 16 && H / 128 >= 8 && Is / 128 >= 8) {
+        const int rows = T * k;
+        const int slots = E < rows ? E : rows;
+        uint16_t* h = static_cast<uint16_t*>(ws);
+        SlotDesc* desc =
+            reinterpret_cast<SlotDesc*>(static_cast<char*>(ws) + h_bytes(T, k, I));
+        constexpr int ipw1 = kMfmaWaves / SMOE_SH_GU_WAVES;  // items per workgroup
+        constexpr int ipw2 = kMfmaWaves / SMOE_SH_DN_WAVES;
+        const size_t red1 = (size_t)kMfmaWaves * 2 * 64 * 16, red2 = red1 / 2;
+        PhasePlan m1 = plan_mfma(1, T, H, 2 * I, I);
+        if (m1.lds < red1) m1.lds = red1;
+        const W4Args b1 = phase_args(m1, x, sorted_token, off, active, n_active, experts, H,
+                                     2 * I, I, T, E, h, err, desc);
+        RowsShared s1 = g1;
+        s1.wg0 = slots * m1.nCB;
+        if (SMOE_SH_FRONT_MFMA) s1.nfront = (Is / 16 + ipw1 - 1) / ipw1;
+        const dim3 block(64 * kMfmaWaves);
+        hipLaunchKernelGGL((w4_mfma_kernel<1, -1>), dim3(s1.wg0 + (Is / 16 + ipw1 - 1) / ipw1),
+                           block, m1.lds, s, b1, s1);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        PhasePlan m2 = plan_mfma(2, T, I, H, I);
+        if (m2.lds < red2) m2.lds = red2;
+        const W4Args b2 =
+            phase_args(m2, h, nullptr, off, active, n_active, experts, I, H, I, T, E, y, err, desc);
+        RowsShared s2 = g2;
+        s2.wg0 = slots * m2.nCB;
+        if (SMOE_SH_FRONT_MFMA) s2.nfront = (H / 16 + ipw2 - 1) / ipw2;
+        hipLaunchKernelGGL((w4_mfma_kernel<2, -1>), dim3(s2.wg0 + (H / 16 + ipw2 - 1) / ipw2),
+                           block, m2.lds, s, b2, s2);
         return hipGetLastError();
     }
     hipError_t e = launch_w4a16_ffn(x, sorted_token, off, active, n_active, experts, T, k, H, I,

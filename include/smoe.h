@@ -233,10 +233,11 @@ smoe_status w4a16_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
  * shared expert over all T rows of x ([S1] Key Contributions 2: the draft
  * keeps the shared experts at FP16 beside the INT4 routed experts; Key
  * Contributions 4: the draft step's sub-computations batched into few
- * launches).  With 2..4 rows its columns run as extra workgroups of the two
- * multi-row INT4 launches where the column routine's registers fit them (H
- * in 1544-2048 or 3592-4096, shared_I in 2568-3072 or 3592-4096), else in
- * launches of their own after them.
+ * launches).  Its columns run as extra workgroups of the two multi-row INT4
+ * launches: with 2..4 rows through the matrix-vector routine where its
+ * registers fit them (H in 1544-2048 or 3592-4096, shared_I in 2568-3072 or
+ * 3592-4096), with 5..16 rows as 16-column MFMA items (H and shared_I of at
+ * least 1024); otherwise in launches of their own after them.
  *
  *   x .. workspace, err_word, stream: as w4a16_grouped_ffn (y_sorted is
  *                  bit-identical to that call's)

@@ -898,12 +898,13 @@ def test_verify_grouped_gemm_shared(shape, T):
     say(f"  shared l2={st['l2']:.2e} maxabs={st['maxabs']:.2e}")
 
 
-# DeepSeek: the shared columns inside the multi-row launches (T 2-4), then
-# the one-expert ring kernels after them (T 9, 16); Qwen (shared intermediate
-# 5632): launches of their own after the multi-row (T 4) or one-token (T 1)
+# DeepSeek: the shared columns inside the multi-row launches (T 2-4: the
+# matrix-vector routine; T 5-16: MFMA items), then the one-expert ring
+# kernels after them (T 17); Qwen (shared intermediate 5632): MFMA items
+# (T 16), launches of their own after the multi-row (T 4) or one-token (T 1)
 # launches.
-W4_SHARED_CASES = [(synth.DS, 2), (synth.DS, 4), (synth.DS, 9), (synth.DS, 16),
-                   (synth.QWEN, 4), (synth.QWEN, 1)]
+W4_SHARED_CASES = [(synth.DS, 2), (synth.DS, 4), (synth.DS, 5), (synth.DS, 9), (synth.DS, 16),
+                   (synth.DS, 17), (synth.QWEN, 4), (synth.QWEN, 16), (synth.QWEN, 1)]
 
 
 @pytest.mark.parametrize("shape,T", W4_SHARED_CASES, ids=lambda v: getattr(v, "name", str(v)))
