@@ -515,6 +515,38 @@ __device__ __forceinline__ void finish_rows(uint4* xs, float4* sums, int nrows, 
     __syncthreads();
 }
 
+// finish_rows<4> for chunks staged in natural order: each (row, group)'s
+// chunks are read, permuted in place and summed as finish_rows<4> sums the
+// permuted chunks (the same values in the same order).  The caller has made
+// every chunk visible (waits and a barrier); ends with a barrier.
+__device__ __forceinline__ void finish_rows_natural4(uint4* xs, float4* sums, int nrows, int K8,
+                                                     int G) {
+#pragma unroll 1
+    for (int idx = threadIdx.x; idx < nrows * G; idx += blockDim.x) {
+        const int j = idx / G;
+        const int gg = idx - j * G;
+        uint4* xr = xs + j * K8 + gg * 16;
+        float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll 4
+        for (int i = 0; i < 16; ++i) {
+            const uint4 p = permute_chunk<4>(xr[i]);
+            xr[i] = p;
+            const h2_t x0 = as_h2(p.x), x1 = as_h2(p.y), x2 = as_h2(p.z), x3 = as_h2(p.w);
+            s0 += ((float)x0.x + (float)x0.y) + ((float)x2.x + (float)x2.y);
+            s1 += ((float)x1.x + (float)x1.y) + ((float)x3.x + (float)x3.y);
+        }
+        sums[j * G + gg] = make_float4(s0, s1, 0.0f, 0.0f);
+    }
+    __syncthreads();
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Stage activation rows src_row(j), j < nrows, into LDS rows 0..nrows-1 as
 // dot2 pairs, then their per-class sums.
 template <int BITS, typename RowPtr>
@@ -951,7 +983,10 @@ __attribute__((amdgpu_waves_per_eu(w4_waves_per_eu<MAXM, NG>()))) void w4_kernel
 // draft layer step: T = 16 104.0 -> 99.4 us, T = 4 65.5 -> 64.0 us; the down
 // projection at four waves per SIMD (127 VGPRs) a further 2.6 us at T = 16.
 // Four buffers (every group of a wave requested up front; 201 VGPRs, two
-// waves per SIMD) were slower: 72.2 and 119.7 us.
+// waves per SIMD) were slower: 72.2 and 119.7 us.  Staging the rows with
+// global->LDS loads instead of through registers frees 32 VGPRs (153 -> 122
+// for the gate/up projection: four waves per SIMD, four workgroups per CU):
+// layer step T = 4 52.2 -> 49.1 us, T = 16 90.4 -> 85.1 us.
 #ifndef SMOE_W4_MFMA_WAVES
 #define SMOE_W4_MFMA_WAVES 4
 #endif
@@ -963,6 +998,9 @@ __attribute__((amdgpu_waves_per_eu(w4_waves_per_eu<MAXM, NG>()))) void w4_kernel
 #endif
 #ifndef SMOE_W4_MFMA_BUFS
 #define SMOE_W4_MFMA_BUFS 2
+#endif
+#ifndef SMOE_W4_MFMA_DMA
+#define SMOE_W4_MFMA_DMA 1  // activation rows staged by global->LDS loads
 #endif
 constexpr int kMfmaWaves = SMOE_W4_MFMA_WAVES;
 constexpr int kMfmaBufs = SMOE_W4_MFMA_BUFS;  // groups of a wave in flight
@@ -1253,8 +1291,60 @@ w4_mfma_kernel(W4Args a, RowsShared sh) {
         // groups, and the rows are written to LDS while the weights are in
         // flight (requests are unconditional, so the wait for the rows is an
         // exact count that leaves the weights outstanding)
-        uint4 xv[kRowChunksPerThread];
         const int nch = nrows * K8;
+        // A operand row (MFMA row l%16) and the LDS rows of this lane's D rows
+        // (requested before the rows, so one wait covers both)
+        const bool aok = q < M;
+        const int ar = direct ? a.sorted_token[mc + (aok ? q : 0)] : (aok ? q : 0);
+        int drow[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * kq + i;
+            const int rr = r < M ? r : 0;
+            drow[i] = direct ? a.sorted_token[mc + rr] : rr;
+        }
+#if SMOE_W4_MFMA_DMA
+        // The rows go straight to LDS in natural order (global->LDS loads:
+        // a wave's instruction fills 64 consecutive 16-byte chunks, and no
+        // register holds them), requested before the weights; once they have
+        // landed their pairs are permuted in place and the sums taken.
+        if (stage) {
+            const bool gath = PHASE == 1 && !direct;
+#pragma unroll
+            for (int u = 0; u < kRowChunksPerThread; ++u) {
+                const int b0 = wave_u * 64 + u * (int)blockDim.x;  // the wave's first chunk
+                if (b0 < nch) {
+                    // gathered rows: the (at most two, K8 >= 64) rows of the
+                    // wave's chunks take their tokens through scalar loads
+                    const int jlo = b0 / K8;
+                    const int jhi = jlo + 1 < nrows ? jlo + 1 : nrows - 1;
+                    const int tlo = gath ? ld_const(a.sorted_token + mc + jlo) : 0;
+                    const int thi = gath ? ld_const(a.sorted_token + mc + jhi) : 0;
+                    int idx = b0 + lane;
+                    idx = idx < nch ? idx : nch - 1;  // (its LDS slot lies past the rows)
+                    const int j = idx / K8;
+                    size_t r;
+                    if (gath) r = (size_t)((j == jlo) ? tlo : thi);
+                    else r = direct ? (size_t)j : (size_t)(mc + j);
+                    __builtin_amdgcn_global_load_lds(
+                        (const void*)(a.xin + r * K + 8 * (idx - j * K8)),
+                        (__attribute__((address_space(3))) void*)(l.xs + b0), 16, 0, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < kMfmaBufs; ++b) mfma_load(L[b], src, g0 + b * kMfmaWaves, G, colc, kq);
+        __builtin_amdgcn_sched_barrier(0);
+        if (stage) {
+            // this wave's chunks have landed (the weight requests after them
+            // stay in flight), then every wave's: a plain barrier (a fenced
+            // one would also wait for the weights)
+            wait_vm<6 * kMfmaBufs>();
+            __builtin_amdgcn_s_barrier();
+            finish_rows_natural4(l.xs, l.sums, nrows, K8, G);
+        }
+#else
+        uint4 xv[kRowChunksPerThread];
         if (stage && PHASE == 1 && !direct && K8 >= 64) {
             // gathered rows: a wave's 64 consecutive chunks span at most two
             // rows, whose tokens come through scalar loads issued together
@@ -1305,16 +1395,7 @@ w4_mfma_kernel(W4Args a, RowsShared sh) {
             }
             finish_rows<4>(l.xs, l.sums, nrows, K8, G);
         }
-        // A operand row (MFMA row l%16) and the LDS rows of this lane's D rows
-        const bool aok = q < M;
-        const int ar = direct ? a.sorted_token[mc + (aok ? q : 0)] : (aok ? q : 0);
-        int drow[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * kq + i;
-            const int rr = r < M ? r : 0;
-            drow[i] = direct ? a.sorted_token[mc + rr] : rr;
-        }
+#endif
         f4_t acc[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[c] = f4_t{0.f, 0.f, 0.f, 0.f};
@@ -2191,7 +2272,9 @@ PhasePlan plan_mfma(int phase, int T, int K, int N, int I) {
     p.mch = cap < kMfmaRows ? cap : kMfmaRows;
     p.direct = (phase == 1 && T <= cap) ? 1 : 0;
     p.xr = p.direct ? T : p.mch;
-    p.lds = (size_t)p.xr * row_bytes + (size_t)kMfmaWaves * p.mch * 64 * 4;
+    // + 1 KB: a wave's last global->LDS row load may fill up to 63 chunks
+    // past the rows (into the sums and the reduction area, both unused then)
+    p.lds = (size_t)p.xr * row_bytes + (size_t)kMfmaWaves * p.mch * 64 * 4 + 1024;
     p.ng = 1;
     return p;
 }
