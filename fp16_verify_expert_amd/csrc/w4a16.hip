@@ -2492,8 +2492,10 @@ hipError_t launch_w4a16_ffn_shared(const uint16_t* x, const int32_t* sorted_toke
         return hipGetLastError();
     }
     // 5-16 rows: 16-column MFMA items with the one-group ring launches'
-    // arithmetic (those launches' geometry needs at least 8 steps of 128 K)
-    if (!gemv && mfma && T <= 16 && H / 128 >= 8 && Is / 128 >= 8) {
+    // arithmetic (those launches' geometry needs at least 8 steps of 128 K;
+    // the items' buffer offsets are 32-bit)
+    if (!gemv && mfma && T <= 16 && H / 128 >= 8 && Is / 128 >= 8 &&
+        4LL * Is * H < 0x7FFFFFFFLL) {
         const int rows = T * k;
         const int slots = E < rows ? E : rows;
         uint16_t* h = static_cast<uint16_t*>(ws);
