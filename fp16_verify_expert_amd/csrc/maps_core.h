@@ -173,7 +173,11 @@ SMOE_DEV void gather_block(const int32_t* ids, int n, int k, int E, int32_t* __r
 // it): thread e < E counts the pairs of expert e (and adds that count to the
 // ELB row), thread p counts the earlier pairs with its id, so no loop runs
 // over the distinct ids of a wave.  The same stable counting sort as
-// gather_block, so the same maps.
+// gather_block, so the same maps.  kDistinct (the ids of a token are
+// distinct, as a top-k's are) with at most 64 tokens: the counts come from
+// LDS atomics and a pair's rank within its expert is the number of earlier
+// tokens in the expert's token bitmask, with no loop over the pairs.
+template <bool kDistinct = false>
 SMOE_DEV void small_maps(const int32_t* ids_s, int n, int k, int E,
                          int32_t* __restrict__ counters_row, int32_t* __restrict__ off,
                          int32_t* __restrict__ sorted_token, int32_t* __restrict__ sorted_pair,
@@ -182,21 +186,42 @@ SMOE_DEV void small_maps(const int32_t* ids_s, int n, int k, int E,
     __shared__ int cnt_s[256];
     __shared__ int base_s[256];
     __shared__ int nvalid_s;
+    __shared__ unsigned long long tmask_s[kDistinct ? 256 : 1];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const bool masks = kDistinct && n <= 64 * k;  // at most 64 tokens
 
     // 1. per-expert counts (and the ELB increments); invalid ids flagged
-    if (tid < E) {
-        int c = 0;
+    if (masks) {
+        if (tid < E) {
+            cnt_s[tid] = 0;
+            tmask_s[tid] = 0ull;
+        }
+        __syncthreads();
+        if (tid < n) {
+            const int e = ids_s[tid];
+            if (e < 0 || e >= E) {
+                flag_error(err, SMOE_DERR_BAD_ID);
+            } else {
+                atomicAdd(&cnt_s[e], 1);
+                atomicOr(&tmask_s[e], 1ull << (tid / k));
+            }
+        }
+        __syncthreads();
+        if (tid < E && counters_row && cnt_s[tid]) atomicAdd(counters_row + tid, cnt_s[tid]);
+    } else {
+        if (tid < E) {
+            int c = 0;
 #pragma unroll 8
-        for (int q = 0; q < n; ++q) c += (ids_s[q] == tid) ? 1 : 0;
-        cnt_s[tid] = c;
-        if (counters_row && c) atomicAdd(counters_row + tid, c);
-    }
-    if (tid < n) {
-        const int e = ids_s[tid];
-        if (e < 0 || e >= E) flag_error(err, SMOE_DERR_BAD_ID);
+            for (int q = 0; q < n; ++q) c += (ids_s[q] == tid) ? 1 : 0;
+            cnt_s[tid] = c;
+            if (counters_row && c) atomicAdd(counters_row + tid, c);
+        }
+        if (tid < n) {
+            const int e = ids_s[tid];
+            if (e < 0 || e >= E) flag_error(err, SMOE_DERR_BAD_ID);
+        }
     }
     __syncthreads();
 
@@ -252,8 +277,14 @@ SMOE_DEV void small_maps(const int32_t* ids_s, int n, int k, int E,
         const int e = ids_s[p];
         if (e >= 0 && e < E) {
             int r = 0;
+            if (masks) {
+                // earlier pairs of e: one per earlier token that chose e
+                const int t = p / k;
+                r = __popcll(tmask_s[e] & ((1ull << t) - 1ull));
+            } else {
 #pragma unroll 8
-            for (int q = 0; q < p; ++q) r += (ids_s[q] == e) ? 1 : 0;
+                for (int q = 0; q < p; ++q) r += (ids_s[q] == e) ? 1 : 0;
+            }
             const int pos = base_s[e] + r;
             sorted_pair[pos] = p;
             sorted_token[pos] = p / k;

@@ -56,8 +56,8 @@ SMOE_DEV void plan_from_logits(const float* logit, int32_t* ids_s, int T, int E,
                                   pair_pos, active, n_active);
         return;
     }
-    smoe_maps::small_maps(ids_s, T * k, k, E, counters_row, off, sorted_token, sorted_pair,
-                          pair_pos, active, n_active, err);
+    smoe_maps::small_maps<true>(ids_s, T * k, k, E, counters_row, off, sorted_token,
+                                sorted_pair, pair_pos, active, n_active, err);
 }
 
 __global__ __launch_bounds__(kPlanThreads) void route_plan_kernel(
@@ -117,8 +117,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_tail_kernel(
     __shared__ int32_t ids_s[kPlanThreads];
     if ((int)threadIdx.x < n) ids_s[threadIdx.x] = ids[threadIdx.x];
     __syncthreads();
-    smoe_maps::small_maps(ids_s, n, k, E, counters_row, off, sorted_token, sorted_pair, pair_pos,
-                          active, n_active, err);
+    smoe_maps::small_maps<true>(ids_s, n, k, E, counters_row, off, sorted_token, sorted_pair,
+                                pair_pos, active, n_active, err);
 }
 
 #ifndef SMOE_PLAN_SPREAD_ELEMS

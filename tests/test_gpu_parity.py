@@ -902,9 +902,10 @@ def test_verify_grouped_gemm_shared(shape, T):
 # matrix-vector routine; T 5-16: MFMA items), then the one-expert ring
 # kernels after them (T 17); Qwen (shared intermediate 5632): MFMA items
 # (T 16), launches of their own after the multi-row (T 4) or one-token (T 1)
-# launches.
+# launches; hidden and shared intermediate 4096 (8 chunks per lane both ways).
 W4_SHARED_CASES = [(synth.DS, 2), (synth.DS, 4), (synth.DS, 5), (synth.DS, 9), (synth.DS, 16),
-                   (synth.DS, 17), (synth.QWEN, 4), (synth.QWEN, 16), (synth.QWEN, 1)]
+                   (synth.DS, 17), (synth.QWEN, 4), (synth.QWEN, 16), (synth.QWEN, 1),
+                   (_PHI_SHV, 3), (_PHI_SHV, 9)]
 
 
 @pytest.mark.parametrize("shape,T", W4_SHARED_CASES, ids=lambda v: getattr(v, "name", str(v)))
