@@ -22,6 +22,10 @@ Printed JSON line (rank 0):
   roofline    the dominant kernel of the step (verify_grouped_gemm, HBM
               bound): touched FP16 weight bytes per call / average call time
   roofline_draft  the same for w4a16_grouped_ffn (INT4 bytes)
+  ds_draft, qwen_verify, qwen_chunk  the other configurations' layers: the
+              DeepSeek-V2-Lite draft step at T = 1/4/16, the Qwen1.5-MoE
+              verify layer at K+1 = 9, the 24-layer Qwen chunk (16 draft steps,
+              ELB snapshot, placement, staged verify)
   cpu_baseline    the CPU oracle on a bounded sample of draft steps
 """
 from __future__ import annotations
@@ -525,6 +529,10 @@ def main():
         res["ds_draft"] = {"config": DS_WORKLOAD, "steps": K_o, "results": ds_res}
         res["qwen_verify"] = {"config": QWEN_VERIFY_WORKLOAD, "steps": K_o,
                               **qwen_verify_results(K_o, min(args.warmup, 3))}
+        # the 24-layer chunk (one timed chunk after an untimed one)
+        c5 = qwen_chunk_results(24, 1, 1)
+        res["qwen_chunk"] = {k2: c5[k2] for k2 in ("config", "draft", "placement",
+                                                     "verify_staged", "verify_all_resident")}
 
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -1088,6 +1096,13 @@ def bench_qwen_rounds(args):
 
 
 def bench_qwen_chunk(args):
+    """The Qwen-shaped draft chunk + verify (qwen_chunk_results) as a line of
+    its own."""
+    out = qwen_chunk_results(args.layers, args.steps, args.warmup, args.no_graph)
+    print(json.dumps(out), flush=True)
+
+
+def qwen_chunk_results(L, steps, warmup, no_graph=False):
     """Draft chunk + verify over L Qwen-shaped layers with 16 of 60 FP16
     experts resident per layer.  One step = 16 INT4 draft decode steps through
     all layers (ELB table [L, 60]), the chunk-boundary snapshot and placement of
@@ -1105,7 +1120,7 @@ def bench_qwen_chunk(args):
     torch.cuda.set_device(0)
     dev = torch.device("cuda")
     s = synth.QWEN_CHUNK
-    L, STEPS, TV, NRES = args.layers, 16, 17, 16
+    STEPS, TV, NRES = 16, 17, 16
     t0 = time.perf_counter()
     layers, full = qwen_layers(L, dev)
     gen_s = time.perf_counter() - t0
@@ -1121,7 +1136,7 @@ def bench_qwen_chunk(args):
         before = dict(eng.stats)
         ev[0].record()
         for st in range(STEPS):
-            if args.no_graph:
+            if no_graph:
                 eng.draft_step(xs[st])
             else:
                 eng.draft_step_graph(xs[st])
@@ -1143,11 +1158,11 @@ def bench_qwen_chunk(args):
                     shared_bytes=STEPS * L * s.shared_f16_bytes, stats=d,
                     place_bytes=L * NRES * s.f16_bytes_per_expert)
 
-    if not args.no_graph:
+    if not no_graph:
         eng.capture_draft()
-    for c in range(args.warmup and 1):
+    for c in range(warmup and 1):
         chunk(c, False)
-    res_list = [chunk(100 + c, True) for c in range(max(1, min(args.steps, 3)))]
+    res_list = [chunk(100 + c, True) for c in range(max(1, min(steps, 3)))]
     n = len(res_list)
     avg = lambda key: sum(r[key] for r in res_list) / n
     draft_ms, verify_ms, verify_res_ms, place_ms = (avg("draft_ms"), avg("verify_ms"),
@@ -1173,7 +1188,7 @@ def bench_qwen_chunk(args):
         "draft": {"ms": round(draft_ms, 3), "int4_gbps": round(value, 2),
                   "int4_plus_shared_gbps": round((int4_b + sh_b) / (draft_ms * 1e-3) / 1e9, 2),
                   "int4_bytes": round(int4_b), "shared_f16_bytes": round(sh_b),
-                  "launch": "eager" if args.no_graph else "hip_graph",
+                  "launch": "eager" if no_graph else "hip_graph",
                   "us_per_layer_step": round(1e3 * draft_ms / (STEPS * L), 2)},
         "placement": {"ms": round(place_ms, 3), "bytes": res_list[0]["place_bytes"],
                       "h2d_gbps": round(res_list[0]["place_bytes"] / (place_ms * 1e-3) / 1e9, 2)},
@@ -1187,7 +1202,9 @@ def bench_qwen_chunk(args):
                                 "weight_gbps": round(vbytes / (verify_res_ms * 1e-3) / 1e9, 2)},
         "gen_s": round(gen_s, 1),
     }
-    print(json.dumps(out), flush=True)
+    del eng, layers, full
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(layer, s, n):
