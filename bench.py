@@ -101,8 +101,8 @@ def main():
         args.graph = "on" if args.workload == "qwen_chunk" else "off"
     args.no_graph = args.graph == "off"
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "the path is single-GPU and no multi-GPU figure is produced.", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); the path is "
+              "single-GPU and no multi-GPU figure is produced.", file=sys.stderr)
         sys.exit(2)
     if args.workload == "qwen_chunk":
         return bench_qwen_chunk(args)
