@@ -1003,6 +1003,11 @@ __attribute__((amdgpu_waves_per_eu(w4_waves_per_eu<MAXM, NG>()))) void w4_kernel
 #define SMOE_W4_MFMA_DMA 1  // activation rows staged by global->LDS loads
 #endif
 constexpr int kMfmaWaves = SMOE_W4_MFMA_WAVES;
+#ifndef SMOE_W4_MFMA_WAVES2
+#define SMOE_W4_MFMA_WAVES2 SMOE_W4_MFMA_WAVES  // down projection
+#endif
+template <int PHASE>
+constexpr int mfma_waves() { return PHASE == 1 ? SMOE_W4_MFMA_WAVES : SMOE_W4_MFMA_WAVES2; }
 constexpr int kMfmaBufs = SMOE_W4_MFMA_BUFS;  // groups of a wave in flight
 constexpr int kMfmaRows = 16;
 constexpr int kMfmaLdsBytes = 32 * 1024;  // activation staging budget
@@ -1137,11 +1142,12 @@ template <int PHASE>
 SMOE_DEV void shared_mfma_item(const RowsShared& sh, int b, f4_t* red) {
     constexpr int NM = (PHASE == 1) ? 2 : 1;
     constexpr int WPI = (PHASE == 1) ? SMOE_SH_GU_WAVES : SMOE_SH_DN_WAVES;  // waves per item
-    static_assert(WPI >= 1 && kMfmaWaves % WPI == 0, "items per workgroup");
+    constexpr int W = mfma_waves<PHASE>();
+    static_assert(WPI >= 1 && W % WPI == 0, "items per workgroup");
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int sub = wave % WPI;
-    const int item = b * (kMfmaWaves / WPI) + wave / WPI;
+    const int item = b * (W / WPI) + wave / WPI;
     const bool live = item * 16 < sh.Ncol;
     const int n0 = live ? item * 16 : 0;
     const int K = sh.K;
@@ -1223,7 +1229,7 @@ SMOE_DEV void shared_mfma_item(const RowsShared& sh, int b, f4_t* red) {
 // (4 per workgroup, the matrix-vector routine with CPLS chunks per lane);
 // CPLS < 0: its 16-column MFMA items (shared_mfma_item).
 template <int PHASE, int CPLS = 0>
-__global__ __launch_bounds__(64 * kMfmaWaves)
+__global__ __launch_bounds__(64 * mfma_waves<PHASE>())
 __attribute__((amdgpu_waves_per_eu(PHASE == 1 ? SMOE_W4_MFMA_WPE : SMOE_W4_MFMA_WPE2))) void
 w4_mfma_kernel(W4Args a, RowsShared sh) {
     extern __shared__ uint4 smem[];
@@ -1272,7 +1278,8 @@ w4_mfma_kernel(W4Args a, RowsShared sh) {
     const int zsh = zero_shift<4>(colc);
     const W4Src src = make_src<4>(wm, K, N);
     const Masks<4> mk;
-    float* red = l.red;  // [kMfmaWaves][MCH][64]
+    constexpr int W = mfma_waves<PHASE>();
+    float* red = l.red;  // [W][MCH][64]
     const bool direct = (PHASE == 1) && a.direct;
     const int g0 = wave;
     MfmaLoad L[kMfmaBufs];
@@ -1333,7 +1340,7 @@ w4_mfma_kernel(W4Args a, RowsShared sh) {
             }
         }
 #pragma unroll
-        for (int b = 0; b < kMfmaBufs; ++b) mfma_load(L[b], src, g0 + b * kMfmaWaves, G, colc, kq);
+        for (int b = 0; b < kMfmaBufs; ++b) mfma_load(L[b], src, g0 + b * W, G, colc, kq);
         __builtin_amdgcn_sched_barrier(0);
         if (stage) {
             // this wave's chunks have landed (the weight requests after them
@@ -1378,7 +1385,7 @@ w4_mfma_kernel(W4Args a, RowsShared sh) {
         }
         // (unconditional: groups past G read nothing and are not multiplied)
 #pragma unroll
-        for (int b = 0; b < kMfmaBufs; ++b) mfma_load(L[b], src, g0 + b * kMfmaWaves, G, colc, kq);
+        for (int b = 0; b < kMfmaBufs; ++b) mfma_load(L[b], src, g0 + b * W, G, colc, kq);
         __builtin_amdgcn_sched_barrier(0);
         if (stage) {
 #pragma unroll
@@ -1402,13 +1409,13 @@ w4_mfma_kernel(W4Args a, RowsShared sh) {
         // groups wave, wave + 4, ... through the buffers, each refilled with
         // the group kMfmaBufs further on as soon as it has been multiplied
         // (branches on the group index are wave-uniform)
-        for (int g = g0; g < G; g += kMfmaBufs * kMfmaWaves) {
+        for (int g = g0; g < G; g += kMfmaBufs * W) {
 #pragma unroll
             for (int b = 0; b < kMfmaBufs; ++b) {
-                const int gb = g + b * kMfmaWaves;
+                const int gb = g + b * W;
                 if (b == 0 || gb < G)
                     mfma_group(L[b], l.xs, l.sums, ar, aok, drow, gb, K8, G, kq, zsh, mk, acc);
-                mfma_load(L[b], src, gb + kMfmaBufs * kMfmaWaves, G, colc, kq);
+                mfma_load(L[b], src, gb + kMfmaBufs * W, G, colc, kq);
             }
         }
         // the waves' tiles, added in a fixed order
@@ -1424,7 +1431,7 @@ w4_mfma_kernel(W4Args a, RowsShared sh) {
             for (int idx = tid; idx < M * 32; idx += blockDim.x) {
                 const int m = idx >> 5, j = idx & 31;
                 float gv = 0.0f, uv = 0.0f;
-                for (int w = 0; w < kMfmaWaves; ++w) {
+                for (int w = 0; w < W; ++w) {
                     gv += red[(w * MCH + m) * 64 + j];
                     uv += red[(w * MCH + m) * 64 + 32 + j];
                 }
@@ -1435,7 +1442,7 @@ w4_mfma_kernel(W4Args a, RowsShared sh) {
                 const int m = idx >> 6, j = idx & 63;
                 if (cb * 64 + j < N) {
                     float v = 0.0f;
-                    for (int w = 0; w < kMfmaWaves; ++w) v += red[(w * MCH + m) * 64 + j];
+                    for (int w = 0; w < W; ++w) v += red[(w * MCH + m) * 64 + j];
                     a.out[(size_t)(mc + m) * N + cb * 64 + j] = f2h(v);
                 }
             }
@@ -2264,7 +2271,8 @@ PhasePlan plan_mfma(int phase, int T, int K, int N, int I) {
     PhasePlan p{};
     p.lpr = 16;
     p.nCB = (phase == 1) ? I / 32 : (N + 63) / 64;
-    p.waves = kMfmaWaves;
+    const int W = (phase == 1) ? mfma_waves<1>() : mfma_waves<2>();
+    p.waves = W;
     const int G = K / 128;
     const size_t row_bytes = (size_t)K * 2 + (size_t)G * 16;
     int cap = (int)(kMfmaLdsBytes / row_bytes);
@@ -2274,7 +2282,7 @@ PhasePlan plan_mfma(int phase, int T, int K, int N, int I) {
     p.xr = p.direct ? T : p.mch;
     // + 1 KB: a wave's last global->LDS row load may fill up to 63 chunks
     // past the rows (into the sums and the reduction area, both unused then)
-    p.lds = (size_t)p.xr * row_bytes + (size_t)kMfmaWaves * p.mch * 64 * 4 + 1024;
+    p.lds = (size_t)p.xr * row_bytes + (size_t)W * p.mch * 64 * 4 + 1024;
     p.ng = 1;
     return p;
 }
@@ -2400,14 +2408,14 @@ hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, cons
         const PhasePlan m1 = plan_mfma(1, T, H, 2 * I, I);
         const W4Args b1 = phase_args(m1, x, sorted_token, off, active, n_active, experts, H,
                                      2 * I, I, T, E, h, err, desc);
-        hipLaunchKernelGGL((w4_mfma_kernel<1>), dim3(slots * m1.nCB), dim3(64 * kMfmaWaves),
+        hipLaunchKernelGGL((w4_mfma_kernel<1>), dim3(slots * m1.nCB), dim3(64 * m1.waves),
                            m1.lds, s, b1, RowsShared{});
         hipError_t e1 = hipGetLastError();
         if (e1 != hipSuccess) return e1;
         const PhasePlan m2 = plan_mfma(2, T, I, H, I);
         const W4Args b2 =
             phase_args(m2, h, nullptr, off, active, n_active, experts, I, H, I, T, E, y, err, desc);
-        hipLaunchKernelGGL((w4_mfma_kernel<2>), dim3(slots * m2.nCB), dim3(64 * kMfmaWaves),
+        hipLaunchKernelGGL((w4_mfma_kernel<2>), dim3(slots * m2.nCB), dim3(64 * m2.waves),
                            m2.lds, s, b2, RowsShared{});
         return hipGetLastError();
     }
@@ -2474,8 +2482,9 @@ hipError_t launch_w4a16_ffn_shared(const uint16_t* x, const int32_t* sorted_toke
                                      2 * I, I, T, E, h, err, desc);
         RowsShared s1 = g1;
         s1.wg0 = slots * m1.nCB;
-        if (SMOE_SH_FRONT_ROWS) s1.nfront = (Is + 3) / 4;
-        const dim3 grid1(slots * m1.nCB + (Is + 3) / 4), block(64 * kMfmaWaves);
+        const int nsh1 = (Is + m1.waves - 1) / m1.waves;  // one column per wave
+        if (SMOE_SH_FRONT_ROWS) s1.nfront = nsh1;
+        const dim3 grid1(slots * m1.nCB + nsh1), block(64 * m1.waves);
         if (c1 == 4) hipLaunchKernelGGL((w4_mfma_kernel<1, 4>), grid1, block, m1.lds, s, b1, s1);
         else hipLaunchKernelGGL((w4_mfma_kernel<1, 8>), grid1, block, m1.lds, s, b1, s1);
         hipError_t e = hipGetLastError();
@@ -2485,10 +2494,11 @@ hipError_t launch_w4a16_ffn_shared(const uint16_t* x, const int32_t* sorted_toke
             phase_args(m2, h, nullptr, off, active, n_active, experts, I, H, I, T, E, y, err, desc);
         RowsShared s2 = g2;
         s2.wg0 = slots * m2.nCB;
-        if (SMOE_SH_FRONT_ROWS) s2.nfront = (H + 3) / 4;
-        const dim3 grid2(slots * m2.nCB + (H + 3) / 4);
-        if (c2 == 6) hipLaunchKernelGGL((w4_mfma_kernel<2, 6>), grid2, block, m2.lds, s, b2, s2);
-        else hipLaunchKernelGGL((w4_mfma_kernel<2, 8>), grid2, block, m2.lds, s, b2, s2);
+        const int nsh2 = (H + m2.waves - 1) / m2.waves;
+        if (SMOE_SH_FRONT_ROWS) s2.nfront = nsh2;
+        const dim3 grid2(slots * m2.nCB + nsh2), block2(64 * m2.waves);
+        if (c2 == 6) hipLaunchKernelGGL((w4_mfma_kernel<2, 6>), grid2, block2, m2.lds, s, b2, s2);
+        else hipLaunchKernelGGL((w4_mfma_kernel<2, 8>), grid2, block2, m2.lds, s, b2, s2);
         return hipGetLastError();
     }
     // 5-16 rows: 16-column MFMA items with the one-group ring launches'
@@ -2501,9 +2511,10 @@ hipError_t launch_w4a16_ffn_shared(const uint16_t* x, const int32_t* sorted_toke
         uint16_t* h = static_cast<uint16_t*>(ws);
         SlotDesc* desc =
             reinterpret_cast<SlotDesc*>(static_cast<char*>(ws) + h_bytes(T, k, I));
-        constexpr int ipw1 = kMfmaWaves / SMOE_SH_GU_WAVES;  // items per workgroup
-        constexpr int ipw2 = kMfmaWaves / SMOE_SH_DN_WAVES;
-        const size_t red1 = (size_t)kMfmaWaves * 2 * 64 * 16, red2 = red1 / 2;
+        constexpr int ipw1 = mfma_waves<1>() / SMOE_SH_GU_WAVES;  // items per workgroup
+        constexpr int ipw2 = mfma_waves<2>() / SMOE_SH_DN_WAVES;
+        const size_t red1 = (size_t)mfma_waves<1>() * 2 * 64 * 16;
+        const size_t red2 = (size_t)mfma_waves<2>() * 64 * 16;
         PhasePlan m1 = plan_mfma(1, T, H, 2 * I, I);
         if (m1.lds < red1) m1.lds = red1;
         const W4Args b1 = phase_args(m1, x, sorted_token, off, active, n_active, experts, H,
@@ -2511,9 +2522,8 @@ hipError_t launch_w4a16_ffn_shared(const uint16_t* x, const int32_t* sorted_toke
         RowsShared s1 = g1;
         s1.wg0 = slots * m1.nCB;
         if (SMOE_SH_FRONT_MFMA) s1.nfront = (Is / 16 + ipw1 - 1) / ipw1;
-        const dim3 block(64 * kMfmaWaves);
         hipLaunchKernelGGL((w4_mfma_kernel<1, -1>), dim3(s1.wg0 + (Is / 16 + ipw1 - 1) / ipw1),
-                           block, m1.lds, s, b1, s1);
+                           dim3(64 * m1.waves), m1.lds, s, b1, s1);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         PhasePlan m2 = plan_mfma(2, T, I, H, I);
@@ -2524,7 +2534,7 @@ hipError_t launch_w4a16_ffn_shared(const uint16_t* x, const int32_t* sorted_toke
         s2.wg0 = slots * m2.nCB;
         if (SMOE_SH_FRONT_MFMA) s2.nfront = (H / 16 + ipw2 - 1) / ipw2;
         hipLaunchKernelGGL((w4_mfma_kernel<2, -1>), dim3(s2.wg0 + (H / 16 + ipw2 - 1) / ipw2),
-                           block, m2.lds, s, b2, s2);
+                           dim3(64 * m2.waves), m2.lds, s, b2, s2);
         return hipGetLastError();
     }
     hipError_t e = launch_w4a16_ffn(x, sorted_token, off, active, n_active, experts, T, k, H, I,
