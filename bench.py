@@ -791,10 +791,12 @@ def ds_draft_results(K, warmup):
         idx = [(warmup + st) % POOL for st in range(K)]
         b_int4 = sum(touched[i] * b4 for i in idx) / K
         b_sh = s.shared_f16_bytes
-        us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / K
+        per = sorted(1e3 * a.elapsed_time(b) for a, b in ev)
+        us = sum(per) / K
         results.append({"T": T, "touched_experts_avg": round(sum(touched[i] for i in idx) / K, 2),
                         "int4_bytes_avg": round(b_int4), "shared_f16_bytes": b_sh,
-                        "step_us": round(us, 2),
+                        "step_us": round(us, 2), "step_us_median": round(per[K // 2], 2),
+                        "step_us_max": round(per[-1], 2),
                         "int4_gbps": round(b_int4 / us / 1e3, 1),
                         "all_weight_gbps": round((b_int4 + b_sh) / us / 1e3, 1),
                         "all_weight_frac_hbm": round((b_int4 + b_sh) / us / 1e3 / HBM_PEAK_GBS, 4),
