@@ -1008,6 +1008,8 @@ constexpr int kMfmaWaves = SMOE_W4_MFMA_WAVES;
 #endif
 template <int PHASE>
 constexpr int mfma_waves() { return PHASE == 1 ? SMOE_W4_MFMA_WAVES : SMOE_W4_MFMA_WAVES2; }
+// the reduction area (>= waves * 256 bytes) absorbs a row load's overrun
+static_assert(mfma_waves<1>() >= 4 && mfma_waves<2>() >= 4, "at least 4 waves per workgroup");
 constexpr int kMfmaBufs = SMOE_W4_MFMA_BUFS;  // groups of a wave in flight
 constexpr int kMfmaRows = 16;
 constexpr int kMfmaLdsBytes = 32 * 1024;  // activation staging budget
@@ -1328,7 +1330,8 @@ w4_mfma_kernel(W4Args a, RowsShared sh) {
                     const int tlo = gath ? ld_const(a.sorted_token + mc + jlo) : 0;
                     const int thi = gath ? ld_const(a.sorted_token + mc + jhi) : 0;
                     int idx = b0 + lane;
-                    idx = idx < nch ? idx : nch - 1;  // (its LDS slot lies past the rows)
+                    idx = idx < nch ? idx : nch - 1;  // (its LDS slot lies past the rows,
+                                                      // in the sums or the reduction area)
                     const int j = idx / K8;
                     size_t r;
                     if (gath) r = (size_t)((j == jlo) ? tlo : thi);
@@ -2280,9 +2283,10 @@ PhasePlan plan_mfma(int phase, int T, int K, int N, int I) {
     p.mch = cap < kMfmaRows ? cap : kMfmaRows;
     p.direct = (phase == 1 && T <= cap) ? 1 : 0;
     p.xr = p.direct ? T : p.mch;
-    // + 1 KB: a wave's last global->LDS row load may fill up to 63 chunks
-    // past the rows (into the sums and the reduction area, both unused then)
-    p.lds = (size_t)p.xr * row_bytes + (size_t)W * p.mch * 64 * 4 + 1024;
+    // (a wave's last global->LDS row load may fill up to 63 chunks, 1008
+    // bytes, past the rows: into the sums and the reduction area, at least
+    // W * 256 bytes together and both unused while rows are staged)
+    p.lds = (size_t)p.xr * row_bytes + (size_t)W * p.mch * 64 * 4;
     p.ng = 1;
     return p;
 }
