@@ -2443,17 +2443,17 @@ hipError_t launch_w4a16_ffn(const uint16_t* x, const int32_t* sorted_token, cons
 
 // The shared expert's projection as launches of its own (4 columns per
 // workgroup), any chunk count of the matrix-vector routine.
+// (chunk counts rounded up as verify_grouped_gemm's matrix-vector launches
+// round them)
 template <int PHASE>
 static hipError_t launch_shared_rows(const RowsShared& sh, int cpl, hipStream_t s) {
     const dim3 grid((sh.Ncol + 3) / 4), block(256);
-    switch (cpl) {
-        case 2: shared_rows_kernel<PHASE, 2><<<grid, block, 0, s>>>(sh); break;
-        case 4: shared_rows_kernel<PHASE, 4><<<grid, block, 0, s>>>(sh); break;
-        case 6: shared_rows_kernel<PHASE, 6><<<grid, block, 0, s>>>(sh); break;
-        case 8: shared_rows_kernel<PHASE, 8><<<grid, block, 0, s>>>(sh); break;
-        case 12: shared_rows_kernel<PHASE, 12><<<grid, block, 0, s>>>(sh); break;
-        default: shared_rows_kernel<PHASE, 16><<<grid, block, 0, s>>>(sh); break;
-    }
+    if (cpl <= 2) shared_rows_kernel<PHASE, 2><<<grid, block, 0, s>>>(sh);
+    else if (cpl <= 4) shared_rows_kernel<PHASE, 4><<<grid, block, 0, s>>>(sh);
+    else if (cpl <= 6) shared_rows_kernel<PHASE, 6><<<grid, block, 0, s>>>(sh);
+    else if (cpl <= 8) shared_rows_kernel<PHASE, 8><<<grid, block, 0, s>>>(sh);
+    else if (cpl <= 12) shared_rows_kernel<PHASE, 12><<<grid, block, 0, s>>>(sh);
+    else shared_rows_kernel<PHASE, 16><<<grid, block, 0, s>>>(sh);
     return hipGetLastError();
 }
 

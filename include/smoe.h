@@ -248,9 +248,10 @@ smoe_status w4a16_grouped_ffn(const uint16_t* x, const int32_t* sorted_token,
  *   shared_out     fp16 [T, H] out: shared_h . w2^T (unscaled: a sigmoid gate
  *                  is the combine's shared_scale)
  * shared_h and shared_out are bit-identical to verify_grouped_gemm's outputs
- * for the shared expert as its only expert with all T rows in order (the
- * matrix-vector routine up to 4 rows, the one-expert ring kernels above),
- * as long as that call stays out of its dense regime (T < 64).  All four
+ * for the shared expert as its only expert with all T rows in order: up to
+ * 4 rows (both take the matrix-vector routine), and for 5..63 rows when H and
+ * shared_I are at least 1024 (both take the one-expert ring arithmetic);
+ * other shapes agree within the FP16 tolerance of the reference.  All four
  * shared pointers are required (SMOE_ERR_NULL), 16-byte aligned
  * (SMOE_ERR_SHAPE).
  * ---------------------------------------------------------------------- */

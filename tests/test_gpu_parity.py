@@ -906,6 +906,9 @@ def test_verify_grouped_gemm_shared(shape, T):
 W4_SHARED_CASES = [(synth.DS, 2), (synth.DS, 4), (synth.DS, 5), (synth.DS, 9), (synth.DS, 16),
                    (synth.DS, 17), (synth.QWEN, 4), (synth.QWEN, 16), (synth.QWEN, 1),
                    (_PHI_SHV, 3), (_PHI_SHV, 9)]
+# below 1024 the verify call takes other kernels for the lone shared expert:
+# the shared output is held to the oracle only
+_TINY_SH = dataclasses.replace(synth.TINY, name="tiny_shared", shared_I=384)
 
 
 @pytest.mark.parametrize("shape,T", W4_SHARED_CASES, ids=lambda v: getattr(v, "name", str(v)))
@@ -943,6 +946,39 @@ def test_w4a16_grouped_ffn_shared(shape, T):
             first = so.clone()
         else:
             assert torch.equal(so, first), "second call differs"
+    say(f"  shared l2={st['l2']:.2e} maxabs={st['maxabs']:.2e}")
+
+
+@pytest.mark.parametrize("T", [3, 9, 20])
+def test_w4a16_grouped_ffn_shared_small(T):
+    """Hidden 256 and shared intermediate 384: the standalone matrix-vector
+    launches (T 3) and the one-group ring launches (T 9, 20) after the routed
+    ones; routed rows bit-identical to w4a16_grouped_ffn's, the shared expert
+    within the bars of the oracle's."""
+    shape = _TINY_SH
+    say(f"w4a16 + shared {shape.name} T={T}")
+    E, k, H, I, Is = shape.E, shape.k, shape.H, shape.I, shape.shared_I
+    L = _layer(shape, (T,), steps=(2,), f16=False)
+    x = synth.tokens(shape, T, step=2)
+    dx = dev(x)
+    err = _err()
+    ids, _, _ = fve.moe_route_topk(dx, L.d_router, k)
+    gm = fve.moe_gather(ids, E, err)
+    ws = fve.new_workspace(0, T, k, H, I, E)
+    y_ref = fve.w4a16_grouped_ffn(dx, gm, L.t4, T, k, H, I, E, ws).clone()
+    shared = (dev(L.shared["w13"]), dev(L.shared["w2"]))
+    ref_sh = oracle.expert_ffn_f16(x, L.shared["w13"], L.shared["w2"])
+    y, so = fve.w4a16_grouped_ffn_shared(dx, gm, L.t4, T, k, H, I, E, ws, shared, err_word=err)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) == 0
+    assert torch.equal(y[:T * k], y_ref[:T * k])
+    if T <= 4:  # both calls take the matrix-vector routine at any size
+        iota = torch.arange(T, dtype=torch.int32, device="cuda")
+        offs = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+        wsv = fve.new_workspace(1, T, 1, H, Is, 1)
+        so_ref = fve.verify_grouped_gemm(dx, iota, offs, L.tsh, T, T, H, Is, 1, wsv)
+        assert torch.equal(so, so_ref[:T])
+    st = assert_fp16_close(host(so), ref_sh, f"w4a16 shared {shape.name} T={T}")
     say(f"  shared l2={st['l2']:.2e} maxabs={st['maxabs']:.2e}")
 
 
