@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-sample", type=int, default=6,
+    ap.add_argument("--cpu-sample", type=int, default=30,
                     help="draft steps of the oracle timed for cpu_baseline (0 = skip)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
