@@ -765,6 +765,37 @@ def test_verify_dense_mask_and_skew():
     del keep
 
 
+def test_verify_dense_forms_bit_identical():
+    """The dense regime's two forms of the tile -- the global->LDS ring (at
+    least a full 128-row tile per expert on average) and the register-staged
+    form -- give the same bits: the same routed rows declared over 8 experts
+    (1024 rows: the ring) and over 16 whose last 8 are empty (the register
+    form), both against the oracle too."""
+    s, T = synth.TINY, 512
+    data = synth.make_layer(s, 0, int4=False, f16=True)
+    t16, keep = upload_f16(data["f16"])
+    t16b, keep_b = upload_f16(list(data["f16"]) + [data["f16"][0]] * s.E)  # 8-15 never touched
+    x = synth.tokens(s, T, step=5)
+    rng = np.random.default_rng(12)
+    ids = np.stack([rng.permutation(s.E)[:s.k] for _ in range(T)]).astype(np.int32)
+    dx = dev(x)
+    gm = fve.moe_gather(dev(ids), s.E)
+    rows = T * s.k
+    assert rows >= 128 * s.E and rows < 128 * 2 * s.E
+    ws = fve.new_workspace(1, T, s.k, s.H, s.I, s.E)
+    ring = fve.verify_grouped_gemm(dx, gm["sorted_token"], gm["offsets"], t16, T, rows, s.H,
+                                   s.I, s.E, ws)
+    off2 = torch.cat([gm["offsets"], gm["offsets"][-1:].repeat(s.E)])
+    ws2 = fve.new_workspace(1, T, s.k, s.H, s.I, 2 * s.E)
+    reg = fve.verify_grouped_gemm(dx, gm["sorted_token"], off2, t16b, T, rows, s.H, s.I,
+                                  2 * s.E, ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(ring[:rows], reg[:rows])
+    ref = oracle.grouped_ffn(x, oracle.gather_maps(ids, s.E), data["f16"], "f16")
+    assert_fp16_close(host(ring)[:rows], ref, "dense forms")
+    del keep, keep_b
+
+
 def test_shared_expert_dense():
     """A shared expert over 128 rows (one group of T rows): dense regime."""
     s, T = synth.QWEN, 128
