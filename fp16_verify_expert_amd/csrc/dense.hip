@@ -524,6 +524,17 @@ hipError_t launch_dense_ffn(const uint16_t* x, const int32_t* sorted_token, cons
                             hipStream_t s) {
     const int slots = active ? (E < rows ? E : rows) : E;
     const int mt_bound = (rows + kBM - 1) / kBM + slots;  // row tiles of all experts, at most
+    // The ring form where the touched experts average at least a full row
+    // tile (measured at T = 2048 on the Phi-3.5-MoE shape, 256 rows per
+    // expert: 1394 -> 1294 us per call); with fewer rows per expert (the
+    // DeepSeek-V2-Lite shape at T = 700, about 66) the register-staged form's
+    // 128-byte row runs stream the weights better (350 against 366 us).  The
+    // ring's down projection takes 256-column tiles when H has no partial
+    // one (half the work items, one round of two per CU at the Phi shape:
+    // 1299 -> 1264 us; H = 384 keeps 128: 37 against 41 us).  Every choice
+    // gives the same bits.
+    const bool ring = rows >= kBM * slots;
+    const int bn2 = (ring && H % 256 == 0) ? 256 : kBN2;
     DenseArgs a1{};
     a1.xin = x;
     a1.sorted_token = sorted_token;
@@ -542,7 +553,7 @@ hipError_t launch_dense_ffn(const uint16_t* x, const int32_t* sorted_token, cons
     a2.sorted_token = nullptr;
     a2.K = I;
     a2.Ncol = H;
-    a2.nNT = (H + kBN2 - 1) / kBN2;
+    a2.nNT = (H + bn2 - 1) / bn2;
     a2.Wpad = ((mt_bound * a2.nNT) + 7) & ~7;
     a2.out = y;
     // the two projections list the same experts; each plan holds its own item bases
@@ -552,17 +563,14 @@ hipError_t launch_dense_ffn(const uint16_t* x, const int32_t* sorted_token, cons
     dense_plan_kernel<<<1, 64, 0, s>>>(off, active, n_active, mask, E, a2.nNT, plan2);
     hipError_t st = hipGetLastError();
     if (st != hipSuccess) return st;
-    // The ring form where the touched experts average at least a full row
-    // tile (measured at T = 2048 on the Phi-3.5-MoE shape, 256 rows per
-    // expert: 1394 -> 1294 us per call); with fewer rows per expert (the
-    // DeepSeek-V2-Lite shape at T = 700, about 66) the register-staged form's
-    // 128-byte row runs stream the weights better (350 against 366 us).  Both
-    // give the same bits.
-    if (rows >= kBM * slots) {
+    if (ring) {
         dense_ring_kernel<1, kBN1, SMOE_DENSE_STAGES><<<a1.Wpad, kThreads, 0, s>>>(a1);
         st = hipGetLastError();
         if (st != hipSuccess) return st;
-        dense_ring_kernel<2, kBN2, SMOE_DENSE_STAGES><<<a2.Wpad, kThreads, 0, s>>>(a2);
+        if (bn2 == 256)
+            dense_ring_kernel<2, 256, SMOE_DENSE_STAGES><<<a2.Wpad, kThreads, 0, s>>>(a2);
+        else
+            dense_ring_kernel<2, kBN2, SMOE_DENSE_STAGES><<<a2.Wpad, kThreads, 0, s>>>(a2);
         return hipGetLastError();
     }
     dense_gemm_kernel<1, kBN1><<<a1.Wpad, kThreads, 0, s>>>(a1);
