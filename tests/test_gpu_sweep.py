@@ -10,7 +10,7 @@ import dataclasses
 import numpy as np
 import pytest
 import torch
-from hypothesis import HealthCheck, given, settings
+from hypothesis import HealthCheck, example, given, settings
 from hypothesis import strategies as st
 
 import fp16_verify_expert_amd as fve
@@ -58,3 +58,81 @@ def test_random_layer_shapes(shape):
         assert_fp16_close(host(got["y"])[:rows], y_ref, f"{kind} FFN {shape}")
         ref = oracle.moe_layer(x, L.router, k, experts, kind)
         assert_fp16_close(host(got["out"]), ref["out"], f"{kind} layer {shape}")
+
+
+@st.composite
+def shared_layer_shapes(draw):
+    E = draw(st.integers(1, 64))
+    k = draw(st.integers(1, min(E, 8)))
+    T = draw(st.sampled_from([1, 1, 2, 3, 4, 5, 8, 9, 16, 17, 33]))
+    H = draw(st.sampled_from([128, 256, 512, 1024, 2048]))
+    I = 128 * draw(st.integers(1, 4))
+    Is = 128 * draw(st.integers(1, 12))
+    gated = draw(st.booleans())
+    return E, k, T, H, I, Is, gated
+
+
+@settings(max_examples=20, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(shared_layer_shapes())
+# branches the draws may miss: MFMA shared items (5-16 rows, hidden and
+# shared intermediate >= 1024), one-token steps with the shared columns fused
+# into both launches (DeepSeek- and Qwen-like chunk counts), few-row
+# matrix-vector items
+@example((16, 4, 9, 1024, 256, 1024, True))
+@example((8, 2, 5, 1024, 128, 1152, False))
+@example((16, 2, 16, 2048, 256, 1536, True))
+@example((64, 6, 1, 2048, 256, 2816, False))
+@example((60, 4, 1, 2048, 128, 5632, True))
+@example((8, 2, 4, 2048, 128, 1024, True))
+def test_random_shared_expert_layers(shape):
+    """Randomised layers with a dense shared expert (gated or not) through the
+    fused entry points, whose launch forms depend on the shape: the one-token
+    draft step (moe_draft_route_ffn: the shared columns inside its launches
+    where their chunk counts allow, else launches of their own), the
+    multi-row draft (w4a16_grouped_ffn_shared: matrix-vector or MFMA shared
+    items, or separate launches) and the verify (verify_grouped_gemm_shared).
+    Routing and maps exact, layer outputs within the fp16 bars of
+    oracle.moe_layer with the shared term."""
+    E, k, T, H, I, Is, gated = shape
+    say(f"shared sweep E={E} k={k} T={T} H={H} I={I} Is={Is} gated={gated}")
+    s = dataclasses.replace(synth.TINY, name=f"sw_{E}_{k}_{H}_{I}_{Is}_{int(gated)}", E=E, k=k,
+                            H=H, I=I, shared_I=Is, shared_gate=gated)
+    x = synth.tokens(s, T, step=E + 3 * k + T + Is // 128)
+    L = Layer(s, [x])
+    assert L.shared is not None and (L.d_gate is not None) == gated
+    dx = dev(x)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sw = (dev(L.shared["w13"]), dev(L.shared["w2"]))
+    r = oracle.route_topk(x, L.router, k, False, L.shared.get("gate"))
+    maps = oracle.gather_maps(r["ids"], E)
+    rows = T * k
+    for kind, experts in (("int4", L.int4), ("f16", L.f16)):
+        if kind == "int4" and T == 1:
+            ws = fve.new_workspace(0, 1, k, H, I, E)
+            ids, w, gate, gm, y, sh = fve.moe_draft_route_ffn(
+                dx, L.d_router, k, L.t4, I, ws, False, L.d_gate, err_word=err, shared=sw)
+        else:
+            ids, w, gate = fve.moe_route_topk(dx, L.d_router, k, False, L.d_gate)
+            gm = fve.moe_gather(ids, E, err)
+            if kind == "int4":
+                ws = fve.new_workspace(0, T, k, H, I, E)
+                y, sh = fve.w4a16_grouped_ffn_shared(dx, gm, L.t4, T, k, H, I, E, ws, sw,
+                                                     err_word=err)
+            else:
+                ws = fve.new_workspace(1, T, k, H, I, E)
+                y, sh = fve.verify_grouped_gemm_shared(
+                    dx, gm["sorted_token"], gm["offsets"], L.t16, T, rows, H, I, E, ws, sw,
+                    active=gm["active"], n_active=gm["n_active"], err_word=err)
+        out = fve.moe_combine(y, gm["pair_pos"], w, sh, gate)
+        torch.cuda.synchronize()
+        assert int(host(err)[0]) == 0
+        assert np.array_equal(host(ids), r["ids"])
+        for key in ("offsets", "active", "n_active"):
+            assert np.array_equal(host(gm[key]).ravel(), np.ravel(maps[key])), key
+        for key in ("sorted_token", "sorted_pair", "pair_pos"):
+            assert np.array_equal(host(gm[key])[:rows], maps[key][:rows]), key
+        ref = oracle.moe_layer(x, L.router, k, experts, kind, shared=L.shared)
+        assert_fp16_close(host(sh), ref["shared_out"], f"{kind} shared {shape}")
+        assert_fp16_close(host(y)[:rows], ref["y_sorted"], f"{kind} FFN {shape}")
+        assert_fp16_close(host(out), ref["out"], f"{kind} layer {shape}")
