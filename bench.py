@@ -31,6 +31,7 @@ Printed JSON line (rank 0):
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -102,6 +103,10 @@ def main():
         print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); the path is "
               "single-GPU and no multi-GPU figure is produced.", file=sys.stderr)
         sys.exit(2)
+    # no cyclic-garbage pass inside a timed region (a host pause there leaves
+    # the GPU idle between a step's events); the run is short-lived
+    gc.collect()
+    gc.disable()
     if args.workload == "qwen_chunk":
         return bench_qwen_chunk(args)
     if args.workload == "route_fidelity":
