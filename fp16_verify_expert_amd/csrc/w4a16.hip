@@ -78,9 +78,6 @@ struct QF {
 #ifndef SMOE_W4_ROWFENCE
 #define SMOE_W4_ROWFENCE 1
 #endif
-#ifndef SMOE_W4_PREFETCH
-#define SMOE_W4_PREFETCH 1
-#endif
 #ifndef SMOE_W4_MFMA
 #define SMOE_W4_MFMA 1  // multi-row 4-bit steps on the MFMA kernel
 #endif
