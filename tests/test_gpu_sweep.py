@@ -136,3 +136,49 @@ def test_random_shared_expert_layers(shape):
         assert_fp16_close(host(sh), ref["shared_out"], f"{kind} shared {shape}")
         assert_fp16_close(host(y)[:rows], ref["y_sorted"], f"{kind} FFN {shape}")
         assert_fp16_close(host(out), ref["out"], f"{kind} layer {shape}")
+
+
+@st.composite
+def dense_shapes(draw):
+    E = draw(st.integers(1, 12))
+    k = draw(st.integers(1, min(E, 4)))
+    per = draw(st.sampled_from([64, 100, 128, 160, 256, 300]))  # mean rows per expert
+    T = max(1, (per * E + k - 1) // k)
+    H = 128 * draw(st.integers(1, 4))
+    I = 128 * draw(st.integers(1, 3))
+    return E, k, T, H, I
+
+
+@settings(max_examples=16, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(dense_shapes())
+# the register-staged form (under a full row tile per expert), the ring form
+# with 256- and 128-column down tiles (H a multiple of 256 or not)
+@example((8, 2, 400, 256, 256))
+@example((4, 2, 512, 512, 128))
+@example((4, 2, 512, 384, 256))
+def test_random_dense_regime(shape):
+    """Randomised shapes in the dense regime of verify_grouped_gemm (at least
+    64 rows per expert): the tiled GEMM in its register-staged or ring form,
+    full and partial column blocks, against the oracle's per-expert loop."""
+    E, k, T, H, I = shape
+    say(f"dense sweep E={E} k={k} T={T} H={H} I={I}")
+    s = dataclasses.replace(synth.TINY, name=f"dn_{E}_{k}_{H}_{I}", E=E, k=k, H=H, I=I)
+    x = synth.tokens(s, T, step=3 * E + k)
+    L = Layer(s, [x], int4=False)
+    dx = dev(x)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    r = oracle.route_topk(x, L.router, k)
+    maps = oracle.gather_maps(r["ids"], E)
+    rows = T * k
+    assert rows >= 64 * min(E, rows)
+    ids, _, _ = fve.moe_route_topk(dx, L.d_router, k)
+    gm = fve.moe_gather(ids, E, err)
+    ws = fve.new_workspace(1, T, k, H, I, E)
+    y = fve.verify_grouped_gemm(dx, gm["sorted_token"], gm["offsets"], L.t16, T, rows, H, I, E,
+                                ws, active=gm["active"], n_active=gm["n_active"], err_word=err)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) == 0
+    assert np.array_equal(host(ids), r["ids"])
+    ref = oracle.grouped_ffn(x, maps, L.f16, "f16")
+    assert_fp16_close(host(y)[:rows], ref, f"dense {shape}")
