@@ -182,3 +182,59 @@ def test_random_dense_regime(shape):
     assert np.array_equal(host(ids), r["ids"])
     ref = oracle.grouped_ffn(x, maps, L.f16, "f16")
     assert_fp16_close(host(y)[:rows], ref, f"dense {shape}")
+
+
+@st.composite
+def draft_format_shapes(draw):
+    E = draw(st.integers(1, 64))
+    k = draw(st.integers(1, min(E, 8)))
+    T = draw(st.sampled_from([1, 1, 2, 3, 4, 7, 16, 17, 33]))
+    H = 128 * draw(st.integers(1, 6))
+    I = 128 * draw(st.integers(1, 6))
+    fmt = draw(st.sampled_from(["int2", "int4", "int8", "awq"]))
+    return E, k, T, H, I, fmt
+
+
+@settings(max_examples=20, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(draft_format_shapes())
+@example((16, 2, 1, 1024, 1024, "int8"))   # long 8-bit reductions at one token
+@example((16, 4, 16, 1024, 512, "int2"))
+@example((8, 2, 5, 512, 384, "awq"))
+def test_random_draft_formats(shape):
+    """Randomised shapes for the other draft formats: wq_grouped_ffn at 2, 4
+    and 8 bits (GPTQ layout) and awq_grouped_ffn (per-input-channel divisors)
+    against the oracle's per-expert loop of the same codes."""
+    E, k, T, H, I, fmt = shape
+    say(f"format sweep {fmt} E={E} k={k} T={T} H={H} I={I}")
+    s = dataclasses.replace(synth.TINY, name=f"fm_{E}_{k}_{H}_{I}", E=E, k=k, H=H, I=I)
+    x = synth.tokens(s, T, step=2 * E + k + T)
+    router = synth.router(s)
+    r = oracle.route_topk(x, router, k)
+    touched = sorted(set(int(e) for e in r["ids"].ravel()))
+    ex = [None] * E
+    for e in touched:
+        w13, w2 = synth.expert_f16(s, 0, e)
+        ex[e] = (synth.expert_awq(s, 0, e, w13, w2) if fmt == "awq"
+                 else synth.expert_int4(w13, w2, bits=int(fmt[3:])))
+    gpu = [None if q is None else {key: tuple(dev(t) for t in q[key]) for key in ("w13", "w2")}
+           for q in ex]
+    table = fve.w4_expert_table(gpu)
+    maps = oracle.gather_maps(r["ids"], E)
+    ref = oracle.grouped_ffn(x, maps, ex, fmt)
+    dx = dev(x)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ids, _, _ = fve.moe_route_topk(dx, dev(router), k)
+    gm = fve.moe_gather(ids, E, err)
+    ws = fve.new_workspace(0, T, k, H, I, E)
+    if fmt == "awq":
+        sc = [None if q is None else (dev(q["a13"]), dev(q["a2"])) for q in ex]
+        stab = fve.awq_scale_table(sc)
+        y = fve.awq_grouped_ffn(dx, gm, table, stab, T, k, H, I, E, ws, err_word=err)
+    else:
+        y = fve.wq_grouped_ffn(dx, gm, table, T, k, H, I, E, ws, int(fmt[3:]), err_word=err)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) == 0
+    assert np.array_equal(host(ids), r["ids"])
+    rows = T * k
+    assert_fp16_close(host(y)[:rows], ref, f"{fmt} FFN {shape}")
