@@ -238,3 +238,72 @@ def test_random_draft_formats(shape):
     assert np.array_equal(host(ids), r["ids"])
     rows = T * k
     assert_fp16_close(host(y)[:rows], ref, f"{fmt} FFN {shape}")
+
+
+@st.composite
+def routing_shapes(draw):
+    E = draw(st.sampled_from([1, 2, 7, 16, 60, 64, 100, 128, 256]))
+    k = draw(st.integers(1, min(E, 16)))
+    T = draw(st.sampled_from([1, 2, 5, 16, 33, 100, 257]))
+    H = 128 * draw(st.integers(1, 16))
+    renorm = draw(st.booleans())
+    gated = draw(st.booleans())
+    return E, k, T, H, renorm, gated
+
+
+@settings(max_examples=24, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(routing_shapes())
+@example((256, 16, 15, 2048, False, True))    # the largest router, spread plan
+@example((256, 16, 257, 2048, False, True))   # beyond the plan's step size: refused
+@example((64, 6, 16, 2048, False, False))     # DeepSeek-like, two-launch plan
+@example((16, 2, 1, 4096, True, False))       # one token, renormalised
+def test_random_routing(shape):
+    """Randomised routing shapes through moe_route_topk and both forms of
+    moe_route_plan (with a logits workspace: spread over the chip where the
+    step is large; without: one workgroup or the routing kernel): ids, ELB
+    counts (layer 1 of 2) and the gather maps exact, weights and the shared
+    gate within 1e-5 of the oracle; steps above the plan's 1024 pairs or
+    4096 logits are refused with a shape error."""
+    E, k, T, H, renorm, gated = shape
+    say(f"routing sweep E={E} k={k} T={T} H={H} renorm={renorm} gated={gated}")
+    s = dataclasses.replace(synth.TINY, name=f"rt_{E}_{k}_{H}", E=E, k=k, H=H,
+                            shared_I=128 if gated else 0, shared_gate=gated,
+                            renormalize=renorm)
+    router = synth.router(s)
+    gate_vec = synth.shared_expert(s)["gate"] if gated else None
+    x = synth.tokens(s, T, step=E + k + T)
+    ref = oracle.route_topk(x, router, k, renorm, gate_vec)
+    maps = oracle.gather_maps(ref["ids"], E)
+    cref = oracle.elb_update(np.zeros((2, E), np.int32), ref["ids"], 1)
+    dx, dr = dev(x), dev(router)
+    dg = dev(gate_vec) if gated else None
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def check(ids, w, gate, what):
+        assert np.array_equal(host(ids), ref["ids"]), what
+        assert np.allclose(host(w), ref["weights"], rtol=1e-5, atol=1e-7), what
+        if gated:
+            assert np.allclose(host(gate), ref["gate"], rtol=1e-5, atol=1e-7), what
+
+    ids, w, gate = fve.moe_route_topk(dx, dr, k, renorm, dg)
+    torch.cuda.synchronize()
+    check(ids, w, gate, "moe_route_topk")
+    rows = T * k
+    for spread in (True, False):
+        counters = torch.zeros((2, E), dtype=torch.int32, device="cuda")
+        if rows > 1024 or T * (E + 1) > 4096:  # beyond the plan's documented sizes: refused
+            with pytest.raises(fve.SmoeError):
+                fve.moe_route_plan(dx, dr, k, renorm, dg, counters=counters, layer=1,
+                                   err_word=err, spread=spread)
+            continue
+        ids, w, gate, gm = fve.moe_route_plan(dx, dr, k, renorm, dg, counters=counters, layer=1,
+                                             err_word=err, spread=spread)
+        torch.cuda.synchronize()
+        assert int(host(err)[0]) == 0
+        check(ids, w, gate, f"moe_route_plan spread={spread}")
+        assert np.array_equal(host(counters), cref), f"ELB spread={spread}"
+        for key in ("offsets", "active", "n_active"):
+            assert np.array_equal(host(gm[key]).ravel(), np.ravel(maps[key])), (key, spread)
+        for key in ("sorted_token", "sorted_pair", "pair_pos"):
+            assert np.array_equal(host(gm[key])[:rows], maps[key][:rows]), (key, spread)
