@@ -307,3 +307,51 @@ def test_random_routing(shape):
             assert np.array_equal(host(gm[key]).ravel(), np.ravel(maps[key])), (key, spread)
         for key in ("sorted_token", "sorted_pair", "pair_pos"):
             assert np.array_equal(host(gm[key])[:rows], maps[key][:rows]), (key, spread)
+
+
+@st.composite
+def one_token_shapes(draw):
+    E = draw(st.sampled_from([1, 2, 8, 16, 60, 64, 100, 256]))
+    k = draw(st.integers(1, min(E, 16)))
+    H = 128 * draw(st.integers(1, 16))
+    I = 128 * draw(st.integers(1, 12))
+    renorm = draw(st.booleans())
+    return E, k, H, I, renorm
+
+
+@settings(max_examples=20, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(one_token_shapes())
+@example((256, 16, 2048, 512, False))
+@example((16, 2, 2048, 1536, True))
+def test_random_one_token_draft(shape):
+    """Randomised one-token draft steps through moe_draft_route_ffn (the
+    routing folded into the gate/up launch; no shared expert) with ELB counts
+    (layer 0 of 1) and moe_combine: ids, counts and maps exact, weights within
+    1e-5, y and the layer output against oracle.moe_layer."""
+    E, k, H, I, renorm = shape
+    say(f"one-token sweep E={E} k={k} H={H} I={I} renorm={renorm}")
+    s = dataclasses.replace(synth.TINY, name=f"ot_{E}_{k}_{H}_{I}", E=E, k=k, H=H, I=I,
+                            renormalize=renorm)
+    x = synth.tokens(s, 1, step=E + k + H // 128)
+    L = Layer(s, [x], f16=False)
+    dx = dev(x)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    counters = torch.zeros((1, E), dtype=torch.int32, device="cuda")
+    ws = fve.new_workspace(0, 1, k, H, I, E)
+    ids, w, _, gm, y = fve.moe_draft_route_ffn(dx, L.d_router, k, L.t4, I, ws, renorm,
+                                               counters=counters, err_word=err)
+    out = fve.moe_combine(y, gm["pair_pos"], w)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) == 0
+    ref = oracle.moe_layer(x, L.router, k, L.int4, "int4", renormalize=renorm)
+    assert np.array_equal(host(ids), ref["route"]["ids"])
+    assert np.allclose(host(w), ref["route"]["weights"], rtol=1e-5, atol=1e-7)
+    assert np.array_equal(host(counters),
+                          oracle.elb_update(np.zeros((1, E), np.int32), ref["route"]["ids"], 0))
+    for key in ("offsets", "active", "n_active"):
+        assert np.array_equal(host(gm[key]).ravel(), np.ravel(ref["maps"][key])), key
+    for key in ("sorted_token", "sorted_pair", "pair_pos"):
+        assert np.array_equal(host(gm[key])[:k], ref["maps"][key][:k]), key
+    assert_fp16_close(host(y)[:k], ref["y_sorted"], f"one-token FFN {shape}")
+    assert_fp16_close(host(out), ref["out"], f"one-token layer {shape}")
