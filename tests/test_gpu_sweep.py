@@ -355,3 +355,66 @@ def test_random_one_token_draft(shape):
         assert np.array_equal(host(gm[key])[:k], ref["maps"][key][:k]), key
     assert_fp16_close(host(y)[:k], ref["y_sorted"], f"one-token FFN {shape}")
     assert_fp16_close(host(out), ref["out"], f"one-token layer {shape}")
+
+
+@st.composite
+def combine_shapes(draw):
+    T = draw(st.sampled_from([1, 1, 2, 3, 8, 9, 17, 33, 100]))
+    k = draw(st.integers(1, 16))
+    H = 128 * draw(st.integers(1, 32))
+    shared = draw(st.sampled_from(["none", "ungated", "gated"]))
+    resid = draw(st.booleans())
+    norm = draw(st.booleans())
+    drop = draw(st.booleans())
+    return T, k, H, shared, resid, norm, drop
+
+
+@settings(max_examples=24, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(combine_shapes())
+@example((1, 6, 2048, "none", True, True, False))
+@example((1, 4, 2048, "gated", True, True, True))
+@example((100, 8, 4096, "ungated", True, True, True))
+def test_random_combine(shape):
+    """Randomised combines: moe_combine (slots, dropped pairs, the shared term
+    with or without its gate, the residual, the norm epilogue) against
+    oracle.combine and oracle.rms_norm; for one token also
+    moe_combine_route_logits, whose out and norm_out equal moe_combine's bit
+    for bit and whose logits equal the oracle's pinned-order fp32 logits of
+    that norm_out."""
+    T, k, H, shared, resid, norm, drop = shape
+    say(f"combine sweep T={T} k={k} H={H} shared={shared} resid={resid} norm={norm} drop={drop}")
+    rng = np.random.default_rng(T * 1000 + k * 10 + H // 128)
+    n = T * k
+    y = rng.standard_normal((n, H)).astype(np.float16)
+    pp = rng.permutation(n).astype(np.int32)
+    if drop:
+        pp[rng.integers(0, n)] = -1
+    w = rng.random((T, k)).astype(np.float32)
+    sh = rng.standard_normal((T, H)).astype(np.float16) if shared != "none" else None
+    c = rng.random(T).astype(np.float32) if shared == "gated" else None
+    res = rng.standard_normal((T, H)).astype(np.float16) if resid else None
+    d = lambda a: None if a is None else dev(a)
+    ref = oracle.combine(y, pp, w.astype(np.float64), sh, c, res)
+    got = fve.moe_combine(dev(y), dev(pp), dev(w), d(sh), d(c), d(res), norm_out=norm)
+    out = got[0] if norm else got
+    torch.cuda.synchronize()
+    assert_fp16_close(host(out), ref, f"combine {shape}", l2=1e-3, maxabs=4e-3)
+    if norm:
+        assert_fp16_close(host(got[1]), oracle.rms_norm(host(out)), f"combine norm {shape}",
+                          l2=1e-3, maxabs=4e-3)
+    if T == 1:
+        E = 1 + (k * 7) % 64
+        rs = dataclasses.replace(synth.TINY, name=f"cb_{E}_{H}", E=E, H=H)
+        router = synth.router(rs, 3)
+        wsg = rng.standard_normal(H).astype(np.float16) if shared == "gated" else None
+        o2, n2, lg = fve.moe_combine_route_logits(dev(y), dev(pp), dev(w), dev(router), d(sh),
+                                                  d(c), d(res), d(wsg))
+        o1, n1 = fve.moe_combine(dev(y), dev(pp), dev(w), d(sh), d(c), d(res), norm_out=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, o1) and torch.equal(n2, n1)
+        ref_lg = oracle.logits_pinned_f32(host(n1), router)[0]
+        assert np.array_equal(host(lg)[:E].view(np.uint32), ref_lg.view(np.uint32))
+        if wsg is not None:
+            ref_g = oracle.logits_pinned_f32(host(n1), wsg[None, :])[0]
+            assert np.array_equal(host(lg)[E:].view(np.uint32), ref_g.view(np.uint32))
