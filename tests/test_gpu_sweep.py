@@ -418,3 +418,51 @@ def test_random_combine(shape):
         if wsg is not None:
             ref_g = oracle.logits_pinned_f32(host(n1), wsg[None, :])[0]
             assert np.array_equal(host(lg)[E:].view(np.uint32), ref_g.view(np.uint32))
+
+
+@st.composite
+def mask_shapes(draw):
+    E = draw(st.integers(2, 64))
+    k = draw(st.integers(1, min(E, 8)))
+    T = draw(st.sampled_from([1, 2, 4, 9, 17, 33, 200]))
+    H = 128 * draw(st.integers(1, 16))
+    I = 128 * draw(st.integers(1, 12))
+    frac = draw(st.sampled_from([0.0, 0.25, 0.5, 1.0]))
+    return E, k, T, H, I, frac
+
+
+@settings(max_examples=20, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(mask_shapes())
+@example((16, 2, 17, 2048, 1024, 0.5))    # ring kernels at K+1 = 17
+@example((8, 2, 200, 256, 256, 0.25))     # dense regime
+@example((60, 4, 9, 2048, 1408, 0.5))     # 2-wave ring, Qwen-like
+def test_random_verify_mask(shape):
+    """verify_grouped_gemm over a random expert mask and then its complement
+    into the same output (hits computed before the staged misses arrive)
+    equals one call over all experts bit for bit, in every launch form the
+    shapes reach (matrix-vector, register, ring and dense regimes)."""
+    E, k, T, H, I, frac = shape
+    say(f"mask sweep E={E} k={k} T={T} H={H} I={I} frac={frac}")
+    s = dataclasses.replace(synth.TINY, name=f"mk_{E}_{k}_{H}_{I}", E=E, k=k, H=H, I=I)
+    x = synth.tokens(s, T, step=5 * E + k + T)
+    L = Layer(s, [x], int4=False)
+    dx = dev(x)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ids, _, _ = fve.moe_route_topk(dx, L.d_router, k)
+    gm = fve.moe_gather(ids, E, err)
+    rows = T * k
+    ws = fve.new_workspace(1, T, k, H, I, E)
+    full = fve.verify_grouped_gemm(dx, gm["sorted_token"], gm["offsets"], L.t16, T, rows, H, I,
+                                   E, ws, active=gm["active"], n_active=gm["n_active"],
+                                   err_word=err)
+    rng = np.random.default_rng(E * 100 + T)
+    hit = torch.from_numpy((rng.random(E) < frac).astype(np.uint8)).cuda()
+    y = torch.full_like(full, float("nan"))
+    for m in (hit, 1 - hit):
+        fve.verify_grouped_gemm(dx, gm["sorted_token"], gm["offsets"], L.t16, T, rows, H, I, E,
+                                ws, active=gm["active"], n_active=gm["n_active"],
+                                expert_mask=m, y_sorted=y, err_word=err)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) == 0
+    assert torch.equal(y[:rows], full[:rows])
