@@ -1575,6 +1575,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void route_w4_kernel(W4Args a, RouteArgs
     const int E = a.E, k = r.k;
 
     const smoe_w4_expert spec = spec_table(a, lane);
+    // the token row, requested with the logits (its latency overlaps the
+    // routing below)
+    uint4 xv[kRowChunksPerThread];
+    request_row(reinterpret_cast<const uint4*>(a.xin), a.K >> 3, xv);
 
     // 1. the router logits of the launch before
     const int nvec = E + (r.wsg ? 1 : 0);
@@ -1603,12 +1607,9 @@ __attribute__((amdgpu_waves_per_eu(2))) void route_w4_kernel(W4Args a, RouteArgs
         for (int i = 0; i < k; ++i) less += (ids_s[i] < ids_s[j]) ? 1 : 0;
         if (less == slot) e = ids_s[j];
     }
-    // 5. this slot's block of the gate/up projection (the token row is in L2
-    //    after the logits; it is requested here to keep registers free)
+    // 5. this slot's block of the gate/up projection
     if (cb == 0) write_slot_desc(a, spec, slot, e);
     if (e >= 0) {
-        uint4 xv[kRowChunksPerThread];
-        request_row(reinterpret_cast<const uint4*>(a.xin), a.K >> 3, xv);
         one_token_block<4, 1, LPR, NG>(a, carve_lds<4>(smem, a), pick_mat<1>(a, spec, e), xv,
                                        slot, cb);
     }
